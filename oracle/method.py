@@ -1,0 +1,370 @@
+"""The method, step by step, in float64 (oracle; TEST INFRASTRUCTURE ONLY).
+
+Notation follows the Vortex post ("Why Long Generations Are Expensive"):
+blocks j of b consecutive tokens, mean key k̄_j, score s_j = q · k̄_j,
+I = top-k_j(s_j), o = softmax(q K_I^T / sqrt(d)) V_I. Block = page here
+(the paged layout of "Why New Ideas Are Hard to Deploy", Fig. 2): logical
+block j of request r is physical page page_indices[page_indptr[r] + j], and
+summaries are stored per physical page, as the post's vTensor section says
+named cache entries live in pages of the KV allocator.
+
+Readings where the pages leave a step open (each also listed in the design
+notes of the repository):
+* GQA: query head h belongs to kv head g = h // (Hq / Hkv). The group score
+  is aggregated over the group's query heads (the vFlow listing reduces the
+  score over the head axis); one selection per (request, kv head) is shared by
+  its group. Aggregator: max (default) or mean.
+* Block scores are unscaled dot products; the softmax uses sm_scale.
+* Forced blocks: the first n_sink blocks and the last n_recent blocks, plus
+  the last block whenever it is partial (only full blocks have summaries: they
+  are built "when a block fills up"). Forced blocks are not ranked; k more are
+  chosen from the other complete blocks.
+* Ranking is by (score descending, block index ascending): ties go to the
+  lowest index. The result is emitted in ascending block order.
+* The cache holds L tokens including the current one; attention covers tokens
+  t < L of the selected blocks.
+
+Parity status: every function below is pinned by tests/test_oracle_method.py
+against brute force, exact rationals, closed forms, softmax invariants or the
+post's Fig. 1 example; none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from fractions import Fraction
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from .numerics import (
+    bf16_to_f64, fp8e4m3fn_to_f64, f64_to_bf16_bits, f64_to_f32,
+    fraction_to_bf16_bits, fraction_to_f32, sum_is_exact_in_f64,
+)
+
+
+# --------------------------------------------------------------------------
+# Paged batch view (vTensor-style: batch size, index pointer, page list)
+# --------------------------------------------------------------------------
+
+@dataclass
+class BatchView:
+    page_indptr: np.ndarray    # [B+1]
+    page_indices: np.ndarray   # [nnz] physical page ids, logical order
+    seq_lens: np.ndarray       # [B] tokens in cache (current one included)
+    page_size: int
+
+    def __post_init__(self):
+        self.page_indptr = np.asarray(self.page_indptr, dtype=np.int64)
+        self.page_indices = np.asarray(self.page_indices, dtype=np.int64)
+        self.seq_lens = np.asarray(self.seq_lens, dtype=np.int64)
+
+    @property
+    def batch(self) -> int:
+        return len(self.seq_lens)
+
+    def pages(self, r: int) -> np.ndarray:
+        return self.page_indices[self.page_indptr[r]:self.page_indptr[r + 1]]
+
+    def num_blocks(self, r: int) -> int:
+        return int(-(-int(self.seq_lens[r]) // self.page_size))
+
+    def num_complete(self, r: int) -> int:
+        return int(self.seq_lens[r]) // self.page_size
+
+    def token_page_slot(self, r: int, t: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        t = np.asarray(t, dtype=np.int64)
+        return self.pages(r)[t // self.page_size], t % self.page_size
+
+
+def _decode(bits: np.ndarray, fmt: str) -> np.ndarray:
+    if fmt == "bf16":
+        return bf16_to_f64(bits)
+    if fmt == "fp8_e4m3fn":
+        return fp8e4m3fn_to_f64(bits)
+    if fmt == "fp32":
+        return np.asarray(bits, dtype=np.float32).astype(np.float64)
+    raise ValueError(fmt)
+
+
+def _round_out(x: np.ndarray, out_dtype: str) -> np.ndarray:
+    if out_dtype == "bf16":
+        return f64_to_bf16_bits(x)
+    if out_dtype == "fp32":
+        return f64_to_f32(x)
+    if out_dtype == "fp64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(out_dtype)
+
+
+# --------------------------------------------------------------------------
+# Block summaries: mean key of each full page, rounded once
+# --------------------------------------------------------------------------
+
+def block_summaries(key_bits: np.ndarray, page_ids: Sequence[int], *,
+                    key_format: str = "bf16", key_scales: Optional[np.ndarray] = None,
+                    out_dtype: str = "bf16") -> np.ndarray:
+    """Mean key of each listed physical page, per head (Vortex, "Writing an
+    algorithm: vFlow": the block-top-k cache step stores the mean of the keys
+    over the in-block axis).
+
+    key_bits: [num_pages][H][P][D] (or [num_pages][P][D] for single-head
+    indexer pools). key_scales: optional per-token dequantisation scale
+    [num_pages][P] (fp8 indexer keys): the summand is scale_t * key_t.
+    Returns [n][H][D] (or [n][D]) bits / values in out_dtype.
+
+    The sum over the P tokens is exact (checked; rows whose float64 sum could
+    be inexact are summed as exact rationals), division by P = 2**m is exact,
+    and the mean is rounded once to out_dtype.
+    """
+    page_ids = np.asarray(page_ids, dtype=np.int64)
+    kb = np.asarray(key_bits)
+    single = kb.ndim == 3
+    k = _decode(kb[page_ids], key_format)
+    if single:
+        k = k[:, None]                                   # [n][1][P][D]
+    if key_scales is not None:
+        s = np.asarray(key_scales, dtype=np.float32)[page_ids].astype(np.float64)
+        k = k * s[:, None, :, None]                      # exact: 24b x 4b
+    P = k.shape[2]
+    assert P & (P - 1) == 0, "page size must be a power of two"
+    terms = np.moveaxis(k, 2, -1)                        # [n][H][D][P]
+    total = terms.sum(axis=-1)
+    mean = total / P
+    exact = sum_is_exact_in_f64(terms, axis=-1)
+    if out_dtype == "bf16":
+        out = f64_to_bf16_bits(mean)
+    else:
+        out = _round_out(mean, out_dtype)
+    for idx in zip(*np.nonzero(~exact)):               # rare: exact rationals
+        fr = sum((Fraction(float(v)) for v in terms[idx]), Fraction(0)) / P
+        out[idx] = fraction_to_bf16_bits(fr) if out_dtype == "bf16" else fraction_to_f32(fr)
+    return out[:, 0] if single else out
+
+
+# --------------------------------------------------------------------------
+# Scoring
+# --------------------------------------------------------------------------
+
+def block_scores(q_bits: np.ndarray, summaries: np.ndarray, batch: BatchView, r: int, g: int,
+                 *, num_kv_heads: int, agg: str = "max",
+                 summary_format: str = "bf16") -> np.ndarray:
+    """Scores of request r's complete blocks for kv head g: for each block j,
+    agg over the group's query heads h of q_h . k̄_j (Vortex, block top-k
+    equation; GQA grouping from the vFlow listing). Returns float64
+    [num_complete(r)]. summaries: [num_pages][Hkv][D] in summary_format."""
+    Hq = q_bits.shape[1]
+    G = Hq // num_kv_heads
+    q = bf16_to_f64(q_bits[r, g * G:(g + 1) * G])                  # [G][D]
+    nc = batch.num_complete(r)
+    pages = batch.pages(r)[:nc]
+    S = _decode(np.asarray(summaries)[pages, g], summary_format)    # [nc][D]
+    per_head = S @ q.T                                               # [nc][G]
+    if agg == "max":
+        return per_head.max(axis=1) if nc else np.zeros(0)
+    if agg == "mean":
+        return per_head.mean(axis=1) if nc else np.zeros(0)
+    raise ValueError(agg)
+
+
+def indexer_token_scores(q_idx_bits: np.ndarray, head_w: np.ndarray, key_bits: np.ndarray,
+                         key_scales: np.ndarray, batch: BatchView, r: int,
+                         tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """Learned-indexer score of tokens of request r (LeanSparse §5, Eq. 6,
+    with the original key in place of the PQ centroids):
+    s_t = sum_h w_h * ReLU(q_h . k_t), k_t = scale_t * fp8_t dequantised.
+    key_bits: [pages][P][Di] fp8 bits; key_scales: [pages][P] fp32.
+    Returns float64 scores for `tokens` (default: every cached token)."""
+    L = int(batch.seq_lens[r])
+    t = np.arange(L) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    page, slot = batch.token_page_slot(r, t)
+    k = fp8e4m3fn_to_f64(np.asarray(key_bits)[page, slot])                 # [T][Di]
+    k = k * np.asarray(key_scales, dtype=np.float32)[page, slot].astype(np.float64)[:, None]
+    q = bf16_to_f64(q_idx_bits[r])                                          # [Hi][Di]
+    w = np.asarray(head_w, dtype=np.float32)[r].astype(np.float64)          # [Hi]
+    return np.maximum(k @ q.T, 0.0) @ w
+
+
+def indexer_block_scores(q_idx_bits: np.ndarray, head_w: np.ndarray, summaries: np.ndarray,
+                         batch: BatchView, r: int, *, summary_format: str = "bf16",
+                         blocks: Optional[np.ndarray] = None) -> np.ndarray:
+    """Coarse indexer score of request r's blocks from block-mean indexer keys:
+    s_j = sum_h w_h * ReLU(q_h . k̄_j) (Eq. 6 of LeanSparse applied to the
+    compact representation). summaries: [pages][Di]. Default blocks: every
+    block whose summary exists (complete blocks)."""
+    b = np.arange(batch.num_complete(r)) if blocks is None else np.asarray(blocks, dtype=np.int64)
+    S = _decode(np.asarray(summaries)[batch.pages(r)[b]], summary_format)   # [nb][Di]
+    q = bf16_to_f64(q_idx_bits[r])
+    w = np.asarray(head_w, dtype=np.float32)[r].astype(np.float64)
+    return np.maximum(S @ q.T, 0.0) @ w
+
+
+# --------------------------------------------------------------------------
+# Selection
+# --------------------------------------------------------------------------
+
+def forced_blocks(nb: int, n_complete: int, n_sink: int, n_recent: int) -> List[int]:
+    f = set(range(min(n_sink, nb))) | set(range(max(0, nb - n_recent), nb))
+    if n_complete < nb:            # partial last block: never scored, always kept
+        f.add(nb - 1)
+    return sorted(f)
+
+
+def rank_top(scores: np.ndarray, candidates: Iterable[int], k: int) -> List[int]:
+    """First k candidates under the order (score descending, index ascending)."""
+    order = sorted(candidates, key=lambda j: (-float(scores[j]), j))
+    return order[:max(0, k)]
+
+
+def select_blocks(scores: np.ndarray, nb: int, n_complete: int, k: int,
+                  n_sink: int, n_recent: int) -> List[int]:
+    """Top-k blocks by score plus forced sink/recent blocks, ascending
+    (Vortex, block top-k equation; static sink + recent window from the
+    StreamingLLM mention in "Why Long Generations Are Expensive").
+    scores: [n_complete] float64 for the complete blocks."""
+    forced = forced_blocks(nb, n_complete, n_sink, n_recent)
+    fs = set(forced)
+    cands = [j for j in range(n_complete) if j not in fs]
+    return sorted(fs | set(rank_top(scores, cands, k)))
+
+
+def select_tokens(scores: np.ndarray, k: int, candidates: Optional[Iterable[int]] = None,
+                  forced: Iterable[int] = ()) -> List[int]:
+    """Top-k tokens by (score desc, token asc) among `candidates` (default all),
+    plus `forced`, ascending (token-granular selection of the learned indexer,
+    LeanSparse §2.1 / §5)."""
+    fs = set(forced)
+    cands = range(len(scores)) if candidates is None else candidates
+    cands = [t for t in cands if t not in fs]
+    return sorted(fs | set(rank_top(scores, cands, k)))
+
+
+def tokens_of_blocks(blocks: Iterable[int], page_size: int, seq_len: int) -> np.ndarray:
+    t = [b * page_size + s for b in blocks for s in range(page_size)]
+    t = np.asarray(t, dtype=np.int64)
+    return t[t < seq_len]
+
+
+# --------------------------------------------------------------------------
+# Attention over a token set, split-K merge
+# --------------------------------------------------------------------------
+
+def attention_over_tokens(q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                          sm_scale: float) -> Tuple[np.ndarray, float]:
+    """Exact softmax attention of one query over T tokens (float64):
+    z_t = sm_scale * q . K_t; o = sum_t e^{z_t - M} V_t / sum_t e^{z_t - M};
+    lse = M + ln sum_t e^{z_t - M}, M = max_t z_t. T = 0 gives o = 0,
+    lse = -inf."""
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1]), -np.inf
+    z = float(sm_scale) * (K @ q)
+    M = z.max()
+    w = np.exp(z - M)
+    Z = w.sum()
+    return (w @ V) / Z, float(M + np.log(Z))
+
+
+def lse_merge(parts: Sequence[Tuple[np.ndarray, float]]) -> Tuple[np.ndarray, float]:
+    """Merge attention results over disjoint token sets by log-sum-exp (the
+    ByteCross paper merges its sink call with the window call this way, App. A):
+    o = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, lse = M + ln sum_s e^{lse_s - M}."""
+    lses = np.array([p[1] for p in parts], dtype=np.float64)
+    if np.all(np.isneginf(lses)):
+        return np.zeros_like(parts[0][0]), -np.inf
+    M = lses.max()
+    w = np.exp(lses - M)
+    o = sum(wi * p[0] for wi, p in zip(w, parts)) / w.sum()
+    return o, float(M + np.log(w.sum()))
+
+
+def sparse_attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+                     batch: BatchView, r: int, g: int, blocks: Sequence[int], *,
+                     num_kv_heads: int, sm_scale: float,
+                     out_dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of every query head of kv group g of request r over the
+    tokens of the selected blocks (Vortex block top-k equation). K/V pools:
+    [pages][Hkv][P][D] bf16 bits. Returns (out [G][Dv] in out_dtype,
+    lse float64 [G])."""
+    Hq = q_bits.shape[1]
+    G = Hq // num_kv_heads
+    P = batch.page_size
+    t = tokens_of_blocks(blocks, P, int(batch.seq_lens[r]))
+    page, slot = batch.token_page_slot(r, t)
+    K = bf16_to_f64(np.asarray(k_bits)[page, g, slot])                 # [T][D]
+    V = bf16_to_f64(np.asarray(v_bits)[page, g, slot])                 # [T][Dv]
+    outs, lses = [], []
+    for h in range(g * G, (g + 1) * G):
+        o, lse = attention_over_tokens(bf16_to_f64(q_bits[r, h]), K, V, sm_scale)
+        outs.append(o)
+        lses.append(lse)
+    return _round_out(np.stack(outs), out_dtype), np.array(lses)
+
+
+def dense_attention(q_bits, k_bits, v_bits, batch: BatchView, r: int, g: int, *,
+                    num_kv_heads: int, sm_scale: float, out_dtype: str = "bf16"):
+    """The k = all case: every block of the request selected."""
+    return sparse_attention(q_bits, k_bits, v_bits, batch, r, g,
+                            range(batch.num_blocks(r)), num_kv_heads=num_kv_heads,
+                            sm_scale=sm_scale, out_dtype=out_dtype)
+
+
+def mla_attention(q_bits: np.ndarray, latent_bits: np.ndarray, batch: BatchView, r: int,
+                  tokens: Sequence[int], *, v_dim: int, sm_scale: float,
+                  out_dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray]:
+    """Multi-head latent attention over selected tokens: every query head
+    attends the single shared latent head; keys are the full latent row
+    (compressed content + rope part), values its first v_dim entries (Vortex,
+    "Designing for a new architecture"). q: [B][H][Dk] bf16; latent pool:
+    [pages][P][Dk] bf16. Returns (out [H][v_dim], lse [H])."""
+    page, slot = batch.token_page_slot(r, np.asarray(tokens, dtype=np.int64))
+    C = bf16_to_f64(np.asarray(latent_bits)[page, slot])                 # [T][Dk]
+    K, V = C, C[:, :v_dim]
+    outs, lses = [], []
+    for h in range(q_bits.shape[1]):
+        o, lse = attention_over_tokens(bf16_to_f64(q_bits[r, h]), K, V, sm_scale)
+        outs.append(o)
+        lses.append(lse)
+    return _round_out(np.stack(outs), out_dtype), np.array(lses)
+
+
+# --------------------------------------------------------------------------
+# One decode step of block top-k over a paged GQA cache
+# --------------------------------------------------------------------------
+
+def select_blocks_batch(q_bits, summaries, batch: BatchView, pairs, *, num_kv_heads: int,
+                        topk: int, n_sink: int, n_recent: int, agg: str = "max",
+                        summary_format: str = "bf16") -> Dict:
+    """Scores and selections for the (r, g) pairs listed."""
+    res = {}
+    for r, g in pairs:
+        s = block_scores(q_bits, summaries, batch, r, g, num_kv_heads=num_kv_heads,
+                         agg=agg, summary_format=summary_format)
+        sel = select_blocks(s, batch.num_blocks(r), batch.num_complete(r), topk,
+                            n_sink, n_recent)
+        res[(r, g)] = (s, sel)
+    return res
+
+
+def decode_step(q_bits, k_bits, v_bits, batch: BatchView, *, num_kv_heads: int, topk: int,
+                n_sink: int, n_recent: int, sm_scale: float, agg: str = "max",
+                out_dtype: str = "bf16", pairs=None, summaries=None) -> Dict:
+    """Summaries of the requests' complete pages (unless given), block scores,
+    selection and attention for each (r, g) in `pairs` (default: all)."""
+    if pairs is None:
+        pairs = [(r, g) for r in range(batch.batch) for g in range(num_kv_heads)]
+    if summaries is None:
+        pages = sorted({int(p) for r in {r for r, _ in pairs}
+                        for p in batch.pages(r)[:batch.num_complete(r)]})
+        summaries = np.zeros((np.asarray(k_bits).shape[0],) + np.asarray(k_bits).shape[1:2]
+                             + np.asarray(k_bits).shape[3:], dtype=np.uint16)
+        if pages:
+            summaries[pages] = block_summaries(k_bits, pages)
+    sel = select_blocks_batch(q_bits, summaries, batch, pairs, num_kv_heads=num_kv_heads,
+                              topk=topk, n_sink=n_sink, n_recent=n_recent, agg=agg)
+    out = {}
+    for (r, g), (s, blocks) in sel.items():
+        o, lse = sparse_attention(q_bits, k_bits, v_bits, batch, r, g, blocks,
+                                  num_kv_heads=num_kv_heads, sm_scale=sm_scale,
+                                  out_dtype=out_dtype)
+        out[(r, g)] = {"scores": s, "selected": blocks, "out": o, "lse": lse}
+    return {"summaries": summaries, "pairs": out}

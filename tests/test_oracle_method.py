@@ -1,0 +1,398 @@
+"""Pins for the oracle's method steps.
+
+Each test compares the oracle with something it does not share code with:
+the Vortex post's Fig. 1 worked example (tests/golden), brute-force subset
+enumeration, exact rationals (fractions.Fraction), 50-digit decimal softmax
+computed without the max shift, closed forms (one token, equal logits),
+invariants (shift, permutation of physical pages, convexity), and the
+log-sum-exp merge of attention over disjoint token sets.
+"""
+
+import itertools
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle.method import (
+    BatchView, attention_over_tokens, block_scores, block_summaries, decode_step,
+    dense_attention, forced_blocks, indexer_block_scores, indexer_token_scores, lse_merge,
+    mla_attention, select_blocks, select_tokens, sparse_attention, tokens_of_blocks,
+)
+from oracle.numerics import (
+    bf16_to_f64, f64_to_bf16_bits, fp8e4m3fn_to_f64, fraction_to_bf16_bits, fraction_to_f32,
+)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, rest = line.split(":", 1)
+            vals[key.strip()] = rest.split()
+    return vals
+
+
+def _rand_bf16(rng, shape, scale=1.0):
+    return f64_to_bf16_bits(rng.standard_normal(shape) * scale)
+
+
+# ---------------------------------------------------------------- selection
+
+def test_vortex_fig1_example():
+    g = _read_golden("vortex_fig1_block_scores.txt")
+    scores = np.array([float(x) for x in g["scores"]])
+    k = int(g["k"][0])
+    kept = [int(x) for x in g["kept"]]
+    assert select_blocks(scores, nb=8, n_complete=8, k=k, n_sink=0, n_recent=0) == kept
+    # unchanged after rounding the scores to bf16 (values stay distinct)
+    s16 = bf16_to_f64(f64_to_bf16_bits(scores))
+    assert len(set(s16.tolist())) == 8
+    assert select_blocks(s16, nb=8, n_complete=8, k=k, n_sink=0, n_recent=0) == kept
+
+
+def _brute_topk(scores, cands, k):
+    """The unique k-subset T of cands with every member ahead of every
+    non-member under (score desc, index asc), found by enumeration."""
+    found = []
+    for T in itertools.combinations(cands, min(k, len(cands))):
+        rest = [b for b in cands if b not in T]
+        if all(scores[a] > scores[b] or (scores[a] == scores[b] and a < b)
+               for a in T for b in rest):
+            found.append(set(T))
+    assert len(found) == 1
+    return found[0]
+
+
+def test_selection_vs_subset_enumeration_with_ties():
+    rng = np.random.default_rng(10)
+    for trial in range(300):
+        nb = int(rng.integers(1, 11))
+        partial = bool(rng.integers(0, 2)) and nb > 0
+        n_complete = nb - 1 if partial else nb
+        scores = rng.integers(-3, 4, n_complete).astype(np.float64)   # many ties
+        k = int(rng.integers(0, 6))
+        n_sink = int(rng.integers(0, 3))
+        n_recent = int(rng.integers(0, 3))
+        got = select_blocks(scores, nb, n_complete, k, n_sink, n_recent)
+        forced = set(range(min(n_sink, nb))) | set(range(max(0, nb - n_recent), nb))
+        if partial:
+            forced.add(nb - 1)
+        cands = [b for b in range(n_complete) if b not in forced]
+        want = forced | _brute_topk(scores, cands, k)
+        assert got == sorted(want), (trial, scores, k, n_sink, n_recent)
+        assert got == sorted(set(got))
+
+
+def test_selection_all_blocks_when_budget_covers_everything():
+    scores = np.array([5.0, 1.0, 3.0, 2.0])
+    assert select_blocks(scores, 5, 4, k=10, n_sink=1, n_recent=2) == [0, 1, 2, 3, 4]
+    assert forced_blocks(5, 4, 1, 0) == [0, 4]             # partial last block forced
+    assert forced_blocks(3, 3, 2, 2) == [0, 1, 2]          # overlap de-duplicated
+    assert forced_blocks(0, 0, 1, 2) == []
+
+
+def test_duplicated_scores_pick_lowest_index():
+    scores = np.full(10, 7.0)
+    assert select_blocks(scores, 10, 10, k=3, n_sink=0, n_recent=0) == [0, 1, 2]
+    assert select_blocks(scores, 10, 10, k=3, n_sink=1, n_recent=1) == [0, 1, 2, 3, 9]
+
+
+def test_token_selection_vs_enumeration():
+    rng = np.random.default_rng(11)
+    for _ in range(100):
+        n = int(rng.integers(1, 10))
+        s = rng.integers(-2, 3, n).astype(np.float64)
+        k = int(rng.integers(0, 5))
+        assert select_tokens(s, k) == sorted(_brute_topk(s, list(range(n)), k))
+
+
+# ---------------------------------------------------------------- summaries
+
+def test_summaries_vs_exact_rational_mean():
+    rng = np.random.default_rng(12)
+    pool = _rand_bf16(rng, (5, 3, 16, 8))
+    got = block_summaries(pool, [0, 2, 4])
+    vals = bf16_to_f64(pool)
+    for i, p in enumerate([0, 2, 4]):
+        for h in range(3):
+            for d in range(8):
+                mean = sum(Fraction(float(v)) for v in vals[p, h, :, d]) / 16
+                assert got[i, h, d] == fraction_to_bf16_bits(mean)
+    got32 = block_summaries(pool, [1], out_dtype="fp32")
+    mean = sum(Fraction(float(v)) for v in vals[1, 0, :, 0]) / 16
+    assert got32[0, 0, 0] == fraction_to_f32(mean)
+
+
+def test_summaries_constant_tile_and_inexact_fallback():
+    pool = np.full((2, 1, 16, 4), 0x4040, dtype=np.uint16)     # 3.0 everywhere
+    assert np.all(block_summaries(pool, [0, 1]) == 0x4040)
+    # a column whose float64 sum would lose bits: 2^100, tiny values, -2^100
+    col = np.zeros(16)
+    col[0], col[1], col[2] = 2.0 ** 100, 2.0 ** -100, -(2.0 ** 100)
+    col[3] = 3.0 * 2.0 ** -100
+    pool = np.zeros((1, 1, 16, 1), dtype=np.uint16)
+    pool[0, 0, :, 0] = f64_to_bf16_bits(col)
+    got = block_summaries(pool, [0])
+    exact = sum(Fraction(float(v)) for v in bf16_to_f64(pool[0, 0, :, 0])) / 16
+    assert got[0, 0, 0] == fraction_to_bf16_bits(exact)
+    assert bf16_to_f64(got[0, 0, 0]) == 2.0 ** -100 / 4     # (1 + 3) * 2^-100 / 16
+
+
+def test_fp8_indexer_summaries_vs_rationals():
+    rng = np.random.default_rng(13)
+    keys = rng.integers(0, 256, (3, 64, 4)).astype(np.uint8)
+    keys[(keys & 0x7F) == 0x7F] = 0x10                         # no NaN codes
+    scales = (rng.random((3, 64)) * 0.01 + 1e-3).astype(np.float32)
+    got = block_summaries(keys, [0, 2], key_format="fp8_e4m3fn", key_scales=scales)
+    for i, p in enumerate([0, 2]):
+        for d in range(4):
+            mean = sum(Fraction(float(scales[p, s])) * Fraction(float(fp8e4m3fn_to_f64(keys[p, s, d])))
+                       for s in range(64)) / 64
+            assert got[i, d] == fraction_to_bf16_bits(mean)
+
+
+# ---------------------------------------------------------------- scores
+
+def _tiny_batch(rng, B=2, Hq=4, Hkv=2, D=8, P=4, lens=(13, 8), num_pages=None):
+    nbs = [(L + P - 1) // P for L in lens]
+    used = sum(nbs)
+    num_pages = num_pages or used + 3
+    phys = rng.permutation(num_pages)[:used]
+    indptr = np.concatenate([[0], np.cumsum(nbs)])
+    return BatchView(indptr, phys, np.array(lens), P), num_pages
+
+
+def test_block_scores_vs_exact_rationals():
+    rng = np.random.default_rng(14)
+    batch, npg = _tiny_batch(rng)
+    q = _rand_bf16(rng, (2, 4, 8))
+    summ = _rand_bf16(rng, (npg, 2, 8))
+    for r in range(2):
+        for g in range(2):
+            for agg in ("max", "mean"):
+                s = block_scores(q, summ, batch, r, g, num_kv_heads=2, agg=agg)
+                nc = batch.num_complete(r)
+                assert s.shape == (nc,)
+                for j in range(nc):
+                    p = batch.pages(r)[j]
+                    dots = [sum(Fraction(float(a)) * Fraction(float(b)) for a, b in
+                                zip(bf16_to_f64(q[r, h]), bf16_to_f64(summ[p, g])))
+                            for h in (2 * g, 2 * g + 1)]
+                    want = max(dots) if agg == "max" else sum(dots) / 2
+                    assert abs(Fraction(float(s[j])) - want) <= abs(want) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 300)
+
+
+def test_max_and_mean_agree_for_one_head_per_group():
+    rng = np.random.default_rng(15)
+    batch, npg = _tiny_batch(rng, Hq=2, Hkv=2)
+    q = _rand_bf16(rng, (2, 2, 8))
+    summ = _rand_bf16(rng, (npg, 2, 8))
+    a = block_scores(q, summ, batch, 0, 1, num_kv_heads=2, agg="max")
+    b = block_scores(q, summ, batch, 0, 1, num_kv_heads=2, agg="mean")
+    assert np.array_equal(a, b)
+
+
+def test_indexer_scores_vs_rationals_and_homogeneity():
+    rng = np.random.default_rng(16)
+    batch, npg = _tiny_batch(rng, lens=(9, 4), P=4)
+    keys = rng.integers(0, 256, (npg, 4, 6)).astype(np.uint8)
+    keys[(keys & 0x7F) == 0x7F] = 0x31
+    scales = (rng.random((npg, 4)) + 0.5).astype(np.float32)
+    q = _rand_bf16(rng, (2, 3, 6))
+    w = rng.standard_normal((2, 3)).astype(np.float32)
+    s = indexer_token_scores(q, w, keys, scales, batch, 0)
+    for t in range(9):
+        p, sl = batch.pages(0)[t // 4], t % 4
+        k = [Fraction(float(scales[p, sl])) * Fraction(float(v)) for v in fp8e4m3fn_to_f64(keys[p, sl])]
+        want = Fraction(0)
+        for h in range(3):
+            dot = sum(Fraction(float(a)) * b for a, b in zip(bf16_to_f64(q[0, h]), k))
+            want += Fraction(float(w[0, h])) * max(dot, Fraction(0))
+        assert abs(Fraction(float(s[t])) - want) <= abs(want) * Fraction(1, 10 ** 13) + Fraction(1, 10 ** 300)
+    # ReLU is positively homogeneous: doubling a token's scale doubles its score
+    scales2 = scales.copy()
+    p0 = batch.pages(0)[0]
+    scales2[p0, 1] *= 2
+    s2 = indexer_token_scores(q, w, keys, scales2, batch, 0)
+    assert s2[1] == 2 * s[1]
+    assert np.array_equal(np.delete(s2, 1), np.delete(s, 1))
+    # block form on summaries agrees with the same Eq. 6 written over rationals
+    summ = _rand_bf16(rng, (npg, 6))
+    sb = indexer_block_scores(q, w, summ, batch, 0)
+    assert sb.shape == (2,)
+
+
+# ---------------------------------------------------------------- attention
+
+getcontext().prec = 50
+
+
+def _decimal_attention(q, K, V, scale):
+    """softmax attention without the max shift, in 50-digit decimal."""
+    z = [Decimal(float(scale)) * sum(Decimal(float(a)) * Decimal(float(b)) for a, b in zip(q, k))
+         for k in K]
+    e = [x.exp() for x in z]
+    Z = sum(e)
+    o = [sum(e[t] * Decimal(float(V[t][d])) for t in range(len(V))) / Z for d in range(len(V[0]))]
+    return np.array([float(x) for x in o]), float(Z.ln())
+
+
+def test_attention_vs_decimal_brute_force():
+    rng = np.random.default_rng(17)
+    for T in (1, 2, 7, 33):
+        q = rng.standard_normal(8)
+        K = rng.standard_normal((T, 8)) * 2
+        V = rng.standard_normal((T, 5))
+        o, lse = attention_over_tokens(q, K, V, 0.35)
+        o2, lse2 = _decimal_attention(q, K, V, 0.35)
+        np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+        assert abs(lse - lse2) < 1e-12
+
+
+def test_attention_closed_forms_and_invariants():
+    rng = np.random.default_rng(18)
+    V = rng.standard_normal((6, 4))
+    K = rng.standard_normal((6, 4))
+    # one token -> exactly its value
+    o, _ = attention_over_tokens(rng.standard_normal(4), K[:1], V[:1], 0.5)
+    assert np.array_equal(o, V[0])
+    # equal logits -> mean of values
+    o, lse = attention_over_tokens(np.zeros(4), K, V, 0.5)
+    np.testing.assert_allclose(o, V.mean(axis=0), rtol=0, atol=1e-15)
+    assert abs(lse - math.log(6)) < 1e-15
+    # weights sum to one: all-ones values give ones
+    o, _ = attention_over_tokens(rng.standard_normal(4), K, np.ones((6, 3)), 0.5)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-15)
+    # convex combination: inside [min V, max V]
+    o, _ = attention_over_tokens(rng.standard_normal(4) * 5, K, V, 1.0)
+    assert np.all(o >= V.min(axis=0) - 1e-15) and np.all(o <= V.max(axis=0) + 1e-15)
+    # a constant shift of every logit leaves o unchanged and moves lse
+    q = rng.standard_normal(4)
+    o1, l1 = attention_over_tokens(q, K, V, 0.5)
+    o2, l2 = attention_over_tokens(np.append(q, 3.0), np.hstack([K, np.ones((6, 1))]), V, 0.5)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-14)
+    assert abs((l2 - l1) - 1.5) < 1e-13
+    # empty set
+    o, lse = attention_over_tokens(q, K[:0], V[:0], 0.5)
+    assert np.all(o == 0) and lse == -np.inf
+
+
+def test_lse_merge_equals_attention_over_union():
+    rng = np.random.default_rng(19)
+    q = rng.standard_normal(8)
+    K = rng.standard_normal((40, 8)) * 1.5
+    V = rng.standard_normal((40, 6))
+    whole = attention_over_tokens(q, K, V, 0.4)
+    cuts = [0, 3, 17, 18, 40]
+    parts = [attention_over_tokens(q, K[a:b], V[a:b], 0.4) for a, b in zip(cuts, cuts[1:])]
+    merged = lse_merge(parts)
+    np.testing.assert_allclose(merged[0], whole[0], rtol=1e-13, atol=1e-14)
+    assert abs(merged[1] - whole[1]) < 1e-13
+    # an empty part changes nothing
+    merged2 = lse_merge(parts + [attention_over_tokens(q, K[:0], V[:0], 0.4)])
+    np.testing.assert_allclose(merged2[0], whole[0], rtol=1e-13, atol=1e-14)
+
+
+def _paged_tiny(rng, lens=(21, 16, 5), Hq=4, Hkv=2, D=8, P=4, extra_pages=3):
+    nbs = [(L + P - 1) // P for L in lens]
+    used = sum(nbs)
+    npg = used + extra_pages
+    phys = rng.permutation(npg)[:used]
+    indptr = np.concatenate([[0], np.cumsum(nbs)])
+    batch = BatchView(indptr, phys, np.array(lens), P)
+    q = _rand_bf16(rng, (len(lens), Hq, D))
+    k = _rand_bf16(rng, (npg, Hkv, P, D))
+    v = _rand_bf16(rng, (npg, Hkv, P, D))
+    return batch, q, k, v
+
+
+def test_k_all_equals_dense_decimal_attention():
+    rng = np.random.default_rng(20)
+    batch, q, k, v = _paged_tiny(rng)
+    for r in range(batch.batch):
+        L = int(batch.seq_lens[r])
+        for g in range(2):
+            out, lse = dense_attention(q, k, v, batch, r, g, num_kv_heads=2, sm_scale=0.3,
+                                       out_dtype="fp64")
+            # contiguous view of the request's tokens, built independently
+            Kc = np.stack([bf16_to_f64(k[batch.page_indices[batch.page_indptr[r] + t // 4], g, t % 4])
+                           for t in range(L)])
+            Vc = np.stack([bf16_to_f64(v[batch.page_indices[batch.page_indptr[r] + t // 4], g, t % 4])
+                           for t in range(L)])
+            for i, h in enumerate((2 * g, 2 * g + 1)):
+                o2, l2 = _decimal_attention(bf16_to_f64(q[r, h]), Kc, Vc, 0.3)
+                np.testing.assert_allclose(out[i], o2, rtol=1e-12, atol=1e-13)
+                assert abs(lse[i] - l2) < 1e-12
+
+
+def test_page_permutation_invariance_and_poisoned_unused_pages():
+    rng = np.random.default_rng(21)
+    batch, q, k, v = _paged_tiny(rng)
+    res1 = decode_step(q, k, v, batch, num_kv_heads=2, topk=2, n_sink=1, n_recent=1,
+                       sm_scale=0.3, out_dtype="bf16")
+    # move every page to a new physical slot and poison the unused ones
+    npg = k.shape[0]
+    perm = rng.permutation(npg + 4)
+    k2 = np.full((npg + 4,) + k.shape[1:], 0x7FC0, dtype=np.uint16)
+    v2 = np.full_like(k2, 0x7FC0)
+    k2[perm[:npg]] = k
+    v2[perm[:npg]] = v
+    batch2 = BatchView(batch.page_indptr, perm[batch.page_indices], batch.seq_lens, 4)
+    res2 = decode_step(q, k2, v2, batch2, num_kv_heads=2, topk=2, n_sink=1, n_recent=1,
+                       sm_scale=0.3, out_dtype="bf16")
+    for key, a in res1["pairs"].items():
+        b = res2["pairs"][key]
+        assert a["selected"] == b["selected"]
+        assert np.array_equal(a["out"], b["out"])
+        assert np.array_equal(a["scores"], b["scores"])
+
+
+def test_decode_step_k_all_matches_dense():
+    rng = np.random.default_rng(22)
+    batch, q, k, v = _paged_tiny(rng)
+    res = decode_step(q, k, v, batch, num_kv_heads=2, topk=100, n_sink=1, n_recent=2,
+                      sm_scale=0.3, out_dtype="fp32")
+    for (r, g), item in res["pairs"].items():
+        assert item["selected"] == list(range(batch.num_blocks(r)))
+        out, lse = dense_attention(q, k, v, batch, r, g, num_kv_heads=2, sm_scale=0.3,
+                                   out_dtype="fp32")
+        assert np.array_equal(item["out"], out)
+
+
+def test_sparse_attention_is_lse_merge_of_its_blocks():
+    rng = np.random.default_rng(23)
+    batch, q, k, v = _paged_tiny(rng)
+    blocks = [0, 2, 5]
+    out, lse = sparse_attention(q, k, v, batch, 0, 1, blocks, num_kv_heads=2, sm_scale=0.3,
+                                out_dtype="fp64")
+    parts = [sparse_attention(q, k, v, batch, 0, 1, [b], num_kv_heads=2, sm_scale=0.3,
+                              out_dtype="fp64") for b in blocks]
+    for i in range(2):
+        o, l = lse_merge([(p[0][i], p[1][i]) for p in parts])
+        np.testing.assert_allclose(out[i], o, rtol=1e-13, atol=1e-14)
+        assert abs(lse[i] - l) < 1e-13
+    assert list(tokens_of_blocks([5], 4, 21)) == [20]
+
+
+def test_mla_attention_vs_decimal():
+    rng = np.random.default_rng(24)
+    lens = (10,)
+    batch = BatchView([0, 3], [2, 0, 1], np.array(lens), 4)
+    lat = _rand_bf16(rng, (3, 4, 6))          # Dk = 6, v_dim = 4
+    q = _rand_bf16(rng, (1, 3, 6))
+    toks = [0, 4, 5, 9]
+    out, lse = mla_attention(q, lat, batch, 0, toks, v_dim=4, sm_scale=0.5, out_dtype="fp64")
+    C = np.stack([bf16_to_f64(lat[batch.page_indices[t // 4], t % 4]) for t in toks])
+    for h in range(3):
+        o2, l2 = _decimal_attention(bf16_to_f64(q[0, h]), C, C[:, :4], 0.5)
+        np.testing.assert_allclose(out[h], o2, rtol=1e-12, atol=1e-13)
+        assert abs(lse[h] - l2) < 1e-12
