@@ -1,0 +1,250 @@
+/*
+ * ls.h -- C ABI of libls, a gfx950 (MI355X) library for the decode-step
+ * query-aware sparse-attention hot path:
+ *
+ *   1. ls_build_block_summaries: the mean key of every full page, per KV head
+ *      (Vortex post, "Writing an algorithm: vFlow": the block-top-k cache
+ *      step stores the mean of the keys over the in-block axis; summaries are
+ *      built once, when a block fills up -- "Why Long Generations Are
+ *      Expensive").
+ *   2. ls_score_select: score each block summary against the current query,
+ *      aggregate over the query heads of a GQA group, and keep the top-k
+ *      blocks plus forced sink / recent blocks (Vortex, block top-k equation
+ *      and Fig. 1; the vFlow listing's GeMM -> head reduction -> topK).
+ *   3. ls_sparse_attn_decode: exact softmax attention of every query head over
+ *      the tokens of the selected blocks of a paged KV cache, split over the
+ *      selected blocks and merged by log-sum-exp (Vortex block top-k
+ *      equation; the merge of attention over disjoint token sets by
+ *      log-sum-exp in "Where Activation Sparsity and KV-Cache Sparsity Cross
+ *      in LLM Decoding", App. A).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer is a DEVICE pointer (hipMalloc'ed or equivalent) unless the
+ *   comment says "host". The caller owns every buffer. The library allocates
+ *   no device memory, keeps no pointer after a call returns (beyond the work
+ *   it enqueued), never synchronises the stream and never reads device data
+ *   back to the host, so every call can be captured in a HIP graph.
+ * - Every call only ENQUEUES kernels on `stream` (0 = the null stream).
+ * - Host-side validation runs before any launch. On failure nothing is
+ *   enqueued, the call returns a non-zero ls_status, and ls_last_error()
+ *   returns a message (thread-local, valid until the next call on the same
+ *   thread). A launch error is reported as LS_ERR_HIP with the HIP message.
+ *   The library never aborts and never throws across this ABI.
+ * - Device-side contract (not checkable on the host without a readback):
+ *   page ids < pool.num_pages; page_indptr non-decreasing; every request r
+ *   has at least ceil(seq_lens[r] / page_size) pages; seq_lens[r] >= 0 and
+ *   ceil(seq_lens[r]/page_size) <= batch.max_blocks; selection entries are
+ *   ascending valid block indices. The kernels guard every such index before
+ *   using it as an address (no out-of-bounds access), but results for a
+ *   request that violates the contract are unspecified.
+ * - Paged pool layout ("HND"): element (page, head, slot, d) of a K or V pool
+ *   is at ((page * num_heads + head) * page_size + slot) * head_dim + d, so
+ *   one (page, head) tile is contiguous. Logical block j of request r (tokens
+ *   j*page_size ... j*page_size + page_size - 1) lives in physical page
+ *   page_indices[page_indptr[r] + j] (the paged layout of the Vortex post,
+ *   "Why New Ideas Are Hard to Deploy", Fig. 2). Block = page.
+ * - Summary pool layout: [num_pages][num_heads][head_dim], indexed by
+ *   PHYSICAL page id, so pages shared between requests share a summary
+ *   (Vortex, "Running it: vTensor": cache entries live in pages of the KV
+ *   allocator).
+ * - bf16 is IEEE binary32's upper half; fp8 is OCP e4m3fn.
+ */
+#ifndef LS_H_
+#define LS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LS_ABI_VERSION 1
+
+typedef enum ls_status {
+  LS_OK = 0,
+  LS_ERR_INVALID = 1,      /* bad argument: null pointer, negative size, mismatch */
+  LS_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype / shape combination) */
+  LS_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than the size query returns */
+  LS_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} ls_status;
+
+typedef enum ls_dtype {
+  LS_DTYPE_BF16 = 1,
+  LS_DTYPE_FP32 = 2,
+  LS_DTYPE_FP8_E4M3FN = 3
+} ls_dtype;
+
+/* GQA aggregation of the per-head block scores of one KV group. */
+enum { LS_AGG_MAX = 0, LS_AGG_MEAN = 1 };
+
+/* Geometry of a paged pool (K, V or summaries). */
+typedef struct ls_pool {
+  int32_t num_pages;   /* physical pages in the pool                     */
+  int32_t num_heads;   /* KV heads per page                              */
+  int32_t page_size;   /* tokens per page (= block size)                 */
+  int32_t head_dim;    /* elements per token per head                    */
+  int32_t dtype;       /* ls_dtype of the pool's elements                */
+} ls_pool;
+
+/* A ragged batch of requests over a paged pool (CSR page table, the
+ * "index-pointer array" + page list of the Vortex post's vTensor). */
+typedef struct ls_batch {
+  int32_t batch_size;            /* host: number of requests (0 is allowed)  */
+  int32_t max_blocks;            /* host: >= ceil(seq_lens[r]/page_size), all r */
+  const int32_t* page_indptr;    /* [batch_size + 1]                         */
+  const int32_t* page_indices;   /* [page_indptr[batch_size]] physical pages */
+  const int32_t* seq_lens;       /* [batch_size] cached tokens, current one included */
+} ls_batch;
+
+/* Selection parameters (passed by host pointer). */
+typedef struct ls_select_params {
+  int32_t struct_size;   /* = sizeof(ls_select_params)                        */
+  int32_t group_agg;     /* LS_AGG_MAX or LS_AGG_MEAN                         */
+  int32_t topk;          /* blocks chosen by score, forced ones not counted;  */
+                         /* -1 => per request from keep_ratio (below)         */
+  float keep_ratio;      /* used when topk == -1: a request with nb blocks    */
+                         /* keeps max(|F|, ceil(keep_ratio*nb)) blocks in all,*/
+                         /* forced blocks F included                          */
+  int32_t n_sink;        /* forced: blocks 0 .. n_sink-1                      */
+  int32_t n_recent;      /* forced: the last n_recent blocks                  */
+  int32_t max_selected;  /* row capacity of `selected` (see ls_score_select)  */
+} ls_select_params;
+
+/* ------------------------------------------------------------------------ */
+/* 1. Block summaries                                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * summaries[p][h][d] = round( (1/page_size) * sum_s keys[p][h][s][d] )
+ * for every physical page p listed in page_ids[0 .. n_pages-1] and every
+ * head h < key_pool.num_heads. The sum over the page's tokens is accumulated
+ * in float64 (exact whenever, within one column, the largest and smallest
+ * non-zero |key| are less than 2^41 apart), page_size is a power of two so the
+ * division is exact, and the mean is rounded ONCE, to nearest-even, to
+ * summary_dtype.
+ *
+ * keys:        key pool, layout HND (see above), dtype key_pool.dtype.
+ * key_scales:  NULL for bf16 keys. For LS_DTYPE_FP8_E4M3FN keys: per-token
+ *              dequantisation scale, fp32 [num_pages][page_size] (the summand
+ *              is key_scales[p][s] * keys[p][h][s][d]); key_pool.num_heads
+ *              must then be 1.
+ * key_pool:    page_size in {16, 32, 64}; head_dim in {64, 128}; dtype bf16 or fp8.
+ * page_ids:    [n_pages] physical page ids to (re)summarise (complete pages).
+ * n_pages:     >= 0; 0 enqueues nothing.
+ * summaries:   [key_pool.num_pages][key_pool.num_heads][head_dim] of
+ *              summary_dtype (LS_DTYPE_BF16 or LS_DTYPE_FP32); only the rows
+ *              of the listed pages are written.
+ */
+ls_status ls_build_block_summaries(const void* keys, const float* key_scales,
+                                   ls_pool key_pool, const int32_t* page_ids,
+                                   int32_t n_pages, void* summaries,
+                                   int32_t summary_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* 2. Scoring and selection                                                  */
+/* ------------------------------------------------------------------------ */
+/*
+ * For every request r and KV head g (G = num_q_heads / num_kv_heads query
+ * heads per group, query head h belongs to group h / G):
+ *   nb = ceil(L/P) blocks, nc = floor(L/P) complete blocks (L = seq_lens[r]),
+ *   forced F = {0 .. min(n_sink,nb)-1} U {max(0,nb-n_recent) .. nb-1}
+ *              U {nb-1 if the last block is partial},
+ *   candidates C = {j < nc} \ F,
+ *   score s_j = agg_{h in group g} sum_d q[r][h][d] * summaries[page(r,j)][g][d]
+ *              (fp32 accumulation of exact bf16 products; unscaled),
+ *   k_r = topk, or from keep_ratio when topk == -1,
+ *   top = the first min(k_r, |C|) candidates ordered by (s_j descending,
+ *         j ascending) -- ties go to the LOWEST block index,
+ *   selected[r][g][0 .. cnt-1] = F U top in ASCENDING order, cnt = |F U top|,
+ *   remaining entries up to max_selected set to -1, selected_count[r][g] = cnt.
+ * The result is deterministic (bitwise identical run to run).
+ *
+ * q:              [batch][num_q_heads][head_dim], q_dtype = LS_DTYPE_BF16.
+ * summaries:      summary pool [num_pages][num_kv_heads][head_dim]; its
+ *                 geometry is `pool` (pool.num_heads = num_kv_heads,
+ *                 pool.page_size = block size, pool.dtype = LS_DTYPE_BF16).
+ * batch:          page table of the requests (block = page).
+ * p:              host pointer; p->max_selected must be >= the largest
+ *                 possible cnt, i.e. >= min(max_blocks, k + n_sink + n_recent + 1)
+ *                 (k_max from keep_ratio when topk == -1).
+ * selected:       [batch][num_kv_heads][p->max_selected] int32 (output).
+ * selected_count: [batch][num_kv_heads] int32 (output).
+ * scores_out:     NULL, or [batch][num_kv_heads][max_blocks] fp32 receiving
+ *                 s_j for candidate blocks (other entries unspecified).
+ * workspace:      device scratch of at least ls_score_select_workspace_size()
+ *                 bytes, 256-byte aligned; contents need not be initialised.
+ * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
+ *            page_size 16; max_blocks <= 16384.
+ */
+size_t ls_score_select_workspace_size(int32_t batch_size, int32_t num_kv_heads,
+                                      int32_t max_blocks);
+
+ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                          const void* summaries, ls_pool pool, ls_batch batch,
+                          const ls_select_params* p, int32_t* selected,
+                          int32_t* selected_count, float* scores_out,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* 3. Sparse attention over the selected blocks                              */
+/* ------------------------------------------------------------------------ */
+/*
+ * For every request r and query head h (group g = h / G):
+ *   T = tokens t < L of the blocks selected[r][g][0 .. cnt-1],
+ *   z_t = sm_scale * sum_d q[r][h][d] * K[t][d],
+ *   out[r][h][:] = sum_t e^{z_t - M} V[t][:] / sum_t e^{z_t - M}, M = max z,
+ *   lse_out[r][h] = M + ln sum_t e^{z_t - M}
+ * with fp32 logits, softmax and accumulation; the work is split over the
+ * selected blocks and the partial results are merged by log-sum-exp in a
+ * fixed order (deterministic). An empty T gives out = 0 and lse = -inf.
+ * The output is rounded once (nearest-even) to out_dtype.
+ *
+ * q:              [batch][num_q_heads][head_dim] bf16.
+ * k_pool, v_pool: K and V pools, layout HND, geometry `pool` (bf16).
+ * selected:       [batch][num_kv_heads][max_selected] ascending block
+ *                 indices (as written by ls_score_select), with counts in
+ *                 selected_count[batch][num_kv_heads]. selected == NULL and
+ *                 selected_count == NULL select EVERY block of each request
+ *                 (the dense "k = all" path; max_selected is then ignored).
+ * sm_scale:       logit scale, e.g. 1/sqrt(head_dim).
+ * out:            [batch][num_q_heads][head_dim] of out_dtype (bf16 or fp32).
+ * lse_out:        NULL or [batch][num_q_heads] fp32.
+ * workspace:      >= ls_sparse_attn_decode_workspace_size() bytes, 256-byte
+ *                 aligned (split partial results); need not be initialised.
+ * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
+ *            page_size 16.
+ */
+size_t ls_sparse_attn_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
+                                            int32_t head_dim, int32_t max_selected,
+                                            int32_t max_blocks);
+
+ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                const void* k_pool, const void* v_pool, ls_pool pool,
+                                ls_batch batch, const int32_t* selected,
+                                const int32_t* selected_count, int32_t max_selected,
+                                float sm_scale, void* out, int32_t out_dtype,
+                                float* lse_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Introspection                                                             */
+/* ------------------------------------------------------------------------ */
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none). Host pointer owned by the library. */
+const char* ls_last_error(void);
+
+/* Library version and build string, e.g. "libls 0.1.0 abi 1 gfx950". */
+const char* ls_version(void);
+
+/* Number of split-K partitions ls_sparse_attn_decode uses for a given
+ * selection capacity (max_selected, or max_blocks on the dense path). */
+int32_t ls_attn_num_splits(int32_t max_selected);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LS_H_ */

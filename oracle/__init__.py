@@ -35,5 +35,5 @@ from .method import (  # noqa: F401
     BatchView, block_summaries, block_scores, select_blocks, select_blocks_batch,
     attention_over_tokens, sparse_attention, dense_attention, lse_merge,
     indexer_token_scores, select_tokens, mla_attention, decode_step,
-    tokens_of_blocks,
+    tokens_of_blocks, topk_from_keep_ratio, forced_blocks,
 )

@@ -210,6 +210,18 @@ def forced_blocks(nb: int, n_complete: int, n_sink: int, n_recent: int) -> List[
     return sorted(f)
 
 
+def topk_from_keep_ratio(nb: int, n_complete: int, keep_ratio: float, n_sink: int,
+                         n_recent: int) -> int:
+    """k for a keep-ratio budget: the request keeps max(|F|, ceil(ratio * nb))
+    blocks in all, forced blocks F included (the ByteCross paper counts its
+    sink tokens inside the kept fraction r_KV, §3.2 and §4.1). The product
+    ratio * nb is taken in fp32, the precision the kernels take it in, since
+    it decides an integer."""
+    nf = len(forced_blocks(nb, n_complete, n_sink, n_recent))
+    total = int(np.ceil(np.float32(keep_ratio) * np.float32(nb)))
+    return max(nf, total) - nf
+
+
 def rank_top(scores: np.ndarray, candidates: Iterable[int], k: int) -> List[int]:
     """First k candidates under the order (score descending, index ascending)."""
     order = sorted(candidates, key=lambda j: (-float(scores[j]), j))

@@ -1,0 +1,189 @@
+"""Decode-step query-aware sparse attention for MI355X (gfx950).
+
+Thin Python binding over libls.so (include/ls.h): argument marshalling only.
+Every step of the path runs in the library's HIP kernels; PyTorch only
+provides device memory and the current stream. Importing this package loads
+the in-tree libls.so and raises ImportError if it has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (LS_AGG_MAX, LS_AGG_MEAN, LS_DTYPE_BF16, LS_DTYPE_FP32,  # noqa: F401
+                   LS_DTYPE_FP8_E4M3FN, LsBatch, LsError, LsPool, LsSelectParams, check)
+
+_L = _lib.load()
+
+__all__ = ["PagedBatch", "build_block_summaries", "score_select", "sparse_attn_decode",
+           "score_select_workspace_size", "sparse_attn_decode_workspace_size",
+           "attn_num_splits", "version", "LsError"]
+
+_DT = {torch.bfloat16: LS_DTYPE_BF16, torch.float32: LS_DTYPE_FP32,
+       torch.float8_e4m3fn: LS_DTYPE_FP8_E4M3FN}
+
+
+def version() -> str:
+    return _L.ls_version().decode()
+
+
+@dataclass
+class PagedBatch:
+    """CSR page table of a ragged batch (device int32 tensors) plus the host
+    bound max_blocks >= ceil(seq_len / page_size) for every request."""
+    page_indptr: torch.Tensor
+    page_indices: torch.Tensor
+    seq_lens: torch.Tensor
+    max_blocks: int
+
+    @property
+    def batch_size(self) -> int:
+        return int(self.seq_lens.numel())
+
+    def c(self) -> LsBatch:
+        for t in (self.page_indptr, self.page_indices, self.seq_lens):
+            _need(t, torch.int32)
+        return LsBatch(self.batch_size, int(self.max_blocks), self.page_indptr.data_ptr(),
+                       self.page_indices.data_ptr(), self.seq_lens.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"expected {dtype}, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> C.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _pool(t: torch.Tensor, num_heads: int, page_size: int, head_dim: int) -> LsPool:
+    return LsPool(int(t.shape[0]), num_heads, page_size, head_dim, _DT[t.dtype])
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ summaries
+
+def build_block_summaries(keys: torch.Tensor, page_ids: torch.Tensor, summaries: torch.Tensor,
+                          key_scales: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Mean key of every listed full page, per head, rounded once.
+
+    keys: bf16 [pages][Hkv][P][D], or fp8-e4m3fn [pages][P][D] with
+    key_scales fp32 [pages][P]. summaries: [pages][Hkv][D] (or [pages][D])
+    bf16 or fp32; rows of the listed pages are overwritten."""
+    _need(keys); _need(page_ids, torch.int32); _need(summaries)
+    if keys.dim() == 4:
+        pool = _pool(keys, keys.shape[1], keys.shape[2], keys.shape[3])
+    else:
+        pool = _pool(keys, 1, keys.shape[1], keys.shape[2])
+    if key_scales is not None:
+        _need(key_scales, torch.float32)
+    check(_L.ls_build_block_summaries(keys.data_ptr(), _ptr(key_scales), pool,
+                                      page_ids.data_ptr(), int(page_ids.numel()),
+                                      summaries.data_ptr(), _DT[summaries.dtype],
+                                      _stream(stream)))
+    return summaries
+
+
+# ------------------------------------------------------------------ selection
+
+def score_select_workspace_size(batch_size: int, num_kv_heads: int, max_blocks: int) -> int:
+    return int(_L.ls_score_select_workspace_size(batch_size, num_kv_heads, max_blocks))
+
+
+def score_select(q: torch.Tensor, summaries: torch.Tensor, page_size: int, batch: PagedBatch, *,
+                 topk: int, n_sink: int, n_recent: int, max_selected: int,
+                 group_agg: str = "max", keep_ratio: float = 0.0,
+                 selected: Optional[torch.Tensor] = None,
+                 selected_count: Optional[torch.Tensor] = None,
+                 scores_out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k blocks per (request, kv head) by GQA-aggregated summary score,
+    plus forced sink/recent blocks, ascending. Returns (selected, counts)."""
+    _need(q, torch.bfloat16); _need(summaries, torch.bfloat16)
+    B, Hq, D = q.shape
+    Hkv = summaries.shape[1]
+    dev = q.device
+    if selected is None:
+        selected = torch.empty(B, Hkv, max_selected, dtype=torch.int32, device=dev)
+    if selected_count is None:
+        selected_count = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    _need(selected, torch.int32); _need(selected_count, torch.int32)
+    if scores_out is not None:
+        _need(scores_out, torch.float32)
+    ws_bytes = score_select_workspace_size(B, Hkv, batch.max_blocks)
+    ws = _workspace(ws_bytes, dev, workspace) if scores_out is None else workspace
+    params = LsSelectParams(C.sizeof(LsSelectParams),
+                            LS_AGG_MAX if group_agg == "max" else LS_AGG_MEAN,
+                            int(topk), float(keep_ratio), int(n_sink), int(n_recent),
+                            int(max_selected))
+    pool = LsPool(int(summaries.shape[0]), int(Hkv), int(page_size), int(D), LS_DTYPE_BF16)
+    check(_L.ls_score_select(q.data_ptr(), LS_DTYPE_BF16, int(Hq), summaries.data_ptr(), pool,
+                             batch.c(), C.byref(params), selected.data_ptr(),
+                             selected_count.data_ptr(), _ptr(scores_out), _ptr(ws),
+                             0 if ws is None else ws.numel() * ws.element_size(),
+                             _stream(stream)))
+    return selected, selected_count
+
+
+# ------------------------------------------------------------------ attention
+
+def attn_num_splits(max_selected: int) -> int:
+    return int(_L.ls_attn_num_splits(int(max_selected)))
+
+
+def sparse_attn_decode_workspace_size(batch_size: int, num_q_heads: int, head_dim: int,
+                                      max_selected: int, max_blocks: int) -> int:
+    return int(_L.ls_sparse_attn_decode_workspace_size(batch_size, num_q_heads, head_dim,
+                                                       max_selected, max_blocks))
+
+
+def sparse_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                       batch: PagedBatch, selected: Optional[torch.Tensor],
+                       selected_count: Optional[torch.Tensor], *, sm_scale: float,
+                       out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+                       lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Exact attention of every query head over the tokens of its group's
+    selected blocks (selected=None: every block, the dense k = all path)."""
+    _need(q, torch.bfloat16); _need(k_pool, torch.bfloat16); _need(v_pool, torch.bfloat16)
+    B, Hq, D = q.shape
+    _, Hkv, P, _ = k_pool.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=out_dtype, device=dev)
+    _need(out)
+    if lse is not None:
+        _need(lse, torch.float32)
+    max_sel = int(selected.shape[-1]) if selected is not None else 0
+    if selected is not None:
+        _need(selected, torch.int32); _need(selected_count, torch.int32)
+    ws_bytes = sparse_attn_decode_workspace_size(B, Hq, D, max_sel, batch.max_blocks)
+    ws = _workspace(ws_bytes, dev, workspace)
+    pool = _pool(k_pool, int(Hkv), int(P), int(D))
+    check(_L.ls_sparse_attn_decode(q.data_ptr(), LS_DTYPE_BF16, int(Hq), k_pool.data_ptr(),
+                                   v_pool.data_ptr(), pool, batch.c(), _ptr(selected),
+                                   _ptr(selected_count), max_sel, float(sm_scale),
+                                   out.data_ptr(), _DT[out.dtype], _ptr(lse), ws.data_ptr(),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
+    return out, lse

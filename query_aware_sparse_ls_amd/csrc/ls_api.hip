@@ -1,0 +1,275 @@
+// C ABI of libls: host-side validation, workspace sizing and kernel dispatch.
+// Every entry point validates its arguments before touching HIP, enqueues on
+// the caller's stream, never synchronises and never allocates device memory.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ls_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ls_status fail(ls_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ls_status ok() {
+  g_err[0] = '\0';
+  return LS_OK;
+}
+
+ls_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(LS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// The kernels read q, pools and summaries 16 bytes at a time.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+ls_status check_batch(const ls_batch& b) {
+  if (b.batch_size < 0) return fail(LS_ERR_INVALID, "batch.batch_size < 0");
+  if (b.batch_size == 0) return ok();
+  if (!b.page_indptr || !b.page_indices || !b.seq_lens)
+    return fail(LS_ERR_INVALID, "batch page_indptr / page_indices / seq_lens must be non-null");
+  if (b.max_blocks < 1) return fail(LS_ERR_INVALID, "batch.max_blocks must be >= 1");
+  return ok();
+}
+
+ls_status check_gqa_pool(const ls_pool& p, const char* which) {
+  if (p.num_pages < 1 || p.num_heads < 1)
+    return fail(LS_ERR_INVALID, "%s: num_pages and num_heads must be >= 1", which);
+  if (p.page_size != 16)
+    return fail(LS_ERR_UNSUPPORTED, "%s: page_size %d (supported: 16)", which, p.page_size);
+  if (p.head_dim != 64 && p.head_dim != 128)
+    return fail(LS_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", which, p.head_dim);
+  if (p.dtype != LS_DTYPE_BF16)
+    return fail(LS_ERR_UNSUPPORTED, "%s: dtype %d (supported: bf16)", which, p.dtype);
+  if (p.num_heads > 16 || !pow2(p.num_heads))
+    return fail(LS_ERR_UNSUPPORTED, "%s: num_heads %d (supported: 1, 2, 4, 8, 16)", which,
+                p.num_heads);
+  return ok();
+}
+
+ls::BatchArgs batch_args(const ls_batch& b, const ls_pool& p) {
+  ls::BatchArgs a;
+  a.batch = b.batch_size;
+  a.max_blocks = b.max_blocks;
+  a.indptr = b.page_indptr;
+  a.indices = b.page_indices;
+  a.seq_lens = b.seq_lens;
+  a.num_pages = p.num_pages;
+  a.page_size = p.page_size;
+  return a;
+}
+
+int max_total_selected(const ls_select_params& p, int max_blocks) {
+  long long forced = (long long)p.n_sink + p.n_recent + 1;
+  long long total;
+  if (p.topk >= 0) {
+    total = forced + p.topk;
+  } else {
+    long long byratio = (long long)std::ceil((double)p.keep_ratio * max_blocks) + 1;
+    total = byratio > forced ? byratio : forced;
+  }
+  return (int)(total < max_blocks ? total : max_blocks);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ls_last_error(void) { return g_err; }
+
+const char* ls_version(void) { return "libls 0.1.0 abi 1 gfx950"; }
+
+int32_t ls_attn_num_splits(int32_t max_selected) {
+  if (max_selected < 1) return 1;
+  return (max_selected + ls::kAttnBlocksPerSplit - 1) / ls::kAttnBlocksPerSplit;
+}
+
+ls_status ls_build_block_summaries(const void* keys, const float* key_scales, ls_pool key_pool,
+                                   const int32_t* page_ids, int32_t n_pages, void* summaries,
+                                   int32_t summary_dtype, hipStream_t stream) {
+  if (n_pages < 0) return fail(LS_ERR_INVALID, "n_pages < 0");
+  if (key_pool.num_pages < 1 || key_pool.num_heads < 1)
+    return fail(LS_ERR_INVALID, "key_pool: num_pages and num_heads must be >= 1");
+  if (!pow2(key_pool.page_size) || key_pool.page_size < 16 || key_pool.page_size > 64)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.page_size %d (supported: 16, 32, 64)",
+                key_pool.page_size);
+  if (key_pool.head_dim != 64 && key_pool.head_dim != 128)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.head_dim %d (supported: 64, 128)", key_pool.head_dim);
+  if (summary_dtype != LS_DTYPE_BF16 && summary_dtype != LS_DTYPE_FP32)
+    return fail(LS_ERR_UNSUPPORTED, "summary_dtype %d (supported: bf16, fp32)", summary_dtype);
+  if (key_pool.dtype == LS_DTYPE_BF16) {
+    if (key_scales) return fail(LS_ERR_INVALID, "key_scales must be NULL for bf16 keys");
+  } else if (key_pool.dtype == LS_DTYPE_FP8_E4M3FN) {
+    if (!key_scales) return fail(LS_ERR_INVALID, "fp8 keys need key_scales");
+    if (key_pool.num_heads != 1)
+      return fail(LS_ERR_UNSUPPORTED, "fp8 key pools must have num_heads == 1");
+  } else {
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.dtype %d (supported: bf16, fp8_e4m3fn)",
+                key_pool.dtype);
+  }
+  if (n_pages == 0) return ok();
+  if (!keys || !page_ids || !summaries)
+    return fail(LS_ERR_INVALID, "keys, page_ids and summaries must be non-null");
+  ls::SummaryArgs a{keys, key_scales, key_pool, page_ids, n_pages, summaries, summary_dtype};
+  return hip_status(ls::launch_summaries(a, stream), "ls_build_block_summaries launch");
+}
+
+size_t ls_score_select_workspace_size(int32_t batch_size, int32_t num_kv_heads,
+                                      int32_t max_blocks) {
+  if (batch_size <= 0 || num_kv_heads <= 0 || max_blocks <= 0) return 0;
+  return align_up((size_t)batch_size * num_kv_heads * max_blocks * sizeof(float));
+}
+
+ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                          const void* summaries, ls_pool pool, ls_batch batch,
+                          const ls_select_params* p, int32_t* selected, int32_t* selected_count,
+                          float* scores_out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (!p) return fail(LS_ERR_INVALID, "params must be non-null");
+  if (p->struct_size != (int32_t)sizeof(ls_select_params))
+    return fail(LS_ERR_INVALID, "params.struct_size %d != %d", p->struct_size,
+                (int)sizeof(ls_select_params));
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  if ((st = check_gqa_pool(pool, "summary pool")) != LS_OK) return st;
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
+    return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                pool.num_heads);
+  if (num_q_heads / pool.num_heads != 4)
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
+                num_q_heads / pool.num_heads);
+  if (p->group_agg != LS_AGG_MAX && p->group_agg != LS_AGG_MEAN)
+    return fail(LS_ERR_INVALID, "group_agg %d", p->group_agg);
+  if (p->n_sink < 0 || p->n_recent < 0) return fail(LS_ERR_INVALID, "n_sink/n_recent < 0");
+  if (p->topk < -1) return fail(LS_ERR_INVALID, "topk %d (>= 0, or -1 for keep_ratio)", p->topk);
+  if (p->topk == -1 && !(p->keep_ratio >= 0.0f && p->keep_ratio <= 1.0f))
+    return fail(LS_ERR_INVALID, "keep_ratio must be in [0, 1]");
+  if (batch.batch_size > 0 && batch.max_blocks > 16384)
+    return fail(LS_ERR_UNSUPPORTED, "max_blocks %d (supported: <= 16384)", batch.max_blocks);
+  if (batch.batch_size == 0) return ok();
+  const int need = max_total_selected(*p, batch.max_blocks);
+  if (p->max_selected < need)
+    return fail(LS_ERR_INVALID, "max_selected %d < %d (largest possible selection)",
+                p->max_selected, need);
+  if (!q || !summaries || !selected || !selected_count)
+    return fail(LS_ERR_INVALID, "q, summaries, selected and selected_count must be non-null");
+  if (!aligned16(q) || !aligned16(summaries))
+    return fail(LS_ERR_INVALID, "q and summaries must be 16-byte aligned");
+  const size_t ws = ls_score_select_workspace_size(batch.batch_size, pool.num_heads,
+                                                   batch.max_blocks);
+  float* scores = scores_out;
+  if (!scores) {
+    if (!workspace || workspace_bytes < ws)
+      return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+    if ((uintptr_t)workspace % kAlign)
+      return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+    scores = static_cast<float*>(workspace);
+  }
+  ls::ScoreArgs sa;
+  sa.q = static_cast<const uint16_t*>(q);
+  sa.summaries = static_cast<const uint16_t*>(summaries);
+  sa.b = batch_args(batch, pool);
+  sa.num_q_heads = num_q_heads;
+  sa.num_kv_heads = pool.num_heads;
+  sa.head_dim = pool.head_dim;
+  sa.group_agg = p->group_agg;
+  sa.n_sink = p->n_sink;
+  sa.n_recent = p->n_recent;
+  sa.scores = scores;
+  hipError_t e = ls::launch_score(sa, stream);
+  if (e != hipSuccess) return hip_status(e, "score kernel launch");
+  ls::TopkArgs ta;
+  ta.scores = scores;
+  ta.b = sa.b;
+  ta.num_kv_heads = pool.num_heads;
+  ta.topk = p->topk;
+  ta.keep_ratio = p->keep_ratio;
+  ta.n_sink = p->n_sink;
+  ta.n_recent = p->n_recent;
+  ta.max_selected = p->max_selected;
+  ta.selected = selected;
+  ta.selected_count = selected_count;
+  return hip_status(ls::launch_topk(ta, stream), "top-k kernel launch");
+}
+
+size_t ls_sparse_attn_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
+                                            int32_t head_dim, int32_t max_selected,
+                                            int32_t max_blocks) {
+  if (batch_size <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const int cap = max_selected > 0 ? max_selected : max_blocks;
+  const size_t S = (size_t)ls_attn_num_splits(cap);
+  return align_up((size_t)batch_size * num_q_heads * S * (head_dim + 2) * sizeof(float));
+}
+
+ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                const void* k_pool, const void* v_pool, ls_pool pool,
+                                ls_batch batch, const int32_t* selected,
+                                const int32_t* selected_count, int32_t max_selected,
+                                float sm_scale, void* out, int32_t out_dtype, float* lse_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  if ((st = check_gqa_pool(pool, "kv pool")) != LS_OK) return st;
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (out_dtype != LS_DTYPE_BF16 && out_dtype != LS_DTYPE_FP32)
+    return fail(LS_ERR_UNSUPPORTED, "out_dtype %d (supported: bf16, fp32)", out_dtype);
+  if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
+    return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                pool.num_heads);
+  if (num_q_heads / pool.num_heads != 4)
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
+                num_q_heads / pool.num_heads);
+  if ((selected == nullptr) != (selected_count == nullptr))
+    return fail(LS_ERR_INVALID, "selected and selected_count must both be set or both NULL");
+  if (selected && max_selected < 1) return fail(LS_ERR_INVALID, "max_selected must be >= 1");
+  if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
+  if (batch.batch_size == 0) return ok();
+  if (!q || !k_pool || !v_pool || !out)
+    return fail(LS_ERR_INVALID, "q, k_pool, v_pool and out must be non-null");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(LS_ERR_INVALID, "q, k_pool and v_pool must be 16-byte aligned");
+  const int cap = selected ? max_selected : batch.max_blocks;
+  const size_t ws = ls_sparse_attn_decode_workspace_size(batch.batch_size, num_q_heads,
+                                                         pool.head_dim, selected ? max_selected : 0,
+                                                         batch.max_blocks);
+  if (!workspace || workspace_bytes < ws)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  ls::AttnArgs aa;
+  aa.q = static_cast<const uint16_t*>(q);
+  aa.k_pool = static_cast<const uint16_t*>(k_pool);
+  aa.v_pool = static_cast<const uint16_t*>(v_pool);
+  aa.b = batch_args(batch, pool);
+  aa.num_q_heads = num_q_heads;
+  aa.num_kv_heads = pool.num_heads;
+  aa.head_dim = pool.head_dim;
+  aa.selected = selected;
+  aa.selected_count = selected_count;
+  aa.max_selected = max_selected;
+  aa.num_splits = ls_attn_num_splits(cap);
+  aa.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  aa.partials = static_cast<float*>(workspace);
+  aa.out = out;
+  aa.out_dtype = out_dtype;
+  aa.lse = lse_out;
+  return hip_status(ls::launch_attn(aa, stream), "attention kernel launch");
+}
+
+}  // extern "C"

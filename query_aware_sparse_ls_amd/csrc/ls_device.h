@@ -1,0 +1,114 @@
+// Device helpers shared by the libls kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ls {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16 ----
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN -> quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp64 -> bf16 with ONE round-to-nearest-even step. First round to fp32 by
+// round-to-odd (truncate, then force the last bit to 1 if anything was cut
+// off), then RNE to bf16: rounding to odd at >= p+2 bits and then to nearest
+// at p bits equals a single rounding to nearest at p bits (Boldo & Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd", IEEE TC 2008). fp32 keeps 24 >= 8+2 bits, also in the
+// subnormal range, where fp32's quantum is 2^16 times finer than bf16's.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  float f = (float)x;                             // nearest-even
+  if (!(fabs(x) <= 3.4028234663852886e38)) {      // inf / NaN / beyond FLT_MAX
+    if (x != x) return 0x7fc0u;
+    // |x| > FLT_MAX: truncation gives FLT_MAX, round-to-odd keeps it odd.
+    uint32_t u = 0x7f7fffffu | (x < 0 ? 0x80000000u : 0u);
+    if (__builtin_isinf(x)) u = x < 0 ? 0xff800000u : 0x7f800000u;
+    return f32_to_bf16_rne(__uint_as_float(u));
+  }
+  double back = (double)f;
+  uint32_t u = __float_as_uint(f);
+  if (back != x) {
+    // truncate toward zero: if rounding went away from zero, step back one ulp
+    if (fabs(back) > fabs(x)) u -= 1u;             // magnitude bits decrement
+    u |= 1u;                                        // sticky -> odd
+  }
+  return f32_to_bf16_rne(__uint_as_float(u));
+}
+
+// OCP fp8 e4m3fn -> fp32, exact (1 sign, 4 exponent bits bias 7, 3 mantissa
+// bits, exponent field 0 subnormal, S.1111.111 NaN, no infinity).
+__device__ __forceinline__ float fp8e4m3fn_to_f32(uint32_t b) {
+  uint32_t e = (b >> 3) & 0xfu, m = b & 7u;
+  float mag;
+  if (e == 0) {
+    mag = (float)m * 0.001953125f;                         // m * 2^-9
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20)); // (1 + m/8) 2^(e-7)
+  }
+  if (e == 15 && m == 7) mag = __uint_as_float(0x7fc00000u);
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------- reductions ----
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Order-preserving map of a (finite) float to uint32; -0.0 is mapped like +0.0
+// so that equal scores compare equal.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 16-byte global load through the vector memory path.
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+}  // namespace ls

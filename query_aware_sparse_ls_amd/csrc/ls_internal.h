@@ -1,0 +1,113 @@
+// Internal launch interface between the C ABI layer (ls_api.hip) and the
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include "../../include/ls.h"
+#include "ls_device.h"
+
+namespace ls {
+
+struct SummaryArgs {
+  const void* keys;
+  const float* key_scales;
+  ls_pool pool;
+  const int32_t* page_ids;
+  int32_t n_pages;
+  void* out;
+  int32_t out_dtype;
+};
+
+// Per-request geometry shared by scoring, selection and attention.
+struct BatchArgs {
+  int32_t batch;
+  int32_t max_blocks;
+  const int32_t* indptr;
+  const int32_t* indices;
+  const int32_t* seq_lens;
+  int32_t num_pages;
+  int32_t page_size;
+};
+
+struct ScoreArgs {
+  const uint16_t* q;          // [B][Hq][D] bf16
+  const uint16_t* summaries;  // [num_pages][Hkv][D] bf16
+  BatchArgs b;
+  int32_t num_q_heads, num_kv_heads, head_dim;
+  int32_t group_agg;
+  int32_t n_sink, n_recent;
+  float* scores;              // [B][Hkv][max_blocks]
+};
+
+struct TopkArgs {
+  const float* scores;        // [B][Hkv][max_blocks]
+  BatchArgs b;
+  int32_t num_kv_heads;
+  int32_t topk;
+  float keep_ratio;
+  int32_t n_sink, n_recent;
+  int32_t max_selected;
+  int32_t* selected;          // [B][Hkv][max_selected]
+  int32_t* selected_count;    // [B][Hkv]
+};
+
+struct AttnArgs {
+  const uint16_t* q;          // [B][Hq][D]
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  BatchArgs b;
+  int32_t num_q_heads, num_kv_heads, head_dim;
+  const int32_t* selected;    // nullptr => dense (every block)
+  const int32_t* selected_count;
+  int32_t max_selected;       // row stride of `selected`
+  int32_t num_splits;
+  float sm_scale_log2;        // sm_scale * log2(e)
+  float* partials;            // [B][Hq][S][D+2]
+  void* out;
+  int32_t out_dtype;
+  float* lse;
+};
+
+hipError_t launch_summaries(const SummaryArgs& a, hipStream_t st);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+// Blocks per attention split (one register-resident chunk per workgroup).
+constexpr int kAttnBlocksPerSplit = 8;
+
+// Request geometry on the device: blocks, complete blocks, and the candidate
+// range [c0, c1) = complete blocks that are neither sink nor recent. The
+// block count is clamped to the pages the request owns and to max_blocks, so
+// a request that breaks the page-table contract cannot make a kernel read
+// outside its page list.
+struct ReqGeom {
+  int L, nb, nc, c0, c1, page_base;
+};
+
+__device__ __forceinline__ ReqGeom req_geom(const BatchArgs& b, int r, int n_sink, int n_recent) {
+  ReqGeom g;
+  int L = b.seq_lens[r];
+  L = L < 0 ? 0 : L;
+  const int p0 = b.indptr[r], p1 = b.indptr[r + 1];
+  int npg = p1 - p0;
+  npg = npg < 0 ? 0 : npg;
+  int nb = (L + b.page_size - 1) / b.page_size;
+  const int cap = npg < b.max_blocks ? npg : b.max_blocks;
+  if (nb > cap) {
+    nb = cap;
+    L = nb * b.page_size;
+  }
+  g.L = L;
+  g.nb = nb;
+  g.nc = L / b.page_size;
+  const int s = n_sink < nb ? n_sink : nb;
+  int rec = nb - n_recent;
+  rec = rec < 0 ? 0 : rec;
+  g.c0 = s;
+  g.c1 = g.nc < rec ? g.nc : rec;
+  if (g.c1 < g.c0) g.c1 = g.c0;
+  g.page_base = p0;
+  return g;
+}
+
+}  // namespace ls

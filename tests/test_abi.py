@@ -1,0 +1,140 @@
+"""The C ABI: the library loads, exports every function include/ls.h declares,
+and rejects invalid arguments on the host before any HIP call (these tests
+never launch a kernel, so they run without a GPU)."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from query_aware_sparse_ls_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ls.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ls_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.load()
+    names = _declared()
+    assert {"ls_build_block_summaries", "ls_score_select", "ls_sparse_attn_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                        text=True).stdout
+    exported = set(re.findall(r" T (ls_\w+)", nm))
+    assert set(names) <= exported
+    # and the binding declares a signature for each
+    assert set(names) == set(_lib._SIGS)
+
+
+def test_version_and_empty_error():
+    lib = _lib.load()
+    assert b"gfx950" in lib.ls_version()
+    assert b"abi 1" in lib.ls_version()
+
+
+def _pool(**kw):
+    d = dict(num_pages=8, num_heads=8, page_size=16, head_dim=128, dtype=_lib.LS_DTYPE_BF16)
+    d.update(kw)
+    return _lib.LsPool(**d)
+
+
+def _batch(**kw):
+    d = dict(batch_size=2, max_blocks=4, page_indptr=16, page_indices=32, seq_lens=48)
+    d.update(kw)
+    return _lib.LsBatch(**d)
+
+
+def _params(**kw):
+    d = dict(struct_size=C.sizeof(_lib.LsSelectParams), group_agg=0, topk=2, keep_ratio=0.0,
+             n_sink=1, n_recent=1, max_selected=4)
+    d.update(kw)
+    return _lib.LsSelectParams(**d)
+
+
+FAKE = 4096  # never dereferenced: every call below fails validation first
+
+
+def _score(lib, p=None, pool=None, batch=None, **kw):
+    args = dict(q=FAKE, q_dtype=_lib.LS_DTYPE_BF16, num_q_heads=32, summaries=FAKE,
+                pool=pool or _pool(), batch=batch or _batch(), sel=FAKE, cnt=FAKE,
+                scores=None, ws=None, ws_bytes=0)
+    args.update(kw)
+    pp = C.byref(p) if p is not None else None
+    return lib.ls_score_select(args["q"], args["q_dtype"], args["num_q_heads"], args["summaries"],
+                               args["pool"], args["batch"], pp, args["sel"], args["cnt"],
+                               args["scores"], args["ws"], args["ws_bytes"], None)
+
+
+def test_score_select_validation():
+    lib = _lib.load()
+    assert _score(lib, p=None) == _lib.LS_ERR_INVALID
+    assert b"params" in lib.ls_last_error()
+    assert _score(lib, p=_params(struct_size=4)) == _lib.LS_ERR_INVALID
+    assert _score(lib, p=_params(), pool=_pool(head_dim=96)) == _lib.LS_ERR_UNSUPPORTED
+    assert _score(lib, p=_params(), pool=_pool(page_size=8)) == _lib.LS_ERR_UNSUPPORTED
+    assert _score(lib, p=_params(), num_q_heads=30) == _lib.LS_ERR_INVALID
+    assert _score(lib, p=_params(), num_q_heads=16) == _lib.LS_ERR_UNSUPPORTED  # group 2
+    assert _score(lib, p=_params(), q_dtype=_lib.LS_DTYPE_FP32) == _lib.LS_ERR_UNSUPPORTED
+    assert _score(lib, p=_params(group_agg=7)) == _lib.LS_ERR_INVALID
+    assert _score(lib, p=_params(topk=-3)) == _lib.LS_ERR_INVALID
+    assert _score(lib, p=_params(topk=-1, keep_ratio=1.5)) == _lib.LS_ERR_INVALID
+    assert _score(lib, p=_params(max_selected=2)) == _lib.LS_ERR_INVALID
+    assert b"max_selected" in lib.ls_last_error()
+    assert _score(lib, p=_params(), batch=_batch(page_indptr=None)) == _lib.LS_ERR_INVALID
+    assert _score(lib, p=_params(), batch=_batch(max_blocks=20000)) == _lib.LS_ERR_UNSUPPORTED
+    assert _score(lib, p=_params(), sel=None) == _lib.LS_ERR_INVALID
+    # workspace too small (no scores_out given)
+    assert _score(lib, p=_params(), ws=FAKE, ws_bytes=16) == _lib.LS_ERR_WORKSPACE
+    # empty batch: valid, nothing enqueued
+    assert _score(lib, p=_params(), batch=_batch(batch_size=0)) == _lib.LS_OK
+    assert lib.ls_last_error() == b""
+
+
+def test_attention_validation():
+    lib = _lib.load()
+
+    def call(**kw):
+        a = dict(q=FAKE, q_dtype=_lib.LS_DTYPE_BF16, hq=32, k=FAKE, v=FAKE, pool=_pool(),
+                 batch=_batch(), sel=FAKE, cnt=FAKE, max_sel=8, scale=0.1, out=FAKE,
+                 out_dtype=_lib.LS_DTYPE_BF16, lse=None, ws=FAKE, ws_bytes=0)
+        a.update(kw)
+        return lib.ls_sparse_attn_decode(a["q"], a["q_dtype"], a["hq"], a["k"], a["v"], a["pool"],
+                                         a["batch"], a["sel"], a["cnt"], a["max_sel"], a["scale"],
+                                         a["out"], a["out_dtype"], a["lse"], a["ws"],
+                                         a["ws_bytes"], None)
+
+    assert call() == _lib.LS_ERR_WORKSPACE
+    assert call(sel=None) == _lib.LS_ERR_INVALID                 # one of the pair missing
+    assert call(out_dtype=_lib.LS_DTYPE_FP8_E4M3FN) == _lib.LS_ERR_UNSUPPORTED
+    assert call(scale=float("inf")) == _lib.LS_ERR_INVALID
+    assert call(pool=_pool(dtype=_lib.LS_DTYPE_FP32)) == _lib.LS_ERR_UNSUPPORTED
+    assert call(k=None) == _lib.LS_ERR_INVALID
+    assert call(ws=FAKE + 1, ws_bytes=1 << 30) == _lib.LS_ERR_INVALID   # misaligned workspace
+    assert call(q=FAKE + 2, ws=FAKE, ws_bytes=1 << 30) == _lib.LS_ERR_INVALID  # misaligned q
+    assert call(batch=_batch(batch_size=0)) == _lib.LS_OK
+    need = lib.ls_sparse_attn_decode_workspace_size(2, 32, 128, 8, 4)
+    assert need >= 2 * 32 * lib.ls_attn_num_splits(8) * 130 * 4
+    assert lib.ls_attn_num_splits(67) == 9 and lib.ls_attn_num_splits(2048) == 256
+
+
+def test_summaries_validation():
+    lib = _lib.load()
+    f = lib.ls_build_block_summaries
+    assert f(FAKE, None, _pool(), FAKE, -1, FAKE, _lib.LS_DTYPE_BF16, None) == _lib.LS_ERR_INVALID
+    assert f(FAKE, None, _pool(), FAKE, 0, FAKE, _lib.LS_DTYPE_BF16, None) == _lib.LS_OK
+    assert f(FAKE, None, _pool(page_size=12), FAKE, 1, FAKE, 1, None) == _lib.LS_ERR_UNSUPPORTED
+    assert f(FAKE, None, _pool(dtype=_lib.LS_DTYPE_FP8_E4M3FN, num_heads=1), FAKE, 1, FAKE, 1,
+             None) == _lib.LS_ERR_INVALID                      # fp8 needs scales
+    assert f(FAKE, FAKE, _pool(), FAKE, 1, FAKE, 1, None) == _lib.LS_ERR_INVALID  # bf16 + scales
+    assert f(FAKE, None, _pool(), FAKE, 1, FAKE, _lib.LS_DTYPE_FP8_E4M3FN,
+             None) == _lib.LS_ERR_UNSUPPORTED
+    assert f(None, None, _pool(), FAKE, 1, FAKE, 1, None) == _lib.LS_ERR_INVALID

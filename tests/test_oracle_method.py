@@ -396,3 +396,17 @@ def test_mla_attention_vs_decimal():
         o2, l2 = _decimal_attention(bf16_to_f64(q[0, h]), C, C[:, :4], 0.5)
         np.testing.assert_allclose(out[h], o2, rtol=1e-12, atol=1e-13)
         assert abs(lse[h] - l2) < 1e-12
+
+
+def test_keep_ratio_budget_closed_forms():
+    from oracle.method import topk_from_keep_ratio
+    # ratio 1 keeps every block: k = every candidate
+    assert topk_from_keep_ratio(100, 100, 1.0, 1, 2) == 97
+    assert topk_from_keep_ratio(100, 99, 1.0, 1, 2) == 97      # partial last is recent
+    # 1/16 of 2048 blocks = 128 kept in all, 3 of them forced
+    assert topk_from_keep_ratio(2048, 2048, 1 / 16, 1, 2) == 125
+    # a budget below the forced count keeps only the forced blocks
+    assert topk_from_keep_ratio(10, 10, 1 / 64, 1, 2) == 0
+    # ceil: 1/64 of 130 = 2.03 -> 3 kept in all, 3 forced -> k = 0; of 200 -> 4 -> k = 1
+    assert topk_from_keep_ratio(130, 130, 1 / 64, 1, 2) == 0
+    assert topk_from_keep_ratio(200, 200, 1 / 64, 1, 2) == 1
