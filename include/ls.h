@@ -230,6 +230,43 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* 4. The whole step in one launch                                           */
+/* ------------------------------------------------------------------------ */
+/*
+ * ls_score_select followed by ls_sparse_attn_decode (same definitions, same
+ * results bit for bit up to the order of split merges, which is fixed), run
+ * as ONE persistent kernel so that the selection and attention of one request
+ * overlap the scoring of the others (the Vortex post fuses operators of a
+ * step and balances workgroups across requests, "Making it fast").
+ *
+ * Arguments: as ls_score_select (q, summaries, batch, p, selected,
+ * selected_count) and ls_sparse_attn_decode (k_pool, v_pool with geometry
+ * `pool`, sm_scale, out, out_dtype, lse_out); the summary pool shares the
+ * K/V pool's num_pages, num_heads and head_dim.
+ * workspace: >= ls_sparse_decode_step_workspace_size() bytes, 256-byte
+ *   aligned. Its first ls_sparse_decode_step_control_bytes() bytes are a
+ *   control block that MUST be zero before the first call; every call that
+ *   runs to completion leaves it zero again, so a workspace zeroed once can be
+ *   reused by later calls on the same stream (concurrent calls need separate
+ *   workspaces). The rest need not be initialised.
+ * Supported: head_dim 64 or 128; num_kv_heads 2, 4 or 8; GQA group 4;
+ *   page_size 16; max_blocks <= 4096 (otherwise LS_ERR_UNSUPPORTED: use the
+ *   two separate calls).
+ */
+size_t ls_sparse_decode_step_control_bytes(int32_t batch_size, int32_t num_kv_heads);
+
+size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t max_blocks, int32_t max_selected);
+
+ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                const void* summaries, const void* k_pool, const void* v_pool,
+                                ls_pool pool, ls_batch batch, const ls_select_params* p,
+                                int32_t* selected, int32_t* selected_count, float sm_scale,
+                                void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Introspection                                                             */
 /* ------------------------------------------------------------------------ */
 /* Message for the last non-OK status returned on the calling thread ("" if

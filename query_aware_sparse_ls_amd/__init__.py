@@ -22,7 +22,8 @@ _L = _lib.load()
 
 __all__ = ["PagedBatch", "build_block_summaries", "score_select", "sparse_attn_decode",
            "score_select_workspace_size", "sparse_attn_decode_workspace_size",
-           "attn_num_splits", "version", "LsError"]
+           "attn_num_splits", "version", "LsError", "sparse_decode_step",
+           "sparse_decode_step_workspace"]
 
 _DT = {torch.bfloat16: LS_DTYPE_BF16, torch.float32: LS_DTYPE_FP32,
        torch.float8_e4m3fn: LS_DTYPE_FP8_E4M3FN}
@@ -187,3 +188,57 @@ def sparse_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
                                    out.data_ptr(), _DT[out.dtype], _ptr(lse), ws.data_ptr(),
                                    ws.numel() * ws.element_size(), _stream(stream)))
     return out, lse
+
+
+# ------------------------------------------------------------------ fused step
+
+def sparse_decode_step_workspace(batch_size: int, num_q_heads: int, num_kv_heads: int,
+                                 head_dim: int, max_blocks: int, max_selected: int,
+                                 device) -> torch.Tensor:
+    """A workspace for sparse_decode_step, zero-filled (its control block must
+    start at zero; each completed call leaves it zero for the next)."""
+    n = int(_L.ls_sparse_decode_step_workspace_size(batch_size, num_q_heads, num_kv_heads,
+                                                   head_dim, max_blocks, max_selected))
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.Tensor,
+                       v_pool: torch.Tensor, batch: PagedBatch, *, topk: int, n_sink: int,
+                       n_recent: int, max_selected: int, sm_scale: float,
+                       group_agg: str = "max", keep_ratio: float = 0.0,
+                       selected: Optional[torch.Tensor] = None,
+                       selected_count: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+                       lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """score_select + sparse_attn_decode in one persistent launch.
+    Returns (out, lse, selected, selected_count)."""
+    _need(q, torch.bfloat16); _need(summaries, torch.bfloat16)
+    _need(k_pool, torch.bfloat16); _need(v_pool, torch.bfloat16)
+    B, Hq, D = q.shape
+    _, Hkv, P, _ = k_pool.shape
+    dev = q.device
+    if selected is None:
+        selected = torch.empty(B, Hkv, max_selected, dtype=torch.int32, device=dev)
+    if selected_count is None:
+        selected_count = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = sparse_decode_step_workspace(B, Hq, int(Hkv), D, batch.max_blocks,
+                                                 max_selected, dev)
+    _need(selected, torch.int32); _need(selected_count, torch.int32); _need(out)
+    if lse is not None:
+        _need(lse, torch.float32)
+    params = LsSelectParams(C.sizeof(LsSelectParams),
+                            LS_AGG_MAX if group_agg == "max" else LS_AGG_MEAN,
+                            int(topk), float(keep_ratio), int(n_sink), int(n_recent),
+                            int(max_selected))
+    pool = _pool(k_pool, int(Hkv), int(P), int(D))
+    check(_L.ls_sparse_decode_step(q.data_ptr(), LS_DTYPE_BF16, int(Hq), summaries.data_ptr(),
+                                   k_pool.data_ptr(), v_pool.data_ptr(), pool, batch.c(),
+                                   C.byref(params), selected.data_ptr(), selected_count.data_ptr(),
+                                   float(sm_scale), out.data_ptr(), _DT[out.dtype], _ptr(lse),
+                                   workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse, selected, selected_count

@@ -1,6 +1,8 @@
 """Build libls.so for gfx950 with hipcc (in-tree: the .so lands next to this file).
 
-    python -m query_aware_sparse_ls_amd.build [-j N] [-v]
+    python query_aware_sparse_ls_amd/build.py [-j N] [-v]
+
+(run it as a script: importing the package would load the library first)
 
 Every .hip file under csrc/ is compiled to an object in _build/ (at the
 repository root, git-ignored) and linked into query_aware_sparse_ls_amd/libls.so.

@@ -21,12 +21,11 @@
 // One workgroup of 256 threads per (request, KV head); thread t holds the
 // scores of candidates [t*PER, t*PER + PER) in registers, so index order is
 // thread order, then register order.
-#include "ls_internal.h"
+#include "dev_topk.h"
 
 namespace ls {
 
 constexpr int kTopkThreads = 256;
-constexpr int kTopkMaxIters = 24;
 
 struct TopkShared {
   int hist[256];
@@ -99,17 +98,14 @@ __device__ __forceinline__ uint64_t lowest_index_fill(TopkShared& sh, uint64_t p
 }
 
 template <int PER>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kTopkThreads) void topk_wg_kernel(TopkArgs a) {
   __shared__ TopkShared sh;
   const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const ReqGeom geo = req_geom(a.b, r, a.n_sink, a.n_recent);
   const int ncand = geo.c1 - geo.c0;
   const int nforced = geo.nb - ncand;
-  int k = a.topk;
-  if (k < 0) {
-    const int total = (int)ceilf(a.keep_ratio * (float)geo.nb);
-    k = (total > nforced ? total : nforced) - nforced;
-  }
+  (void)nforced;
+  const int k = topk_budget(a, geo);
   int need = k < ncand ? k : ncand;
 
   const float* srow = a.scores + ((size_t)r * a.num_kv_heads + g) * a.b.max_blocks + geo.c0;
@@ -309,22 +305,42 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     a.selected_count[(size_t)r * a.num_kv_heads + g] = total < a.max_selected ? total : a.max_selected;
 }
 
+// One wave per (request, kv head), four per workgroup.
+template <int MAXC>
+__global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
+  __shared__ WaveTopkLds<MAXC> sh[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= a.b.batch * a.num_kv_heads) return;
+  const int r = item / a.num_kv_heads, g = item % a.num_kv_heads;
+  const ReqGeom geo = req_geom(a.b, r, a.n_sink, a.n_recent);
+  const float* srow = a.scores + ((size_t)r * a.num_kv_heads + g) * a.b.max_blocks + geo.c0;
+  topk_wave<MAXC>(srow, geo, topk_budget(a, geo), a.selected + (size_t)item * a.max_selected,
+                  a.max_selected, a.selected_count + item, sh[wave], lane);
+}
+
+template <int MAXC>
+static hipError_t launch_wave(const TopkArgs& a, hipStream_t st) {
+  const int items = a.b.batch * a.num_kv_heads;
+  hipLaunchKernelGGL((topk_wave_kernel<MAXC>), dim3((items + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int PER>
-static hipError_t launch(const TopkArgs& a, hipStream_t st) {
+static hipError_t launch_wg(const TopkArgs& a, hipStream_t st) {
   dim3 grid(a.num_kv_heads, a.b.batch);
-  hipLaunchKernelGGL((topk_kernel<PER>), grid, dim3(kTopkThreads), 0, st, a);
+  hipLaunchKernelGGL((topk_wg_kernel<PER>), grid, dim3(kTopkThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
-  const int per = (a.b.max_blocks + kTopkThreads - 1) / kTopkThreads;
-  if (per <= 1) return launch<1>(a, st);
-  if (per <= 2) return launch<2>(a, st);
-  if (per <= 4) return launch<4>(a, st);
-  if (per <= 8) return launch<8>(a, st);
-  if (per <= 16) return launch<16>(a, st);
-  if (per <= 32) return launch<32>(a, st);
-  return launch<64>(a, st);
+  const int n = a.b.max_blocks;
+  if (n <= 512) return launch_wave<512>(a, st);
+  if (n <= 2048) return launch_wave<2048>(a, st);
+  if (n <= 4096) return launch_wave<4096>(a, st);
+  const int pwg = (n + kTopkThreads - 1) / kTopkThreads;
+  if (pwg <= 32) return launch_wg<32>(a, st);
+  return launch_wg<64>(a, st);
 }
 
 }  // namespace ls

@@ -272,4 +272,118 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
   return hip_status(ls::launch_attn(aa, stream), "attention kernel launch");
 }
 
+size_t ls_sparse_decode_step_control_bytes(int32_t batch_size, int32_t num_kv_heads) {
+  if (batch_size <= 0 || num_kv_heads <= 0) return 0;
+  return ls::step_ctl_bytes(batch_size, num_kv_heads);
+}
+
+size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t max_blocks, int32_t max_selected) {
+  if (batch_size <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks <= 0 || max_selected <= 0)
+    return 0;
+  return ls::step_ctl_bytes(batch_size, num_kv_heads) +
+         ls_score_select_workspace_size(batch_size, num_kv_heads, max_blocks) +
+         ls_sparse_attn_decode_workspace_size(batch_size, num_q_heads, head_dim, max_selected,
+                                              max_blocks);
+}
+
+ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                const void* summaries, const void* k_pool, const void* v_pool,
+                                ls_pool pool, ls_batch batch, const ls_select_params* p,
+                                int32_t* selected, int32_t* selected_count, float sm_scale,
+                                void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!p) return fail(LS_ERR_INVALID, "params must be non-null");
+  if (p->struct_size != (int32_t)sizeof(ls_select_params))
+    return fail(LS_ERR_INVALID, "params.struct_size %d != %d", p->struct_size,
+                (int)sizeof(ls_select_params));
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  if ((st = check_gqa_pool(pool, "kv pool")) != LS_OK) return st;
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (out_dtype != LS_DTYPE_BF16 && out_dtype != LS_DTYPE_FP32)
+    return fail(LS_ERR_UNSUPPORTED, "out_dtype %d (supported: bf16, fp32)", out_dtype);
+  if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
+    return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                pool.num_heads);
+  if (num_q_heads / pool.num_heads != 4)
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
+                num_q_heads / pool.num_heads);
+  if (p->group_agg != LS_AGG_MAX && p->group_agg != LS_AGG_MEAN)
+    return fail(LS_ERR_INVALID, "group_agg %d", p->group_agg);
+  if (p->n_sink < 0 || p->n_recent < 0) return fail(LS_ERR_INVALID, "n_sink/n_recent < 0");
+  if (p->topk < -1) return fail(LS_ERR_INVALID, "topk %d (>= 0, or -1 for keep_ratio)", p->topk);
+  if (p->topk == -1 && !(p->keep_ratio >= 0.0f && p->keep_ratio <= 1.0f))
+    return fail(LS_ERR_INVALID, "keep_ratio must be in [0, 1]");
+  if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
+  if (batch.batch_size == 0) return ok();
+  if (!ls::step_supported(pool.head_dim, pool.num_heads, batch.max_blocks))
+    return fail(LS_ERR_UNSUPPORTED,
+                "fused step: head_dim %d, num_kv_heads %d, max_blocks %d (supported: 64/128, "
+                "2/4/8, <= 4096); use ls_score_select + ls_sparse_attn_decode",
+                pool.head_dim, pool.num_heads, batch.max_blocks);
+  const int need = max_total_selected(*p, batch.max_blocks);
+  if (p->max_selected < need)
+    return fail(LS_ERR_INVALID, "max_selected %d < %d (largest possible selection)",
+                p->max_selected, need);
+  if (!q || !summaries || !k_pool || !v_pool || !selected || !selected_count || !out)
+    return fail(LS_ERR_INVALID, "q, summaries, pools, selection and out must be non-null");
+  if (!aligned16(q) || !aligned16(summaries) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(LS_ERR_INVALID, "q, summaries, k_pool and v_pool must be 16-byte aligned");
+  const size_t ws = ls_sparse_decode_step_workspace_size(batch.batch_size, num_q_heads,
+                                                         pool.num_heads, pool.head_dim,
+                                                         batch.max_blocks, p->max_selected);
+  if (!workspace || workspace_bytes < ws)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  char* w = static_cast<char*>(workspace);
+  const size_t ctl_b = ls::step_ctl_bytes(batch.batch_size, pool.num_heads);
+  const size_t sc_b = ls_score_select_workspace_size(batch.batch_size, pool.num_heads,
+                                                     batch.max_blocks);
+  ls::StepLaunch L;
+  L.ctl = w;
+  float* scores = reinterpret_cast<float*>(w + ctl_b);
+  float* partials = reinterpret_cast<float*>(w + ctl_b + sc_b);
+  L.sc.q = static_cast<const uint16_t*>(q);
+  L.sc.summaries = static_cast<const uint16_t*>(summaries);
+  L.sc.b = batch_args(batch, pool);
+  L.sc.num_q_heads = num_q_heads;
+  L.sc.num_kv_heads = pool.num_heads;
+  L.sc.head_dim = pool.head_dim;
+  L.sc.group_agg = p->group_agg;
+  L.sc.n_sink = p->n_sink;
+  L.sc.n_recent = p->n_recent;
+  L.sc.scores = scores;
+  L.tk.scores = scores;
+  L.tk.b = L.sc.b;
+  L.tk.num_kv_heads = pool.num_heads;
+  L.tk.topk = p->topk;
+  L.tk.keep_ratio = p->keep_ratio;
+  L.tk.n_sink = p->n_sink;
+  L.tk.n_recent = p->n_recent;
+  L.tk.max_selected = p->max_selected;
+  L.tk.selected = selected;
+  L.tk.selected_count = selected_count;
+  L.at.q = L.sc.q;
+  L.at.k_pool = static_cast<const uint16_t*>(k_pool);
+  L.at.v_pool = static_cast<const uint16_t*>(v_pool);
+  L.at.b = L.sc.b;
+  L.at.num_q_heads = num_q_heads;
+  L.at.num_kv_heads = pool.num_heads;
+  L.at.head_dim = pool.head_dim;
+  L.at.selected = selected;
+  L.at.selected_count = selected_count;
+  L.at.max_selected = p->max_selected;
+  L.at.num_splits = ls_attn_num_splits(p->max_selected);
+  L.at.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  L.at.partials = partials;
+  L.at.out = out;
+  L.at.out_dtype = out_dtype;
+  L.at.lse = lse_out;
+  return hip_status(ls::launch_step(L, stream), "decode-step kernel launch");
+}
+
 }  // extern "C"

@@ -98,6 +98,42 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
+// ------------------------------------------------------------------ DPP ----
+// Sum over aligned groups of LPR lanes (LPR = 4, 8 or 16: DPP works inside
+// 16-lane rows), every lane of the group receiving the total: two quad
+// swaps, then the half-row mirror (pairs quads inside 8 lanes), then the row
+// mirror (pairs the 8-lane halves of a row).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16, "group size");
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  if constexpr (LPR >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
+  if constexpr (LPR >= 16) v += dpp_mov<kDppRowMirror>(v);
+  return v;
+}
+
+// Order LDS traffic of one wavefront: every LDS access issued before this
+// point has completed before any issued after it (wave-synchronous code).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
+  return wave_incl_scan(v, lane) - v;
+}
+
 // Order-preserving map of a (finite) float to uint32; -0.0 is mapped like +0.0
 // so that equal scores compare equal.
 __device__ __forceinline__ uint32_t score_key(float f) {

@@ -67,13 +67,23 @@ struct AttnArgs {
   float* lse;
 };
 
+struct StepLaunch {
+  ScoreArgs sc;
+  TopkArgs tk;
+  AttnArgs at;
+  void* ctl;    // zeroed control block (tickets, counters), step_ctl_bytes()
+};
+
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t st);
+hipError_t launch_step(const StepLaunch& a, hipStream_t st);
+size_t step_ctl_bytes(int batch, int hkv);
+bool step_supported(int head_dim, int hkv, int max_blocks);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
 // Blocks per attention split (one register-resident chunk per workgroup).
-constexpr int kAttnBlocksPerSplit = 8;
+constexpr int kAttnBlocksPerSplit = 4;
 
 // Request geometry on the device: blocks, complete blocks, and the candidate
 // range [c0, c1) = complete blocks that are neither sink nor recent. The

@@ -180,3 +180,40 @@ def check_pair(inp: BlockTopKInputs, res: GpuStep, r: int, g: int, *, topk, n_si
     assert np.array_equal(np.isfinite(glse), fin)
     np.testing.assert_allclose(glse[fin], lse[fin], rtol=2e-6, atol=2e-5)
     return info
+
+
+def run_gpu_fused(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None, agg=None,
+                  out_dtype=None, keep_ratio=0.0, sm_scale=None, workspace=None,
+                  summaries=None) -> GpuStep:
+    """The fused one-launch step (ls_sparse_decode_step); scores are read
+    back from its workspace for the parity checks."""
+    import query_aware_sparse_ls_amd as ls
+    cfg = inp.cfg
+    topk = inp.topk if topk is None else topk
+    n_sink = cfg.n_sink if n_sink is None else n_sink
+    n_recent = cfg.n_recent if n_recent is None else n_recent
+    agg = cfg.group_agg if agg is None else agg
+    out_dtype = out_dtype or (torch.float32 if cfg.out_dtype == "fp32" else torch.bfloat16)
+    sm_scale = (1.0 / math.sqrt(cfg.head_dim)) if sm_scale is None else sm_scale
+    dev = inp.k_pool.device
+    B, Hq, D = inp.q.shape
+    Hkv = cfg.num_kv_heads
+    batch = paged_batch(inp)
+    if summaries is None:
+        summaries = torch.zeros(inp.num_pages, Hkv, D, dtype=torch.bfloat16, device=dev)
+        ls.build_block_summaries(inp.k_pool, complete_pages(inp).to(dev), summaries)
+    maxsel = max_selected_for(topk, n_sink, n_recent, batch.max_blocks, keep_ratio)
+    if workspace is None:
+        workspace = ls.sparse_decode_step_workspace(B, Hq, Hkv, D, batch.max_blocks, maxsel, dev)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    out, _, sel, cnt = ls.sparse_decode_step(
+        inp.q, summaries, inp.k_pool, inp.v_pool, batch, topk=topk, n_sink=n_sink,
+        n_recent=n_recent, max_selected=maxsel, sm_scale=sm_scale, group_agg=agg,
+        keep_ratio=keep_ratio, out_dtype=out_dtype, lse=lse, workspace=workspace)
+    torch.cuda.synchronize()
+    ctl = int(ls._L.ls_sparse_decode_step_control_bytes(B, Hkv))
+    n = B * Hkv * batch.max_blocks
+    scores = workspace[ctl:ctl + 4 * n].view(torch.float32).view(B, Hkv, batch.max_blocks)
+    # every completed call must leave the control block zero
+    assert int(workspace[:ctl].count_nonzero()) == 0, "control block not reset"
+    return GpuStep(summaries, scores, sel, cnt, out, lse)

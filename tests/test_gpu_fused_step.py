@@ -1,0 +1,126 @@
+"""The fused one-launch decode step (ls_sparse_decode_step): identical to
+the separate calls, correct against the oracle, reusable workspace, and
+replayable from a HIP graph."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from parity_util import check_pair, run_gpu_fused, run_gpu_step, say
+from workloads import LLAMA8B_32K_B16, TINY_4K, RAGGED_B64, make_block_topk_inputs, reduced
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _kw(inp, **over):
+    cfg = inp.cfg
+    kw = dict(topk=inp.topk, n_sink=cfg.n_sink, n_recent=cfg.n_recent, agg=cfg.group_agg,
+              sm_scale=1.0 / math.sqrt(cfg.head_dim),
+              out_dtype=torch.float32 if cfg.out_dtype == "fp32" else torch.bfloat16)
+    kw.update(over)
+    return kw
+
+
+def _same(a, b):
+    assert torch.equal(a.counts, b.counts)
+    for r in range(a.counts.shape[0]):
+        for g in range(a.counts.shape[1]):
+            n = int(a.counts[r, g])
+            assert torch.equal(a.selected[r, g, :n], b.selected[r, g, :n])
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.lse, b.lse)
+
+
+@pytest.mark.parametrize("cfg", [
+    TINY_4K,
+    reduced(LLAMA8B_32K_B16, batch=3, context=4096 + 5),
+    reduced(LLAMA8B_32K_B16, batch=11, context=1000),
+    reduced(RAGGED_B64, batch=9, ragged_range=(40, 5000), topk=8, keep_ratio=None),
+], ids=["tiny", "8b_b3", "8b_b11", "ragged_b9"])
+def test_fused_equals_separate_and_oracle(cfg):
+    say(f"fused step vs separate calls and oracle: {cfg.name}")
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=31)
+    sep = run_gpu_step(inp)
+    fus = run_gpu_fused(inp, summaries=sep.summaries)
+    _same(sep, fus)
+    for r in range(cfg.batch):
+        for g in range(cfg.num_kv_heads):
+            check_pair(inp, fus, r, g, **_kw(inp))
+
+
+def test_fused_workspace_reuse_across_calls():
+    say("fused step: one workspace, three different steps")
+    import query_aware_sparse_ls_amd as ls
+    cfg = reduced(LLAMA8B_32K_B16, batch=4, context=3000)
+    ws = None
+    for seed in (1, 2, 3):
+        inp = make_block_topk_inputs(cfg, device="cuda", seed=seed)
+        if ws is None:
+            B, Hq, D = inp.q.shape
+            ws = ls.sparse_decode_step_workspace(B, Hq, cfg.num_kv_heads, D, inp.max_blocks(),
+                                                 inp.topk + 4, "cuda")
+        sep = run_gpu_step(inp)
+        fus = run_gpu_fused(inp, summaries=sep.summaries, workspace=ws)
+        _same(sep, fus)
+
+
+def test_fused_step_hip_graph_replay():
+    say("fused step captured in a HIP graph, replayed with eager work in between")
+    import query_aware_sparse_ls_amd as ls
+    cfg = reduced(LLAMA8B_32K_B16, batch=4, context=5000)
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=4)
+    eager = run_gpu_step(inp)
+    B, Hq, D = inp.q.shape
+    batch = ls.PagedBatch(inp.page_indptr, inp.page_indices, inp.seq_lens, inp.max_blocks())
+    maxsel = inp.topk + cfg.n_sink + cfg.n_recent + 1
+    ws = ls.sparse_decode_step_workspace(B, Hq, cfg.num_kv_heads, D, batch.max_blocks, maxsel,
+                                         "cuda")
+    sel = torch.empty(B, cfg.num_kv_heads, maxsel, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, cfg.num_kv_heads, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+
+    def step():
+        ls.sparse_decode_step(inp.q, eager.summaries, inp.k_pool, inp.v_pool, batch,
+                              topk=inp.topk, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                              max_selected=maxsel, sm_scale=1.0 / math.sqrt(D), selected=sel,
+                              selected_count=cnt, out=out, lse=lse, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(5):
+        out.zero_(); lse.zero_(); sel.fill_(-7); cnt.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager.out), f"replay {i}"
+        assert torch.equal(lse, eager.lse)
+        assert torch.equal(cnt, eager.counts)
+        _ = run_gpu_step(inp)            # unrelated eager work between replays
+    assert int(ws[:int(ls._L.ls_sparse_decode_step_control_bytes(B, cfg.num_kv_heads))]
+               .count_nonzero()) == 0
+
+
+def test_fused_full_size_llama8b_32k_b16():
+    cfg = LLAMA8B_32K_B16
+    say(f"fused step at full size: {cfg.name}")
+    inp = make_block_topk_inputs(cfg, device="cuda")
+    sep = run_gpu_step(inp)
+    fus = run_gpu_fused(inp, summaries=sep.summaries)
+    _same(sep, fus)
+    for r, g in [(0, 0), (7, 3), (15, 7)]:
+        check_pair(inp, fus, r, g, **_kw(inp))

@@ -8,6 +8,8 @@ or 1e-5 (fp32) of the oracle's attention over the GPU's own selection.
 import math
 
 import numpy as np
+
+import oracle
 import pytest
 import torch
 
@@ -178,9 +180,25 @@ def test_llama8b_32k_b16_full_size_sampled():
     for r, g in sorted(pairs):
         bands += check_pair(inp, res, r, g, **{k: v for k, v in _kw(inp, res).items()
                                                if k != "res"})["band"]
-    # every hot block of every (r, g) is selected
-    for (r, g), hot in inp.hot_blocks.items():
-        sel = set(res.selected[r, g, :int(res.counts[r, g])].tolist())
-        assert set(hot) <= sel
+    # every (r, g) selection against the oracle's ranking of the GPU summaries
+    # (those are bit-exact wherever checked above)
+    from oracle.method import BatchView
+    from parity_util import check_selection
+    summ = bf16_bits(res.summaries)
+    bv = BatchView(inp.page_indptr.cpu().numpy(), inp.page_indices.cpu().numpy(),
+                   inp.seq_lens.cpu().numpy(), cfg.page_size)
+    q = bf16_bits(inp.q)
+    hot_hit = hot_all = 0
+    for r in range(cfg.batch):
+        for g in range(cfg.num_kv_heads):
+            s = oracle.block_scores(q, summ, bv, r, g, num_kv_heads=cfg.num_kv_heads, agg="max")
+            sel = res.selected[r, g, :int(res.counts[r, g])].tolist()
+            bands += check_selection(sel, s, 2048, 2048, cfg.topk, cfg.n_sink, cfg.n_recent)["band"]
+            hot = inp.hot_blocks[(r, g)]
+            hot_hit += len(set(hot) & set(sel))
+            hot_all += len(hot)
     assert (res.counts == 67).all()
-    say(f"near-tie band blocks over sampled pairs: {bands}")
+    # the +2 sigma hot blocks dominate the selection (not all: a hot block can
+    # still rank below the 64th score)
+    assert hot_hit >= 0.95 * hot_all, (hot_hit, hot_all)
+    say(f"near-tie band blocks: {bands}; hot blocks selected {hot_hit}/{hot_all}")
