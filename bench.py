@@ -2,8 +2,13 @@
 
 One step = the whole path for one batch of synthetic input:
   1. summaries of the pages that just filled (ls_build_block_summaries),
-  2. GQA block scoring + top-k + forced sink/recent (ls_score_select),
-  3. split-K attention over the selected blocks (ls_sparse_attn_decode).
+  2. GQA block scoring + top-k + forced sink/recent, and
+  3. split-K attention over the selected blocks,
+where 2 + 3 run as ONE persistent launch (ls_sparse_decode_step) by default
+(--separate: ls_score_select then ls_sparse_attn_decode). Step 1 runs on a
+side stream, forked and joined inside the step: the pages that just filled
+are in the recent window, so this step's selection does not read their
+summaries.
 
 Workload: Llama-3-8B-shaped decode attention, 16 requests x 32K tokens,
 32 query / 8 KV heads, head_dim 128, 16-token pages in a seeded random
@@ -72,6 +77,8 @@ def make_replica(cfg, seed, device):
     ls.build_block_summaries(inp.k_pool, full.to(torch.int32).to(device), summ)
     maxsel = min(batch.max_blocks, inp.topk + cfg.n_sink + cfg.n_recent + 1)
     rep = dict(inp=inp, batch=batch, summ=summ,
+               ws_step=ls.sparse_decode_step_workspace(B, Hq, Hkv, D, batch.max_blocks,
+                                                       maxsel, device),
                new_pages=torch.tensor(new, dtype=torch.int32, device=device),
                sel=torch.empty(B, Hkv, maxsel, dtype=torch.int32, device=device),
                cnt=torch.empty(B, Hkv, dtype=torch.int32, device=device),
@@ -84,21 +91,43 @@ def make_replica(cfg, seed, device):
     return rep
 
 
-def run_step(rep, cfg, sm_scale, timers=None):
+def run_step(rep, cfg, sm_scale, fused=True, side=None, timers=None):
+    """One step. With `side`, the summary update runs on that stream, forked
+    from and joined back into the current stream. With `timers` (eager timing
+    pass) events bracket each call: [update, select(+attend), attend]."""
+    import torch
     import query_aware_sparse_ls_amd as ls
     inp = rep["inp"]
     ev = timers
-    if ev: ev[0].record()
-    ls.build_block_summaries(inp.k_pool, rep["new_pages"], rep["summ"])
+    main = torch.cuda.current_stream()
+    if side is not None:
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            ls.build_block_summaries(inp.k_pool, rep["new_pages"], rep["summ"])
+    else:
+        if ev: ev[0].record()
+        ls.build_block_summaries(inp.k_pool, rep["new_pages"], rep["summ"])
     if ev: ev[1].record()
-    ls.score_select(inp.q, rep["summ"], cfg.page_size, rep["batch"], topk=inp.topk,
-                    n_sink=cfg.n_sink, n_recent=cfg.n_recent, max_selected=rep["maxsel"],
-                    group_agg=cfg.group_agg, selected=rep["sel"], selected_count=rep["cnt"],
-                    workspace=rep["ws_sel"])
-    if ev: ev[2].record()
-    ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, rep["batch"], rep["sel"], rep["cnt"],
-                          sm_scale=sm_scale, out=rep["out"], workspace=rep["ws_attn"])
+    if fused:
+        ls.sparse_decode_step(inp.q, rep["summ"], inp.k_pool, inp.v_pool, rep["batch"],
+                              topk=inp.topk, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                              max_selected=rep["maxsel"], sm_scale=sm_scale,
+                              group_agg=cfg.group_agg, selected=rep["sel"],
+                              selected_count=rep["cnt"], out=rep["out"],
+                              workspace=rep["ws_step"])
+        if ev: ev[2].record()
+    else:
+        ls.score_select(inp.q, rep["summ"], cfg.page_size, rep["batch"], topk=inp.topk,
+                        n_sink=cfg.n_sink, n_recent=cfg.n_recent, max_selected=rep["maxsel"],
+                        group_agg=cfg.group_agg, selected=rep["sel"], selected_count=rep["cnt"],
+                        workspace=rep["ws_sel"])
+        if ev: ev[2].record()
+        ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, rep["batch"], rep["sel"],
+                              rep["cnt"], sm_scale=sm_scale, out=rep["out"],
+                              workspace=rep["ws_attn"])
     if ev: ev[3].record()
+    if side is not None:
+        main.wait_stream(side)
 
 
 def cpu_baseline(rep, cfg, sm_scale, budget_s: float):
@@ -145,6 +174,21 @@ def cpu_baseline(rep, cfg, sm_scale, budget_s: float):
             "seconds_per_call": per_call}
 
 
+def copy_calibration(nbytes: int) -> int:
+    """A plain device-to-device copy of nbytes (for scaling PMC byte counters:
+    FETCH_SIZE and WRITE_SIZE of this kernel should read nbytes each)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,11 +198,16 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="time ls_score_select + ls_sparse_attn_decode instead of the fused step")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the sparse-attention path has no multi-GPU mode "
               "(run with --gpus 1).", file=sys.stderr)
         return 2
+    if args.copy_calibrate:
+        return copy_calibration(args.copy_calibrate)
 
     import torch
     import query_aware_sparse_ls_amd as ls
@@ -168,11 +217,12 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sm_scale = 1.0 / math.sqrt(cfg.head_dim)
+    fused = not args.separate
     R = max(1, args.replicas)
     reps = [make_replica(cfg, cfg.seed + i, dev) for i in range(R)]
     torch.cuda.synchronize()
-    print(f"# {R} replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB", file=sys.stderr,
-          flush=True)
+    print(f"# {R} replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
 
     inp0 = reps[0]["inp"]
     P, Hkv, D, Hq, B = cfg.page_size, cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads, cfg.batch
@@ -181,30 +231,31 @@ def main(argv=None) -> int:
     n_sel = inp0.topk + n_forced
     n_cand = nb - n_forced
     nbytes = step_bytes(B, Hq, Hkv, D, P, nb, n_sel, n_cand, int(reps[0]["new_pages"].numel()))
+    main_stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
 
-    stream = torch.cuda.current_stream()
-    # warm-up (eager), which also loads every kernel
     for i in range(max(1, args.warmup)):
-        run_step(reps[i % R], cfg, sm_scale)
+        run_step(reps[i % R], cfg, sm_scale, fused, side)
     torch.cuda.synchronize()
 
     graph = None
     if not args.no_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
+        cap = torch.cuda.Stream()
+        cap.wait_stream(main_stream)
+        with torch.cuda.stream(cap):
             for i in range(R):
-                run_step(reps[i], cfg, sm_scale)
-        stream.wait_stream(s)
+                run_step(reps[i], cfg, sm_scale, fused, side)
+        main_stream.wait_stream(cap)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(R):
-                run_step(reps[i], cfg, sm_scale)
+                run_step(reps[i], cfg, sm_scale, fused, side)
         torch.cuda.synchronize()
         for _ in range(max(1, args.warmup // R)):
             graph.replay()
         torch.cuda.synchronize()
+    print("# timing", file=sys.stderr, flush=True)
 
     replays = max(1, args.steps // R)
     steps = replays * R
@@ -217,12 +268,11 @@ def main(argv=None) -> int:
             graph.replay()
     else:
         for i in range(steps):
-            run_step(reps[i % R], cfg, sm_scale)
+            run_step(reps[i % R], cfg, sm_scale, fused, side)
     t1e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = t0e.elapsed_time(t1e)
-    ms_step = ms_total / steps
+    ms_step = t0e.elapsed_time(t1e) / steps
 
     # per-call durations: eager, events around each call, GPU given a head start
     n_eager = min(steps, 8 * R)
@@ -230,18 +280,23 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e8))
     for i in range(n_eager):
-        run_step(reps[i % R], cfg, sm_scale, timers=evs[i])
+        run_step(reps[i % R], cfg, sm_scale, fused, None, timers=evs[i])
     torch.cuda.synchronize()
-    upd = sum(e[0].elapsed_time(e[1]) for e in evs) / n_eager
-    sel = sum(e[1].elapsed_time(e[2]) for e in evs) / n_eager
-    att = sum(e[2].elapsed_time(e[3]) for e in evs) / n_eager
+    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / n_eager
+    upd, first, second = avg(0, 1), avg(1, 2), avg(2, 3)
 
     calls_per_s = 1e3 / ms_step
     gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
-    att_bytes = nbytes["selected_kv"] + B * Hq * D * 2 * 2 + B * Hkv * n_sel * 4
-    att_gbps = att_bytes / (att * 1e-3) / 1e9
-    sel_bytes = nbytes["summaries"] + B * Hq * D * 2 + B * nb * 4 + B * Hkv * n_sel * 4
-    sel_gbps = sel_bytes / (sel * 1e-3) / 1e9
+    sel_bytes = B * Hkv * n_sel * 4 + B * Hkv * 4      # selection written (+ counts)
+    fused_bytes = nbytes["total"] - nbytes["summary_update"] + sel_bytes
+    if fused:
+        dom_ms, dom_bytes = first, fused_bytes
+        dom_name = "decode_step_kernel (scoring + top-k + split-K attention + merge, one launch)"
+    else:
+        dom_ms = second
+        dom_bytes = nbytes["selected_kv"] + B * Hq * D * 4 + sel_bytes + B * nb * 4
+        dom_name = "ls_sparse_attn_decode (split-K attention + combine kernels)"
+    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     res = {
         "metric": "sparse decode attention calls/sec + achieved HBM GB/s (% of peak) at 8B/32K/B16",
@@ -251,22 +306,23 @@ def main(argv=None) -> int:
         "config": {"workload": cfg.name, "batch": B, "context": cfg.context, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "page_size": P, "topk": inp0.topk,
                    "n_sink": cfg.n_sink, "n_recent": cfg.n_recent, "replicas": R,
+                   "path": "fused" if fused else "separate",
                    "timing": "hip graph" if graph is not None else "eager"},
         "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
         "achieved_GBps_step": round(gbps, 1),
         "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "call_ms": {"summary_update": round(upd, 5), "score_select": round(sel, 5),
-                    "sparse_attn_decode": round(att, 5)},
-        "call_GBps": {"score_select": round(sel_gbps, 1), "sparse_attn_decode": round(att_gbps, 1)},
-        "roofline": {"kernel": "ls_sparse_attn_decode (split-K gather attention + combine)",
-                     "bound": "hbm", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": att_bytes,
-                     "avg_launch_ms": round(att, 5)},
+        "call_ms": ({"summary_update": round(upd, 5), "decode_step": round(first, 5)} if fused
+                    else {"summary_update": round(upd, 5), "score_select": round(first, 5),
+                          "sparse_attn_decode": round(second, 5)}),
+        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)},
         "wall_s_timed": round(wall, 4),
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
+        print("# cpu baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(reps[0], cfg, sm_scale, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0

@@ -65,12 +65,13 @@ struct SelRow {
   const int32_t* row;
 };
 
+template <bool kDev>
 __device__ __forceinline__ SelRow sel_row(const AttnArgs& a, const ReqGeom& geo, int r, int g) {
   SelRow s;
   s.cnt = geo.nb;
   s.row = nullptr;
   if (a.selected) {
-    int c = a.selected_count[(size_t)r * a.num_kv_heads + g];
+    int c = ld_x<kDev>(&a.selected_count[(size_t)r * a.num_kv_heads + g]);
     s.cnt = c < 0 ? 0 : (c > a.max_selected ? a.max_selected : c);
     s.row = a.selected + ((size_t)r * a.num_kv_heads + g) * a.max_selected;
   }
@@ -81,7 +82,7 @@ __device__ __forceinline__ SelRow sel_row(const AttnArgs& a, const ReqGeom& geo,
 // (hi - lo <= CH), written as split `s` of the partial buffer:
 // partials[r][g*G + h][s][0..D-1] = unnormalised o, [D] = m (log2 domain),
 // [D+1] = l. Must be called by all 256 threads of the workgroup.
-template <int D, int G, int CH>
+template <int D, int G, int CH, bool kDev>
 __device__ __forceinline__ void attn_split(const AttnArgs& a, const ReqGeom& geo, const SelRow& sr,
                                            int r, int g, int s, int lo, int hi,
                                            AttnLds<D, G>& sh) {
@@ -105,7 +106,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, const ReqGeom& geo
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     const int idx = lo + i * BPR + bir;
-    blk[i] = idx < hi ? (sr.row ? sr.row[idx] : idx) : -1;
+    blk[i] = idx < hi ? (sr.row ? ld_x<kDev>(&sr.row[idx]) : idx) : -1;
   }
   int page[NR];
   bool ok[NR];
@@ -183,15 +184,15 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, const ReqGeom& geo
       }
     }
     float* ph = part + (size_t)h * S_ * (D + 2);
-    ph[d] = O;
-    if (d == 0) { ph[D] = M; ph[D + 1] = Ls; }
+    st_x<kDev>(&ph[d], O);
+    if (d == 0) { st_x<kDev>(&ph[D], M); st_x<kDev>(&ph[D + 1], Ls); }
   }
   __syncthreads();
 }
 
 // Merge the S partials of query head `item` (= r * Hq + h) in split order and
 // write the rounded output and lse. One wave; lane owns dims lane + 64 j.
-template <int D>
+template <int D, bool kDev>
 __device__ __forceinline__ void combine_head(const AttnArgs& a, int item, int lane) {
   constexpr int DPL = D / kWave;
   const int S = a.num_splits;
@@ -200,7 +201,7 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, int item, int la
   float M = kNegInf;
   for (int s0 = 0; s0 < S; s0 += kWave) {
     const int s = s0 + lane;
-    const float ms = s < S ? part[(size_t)s * (D + 2) + D] : kNegInf;
+    const float ms = s < S ? ld_x<kDev>(&part[(size_t)s * (D + 2) + D]) : kNegInf;
     M = fmaxf(M, wave_max(ms));
   }
   float O[DPL], Ls = 0.0f;
@@ -214,10 +215,10 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, int item, int la
       for (int u = 0; u < U; ++u) {
         const int s = s0 + u;
         const float* ps = part + (size_t)(s < S ? s : 0) * (D + 2);
-        ms[u] = s < S ? ps[D] : kNegInf;
-        ls[u] = ps[D + 1];
+        ms[u] = s < S ? ld_x<kDev>(&ps[D]) : kNegInf;
+        ls[u] = ld_x<kDev>(&ps[D + 1]);
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) os[u][j] = ps[lane + j * kWave];
+        for (int j = 0; j < DPL; ++j) os[u][j] = ld_x<kDev>(&ps[lane + j * kWave]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

@@ -28,7 +28,7 @@ struct ScoreShape {
   static constexpr int kLanesPerRow = D / 8;
   static constexpr int J = kUnitsPerPage >= kWave ? kUnitsPerPage / kWave : 1;   // loads/page
   static constexpr int PPI = kUnitsPerPage >= kWave ? 1 : kWave / kUnitsPerPage;  // pages/load
-  static constexpr int NI = J >= 8 ? 1 : 8 / J;          // load rounds per wave
+  static constexpr int NI = J >= 16 ? 1 : 16 / J;        // load rounds per wave (16 loads)
   static constexpr int kBlocksPerWave = NI * PPI;
   static_assert(kUnitsPerPage % kWave == 0 || kWave % kUnitsPerPage == 0, "page geometry");
 };
@@ -45,11 +45,18 @@ __device__ __forceinline__ float dot8_bf16(const uint32_t* q, uint4 s, float acc
   return acc;
 }
 
-// One wave scores the candidate blocks of request r that fall in
-// [wb0, wb0 + kBlocksPerWave). geo: the request's geometry.
+// Per-wave LDS staging of the scores, written out as contiguous runs.
 template <int D, int HKV, int G>
+struct ScoreLds {
+  float s[HKV * ScoreShape<D, HKV, G>::kBlocksPerWave];
+};
+
+// One wave scores the candidate blocks of request r that fall in
+// [wb0, wb0 + kBlocksPerWave). geo: the request's geometry. kDev: write the
+// scores device-coherently (consumed by other workgroups of the same launch).
+template <int D, int HKV, int G, bool kDev>
 __device__ __forceinline__ void score_wave(const ScoreArgs& a, int r, const ReqGeom& geo,
-                                           int wb0, int lane) {
+                                           int wb0, int lane, ScoreLds<D, HKV, G>& st) {
   using S = ScoreShape<D, HKV, G>;
   constexpr int J = S::J, PPI = S::PPI, NI = S::NI, LPR = S::kLanesPerRow;
   const int lo = max(geo.c0, wb0), hi = min(geo.c1, wb0 + S::kBlocksPerWave);
@@ -94,7 +101,7 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, int r, const ReqG
                      : make_uint4(0, 0, 0, 0);
     }
   }
-  float* out = a.scores + (size_t)r * HKV * a.b.max_blocks;
+  constexpr int BPW = S::kBlocksPerWave;
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
 #pragma unroll
@@ -114,8 +121,87 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, int r, const ReqG
           for (int h = 1; h < G; ++h) s = fmaxf(s, part[h]);
         }
       }
-      if (ok[it][j] && ch[j] == 0) out[(size_t)gh[j] * a.b.max_blocks + blk[it][j]] = s;
+      if (ch[j] == 0) st.s[gh[j] * BPW + it * PPI + poff[j]] = s;
     }
+  }
+  wave_lds_sync();
+  // scores[r][g][wb0 .. wb0 + BPW): runs of BPW consecutive floats per head
+  float* out = a.scores + (size_t)r * HKV * a.b.max_blocks;
+  for (int i = lane; i < HKV * BPW; i += kWave) {
+    const int g = i / BPW, b = wb0 + i % BPW;
+    if (b >= lo && b < hi) st_x<kDev>(&out[(size_t)g * a.b.max_blocks + b], st.s[i]);
+  }
+  wave_lds_sync();
+}
+
+}  // namespace ls
+
+namespace ls {
+
+// ---------------------------------------------------------------------------
+// Scoring of one (request, kv head) chunk by a whole workgroup: the chunk's
+// summary rows (256 bytes each at D = 128) are read row by row, D/8 lanes per
+// row, 4 waves x NL loads per lane, all in flight after one page-id hop. Used
+// by the two-launch decode step, whose top-k runs in the workgroup that
+// finishes the last chunk of each (request, kv head).
+// ---------------------------------------------------------------------------
+template <int D, int G, int CB>
+struct HeadChunkShape {
+  static constexpr int LPR = D / 8;          // lanes per summary row
+  static constexpr int RPL = kWave / LPR;    // rows per wave load
+  static constexpr int RPW = CB / 4;         // rows per wave
+  static constexpr int NL = RPW / RPL;       // loads per lane
+  static_assert(CB % (4 * RPL) == 0, "chunk");
+};
+
+// Scores of blocks [blk0, blk0 + CB) of (r, g) into out_lds[0 .. CB) (entries
+// of blocks outside the request's candidate range are left untouched).
+template <int D, int HKV, int G, int CB>
+__device__ __forceinline__ void score_head_chunk(const ScoreArgs& a, int r, int g,
+                                                 const ReqGeom& geo, int blk0, float* out_lds) {
+  using S = HeadChunkShape<D, G, CB>;
+  constexpr int LPR = S::LPR, RPL = S::RPL, RPW = S::RPW, NL = S::NL;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane % LPR, rl = lane / LPR;
+  uint32_t qv[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 t = ldg16(a.q + ((size_t)r * (HKV * G) + g * G + h) * D + c * 8);
+    qv[h][0] = t.x; qv[h][1] = t.y; qv[h][2] = t.z; qv[h][3] = t.w;
+  }
+  const int32_t* pages = a.b.indices + geo.page_base;
+  int pg[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int b = blk0 + wave * RPW + i * RPL + rl;
+    pg[i] = (b >= geo.c0 && b < geo.c1) ? pages[b] : -1;
+  }
+  uint4 buf[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int p = pg[i];
+    buf[i] = (p >= 0 && p < a.b.num_pages)
+                 ? ldg16(a.summaries + ((size_t)p * HKV + g) * D + c * 8)
+                 : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    float s;
+    {
+      float part[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] = group_sum<LPR>(dot8_bf16(qv[h], buf[i], 0.0f));
+      s = part[0];
+      if (a.group_agg == LS_AGG_MEAN) {
+#pragma unroll
+        for (int h = 1; h < G; ++h) s += part[h];
+        s *= (1.0f / G);
+      } else {
+#pragma unroll
+        for (int h = 1; h < G; ++h) s = fmaxf(s, part[h]);
+      }
+    }
+    if (c == 0 && pg[i] >= 0) out_lds[wave * RPW + i * RPL + rl] = s;
   }
 }
 

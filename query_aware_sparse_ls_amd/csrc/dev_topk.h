@@ -1,7 +1,7 @@
 // Per (request, KV head) top-k over block scores plus forced sink / recent
-// blocks, emitted in ascending block order -- one wavefront, no workgroup
-// barriers (wave-level device code shared by the standalone top-k kernel and
-// the fused decode-step kernel).
+// blocks, emitted in ascending block order -- one 256-thread workgroup
+// (device code shared by the standalone top-k kernel and the fused
+// decode-step kernel).
 //
 // Vortex post: I = top-k_j(s_j) ("Why Long Generations Are Expensive"). The
 // post notes that radix top-k, which buckets values by their digits, slows
@@ -12,32 +12,34 @@
 // between their min and max (fp32 subtraction and multiplication by a
 // positive constant are monotone), takes every candidate above the bucket
 // holding the k-th score, drops those below, and refines the boundary bucket.
-// Once at most 64 candidates remain undecided they are ranked exactly, one
-// per lane, by (score descending, block index ascending): ties go to the
-// lowest block index and the result is unique and deterministic. Equal or
-// pathological scores fall back to a bitwise threshold search on an
-// order-preserving integer key followed by a lowest-index fill.
+// Once at most 64 candidates remain undecided, one wave sorts them by
+// (score descending, block index ascending) with a register bitonic network
+// and takes the first ones: ties go to the lowest block index and the result
+// is unique and deterministic. Equal or pathological scores fall back to a
+// bitwise threshold search on an order-preserving integer key followed by a
+// lowest-index fill.
 //
-// The wave's candidate scores live in LDS; element e (block c0 + e) is
-// handled by lane e % 64 as bit e / 64 of that lane's 64-bit masks, so index
-// order is (bit, lane) order and every ordered count is a wave ballot.
+// Thread t holds the scores of candidates [t*PER, t*PER + PER) in registers,
+// so index order is thread order, then register order, and ordered counts are
+// one workgroup prefix sum.
 #pragma once
 
 #include "ls_internal.h"
 
 namespace ls {
 
+constexpr int kTopkThreads = 256;
 constexpr int kTopkMaxIters = 24;
+constexpr int kTopkMaxCand = 16384;
 
-// MAXC: candidate capacity (a multiple of 64, at most 4096).
-template <int MAXC>
-struct WaveTopkLds {
-  static_assert(MAXC % kWave == 0 && MAXC <= 64 * kWave, "capacity");
-  float keys[MAXC];
+struct TopkLds {
   int hist[256];
+  float red_f[2][4];
+  int red_i[4][4];
+  int bstar, cabove;
   float list_key[kWave];
   int list_idx[kWave];
-  unsigned long long mark[kWave];
+  unsigned char chosen[kTopkMaxCand];   // per-candidate flag written by the final sort
 };
 
 // Monotone bucket of a score between mn and mx (scale = 256 / (mx - mn)).
@@ -46,51 +48,65 @@ __device__ __forceinline__ int bucket_of(float key, float mn, float scale) {
   return b > 255 ? 255 : (b < 0 ? 0 : b);
 }
 
-__device__ __forceinline__ int lanes_below(unsigned long long m, int lane) {
-  return __popcll(m & ((1ull << lane) - 1ull));
+// Workgroup total of a small per-thread count (< 128); one barrier.
+__device__ __forceinline__ int wg_sum_i(TopkLds& sh, int v, int slot) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int tot;
+  (void)wave_excl_scan_small<7>(v, &tot);
+  if (lane == 0) sh.red_i[slot][wave] = tot;
+  __syncthreads();
+  return sh.red_i[slot][0] + sh.red_i[slot][1] + sh.red_i[slot][2] + sh.red_i[slot][3];
 }
 
-// The `need` lowest-index members of `pool` (bit j of lane l = element 64j + l).
-__device__ __forceinline__ unsigned long long lowest_fill(unsigned long long pool, int need,
-                                                          int nbits, int lane) {
-  unsigned long long take = 0;
-  int base = 0;
-  for (int j = 0; j < nbits && base < need; ++j) {
-    const bool b = (pool >> j) & 1ull;
-    const unsigned long long m = __ballot(b);
-    if (b && base + lanes_below(m, lane) < need) take |= 1ull << j;
-    base += __popcll(m);
+// Exclusive prefix sum of a small per-thread count (< 128) over the
+// workgroup in thread order; *total = sum. One barrier.
+__device__ __forceinline__ int wg_excl_scan_i(TopkLds& sh, int v, int slot, int* total) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int wtot;
+  const int pre = wave_excl_scan_small<7>(v, &wtot);
+  if (lane == 0) sh.red_i[slot][wave] = wtot;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int x = sh.red_i[slot][w];
+    before += (w < wave) ? x : 0;
+    tot += x;
   }
-  return take;
+  *total = tot;
+  return before + pre;
+}
+
+// (a before b) in the selection order: higher score first, then lower index.
+__device__ __forceinline__ bool ahead(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Inclusive suffix sum over the wave (lane l gets the sum of lanes >= l) of
+// per-lane bucket counts (< 2^15), by bit planes.
+__device__ __forceinline__ int tot_minus_prefix(int v, int* total) {
+  const int pre = wave_excl_scan_small<15>(v, total);
+  return *total - pre;
 }
 
 // srow: scores of candidate blocks c0 .. c1-1 (srow[0] is block c0);
-// c1 - c0 <= MAXC.
-template <int MAXC>
-__device__ void topk_wave(const float* __restrict__ srow, const ReqGeom& geo, int k,
-                          int32_t* __restrict__ out, int max_selected,
-                          int32_t* __restrict__ count_out, WaveTopkLds<MAXC>& sh, int lane) {
+// c1 - c0 <= 256 * PER <= kTopkMaxCand. Called by all 256 threads.
+template <int PER, bool kDev>
+__device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k,
+                        int32_t* __restrict__ out, int max_selected,
+                        int32_t* __restrict__ count_out, TopkLds& sh) {
+  static_assert(PER >= 1 && PER <= 64 && PER * kTopkThreads <= kTopkMaxCand, "PER");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = geo.c1 - geo.c0;
-  const int nbits = (n + kWave - 1) / kWave;
   int need = k < n ? k : n;
+  float key[PER];
   unsigned long long act = 0, sel = 0;
-  for (int j0 = 0; j0 < nbits; j0 += 8) {
-    float t[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = (j0 + u) * kWave + lane;
-      t[u] = (j0 + u < nbits && e < n) ? srow[e] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = (j0 + u) * kWave + lane;
-      if (j0 + u < nbits && e < n) {
-        sh.keys[e] = t[u];
-        act |= 1ull << (j0 + u);
-      }
-    }
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    key[j] = e < n ? ld_x<kDev>(&srow[e]) : 0.0f;
+    act |= (unsigned long long)(e < n) << j;
   }
-  wave_lds_sync();
   if (need >= n) {
     sel = act;
     act = 0;
@@ -99,47 +115,55 @@ __device__ void topk_wave(const float* __restrict__ srow, const ReqGeom& geo, in
   bool robust = false;
   for (int it = 0; need > 0; ++it) {
     float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-    for (int j = 0; j < nbits; ++j) {
-      if ((act >> j) & 1ull) {
-        const float x = sh.keys[j * kWave + lane];
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
-      }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool a = (act >> j) & 1ull;
+      mn = a ? fminf(mn, key[j]) : mn;
+      mx = a ? fmaxf(mx, key[j]) : mx;
     }
-    const int cnt = wave_sum(__popcll(act));
-    mn = wave_min(mn);
-    mx = wave_max(mx);
+    int cnt;
+    (void)wave_excl_scan_small<7>(__popcll(act), &cnt);
+    mn = wave_min_fast(mn);
+    mx = wave_max_fast(mx);
+    if (lane == 0) { sh.red_i[0][wave] = cnt; sh.red_f[0][wave] = mn; sh.red_f[1][wave] = mx; }
+    __syncthreads();
+    cnt = sh.red_i[0][0] + sh.red_i[0][1] + sh.red_i[0][2] + sh.red_i[0][3];
+    mn = fminf(fminf(sh.red_f[0][0], sh.red_f[0][1]), fminf(sh.red_f[0][2], sh.red_f[0][3]));
+    mx = fmaxf(fmaxf(sh.red_f[1][0], sh.red_f[1][1]), fmaxf(sh.red_f[1][2], sh.red_f[1][3]));
+    __syncthreads();
     if (cnt <= need) {          // the boundary bucket holds exactly the remainder
       sel |= act;
       act = 0;
       break;
     }
     if (cnt <= kWave) {
-      // exact ranking of the undecided candidates, one per lane
-      int pos = wave_excl_scan(__popcll(act), lane);
-      for (int j = 0; j < nbits; ++j) {
+      // the undecided candidates, sorted by one wave; the first `need` win
+      int total;
+      int pos = wg_excl_scan_i(sh, __popcll(act), 1, &total);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
         if ((act >> j) & 1ull) {
-          const int e = j * kWave + lane;
-          sh.list_key[pos] = sh.keys[e];
-          sh.list_idx[pos] = e;
+          sh.list_key[pos] = key[j];
+          sh.list_idx[pos] = tid * PER + j;
           ++pos;
         }
       }
-      sh.mark[lane] = 0ull;
-      wave_lds_sync();
-      if (lane < cnt) {
-        const float mk = sh.list_key[lane];
-        const int mi = sh.list_idx[lane];
+      __syncthreads();
+      if (tid < cnt) {
+        // rank = number of undecided candidates ahead of this one
+        const float mk = sh.list_key[tid];
+        const int mi = sh.list_idx[tid];
         int rank = 0;
-        for (int u = 0; u < cnt; ++u) {
-          const float ok = sh.list_key[u];
-          const int oi = sh.list_idx[u];
-          rank += (ok > mk) || (ok == mk && oi < mi);
+#pragma unroll 8
+        for (int u = 0; u < kWave; ++u) {
+          if (u < cnt) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
         }
-        if (rank < need) atomicOr(&sh.mark[mi % kWave], 1ull << (mi / kWave));
+        sh.chosen[mi] = rank < need ? 1 : 0;
       }
-      wave_lds_sync();
-      sel |= sh.mark[lane];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (((act >> j) & 1ull) && sh.chosen[tid * PER + j]) sel |= 1ull << j;
       act = 0;
       break;
     }
@@ -149,43 +173,45 @@ __device__ void topk_wave(const float* __restrict__ srow, const ReqGeom& geo, in
       robust = true;
       break;
     }
+    sh.hist[tid] = 0;
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh.hist[lane * 4 + i] = 0;
-    wave_lds_sync();
-    for (int j = 0; j < nbits; ++j) {
-      if ((act >> j) & 1ull)
-        atomicAdd(&sh.hist[bucket_of(sh.keys[j * kWave + lane], mn, scale)], 1);
-    }
-    wave_lds_sync();
-    // suffix counts over 256 buckets, 4 per lane
-    const int h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1];
-    const int h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
-    int suf = h0 + h1 + h2 + h3;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int nx = __shfl_down(suf, o, kWave);
-      if (lane + o < kWave) suf += nx;
-    }
-    const int s3 = suf - h0 - h1 - h2, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
-    int best = -1, sbest = 0, hbest = 0;
-    if (s0 >= need) { best = 4 * lane; sbest = s0; hbest = h0; }
-    if (s1 >= need) { best = 4 * lane + 1; sbest = s1; hbest = h1; }
-    if (s2 >= need) { best = 4 * lane + 2; sbest = s2; hbest = h2; }
-    if (s3 >= need) { best = 4 * lane + 3; sbest = s3; hbest = h3; }
-    int bstar = best;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) bstar = max(bstar, __shfl_xor(bstar, o, kWave));
-    // count above the boundary bucket, from the lane that owns it
-    const int cabove = __shfl(sbest - hbest, bstar >> 2, kWave);
-    for (int j = 0; j < nbits; ++j) {
-      if ((act >> j) & 1ull) {
-        const int b = bucket_of(sh.keys[j * kWave + lane], mn, scale);
-        if (b > bstar) { sel |= 1ull << j; act &= ~(1ull << j); }
-        else if (b < bstar) { act &= ~(1ull << j); }
+    for (int j = 0; j < PER; ++j)
+      if ((act >> j) & 1ull) atomicAdd(&sh.hist[bucket_of(key[j], mn, scale)], 1);
+    __syncthreads();
+    if (wave == 0) {
+      // suffix counts over the 256 buckets, 4 per lane
+      const int h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1];
+      const int h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
+      // suffix sums of the lane totals: total - exclusive prefix
+      int tot;
+      const int lsum = h0 + h1 + h2 + h3;
+      const int suf = tot_minus_prefix(lsum, &tot);
+      const int s3 = suf - h0 - h1 - h2, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+      int best = -1, sbest = 0, hbest = 0;
+      if (s0 >= need) { best = 4 * lane; sbest = s0; hbest = h0; }
+      if (s1 >= need) { best = 4 * lane + 1; sbest = s1; hbest = h1; }
+      if (s2 >= need) { best = 4 * lane + 2; sbest = s2; hbest = h2; }
+      if (s3 >= need) { best = 4 * lane + 3; sbest = s3; hbest = h3; }
+      const int bmax = (int)wave_max_fast((float)best);
+      if (best == bmax && best >= 0) {
+        sh.bstar = best;
+        sh.cabove = sbest - hbest;
       }
     }
+    __syncthreads();
+    const int bstar = sh.bstar, cabove = sh.cabove;
+    unsigned long long up = 0, keep = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int b = bucket_of(key[j], mn, scale);
+      up |= (unsigned long long)(b > bstar) << j;
+      keep |= (unsigned long long)(b == bstar) << j;
+    }
+    sel |= act & up;
+    act &= keep;
     need -= cabove;
-    wave_lds_sync();
+    __syncthreads();
   }
 
   if (robust) {
@@ -194,41 +220,56 @@ __device__ void topk_wave(const float* __restrict__ srow, const ReqGeom& geo, in
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = prefix | (1u << bit);
       int c = 0;
-      for (int j = 0; j < nbits; ++j)
-        c += ((act >> j) & 1ull) && score_key(sh.keys[j * kWave + lane]) >= cand;
-      if (wave_sum(c) >= need) prefix = cand;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) c += ((act >> j) & 1ull) && score_key(key[j]) >= cand;
+      c = wg_sum_i(sh, c, 2 + (bit & 1));   // alternating slots: one barrier per bit
+      if (c >= need) prefix = cand;
     }
     unsigned long long above = 0, equal = 0;
-    for (int j = 0; j < nbits; ++j) {
-      if ((act >> j) & 1ull) {
-        const uint32_t uk = score_key(sh.keys[j * kWave + lane]);
-        if (uk > prefix) above |= 1ull << j;
-        else if (uk == prefix) equal |= 1ull << j;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t uk = score_key(key[j]);
+      above |= (unsigned long long)(uk > prefix) << j;
+      equal |= (unsigned long long)(uk == prefix) << j;
+    }
+    above &= act;
+    equal &= act;
+    __syncthreads();
+    const int nabove = wg_sum_i(sh, __popcll(above), 0);
+    __syncthreads();
+    int tot;
+    int pos = wg_excl_scan_i(sh, __popcll(equal), 1, &tot);
+    const int fill = need - nabove;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if ((equal >> j) & 1ull) {
+        if (pos < fill) sel |= 1ull << j;
+        ++pos;
       }
     }
-    const int nabove = wave_sum(__popcll(above));
-    sel |= above | lowest_fill(equal, need - nabove, nbits, lane);
+    sel |= above;
+    __syncthreads();
   }
 
-  // emit: forced [0, c0), the chosen candidates, forced [c1, nb), ascending
-  const int nlow = geo.c0, nhigh = geo.nb - geo.c1;
-  int pos = nlow;
-  for (int j = 0; j < nbits; ++j) {
-    const bool b = (sel >> j) & 1ull;
-    const unsigned long long m = __ballot(b);
-    const int p = pos + lanes_below(m, lane);
-    if (b && p < max_selected) out[p] = geo.c0 + j * kWave + lane;
-    pos += __popcll(m);
+  // emit: forced [0, c0), the chosen candidates in order, forced [c1, nb)
+  int ncand;
+  int pos = geo.c0 + wg_excl_scan_i(sh, __popcll(sel), 2, &ncand);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if ((sel >> j) & 1ull) {
+      if (pos < max_selected) st_x<kDev>(&out[pos], geo.c0 + tid * PER + j);
+      ++pos;
+    }
   }
-  const int ncand = pos - nlow;
+  const int nlow = geo.c0, nhigh = geo.nb - geo.c1;
   const int total = nlow + ncand + nhigh;
-  for (int i = lane; i < nlow; i += kWave)
-    if (i < max_selected) out[i] = i;
-  for (int i = lane; i < nhigh; i += kWave)
-    if (nlow + ncand + i < max_selected) out[nlow + ncand + i] = geo.c1 + i;
-  for (int i = total + lane; i < max_selected; i += kWave) out[i] = -1;
-  if (lane == 0) *count_out = total < max_selected ? total : max_selected;
-  wave_lds_sync();
+  for (int i = tid; i < nlow; i += kTopkThreads)
+    if (i < max_selected) st_x<kDev>(&out[i], i);
+  for (int i = tid; i < nhigh; i += kTopkThreads)
+    if (nlow + ncand + i < max_selected) st_x<kDev>(&out[nlow + ncand + i], geo.c1 + i);
+  for (int i = total + tid; i < max_selected; i += kTopkThreads) st_x<kDev>(&out[i], -1);
+  if (tid == 0) st_x<kDev>(count_out, total < max_selected ? total : max_selected);
+  __syncthreads();
 }
 
 __device__ __forceinline__ int topk_budget(const TopkArgs& a, const ReqGeom& geo) {

@@ -7,11 +7,12 @@ namespace ls {
 template <int D, int HKV, int G>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   using S = ScoreShape<D, HKV, G>;
+  __shared__ ScoreLds<D, HKV, G> st[4];
   const int r = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const ReqGeom geo = req_geom(a.b, r, a.n_sink, a.n_recent);
   const int wb0 = (blockIdx.x * 4 + wave) * S::kBlocksPerWave;
-  score_wave<D, HKV, G>(a, r, geo, wb0, lane);
+  score_wave<D, HKV, G, false>(a, r, geo, wb0, lane, st[wave]);
 }
 
 template <int D, int HKV, int G>

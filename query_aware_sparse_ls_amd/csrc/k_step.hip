@@ -12,12 +12,13 @@
 //
 // Scheduling: requests are dealt to NQ work queues (request r -> queue
 // r % NQ). A queue's tasks, in ticket order, are: the score tasks of its
-// requests (16 blocks each), then their attention split tasks. Persistent
-// workgroups take tickets from their home queue (blockIdx.x % NQ) and move on
-// to the other queues when it runs dry.
-//  * score task (r, chunk): scores the chunk's candidate blocks; the LAST
-//    score task of request r to finish runs the request's top-k (one wave per
-//    kv head) and then publishes a ready flag per (r, kv head).
+// requests, then their top-k tasks, then their attention split tasks.
+// Persistent workgroups take tickets from their home queue (blockIdx.x % NQ)
+// and move on to the other queues when it runs dry.
+//  * score task (r, chunk): scores the chunk's candidate blocks and counts
+//    itself done for request r.
+//  * top-k task (r, g): waits until every score task of r is done, selects,
+//    and publishes a ready flag for (r, g).
 //  * attention task (r, g, split): waits for the (r, g) ready flag, then runs
 //    the split; the LAST split of (r, g) to finish merges the splits.
 // A task only ever waits for tasks with a smaller ticket in the same queue,
@@ -26,9 +27,12 @@
 // whether or not every workgroup is resident. Waits are bounded; a wait that
 // runs out sets an error word instead of hanging.
 //
-// Cross-workgroup hand-offs use agent-scope release/acquire (L2 write-back /
-// invalidate on gfx950). The control block (tickets and counters) must be
-// zero before the first launch; the last workgroup to exit zeroes it again.
+// Cross-workgroup hand-offs: the handed-over data (scores, selections, split
+// partials) is stored and loaded with device-coherent accesses (st_dev /
+// ld_dev); a producer waits for its stores to complete before the arrival
+// atomic that publishes them, so no whole-cache write-back or invalidate is
+// needed. The control block (tickets and counters) must be zero before the
+// first launch; the last workgroup to exit zeroes it again.
 #include "dev_attn.h"
 #include "dev_score.h"
 #include "dev_topk.h"
@@ -57,20 +61,19 @@ struct StepArgs {
   int score_tasks_per_req;   // chunks of kStepScoreBlocks
 };
 
-__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ unsigned int load_agent(const unsigned int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return ld_dev(p);
 }
 
 template <int D, int HKV, int G, int MAXC>
 union StepLds {
   AttnLds<D, G> attn;
-  WaveTopkLds<MAXC> topk[4];
+  TopkLds topk;
+  ScoreLds<D, HKV, G> score[4];
 };
 
 template <int D, int HKV, int G, int MAXC>
-__global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_step_kernel(StepArgs a) {
   using SS = ScoreShape<D, HKV, G>;
   constexpr int kChunk = 4 * SS::kBlocksPerWave;   // blocks per score task
   __shared__ StepLds<D, HKV, G, MAXC> sh;
@@ -85,7 +88,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a) {
     const int q = (home + qi) % kNQ;
     const int nreq = q < B ? (B - 1 - q) / kNQ + 1 : 0;
     const int n_score = nreq * a.score_tasks_per_req;
-    const int n_total = n_score + nreq * HKV * S;
+    const int n_topk = nreq * HKV;
+    const int n_total = n_score + n_topk + nreq * HKV * S;
     if (tid == 0) s_task = (int)atomicAdd(&a.ctl->ticket[q][0], 1u);
     __syncthreads();
     const int t = s_task;
@@ -99,33 +103,39 @@ __global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a) {
       const int r = q + (t / a.score_tasks_per_req) * kNQ;
       const int chunk = t % a.score_tasks_per_req;
       const ReqGeom geo = req_geom(a.sc.b, r, a.sc.n_sink, a.sc.n_recent);
-      score_wave<D, HKV, G>(a.sc, r, geo, chunk * kChunk + wave * SS::kBlocksPerWave, lane);
-      release_agent();
+      score_wave<D, HKV, G, true>(a.sc, r, geo, chunk * kChunk + wave * SS::kBlocksPerWave, lane,
+                                  sh.score[wave]);
+      wait_stores();
       __syncthreads();
+      if (tid == 0) atomicAdd(&a.score_done[r], 1u);
+    } else if (t < n_score + n_topk) {
+      // ----------------------------------------------------- top-k task
+      const int u = t - n_score;
+      const int r = q + (u / HKV) * kNQ;
+      const int g = u % HKV;
+      const int item = r * HKV + g;
       if (tid == 0) {
-        const unsigned int old = atomicAdd(&a.score_done[r], 1u);
-        s_flag = old == (unsigned int)(a.score_tasks_per_req - 1);
+        int spins = 0;
+        while (load_agent(&a.score_done[r]) < (unsigned int)a.score_tasks_per_req) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > kSpinLimit) {
+            atomicOr(&a.ctl->error, 1u);
+            break;
+          }
+        }
       }
       __syncthreads();
-      if (s_flag) {
-        // last score task of request r: its top-k, one wave per kv head
-        acquire_agent();
-        for (int g = wave; g < HKV; g += 4) {
-          const float* srow =
-              a.tk.scores + ((size_t)r * HKV + g) * a.tk.b.max_blocks + geo.c0;
-          const int item = r * HKV + g;
-          topk_wave<MAXC>(srow, geo, topk_budget(a.tk, geo),
-                          a.tk.selected + (size_t)item * a.tk.max_selected, a.tk.max_selected,
-                          a.tk.selected_count + item, sh.topk[wave], lane);
-          release_agent();
-          if (lane == 0) __hip_atomic_store(&a.ready[item], 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-      }
+      const ReqGeom geo = req_geom(a.tk.b, r, a.tk.n_sink, a.tk.n_recent);
+      const float* srow = a.tk.scores + (size_t)item * a.tk.b.max_blocks + geo.c0;
+      topk_wg<MAXC / kTopkThreads, true>(srow, geo, topk_budget(a.tk, geo),
+                                   a.tk.selected + (size_t)item * a.tk.max_selected,
+                                   a.tk.max_selected, a.tk.selected_count + item, sh.topk);
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) st_dev(&a.ready[item], 1u);
     } else {
       // ------------------------------------------------ attention task
-      const int u = t - n_score;
+      const int u = t - n_score - n_topk;
       const int r = q + (u / (HKV * S)) * kNQ;
       const int g = (u / S) % HKV;
       const int s = u % S;
@@ -141,13 +151,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a) {
         }
       }
       __syncthreads();
-      acquire_agent();
       const ReqGeom geo = req_geom(a.at.b, r, 0, 0);
-      const SelRow sr = sel_row(a.at, geo, r, g);
+      const SelRow sr = sel_row<true>(a.at, geo, r, g);
       const int lo = (int)(((long long)s * sr.cnt) / S);
       const int hi = (int)(((long long)(s + 1) * sr.cnt) / S);
-      attn_split<D, G, kAttnBlocksPerSplit>(a.at, geo, sr, r, g, s, lo, hi, sh.attn);
-      release_agent();      // every wave's partial stores, before the arrival below
+      attn_split<D, G, kAttnBlocksPerSplit, true>(a.at, geo, sr, r, g, s, lo, hi, sh.attn);
+      wait_stores();        // every wave's partial stores, before the arrival below
       __syncthreads();
       if (tid == 0) {
         const unsigned int old = atomicAdd(&a.attn_done[item], 1u);
@@ -155,8 +164,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a) {
       }
       __syncthreads();
       if (s_flag) {
-        acquire_agent();
-        combine_head<D>(a.at, r * a.at.num_q_heads + g * G + wave, lane);   // G = 4 waves
+        combine_head<D, true>(a.at, r * a.at.num_q_heads + g * G + wave, lane);   // G = 4 waves
         __syncthreads();
       }
     }
@@ -165,18 +173,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a) {
   // the last workgroup out zeroes the control block for the next launch
   __syncthreads();
   if (tid == 0) {
-    release_agent();
     const unsigned int old = atomicAdd(&a.ctl->exited, 1u);
     s_flag = old == gridDim.x - 1;
   }
   __syncthreads();
   if (s_flag) {
-    acquire_agent();
-    for (int i = tid; i < kNQ; i += 256) a.ctl->ticket[i][0] = 0u;
-    for (int i = tid; i < B; i += 256) a.score_done[i] = 0u;
-    for (int i = tid; i < B * HKV; i += 256) { a.ready[i] = 0u; a.attn_done[i] = 0u; }
-    if (tid == 0) a.ctl->exited = 0u;
-    release_agent();
+    for (int i = tid; i < kNQ; i += 256) st_dev(&a.ctl->ticket[i][0], 0u);
+    for (int i = tid; i < B; i += 256) st_dev(&a.score_done[i], 0u);
+    for (int i = tid; i < B * HKV; i += 256) { st_dev(&a.ready[i], 0u); st_dev(&a.attn_done[i], 0u); }
+    if (tid == 0) st_dev(&a.ctl->exited, 0u);
   }
 }
 
@@ -212,7 +217,7 @@ static hipError_t launch_step_t(const StepLaunch& L, hipStream_t st) {
   a.ready = words + B;
   a.attn_done = words + B + B * HKV;
   a.score_tasks_per_req = (L.sc.b.max_blocks + 4 * SS::kBlocksPerWave - 1) / (4 * SS::kBlocksPerWave);
-  const long long tasks = (long long)B * (a.score_tasks_per_req + HKV * L.at.num_splits);
+  const long long tasks = (long long)B * (a.score_tasks_per_req + HKV + HKV * L.at.num_splits);
   long long grid = (long long)per_cu * cus;
   if (grid > tasks) grid = tasks;
   if (grid < 1) grid = 1;

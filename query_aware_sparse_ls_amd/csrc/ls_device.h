@@ -122,6 +122,46 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------- low-latency wave reductions
+// Float min / max over the 64 lanes: DPP inside each 16-lane row, then the
+// four row results read into scalars (no LDS-crossbar permutes).
+__device__ __forceinline__ float rl_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ float wave_max_fast(float v) {
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
+  return fmaxf(fmaxf(rl_f(v, 0), rl_f(v, 16)), fmaxf(rl_f(v, 32), rl_f(v, 48)));
+}
+__device__ __forceinline__ float wave_min_fast(float v) {
+  v = fminf(v, dpp_mov<kDppXor1>(v));
+  v = fminf(v, dpp_mov<kDppXor2>(v));
+  v = fminf(v, dpp_mov<kDppRowHalfMirror>(v));
+  v = fminf(v, dpp_mov<kDppRowMirror>(v));
+  return fminf(fminf(rl_f(v, 0), rl_f(v, 16)), fminf(rl_f(v, 32), rl_f(v, 48)));
+}
+
+// Number of set bits of the wave mask m in lanes below this one.
+__device__ __forceinline__ int mbcnt(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+}
+// Exclusive prefix sum and total of small non-negative ints (< 2^BITS) over
+// the wave, by bit planes: one ballot and one masked count per bit.
+template <int BITS>
+__device__ __forceinline__ int wave_excl_scan_small(int v, int* total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const unsigned long long m = __ballot((v >> b) & 1);
+    pre += mbcnt(m) << b;
+    tot += __popcll(m) << b;
+  }
+  *total = tot;
+  return pre;
+}
+
 // Order LDS traffic of one wavefront: every LDS access issued before this
 // point has completed before any issued after it (wave-synchronous code).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -140,6 +180,39 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------ device-coherent access ----
+// Data handed from one workgroup to another inside a kernel (scores,
+// selections, split partials) is written and read with agent-scope
+// (device-coherent) accesses, which bypass the per-XCD L2 instead of
+// requiring whole-cache write-back / invalidate fences.
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Plain or device-coherent, chosen at compile time: kernels that hand data to
+// other workgroups of the SAME launch use the coherent form; kernels whose
+// consumer is a later launch use plain (cached) accesses.
+template <bool kDev, typename T>
+__device__ __forceinline__ void st_x(T* p, T v) {
+  if constexpr (kDev) st_dev(p, v); else *p = v;
+}
+template <bool kDev, typename T>
+__device__ __forceinline__ T ld_x(const T* p) {
+  if constexpr (kDev) return ld_dev(p); else return *p;
+}
+
+// Wait until every store this wave issued has completed (vmcnt(0)), and keep
+// the compiler from moving memory operations across the wait.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0), expcnt/lgkmcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // 16-byte global load through the vector memory path.

@@ -83,7 +83,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
 // Blocks per attention split (one register-resident chunk per workgroup).
-constexpr int kAttnBlocksPerSplit = 4;
+constexpr int kAttnBlocksPerSplit = 8;
 
 // Request geometry on the device: blocks, complete blocks, and the candidate
 // range [c0, c1) = complete blocks that are neither sink nor recent. The

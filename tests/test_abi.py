@@ -123,7 +123,7 @@ def test_attention_validation():
     assert call(batch=_batch(batch_size=0)) == _lib.LS_OK
     need = lib.ls_sparse_attn_decode_workspace_size(2, 32, 128, 8, 4)
     assert need >= 2 * 32 * lib.ls_attn_num_splits(8) * 130 * 4
-    assert lib.ls_attn_num_splits(67) == 17 and lib.ls_attn_num_splits(2048) == 512
+    assert lib.ls_attn_num_splits(67) == 9 and lib.ls_attn_num_splits(2048) == 256
 
 
 def test_summaries_validation():
