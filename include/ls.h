@@ -197,10 +197,15 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
  *   z_t = sm_scale * sum_d q[r][h][d] * K[t][d],
  *   out[r][h][:] = sum_t e^{z_t - M} V[t][:] / sum_t e^{z_t - M}, M = max z,
  *   lse_out[r][h] = M + ln sum_t e^{z_t - M}
- * with fp32 logits, softmax and accumulation; the work is split over the
- * selected blocks and the partial results are merged by log-sum-exp in a
- * fixed order (deterministic). An empty T gives out = 0 and lse = -inf.
- * The output is rounded once (nearest-even) to out_dtype.
+ * with fp32 logits, softmax and accumulation; partial softmax states over
+ * disjoint token sets are merged by log-sum-exp in a fixed order
+ * (deterministic). With at least 64 (request, kv head) pairs one workgroup
+ * owns each pair and merges on chip; with fewer, the selected blocks are
+ * split over several workgroups whose partial results go through the
+ * workspace and are merged by a second kernel. An empty T gives out = 0 and
+ * lse = -inf. The output is rounded once (nearest-even) to out_dtype.
+ * For a selection written by ls_score_select the entries past the count are
+ * -1; other callers may leave them undefined (they are never read as blocks).
  *
  * q:              [batch][num_q_heads][head_dim] bf16.
  * k_pool, v_pool: K and V pools, layout HND, geometry `pool` (bf16).
@@ -230,31 +235,29 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
-/* 4. The whole step in one launch                                           */
+/* 4. The whole step                                                        */
 /* ------------------------------------------------------------------------ */
 /*
  * ls_score_select followed by ls_sparse_attn_decode (same definitions, same
- * results bit for bit up to the order of split merges, which is fixed), run
- * as ONE persistent kernel so that the selection and attention of one request
- * overlap the scoring of the others (the Vortex post fuses operators of a
- * step and balances workgroups across requests, "Making it fast").
+ * results bit for bit: both take the same kernel path for the same shapes).
+ * With at least 64 (request, kv head) pairs (and max_blocks <= 8192) the
+ * step is ONE launch in which one workgroup owns a
+ * pair from scoring to output: its scores, top-k and selection stay on chip
+ * and its attention merge happens on chip, so no intermediate result goes
+ * through memory and no workgroup waits for another (the Vortex post fuses
+ * the operators of a decode step, "Making it fast"). Otherwise it runs the
+ * split kernels of the two calls back to back.
  *
  * Arguments: as ls_score_select (q, summaries, batch, p, selected,
  * selected_count) and ls_sparse_attn_decode (k_pool, v_pool with geometry
  * `pool`, sm_scale, out, out_dtype, lse_out); the summary pool shares the
  * K/V pool's num_pages, num_heads and head_dim.
  * workspace: >= ls_sparse_decode_step_workspace_size() bytes, 256-byte
- *   aligned. Its first ls_sparse_decode_step_control_bytes() bytes are a
- *   control block that MUST be zero before the first call; every call that
- *   runs to completion leaves it zero again, so a workspace zeroed once can be
- *   reused by later calls on the same stream (concurrent calls need separate
- *   workspaces). The rest need not be initialised.
- * Supported: head_dim 64 or 128; num_kv_heads 2, 4 or 8; GQA group 4;
- *   page_size 16; max_blocks <= 4096 (otherwise LS_ERR_UNSUPPORTED: use the
- *   two separate calls).
+ *   aligned, need not be initialised (block scores and split partials of the
+ *   split path; calls that run concurrently need separate workspaces).
+ * Supported: head_dim 64 or 128; GQA group 4; page_size 16;
+ *   max_blocks <= 16384.
  */
-size_t ls_sparse_decode_step_control_bytes(int32_t batch_size, int32_t num_kv_heads);
-
 size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_heads,
                                             int32_t num_kv_heads, int32_t head_dim,
                                             int32_t max_blocks, int32_t max_selected);

@@ -195,11 +195,10 @@ def sparse_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
 def sparse_decode_step_workspace(batch_size: int, num_q_heads: int, num_kv_heads: int,
                                  head_dim: int, max_blocks: int, max_selected: int,
                                  device) -> torch.Tensor:
-    """A workspace for sparse_decode_step, zero-filled (its control block must
-    start at zero; each completed call leaves it zero for the next)."""
+    """A workspace for sparse_decode_step (need not be initialised)."""
     n = int(_L.ls_sparse_decode_step_workspace_size(batch_size, num_q_heads, num_kv_heads,
                                                    head_dim, max_blocks, max_selected))
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.Tensor,
@@ -211,8 +210,9 @@ def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.T
                        out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
                        lse: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, stream=None):
-    """score_select + sparse_attn_decode in one persistent launch.
-    Returns (out, lse, selected, selected_count)."""
+    """score_select + sparse_attn_decode as one call (one launch when there
+    are at least 64 (request, kv head) pairs). Returns (out, lse, selected,
+    selected_count)."""
     _need(q, torch.bfloat16); _need(summaries, torch.bfloat16)
     _need(k_pool, torch.bfloat16); _need(v_pool, torch.bfloat16)
     B, Hq, D = q.shape

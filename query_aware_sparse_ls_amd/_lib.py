@@ -43,7 +43,6 @@ _SIGS = {
     "ls_sparse_attn_decode": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, LsPool, LsBatch, _P,
                                         _P, C.c_int32, C.c_float, _P, C.c_int32, _P, _P,
                                         C.c_size_t, _P]),
-    "ls_sparse_decode_step_control_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
     "ls_sparse_decode_step_workspace_size": (C.c_size_t, [C.c_int32] * 6),
     "ls_sparse_decode_step": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, LsPool, LsBatch,
                                         C.POINTER(LsSelectParams), _P, _P, C.c_float, _P,

@@ -8,20 +8,16 @@
 // KV-Cache Sparsity Cross in LLM Decoding", App. A) applies to attention over
 // disjoint token sets.
 //
-// A split is a contiguous, balanced slice of at most CH selected blocks of one
-// (request, kv head). A (page, head) tile is page_size x D contiguous bf16.
+// A split is the run of at most CH consecutive positions of one (request, kv
+// head) selection row. A (page, head) tile is page_size x D contiguous bf16.
 // Thread t owns 8 dims of one token row of every block of the split; a wave
-// instruction reads 1 KB contiguous and the workgroup a whole 4 KB tile. The
-// selection entries and page ids are loaded first (two short hops), then every
-// K and V load of the split is issued before any is used. There is no reuse of
-// K/V across threads, so the data goes straight to registers; LDS only merges
-// the per-row softmax states at the end.
+// instruction reads 1 KB contiguous and the workgroup a whole 4 KB tile. All
+// K and V loads of the split are issued before any is used; there is no reuse
+// of K/V across threads, so the data goes straight to registers.
 //
 // Each group of D/8 lanes owns one token row: the G query heads' logits are
-// v_dot2 partial sums summed over those lanes with DPP adds, and each lane
-// keeps a private softmax state (max m, sum l, o over its 8 dims) per head in
-// the log2 domain (logits pre-scaled by sm_scale * log2 e, so each
-// exponential is one exp2).
+// v_dot2 partial sums summed over those lanes with DPP adds, pre-scaled by
+// sm_scale * log2 e so that each exponential is one exp2.
 #pragma once
 
 #include "ls_internal.h"
@@ -42,9 +38,9 @@ struct AttnShape {
 
 template <int D, int G>
 struct AttnLds {
-  float acc[AttnShape<D, G>::ROWS][G][D];
-  float m[AttnShape<D, G>::ROWS][G];
-  float l[AttnShape<D, G>::ROWS][G];
+  float acc[4][G][D];   // per-wave sums
+  float m[4][G];
+  float l[4][G];
 };
 
 __device__ __forceinline__ float dot8(const uint32_t* q, uint4 s, float acc) {
@@ -59,73 +55,71 @@ __device__ __forceinline__ float dot8(const uint32_t* q, uint4 s, float acc) {
   return acc;
 }
 
-// Number of selected entries of (r, g) and its row of the selection.
-struct SelRow {
-  int cnt;
-  const int32_t* row;
-};
-
-template <bool kDev>
-__device__ __forceinline__ SelRow sel_row(const AttnArgs& a, const ReqGeom& geo, int r, int g) {
-  SelRow s;
-  s.cnt = geo.nb;
-  s.row = nullptr;
-  if (a.selected) {
-    int c = ld_x<kDev>(&a.selected_count[(size_t)r * a.num_kv_heads + g]);
-    s.cnt = c < 0 ? 0 : (c > a.max_selected ? a.max_selected : c);
-    s.row = a.selected + ((size_t)r * a.num_kv_heads + g) * a.max_selected;
-  }
-  return s;
-}
-
-// Attention of kv group g of request r over selection entries [lo, hi)
-// (hi - lo <= CH), written as split `s` of the partial buffer:
-// partials[r][g*G + h][s][0..D-1] = unnormalised o, [D] = m (log2 domain),
-// [D+1] = l. Must be called by all 256 threads of the workgroup.
+// Attention of kv group g of request r over the entries of split s: the
+// positions [s*CH, s*CH + CH) of the (r, g) selection row (of the block list
+// itself on the dense path), written as split s of the partial buffer:
+// partials[r][g*G + h][s][0..D-1] = o relative to the split maximum m,
+// [D] = m (log2 domain), [D+1] = l. Must be called by all 256 threads.
+//
+// Memory hops: (1) q, the selection count and the split's selection entries,
+// all independent; (2) the page table; (3) K and V of every entry, all issued
+// before any is used.
+//
+// Softmax: one maximum per head over the whole split (lane, DPP within the
+// wave, LDS across the 4 waves), then p = 2^(z - m) and the sums over rows by
+// lane-pair exchanges within a wave and LDS across waves, in a fixed order.
 template <int D, int G, int CH, bool kDev>
-__device__ __forceinline__ void attn_split(const AttnArgs& a, const ReqGeom& geo, const SelRow& sr,
-                                           int r, int g, int s, int lo, int hi,
-                                           AttnLds<D, G>& sh) {
+__device__ __forceinline__ void attn_split(const AttnArgs& a, const ReqGeom& geo, int r, int g,
+                                           int s, AttnLds<D, G>& sh) {
   using S = AttnShape<D, G>;
-  constexpr int P = S::P, LPR = S::LPR, RPW = S::RPW, ROWS = S::ROWS, BPR = S::BPR;
-  constexpr int NR = (CH + BPR - 1) / BPR;  // rounds
+  constexpr int P = S::P, LPR = S::LPR, RPW = S::RPW, BPR = S::BPR;
+  static_assert(CH % BPR == 0, "split length must be whole rounds");
+  constexpr int NR = CH / BPR;  // rounds: one block per BPR rows
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row = wave * RPW + lane / LPR;
   const int c = lane % LPR;
   const int bir = row / P, slot = row % P;
   const int HKV = a.num_kv_heads;
+  const size_t item = (size_t)r * HKV + g;
 
+  // hop 1
   uint32_t qv[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const uint4 t = ldg16(a.q + ((size_t)r * a.num_q_heads + g * G + h) * D + c * 8);
     qv[h][0] = t.x; qv[h][1] = t.y; qv[h][2] = t.z; qv[h][3] = t.w;
   }
-  const int32_t* pages = a.b.indices + geo.page_base;
+  const bool sparse = a.selected != nullptr;
+  const int npos = sparse ? a.max_selected : geo.nb;   // positions that exist
+  int cnt = sparse ? ld_x<kDev>(&a.selected_count[item]) : geo.nb;
+  const int32_t* srow = sparse ? a.selected + item * a.max_selected : nullptr;
   int blk[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    const int idx = lo + i * BPR + bir;
-    blk[i] = idx < hi ? (sr.row ? ld_x<kDev>(&sr.row[idx]) : idx) : -1;
+    const int pos = s * CH + i * BPR + bir;
+    blk[i] = pos < npos ? (sparse ? ld_x<kDev>(&srow[pos]) : pos) : -1;
   }
-  int page[NR];
+  cnt = cnt < 0 ? 0 : (cnt > npos ? npos : cnt);
   bool ok[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
+    const int pos = s * CH + i * BPR + bir;
     const int b = blk[i];
-    bool v = b >= 0 && b < geo.nb && b * P + slot < geo.L;
-    page[i] = v ? pages[b] : 0;
+    ok[i] = pos < cnt && b >= 0 && b < geo.nb && b * P + slot < geo.L;
   }
+  // hop 2: page table
+  const int32_t* pages = a.b.indices + geo.page_base;
+  int page[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) page[i] = ok[i] ? pages[blk[i]] : -1;
+  // hop 3
   uint4 kr[NR], vr[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    const int b = blk[i];
-    bool v = b >= 0 && b < geo.nb && b * P + slot < geo.L && page[i] >= 0 &&
-             page[i] < a.b.num_pages;
-    ok[i] = v;
-    const size_t off = (((size_t)page[i] * HKV + g) * P + slot) * D + c * 8;
-    kr[i] = v ? ldg16(a.k_pool + off) : make_uint4(0, 0, 0, 0);
-    vr[i] = v ? ldg16(a.v_pool + off) : make_uint4(0, 0, 0, 0);
+    ok[i] = ok[i] && page[i] >= 0 && page[i] < a.b.num_pages;
+    const size_t off = (((size_t)(ok[i] ? page[i] : 0) * HKV + g) * P + slot) * D + c * 8;
+    kr[i] = ok[i] ? ldg16(a.k_pool + off) : make_uint4(0, 0, 0, 0);
+    vr[i] = ok[i] ? ldg16(a.v_pool + off) : make_uint4(0, 0, 0, 0);
   }
 
   float z[NR][G];
@@ -135,20 +129,30 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, const ReqGeom& geo
     for (int h = 0; h < G; ++h)
       z[i][h] = ok[i] ? group_sum<LPR>(dot8(qv[h], kr[i], 0.0f)) * a.sm_scale_log2 : kNegInf;
   }
-  float m[G], l[G], acc[G][8];
+  // split maximum per head
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float mx = kNegInf;
 #pragma unroll
     for (int i = 0; i < NR; ++i) mx = fmaxf(mx, z[i][h]);
-    m[h] = mx;
+    mx = wave_max_fast(mx);
+    if (lane == 0) sh.m[wave][h] = mx;
+  }
+  __syncthreads();
+  float M[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    M[h] = fmaxf(fmaxf(sh.m[0][h], sh.m[1][h]), fmaxf(sh.m[2][h], sh.m[3][h]));
+  float l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
     l[h] = 0.0f;
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[h][d] = 0.0f;
-    if (mx != kNegInf) {
+    if (M[h] != kNegInf) {
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
-        const float p = ok[i] ? exp2f(z[i][h] - mx) : 0.0f;
+        const float p = ok[i] ? exp2f(z[i][h] - M[h]) : 0.0f;
         l[h] += p;
         const uint4 v = vr[i];
         acc[h][0] += p * bf16_lo(v.x); acc[h][1] += p * bf16_hi(v.x);
@@ -158,34 +162,41 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, const ReqGeom& geo
       }
     }
   }
-
+  // sum over the RPW rows of the wave (lanes that differ in the row bits),
+  // by lane-pair exchanges in a fixed order
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float4* dst = reinterpret_cast<float4*>(&sh.acc[row][h][c * 8]);
-    dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-    dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    if (c == 0) { sh.m[row][h] = m[h]; sh.l[row][h] = l[h]; }
+    if constexpr (LPR <= 8) {
+      l[h] = xor_pair_sum<8>(l[h]);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[h][d] = xor_pair_sum<8>(acc[h][d]);
+    }
+    l[h] = xor_pair_sum<32>(xor_pair_sum<16>(l[h]));
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[h][d] = xor_pair_sum<32>(xor_pair_sum<16>(acc[h][d]));
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float4* dst = reinterpret_cast<float4*>(&sh.acc[wave][h][c * 8]);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      if (c == 0) sh.l[wave][h] = l[h];
+    }
   }
   __syncthreads();
   const int S_ = a.num_splits;
   float* part = a.partials + (((size_t)r * a.num_q_heads + g * G) * S_ + s) * (D + 2);
   for (int o = tid; o < G * D; o += 256) {
     const int h = o / D, d = o % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < ROWS; ++w) M = fmaxf(M, sh.m[w][h]);
-    float O = 0.0f, Ls = 0.0f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < ROWS; ++w) {
-        const float e = exp2f(sh.m[w][h] - M);  // rows with m = -inf give 0
-        O += e * sh.acc[w][h][d];
-        Ls += e * sh.l[w][h];
-      }
-    }
+    const float O = ((sh.acc[0][h][d] + sh.acc[1][h][d]) + sh.acc[2][h][d]) + sh.acc[3][h][d];
     float* ph = part + (size_t)h * S_ * (D + 2);
     st_x<kDev>(&ph[d], O);
-    if (d == 0) { st_x<kDev>(&ph[D], M); st_x<kDev>(&ph[D + 1], Ls); }
+    if (d == 0) {
+      const float Ls = ((sh.l[0][h] + sh.l[1][h]) + sh.l[2][h]) + sh.l[3][h];
+      st_x<kDev>(&ph[D], M[h]);
+      st_x<kDev>(&ph[D + 1], Ls);
+    }
   }
   __syncthreads();
 }

@@ -1,0 +1,440 @@
+// Per-(request, kv head) workgroup code: ONE 512-thread workgroup owns a whole
+// (request r, kv head g) pair and runs its steps back to back -- block scoring
+// into LDS, top-k from LDS, attention over the selection with the merge of
+// all partial softmax states in LDS. Nothing is handed between workgroups, so
+// there are no split partials, arrival counters or extra launches.
+//
+// Both contractions run on the matrix cores (v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x16_bf16). For a 16-row tile of keys K (summary rows or the
+// 16 tokens of a block) and the GQA group's G = 4 query heads, the product
+// K . Q^T is a 16 x 16 MFMA whose 16 columns are the query heads, zero-padded
+// from 4; the vector ALU alone cannot keep up with HBM here (about 50 VALU
+// wave-instructions per 512 bytes of K and V at G = 4, against the ~10 bytes
+// per wave-instruction the chip's VALU rate allows at full bandwidth).
+//  * K operand: lane i holds row i%16, dims [32j + 8(i/16), +8) of k-step j.
+//    Rows are loaded from memory in the plain row-major order instead (each
+//    wave load instruction reads 1 KB contiguous: whole 128-byte lines), and
+//    reach the operand layout through a padded LDS tile per wave: loading the
+//    operand layout directly (16 rows x 64 B per instruction) measured about
+//    1.6x slower on this chip, and worse the more loads are in flight.
+//  * Q^T operand: lane i holds q[head i%16][the same dims] (0 for head >= 4).
+//  * Output: lane i holds head i%16 for rows 4(i/16) .. 4(i/16)+3.
+// The attention output P . V is a 16 x 16 x 16 MFMA per 16 output dims with P
+// (heads x tokens) in exactly that output layout, and V (tokens x dims) as
+// the B operand: lane i needs 4 tokens of one dim, a column of the row-major
+// V tile, read from the wave's LDS copy of the tile (rows padded so the
+// column reads hit 32 distinct banks). P is split into bf16 parts, p = hi + lo (+ lo2
+// for fp32 output), so the products keep fp32-level accuracy.
+#pragma once
+
+#include "dev_attn.h"
+#include "dev_score.h"
+#include "dev_topk.h"
+
+namespace ls {
+
+constexpr int kItemThreads = 512;
+constexpr int kItemWaves = kItemThreads / kWave;
+constexpr int kItemScorePrefetch = 6;   // summary tiles in flight per wave
+constexpr int kItemPrefetch = 4;        // K/V blocks in flight per wave
+// Walk entries past the selection that item_attn may read: wave w refills
+// its slots with position w + 8(k + kItemPrefetch) for k < nbw + kItemPrefetch
+// - 1, nbw = ceil((cnt - w) / 8), i.e. at most cnt + 7 + 8(2 kItemPrefetch - 2).
+constexpr int kItemEntryPad = kItemWaves * 2 * kItemPrefetch;
+static_assert(kItemEntryPad >= 7 + kItemWaves * (2 * kItemPrefetch - 2) + 1, "entry padding");
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_16x16x16(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+// Q^T as the B operand of the D/32 k-steps of a 16x16x32 MFMA (G = 4 heads).
+template <int D>
+struct QOperand {
+  uint4 b[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ QOperand<D> load_q_operand(const uint16_t* q, int num_q_heads, int r,
+                                                      int g) {
+  const int lane = threadIdx.x & 63, h = lane & 15, kq = lane >> 4;
+  QOperand<D> o;
+  const uint16_t* qh = q + ((size_t)r * num_q_heads + g * 4 + (h < 4 ? h : 0)) * D + 8 * kq;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) o.b[j] = h < 4 ? ldg16(qh + 32 * j) : make_uint4(0, 0, 0, 0);
+  return o;
+}
+
+// Page ids of blocks [0, nb) of request r into pg[] (LDS); the caller
+// synchronises before use. One coalesced pass over the page-table row.
+__device__ __forceinline__ void load_page_row(const BatchArgs& b, const ReqGeom& geo, int* pg) {
+  for (int i = threadIdx.x; i < geo.nb; i += kItemThreads) pg[i] = b.indices[geo.page_base + i];
+}
+
+// Row-major staging of a 16 x D bf16 tile: lane i loads rows j*RPI + i/LPR,
+// 16 bytes at dims 8(i%LPR) (LPR = D/8 lanes per row, RPI = 64/LPR rows per
+// instruction, D/32 instructions for 16 rows).
+template <int D>
+struct Stage {
+  static constexpr int LPR = D / 8, RPI = kWave / LPR, NL = D / 32;
+  static constexpr int kKRowWords = D / 2 + 4;   // K tile rows: 16-byte aligned, padded
+  static constexpr int kVRowWords = D / 2 + 2;   // V tile rows: column reads hit 32 banks
+};
+
+// Writes this lane's NL row chunks into a K-style LDS tile (row stride
+// kKRowWords words); zero = write zeros instead.
+template <int D>
+__device__ __forceinline__ void stage_k(uint32_t* tile, const uint4* d, uint32_t zero_mask) {
+  using S = Stage<D>;
+  const int lane = threadIdx.x & 63;
+  uint32_t* dst = tile + (lane / S::LPR) * S::kKRowWords + 4 * (lane % S::LPR);
+  if (__ballot(zero_mask != 0u) == 0) {   // the common case: nothing to clear
+#pragma unroll
+    for (int j = 0; j < S::NL; ++j)
+      *reinterpret_cast<uint4*>(dst + j * S::RPI * S::kKRowWords) = d[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < S::NL; ++j)
+      *reinterpret_cast<uint4*>(dst + j * S::RPI * S::kKRowWords) =
+          ((zero_mask >> j) & 1u) ? make_uint4(0, 0, 0, 0) : d[j];
+  }
+}
+
+// The MFMA A operand of k-step j from a K-style LDS tile: row i%16, dims
+// [32j + 8(i/16), +8).
+template <int D>
+__device__ __forceinline__ uint4 k_operand(const uint32_t* tile, int j) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const uint4*>(tile + (lane & 15) * Stage<D>::kKRowWords + 16 * j +
+                                         4 * (lane >> 4));
+}
+
+// s[b] for every candidate block b in [c0, c1) of (r, g) into sc[] (LDS), from
+// the page ids in pg[] (LDS). Tile t = summary rows of blocks [16t, 16t+16);
+// wave w scores tiles w, w + 8, ... of the candidate range, keeping
+// kItemScorePrefetch tiles of loads in flight (each slot is refilled right
+// after its use; every load is issued -- a row outside the candidates reads
+// page 0 and is discarded -- so the number in flight is fixed). A candidate
+// whose page id is out of range scores 0.
+template <int D, int MAXC>
+__device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, const ReqGeom& geo,
+                                           const int* pg, float* sc, uint32_t* stage) {
+  using ST = Stage<D>;
+  constexpr int KS = D / 32, NL = ST::NL, NS = kItemScorePrefetch;
+  static_assert(NS % 2 == 0, "slots are consumed in pairs");
+  const int HKV = a.num_kv_heads;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int row = lane & 15, kq = lane >> 4;
+  const QOperand<D> qo = load_q_operand<D>(a.q, a.num_q_heads, r, g);
+  const uint16_t* base = a.summaries + (size_t)g * D + 8 * (lane % ST::LPR);
+  const uint32_t pstride = (uint32_t)HKV * D;   // elements per page (< 2^32)
+  uint32_t* tiles = stage + wave * 2 * 16 * ST::kKRowWords;   // two tiles per wave
+  const int t0 = geo.c0 / 16, t1 = (geo.c1 + 15) / 16;
+  const int ntw = t1 - t0 > wave ? (t1 - t0 - wave + kItemWaves - 1) / kItemWaves : 0;
+  // page of the row this lane loads with instruction j of the wave's k-th
+  // tile: -1 if not a candidate, -2 for a candidate with a bad page id
+  auto page_of = [&](int k, int j) {
+    const int b = (t0 + wave + kItemWaves * k) * 16 + j * ST::RPI + lane / ST::LPR;
+    if (k >= ntw || b < geo.c0 || b >= geo.c1) return -1;
+    const int p = pg[b < MAXC ? b : MAXC - 1];
+    return (p >= 0 && p < a.b.num_pages) ? p : -2;
+  };
+  auto issue = [&](int k, uint4* d, uint32_t& badm) {
+    badm = 0;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int p = page_of(k, j);
+      badm |= (uint32_t)(p == -2) << j;
+      d[j] = ldg16(base + (uint64_t)(uint32_t)(p >= 0 ? p : 0) * pstride);
+    }
+  };
+  // score the staged tile and store the candidate rows (tiles past the
+  // wave's range hold page-0 rows and store nothing)
+  auto finish = [&](const f32x4_t& acc, int k) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = acc[i];
+      if (a.group_agg == LS_AGG_MEAN) {
+        x += dpp_mov<kDppXor1>(x);
+        x += dpp_mov<kDppXor2>(x);
+        x *= 0.25f;
+      } else {
+        x = fmaxf(x, dpp_mov<kDppXor1>(x));
+        x = fmaxf(x, dpp_mov<kDppXor2>(x));
+      }
+      v[i] = x;
+    }
+    if (row == 0) {
+      const int tb = (t0 + wave + kItemWaves * k) * 16 + 4 * kq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tb + i >= geo.c0 && tb + i < geo.c1) sc[tb + i] = v[i];
+    }
+  };
+  uint4 buf[NS][NL];
+  uint32_t badm[NS];   // per slot: bit j = this lane's row of instruction j has a bad page
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    issue(s, buf[s], badm[s]);
+    __builtin_amdgcn_sched_barrier(0);   // issue the slots in order (oldest = slot 0)
+  }
+  for (int k0 = 0; k0 < ntw; k0 += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; s += 2) {
+      // take two slots' rows and refill both at once; the two tiles are then
+      // scored as independent chains, so their LDS and MFMA latencies overlap
+      uint4 c0[NL], c1[NL];
+      const uint32_t b0 = badm[s], b1 = badm[s + 1];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) { c0[j] = buf[s][j]; c1[j] = buf[s + 1][j]; }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(k0 + s + NS, buf[s], badm[s]);
+      issue(k0 + s + 1 + NS, buf[s + 1], badm[s + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t* ta = tiles;
+      uint32_t* tb = tiles + 16 * ST::kKRowWords;
+      stage_k<D>(ta, c0, b0);   // rows with a bad page score 0
+      stage_k<D>(tb, c1, b1);
+      f32x4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        acc0 = mfma_16x16x32(k_operand<D>(ta, j), qo.b[j], acc0);
+        acc1 = mfma_16x16x32(k_operand<D>(tb, j), qo.b[j], acc1);
+      }
+      // acc[i] = q_h . k of tile row 4kq + i, head h = lane%16; aggregate
+      // the group's heads 0..3 (the first quad of each 16-lane row)
+      finish(acc0, k0 + s);
+      finish(acc1, k0 + s + 1);
+    }
+  }
+}
+
+// LDS of the attention: per-wave V staging tiles and the wave states.
+template <int D>
+struct alignas(16) ItemAttnLds {   // 16-byte aligned: the tiles take 16-byte LDS accesses
+  alignas(16) uint32_t k[kItemWaves][16 * Stage<D>::kKRowWords];
+  alignas(16) uint32_t v[kItemWaves][16 * Stage<D>::kVRowWords];
+  float acc[kItemWaves][4][D];
+  float m[kItemWaves][4];
+  float l[kItemWaves][4];
+};
+
+// Rewrites the selection sel[0 .. npad) (LDS) in place into walk entries:
+// e = page * 32 + (valid tokens of the block) for positions < cnt whose block
+// and page are valid, -1 otherwise. Requires num_pages < 2^26.
+__device__ __forceinline__ void item_entries(const AttnArgs& a, const ReqGeom& geo, int* sel,
+                                             int cnt, const int* pg, int npad) {
+  for (int pos = threadIdx.x; pos < npad; pos += kItemThreads) {
+    int e = -1;
+    if (pos < cnt) {
+      const int blk = sel[pos];
+      if (blk >= 0 && blk < geo.nb) {
+        const int p = pg[blk];
+        const int nt = geo.L - blk * 16 < 16 ? geo.L - blk * 16 : 16;
+        if (p >= 0 && p < a.b.num_pages && nt > 0) e = p * 32 + nt;
+      }
+    }
+    sel[pos] = e;
+  }
+}
+
+// Number of walk entries item_attn reads for a selection of cnt blocks.
+__device__ __forceinline__ int item_entry_count(int cnt) { return cnt + kItemEntryPad; }
+
+// bf16 bits of x rounded to nearest even; *rest = x - that value.
+__device__ __forceinline__ uint32_t bf16_split(float x, float* rest) {
+  const uint32_t b = f32_to_bf16_rne(x);
+  *rest = x - __uint_as_float(b << 16);
+  return b;
+}
+
+// Attention of the G = 4 query heads of (r, g) over the walk entries ent[]
+// (LDS, from item_entries; cnt = selection size), written as out / lse.
+// Wave w takes selection positions w, w + 8, ...; per block it computes the
+// 16 x 4 logits with D/32 MFMAs, updates its per-head softmax state (max m,
+// sum l; the o accumulator is rescaled only when a head's max grows), and
+// adds P . V with D/16 MFMAs per bf16 part of P. Blocks are prefetched
+// kItemPrefetch ahead per wave. The 8 wave states are merged in LDS in wave
+// order.
+template <int D>
+__device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const int* ent,
+                                          int cnt, ItemAttnLds<D>& sh) {
+  using ST = Stage<D>;
+  constexpr int KS = D / 32, NL = ST::NL, NT = D / 16, NPF = kItemPrefetch;
+  constexpr int RW = ST::kVRowWords;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int row = lane & 15, kq = lane >> 4;
+  const bool head_lane = row < 4;
+  cnt = __builtin_amdgcn_readfirstlane(cnt);   // uniform over the workgroup
+  const int HKV = a.num_kv_heads;
+  const bool out32 = a.out_dtype == LS_DTYPE_FP32;
+  const QOperand<D> qo = load_q_operand<D>(a.q, a.num_q_heads, r, g);
+  const uint32_t pstride = (uint32_t)HKV * 16 * D;   // elements per page (< 2^32)
+  // row-major loads: instruction j reads tile rows j*RPI + lane/LPR
+  const size_t lofs = ((size_t)g * 16 + lane / ST::LPR) * D + 8 * (lane % ST::LPR);
+  const uint16_t* kb = a.k_pool + lofs;
+  const uint16_t* vb = a.v_pool + lofs;
+  uint32_t* kt = sh.k[wave];
+  uint32_t* vt = sh.v[wave];
+  const int nbw = cnt > wave ? (cnt - wave + kItemWaves - 1) / kItemWaves : 0;
+  const int nent = item_entry_count(cnt);   // entries written by item_entries
+
+  uint4 kr[NPF][NL], vr[NPF][NL];
+  int ntok[NPF];
+#pragma unroll
+  for (int s = 0; s < NPF; ++s) {
+    const int ie = wave + kItemWaves * s;
+    const int e = ie < nent ? ent[ie] : -1;
+    ntok[s] = e >= 0 ? (e & 31) : 0;
+    const uint64_t off = (uint64_t)(uint32_t)(e >= 0 ? e >> 5 : 0) * pstride;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      kr[s][j] = ldg16(kb + off + (size_t)j * ST::RPI * D);
+      vr[s][j] = ldg16(vb + off + (size_t)j * ST::RPI * D);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // issue the slots in order (oldest = slot 0)
+  }
+  f32x4_t o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = kNegInf, l = 0.0f;   // state of head `row` (meaningful in head lanes)
+
+  for (int k0 = 0; k0 < nbw; k0 += NPF) {
+#pragma unroll
+    for (int s = 0; s < NPF; ++s) {
+      const int k = k0 + s;
+      // the block that refills this slot (entries past the written ones read as empty)
+      const int ie = wave + kItemWaves * (k + NPF);
+      const int en = ie < nent ? ent[ie] : -1;
+      if (k < nbw) {
+        // stage the K and V tiles (row-major, padded rows)
+        stage_k<D>(kt, kr[s], 0u);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          uint32_t* d = vt + (j * ST::RPI + lane / ST::LPR) * RW + 4 * (lane % ST::LPR);
+          *reinterpret_cast<uint2*>(d) = make_uint2(vr[s][j].x, vr[s][j].y);
+          *reinterpret_cast<uint2*>(d + 2) = make_uint2(vr[s][j].z, vr[s][j].w);
+        }
+        wave_lds_sync();
+        // logits: lane holds head `row` for tokens 4kq + i
+        f32x4_t z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) z4 = mfma_16x16x32(k_operand<D>(kt, j), qo.b[j], z4);
+        float z[4], bm = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = head_lane && 4 * kq + i < ntok[s];
+          z[i] = ok ? z4[i] * a.sm_scale_log2 : kNegInf;
+          bm = fmaxf(bm, z[i]);
+        }
+        float lo, hi;
+        xor_pair<16>(bm, lo, hi);
+        bm = fmaxf(lo, hi);
+        xor_pair<32>(bm, lo, hi);
+        bm = fmaxf(lo, hi);
+        const float mn = fmaxf(m, bm);
+        const float alpha = mn == kNegInf ? 1.0f : exp2f(m - mn);
+        float p[4], ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = z[i] == kNegInf ? 0.0f : exp2f(z[i] - mn);
+          ps += p[i];
+        }
+        xor_pair<16>(ps, lo, hi);
+        ps = lo + hi;
+        xor_pair<32>(ps, lo, hi);
+        ps = lo + hi;
+        l = l * alpha + ps;
+        m = mn;
+        // rescale o where a head's max grew (o rows = heads 0..3 in lanes 0..15)
+        const float a0 = rl_f(alpha, 0), a1 = rl_f(alpha, 1), a2 = rl_f(alpha, 2),
+                    a3 = rl_f(alpha, 3);
+        if (a0 != 1.0f || a1 != 1.0f || a2 != 1.0f || a3 != 1.0f) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            o[n][0] *= a0; o[n][1] *= a1; o[n][2] *= a2; o[n][3] *= a3;
+          }
+        }
+        // P in bf16 parts, in the A-operand layout (row = head, k = 4 tokens)
+        float r1[4], r2[4];
+        uint32_t h16[4], l16[4], m16[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h16[i] = bf16_split(p[i], &r1[i]);
+          l16[i] = bf16_split(r1[i], &r2[i]);
+          m16[i] = f32_to_bf16_rne(r2[i]);
+        }
+        const uint2 ph = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
+        const uint2 pl = make_uint2(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16));
+        const uint2 pm = make_uint2(m16[0] | (m16[1] << 16), m16[2] | (m16[3] << 16));
+        // o += P . V, one 16-dim tile at a time; B = V[tokens 4kq..+4][dim]
+        const uint16_t* vcol = reinterpret_cast<const uint16_t*>(vt) + 4 * kq * (2 * RW) + row;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const uint16_t* c = vcol + 16 * n;
+          const uint2 vb2 = make_uint2((uint32_t)c[0] | ((uint32_t)c[2 * RW] << 16),
+                                       (uint32_t)c[4 * RW] | ((uint32_t)c[6 * RW] << 16));
+          o[n] = mfma_16x16x16(ph, vb2, o[n]);
+          o[n] = mfma_16x16x16(pl, vb2, o[n]);
+          if (out32) o[n] = mfma_16x16x16(pm, vb2, o[n]);
+        }
+        wave_lds_sync();
+      }
+      __builtin_amdgcn_sched_barrier(0);   // refill after the use (loads complete in order)
+      ntok[s] = en >= 0 ? (en & 31) : 0;
+      const uint64_t off = (uint64_t)(uint32_t)(en >= 0 ? en >> 5 : 0) * pstride;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        kr[s][j] = ldg16(kb + off + (size_t)j * ST::RPI * D);
+        vr[s][j] = ldg16(vb + off + (size_t)j * ST::RPI * D);
+      }
+    }
+  }
+  // wave states to LDS: o rows 0..3 (heads) live in lanes 0..15
+  if (kq == 0) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) sh.acc[wave][h][16 * n + row] = o[n][h];
+    }
+  }
+  if (lane < 4) {
+    sh.m[wave][lane] = m;
+    sh.l[wave][lane] = l;
+  }
+  __syncthreads();
+  // merge the 8 wave states in wave order; one output element per thread
+  for (int e = tid; e < 4 * D; e += kItemThreads) {
+    const int h = e / D, d = e % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kItemWaves; ++w) M = fmaxf(M, sh.m[w][h]);
+    float O = 0.0f, Ls = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kItemWaves; ++w) {
+        const float f = exp2f(sh.m[w][h] - M);   // waves with m = -inf give 0
+        O += f * sh.acc[w][h][d];
+        Ls += f * sh.l[w][h];
+      }
+    }
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    const size_t idx = ((size_t)r * a.num_q_heads + g * 4 + h) * D + d;
+    if (out32) reinterpret_cast<float*>(a.out)[idx] = O * inv;
+    else reinterpret_cast<uint16_t*>(a.out)[idx] = f32_to_bf16_rne(O * inv);
+    if (a.lse && d == 0)
+      a.lse[(size_t)r * a.num_q_heads + g * 4 + h] =
+          (M == kNegInf || !(Ls > 0.0f)) ? kNegInf : (M + log2f(Ls)) * kLn2;
+  }
+}
+
+}  // namespace ls

@@ -135,74 +135,3 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, int r, const ReqG
 }
 
 }  // namespace ls
-
-namespace ls {
-
-// ---------------------------------------------------------------------------
-// Scoring of one (request, kv head) chunk by a whole workgroup: the chunk's
-// summary rows (256 bytes each at D = 128) are read row by row, D/8 lanes per
-// row, 4 waves x NL loads per lane, all in flight after one page-id hop. Used
-// by the two-launch decode step, whose top-k runs in the workgroup that
-// finishes the last chunk of each (request, kv head).
-// ---------------------------------------------------------------------------
-template <int D, int G, int CB>
-struct HeadChunkShape {
-  static constexpr int LPR = D / 8;          // lanes per summary row
-  static constexpr int RPL = kWave / LPR;    // rows per wave load
-  static constexpr int RPW = CB / 4;         // rows per wave
-  static constexpr int NL = RPW / RPL;       // loads per lane
-  static_assert(CB % (4 * RPL) == 0, "chunk");
-};
-
-// Scores of blocks [blk0, blk0 + CB) of (r, g) into out_lds[0 .. CB) (entries
-// of blocks outside the request's candidate range are left untouched).
-template <int D, int HKV, int G, int CB>
-__device__ __forceinline__ void score_head_chunk(const ScoreArgs& a, int r, int g,
-                                                 const ReqGeom& geo, int blk0, float* out_lds) {
-  using S = HeadChunkShape<D, G, CB>;
-  constexpr int LPR = S::LPR, RPL = S::RPL, RPW = S::RPW, NL = S::NL;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = lane % LPR, rl = lane / LPR;
-  uint32_t qv[G][4];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 t = ldg16(a.q + ((size_t)r * (HKV * G) + g * G + h) * D + c * 8);
-    qv[h][0] = t.x; qv[h][1] = t.y; qv[h][2] = t.z; qv[h][3] = t.w;
-  }
-  const int32_t* pages = a.b.indices + geo.page_base;
-  int pg[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int b = blk0 + wave * RPW + i * RPL + rl;
-    pg[i] = (b >= geo.c0 && b < geo.c1) ? pages[b] : -1;
-  }
-  uint4 buf[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int p = pg[i];
-    buf[i] = (p >= 0 && p < a.b.num_pages)
-                 ? ldg16(a.summaries + ((size_t)p * HKV + g) * D + c * 8)
-                 : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    float s;
-    {
-      float part[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) part[h] = group_sum<LPR>(dot8_bf16(qv[h], buf[i], 0.0f));
-      s = part[0];
-      if (a.group_agg == LS_AGG_MEAN) {
-#pragma unroll
-        for (int h = 1; h < G; ++h) s += part[h];
-        s *= (1.0f / G);
-      } else {
-#pragma unroll
-        for (int h = 1; h < G; ++h) s = fmaxf(s, part[h]);
-      }
-    }
-    if (c == 0 && pg[i] >= 0) out_lds[wave * RPW + i * RPL + rl] = s;
-  }
-}
-
-}  // namespace ls

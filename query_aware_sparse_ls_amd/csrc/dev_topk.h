@@ -1,7 +1,7 @@
 // Per (request, KV head) top-k over block scores plus forced sink / recent
-// blocks, emitted in ascending block order -- one 256-thread workgroup
-// (device code shared by the standalone top-k kernel and the fused
-// decode-step kernel).
+// blocks, emitted in ascending block order -- one workgroup of 256 or 1024
+// threads (device code shared by the standalone top-k kernel and the
+// per-(request, kv head) selection and decode-step kernels).
 //
 // Vortex post: I = top-k_j(s_j) ("Why Long Generations Are Expensive"). The
 // post notes that radix top-k, which buckets values by their digits, slows
@@ -12,12 +12,12 @@
 // between their min and max (fp32 subtraction and multiplication by a
 // positive constant are monotone), takes every candidate above the bucket
 // holding the k-th score, drops those below, and refines the boundary bucket.
-// Once at most 64 candidates remain undecided, one wave sorts them by
-// (score descending, block index ascending) with a register bitonic network
-// and takes the first ones: ties go to the lowest block index and the result
-// is unique and deterministic. Equal or pathological scores fall back to a
-// bitwise threshold search on an order-preserving integer key followed by a
-// lowest-index fill.
+// Once at most 64 candidates remain undecided, each of them is ranked by
+// counting the undecided candidates ahead of it in the order (score
+// descending, block index ascending), and the first ones are taken: ties go
+// to the lowest block index and the result is unique and deterministic.
+// Equal or pathological scores fall back to a bitwise threshold search on an
+// order-preserving integer key followed by a lowest-index fill.
 //
 // Thread t holds the scores of candidates [t*PER, t*PER + PER) in registers,
 // so index order is thread order, then register order, and ordered counts are
@@ -28,18 +28,19 @@
 
 namespace ls {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 256;     // workgroup size of the standalone top-k kernel
 constexpr int kTopkMaxIters = 24;
 constexpr int kTopkMaxCand = 16384;
+constexpr int kTopkMaxWaves = 16;     // workgroups of up to 1024 threads
 
 struct TopkLds {
   int hist[256];
-  float red_f[2][4];
-  int red_i[4][4];
+  float red_f[2][kTopkMaxWaves];
+  int red_i[4][kTopkMaxWaves];
   int bstar, cabove;
   float list_key[kWave];
   int list_idx[kWave];
-  unsigned char chosen[kTopkMaxCand];   // per-candidate flag written by the final sort
+  int chosen[kWave];    // final-sort verdict per list position
 };
 
 // Monotone bucket of a score between mn and mx (scale = 256 / (mx - mn)).
@@ -48,18 +49,24 @@ __device__ __forceinline__ int bucket_of(float key, float mn, float scale) {
   return b > 255 ? 255 : (b < 0 ? 0 : b);
 }
 
-// Workgroup total of a small per-thread count (< 128); one barrier.
+// Workgroup total of a small per-thread count (< 128) over NW waves; one
+// barrier.
+template <int NW>
 __device__ __forceinline__ int wg_sum_i(TopkLds& sh, int v, int slot) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int tot;
   (void)wave_excl_scan_small<7>(v, &tot);
   if (lane == 0) sh.red_i[slot][wave] = tot;
   __syncthreads();
-  return sh.red_i[slot][0] + sh.red_i[slot][1] + sh.red_i[slot][2] + sh.red_i[slot][3];
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += sh.red_i[slot][w];
+  return s;
 }
 
-// Exclusive prefix sum of a small per-thread count (< 128) over the
-// workgroup in thread order; *total = sum. One barrier.
+// Exclusive prefix sum of a small per-thread count (< 128) over the NW waves
+// of the workgroup in thread order; *total = sum. One barrier.
+template <int NW>
 __device__ __forceinline__ int wg_excl_scan_i(TopkLds& sh, int v, int slot, int* total) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int wtot;
@@ -68,7 +75,7 @@ __device__ __forceinline__ int wg_excl_scan_i(TopkLds& sh, int v, int slot, int*
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int x = sh.red_i[slot][w];
     before += (w < wave) ? x : 0;
     tot += x;
@@ -89,13 +96,19 @@ __device__ __forceinline__ int tot_minus_prefix(int v, int* total) {
   return *total - pre;
 }
 
-// srow: scores of candidate blocks c0 .. c1-1 (srow[0] is block c0);
-// c1 - c0 <= 256 * PER <= kTopkMaxCand. Called by all 256 threads.
-template <int PER, bool kDev>
-__device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k,
+// srow: scores of candidate blocks c0 .. c1-1 (srow[0] is block c0), in
+// global memory or LDS; c1 - c0 <= NT * PER <= kTopkMaxCand. Called by all
+// NT threads of the workgroup. The selection goes to out[0 .. max_selected)
+// (unused entries -1) and its size to *count_out; sel_lds, when given, gets a
+// copy of the first min(total, max_selected) entries. Returns that count.
+template <int PER, int NT = kTopkThreads>
+__device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k,
                         int32_t* __restrict__ out, int max_selected,
-                        int32_t* __restrict__ count_out, TopkLds& sh) {
-  static_assert(PER >= 1 && PER <= 64 && PER * kTopkThreads <= kTopkMaxCand, "PER");
+                        int32_t* __restrict__ count_out, TopkLds& sh,
+                        int32_t* __restrict__ sel_lds = nullptr) {
+  constexpr int NW = NT / kWave;
+  static_assert(NT % kWave == 0 && NW <= kTopkMaxWaves && NT >= 256, "workgroup size");
+  static_assert(PER >= 1 && PER <= 64 && PER * NT <= kTopkMaxCand, "PER");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = geo.c1 - geo.c0;
   int need = k < n ? k : n;
@@ -104,7 +117,7 @@ __device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int 
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int e = tid * PER + j;
-    key[j] = e < n ? ld_x<kDev>(&srow[e]) : 0.0f;
+    key[j] = e < n ? srow[e] : 0.0f;
     act |= (unsigned long long)(e < n) << j;
   }
   if (need >= n) {
@@ -127,9 +140,13 @@ __device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int 
     mx = wave_max_fast(mx);
     if (lane == 0) { sh.red_i[0][wave] = cnt; sh.red_f[0][wave] = mn; sh.red_f[1][wave] = mx; }
     __syncthreads();
-    cnt = sh.red_i[0][0] + sh.red_i[0][1] + sh.red_i[0][2] + sh.red_i[0][3];
-    mn = fminf(fminf(sh.red_f[0][0], sh.red_f[0][1]), fminf(sh.red_f[0][2], sh.red_f[0][3]));
-    mx = fmaxf(fmaxf(sh.red_f[1][0], sh.red_f[1][1]), fmaxf(sh.red_f[1][2], sh.red_f[1][3]));
+    cnt = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      cnt += sh.red_i[0][w];
+      mn = fminf(mn, sh.red_f[0][w]);
+      mx = fmaxf(mx, sh.red_f[1][w]);
+    }
     __syncthreads();
     if (cnt <= need) {          // the boundary bucket holds exactly the remainder
       sel |= act;
@@ -139,7 +156,8 @@ __device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int 
     if (cnt <= kWave) {
       // the undecided candidates, sorted by one wave; the first `need` win
       int total;
-      int pos = wg_excl_scan_i(sh, __popcll(act), 1, &total);
+      const int pos0 = wg_excl_scan_i<NW>(sh, __popcll(act), 1, &total);
+      int pos = pos0;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         if ((act >> j) & 1ull) {
@@ -158,12 +176,17 @@ __device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int 
         for (int u = 0; u < kWave; ++u) {
           if (u < cnt) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
         }
-        sh.chosen[mi] = rank < need ? 1 : 0;
+        sh.chosen[tid] = rank < need ? 1 : 0;
       }
       __syncthreads();
+      pos = pos0;
 #pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (((act >> j) & 1ull) && sh.chosen[tid * PER + j]) sel |= 1ull << j;
+      for (int j = 0; j < PER; ++j) {
+        if ((act >> j) & 1ull) {
+          if (sh.chosen[pos]) sel |= 1ull << j;
+          ++pos;
+        }
+      }
       act = 0;
       break;
     }
@@ -173,7 +196,7 @@ __device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int 
       robust = true;
       break;
     }
-    sh.hist[tid] = 0;
+    if (tid < 256) sh.hist[tid] = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < PER; ++j)
@@ -222,7 +245,7 @@ __device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int 
       int c = 0;
 #pragma unroll
       for (int j = 0; j < PER; ++j) c += ((act >> j) & 1ull) && score_key(key[j]) >= cand;
-      c = wg_sum_i(sh, c, 2 + (bit & 1));   // alternating slots: one barrier per bit
+      c = wg_sum_i<NW>(sh, c, 2 + (bit & 1));   // alternating slots: one barrier per bit
       if (c >= need) prefix = cand;
     }
     unsigned long long above = 0, equal = 0;
@@ -235,10 +258,10 @@ __device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int 
     above &= act;
     equal &= act;
     __syncthreads();
-    const int nabove = wg_sum_i(sh, __popcll(above), 0);
+    const int nabove = wg_sum_i<NW>(sh, __popcll(above), 0);
     __syncthreads();
     int tot;
-    int pos = wg_excl_scan_i(sh, __popcll(equal), 1, &tot);
+    int pos = wg_excl_scan_i<NW>(sh, __popcll(equal), 1, &tot);
     const int fill = need - nabove;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -253,23 +276,38 @@ __device__ void topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int 
 
   // emit: forced [0, c0), the chosen candidates in order, forced [c1, nb)
   int ncand;
-  int pos = geo.c0 + wg_excl_scan_i(sh, __popcll(sel), 2, &ncand);
+  int pos = geo.c0 + wg_excl_scan_i<NW>(sh, __popcll(sel), 2, &ncand);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     if ((sel >> j) & 1ull) {
-      if (pos < max_selected) st_x<kDev>(&out[pos], geo.c0 + tid * PER + j);
+      if (pos < max_selected) {
+        const int b = geo.c0 + tid * PER + j;
+        out[pos] = b;
+        if (sel_lds) sel_lds[pos] = b;
+      }
       ++pos;
     }
   }
   const int nlow = geo.c0, nhigh = geo.nb - geo.c1;
   const int total = nlow + ncand + nhigh;
-  for (int i = tid; i < nlow; i += kTopkThreads)
-    if (i < max_selected) st_x<kDev>(&out[i], i);
-  for (int i = tid; i < nhigh; i += kTopkThreads)
-    if (nlow + ncand + i < max_selected) st_x<kDev>(&out[nlow + ncand + i], geo.c1 + i);
-  for (int i = total + tid; i < max_selected; i += kTopkThreads) st_x<kDev>(&out[i], -1);
-  if (tid == 0) st_x<kDev>(count_out, total < max_selected ? total : max_selected);
+  for (int i = tid; i < nlow; i += NT) {
+    if (i < max_selected) {
+      out[i] = i;
+      if (sel_lds) sel_lds[i] = i;
+    }
+  }
+  for (int i = tid; i < nhigh; i += NT) {
+    const int p = nlow + ncand + i;
+    if (p < max_selected) {
+      out[p] = geo.c1 + i;
+      if (sel_lds) sel_lds[p] = geo.c1 + i;
+    }
+  }
+  for (int i = total + tid; i < max_selected; i += NT) out[i] = -1;
+  const int stored = total < max_selected ? total : max_selected;
+  if (tid == 0) *count_out = stored;
   __syncthreads();
+  return stored;
 }
 
 __device__ __forceinline__ int topk_budget(const TopkArgs& a, const ReqGeom& geo) {

@@ -9,11 +9,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   __shared__ AttnLds<D, G> sh;
   const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const ReqGeom geo = req_geom(a.b, r, 0, 0);
-  const SelRow sr = sel_row<false>(a, geo, r, g);
-  const int S = a.num_splits;
-  const int lo = (int)(((long long)s * sr.cnt) / S);
-  const int hi = (int)(((long long)(s + 1) * sr.cnt) / S);
-  attn_split<D, G, kAttnBlocksPerSplit, false>(a, geo, sr, r, g, s, lo, hi, sh);
+  attn_split<D, G, kAttnBlocksPerSplit, false>(a, geo, r, g, s, sh);
 }
 
 template <int D>

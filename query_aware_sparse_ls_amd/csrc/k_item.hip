@@ -1,0 +1,159 @@
+// Per-(request, kv head) kernels: one 1024-thread workgroup per pair, grid
+// (num_kv_heads, batch). See dev_item.h for the method and the memory walk.
+//  * select_item_kernel: scoring + top-k (ls_score_select),
+//  * attn_item_kernel:   attention over a given selection (ls_sparse_attn_decode),
+//  * step_item_kernel:   the whole decode step of the pair (ls_sparse_decode_step);
+//    the selection goes to the caller's buffers and stays in LDS for the
+//    attention, so the step is one launch with no hand-off between workgroups.
+#include "dev_item.h"
+
+namespace ls {
+
+template <int D, int MAXC>
+__global__ __launch_bounds__(kItemThreads) void select_item_kernel(ScoreArgs sa, TopkArgs ta) {
+  __shared__ int pg[MAXC];
+  __shared__ float sc[MAXC];
+  __shared__ TopkLds tk;
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kItemWaves * 2 * 16 * Stage<D>::kKRowWords];
+  const int g = blockIdx.x, r = blockIdx.y;
+  const int item = r * sa.num_kv_heads + g;
+  const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
+  load_page_row(sa.b, geo, pg);
+  __syncthreads();
+  item_score<D, MAXC>(sa, r, g, geo, pg, sc, stage);
+  __syncthreads();
+  if (sa.scores) {
+    float* out = sa.scores + (size_t)item * sa.b.max_blocks;
+    for (int b = geo.c0 + threadIdx.x; b < geo.c1; b += kItemThreads) out[b] = sc[b];
+  }
+  (void)topk_wg<MAXC / kItemThreads, kItemThreads>(
+      sc + geo.c0, geo, topk_budget(ta, geo), ta.selected + (size_t)item * ta.max_selected,
+      ta.max_selected, ta.selected_count + item, tk);
+}
+
+template <int D, int MAXC>
+__global__ __launch_bounds__(kItemThreads) void attn_item_kernel(AttnArgs a) {
+  __shared__ int pg[MAXC];
+  __shared__ int sel[MAXC + kItemEntryPad];
+  __shared__ ItemAttnLds<D> sh;
+  const int g = blockIdx.x, r = blockIdx.y;
+  const size_t item = (size_t)r * a.num_kv_heads + g;
+  const ReqGeom geo = req_geom(a.b, r, 0, 0);
+  load_page_row(a.b, geo, pg);
+  int cnt;
+  if (a.selected) {
+    // the count and the entries in one hop; entries past the count are unused
+    cnt = a.selected_count[item];
+    const int n = a.max_selected < MAXC ? a.max_selected : MAXC;
+    const int32_t* row = a.selected + item * a.max_selected;
+    for (int i = threadIdx.x; i < n; i += kItemThreads) sel[i] = row[i];
+    cnt = cnt < 0 ? 0 : (cnt > n ? n : cnt);
+  } else {
+    cnt = geo.nb;
+    for (int i = threadIdx.x; i < geo.nb; i += kItemThreads) sel[i] = i;
+  }
+  __syncthreads();
+  item_entries(a, geo, sel, cnt, pg, item_entry_count(cnt));
+  __syncthreads();
+  item_attn<D>(a, r, g, sel, cnt, sh);
+}
+
+template <int D, int MAXC>
+__global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, TopkArgs ta,
+                                                                 AttnArgs aa) {
+  __shared__ int pg[MAXC];
+  __shared__ int sel[MAXC + kItemEntryPad];
+  __shared__ union {
+    struct {
+      float sc[MAXC];
+      TopkLds tk;
+      alignas(16) uint32_t stage[kItemWaves * 2 * 16 * Stage<D>::kKRowWords];
+    } s;
+    ItemAttnLds<D> at;
+  } u;
+  const int g = blockIdx.x, r = blockIdx.y;
+  const int item = r * sa.num_kv_heads + g;
+  const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
+  load_page_row(sa.b, geo, pg);
+  __syncthreads();
+  item_score<D, MAXC>(sa, r, g, geo, pg, u.s.sc, u.s.stage);
+  __syncthreads();
+  const int cnt = topk_wg<MAXC / kItemThreads, kItemThreads>(
+      u.s.sc + geo.c0, geo, topk_budget(ta, geo), ta.selected + (size_t)item * ta.max_selected,
+      ta.max_selected, ta.selected_count + item, u.s.tk, sel);
+  item_entries(aa, geo, sel, cnt, pg, item_entry_count(cnt));
+  __syncthreads();
+  item_attn<D>(aa, r, g, sel, cnt, u.at);
+}
+
+bool item_path(int batch, int hkv, int head_dim, int group, int max_blocks, int num_pages) {
+  return (long long)batch * hkv >= kItemMinPairs && group == 4 &&
+         (head_dim == 128 || head_dim == 64) && max_blocks <= 8192 && num_pages < (1 << 26);
+}
+
+#define LS_ITEM_DISPATCH(LAUNCH)                      \
+  if (D == 128) {                                     \
+    if (n <= 1024) LAUNCH(128, 1024);                 \
+    if (n <= 2048) LAUNCH(128, 2048);                 \
+    if (n <= 4096) LAUNCH(128, 4096);                 \
+    LAUNCH(128, 8192);                                \
+  }                                                   \
+  if (n <= 1024) LAUNCH(64, 1024);                    \
+  if (n <= 2048) LAUNCH(64, 2048);                    \
+  if (n <= 4096) LAUNCH(64, 4096);                    \
+  LAUNCH(64, 8192);
+
+hipError_t launch_select_item(const ScoreArgs& sa, const TopkArgs& ta, hipStream_t st) {
+  const int D = sa.head_dim, n = sa.b.max_blocks;
+  const dim3 grid(sa.num_kv_heads, sa.b.batch);
+#define LAUNCH(DD, MC)                                                                      \
+  do {                                                                                      \
+    hipLaunchKernelGGL((select_item_kernel<DD, MC>), grid, dim3(kItemThreads), 0, st, sa, ta); \
+    return hipGetLastError();                                                               \
+  } while (0)
+  LS_ITEM_DISPATCH(LAUNCH)
+#undef LAUNCH
+}
+
+hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st) {
+  const int D = a.head_dim, n = a.b.max_blocks;
+  const dim3 grid(a.num_kv_heads, a.b.batch);
+#define LAUNCH(DD, MC)                                                                  \
+  do {                                                                                  \
+    hipLaunchKernelGGL((attn_item_kernel<DD, MC>), grid, dim3(kItemThreads), 0, st, a); \
+    return hipGetLastError();                                                           \
+  } while (0)
+  LS_ITEM_DISPATCH(LAUNCH)
+#undef LAUNCH
+}
+
+hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,
+                            hipStream_t st) {
+  const int D = sa.head_dim, n = sa.b.max_blocks;
+  if (n > 4096) {
+    // the one-launch form does not fit in LDS: the two per-pair launches,
+    // which are the separate calls (same results)
+    const hipError_t e = launch_select_item(sa, ta, st);
+    return e != hipSuccess ? e : launch_attn_item(aa, st);
+  }
+  const dim3 grid(sa.num_kv_heads, sa.b.batch);
+#define LAUNCH(DD, MC)                                                                      \
+  do {                                                                                      \
+    hipLaunchKernelGGL((step_item_kernel<DD, MC>), grid, dim3(kItemThreads), 0, st, sa, ta, \
+                       aa);                                                                 \
+    return hipGetLastError();                                                               \
+  } while (0)
+  if (D == 128) {
+    if (n <= 1024) LAUNCH(128, 1024);
+    if (n <= 2048) LAUNCH(128, 2048);
+    LAUNCH(128, 4096);
+  }
+  if (n <= 1024) LAUNCH(64, 1024);
+  if (n <= 2048) LAUNCH(64, 2048);
+  LAUNCH(64, 4096);
+#undef LAUNCH
+}
+
+#undef LS_ITEM_DISPATCH
+
+}  // namespace ls

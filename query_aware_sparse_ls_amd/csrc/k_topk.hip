@@ -11,7 +11,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const ReqGeom geo = req_geom(a.b, r, a.n_sink, a.n_recent);
   const int item = r * a.num_kv_heads + g;
   const float* srow = a.scores + (size_t)item * a.b.max_blocks + geo.c0;
-  topk_wg<PER, false>(srow, geo, topk_budget(a, geo), a.selected + (size_t)item * a.max_selected,
+  topk_wg<PER>(srow, geo, topk_budget(a, geo), a.selected + (size_t)item * a.max_selected,
                a.max_selected, a.selected_count + item, sh);
 }
 

@@ -86,6 +86,63 @@ int max_total_selected(const ls_select_params& p, int max_blocks) {
   return (int)(total < max_blocks ? total : max_blocks);
 }
 
+ls::ScoreArgs score_args(const void* q, int num_q_heads, const void* summaries,
+                         const ls_pool& pool, const ls_batch& batch, const ls_select_params& p,
+                         float* scores) {
+  ls::ScoreArgs sa;
+  sa.q = static_cast<const uint16_t*>(q);
+  sa.summaries = static_cast<const uint16_t*>(summaries);
+  sa.b = batch_args(batch, pool);
+  sa.num_q_heads = num_q_heads;
+  sa.num_kv_heads = pool.num_heads;
+  sa.head_dim = pool.head_dim;
+  sa.group_agg = p.group_agg;
+  sa.n_sink = p.n_sink;
+  sa.n_recent = p.n_recent;
+  sa.scores = scores;
+  return sa;
+}
+
+ls::TopkArgs topk_args(const ls::ScoreArgs& sa, const ls_select_params& p, const float* scores,
+                       int32_t* selected, int32_t* selected_count) {
+  ls::TopkArgs ta;
+  ta.scores = scores;
+  ta.b = sa.b;
+  ta.num_kv_heads = sa.num_kv_heads;
+  ta.topk = p.topk;
+  ta.keep_ratio = p.keep_ratio;
+  ta.n_sink = p.n_sink;
+  ta.n_recent = p.n_recent;
+  ta.max_selected = p.max_selected;
+  ta.selected = selected;
+  ta.selected_count = selected_count;
+  return ta;
+}
+
+ls::AttnArgs attn_args(const void* q, int num_q_heads, const void* k_pool, const void* v_pool,
+                       const ls_pool& pool, const ls_batch& batch, const int32_t* selected,
+                       const int32_t* selected_count, int max_selected, int num_splits,
+                       float sm_scale, float* partials, void* out, int out_dtype, float* lse) {
+  ls::AttnArgs aa;
+  aa.q = static_cast<const uint16_t*>(q);
+  aa.k_pool = static_cast<const uint16_t*>(k_pool);
+  aa.v_pool = static_cast<const uint16_t*>(v_pool);
+  aa.b = batch_args(batch, pool);
+  aa.num_q_heads = num_q_heads;
+  aa.num_kv_heads = pool.num_heads;
+  aa.head_dim = pool.head_dim;
+  aa.selected = selected;
+  aa.selected_count = selected_count;
+  aa.max_selected = max_selected;
+  aa.num_splits = num_splits;
+  aa.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  aa.partials = partials;
+  aa.out = out;
+  aa.out_dtype = out_dtype;
+  aa.lse = lse;
+  return aa;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,30 +238,16 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
       return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
     scores = static_cast<float*>(workspace);
   }
-  ls::ScoreArgs sa;
-  sa.q = static_cast<const uint16_t*>(q);
-  sa.summaries = static_cast<const uint16_t*>(summaries);
-  sa.b = batch_args(batch, pool);
-  sa.num_q_heads = num_q_heads;
-  sa.num_kv_heads = pool.num_heads;
-  sa.head_dim = pool.head_dim;
-  sa.group_agg = p->group_agg;
-  sa.n_sink = p->n_sink;
-  sa.n_recent = p->n_recent;
-  sa.scores = scores;
+  const ls::ScoreArgs sa = score_args(q, num_q_heads, summaries, pool, batch, *p, scores);
+  const ls::TopkArgs ta = topk_args(sa, *p, scores, selected, selected_count);
+  if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, num_q_heads / pool.num_heads,
+                    batch.max_blocks, pool.num_pages)) {
+    ls::ScoreArgs si = sa;
+    si.scores = scores_out;   // scores stay in LDS unless the caller asked for them
+    return hip_status(ls::launch_select_item(si, ta, stream), "selection kernel launch");
+  }
   hipError_t e = ls::launch_score(sa, stream);
   if (e != hipSuccess) return hip_status(e, "score kernel launch");
-  ls::TopkArgs ta;
-  ta.scores = scores;
-  ta.b = sa.b;
-  ta.num_kv_heads = pool.num_heads;
-  ta.topk = p->topk;
-  ta.keep_ratio = p->keep_ratio;
-  ta.n_sink = p->n_sink;
-  ta.n_recent = p->n_recent;
-  ta.max_selected = p->max_selected;
-  ta.selected = selected;
-  ta.selected_count = selected_count;
   return hip_status(ls::launch_topk(ta, stream), "top-k kernel launch");
 }
 
@@ -252,29 +295,14 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
     return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
   if ((uintptr_t)workspace % kAlign)
     return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
-  ls::AttnArgs aa;
-  aa.q = static_cast<const uint16_t*>(q);
-  aa.k_pool = static_cast<const uint16_t*>(k_pool);
-  aa.v_pool = static_cast<const uint16_t*>(v_pool);
-  aa.b = batch_args(batch, pool);
-  aa.num_q_heads = num_q_heads;
-  aa.num_kv_heads = pool.num_heads;
-  aa.head_dim = pool.head_dim;
-  aa.selected = selected;
-  aa.selected_count = selected_count;
-  aa.max_selected = max_selected;
-  aa.num_splits = ls_attn_num_splits(cap);
-  aa.sm_scale_log2 = sm_scale * 1.4426950408889634f;
-  aa.partials = static_cast<float*>(workspace);
-  aa.out = out;
-  aa.out_dtype = out_dtype;
-  aa.lse = lse_out;
+  const ls::AttnArgs aa = attn_args(q, num_q_heads, k_pool, v_pool, pool, batch, selected,
+                                    selected_count, max_selected, ls_attn_num_splits(cap),
+                                    sm_scale, static_cast<float*>(workspace), out, out_dtype,
+                                    lse_out);
+  if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, num_q_heads / pool.num_heads,
+                    batch.max_blocks, pool.num_pages))
+    return hip_status(ls::launch_attn_item(aa, stream), "attention kernel launch");
   return hip_status(ls::launch_attn(aa, stream), "attention kernel launch");
-}
-
-size_t ls_sparse_decode_step_control_bytes(int32_t batch_size, int32_t num_kv_heads) {
-  if (batch_size <= 0 || num_kv_heads <= 0) return 0;
-  return ls::step_ctl_bytes(batch_size, num_kv_heads);
 }
 
 size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_heads,
@@ -283,8 +311,7 @@ size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_he
   if (batch_size <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_blocks <= 0 || max_selected <= 0)
     return 0;
-  return ls::step_ctl_bytes(batch_size, num_kv_heads) +
-         ls_score_select_workspace_size(batch_size, num_kv_heads, max_blocks) +
+  return ls_score_select_workspace_size(batch_size, num_kv_heads, max_blocks) +
          ls_sparse_attn_decode_workspace_size(batch_size, num_q_heads, head_dim, max_selected,
                                               max_blocks);
 }
@@ -319,11 +346,8 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
     return fail(LS_ERR_INVALID, "keep_ratio must be in [0, 1]");
   if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
   if (batch.batch_size == 0) return ok();
-  if (!ls::step_supported(pool.head_dim, pool.num_heads, batch.max_blocks))
-    return fail(LS_ERR_UNSUPPORTED,
-                "fused step: head_dim %d, num_kv_heads %d, max_blocks %d (supported: 64/128, "
-                "2/4/8, <= 4096); use ls_score_select + ls_sparse_attn_decode",
-                pool.head_dim, pool.num_heads, batch.max_blocks);
+  if (batch.max_blocks > 16384)
+    return fail(LS_ERR_UNSUPPORTED, "max_blocks %d (supported: <= 16384)", batch.max_blocks);
   const int need = max_total_selected(*p, batch.max_blocks);
   if (p->max_selected < need)
     return fail(LS_ERR_INVALID, "max_selected %d < %d (largest possible selection)",
@@ -340,50 +364,25 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
   if ((uintptr_t)workspace % kAlign)
     return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
   char* w = static_cast<char*>(workspace);
-  const size_t ctl_b = ls::step_ctl_bytes(batch.batch_size, pool.num_heads);
-  const size_t sc_b = ls_score_select_workspace_size(batch.batch_size, pool.num_heads,
-                                                     batch.max_blocks);
-  ls::StepLaunch L;
-  L.ctl = w;
-  float* scores = reinterpret_cast<float*>(w + ctl_b);
-  float* partials = reinterpret_cast<float*>(w + ctl_b + sc_b);
-  L.sc.q = static_cast<const uint16_t*>(q);
-  L.sc.summaries = static_cast<const uint16_t*>(summaries);
-  L.sc.b = batch_args(batch, pool);
-  L.sc.num_q_heads = num_q_heads;
-  L.sc.num_kv_heads = pool.num_heads;
-  L.sc.head_dim = pool.head_dim;
-  L.sc.group_agg = p->group_agg;
-  L.sc.n_sink = p->n_sink;
-  L.sc.n_recent = p->n_recent;
-  L.sc.scores = scores;
-  L.tk.scores = scores;
-  L.tk.b = L.sc.b;
-  L.tk.num_kv_heads = pool.num_heads;
-  L.tk.topk = p->topk;
-  L.tk.keep_ratio = p->keep_ratio;
-  L.tk.n_sink = p->n_sink;
-  L.tk.n_recent = p->n_recent;
-  L.tk.max_selected = p->max_selected;
-  L.tk.selected = selected;
-  L.tk.selected_count = selected_count;
-  L.at.q = L.sc.q;
-  L.at.k_pool = static_cast<const uint16_t*>(k_pool);
-  L.at.v_pool = static_cast<const uint16_t*>(v_pool);
-  L.at.b = L.sc.b;
-  L.at.num_q_heads = num_q_heads;
-  L.at.num_kv_heads = pool.num_heads;
-  L.at.head_dim = pool.head_dim;
-  L.at.selected = selected;
-  L.at.selected_count = selected_count;
-  L.at.max_selected = p->max_selected;
-  L.at.num_splits = ls_attn_num_splits(p->max_selected);
-  L.at.sm_scale_log2 = sm_scale * 1.4426950408889634f;
-  L.at.partials = partials;
-  L.at.out = out;
-  L.at.out_dtype = out_dtype;
-  L.at.lse = lse_out;
-  return hip_status(ls::launch_step(L, stream), "decode-step kernel launch");
+  float* scores = reinterpret_cast<float*>(w);
+  float* partials = reinterpret_cast<float*>(
+      w + ls_score_select_workspace_size(batch.batch_size, pool.num_heads, batch.max_blocks));
+  const ls::ScoreArgs sa = score_args(q, num_q_heads, summaries, pool, batch, *p, scores);
+  const ls::TopkArgs ta = topk_args(sa, *p, scores, selected, selected_count);
+  const ls::AttnArgs aa = attn_args(q, num_q_heads, k_pool, v_pool, pool, batch, selected,
+                                    selected_count, p->max_selected,
+                                    ls_attn_num_splits(p->max_selected), sm_scale, partials, out,
+                                    out_dtype, lse_out);
+  if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, num_q_heads / pool.num_heads,
+                    batch.max_blocks, pool.num_pages)) {
+    ls::ScoreArgs si = sa;
+    si.scores = nullptr;
+    return hip_status(ls::launch_step_item(si, ta, aa, stream), "decode-step kernel launch");
+  }
+  hipError_t e = ls::launch_score(sa, stream);
+  if (e == hipSuccess) e = ls::launch_topk(ta, stream);
+  if (e == hipSuccess) e = ls::launch_attn(aa, stream);
+  return hip_status(e, "decode-step kernel launches");
 }
 
 }  // extern "C"

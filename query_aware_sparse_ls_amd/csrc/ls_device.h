@@ -122,6 +122,40 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ------------------------------------------------- lane-pair exchanges ----
+// The values of this lane and of lane ^ O (O = 8, 16 or 32), returned in lane
+// order: lo = value of the lane whose bit O is clear, hi = the other. Both
+// lanes of a pair get the same (lo, hi), so a pair combined as f(lo, hi) is
+// identical in both lanes. VALU only: DPP row_ror:8 inside 16-lane rows, and
+// gfx950's v_permlane16_swap / v_permlane32_swap across rows (no LDS path).
+template <int O>
+__device__ __forceinline__ void xor_pair(float v, float& lo, float& hi) {
+  static_assert(O == 8 || O == 16 || O == 32, "lane distance");
+  const unsigned u = __float_as_uint(v);
+  if constexpr (O == 8) {
+    const float w = __uint_as_float(__builtin_amdgcn_update_dpp(0u, u, 0x128, 0xf, 0xf, false));
+    const bool upper = (__lane_id() & 8) != 0;
+    lo = upper ? w : v;
+    hi = upper ? v : w;
+  } else if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  }
+}
+
+// Sum of the value over lanes l and l ^ O, identical in both lanes.
+template <int O>
+__device__ __forceinline__ float xor_pair_sum(float v) {
+  float lo, hi;
+  xor_pair<O>(v, lo, hi);
+  return lo + hi;
+}
+
 // ---------------------------------------------- low-latency wave reductions
 // Float min / max over the 64 lanes: DPP inside each 16-lane row, then the
 // four row results read into scalars (no LDS-crossbar permutes).
@@ -141,6 +175,11 @@ __device__ __forceinline__ float wave_min_fast(float v) {
   v = fminf(v, dpp_mov<kDppRowHalfMirror>(v));
   v = fminf(v, dpp_mov<kDppRowMirror>(v));
   return fminf(fminf(rl_f(v, 0), rl_f(v, 16)), fminf(rl_f(v, 32), rl_f(v, 48)));
+}
+
+// Index of this thread's wave in the workgroup, known uniform to the compiler.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
 // Number of set bits of the wave mask m in lanes below this one.

@@ -67,20 +67,21 @@ struct AttnArgs {
   float* lse;
 };
 
-struct StepLaunch {
-  ScoreArgs sc;
-  TopkArgs tk;
-  AttnArgs at;
-  void* ctl;    // zeroed control block (tickets, counters), step_ctl_bytes()
-};
-
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t st);
-hipError_t launch_step(const StepLaunch& a, hipStream_t st);
-size_t step_ctl_bytes(int batch, int hkv);
-bool step_supported(int head_dim, int hkv, int max_blocks);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+// Per-(request, kv head) kernels (one 1024-thread workgroup per pair), used
+// when there are at least kItemMinPairs pairs: the selection and the
+// attention of a pair then fit one workgroup each, with no cross-workgroup
+// merge. ScoreArgs.scores may be null for these (scores stay in LDS).
+constexpr int kItemMinPairs = 64;
+bool item_path(int batch, int hkv, int head_dim, int group, int max_blocks, int num_pages);
+hipError_t launch_select_item(const ScoreArgs& sa, const TopkArgs& ta, hipStream_t st);
+hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st);
+hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,
+                            hipStream_t st);
 
 // Blocks per attention split (one register-resident chunk per workgroup).
 constexpr int kAttnBlocksPerSplit = 8;

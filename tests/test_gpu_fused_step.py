@@ -1,4 +1,4 @@
-"""The fused one-launch decode step (ls_sparse_decode_step): identical to
+"""The whole decode step in one call (ls_sparse_decode_step): identical to
 the separate calls, correct against the oracle, reusable workspace, and
 replayable from a HIP graph."""
 
@@ -111,8 +111,6 @@ def test_fused_step_hip_graph_replay():
         assert torch.equal(lse, eager.lse)
         assert torch.equal(cnt, eager.counts)
         _ = run_gpu_step(inp)            # unrelated eager work between replays
-    assert int(ws[:int(ls._L.ls_sparse_decode_step_control_bytes(B, cfg.num_kv_heads))]
-               .count_nonzero()) == 0
 
 
 def test_fused_full_size_llama8b_32k_b16():
