@@ -20,8 +20,9 @@ query), R x step bytes >> the 256 MB Infinity Cache, so consecutive steps
 cannot be served from it. One HIP graph holds one step per replica; it is
 replayed, and the timed region (hipEvents on the launch stream, bracketed by
 device synchronisations) covers exactly `steps` steps. A second, eager pass
-puts hipEvents around each library call (behind a GPU-side sleep so the host
-enqueues ahead of the device) for the per-call durations the roofline uses.
+times each library call alone: 8R launches of it back to back between two
+hipEvents (behind a GPU-side sleep so the host enqueues ahead of the device);
+that mean launch duration prices the roofline line.
 
 Prints ONE JSON line.
 """
@@ -91,23 +92,16 @@ def make_replica(cfg, seed, device):
     return rep
 
 
-def run_step(rep, cfg, sm_scale, fused=True, side=None, timers=None):
-    """One step. With `side`, the summary update runs on that stream, forked
-    from and joined back into the current stream. With `timers` (eager timing
-    pass) events bracket each call: [update, select(+attend), attend]."""
-    import torch
+def call_update(rep):
+    """Summaries of the pages that filled at this step."""
+    import query_aware_sparse_ls_amd as ls
+    ls.build_block_summaries(rep["inp"].k_pool, rep["new_pages"], rep["summ"])
+
+
+def call_first(rep, cfg, sm_scale, fused):
+    """The whole step (fused), or scoring + selection (separate)."""
     import query_aware_sparse_ls_amd as ls
     inp = rep["inp"]
-    ev = timers
-    main = torch.cuda.current_stream()
-    if side is not None:
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            ls.build_block_summaries(inp.k_pool, rep["new_pages"], rep["summ"])
-    else:
-        if ev: ev[0].record()
-        ls.build_block_summaries(inp.k_pool, rep["new_pages"], rep["summ"])
-    if ev: ev[1].record()
     if fused:
         ls.sparse_decode_step(inp.q, rep["summ"], inp.k_pool, inp.v_pool, rep["batch"],
                               topk=inp.topk, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
@@ -115,45 +109,99 @@ def run_step(rep, cfg, sm_scale, fused=True, side=None, timers=None):
                               group_agg=cfg.group_agg, selected=rep["sel"],
                               selected_count=rep["cnt"], out=rep["out"],
                               workspace=rep["ws_step"])
-        if ev: ev[2].record()
     else:
         ls.score_select(inp.q, rep["summ"], cfg.page_size, rep["batch"], topk=inp.topk,
                         n_sink=cfg.n_sink, n_recent=cfg.n_recent, max_selected=rep["maxsel"],
                         group_agg=cfg.group_agg, selected=rep["sel"], selected_count=rep["cnt"],
                         workspace=rep["ws_sel"])
-        if ev: ev[2].record()
-        ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, rep["batch"], rep["sel"],
-                              rep["cnt"], sm_scale=sm_scale, out=rep["out"],
-                              workspace=rep["ws_attn"])
-    if ev: ev[3].record()
+
+
+def call_second(rep, sm_scale):
+    """Attention over the selection (separate path only)."""
+    import query_aware_sparse_ls_amd as ls
+    inp = rep["inp"]
+    ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, rep["batch"], rep["sel"], rep["cnt"],
+                          sm_scale=sm_scale, out=rep["out"], workspace=rep["ws_attn"])
+
+
+def run_step(rep, cfg, sm_scale, fused=True, side=None):
+    """One step. With `side`, the summary update runs on that stream, forked
+    from and joined back into the current stream."""
+    import torch
+    main = torch.cuda.current_stream()
+    if side is not None:
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            call_update(rep)
+    else:
+        call_update(rep)
+    call_first(rep, cfg, sm_scale, fused)
+    if not fused:
+        call_second(rep, sm_scale)
     if side is not None:
         main.wait_stream(side)
+
+
+def per_call_ms(reps, cfg, sm_scale, fused, n):
+    """Mean duration of each library call of the step: n launches of one call
+    back to back (cycling over the replicas) between two HIP events on the
+    launch stream, queued behind a GPU-side sleep so that the host is ahead
+    of the device and the launches run back to back."""
+    import torch
+    R = len(reps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    ev[0].record()
+    for i in range(n):
+        call_update(reps[i % R])
+    ev[1].record()
+    for i in range(n):
+        call_first(reps[i % R], cfg, sm_scale, fused)
+    ev[2].record()
+    if not fused:
+        for i in range(n):
+            call_second(reps[i % R], sm_scale)
+    ev[3].record()
+    torch.cuda.synchronize()
+    return [ev[a].elapsed_time(ev[a + 1]) / n for a in range(3)]
 
 
 def cpu_baseline(rep, cfg, sm_scale, budget_s: float):
     """Time the oracle (unchanged, one thread) on whole requests of replica 0:
     summary update of the request's new page, scores, selection and attention
-    for all its kv heads. Scaled to one call (all requests)."""
+    for all its kv heads. Requests are taken in turn (wrapping around) until
+    `budget_s` seconds of oracle time are spent; the mean time per request,
+    times the batch size, is the time of one call."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
     from workloads import bf16_bits
     inp = rep["inp"]
-    P, Hkv, D, G = cfg.page_size, cfg.num_kv_heads, cfg.head_dim, cfg.group
-    times, done = [], 0
+    P, Hkv = cfg.page_size, cfg.num_kv_heads
+    prepared = {}
+
+    def prepare(r):
+        L = int(inp.seq_lens[r])
+        nb = -(-L // P)
+        p0 = int(inp.page_indptr[r])
+        pages = inp.page_indices[p0:p0 + nb].long()
+        k = bf16_bits(inp.k_pool[pages].contiguous())
+        v = bf16_bits(inp.v_pool[pages].contiguous())
+        q = bf16_bits(inp.q[r:r + 1].contiguous())
+        bv = oracle.BatchView(np.array([0, nb]), np.arange(nb), np.array([L]), P)
+        nc = L // P
+        summ = np.zeros((nb, Hkv, cfg.head_dim), dtype=np.uint16)
+        summ[:nc] = oracle.block_summaries(k, np.arange(nc))      # setup: not timed
+        return L, nc, k, v, q, bv, summ
+
+    times = []
     with threadpool_limits(1):
-        for r in range(cfg.batch):
-            L = int(inp.seq_lens[r])
-            nb = -(-L // P)
-            p0 = int(inp.page_indptr[r])
-            pages = inp.page_indices[p0:p0 + nb].long()
-            k = bf16_bits(inp.k_pool[pages].contiguous())
-            v = bf16_bits(inp.v_pool[pages].contiguous())
-            q = bf16_bits(inp.q[r:r + 1].contiguous())
-            bv = oracle.BatchView(np.array([0, nb]), np.arange(nb), np.array([L]), P)
-            nc = L // P
-            summ = np.zeros((nb, Hkv, D), dtype=np.uint16)
-            summ[:nc] = oracle.block_summaries(k, np.arange(nc))      # setup: not timed
+        while sum(times) < budget_s:
+            r = len(times) % cfg.batch
+            if r not in prepared:
+                prepared[r] = prepare(r)
+            L, nc, k, v, q, bv, summ = prepared[r]
             t0 = time.perf_counter()
             new = [nc - 1] if L % P == 0 and nc > 0 else []
             if new:
@@ -162,15 +210,12 @@ def cpu_baseline(rep, cfg, sm_scale, budget_s: float):
                                n_recent=cfg.n_recent, sm_scale=np.float32(sm_scale),
                                agg=cfg.group_agg, out_dtype="bf16", summaries=summ)
             times.append(time.perf_counter() - t0)
-            done += 1
-            if sum(times) >= budget_s:
-                break
-    per_request = sum(times) / done
-    per_call = per_request * cfg.batch
+    per_call = sum(times) / len(times) * cfg.batch
     return {"value": 1.0 / per_call, "unit": "calls/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {cfg.batch} requests of one call (all {Hkv} kv heads each: "
-                      f"new-page summary, scores, top-k selection, attention), float64 NumPy, "
-                      f"one thread; scaled x{cfg.batch / done:.1f} to a full call",
+            "sample": f"{len(times)} request-steps ({len(times) / cfg.batch:.1f} calls' worth; "
+                      f"each: new-page summary, scores, top-k selection and attention for all "
+                      f"{Hkv} kv heads of one request), float64 NumPy on one thread, "
+                      f"{sum(times):.1f} s; mean per request x {cfg.batch} requests = one call",
             "seconds_per_call": per_call}
 
 
@@ -189,6 +234,114 @@ def copy_calibration(nbytes: int) -> int:
     return 0
 
 
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+CSRC_DIR = os.path.join(ROOT, "query_aware_sparse_ls_amd", "csrc")
+
+
+def library_source_digest() -> str:
+    """sha256 over every HIP/C++ source of the library (names and bytes, in
+    name order). A traffic figure taken from PMC counters is reported only
+    while this digest equals the one stored next to it."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC_DIR)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC_DIR, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel_key: str):
+    """HBM bytes per launch of `kernel_key` from the committed PMC summary
+    (profiles/<kernel_key>.md, a JSON object on its `traffic-json:` line),
+    or None when there is none or the library sources changed since."""
+    path = os.path.join(PROFILE_DIR, kernel_key + ".md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic-json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("source_sha256") != library_source_digest():
+                return None
+            return rec
+    return None
+
+
+def _kernel_stats(csv_path: str):
+    import csv
+    rows = {}
+    for row in csv.DictReader(open(csv_path)):
+        rows[row["Name"]] = {"calls": int(row["Calls"]), "avg_us": float(row["AverageNs"]) / 1e3,
+                             "min_us": float(row["MinNs"]) / 1e3,
+                             "max_us": float(row["MaxNs"]) / 1e3}
+    return rows
+
+
+def _counter_per_dispatch(csv_path: str, counter: str, match: str):
+    """Mean value of `counter` over the dispatches whose kernel name contains
+    `match`, with the dispatch count and the grid size seen."""
+    import csv
+    vals, grids = [], set()
+    for row in csv.DictReader(open(csv_path)):
+        if row["Counter_Name"] == counter and match in row["Kernel_Name"]:
+            vals.append(float(row["Counter_Value"]))
+            grids.add(int(row["Grid_Size"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples for kernels matching {match!r} in {csv_path}")
+    return sum(vals) / len(vals), len(vals), sorted(grids)
+
+
+def summarize_profiles(args) -> int:
+    """Write profiles/<kernel_key>.md from rocprofv3 CSV output: the
+    kernel-trace statistics, FETCH_SIZE / WRITE_SIZE per dispatch of the
+    kernel, and the same counters for a plain copy of a known byte count,
+    which scale the kernel's counters to bytes."""
+    key, match = args.kernel_key, args.kernel_match
+    stats = _kernel_stats(os.path.join(args.kt_dir, "run_kernel_stats.csv"))
+    fetch, nf, grid = _counter_per_dispatch(os.path.join(args.fetch_dir, "run_counter_collection.csv"),
+                                            "FETCH_SIZE", match)
+    write, nw, _ = _counter_per_dispatch(os.path.join(args.write_dir, "run_counter_collection.csv"),
+                                         "WRITE_SIZE", match)
+    cb = args.copy_bytes
+    cfetch, _, _ = _counter_per_dispatch(os.path.join(args.copy_fetch_dir, "run_counter_collection.csv"),
+                                         "FETCH_SIZE", "copyBuffer")
+    cwrite, _, _ = _counter_per_dispatch(os.path.join(args.copy_write_dir, "run_counter_collection.csv"),
+                                         "WRITE_SIZE", "copyBuffer")
+    f_scale = cb / (cfetch * 1024.0)      # bytes per counted KiB
+    w_scale = cb / (cwrite * 1024.0)
+    traffic = fetch * 1024.0 * f_scale + write * 1024.0 * w_scale
+    ours = {n: v for n, v in stats.items() if "ls::" in n}
+    lines = [f"# {key}: kernel time and HBM traffic", "",
+             f"Workload: {args.workload}", "",
+             "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+             "```", args.kt_cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for n, v in sorted(ours.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["calls"]):
+        lines.append(f"| `{n[:110]}` | {v['calls']} | {v['avg_us']:.2f} | {v['min_us']:.2f} | "
+                     f"{v['max_us']:.2f} |")
+    lines += ["", "## HBM counters per dispatch (rocprofv3 --pmc, one counter per run)", "",
+              "```", args.fetch_cmd, args.write_cmd, args.copy_fetch_cmd, args.copy_write_cmd, "```", "",
+              f"* kernel `{match}` (grid {grid}): FETCH_SIZE {fetch:.1f} KiB over {nf} dispatches, "
+              f"WRITE_SIZE {write:.1f} KiB over {nw} dispatches",
+              f"* plain copy (`__amd_rocclr_copyBuffer`, {cb} bytes read and written): "
+              f"FETCH_SIZE {cfetch:.1f} KiB, WRITE_SIZE {cwrite:.1f} KiB",
+              f"* scale (copy bytes / counter bytes): FETCH_SIZE x {f_scale:.4f}, "
+              f"WRITE_SIZE x {w_scale:.4f}",
+              f"* traffic per launch: {fetch * 1024 * f_scale:.0f} B read + "
+              f"{write * 1024 * w_scale:.0f} B written = {traffic:.0f} B", ""]
+    rec = {"kernel": match, "traffic_bytes": round(traffic), "read_bytes": round(fetch * 1024 * f_scale),
+           "write_bytes": round(write * 1024 * w_scale), "fetch_kib": fetch, "write_kib": write,
+           "copy_bytes": cb, "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
+           "source_sha256": library_source_digest()}
+    lines.append("traffic-json: " + json.dumps(rec))
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    with open(os.path.join(PROFILE_DIR, key + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(rec))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,8 +353,18 @@ def main(argv=None) -> int:
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time ls_score_select + ls_sparse_attn_decode instead of the fused step")
-    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (PMC byte-counter scale)")
+    ap.add_argument("--summarize-profiles", action="store_true",
+                    help="write profiles/<kernel-key>.md from rocprofv3 CSV directories")
+    for a in ("kernel-key", "kernel-match", "workload", "kt-dir", "fetch-dir", "write-dir",
+              "copy-fetch-dir", "copy-write-dir", "kt-cmd", "fetch-cmd", "write-cmd",
+              "copy-fetch-cmd", "copy-write-cmd"):
+        ap.add_argument("--" + a, default="")
+    ap.add_argument("--copy-bytes", type=int, default=0)
     args = ap.parse_args(argv)
+    if args.summarize_profiles:
+        return summarize_profiles(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the sparse-attention path has no multi-GPU mode "
               "(run with --gpus 1).", file=sys.stderr)
@@ -274,29 +437,23 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - wall0
     ms_step = t0e.elapsed_time(t1e) / steps
 
-    # per-call durations: eager, events around each call, GPU given a head start
-    n_eager = min(steps, 8 * R)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_eager)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2e8))
-    for i in range(n_eager):
-        run_step(reps[i % R], cfg, sm_scale, fused, None, timers=evs[i])
-    torch.cuda.synchronize()
-    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / n_eager
-    upd, first, second = avg(0, 1), avg(1, 2), avg(2, 3)
+    # per-call durations (eager, back-to-back launches of one call)
+    upd, first, second = per_call_ms(reps, cfg, sm_scale, fused, min(steps, 8 * R))
 
     calls_per_s = 1e3 / ms_step
     gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
     sel_bytes = B * Hkv * n_sel * 4 + B * Hkv * 4      # selection written (+ counts)
     fused_bytes = nbytes["total"] - nbytes["summary_update"] + sel_bytes
     if fused:
+        # one (request, kv head) pair per workgroup: the whole call is one launch
         dom_ms, dom_bytes = first, fused_bytes
-        dom_name = "decode_step_kernel (scoring + top-k + split-K attention + merge, one launch)"
+        dom_key, dom_match = "step_item_kernel.llama8b_32k_b16", "ls::step_item_kernel<128, 2048>"
     else:
         dom_ms = second
-        dom_bytes = nbytes["selected_kv"] + B * Hq * D * 4 + sel_bytes + B * nb * 4
-        dom_name = "ls_sparse_attn_decode (split-K attention + combine kernels)"
+        dom_bytes = nbytes["selected_kv"] + B * Hq * D * 2 + sel_bytes + B * nb * 4
+        dom_key, dom_match = "attn_item_kernel.llama8b_32k_b16", "ls::attn_item_kernel<128, 2048>"
     dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+    tr = stored_traffic(dom_key)
 
     res = {
         "metric": "sparse decode attention calls/sec + achieved HBM GB/s (% of peak) at 8B/32K/B16",
@@ -314,10 +471,13 @@ def main(argv=None) -> int:
         "call_ms": ({"summary_update": round(upd, 5), "decode_step": round(first, 5)} if fused
                     else {"summary_update": round(upd, 5), "score_select": round(first, 5),
                           "sparse_attn_decode": round(second, 5)}),
-        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": round(dom_gbps, 1),
+        "roofline": {"kernel": dom_match, "bound": "hbm", "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)},
+                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": tr["traffic_bytes"] if tr else None,
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_ms": round(dom_ms, 5),
+                     "traffic_source": f"profiles/{dom_key}.md" if tr else None},
         "wall_s_timed": round(wall, 4),
         "device": torch.cuda.get_device_name(0),
     }
