@@ -380,3 +380,35 @@ def decode_step(q_bits, k_bits, v_bits, batch: BatchView, *, num_kv_heads: int, 
                                   out_dtype=out_dtype)
         out[(r, g)] = {"scores": s, "selected": blocks, "out": o, "lse": lse}
     return {"summaries": summaries, "pairs": out}
+
+
+# --------------------------------------------------------------------------
+# Coarse-to-fine token selection with a learned indexer
+# --------------------------------------------------------------------------
+
+def coarse_to_fine_select(q_idx_bits: np.ndarray, head_w: np.ndarray, key_bits: np.ndarray,
+                          key_scales: np.ndarray, summaries: np.ndarray, batch: BatchView,
+                          r: int, *, topk_blocks: int, n_recent_blocks: int, topk_tokens: int,
+                          summary_format: str = "bf16") -> Dict:
+    """Coarse-to-fine selection of request r (LeanSparse §5: a coarse pass
+    over a compact representation picks candidate blocks, then exact indexer
+    scores of the candidates' tokens pick the tokens; tokens outside the
+    kept blocks cannot come back):
+      1. coarse score of every complete block from its block-mean key,
+      2. the top topk_blocks blocks plus the last n_recent_blocks (and a
+         partial last block) -- select_blocks with no sink,
+      3. exact Eq. 6 score of every cached token of those blocks,
+      4. the top topk_tokens of them by (score desc, token asc).
+    Returns {"blocks", "block_scores", "tokens" (ascending), "token_scores"}."""
+    nb, nc = batch.num_blocks(r), batch.num_complete(r)
+    L = int(batch.seq_lens[r])
+    sb = indexer_block_scores(q_idx_bits, head_w, summaries, batch, r,
+                              summary_format=summary_format)
+    blocks = select_blocks(sb, nb, nc, topk_blocks, 0, n_recent_blocks)
+    toks = tokens_of_blocks(blocks, batch.page_size, L)
+    st = indexer_token_scores(q_idx_bits, head_w, key_bits, key_scales, batch, r, tokens=toks)
+    full = np.full(L, -np.inf)
+    full[toks] = st
+    sel = select_tokens(full, topk_tokens, candidates=toks.tolist())
+    return {"blocks": blocks, "block_scores": sb, "tokens": sel,
+            "token_scores": dict(zip(toks.tolist(), st.tolist()))}

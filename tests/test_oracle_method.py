@@ -18,7 +18,8 @@ import numpy as np
 import pytest
 
 from oracle.method import (
-    BatchView, attention_over_tokens, block_scores, block_summaries, decode_step,
+    BatchView, attention_over_tokens, block_scores, block_summaries, coarse_to_fine_select,
+    decode_step,
     dense_attention, forced_blocks, indexer_block_scores, indexer_token_scores, lse_merge,
     mla_attention, select_blocks, select_tokens, sparse_attention, tokens_of_blocks,
 )
@@ -410,3 +411,56 @@ def test_keep_ratio_budget_closed_forms():
     # ceil: 1/64 of 130 = 2.03 -> 3 kept in all, 3 forced -> k = 0; of 200 -> 4 -> k = 1
     assert topk_from_keep_ratio(130, 130, 1 / 64, 1, 2) == 0
     assert topk_from_keep_ratio(200, 200, 1 / 64, 1, 2) == 1
+
+
+# ------------------------------------------------------------ coarse-to-fine
+
+def _indexer_problem(rng, lens, P, H=3, D=6):
+    batch, npg = _tiny_batch(rng, lens=lens, P=P)
+    keys = rng.integers(0, 256, (npg, P, D)).astype(np.uint8)
+    keys[(keys & 0x7F) == 0x7F] = 0x31          # no NaN encodings
+    scales = (rng.random((npg, P)) + 0.5).astype(np.float32)
+    q = _rand_bf16(rng, (len(lens), H, D))
+    w = rng.standard_normal((len(lens), H)).astype(np.float32)
+    summ = block_summaries(keys, range(npg), key_format="fp8_e4m3fn", key_scales=scales)
+    return batch, keys, scales, q, w, summ
+
+
+def test_coarse_to_fine_with_every_block_kept_is_exact_token_topk():
+    rng = np.random.default_rng(31)
+    batch, keys, scales, q, w, summ = _indexer_problem(rng, lens=(37, 16), P=4)
+    for r in range(2):
+        L = int(batch.seq_lens[r])
+        res = coarse_to_fine_select(q, w, keys, scales, summ, batch, r,
+                                    topk_blocks=batch.num_blocks(r), n_recent_blocks=1,
+                                    topk_tokens=5)
+        assert res["blocks"] == list(range(batch.num_blocks(r)))
+        s = indexer_token_scores(q, w, keys, scales, batch, r)
+        # pairwise dominance characterises the top-k set: every kept token
+        # beats every dropped token under (score desc, token asc)
+        kept = set(res["tokens"])
+        assert len(kept) == min(5, L)
+        for a in kept:
+            for b in set(range(L)) - kept:
+                assert s[a] > s[b] or (s[a] == s[b] and a < b)
+
+
+def test_coarse_to_fine_never_leaves_the_kept_blocks():
+    rng = np.random.default_rng(32)
+    batch, keys, scales, q, w, summ = _indexer_problem(rng, lens=(64,), P=4)
+    res = coarse_to_fine_select(q, w, keys, scales, summ, batch, 0, topk_blocks=3,
+                                n_recent_blocks=1, topk_tokens=6)
+    nb = batch.num_blocks(0)
+    assert len(res["blocks"]) == 4 and nb - 1 in res["blocks"]
+    # the coarse pass ranks blocks by the block-mean score (brute force)
+    sb = indexer_block_scores(q, w, summ, batch, 0)
+    cands = [j for j in range(nb) if j != nb - 1]
+    top = sorted(cands, key=lambda j: (-sb[j], j))[:3]
+    assert sorted(top + [nb - 1]) == res["blocks"]
+    allowed = set(tokens_of_blocks(res["blocks"], 4, 64).tolist())
+    assert set(res["tokens"]) <= allowed and len(res["tokens"]) == 6
+    # among the kept blocks' tokens the choice is the exact top-6
+    s = indexer_token_scores(q, w, keys, scales, batch, 0)
+    for a in res["tokens"]:
+        for b in allowed - set(res["tokens"]):
+            assert s[a] > s[b] or (s[a] == s[b] and a < b)
