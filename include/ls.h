@@ -270,6 +270,129 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* 5. Learned-indexer selection                                             */
+/* ------------------------------------------------------------------------ */
+/*
+ * Score every unit u of request r with a learned indexer and keep the top-k
+ * (LeanSparse, "Memory-Efficient Serving for Native Sparse-Attention LLMs",
+ * Eq. 6, with the original keys in place of its compressed codes):
+ *
+ *   s_u = sum_{h < num_heads} head_weights[r][h] * max(0, sigma_u * (q[r][h] . key_u))
+ *
+ * (fp32 accumulation of exact products; bf16 q, fp8 or bf16 keys, 128 dims).
+ * Units are:
+ *   LS_SEL_TOKENS -- the cached tokens t < L of the request (key_u = the fp8
+ *     indexer key of token t, sigma_u = key_scales[page][slot], 1 if
+ *     key_scales is NULL); with a candidate list, only the tokens of the
+ *     blocks cand_blocks[r][0 .. cand_counts[r]-1] (coarse-to-fine: the
+ *     exact pass restricted to the blocks a coarse pass kept). No forced
+ *     units. selected[r][0 .. cnt-1] = the first min(topk, #units) units under
+ *     the order (s descending, token ascending), as TOKEN ids, ascending;
+ *     remaining entries up to max_selected are -1.
+ *   LS_SEL_BLOCKS -- the blocks (= pages) of the request, scored through
+ *     their block-mean indexer key (built by ls_build_block_summaries from
+ *     the fp8 keys and scales; sigma = 1). Forced and candidate blocks exactly
+ *     as in ls_score_select (sink / recent blocks and the partial last block
+ *     are forced, not ranked); ties go to the lowest block index.
+ * The result is deterministic. Selection ties are decided on fp32 scores.
+ *
+ * q:            [batch][num_heads][128] bf16 (num_heads 16, 32 or 64).
+ * head_weights: [batch][num_heads] fp32.
+ * keys:         LS_SEL_TOKENS: fp8 e4m3fn indexer key pool [num_pages]
+ *               [page_size][128] (key_pool.dtype LS_DTYPE_FP8_E4M3FN);
+ *               LS_SEL_BLOCKS: bf16 block-mean keys [num_pages][128]
+ *               (key_pool.dtype LS_DTYPE_BF16). key_pool.num_heads = 1,
+ *               head_dim = 128, page_size 16, 32 or 64 (tokens per block).
+ * key_scales:   tokens: NULL or [num_pages][page_size] fp32; blocks: NULL.
+ * batch:        page table of the indexer pool (block = page).
+ * cand_blocks:  tokens only, optional: [batch][cand_cap] ascending block
+ *               indices with counts cand_counts[batch] (e.g. the selection
+ *               of a LS_SEL_BLOCKS call); entries past the count are ignored.
+ * p:            host pointer. max_selected >= topk (tokens), or
+ *               >= min(max_blocks, topk + n_sink + n_recent + 1) (blocks).
+ * selected, selected_count: [batch][max_selected] int32, [batch] int32.
+ * scores_out:   NULL, or [batch][ls_indexer_score_stride(granularity, U)]
+ *               fp32 receiving s_u at unit u (tokens: unit = position in the
+ *               token range or candidate list, u = c * page_size + slot for
+ *               candidate c; blocks: unit = block index, candidates only).
+ * workspace:    >= ls_indexer_select_workspace_size(batch, granularity, U)
+ *               bytes, 256-byte aligned, need not be initialised; U = units
+ *               per request at most: tokens max_blocks * page_size, or
+ *               cand_cap * page_size with candidates (<= 262144); blocks
+ *               max_blocks (<= 16384).
+ * Token mode is three launches: a histogram of the score keys while scoring,
+ * a pass that keeps every unit above the k-th score's 12-bit bucket and
+ * gathers that bucket's units, and the ranking of those by the rest of their
+ * key (in the last workgroup of each request to finish the pass).
+ */
+enum { LS_SEL_TOKENS = 0, LS_SEL_BLOCKS = 1 };
+
+typedef struct ls_indexer_params {
+  int32_t struct_size;   /* = sizeof(ls_indexer_params)                       */
+  int32_t granularity;   /* LS_SEL_TOKENS or LS_SEL_BLOCKS                    */
+  int32_t topk;          /* units chosen by score (forced blocks not counted) */
+  int32_t n_sink;        /* blocks only: forced blocks 0 .. n_sink-1          */
+  int32_t n_recent;      /* blocks only: forced last n_recent blocks          */
+  int32_t max_selected;  /* row capacity of `selected`                        */
+} ls_indexer_params;
+
+/* Row stride (in floats) of scores_out for up to max_units units. */
+int32_t ls_indexer_score_stride(int32_t granularity, int32_t max_units);
+
+size_t ls_indexer_select_workspace_size(int32_t batch_size, int32_t granularity,
+                                        int32_t max_units);
+
+ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
+                            const float* head_weights, const void* keys, const float* key_scales,
+                            ls_pool key_pool, ls_batch batch, const int32_t* cand_blocks,
+                            const int32_t* cand_counts, int32_t cand_cap,
+                            const ls_indexer_params* p, int32_t* selected,
+                            int32_t* selected_count, float* scores_out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* 6. Sparse multi-head latent attention over selected tokens               */
+/* ------------------------------------------------------------------------ */
+/*
+ * For every request r and query head h, attention over the latent rows c_t
+ * of the selected tokens t < L (Vortex post, "Designing for a new
+ * architecture": every query head attends one shared latent head whose rows
+ * are both key -- all 576 entries, compressed content plus rope part -- and
+ * value -- the first 512 entries):
+ *   z_t = sm_scale * sum_{d<576} q[r][h][d] * c_t[d],
+ *   out[r][h][:] = sum_t e^{z_t - M} c_t[0:512] / sum_t e^{z_t - M},
+ *   lse_out[r][h] = M + ln sum_t e^{z_t - M}
+ * fp32 logits, softmax and accumulation; the token set is split over
+ * workgroups of 256 selected tokens whose partial states are merged by
+ * log-sum-exp in split order (deterministic). Empty T: out = 0, lse = -inf.
+ * Output rounded once (nearest-even) to out_dtype.
+ *
+ * q:        [batch][num_q_heads][576] bf16; num_q_heads a multiple of 16 (<= 256).
+ * latent:   [num_pages][page_size][576] bf16 (pool.num_heads = 1,
+ *           pool.head_dim = 576, pool.dtype = LS_DTYPE_BF16).
+ * selected: [batch][max_selected] token ids (e.g. from ls_indexer_select),
+ *           counts in selected_count[batch]; ids outside [0, L) are skipped.
+ *           selected == NULL and selected_count == NULL attend every cached
+ *           token (dense).
+ * out:      [batch][num_q_heads][512] of out_dtype (bf16 or fp32).
+ * lse_out:  NULL or [batch][num_q_heads] fp32.
+ * workspace: >= ls_sparse_mla_decode_workspace_size(batch, num_q_heads,
+ *           max_selected, or max_blocks * page_size when dense) bytes,
+ *           256-byte aligned (split partial states); need not be initialised.
+ */
+int32_t ls_mla_num_splits(int32_t max_tokens);
+
+size_t ls_sparse_mla_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
+                                           int32_t max_tokens);
+
+ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                               const void* latent, ls_pool pool, ls_batch batch,
+                               const int32_t* selected, const int32_t* selected_count,
+                               int32_t max_selected, float sm_scale, void* out,
+                               int32_t out_dtype, float* lse_out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Introspection                                                             */
 /* ------------------------------------------------------------------------ */
 /* Message for the last non-OK status returned on the calling thread ("" if

@@ -28,6 +28,7 @@ the oracle itself (brute force, exact rationals, closed forms, the pages'
 worked example), except where a header says "parity unpinned".
 """
 
+from . import method, numerics  # noqa: F401
 from .numerics import (  # noqa: F401
     bf16_to_f64, fp8e4m3fn_to_f64, f64_to_bf16_bits, f64_to_f32, fraction_to_bf16_bits,
 )
@@ -35,5 +36,6 @@ from .method import (  # noqa: F401
     BatchView, block_summaries, block_scores, select_blocks, select_blocks_batch,
     attention_over_tokens, sparse_attention, dense_attention, lse_merge,
     indexer_token_scores, select_tokens, mla_attention, decode_step,
-    tokens_of_blocks, topk_from_keep_ratio, forced_blocks,
+    tokens_of_blocks, topk_from_keep_ratio, forced_blocks, indexer_block_scores,
+    coarse_to_fine_select,
 )

@@ -16,14 +16,17 @@ import torch
 
 from . import _lib
 from ._lib import (LS_AGG_MAX, LS_AGG_MEAN, LS_DTYPE_BF16, LS_DTYPE_FP32,  # noqa: F401
-                   LS_DTYPE_FP8_E4M3FN, LsBatch, LsError, LsPool, LsSelectParams, check)
+                   LS_DTYPE_FP8_E4M3FN, LS_SEL_BLOCKS, LS_SEL_TOKENS, LsBatch, LsError,
+                   LsIndexerParams, LsPool, LsSelectParams, check)
 
 _L = _lib.load()
 
 __all__ = ["PagedBatch", "build_block_summaries", "score_select", "sparse_attn_decode",
            "score_select_workspace_size", "sparse_attn_decode_workspace_size",
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
-           "sparse_decode_step_workspace"]
+           "sparse_decode_step_workspace", "indexer_select", "indexer_select_workspace_size",
+           "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
+           "mla_num_splits"]
 
 _DT = {torch.bfloat16: LS_DTYPE_BF16, torch.float32: LS_DTYPE_FP32,
        torch.float8_e4m3fn: LS_DTYPE_FP8_E4M3FN}
@@ -242,3 +245,107 @@ def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.T
                                    workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse, selected, selected_count
+
+
+# ------------------------------------------------------------ learned indexer
+
+def indexer_score_stride(granularity: str, max_units: int) -> int:
+    g = LS_SEL_TOKENS if granularity == "tokens" else LS_SEL_BLOCKS
+    return int(_L.ls_indexer_score_stride(g, int(max_units)))
+
+
+def indexer_select_workspace_size(batch_size: int, granularity: str, max_units: int) -> int:
+    g = LS_SEL_TOKENS if granularity == "tokens" else LS_SEL_BLOCKS
+    return int(_L.ls_indexer_select_workspace_size(int(batch_size), g, int(max_units)))
+
+
+def indexer_select(q: torch.Tensor, head_weights: torch.Tensor, keys: torch.Tensor,
+                   page_size: int, batch: PagedBatch, *, granularity: str, topk: int,
+                   max_selected: int, key_scales: Optional[torch.Tensor] = None,
+                   cand_blocks: Optional[torch.Tensor] = None,
+                   cand_counts: Optional[torch.Tensor] = None,
+                   n_sink: int = 0, n_recent: int = 0,
+                   selected: Optional[torch.Tensor] = None,
+                   selected_count: Optional[torch.Tensor] = None,
+                   scores_out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k tokens (fp8 indexer keys [pages][P][128], granularity "tokens")
+    or blocks (bf16 block-mean keys [pages][128], granularity "blocks") per
+    request by the learned-indexer score sum_h w_h ReLU(sigma q_h . k).
+    Returns (selected [B][max_selected], counts [B])."""
+    _need(q, torch.bfloat16); _need(head_weights, torch.float32); _need(keys)
+    B, H, D = q.shape
+    dev = q.device
+    tokens = granularity == "tokens"
+    g = LS_SEL_TOKENS if tokens else LS_SEL_BLOCKS
+    if selected is None:
+        selected = torch.empty(B, max_selected, dtype=torch.int32, device=dev)
+    if selected_count is None:
+        selected_count = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(selected, torch.int32); _need(selected_count, torch.int32)
+    cand_cap = 0
+    if cand_blocks is not None:
+        _need(cand_blocks, torch.int32); _need(cand_counts, torch.int32)
+        cand_cap = int(cand_blocks.shape[-1])
+    if key_scales is not None:
+        _need(key_scales, torch.float32)
+    if scores_out is not None:
+        _need(scores_out, torch.float32)
+    if tokens:
+        max_units = (cand_cap if cand_blocks is not None else batch.max_blocks) * page_size
+    else:
+        max_units = batch.max_blocks
+    ws = _workspace(int(_L.ls_indexer_select_workspace_size(B, g, max_units)), dev, workspace)
+    params = LsIndexerParams(C.sizeof(LsIndexerParams), g, int(topk), int(n_sink),
+                             int(n_recent), int(max_selected))
+    pool = LsPool(int(keys.shape[0]), 1, int(page_size), int(D), _DT[keys.dtype])
+    check(_L.ls_indexer_select(q.data_ptr(), LS_DTYPE_BF16, int(H), head_weights.data_ptr(),
+                               keys.data_ptr(), _ptr(key_scales), pool, batch.c(),
+                               _ptr(cand_blocks), _ptr(cand_counts), cand_cap, C.byref(params),
+                               selected.data_ptr(), selected_count.data_ptr(), _ptr(scores_out),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return selected, selected_count
+
+
+# ----------------------------------------------------------------- sparse MLA
+
+def mla_num_splits(max_tokens: int) -> int:
+    return int(_L.ls_mla_num_splits(int(max_tokens)))
+
+
+def sparse_mla_decode_workspace_size(batch_size: int, num_q_heads: int, max_tokens: int) -> int:
+    return int(_L.ls_sparse_mla_decode_workspace_size(int(batch_size), int(num_q_heads),
+                                                      int(max_tokens)))
+
+
+def sparse_mla_decode(q: torch.Tensor, latent: torch.Tensor, batch: PagedBatch,
+                      selected: Optional[torch.Tensor], selected_count: Optional[torch.Tensor], *,
+                      sm_scale: float, out: Optional[torch.Tensor] = None,
+                      out_dtype=torch.bfloat16, lse: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention of every query head over the latent rows [pages][P][576] of
+    the selected tokens (values: the first 512 entries). selected = None
+    attends every cached token. Returns (out [B][H][512], lse or None)."""
+    _need(q, torch.bfloat16); _need(latent, torch.bfloat16)
+    B, H, Dk = q.shape
+    P = int(latent.shape[1])
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, H, 512, dtype=out_dtype, device=dev)
+    _need(out)
+    if lse is not None:
+        _need(lse, torch.float32)
+    max_sel = 0
+    if selected is not None:
+        _need(selected, torch.int32); _need(selected_count, torch.int32)
+        max_sel = int(selected.shape[-1])
+    cap = max_sel if selected is not None else batch.max_blocks * P
+    ws = _workspace(sparse_mla_decode_workspace_size(B, H, cap), dev, workspace)
+    pool = LsPool(int(latent.shape[0]), 1, P, int(Dk), LS_DTYPE_BF16)
+    check(_L.ls_sparse_mla_decode(q.data_ptr(), LS_DTYPE_BF16, int(H), latent.data_ptr(), pool,
+                                  batch.c(), _ptr(selected), _ptr(selected_count), max_sel,
+                                  float(sm_scale), out.data_ptr(), _DT[out.dtype], _ptr(lse),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out, lse

@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libls.so")
 LS_OK, LS_ERR_INVALID, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = range(5)
 LS_DTYPE_BF16, LS_DTYPE_FP32, LS_DTYPE_FP8_E4M3FN = 1, 2, 3
 LS_AGG_MAX, LS_AGG_MEAN = 0, 1
+LS_SEL_TOKENS, LS_SEL_BLOCKS = 0, 1
 
 # every function the header declares, with its ctypes signature
 EXPORTS = {}
@@ -33,6 +34,11 @@ class LsSelectParams(C.Structure):
                 ("max_selected", C.c_int32)]
 
 
+class LsIndexerParams(C.Structure):
+    _fields_ = [("struct_size", C.c_int32), ("granularity", C.c_int32), ("topk", C.c_int32),
+                ("n_sink", C.c_int32), ("n_recent", C.c_int32), ("max_selected", C.c_int32)]
+
+
 _P = C.c_void_p
 _SIGS = {
     "ls_build_block_summaries": (C.c_int, [_P, _P, LsPool, _P, C.c_int32, _P, C.c_int32, _P]),
@@ -47,6 +53,16 @@ _SIGS = {
     "ls_sparse_decode_step": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, LsPool, LsBatch,
                                         C.POINTER(LsSelectParams), _P, _P, C.c_float, _P,
                                         C.c_int32, _P, _P, C.c_size_t, _P]),
+    "ls_indexer_score_stride": (C.c_int32, [C.c_int32, C.c_int32]),
+    "ls_indexer_select_workspace_size": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32]),
+    "ls_indexer_select": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, LsPool, LsBatch, _P,
+                                    _P, C.c_int32, C.POINTER(LsIndexerParams), _P, _P, _P, _P,
+                                    C.c_size_t, _P]),
+    "ls_mla_num_splits": (C.c_int32, [C.c_int32]),
+    "ls_sparse_mla_decode_workspace_size": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32]),
+    "ls_sparse_mla_decode": (C.c_int, [_P, C.c_int32, C.c_int32, _P, LsPool, LsBatch, _P, _P,
+                                       C.c_int32, C.c_float, _P, C.c_int32, _P, _P, C.c_size_t,
+                                       _P]),
     "ls_last_error": (C.c_char_p, []),
     "ls_version": (C.c_char_p, []),
     "ls_attn_num_splits": (C.c_int32, [C.c_int32]),

@@ -24,8 +24,6 @@
 
 namespace ls {
 
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int D, int G>
 struct AttnShape {

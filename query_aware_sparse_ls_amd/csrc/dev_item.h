@@ -28,6 +28,7 @@
 #pragma once
 
 #include "dev_attn.h"
+#include "dev_mfma.h"
 #include "dev_score.h"
 #include "dev_topk.h"
 
@@ -42,19 +43,6 @@ constexpr int kItemPrefetch = 4;        // K/V blocks in flight per wave
 // - 1, nbw = ceil((cnt - w) / 8), i.e. at most cnt + 7 + 8(2 kItemPrefetch - 2).
 constexpr int kItemEntryPad = kItemWaves * 2 * kItemPrefetch;
 static_assert(kItemEntryPad >= 7 + kItemWaves * (2 * kItemPrefetch - 2) + 1, "entry padding");
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma_16x16x32(uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma_16x16x16(uint2 a, uint2 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
-}
 
 // Q^T as the B operand of the D/32 k-steps of a 16x16x32 MFMA (G = 4 heads).
 template <int D>

@@ -6,6 +6,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <algorithm>
+
 #include "ls_internal.h"
 
 namespace {
@@ -383,6 +385,221 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
   if (e == hipSuccess) e = ls::launch_topk(ta, stream);
   if (e == hipSuccess) e = ls::launch_attn(aa, stream);
   return hip_status(e, "decode-step kernel launches");
+}
+
+// ------------------------------------------------------ learned indexer ----
+
+int32_t ls_indexer_score_stride(int32_t granularity, int32_t max_units) {
+  if (max_units <= 0) return 0;
+  if (granularity == LS_SEL_BLOCKS) return max_units;
+  return (max_units + ls::kIdxMarkUnits - 1) / ls::kIdxMarkUnits * ls::kIdxMarkUnits;
+}
+
+size_t ls_indexer_select_workspace_size(int32_t batch_size, int32_t granularity,
+                                        int32_t max_units) {
+  if (batch_size <= 0 || max_units <= 0) return 0;
+  const size_t B = (size_t)batch_size;
+  const size_t U = (size_t)ls_indexer_score_stride(granularity, max_units);
+  size_t ws = align_up(B * U * sizeof(float));   // scores
+  if (granularity == LS_SEL_TOKENS) {
+    ws += align_up(B * ls::kIdxBins * sizeof(uint32_t));    // histogram
+    ws += align_up(B * 4 * sizeof(uint32_t));               // counters
+    ws += align_up(B * ls::kIdxCandCap * sizeof(uint2));    // candidates
+    ws += align_up(B * (U / 32) * sizeof(uint32_t));        // bitmap
+  }
+  return ws;
+}
+
+ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
+                            const float* head_weights, const void* keys, const float* key_scales,
+                            ls_pool key_pool, ls_batch batch, const int32_t* cand_blocks,
+                            const int32_t* cand_counts, int32_t cand_cap,
+                            const ls_indexer_params* p, int32_t* selected,
+                            int32_t* selected_count, float* scores_out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!p) return fail(LS_ERR_INVALID, "params must be non-null");
+  if (p->struct_size != (int32_t)sizeof(ls_indexer_params))
+    return fail(LS_ERR_INVALID, "params.struct_size %d != %d", p->struct_size,
+                (int)sizeof(ls_indexer_params));
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  const bool tokens = p->granularity == LS_SEL_TOKENS;
+  if (!tokens && p->granularity != LS_SEL_BLOCKS)
+    return fail(LS_ERR_INVALID, "granularity %d (LS_SEL_TOKENS or LS_SEL_BLOCKS)", p->granularity);
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (num_heads != 16 && num_heads != 32 && num_heads != 64)
+    return fail(LS_ERR_UNSUPPORTED, "num_heads %d (supported: 16, 32, 64)", num_heads);
+  if (key_pool.num_pages < 1) return fail(LS_ERR_INVALID, "key_pool.num_pages must be >= 1");
+  if (key_pool.num_heads != 1)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.num_heads %d (supported: 1)", key_pool.num_heads);
+  if (key_pool.head_dim != 128)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.head_dim %d (supported: 128)", key_pool.head_dim);
+  if (key_pool.page_size != 16 && key_pool.page_size != 32 && key_pool.page_size != 64)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.page_size %d (supported: 16, 32, 64)",
+                key_pool.page_size);
+  if (p->topk < 0) return fail(LS_ERR_INVALID, "topk %d must be >= 0", p->topk);
+  if (p->n_sink < 0 || p->n_recent < 0) return fail(LS_ERR_INVALID, "n_sink/n_recent < 0");
+  int max_units;
+  if (tokens) {
+    if (key_pool.dtype != LS_DTYPE_FP8_E4M3FN)
+      return fail(LS_ERR_UNSUPPORTED, "token keys must be fp8_e4m3fn");
+    if (p->n_sink || p->n_recent)
+      return fail(LS_ERR_UNSUPPORTED, "forced units are supported for blocks only");
+    if (cand_blocks) {
+      if (!cand_counts || cand_cap < 1)
+        return fail(LS_ERR_INVALID, "cand_blocks needs cand_counts and cand_cap >= 1");
+      max_units = cand_cap * key_pool.page_size;
+    } else {
+      max_units = batch.max_blocks * key_pool.page_size;
+    }
+    if (batch.batch_size > 0 && (max_units < 1 || max_units > ls::kIdxMaxUnits))
+      return fail(LS_ERR_UNSUPPORTED, "%d tokens per request (supported: <= %d)", max_units,
+                  ls::kIdxMaxUnits);
+    if (p->max_selected < p->topk)
+      return fail(LS_ERR_INVALID, "max_selected %d < topk %d", p->max_selected, p->topk);
+  } else {
+    if (key_pool.dtype != LS_DTYPE_BF16)
+      return fail(LS_ERR_UNSUPPORTED, "block summaries must be bf16");
+    if (key_scales) return fail(LS_ERR_INVALID, "key_scales must be NULL for block summaries");
+    if (cand_blocks) return fail(LS_ERR_UNSUPPORTED, "candidate lists are for tokens only");
+    if (batch.batch_size > 0 && batch.max_blocks > 16384)
+      return fail(LS_ERR_UNSUPPORTED, "max_blocks %d (supported: <= 16384)", batch.max_blocks);
+    max_units = batch.max_blocks;
+    const long long need = std::min<long long>(batch.max_blocks,
+                                               (long long)p->topk + p->n_sink + p->n_recent + 1);
+    if (p->max_selected < need)
+      return fail(LS_ERR_INVALID, "max_selected %d < %lld (largest possible selection)",
+                  p->max_selected, need);
+  }
+  if (batch.batch_size == 0) return ok();
+  if (!q || !head_weights || !keys || !selected || !selected_count)
+    return fail(LS_ERR_INVALID, "q, head_weights, keys, selected and selected_count must be non-null");
+  if (!aligned16(q) || !aligned16(keys))
+    return fail(LS_ERR_INVALID, "q and keys must be 16-byte aligned");
+  const size_t ws = ls_indexer_select_workspace_size(batch.batch_size, p->granularity, max_units);
+  if (!workspace || workspace_bytes < ws)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+
+  const size_t B = (size_t)batch.batch_size;
+  const int U = ls_indexer_score_stride(p->granularity, max_units);
+  char* w = static_cast<char*>(workspace);
+  ls::IndexerArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.w = head_weights;
+  a.keys = keys;
+  a.scales = key_scales;
+  a.b = batch_args(batch, key_pool);
+  a.num_heads = num_heads;
+  a.cand_blocks = cand_blocks;
+  a.cand_counts = cand_counts;
+  a.cand_cap = cand_cap;
+  a.max_units = U;
+  a.n_sink = p->n_sink;
+  a.n_recent = p->n_recent;
+  a.scores = scores_out ? scores_out : reinterpret_cast<float*>(w);
+  w += align_up(B * U * sizeof(float));
+  a.topk = p->topk;
+  a.max_selected = p->max_selected;
+  a.selected = selected;
+  a.selected_count = selected_count;
+  // enough workgroups to cover the chip: 1024 units each unless that leaves
+  // fewer than ~512 workgroups
+  int tiles = 64;
+  while (tiles > 4 && (long long)B * ((U + 16 * tiles - 1) / (16 * tiles)) < 512) tiles /= 2;
+  a.tiles_per_wg = tiles;
+  if (!tokens) {
+    hipError_t e = ls::launch_indexer_score(a, ls::kIdxBlocks, stream);
+    if (e != hipSuccess) return hip_status(e, "indexer score kernel launch");
+    ls::TopkArgs ta{};
+    ta.scores = a.scores;
+    ta.b = a.b;
+    ta.num_kv_heads = 1;
+    ta.topk = p->topk;
+    ta.keep_ratio = 0.0f;
+    ta.n_sink = p->n_sink;
+    ta.n_recent = p->n_recent;
+    ta.max_selected = p->max_selected;
+    ta.selected = selected;
+    ta.selected_count = selected_count;
+    return hip_status(ls::launch_topk(ta, stream), "top-k kernel launch");
+  }
+  a.hist = reinterpret_cast<uint32_t*>(w);
+  w += align_up(B * ls::kIdxBins * sizeof(uint32_t));
+  a.ctl = reinterpret_cast<uint32_t*>(w);
+  w += align_up(B * 4 * sizeof(uint32_t));
+  a.cand = reinterpret_cast<uint2*>(w);
+  w += align_up(B * ls::kIdxCandCap * sizeof(uint2));
+  a.bitmap = reinterpret_cast<uint32_t*>(w);
+  return hip_status(ls::launch_indexer_token_select(a, stream), "indexer selection launches");
+}
+
+// ------------------------------------------------------------ sparse MLA ----
+
+int32_t ls_mla_num_splits(int32_t max_tokens) {
+  if (max_tokens < 1) return 1;
+  return (max_tokens + ls::kMlaSplitTokens - 1) / ls::kMlaSplitTokens;
+}
+
+size_t ls_sparse_mla_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
+                                           int32_t max_tokens) {
+  if (batch_size <= 0 || num_q_heads <= 0) return 0;
+  return align_up((size_t)batch_size * num_q_heads * ls_mla_num_splits(max_tokens) * (512 + 4) *
+                  sizeof(float));
+}
+
+ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                               const void* latent, ls_pool pool, ls_batch batch,
+                               const int32_t* selected, const int32_t* selected_count,
+                               int32_t max_selected, float sm_scale, void* out,
+                               int32_t out_dtype, float* lse_out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (out_dtype != LS_DTYPE_BF16 && out_dtype != LS_DTYPE_FP32)
+    return fail(LS_ERR_UNSUPPORTED, "out_dtype %d (supported: bf16, fp32)", out_dtype);
+  if (pool.num_pages < 1) return fail(LS_ERR_INVALID, "pool.num_pages must be >= 1");
+  if (pool.num_heads != 1 || pool.head_dim != 576 || pool.dtype != LS_DTYPE_BF16)
+    return fail(LS_ERR_UNSUPPORTED, "latent pool must be bf16 with num_heads 1 and head_dim 576");
+  if (pool.page_size < 1 || pool.page_size > 1024)
+    return fail(LS_ERR_UNSUPPORTED, "pool.page_size %d (supported: 1 .. 1024)", pool.page_size);
+  if (num_q_heads < 16 || num_q_heads > 256 || num_q_heads % 16 != 0)
+    return fail(LS_ERR_UNSUPPORTED, "num_q_heads %d (supported: multiples of 16 up to 256)",
+                num_q_heads);
+  if ((selected == nullptr) != (selected_count == nullptr))
+    return fail(LS_ERR_INVALID, "selected and selected_count must both be set or both NULL");
+  if (selected && max_selected < 1) return fail(LS_ERR_INVALID, "max_selected must be >= 1");
+  if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
+  if (batch.batch_size == 0) return ok();
+  if (!q || !latent || !out) return fail(LS_ERR_INVALID, "q, latent and out must be non-null");
+  if (!aligned16(q) || !aligned16(latent))
+    return fail(LS_ERR_INVALID, "q and latent must be 16-byte aligned");
+  const long long dense = (long long)batch.max_blocks * pool.page_size;
+  if (!selected && dense > (1 << 24))
+    return fail(LS_ERR_UNSUPPORTED, "dense MLA over %lld tokens (supported: <= 2^24)", dense);
+  const int cap = selected ? max_selected : (int)dense;
+  const size_t ws = ls_sparse_mla_decode_workspace_size(batch.batch_size, num_q_heads, cap);
+  if (!workspace || workspace_bytes < ws)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  ls::MlaArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.latent = static_cast<const uint16_t*>(latent);
+  a.b = batch_args(batch, pool);
+  a.num_q_heads = num_q_heads;
+  a.selected = selected;
+  a.selected_count = selected_count;
+  a.max_selected = selected ? max_selected : 0;
+  a.num_splits = ls_mla_num_splits(cap);
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.partials = static_cast<float*>(workspace);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.lse = lse_out;
+  return hip_status(ls::launch_mla(a, stream), "MLA kernel launches");
 }
 
 }  // extern "C"

@@ -7,6 +7,8 @@
 namespace ls {
 
 constexpr int kWave = 64;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 

@@ -83,6 +83,65 @@ hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st);
 hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,
                             hipStream_t st);
 
+// Learned-indexer selection (k_indexer.hip): scoring of tokens (fp8 keys) or
+// blocks (bf16 block-mean keys) and the token top-k.
+constexpr int kIdxBins = 4096;          // first radix digit: score key bits [31:20]
+constexpr int kIdxMarkUnits = 4096;     // units per mark workgroup (score row strides are multiples)
+constexpr int kIdxCandCap = 8192;       // candidates of the threshold bin ranked from LDS
+constexpr int kIdxMaxUnits = 262144;    // units per request (token mode)
+
+enum { kIdxTokens = 0, kIdxBlocks = 1 };
+
+struct IndexerArgs {
+  const uint16_t* q;           // [B][H][128] bf16
+  const float* w;              // [B][H]
+  const void* keys;            // tokens: fp8 [num_pages][P][128]; blocks: bf16 [num_pages][128]
+  const float* scales;         // tokens: [num_pages][P] or null (1); blocks: unused
+  BatchArgs b;
+  int32_t num_heads;
+  const int32_t* cand_blocks;  // tokens, optional: [B][cand_cap] ascending block ids
+  const int32_t* cand_counts;  // [B]
+  int32_t cand_cap;
+  int32_t max_units;           // row stride of scores (units per request, max)
+  int32_t tiles_per_wg;        // multiple of 4, <= 128
+  int32_t n_sink, n_recent;    // blocks mode: forced blocks (not scored)
+  float* scores;               // [B][max_units]
+  uint32_t* hist;              // tokens: [B][kIdxBins]
+  int32_t topk;
+  int32_t max_selected;
+  uint32_t* ctl;               // tokens: [B][4] (candidates, arrivals)
+  uint2* cand;                 // tokens: [B][kIdxCandCap] (key, unit)
+  uint32_t* bitmap;            // tokens: [B][max_units / 32]
+  int32_t* selected;           // tokens: [B][max_selected]
+  int32_t* selected_count;     // tokens: [B]
+};
+
+hipError_t launch_indexer_score(const IndexerArgs& a, int mode, hipStream_t st);
+// zero the histogram and counters, score, mark + finish (three launches)
+hipError_t launch_indexer_token_select(const IndexerArgs& a, hipStream_t st);
+
+// Sparse MLA attention (k_mla.hip): one workgroup per (request, 16 query
+// heads, kMlaSplitTokens selected tokens), then a log-sum-exp combine.
+constexpr int kMlaSplitTokens = 256;
+
+struct MlaArgs {
+  const uint16_t* q;          // [B][H][576] bf16
+  const uint16_t* latent;     // [num_pages][P][576] bf16
+  BatchArgs b;
+  int32_t num_q_heads;
+  const int32_t* selected;    // [B][max_selected] token ids, or null (every cached token)
+  const int32_t* selected_count;
+  int32_t max_selected;
+  int32_t num_splits;
+  float sm_scale_log2;
+  float* partials;            // [B][H][S][512 + 4] (o, m, l, pad)
+  void* out;                  // [B][H][512]
+  int32_t out_dtype;
+  float* lse;
+};
+
+hipError_t launch_mla(const MlaArgs& a, hipStream_t st);
+
 // Blocks per attention split (one register-resident chunk per workgroup).
 constexpr int kAttnBlocksPerSplit = 8;
 
