@@ -342,6 +342,188 @@ def summarize_profiles(args) -> int:
     return 0
 
 
+
+# ------------------------------------------------- learned-indexer paths ----
+
+def indexer_step_bytes(cfg, coarse: bool):
+    """Algorithmic bytes of one learned-indexer step (per call, all requests).
+    Token keys are fp8 (1 B per dim) with one fp32 scale per token; latent
+    rows are 576 bf16 (the whole row is read: key = all 576 dims)."""
+    B, L, H, D, P = cfg.batch, cfg.context, cfg.index_heads, cfg.index_dim, cfg.page_size
+    k = cfg.topk_tokens
+    dk = cfg.kv_lora_dim + cfg.rope_dim
+    d = {"q_idx_w": B * H * (D * 2 + 4), "selection": B * k * 4,
+         "mla_kv": B * k * dk * 2, "q_mla": B * cfg.mla_heads * dk * 2,
+         "out": B * cfg.mla_heads * cfg.kv_lora_dim * 2}
+    if coarse:
+        nb = L // P
+        kb = cfg.coarse_topk_blocks + 1                  # + the forced last block
+        d["coarse_summaries"] = B * (nb - 1) * D * 2     # every complete, non-forced block
+        d["block_selection"] = B * kb * 4
+        d["candidate_keys"] = B * kb * P * (D + 4)
+    else:
+        d["indexer_keys"] = B * L * (D + 4)
+    d["total"] = sum(d.values())
+    return d
+
+
+def bench_indexer(args, coarse: bool) -> int:
+    """Time the learned-indexer path: token top-k over every cached token
+    (128K workload) or coarse block top-k -> exact token top-k among the kept
+    blocks (950K workload), then sparse MLA over the selected tokens."""
+    import torch
+    import query_aware_sparse_ls_amd as ls
+    from workloads import (COARSE_TO_FINE_950K, INDEXER_128K, indexer_queries,
+                           make_indexer_inputs)
+    cfg = COARSE_TO_FINE_950K if coarse else INDEXER_128K
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, P, k = cfg.batch, cfg.page_size, cfg.topk_tokens
+    nb = cfg.context // P
+    sm = 1.0 / math.sqrt(cfg.kv_lora_dim + cfg.rope_dim)
+    R = max(1, args.replicas)
+    reps = []
+    base = make_indexer_inputs(cfg, device=dev)
+    summ = None
+    if coarse:
+        # one cache; replicas differ in their queries and own a copy of the
+        # block means (read in full every step)
+        npg = base.idx_keys.shape[0]
+        summ = torch.zeros(npg, cfg.index_dim, dtype=torch.bfloat16, device=dev)
+        ls.build_block_summaries(base.idx_keys, torch.arange(npg, dtype=torch.int32, device=dev),
+                                 summ, key_scales=base.idx_scale)
+    for i in range(R):
+        if coarse:
+            q_idx, w, q_mla = indexer_queries(cfg, cfg.seed + 7 * i, dev)
+            inp = base
+            rep = dict(q_idx=q_idx, w=w, q_mla=q_mla, summ=summ.clone())
+        else:
+            inp = base if i == 0 else make_indexer_inputs(cfg, device=dev, seed=cfg.seed + 7 * i)
+            rep = dict(q_idx=inp.q_idx, w=inp.head_w, q_mla=inp.q_mla)
+        rep.update(inp=inp,
+                   ib=ls.PagedBatch(inp.idx_indptr, inp.idx_indices, inp.seq_lens, nb),
+                   kb=ls.PagedBatch(inp.kv_indptr, inp.kv_indices, inp.seq_lens, nb),
+                   sel=torch.empty(B, k, dtype=torch.int32, device=dev),
+                   cnt=torch.empty(B, dtype=torch.int32, device=dev),
+                   out=torch.empty(B, cfg.mla_heads, cfg.kv_lora_dim, dtype=torch.bfloat16,
+                                   device=dev),
+                   ws_mla=torch.empty(ls.sparse_mla_decode_workspace_size(B, cfg.mla_heads, k),
+                                      dtype=torch.uint8, device=dev))
+        if coarse:
+            kb = cfg.coarse_topk_blocks + 2
+            rep.update(bsel=torch.empty(B, kb, dtype=torch.int32, device=dev),
+                       bcnt=torch.empty(B, dtype=torch.int32, device=dev),
+                       ws_b=torch.empty(ls.indexer_select_workspace_size(B, "blocks", nb),
+                                        dtype=torch.uint8, device=dev),
+                       ws_t=torch.empty(ls.indexer_select_workspace_size(B, "tokens", kb * P),
+                                        dtype=torch.uint8, device=dev))
+        else:
+            rep["ws_t"] = torch.empty(ls.indexer_select_workspace_size(B, "tokens", nb * P),
+                                      dtype=torch.uint8, device=dev)
+        reps.append(rep)
+    torch.cuda.synchronize()
+    print(f"# {R} replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
+
+    def c_blocks(rp):
+        ls.indexer_select(rp["q_idx"], rp["w"], rp["summ"], P, rp["ib"], granularity="blocks",
+                          topk=cfg.coarse_topk_blocks, n_recent=1,
+                          max_selected=cfg.coarse_topk_blocks + 2, selected=rp["bsel"],
+                          selected_count=rp["bcnt"], workspace=rp["ws_b"])
+
+    def c_tokens(rp):
+        inp = rp["inp"]
+        ls.indexer_select(rp["q_idx"], rp["w"], inp.idx_keys, P, rp["ib"], granularity="tokens",
+                          topk=k, max_selected=k, key_scales=inp.idx_scale,
+                          cand_blocks=rp.get("bsel"), cand_counts=rp.get("bcnt"),
+                          selected=rp["sel"], selected_count=rp["cnt"], workspace=rp["ws_t"])
+
+    def c_mla(rp):
+        ls.sparse_mla_decode(rp["q_mla"], rp["inp"].latent, rp["kb"], rp["sel"], rp["cnt"],
+                             sm_scale=sm, out=rp["out"], workspace=rp["ws_mla"])
+
+    calls = ([("coarse_block_select", c_blocks)] if coarse else []) + \
+        [("token_select", c_tokens), ("sparse_mla", c_mla)]
+
+    def step(rp):
+        for _, f in calls:
+            f(rp)
+
+    for i in range(max(1, args.warmup)):
+        step(reps[i % R])
+    torch.cuda.synchronize()
+    main_stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(main_stream)
+    with torch.cuda.stream(cap):
+        for rp in reps:
+            step(rp)
+    main_stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for rp in reps:
+            step(rp)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    replays = max(1, args.steps // R)
+    steps = replays * R
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # per-call durations: n launches of one call back to back between events
+    n = min(steps, 4 * R)
+    per = {}
+    for name, f in calls:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(1e8))
+        a.record()
+        for i in range(n):
+            f(reps[i % R])
+        b.record()
+        torch.cuda.synchronize()
+        per[name] = a.elapsed_time(b) / n
+    nbytes = indexer_step_bytes(cfg, coarse)
+    gbps = nbytes["total"] / (ms * 1e-3) / 1e9
+    dom = max(per, key=per.get)
+    if dom == "token_select":
+        dbytes = (nbytes["candidate_keys"] if coarse else nbytes["indexer_keys"]) + \
+            nbytes["q_idx_w"] + nbytes["selection"]
+    elif dom == "sparse_mla":
+        dbytes = nbytes["mla_kv"] + nbytes["q_mla"] + nbytes["out"] + nbytes["selection"]
+    else:
+        dbytes = nbytes["coarse_summaries"] + nbytes["q_idx_w"] + nbytes["block_selection"]
+    dgbps = dbytes / (per[dom] * 1e-3) / 1e9
+    res = {"metric": ("coarse-to-fine indexer selection + sparse MLA decode calls/sec"
+                      if coarse else "learned-indexer token selection + sparse MLA decode calls/sec"),
+           "value": round(1e3 / ms, 1), "unit": "calls/s", "n_gpus": 1, "steps": steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg.name, "batch": B, "context": cfg.context,
+                      "index_heads": cfg.index_heads, "topk_tokens": k,
+                      "mla_heads": cfg.mla_heads, "page_size": P, "replicas": R,
+                      **({"coarse_topk_blocks": cfg.coarse_topk_blocks} if coarse else {})},
+           "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
+           "achieved_GBps_step": round(gbps, 1),
+           "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
+           "call_ms": {kk: round(v, 5) for kk, v in per.items()},
+           "roofline": {"kernel": dom + " (library call)", "bound": "hbm",
+                        "achieved": round(dgbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(dgbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "algorithmic_bytes_per_launch": dbytes,
+                        "avg_launch_ms": round(per[dom], 5)},
+           "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,6 +544,10 @@ def main(argv=None) -> int:
               "copy-fetch-cmd", "copy-write-cmd"):
         ap.add_argument("--" + a, default="")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine"),
+                    default="block-topk",
+                    help="block-topk: the 8B/32K/B16 block top-k step (default); indexer: "
+                         "token top-2048 of 8 x 128K + sparse MLA; coarse-to-fine: 4 x 950K")
     args = ap.parse_args(argv)
     if args.summarize_profiles:
         return summarize_profiles(args)
@@ -371,6 +557,8 @@ def main(argv=None) -> int:
         return 2
     if args.copy_calibrate:
         return copy_calibration(args.copy_calibrate)
+    if args.path != "block-topk":
+        return bench_indexer(args, coarse=args.path == "coarse-to-fine")
 
     import torch
     import query_aware_sparse_ls_amd as ls

@@ -23,19 +23,20 @@
 // leaves every dot product unchanged (the sum over dims is over the same
 // pairs).
 //
-// Token top-k (k of up to 262,144 units per request, ties to the lowest unit):
-//  1. the scoring workgroups histogram the top 12 bits of an order-preserving
-//     integer key of their scores in LDS and add the non-zero bins into a
-//     per-request global histogram (device-scope atomics);
-//  2. the mark kernel finds, per request, the bin b* holding the k-th score;
-//     units above b* are selected (bitmap), units in b* become candidates
-//     (key, unit) appended to a per-request list;
-//  3. the last mark workgroup of each request (arrival counter) ranks the
-//     candidates by the remaining 20 key bits (two 10-bit histogram passes),
-//     sets the bitmap bits of those above the k-th key, takes the units equal
-//     to it lowest index first, and emits the bitmap in ascending order.
-//     If b* holds more candidates than fit in LDS, the same ranking streams
-//     the request's scores instead (slower, same result).
+// Token top-k (k of up to 262,144 units per request, ties to the lowest unit),
+// a three-digit radix select over an order-preserving integer key of the
+// scores:
+//  1. the scoring workgroups histogram the key's top 12 bits in LDS and add
+//     the non-zero bins into a per-request global histogram (device-scope
+//     atomics);
+//  2. the mark kernel finds, per request, the bucket b* holding the k-th
+//     score; units above b* are selected (bitmap), units in b* are appended
+//     to a per-request list and histogrammed by their next 12 key bits;
+//  3. the last mark workgroup of each request (arrival counter) finds the
+//     second digit from that histogram, the third (last 8 bits) in one pass
+//     over the list, marks the listed units above the k-th key, takes the
+//     ones equal to it lowest index first, and emits the bitmap in ascending
+//     order.
 #pragma once
 
 #include "ls_internal.h"
@@ -45,7 +46,7 @@ namespace ls {
 constexpr int kIdxDim = 128;            // indexer key / query dim
 constexpr int kIdxThreads = 256;
 constexpr int kIdxWaves = kIdxThreads / kWave;
-constexpr int kIdxPrefetch = 4;         // key tiles in flight per wave
+constexpr int kIdxPrefetch = 6;         // key tiles in flight per wave
 constexpr int kIdxMaxTilesPerWg = 128;  // units per scoring workgroup <= 2048
 constexpr int kIdxMaxWords = kIdxMaxUnits / 32;
 

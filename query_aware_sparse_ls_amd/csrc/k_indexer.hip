@@ -241,28 +241,23 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
 
 __global__ __launch_bounds__(kIdxThreads) void idx_zero_kernel(uint32_t* hist, uint32_t* ctl,
                                                                int batch) {
-  const int n = batch * kIdxBins;
+  const int n = 2 * batch * kIdxBins;   // first-digit and second-digit histograms
   for (int i = blockIdx.x * kIdxThreads + threadIdx.x; i < n; i += gridDim.x * kIdxThreads)
     hist[i] = 0u;
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < batch * 4; i += kIdxThreads) ctl[i] = 0u;
 }
 
-struct IdxFinLds {
-  uint32_t bm[kIdxMaxWords];
-  uint32_t tie[kIdxMaxWords];
-  uint32_t ckey[kIdxCandCap];
-  int32_t cunit[kIdxCandCap];
-  int32_t h2[1024];
-};
+constexpr int kIdxMarkThreads = 512;
+constexpr int kIdxMarkWaves = kIdxMarkThreads / kWave;
 
 struct IdxMarkLds {
-  union {
-    uint32_t hist[kIdxBins];
-    IdxFinLds fin;
-  } u;
-  int red[kIdxWaves];
-  int bstar, cabove, cat, kr, nvalid, last, b2, need;
+  uint32_t h[kIdxBins];        // digit histograms (first, then second, then third digit)
+  uint32_t h2[kIdxBins];       // this workgroup's second-digit histogram of bucket b*
+  uint32_t bm[kIdxMaxWords];   // finish: selected units
+  uint32_t tie[kIdxMaxWords];  // finish: units equal to the k-th key
+  int red[kIdxMarkWaves];
+  int bstar, cabove, kr, last, b2, above2, b3, above3;
 };
 
 // Exclusive prefix sum over the workgroup in thread order; *total = sum.
@@ -273,7 +268,7 @@ __device__ __forceinline__ int idx_block_scan(int v, int* red, int* total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kIdxWaves; ++w) {
+  for (int w = 0; w < kIdxMarkWaves; ++w) {
     const int x = red[w];
     before += w < wave ? x : 0;
     tot += x;
@@ -283,26 +278,26 @@ __device__ __forceinline__ int idx_block_scan(int v, int* red, int* total) {
   return before + inc - v;
 }
 
-// Digit search from the top: the bin b of h[0 .. nbins) (each thread owns
-// nbins / kIdxThreads consecutive bins) at which the count of elements in
-// bins > b is < need and the count in bins >= b is >= need. Returns (via
-// LDS) b and the count above it. need >= 1 and sum(h) >= need.
-__device__ __forceinline__ void idx_find_digit(const int32_t* h, int nbins, int need, int* red,
+// Digit search from the top over h[0 .. nbins) (nbins a multiple of the
+// workgroup size): the bin b with (count above b) < need <= (count at or
+// above b). Writes b and the count above it (one thread), then synchronises.
+// need >= 1 and sum(h) >= need.
+__device__ __forceinline__ void idx_find_digit(const uint32_t* h, int nbins, int need, int* red,
                                                int* b_out, int* above_out) {
-  const int per = nbins / kIdxThreads, t = threadIdx.x;
+  const int per = nbins / kIdxMarkThreads, t = threadIdx.x;
   int mine = 0;
-  for (int i = 0; i < per; ++i) mine += h[t * per + i];
+  for (int i = 0; i < per; ++i) mine += (int)h[t * per + i];
   int tot;
   const int excl = idx_block_scan(mine, red, &tot);
   int above = tot - excl - mine;   // elements in bins of higher threads
   if (above < need && above + mine >= need) {
     for (int b = t * per + per - 1; b >= t * per; --b) {
-      if (above + h[b] >= need) {
+      if (above + (int)h[b] >= need) {
         *b_out = b;
         *above_out = above;
         break;
       }
-      above += h[b];
+      above += (int)h[b];
     }
   }
   __syncthreads();
@@ -315,7 +310,10 @@ __device__ __forceinline__ int idx_token_of(const IndexerArgs& a, const IdxUnits
   return a.cand_blocks[(size_t)r * a.cand_cap + u / P] * P + u % P;
 }
 
-__global__ __launch_bounds__(kIdxThreads) void idx_mark_kernel(IndexerArgs a) {
+// Second digit of a score key: bits [19:8]; third digit: bits [7:0].
+__device__ __forceinline__ uint32_t idx_d2(uint32_t key) { return (key >> 8) & 0xFFFu; }
+
+__global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a) {
   __shared__ IdxMarkLds sh;
   const int r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();
@@ -324,37 +322,39 @@ __global__ __launch_bounds__(kIdxThreads) void idx_mark_kernel(IndexerArgs a) {
   uint32_t* bmrow = a.bitmap + (size_t)r * nwords_row;
   uint32_t* ctl = a.ctl + (size_t)r * 4;
   const float* srow = a.scores + (size_t)r * a.max_units;
+  uint2* crow = a.cand + (size_t)r * a.max_units;
+  uint32_t* gh2 = a.hist + ((size_t)a.b.batch + r) * kIdxBins;
 
-  // 1. threshold bin from the request's histogram
+  // 1. threshold bucket b* from the request's first-digit histogram
   const uint32_t* gh = a.hist + (size_t)r * kIdxBins;
-  for (int i = tid; i < kIdxBins; i += kIdxThreads) sh.u.hist[i] = gh[i];
+  for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) {
+    sh.h[i] = gh[i];
+    sh.h2[i] = 0u;
+  }
   if (tid == 0) {
     sh.bstar = kIdxBins;   // nothing definite, no candidates
     sh.cabove = 0;
-    sh.cat = 0;
   }
   __syncthreads();
   {
     int mine = 0;
-    constexpr int per = kIdxBins / kIdxThreads;
-    for (int i = 0; i < per; ++i) mine += (int)sh.u.hist[tid * per + i];
+    constexpr int per = kIdxBins / kIdxMarkThreads;
+    for (int i = 0; i < per; ++i) mine += (int)sh.h[tid * per + i];
     int tot;
     const int excl = idx_block_scan(mine, sh.red, &tot);
     const int kr = a.topk < tot ? a.topk : tot;
     if (tid == 0) {
       sh.kr = kr;
-      sh.nvalid = tot;
       if (kr >= tot && tot > 0) sh.bstar = -1;   // every valid unit is selected
     }
     if (kr > 0 && kr < tot) {
       int above = tot - excl - mine;
       if (above < kr && above + mine >= kr) {
         for (int b = tid * per + per - 1; b >= tid * per; --b) {
-          const int hb = (int)sh.u.hist[b];
+          const int hb = (int)sh.h[b];
           if (above + hb >= kr) {
             sh.bstar = b;
             sh.cabove = above;
-            sh.cat = hb;
             break;
           }
           above += hb;
@@ -363,123 +363,167 @@ __global__ __launch_bounds__(kIdxThreads) void idx_mark_kernel(IndexerArgs a) {
     }
   }
   __syncthreads();
-  const int bstar = sh.bstar, cat = sh.cat;
-  const bool collect = bstar >= 0 && bstar < kIdxBins && cat <= kIdxCandCap;
+  const int bstar = sh.bstar;
+  const bool refine = bstar >= 0 && bstar < kIdxBins;
 
-  // 2. mark this chunk's units: selected bits, and candidates in bin b*
+  // 2. this chunk: selected bits above b*; units of b* to the candidate list
+  // and into the second-digit histogram
   const int cu0 = chunk * kIdxMarkUnits;
-  for (int it = 0; it < kIdxMarkUnits / kIdxThreads; ++it) {
-    const int ub = cu0 + it * kIdxThreads + wave * kWave;   // wave's 64 units
-    if (ub >= g.n) break;                                    // uniform per wave
-    const int u = ub + lane;
+  constexpr int IT = kIdxMarkUnits / kIdxMarkThreads;
+  float sv[IT];
+  bool vv[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {   // all of this thread's score loads in flight at once
+    const int u = cu0 + it * kIdxMarkThreads + wave * kWave + lane;
     int tok;
-    const bool valid = idx_unit_block(a, g, r, u, &tok) >= 0;
-    uint32_t key = 0u, bin = 0u;
-    if (valid) {
-      key = score_key(srow[u]);
-      bin = idx_bin(key);
-    }
-    const bool def = valid && (bstar < 0 || (int)bin > bstar);
-    const bool cnd = collect && valid && (int)bin == bstar;
+    vv[it] = idx_unit_block(a, g, r, u, &tok) >= 0;
+    sv[it] = vv[it] ? srow[u] : 0.0f;
+  }
+  // selected bits; this wave's bucket-b* units counted first, so that the
+  // workgroup reserves its slots of the list with ONE returning atomic
+  uint32_t key[IT];
+  unsigned long long cmask[IT];
+  int wcount = 0;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int ub = cu0 + it * kIdxMarkThreads + wave * kWave;   // wave's 64 units
+    const bool valid = vv[it];
+    key[it] = valid ? score_key(sv[it]) : 0u;
+    const int bin = (int)idx_bin(key[it]);
+    const bool def = valid && (bstar < 0 || bin > bstar);
+    cmask[it] = __ballot(refine && valid && bin == bstar);
+    wcount += __popcll(cmask[it]);
     const unsigned long long dm = __ballot(def);
-    if (lane == 0) {
+    if (lane == 0 && ub < g.n) {
       st_dev(bmrow + ub / 32, (uint32_t)dm);
       st_dev(bmrow + ub / 32 + 1, (uint32_t)(dm >> 32));
     }
-    const unsigned long long cm = __ballot(cnd);
-    if (cm) {
-      int base = 0;
-      if (lane == 0) base = (int)atomicAdd(ctl, (uint32_t)__popcll(cm));
-      base = __shfl(base, 0);
-      if (cnd) {
-        const int pos = base + mbcnt(cm);
-        if (pos < kIdxCandCap) st_dev(a.cand + (size_t)r * kIdxCandCap + pos, make_uint2(key, (uint32_t)u));
-      }
-    }
   }
-  // 3. arrival; the last workgroup of the request finishes it (every thread's
-  // bitmap and candidate stores are complete and visible device-wide before
-  // the workgroup's arrival is counted)
-  __threadfence();
+  if (lane == 0) sh.red[wave] = wcount;
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(ctl + 1, 1u, __ATOMIC_ACQ_REL,
+    int tot = 0;
+    for (int w = 0; w < kIdxMarkWaves; ++w) {
+      const int c = sh.red[w];
+      sh.red[w] = tot;   // the wave's offset in the workgroup's slots
+      tot += c;
+    }
+    sh.b2 = tot ? (int)atomicAdd(ctl, (uint32_t)tot) : 0;   // the workgroup's first slot
+  }
+  __syncthreads();
+  int cpos = sh.b2 + sh.red[wave];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const unsigned long long cm = cmask[it];
+    if (cm) {
+      if ((cm >> lane) & 1ull) {
+        const int u = cu0 + it * kIdxMarkThreads + wave * kWave + lane;
+        st_dev(crow + cpos + mbcnt(cm), make_uint2(key[it], (uint32_t)u));
+        atomicAdd(&sh.h2[idx_d2(key[it])], 1u);
+      }
+      cpos += __popcll(cm);
+    }
+  }
+  __syncthreads();
+  if (refine) {
+    for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) {
+      const uint32_t c = sh.h2[i];
+      if (c) atomicAdd(gh2 + i, c);
+    }
+  }
+  // 3. arrival; the last workgroup of the request finishes it. Everything
+  // handed over (bitmap words, listed units, histogram adds, the list
+  // counter) goes through device-coherent stores or atomics, which write
+  // through the XCD's L2, and every thread waits for its own to complete
+  // before the workgroup's arrival is counted (no release fence: that would
+  // write back the whole L2 under every other workgroup). The finishing
+  // workgroup takes one acquire fence (its XCD's L2 drops stale lines) and
+  // then reads everything with plain, pipelined loads.
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(ctl + 1, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     sh.last = prev == gridDim.x - 1;
   }
   __syncthreads();
   if (!sh.last) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  IdxFinLds& f = sh.u.fin;   // the histogram is no longer needed
   const int kr = sh.kr;
   const int nwr = (g.n + 31) / 32;
-  for (int w = tid; w < nwr; w += kIdxThreads) {
-    f.bm[w] = ld_dev(bmrow + w);
-    f.tie[w] = 0u;
+  for (int w = tid; w < nwr; w += kIdxMarkThreads) {
+    sh.bm[w] = bmrow[w];
+    sh.tie[w] = 0u;
   }
   int ties_to_take = 0;
-  if (bstar >= 0 && bstar < kIdxBins) {
-    const int need = kr - sh.cabove;   // >= 1 units of bin b* to select
-    int nc = collect ? (int)ld_dev(ctl) : 0;
-    nc = nc < kIdxCandCap ? nc : kIdxCandCap;
-    if (collect) {
-      for (int i = tid; i < nc; i += kIdxThreads) {
-        const uint2 c = ld_dev(a.cand + (size_t)r * kIdxCandCap + i);
-        f.ckey[i] = c.x;
-        f.cunit[i] = (int)c.y;
+  if (refine) {
+    const int need = kr - sh.cabove;   // >= 1 units of bucket b* to select
+    const int nc = (int)ld_dev(ctl);   // units in bucket b*
+    for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) sh.h[i] = gh2[i];
+    __syncthreads();
+    idx_find_digit(sh.h, kIdxBins, need, sh.red, &sh.b2, &sh.above2);
+    const uint32_t b2 = (uint32_t)sh.b2;
+    const int need2 = need - sh.above2;
+    // third digit over the candidates whose second digit is b2
+    for (int i = tid; i < 256; i += kIdxMarkThreads) sh.h[i] = 0u;
+    __syncthreads();
+    constexpr int UN = 4;   // candidate loads in flight per thread
+    for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
+      uint2 c[UN];
+#pragma unroll
+      for (int j = 0; j < UN; ++j) {
+        const int i = i0 + j * kIdxMarkThreads + tid;
+        c[j] = i < nc ? crow[i] : make_uint2(0u, 0xFFFFFFFFu);
+      }
+#pragma unroll
+      for (int j = 0; j < UN; ++j)
+        if (c[j].y != 0xFFFFFFFFu && idx_d2(c[j].x) == b2) atomicAdd(&sh.h[c[j].x & 255u], 1u);
+    }
+    __syncthreads();
+    {
+      // 256 bins over 512 threads: the first 256 threads own one bin each
+      const int t = tid;
+      const int mine = t < 256 ? (int)sh.h[t] : 0;
+      int tot;
+      const int excl = idx_block_scan(t < 256 ? mine : 0, sh.red, &tot);
+      const int above = tot - excl - mine;
+      if (t < 256 && above < need2 && above + mine >= need2) {
+        sh.b3 = t;
+        sh.above3 = above;
+      }
+      __syncthreads();
+    }
+    const uint32_t theta = ((uint32_t)bstar << 20) | (b2 << 8) | (uint32_t)sh.b3;
+    ties_to_take = need2 - sh.above3;
+    for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
+      uint2 c[UN];
+#pragma unroll
+      for (int j = 0; j < UN; ++j) {
+        const int i = i0 + j * kIdxMarkThreads + tid;
+        c[j] = i < nc ? crow[i] : make_uint2(0u, 0xFFFFFFFFu);
+      }
+#pragma unroll
+      for (int j = 0; j < UN; ++j) {
+        if (c[j].y == 0xFFFFFFFFu) continue;
+        const uint32_t u = c[j].y;
+        if (c[j].x > theta) atomicOr(&sh.bm[u >> 5], 1u << (u & 31));
+        else if (c[j].x == theta) atomicOr(&sh.tie[u >> 5], 1u << (u & 31));
       }
     }
-    // visit every candidate (unit in bin b*): from LDS, or by streaming the
-    // request's scores when they did not fit
-    auto for_each = [&](auto&& fn) {
-      if (collect) {
-        for (int i = tid; i < nc; i += kIdxThreads) fn(f.ckey[i], f.cunit[i]);
-      } else {
-        for (int u = tid; u < g.n; u += kIdxThreads) {
-          int tok;
-          if (idx_unit_block(a, g, r, u, &tok) < 0) continue;
-          const uint32_t key = score_key(srow[u]);
-          if ((int)idx_bin(key) == bstar) fn(key, u);
-        }
-      }
-    };
-    // second digit: key bits [19:10]
-    for (int i = tid; i < 1024; i += kIdxThreads) f.h2[i] = 0;
-    __syncthreads();
-    for_each([&](uint32_t key, int) { atomicAdd(&f.h2[(key >> 10) & 1023u], 1); });
-    __syncthreads();
-    idx_find_digit(f.h2, 1024, need, sh.red, &sh.b2, &sh.need);
-    const int b2 = sh.b2, need2 = need - sh.need;
-    // third digit: key bits [9:0] of the candidates with digit 2 == b2
-    for (int i = tid; i < 1024; i += kIdxThreads) f.h2[i] = 0;
-    __syncthreads();
-    for_each([&](uint32_t key, int) {
-      if ((int)((key >> 10) & 1023u) == b2) atomicAdd(&f.h2[key & 1023u], 1);
-    });
-    __syncthreads();
-    idx_find_digit(f.h2, 1024, need2, sh.red, &sh.b2, &sh.need);
-    const uint32_t theta = ((uint32_t)bstar << 20) | ((uint32_t)b2 << 10) | (uint32_t)sh.b2;
-    ties_to_take = need2 - sh.need;
-    for_each([&](uint32_t key, int u) {
-      if (key > theta) atomicOr(&f.bm[u >> 5], 1u << (u & 31));
-      else if (key == theta) atomicOr(&f.tie[u >> 5], 1u << (u & 31));
-    });
-    __syncthreads();
-  } else {
-    __syncthreads();
   }
+  __syncthreads();
 
   // 4. emit in ascending unit order: the bitmap plus the first ties
-  const int wpt = (nwr + kIdxThreads - 1) / kIdxThreads;
+  const int wpt = (nwr + kIdxMarkThreads - 1) / kIdxMarkThreads;
   const int w0 = tid * wpt, w1 = w0 + wpt < nwr ? w0 + wpt : nwr;
   int tcount = 0;
-  for (int w = w0; w < w1; ++w) tcount += __popc(f.tie[w]);
+  for (int w = w0; w < w1; ++w) tcount += __popc(sh.tie[w]);
   int ttot;
   int tpre = idx_block_scan(tcount, sh.red, &ttot);
   int scount = 0;
   for (int w = w0; w < w1; ++w) {
-    uint32_t x = f.tie[w], kept = 0u;
+    uint32_t x = sh.tie[w], kept = 0u;
     int take = ties_to_take - tpre;
     const int pc = __popc(x);
     take = take < 0 ? 0 : (take > pc ? pc : take);
@@ -489,15 +533,15 @@ __global__ __launch_bounds__(kIdxThreads) void idx_mark_kernel(IndexerArgs a) {
       x ^= low;
     }
     tpre += pc;
-    const uint32_t sel = f.bm[w] | kept;
-    f.bm[w] = sel;
+    const uint32_t sel = sh.bm[w] | kept;
+    sh.bm[w] = sel;
     scount += __popc(sel);
   }
   int stot;
   int pos = idx_block_scan(scount, sh.red, &stot);
   int32_t* out = a.selected + (size_t)r * a.max_selected;
   for (int w = w0; w < w1; ++w) {
-    uint32_t x = f.bm[w];
+    uint32_t x = sh.bm[w];
     while (x) {
       const int b = __ffs(x) - 1;
       x &= x - 1u;
@@ -505,7 +549,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_mark_kernel(IndexerArgs a) {
       ++pos;
     }
   }
-  for (int i = stot + tid; i < a.max_selected; i += kIdxThreads) out[i] = -1;
+  for (int i = stot + tid; i < a.max_selected; i += kIdxMarkThreads) out[i] = -1;
   if (tid == 0) a.selected_count[r] = stot < a.max_selected ? stot : a.max_selected;
 }
 
@@ -536,7 +580,7 @@ hipError_t launch_indexer_token_select(const IndexerArgs& a, hipStream_t st) {
   e = launch_score_mode<kIdxTokens>(a, st);
   if (e != hipSuccess) return e;
   dim3 grid((a.max_units + kIdxMarkUnits - 1) / kIdxMarkUnits, a.b.batch);
-  hipLaunchKernelGGL(idx_mark_kernel, grid, dim3(kIdxThreads), 0, st, a);
+  hipLaunchKernelGGL(idx_mark_kernel, grid, dim3(kIdxMarkThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ __device__ __forceinline__ uint32_t mla_bf16_split(float x, float* rest) {
   return b;
 }
 
-__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
+// two workgroups per CU (<= 256 registers per lane)
+__global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
   __shared__ MlaLds sh;
   const int S = a.num_splits;
   const int nrs = a.b.batch * S;
@@ -87,9 +88,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
 
   const bool out32 = a.out_dtype == LS_DTYPE_FP32;
   const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
-  // tile loads: chunk c = tid + 256 i -> token c / 72, 16 bytes at 8 (c % 72)
-  uint4 ld[kMlaChunksPerThread];
-  auto issue = [&](int t) {
+  // tile loads: chunk c = tid + 256 i -> token c / 72, 16 bytes at 8 (c % 72);
+  // two tiles of loads are in flight (register buffers A and B)
+  auto issue = [&](int t, uint4* ld) {
 #pragma unroll
     for (int i = 0; i < kMlaChunksPerThread; ++i) {
       const int c = tid + kMlaThreads * i;
@@ -102,16 +103,15 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m = kNegInf, l = 0.0f;   // state of head `col`
-  issue(0);
-  for (int t = 0; t < ntiles; ++t) {
-    // stage tile t, then start loading tile t + 1
+  auto tile_step = [&](int t, uint4* ld) {
+    // stage tile t, then start loading tile t + 2 into the same registers
 #pragma unroll
     for (int i = 0; i < kMlaChunksPerThread; ++i) {
       const int c = tid + kMlaThreads * i;
       *reinterpret_cast<uint4*>(sh.tile + (c / (kMlaDk / 8)) * kMlaRowWords + 4 * (c % (kMlaDk / 8))) = ld[i];
     }
     __syncthreads();
-    issue(t + 1);
+    issue(t + 2, ld);
     // partial logits over this wave's k-steps: rows = tokens, cols = heads
     f32x4_t z0 = {0.0f, 0.0f, 0.0f, 0.0f}, z1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -201,6 +201,13 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
       if (out32) o[n] = mfma_16x16x32(pm, vb, o[n]);
     }
     __syncthreads();   // the tile and the logit partials are rewritten next
+  };
+  uint4 ldA[kMlaChunksPerThread], ldB[kMlaChunksPerThread];
+  issue(0, ldA);
+  issue(1, ldB);
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, ldA);
+    if (t + 1 < ntiles) tile_step(t + 1, ldB);
   }
   // partial state: o rows = heads 4kq + i, column = dim 128 wave + 16 n + col
   float* part = a.partials + (((size_t)r * H + kMlaHeadsPerWg * hg) * S + s) * (kMlaPartStride);

@@ -402,10 +402,10 @@ size_t ls_indexer_select_workspace_size(int32_t batch_size, int32_t granularity,
   const size_t U = (size_t)ls_indexer_score_stride(granularity, max_units);
   size_t ws = align_up(B * U * sizeof(float));   // scores
   if (granularity == LS_SEL_TOKENS) {
-    ws += align_up(B * ls::kIdxBins * sizeof(uint32_t));    // histogram
-    ws += align_up(B * 4 * sizeof(uint32_t));               // counters
-    ws += align_up(B * ls::kIdxCandCap * sizeof(uint2));    // candidates
-    ws += align_up(B * (U / 32) * sizeof(uint32_t));        // bitmap
+    ws += align_up(2 * B * ls::kIdxBins * sizeof(uint32_t));   // digit histograms
+    ws += align_up(B * 4 * sizeof(uint32_t));                  // counters
+    ws += align_up(B * U * sizeof(uint2));                     // threshold-bucket units
+    ws += align_up(B * (U / 32) * sizeof(uint32_t));           // bitmap
   }
   return ws;
 }
@@ -504,9 +504,9 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
   a.max_selected = p->max_selected;
   a.selected = selected;
   a.selected_count = selected_count;
-  // enough workgroups to cover the chip: 1024 units each unless that leaves
-  // fewer than ~512 workgroups
-  int tiles = 64;
+  // enough workgroups to cover the chip: 2048 units each unless that leaves
+  // fewer than ~512 workgroups (two per CU)
+  int tiles = 128;
   while (tiles > 4 && (long long)B * ((U + 16 * tiles - 1) / (16 * tiles)) < 512) tiles /= 2;
   a.tiles_per_wg = tiles;
   if (!tokens) {
@@ -526,11 +526,11 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
     return hip_status(ls::launch_topk(ta, stream), "top-k kernel launch");
   }
   a.hist = reinterpret_cast<uint32_t*>(w);
-  w += align_up(B * ls::kIdxBins * sizeof(uint32_t));
+  w += align_up(2 * B * ls::kIdxBins * sizeof(uint32_t));
   a.ctl = reinterpret_cast<uint32_t*>(w);
   w += align_up(B * 4 * sizeof(uint32_t));
   a.cand = reinterpret_cast<uint2*>(w);
-  w += align_up(B * ls::kIdxCandCap * sizeof(uint2));
+  w += align_up(B * U * sizeof(uint2));
   a.bitmap = reinterpret_cast<uint32_t*>(w);
   return hip_status(ls::launch_indexer_token_select(a, stream), "indexer selection launches");
 }

@@ -87,7 +87,6 @@ hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnA
 // blocks (bf16 block-mean keys) and the token top-k.
 constexpr int kIdxBins = 4096;          // first radix digit: score key bits [31:20]
 constexpr int kIdxMarkUnits = 4096;     // units per mark workgroup (score row strides are multiples)
-constexpr int kIdxCandCap = 8192;       // candidates of the threshold bin ranked from LDS
 constexpr int kIdxMaxUnits = 262144;    // units per request (token mode)
 
 enum { kIdxTokens = 0, kIdxBlocks = 1 };
@@ -106,11 +105,11 @@ struct IndexerArgs {
   int32_t tiles_per_wg;        // multiple of 4, <= 128
   int32_t n_sink, n_recent;    // blocks mode: forced blocks (not scored)
   float* scores;               // [B][max_units]
-  uint32_t* hist;              // tokens: [B][kIdxBins]
+  uint32_t* hist;              // tokens: [2][B][kIdxBins] (first / second digit)
   int32_t topk;
   int32_t max_selected;
   uint32_t* ctl;               // tokens: [B][4] (candidates, arrivals)
-  uint2* cand;                 // tokens: [B][kIdxCandCap] (key, unit)
+  uint2* cand;                 // tokens: [B][max_units] (key, unit) of the threshold bucket
   uint32_t* bitmap;            // tokens: [B][max_units / 32]
   int32_t* selected;           // tokens: [B][max_selected]
   int32_t* selected_count;     // tokens: [B]

@@ -23,6 +23,7 @@ from .generate import (  # noqa: F401
     make_block_topk_inputs,
     IndexerInputs,
     make_indexer_inputs,
+    indexer_queries,
     bf16_bits,
     fp8_bits,
 )

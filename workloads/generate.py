@@ -247,16 +247,31 @@ def _clustered(n_tok: int, dim: int, n_clusters: int, sigma: float, dg, device):
     return out
 
 
+def _indexer_queries(cfg: IndexerConfig, cg: torch.Generator):
+    """Indexer queries (bf16), head weights (N(0,1)/sqrt(H), fp32) and MLA
+    queries (bf16), drawn in that order from the CPU generator."""
+    B = cfg.batch
+    q_idx = torch.randn(B, cfg.index_heads, cfg.index_dim, generator=cg).to(torch.bfloat16)
+    head_w = (torch.randn(B, cfg.index_heads, generator=cg) / math.sqrt(cfg.index_heads)).float()
+    q_mla = torch.randn(B, cfg.mla_heads, cfg.kv_lora_dim + cfg.rope_dim,
+                        generator=cg).to(torch.bfloat16)
+    return q_idx, head_w, q_mla
+
+
+def indexer_queries(cfg: IndexerConfig, seed: int, device="cpu"):
+    """Another set of (q_idx, head_w, q_mla) for the same cache: the first
+    draws of make_indexer_inputs(cfg, seed=seed)."""
+    q_idx, head_w, q_mla = _indexer_queries(cfg, _cpu_gen(seed))
+    return q_idx.to(device), head_w.to(device), q_mla.to(device)
+
+
 def make_indexer_inputs(cfg: IndexerConfig, device="cpu", seed: Optional[int] = None) -> IndexerInputs:
     seed = cfg.seed if seed is None else seed
     cg = _cpu_gen(seed)
     B, P, L = cfg.batch, cfg.page_size, cfg.context
     nb = (L + P - 1) // P
     used = B * nb
-    q_idx = torch.randn(B, cfg.index_heads, cfg.index_dim, generator=cg).to(torch.bfloat16)
-    head_w = (torch.randn(B, cfg.index_heads, generator=cg) / math.sqrt(cfg.index_heads)).float()
-    q_mla = torch.randn(B, cfg.mla_heads, cfg.kv_lora_dim + cfg.rope_dim,
-                        generator=cg).to(torch.bfloat16)
+    q_idx, head_w, q_mla = _indexer_queries(cfg, cg)
     idx_perm = torch.randperm(used, generator=cg).to(torch.int32)
     kv_perm = torch.randperm(used, generator=cg).to(torch.int32)
     indptr = torch.arange(0, used + 1, nb, dtype=torch.int32)
