@@ -141,7 +141,7 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
     for (int j = 0; j < NL; ++j) {
       const int p = page_of(k, j);
       badm |= (uint32_t)(p == -2) << j;
-      d[j] = ldg16(base + (uint64_t)(uint32_t)(p >= 0 ? p : 0) * pstride);
+      d[j] = ldg16_stream(base + (uint64_t)(uint32_t)(p >= 0 ? p : 0) * pstride);
     }
   };
   // score the staged tile and store the candidate rows (tiles past the
@@ -253,9 +253,23 @@ __device__ __forceinline__ uint32_t bf16_split(float x, float* rest) {
 // adds P . V with D/16 MFMAs per bf16 part of P. Blocks are prefetched
 // kItemPrefetch ahead per wave. The 8 wave states are merged in LDS in wave
 // order.
+// Floats of a pair's exchange area (two merged states of 4 heads: o, then m, l).
+template <int D>
+constexpr int kPairFloats = 2 * 4 * D + 16;
+
+// Exchange area of a (request, kv head) pair whose selection is attended by
+// two workgroups: each publishes its merged state (o[4][D], m[4], l[4]) and
+// the second to arrive merges both and writes the output.
+struct ItemPair {
+  float* part;         // [2][4][D] o, then [2][4][2] (m, l)
+  uint32_t* arrivals;  // zero before the launch
+  int half;            // which of the two workgroups this is
+};
+
 template <int D>
 __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const int* ent,
-                                          int cnt, ItemAttnLds<D>& sh) {
+                                          int cnt, ItemAttnLds<D>& sh,
+                                          const ItemPair* pair = nullptr) {
   using ST = Stage<D>;
   constexpr int KS = D / 32, NL = ST::NL, NT = D / 16, NPF = kItemPrefetch;
   constexpr int RW = ST::kVRowWords;
@@ -273,21 +287,25 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
   const uint16_t* vb = a.v_pool + lofs;
   uint32_t* kt = sh.k[wave];
   uint32_t* vt = sh.v[wave];
-  const int nbw = cnt > wave ? (cnt - wave + kItemWaves - 1) / kItemWaves : 0;
+  // wave w walks selection positions first, first + step, ... (one
+  // workgroup: w, w + 8, ...; a pair: w + 8 half, w + 8 half + 16, ...)
+  const int step = pair ? 2 * kItemWaves : kItemWaves;
+  const int first = wave + (pair ? kItemWaves * pair->half : 0);
+  const int nbw = cnt > first ? (cnt - first + step - 1) / step : 0;
   const int nent = item_entry_count(cnt);   // entries written by item_entries
 
   uint4 kr[NPF][NL], vr[NPF][NL];
   int ntok[NPF];
 #pragma unroll
   for (int s = 0; s < NPF; ++s) {
-    const int ie = wave + kItemWaves * s;
+    const int ie = first + step * s;
     const int e = ie < nent ? ent[ie] : -1;
     ntok[s] = e >= 0 ? (e & 31) : 0;
     const uint64_t off = (uint64_t)(uint32_t)(e >= 0 ? e >> 5 : 0) * pstride;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      kr[s][j] = ldg16(kb + off + (size_t)j * ST::RPI * D);
-      vr[s][j] = ldg16(vb + off + (size_t)j * ST::RPI * D);
+      kr[s][j] = ldg16_stream(kb + off + (size_t)j * ST::RPI * D);
+      vr[s][j] = ldg16_stream(vb + off + (size_t)j * ST::RPI * D);
     }
     __builtin_amdgcn_sched_barrier(0);   // issue the slots in order (oldest = slot 0)
   }
@@ -301,7 +319,7 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
     for (int s = 0; s < NPF; ++s) {
       const int k = k0 + s;
       // the block that refills this slot (entries past the written ones read as empty)
-      const int ie = wave + kItemWaves * (k + NPF);
+      const int ie = first + step * (k + NPF);
       const int en = ie < nent ? ent[ie] : -1;
       if (k < nbw) {
         // stage the K and V tiles (row-major, padded rows)
@@ -382,8 +400,8 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
       const uint64_t off = (uint64_t)(uint32_t)(en >= 0 ? en >> 5 : 0) * pstride;
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        kr[s][j] = ldg16(kb + off + (size_t)j * ST::RPI * D);
-        vr[s][j] = ldg16(vb + off + (size_t)j * ST::RPI * D);
+        kr[s][j] = ldg16_stream(kb + off + (size_t)j * ST::RPI * D);
+        vr[s][j] = ldg16_stream(vb + off + (size_t)j * ST::RPI * D);
       }
     }
   }
@@ -401,12 +419,14 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
   }
   __syncthreads();
   // merge the 8 wave states in wave order; one output element per thread
-  for (int e = tid; e < 4 * D; e += kItemThreads) {
-    const int h = e / D, d = e % D;
-    float M = kNegInf;
+  // (4 D <= 512 elements)
+  static_assert(4 * D <= kItemThreads, "one merged element per thread");
+  const int e = tid;
+  const int h = e / D, d = e % D;
+  float M = kNegInf, O = 0.0f, Ls = 0.0f;
+  if (e < 4 * D) {
 #pragma unroll
     for (int w = 0; w < kItemWaves; ++w) M = fmaxf(M, sh.m[w][h]);
-    float O = 0.0f, Ls = 0.0f;
     if (M != kNegInf) {
 #pragma unroll
       for (int w = 0; w < kItemWaves; ++w) {
@@ -415,6 +435,48 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
         Ls += f * sh.l[w][h];
       }
     }
+  }
+  if (pair) {
+    // publish, count the arrival, and let the second workgroup finish
+    float* mine = pair->part + (size_t)pair->half * 4 * D;
+    float* ml = pair->part + 2 * 4 * D;
+    if (e < 4 * D) {
+      st_dev(mine + e, O);
+      if (d == 0) {
+        st_dev(ml + pair->half * 8 + 2 * h, M);
+        st_dev(ml + pair->half * 8 + 2 * h + 1, Ls);
+      }
+    }
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(pair->arrivals, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      sh.m[0][0] = __int_as_float(prev == 1u ? 1 : 0);
+    }
+    __syncthreads();
+    if (__float_as_int(sh.m[0][0]) == 0) return;   // the other workgroup finishes
+    if (e < 4 * D) {
+      const int oh = 1 - pair->half;
+      const float Mo = ld_dev(ml + oh * 8 + 2 * h), Lo = ld_dev(ml + oh * 8 + 2 * h + 1);
+      const float Oo = ld_dev(pair->part + (size_t)oh * 4 * D + e);
+      // merge in half order (half 0 first), so the result does not depend on
+      // which workgroup arrives last
+      const float M0 = pair->half == 0 ? M : Mo, M1 = pair->half == 0 ? Mo : M;
+      const float O0 = pair->half == 0 ? O : Oo, O1 = pair->half == 0 ? Oo : O;
+      const float L0 = pair->half == 0 ? Ls : Lo, L1 = pair->half == 0 ? Lo : Ls;
+      const float Mn = fmaxf(M0, M1);
+      O = 0.0f;
+      Ls = 0.0f;
+      if (Mn != kNegInf) {
+        const float f0 = exp2f(M0 - Mn), f1 = exp2f(M1 - Mn);
+        O = f0 * O0 + f1 * O1;
+        Ls = f0 * L0 + f1 * L1;
+      }
+      M = Mn;
+    }
+  }
+  if (e < 4 * D) {
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
     const size_t idx = ((size_t)r * a.num_q_heads + g * 4 + h) * D + d;
     if (out32) reinterpret_cast<float*>(a.out)[idx] = O * inv;

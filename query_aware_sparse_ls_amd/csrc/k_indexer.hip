@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
       size_t off;
       const int page = row_page(k, j, &off);
       badm |= (uint32_t)(page == -2) << j;
-      d[j] = ldg16(kbase + off + 16 * (lane % T::LPR));
+      if constexpr (MODE == kIdxTokens) d[j] = ldg16_stream(kbase + off + 16 * (lane % T::LPR));
+      else d[j] = ldg16(kbase + off + 16 * (lane % T::LPR));
     }
     sig = 1.0f;
     if constexpr (MODE == kIdxTokens) {

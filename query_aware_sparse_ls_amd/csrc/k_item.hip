@@ -86,6 +86,103 @@ __global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, T
   item_attn<D>(aa, r, g, sel, cnt, u.at);
 }
 
+// ---------------------------------------------------------------------------
+// Two workgroups per pair (batches with at most kPairMaxPairs pairs, so that
+// the grid still covers the chip): the scoring is split over the pair's two
+// workgroups (score_part_kernel, scores through HBM), then both workgroups
+// rank the same scores (identical selections), each attends every other group
+// of 8 selection positions, and the second to finish merges the two softmax
+// states (arrival counter, no waiting).
+
+// Scores of half `blockIdx.x` of the candidate tiles of pair (r, g) into the
+// score row; also zeroes the pair's arrival counter for the attention launch.
+template <int D, int MAXC>
+__global__ __launch_bounds__(kItemThreads) void score_part_kernel(ScoreArgs sa, float* scores,
+                                                                  uint32_t* arrivals) {
+  __shared__ int pg[MAXC];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kItemWaves * 2 * 16 * Stage<D>::kKRowWords];
+  const int part = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int item = r * sa.num_kv_heads + g;
+  if (part == 0 && threadIdx.x == 0) arrivals[item] = 0u;
+  ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
+  const int t0 = geo.c0 / 16, t1 = (geo.c1 + 15) / 16;
+  const int half = (t1 - t0 + 1) / 2;
+  const int lo = (t0 + part * half) * 16, hi = (t0 + (part + 1) * half) * 16;
+  geo.c0 = geo.c0 > lo ? geo.c0 : lo;
+  geo.c1 = geo.c1 < hi ? geo.c1 : hi;
+  if (geo.c1 <= geo.c0) return;
+  for (int b = geo.c0 + threadIdx.x; b < geo.c1; b += kItemThreads)
+    pg[b] = sa.b.indices[geo.page_base + b];
+  __syncthreads();
+  item_score<D, MAXC>(sa, r, g, geo, pg, scores + (size_t)item * sa.b.max_blocks, stage);
+}
+
+template <int D, int MAXC>
+__global__ __launch_bounds__(kItemThreads) void select_attn_pair_kernel(TopkArgs ta, AttnArgs aa,
+                                                                        float* pair_part,
+                                                                        uint32_t* arrivals) {
+  __shared__ int pg[MAXC];
+  __shared__ int sel[MAXC + kItemEntryPad];
+  __shared__ union {
+    struct {
+      float sc[MAXC];
+      TopkLds tk;
+    } s;
+    ItemAttnLds<D> at;
+  } u;
+  const int half = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int item = r * ta.num_kv_heads + g;
+  const ReqGeom geo = req_geom(ta.b, r, ta.n_sink, ta.n_recent);
+  load_page_row(ta.b, geo, pg);
+  const float* srow = ta.scores + (size_t)item * ta.b.max_blocks;
+  for (int b = geo.c0 + threadIdx.x; b < geo.c1; b += kItemThreads) u.s.sc[b] = srow[b];
+  __syncthreads();
+  const int cnt = topk_wg<MAXC / kItemThreads, kItemThreads>(
+      u.s.sc + geo.c0, geo, topk_budget(ta, geo), ta.selected + (size_t)item * ta.max_selected,
+      ta.max_selected, ta.selected_count + item, u.s.tk, sel);
+  item_entries(aa, geo, sel, cnt, pg, item_entry_count(cnt));
+  __syncthreads();
+  const ItemPair pr{pair_part + (size_t)item * kPairFloats<D>, arrivals + item, half};
+  item_attn<D>(aa, r, g, sel, cnt, u.at, &pr);
+}
+
+__global__ void pair_zero_kernel(uint32_t* arrivals, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) arrivals[i] = 0u;
+}
+
+template <int D, int MAXC>
+__global__ __launch_bounds__(kItemThreads) void attn_pair_kernel(AttnArgs a, float* pair_part,
+                                                                 uint32_t* arrivals) {
+  __shared__ int pg[MAXC];
+  __shared__ int sel[MAXC + kItemEntryPad];
+  __shared__ ItemAttnLds<D> sh;
+  const int half = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const size_t item = (size_t)r * a.num_kv_heads + g;
+  const ReqGeom geo = req_geom(a.b, r, 0, 0);
+  load_page_row(a.b, geo, pg);
+  int cnt;
+  if (a.selected) {
+    cnt = a.selected_count[item];
+    const int n = a.max_selected < MAXC ? a.max_selected : MAXC;
+    const int32_t* row = a.selected + item * a.max_selected;
+    for (int i = threadIdx.x; i < n; i += kItemThreads) sel[i] = row[i];
+    cnt = cnt < 0 ? 0 : (cnt > n ? n : cnt);
+  } else {
+    cnt = geo.nb;
+    for (int i = threadIdx.x; i < geo.nb; i += kItemThreads) sel[i] = i;
+  }
+  __syncthreads();
+  item_entries(a, geo, sel, cnt, pg, item_entry_count(cnt));
+  __syncthreads();
+  const ItemPair pr{pair_part + item * kPairFloats<D>, arrivals + item, half};
+  item_attn<D>(a, r, g, sel, cnt, sh, &pr);
+}
+
+bool pair_path(int batch, int hkv, int max_blocks) {
+  return (long long)batch * hkv <= kPairMaxPairs && max_blocks > kPairMinBlocks;
+}
+
 bool item_path(int batch, int hkv, int head_dim, int group, int max_blocks, int num_pages) {
   return (long long)batch * hkv >= kItemMinPairs && group == 4 &&
          (head_dim == 128 || head_dim == 64) && max_blocks <= 8192 && num_pages < (1 << 26);
@@ -117,6 +214,23 @@ hipError_t launch_select_item(const ScoreArgs& sa, const TopkArgs& ta, hipStream
 
 hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st) {
   const int D = a.head_dim, n = a.b.max_blocks;
+  if (pair_path(a.b.batch, a.num_kv_heads, n)) {
+    const int pairs = a.b.batch * a.num_kv_heads;
+    float* part = a.partials;
+    uint32_t* arr = pair_arrivals(a.partials, pairs, D);
+    hipLaunchKernelGGL(pair_zero_kernel, dim3((pairs + 255) / 256), dim3(256), 0, st, arr, pairs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid2(2, a.num_kv_heads, a.b.batch);
+#define LAUNCH(DD, MC)                                                                    \
+  do {                                                                                    \
+    hipLaunchKernelGGL((attn_pair_kernel<DD, MC>), grid2, dim3(kItemThreads), 0, st, a, part, \
+                       arr);                                                              \
+    return hipGetLastError();                                                             \
+  } while (0)
+    LS_ITEM_DISPATCH(LAUNCH)
+#undef LAUNCH
+  }
   const dim3 grid(a.num_kv_heads, a.b.batch);
 #define LAUNCH(DD, MC)                                                                  \
   do {                                                                                  \
@@ -130,6 +244,25 @@ hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st) {
 hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,
                             hipStream_t st) {
   const int D = sa.head_dim, n = sa.b.max_blocks;
+  if (pair_path(sa.b.batch, sa.num_kv_heads, n)) {
+    // scoring over both workgroups of each pair, then top-k + attention
+    const int pairs = sa.b.batch * sa.num_kv_heads;
+    float* part = aa.partials;
+    uint32_t* arr = pair_arrivals(aa.partials, pairs, D);
+    const dim3 grid2(2, sa.num_kv_heads, sa.b.batch);
+#define LAUNCH(DD, MC)                                                                       \
+  do {                                                                                       \
+    hipLaunchKernelGGL((score_part_kernel<DD, MC>), grid2, dim3(kItemThreads), 0, st, sa,      \
+                       const_cast<float*>(ta.scores), arr);                                  \
+    hipError_t e = hipGetLastError();                                                        \
+    if (e != hipSuccess) return e;                                                           \
+    hipLaunchKernelGGL((select_attn_pair_kernel<DD, MC>), grid2, dim3(kItemThreads), 0, st, ta, \
+                       aa, part, arr);                                                       \
+    return hipGetLastError();                                                                \
+  } while (0)
+    LS_ITEM_DISPATCH(LAUNCH)
+#undef LAUNCH
+  }
   if (n > 4096) {
     // the one-launch form does not fit in LDS: the two per-pair launches,
     // which are the separate calls (same results)

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
       const int c = tid + kMlaThreads * i;
       const int tok = t * kMlaTile + c / (kMlaDk / 8);
       const int off = (t < ntiles && tok < ntok) ? sh.rowoff[tok] : -1;
-      ld[i] = ldg16(a.latent + (size_t)(uint32_t)(off >= 0 ? off : 0) * kMlaDk + 8 * (c % (kMlaDk / 8)));
+      ld[i] = ldg16_stream(a.latent + (size_t)(uint32_t)(off >= 0 ? off : 0) * kMlaDk + 8 * (c % (kMlaDk / 8)));
     }
   };
   f32x4_t o[8];

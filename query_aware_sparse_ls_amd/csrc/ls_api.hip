@@ -259,7 +259,10 @@ size_t ls_sparse_attn_decode_workspace_size(int32_t batch_size, int32_t num_q_he
   if (batch_size <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
   const int cap = max_selected > 0 ? max_selected : max_blocks;
   const size_t S = (size_t)ls_attn_num_splits(cap);
-  return align_up((size_t)batch_size * num_q_heads * S * (head_dim + 2) * sizeof(float));
+  const size_t split = (size_t)batch_size * num_q_heads * S * (head_dim + 2) * sizeof(float);
+  // exchange areas of the two-workgroup pair path (GQA groups of 4)
+  const size_t pair = ls::pair_workspace_bytes(batch_size * ((num_q_heads + 3) / 4), head_dim);
+  return align_up(split > pair ? split : pair);
 }
 
 ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,

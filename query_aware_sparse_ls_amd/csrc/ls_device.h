@@ -261,4 +261,12 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte streaming load: data read once (key/value tiles, summary rows),
+// marked non-temporal so it does not displace reused lines in the caches.
+__device__ __forceinline__ uint4 ldg16_stream(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 }  // namespace ls

@@ -78,6 +78,24 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 // merge. ScoreArgs.scores may be null for these (scores stay in LDS).
 constexpr int kItemMinPairs = 64;
 bool item_path(int batch, int hkv, int head_dim, int group, int max_blocks, int num_pages);
+// Requests of more than kPairMinBlocks blocks, in batches of at most
+// kPairMaxPairs pairs, take two workgroups per pair (scoring split in half,
+// attention positions interleaved, softmax states merged by the second to
+// finish): the one-workgroup step does not fit in LDS there, and the grid
+// still covers the chip. The attention workspace then holds the pairs'
+// exchange areas (2 * 4 * D + 16 floats each, rounded) followed by their
+// arrival counters.
+constexpr int kPairMaxPairs = 256;
+constexpr int kPairMinBlocks = 4096;
+bool pair_path(int batch, int hkv, int max_blocks);
+inline size_t pair_workspace_bytes(int pairs, int head_dim) {
+  const size_t f = (size_t)pairs * (2 * 4 * head_dim + 16) * sizeof(float);
+  return (f + 255) / 256 * 256 + (size_t)pairs * sizeof(uint32_t);
+}
+inline uint32_t* pair_arrivals(float* partials, int pairs, int head_dim) {
+  const size_t f = (size_t)pairs * (2 * 4 * head_dim + 16) * sizeof(float);
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(partials) + (f + 255) / 256 * 256);
+}
 hipError_t launch_select_item(const ScoreArgs& sa, const TopkArgs& ta, hipStream_t st);
 hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st);
 hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,

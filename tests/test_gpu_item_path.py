@@ -130,3 +130,20 @@ def test_item_path_ties_go_to_lowest_index():
         for g in range(cfg.num_kv_heads):
             got = res.selected[r, g, :int(res.counts[r, g])].tolist()
             assert got == [0, 1, 2, 3, 4, 5, nb - 1], got
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("d128 128 pairs", reduced(LLAMA8B_32K_B16, batch=16, context=100000)),
+    ("d64 64 pairs", reduced(TINY_4K, batch=32, context=70000, n_hot=40, out_dtype="bf16")),
+])
+def test_pair_path_long_requests(name, cfg):
+    """Requests of more than 4096 blocks in batches of at most 256 pairs take
+    two workgroups per pair (split scoring, interleaved attention positions,
+    merged softmax states): oracle parity and step == separate calls."""
+    say(f"two workgroups per pair: {name}, L={cfg.context}")
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=77)
+    res = run_gpu_step(inp)
+    fus = run_gpu_fused(inp, summaries=res.summaries)
+    _same(res, fus)
+    for r, g in _pairs(cfg, 5, seed=5):
+        check_pair(inp, res, r, g, **_kw(inp))
