@@ -367,7 +367,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
  * log-sum-exp in split order (deterministic). Empty T: out = 0, lse = -inf.
  * Output rounded once (nearest-even) to out_dtype.
  *
- * q:        [batch][num_q_heads][576] bf16; num_q_heads a multiple of 16 (<= 256).
+ * q:        [batch][num_q_heads][576] bf16; num_q_heads a multiple of 32 (<= 256).
  * latent:   [num_pages][page_size][576] bf16 (pool.num_heads = 1,
  *           pool.head_dim = 576, pool.dtype = LS_DTYPE_BF16).
  * selected: [batch][max_selected] token ids (e.g. from ls_indexer_select),

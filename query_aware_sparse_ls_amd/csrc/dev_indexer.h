@@ -82,16 +82,16 @@ __device__ __forceinline__ IdxUnits idx_units(const IndexerArgs& a, int r) {
 // Block of unit u (token mode) or -1 when the unit is not a cached token.
 __device__ __forceinline__ int idx_unit_block(const IndexerArgs& a, const IdxUnits& g, int r,
                                               int u, int* token) {
-  const int P = a.b.page_size;
+  const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);   // a power of two
   if (u < 0 || u >= g.n) return -1;
   int blk;
   if (g.ncand < 0) {
-    blk = u / P;
+    blk = u >> PS;
   } else {
-    blk = a.cand_blocks[(size_t)r * a.cand_cap + u / P];
+    blk = a.cand_blocks[(size_t)r * a.cand_cap + (u >> PS)];
     if (blk < 0 || blk >= g.nb) return -1;
   }
-  const int t = blk * P + u % P;
+  const int t = blk * P + (u & (P - 1));
   if (t >= g.L) return -1;
   *token = t;
   return blk;

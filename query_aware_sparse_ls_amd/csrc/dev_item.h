@@ -22,8 +22,8 @@
 // The attention output P . V is a 16 x 16 x 16 MFMA per 16 output dims with P
 // (heads x tokens) in exactly that output layout, and V (tokens x dims) as
 // the B operand: lane i needs 4 tokens of one dim, a column of the row-major
-// V tile, read from the wave's LDS copy of the tile (rows padded so the
-// column reads hit 32 distinct banks). P is split into bf16 parts, p = hi + lo (+ lo2
+// V tile, gathered from the wave's LDS copy of the tile with one transpose
+// read (ds_read_b64_tr_b16) per 16-dim tile. P is split into bf16 parts, p = hi + lo (+ lo2
 // for fp32 output), so the products keep fp32-level accuracy.
 #pragma once
 
@@ -74,7 +74,7 @@ template <int D>
 struct Stage {
   static constexpr int LPR = D / 8, RPI = kWave / LPR, NL = D / 32;
   static constexpr int kKRowWords = D / 2 + 4;   // K tile rows: 16-byte aligned, padded
-  static constexpr int kVRowWords = D / 2 + 2;   // V tile rows: column reads hit 32 banks
+  static constexpr int kVRowWords = D / 2 + 8;   // V tile rows: the 4 rows of a transpose read hit 32 distinct banks
 };
 
 // Writes this lane's NL row chunks into a K-style LDS tile (row stride
@@ -382,13 +382,14 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
         const uint2 ph = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
         const uint2 pl = make_uint2(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16));
         const uint2 pm = make_uint2(m16[0] | (m16[1] << 16), m16[2] | (m16[3] << 16));
-        // o += P . V, one 16-dim tile at a time; B = V[tokens 4kq..+4][dim]
-        const uint16_t* vcol = reinterpret_cast<const uint16_t*>(vt) + 4 * kq * (2 * RW) + row;
+        // o += P . V, one 16-dim tile at a time; B = V[tokens 4kq..+4][dim],
+        // gathered by one transpose read: this lane addresses row
+        // 4 kq + row / 4 at columns 4 (row % 4) of the 16-dim tile
+        const uint16_t* vrow = reinterpret_cast<const uint16_t*>(vt) +
+                               (4 * kq + (row >> 2)) * (2 * RW) + 4 * (row & 3);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const uint16_t* c = vcol + 16 * n;
-          const uint2 vb2 = make_uint2((uint32_t)c[0] | ((uint32_t)c[2 * RW] << 16),
-                                       (uint32_t)c[4 * RW] | ((uint32_t)c[6 * RW] << 16));
+          const uint2 vb2 = lds_read_tr16(vrow + 16 * n);
           o[n] = mfma_16x16x16(ph, vb2, o[n]);
           o[n] = mfma_16x16x16(pl, vb2, o[n]);
           if (out32) o[n] = mfma_16x16x16(pm, vb2, o[n]);

@@ -22,4 +22,19 @@ __device__ __forceinline__ f32x4_t mfma_16x16x16(uint2 a, uint2 b, f32x4_t c) {
                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
 }
 
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane 16G + L' receives, as element j (j < 4), 16-bit element L' % 4 of the
+// 8-byte word addressed by lane 16G + 4j + L' / 4. So if lane 16G + 4j + a
+// addresses row R(G, j) at columns 4a .. 4a + 3 of a row-major bf16 tile,
+// lane 16G + c receives column c of rows R(G, 0) .. R(G, 3): four k-values
+// of one column, the B-operand layout of the matrix cores, in one read.
+// (Layout checked on the device: lane L reading word L returns words
+// 4j + L/4 element L%4 within its 16-lane group.) p must be 8-byte aligned.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
 }  // namespace ls

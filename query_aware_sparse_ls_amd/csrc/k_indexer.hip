@@ -20,11 +20,12 @@ struct IdxTile {
   static constexpr int RW = kRowBytes / 4 + 4;               // LDS row stride (words), padded
 };
 
-template <int MODE>
+template <int MODE, int NHT>
 struct IdxScoreLds {
   alignas(16) uint32_t tiles[kIdxWaves][2][16 * IdxTile<MODE>::RW];
-  float sc[kIdxMaxTilesPerWg * 16];
-  int pg[kIdxMaxTilesPerWg * 16 + 1];
+  uint4 q[NHT][4][kWave];   // the q operand, in lane order (one 16-byte read per lane)
+  // page ids of the workgroup's blocks: one per 16+ tokens, one per block
+  int pg[MODE == kIdxTokens ? kIdxMaxTilesPerWg + 1 : kIdxMaxTilesPerWg * 16];
   uint32_t hist[MODE == kIdxTokens ? kIdxBins : 1];
 };
 
@@ -32,10 +33,11 @@ template <int MODE, int NHT>
 __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
   using T = IdxTile<MODE>;
   constexpr int NL = T::NL, NS = kIdxPrefetch, H = 16 * NHT;
-  __shared__ IdxScoreLds<MODE> sh;
+  __shared__ IdxScoreLds<MODE, NHT> sh;
   const int r = blockIdx.y, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
-  const int P = a.b.page_size;
+  const int P = a.b.page_size;                 // 16, 32 or 64
+  const int PS = __builtin_ctz((unsigned)P);    // units -> (block, slot) by shift and mask
   const int upw = a.tiles_per_wg * 16;
   const int u0 = blockIdx.x * upw;
 
@@ -56,8 +58,8 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
   if (u0 >= n_units) return;
 
   // page ids of the workgroup's blocks (-1: no unit of this block is scored)
-  const int bi0 = MODE == kIdxTokens ? u0 / P : u0;
-  const int npg = MODE == kIdxTokens ? (upw + P - 1) / P : upw;
+  const int bi0 = MODE == kIdxTokens ? u0 >> PS : u0;
+  const int npg = MODE == kIdxTokens ? (upw + P - 1) >> PS : upw;
   for (int i = tid; i < npg; i += kIdxThreads) {
     const int bi = bi0 + i;
     int page = -1;
@@ -83,19 +85,20 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
 
   // q (A operand: row = head 16ht + col, dims 32kq + 8s .. +8 of k-step s)
   // and the head weights of this lane's output rows (heads 16ht + 4kq + i)
-  uint4 qa[NHT][4];
+  // (kept in LDS: in registers it would cost 16 NHT VGPRs and occupancy)
   float wv[NHT][4];
+  for (int e = tid; e < NHT * 4 * kWave; e += kIdxThreads) {
+    const int ht = e / (4 * kWave), s = (e / kWave) % 4, ln = e % kWave;
+    sh.q[ht][s][ln] = ldg16(a.q + ((size_t)r * H + 16 * ht + (ln & 15)) * kIdxDim + 32 * (ln >> 4) + 8 * s);
+  }
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    const uint16_t* qh = a.q + ((size_t)r * H + 16 * ht + col) * kIdxDim + 32 * kq;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qa[ht][s] = ldg16(qh + 8 * s);
+  for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)r * H + 16 * ht + 4 * kq + i];
-  }
   __syncthreads();
 
   const int ntw = a.tiles_per_wg / kIdxWaves;
+  float* srow = a.scores + (size_t)r * a.max_units + u0;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.keys);
   // the row this lane loads with instruction j of the wave's k-th tile and
   // its page slot (-1: not scored, -2: bad page)
@@ -104,9 +107,9 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
     const int u = 16 * t + j * T::RPI + lane / T::LPR;   // unit of the row (in the wg)
     int pslot, page;
     if constexpr (MODE == kIdxTokens) {
-      pslot = (u0 + u) / P - bi0;
+      pslot = ((u0 + u) >> PS) - bi0;
       page = k < ntw ? sh.pg[pslot] : -1;
-      const int slot = (u0 + u) % P;
+      const int slot = (u0 + u) & (P - 1);
       *off = ((size_t)(uint32_t)(page >= 0 ? page : 0) * P + slot) * kIdxDim;
     } else {
       pslot = u;
@@ -130,8 +133,8 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
       if (a.scales) {
         const int t = wave + kIdxWaves * k;
         const int u = u0 + 16 * t + col;
-        const int page = k < ntw ? sh.pg[u / P - bi0] : -1;
-        sig = a.scales[(size_t)(uint32_t)(page >= 0 ? page : 0) * P + u % P];
+        const int page = k < ntw ? sh.pg[(u >> PS) - bi0] : -1;
+        sig = a.scales[(size_t)(uint32_t)(page >= 0 ? page : 0) * P + (u & (P - 1))];
       }
     }
   };
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
         for (int ht = 0; ht < NHT; ++ht) {
           acc[ht] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) acc[ht] = mfma_16x16x32(qa[ht][s2], kb[s2], acc[ht]);
+          for (int s2 = 0; s2 < 4; ++s2) acc[ht] = mfma_16x16x32(sh.q[ht][s2][lane], kb[s2], acc[ht]);
         }
         // s = sum_h w_h max(0, sigma * d_h); lane holds heads 16ht + 4kq + i
         float v = 0.0f;
@@ -220,15 +223,12 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
           } else {
             valid = u0 + ul >= c0 && u0 + ul < c1;
           }
-          sh.sc[ul] = valid ? v : 0.0f;
+          if (u0 + ul < n_units) srow[ul] = valid ? v : 0.0f;
         }
       }
     }
   }
   __syncthreads();
-  float* srow = a.scores + (size_t)r * a.max_units + u0;
-  const int nw = n_units - u0 < upw ? n_units - u0 : upw;
-  for (int i = tid; i < nw; i += kIdxThreads) srow[i] = sh.sc[i];
   if constexpr (MODE == kIdxTokens) {
     uint32_t* gh = a.hist + (size_t)r * kIdxBins;
     for (int i = tid; i < kIdxBins; i += kIdxThreads) {
@@ -307,8 +307,8 @@ __device__ __forceinline__ void idx_find_digit(const uint32_t* h, int nbins, int
 __device__ __forceinline__ int idx_token_of(const IndexerArgs& a, const IdxUnits& g, int r,
                                            int u) {
   if (g.ncand < 0) return u;
-  const int P = a.b.page_size;
-  return a.cand_blocks[(size_t)r * a.cand_cap + u / P] * P + u % P;
+  const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);
+  return a.cand_blocks[(size_t)r * a.cand_cap + (u >> PS)] * P + (u & (P - 1));
 }
 
 // Second digit of a score key: bits [19:8]; third digit: bits [7:0].

@@ -9,18 +9,19 @@
 // the partial softmax states are merged by log-sum-exp in a second kernel,
 // in split order (deterministic).
 //
-// Workgroup (r, 16-head group, split), 4 waves. Per 32-token tile, staged in
-// LDS from contiguous 1152-byte token rows:
+// Workgroup (r, 32 heads, split), 8 waves; the latent rows of a 64-token
+// tile are staged once in LDS (contiguous 1152-byte token rows) and shared by
+// both 16-head tiles:
 //  * logits z^T = C . q^T on the matrix cores (16x16x32 bf16): A = latent rows
 //    (16 tokens x 32 dims), B = q^T (32 dims x 16 heads); the 18 k-steps are
-//    split over the 4 waves and the partial logits are summed through LDS, so
-//    every wave ends up with lane i holding head i%16, tokens 4(i/16)+j of
-//    both 16-token halves;
-//  * online softmax per head (every wave keeps the same state);
-//  * o += P . V with wave w owning output dims [128w, 128w+128): A = P (16
-//    heads x 32 tokens, split into bf16 parts hi + lo (+ lo2 for fp32 output)
-//    for fp32-level accuracy), B = V columns read from the LDS tile in the
-//    token order of P's k-slices.
+//    split over the 4 waves of a head tile and their partial logits summed
+//    through LDS, so each wave ends up with lane i holding head i%16, tokens
+//    4(i/16)+j of each 16-token row tile;
+//  * online softmax per head (the 4 waves of a head tile keep the same state);
+//  * o += P . V with the 4 waves of a head tile owning 128 output dims each:
+//    A = P (16 heads x 32 tokens, split into bf16 parts hi + lo (+ lo2 for
+//    fp32 output) for fp32-level accuracy), B = V columns read from the LDS
+//    tile in the token order of P's k-slices.
 #include "dev_mfma.h"
 #include "ls_internal.h"
 
@@ -28,18 +29,19 @@ namespace ls {
 
 constexpr int kMlaDk = 576, kMlaDv = 512;
 constexpr int kMlaPartStride = kMlaDv + 4;   // o[512], m, l, pad: 16-byte aligned rows
-constexpr int kMlaThreads = 256, kMlaWaves = 4;
-constexpr int kMlaHeadsPerWg = 16;
-constexpr int kMlaTile = 32;                           // tokens per LDS tile
+constexpr int kMlaThreads = 512, kMlaWaves = 8;
+constexpr int kMlaHeadsPerWg = 32;                     // two 16-head tiles
+constexpr int kMlaTile = 64;                           // tokens per LDS tile (4 MFMA row tiles)
 constexpr int kMlaRowWords = kMlaDk / 2 + 4;           // 1168-byte padded rows (16-byte aligned)
 constexpr int kMlaChunks = kMlaTile * (kMlaDk / 8);    // 16-byte chunks per tile
 constexpr int kMlaChunksPerThread = kMlaChunks / kMlaThreads;
 static_assert(kMlaChunks % kMlaThreads == 0, "tile chunks per thread");
+static_assert(kMlaSplitTokens % kMlaTile == 0, "whole tiles per split");
 
 struct MlaLds {
   alignas(16) uint32_t tile[kMlaTile * kMlaRowWords];
-  f32x4_t red[kMlaWaves][2][kWave];
-  int rowoff[kMlaSplitTokens];   // token row index in the pool (page * P + slot), -1 = skip
+  f32x4_t red[kMlaWaves][4][kWave];   // partial logits: wave, 16-token row tile, lane
+  int rowoff[kMlaSplitTokens];        // token row index in the pool (page * P + slot), -1 = skip
 };
 
 __device__ __forceinline__ uint32_t mla_bf16_split(float x, float* rest) {
@@ -48,8 +50,11 @@ __device__ __forceinline__ uint32_t mla_bf16_split(float x, float* rest) {
   return b;
 }
 
-// two workgroups per CU (<= 256 registers per lane)
-__global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
+// Workgroup (request r, 32 heads, split s), 8 waves. Wave w works on head
+// tile w / 4 (16 heads): the QK^T k-steps of quarter w % 4 (5, 5, 4, 4 of the
+// 18), summed with the other three waves of its head tile through LDS, and
+// the output dims [128 (w % 4), + 128) of P . V.
+__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   __shared__ MlaLds sh;
   const int S = a.num_splits;
   const int nrs = a.b.batch * S;
@@ -57,6 +62,7 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
   const int r = rs / S, s = rs % S;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
+  const int ht = wave >> 2, sub = wave & 3;
   const int P = a.b.page_size;
   const int H = a.num_q_heads;
 
@@ -77,18 +83,19 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
     }
     sh.rowoff[i] = off;
   }
-  // q^T operand for this wave's k-steps: head 16hg + col, dims 32k + 8kq
-  const int ks0 = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
-  const int nks = wave < 2 ? 5 : 4;
+  // q^T operand of this wave's k-steps: head 32 hg + 16 ht + col, dims 32k + 8kq
+  const int ks0 = sub < 2 ? 5 * sub : 10 + 4 * (sub - 2);
+  const int nks = sub < 2 ? 5 : 4;
+  const int head0 = kMlaHeadsPerWg * hg + 16 * ht;
   uint4 qb[5];
-  const uint16_t* qh = a.q + ((size_t)r * H + kMlaHeadsPerWg * hg + col) * kMlaDk + 8 * kq;
+  const uint16_t* qh = a.q + ((size_t)r * H + head0 + col) * kMlaDk + 8 * kq;
 #pragma unroll
   for (int k = 0; k < 5; ++k) qb[k] = k < nks ? ldg16(qh + 32 * (ks0 + k)) : make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   const bool out32 = a.out_dtype == LS_DTYPE_FP32;
   const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
-  // tile loads: chunk c = tid + 256 i -> token c / 72, 16 bytes at 8 (c % 72);
+  // tile loads: chunk c = tid + 512 i -> token c / 72, 16 bytes at 8 (c % 72);
   // two tiles of loads are in flight (register buffers A and B)
   auto issue = [&](int t, uint4* ld) {
 #pragma unroll
@@ -102,7 +109,8 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
   f32x4_t o[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = kNegInf, l = 0.0f;   // state of head `col`
+  float m = kNegInf, l = 0.0f;   // state of head head0 + col
+  constexpr int RS = 2 * kMlaRowWords;   // LDS row stride in bf16 elements
   auto tile_step = [&](int t, uint4* ld) {
     // stage tile t, then start loading tile t + 2 into the same registers
 #pragma unroll
@@ -112,38 +120,42 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
     }
     __syncthreads();
     issue(t + 2, ld);
-    // partial logits over this wave's k-steps: rows = tokens, cols = heads
-    f32x4_t z0 = {0.0f, 0.0f, 0.0f, 0.0f}, z1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    // partial logits over this wave's k-steps, 4 row tiles of 16 tokens
+    f32x4_t z[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
       if (k < nks) {
         const int w0 = 16 * (ks0 + k) + 4 * kq;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(sh.tile + col * kMlaRowWords + w0);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(sh.tile + (16 + col) * kMlaRowWords + w0);
-        z0 = mfma_16x16x32(a0, qb[k], z0);
-        z1 = mfma_16x16x32(a1, qb[k], z1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 av = *reinterpret_cast<const uint4*>(sh.tile + (16 * j + col) * kMlaRowWords + w0);
+          z[j] = mfma_16x16x32(av, qb[k], z[j]);
+        }
       }
     }
-    sh.red[wave][0][lane] = z0;
-    sh.red[wave][1][lane] = z1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sh.red[wave][j][lane] = z[j];
     __syncthreads();
-    f32x4_t zs0 = sh.red[0][0][lane], zs1 = sh.red[0][1][lane];
+    // full logits of head tile ht: lane = head col, tokens 16 j + 4 kq + i
+    float zz[16], bm = kNegInf;
 #pragma unroll
-    for (int w = 1; w < kMlaWaves; ++w) {
-      const f32x4_t x0 = sh.red[w][0][lane], x1 = sh.red[w][1][lane];
+    for (int j = 0; j < 4; ++j) {
+      f32x4_t acc = sh.red[4 * ht][j][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { zs0[i] += x0[i]; zs1[i] += x1[i]; }
+      for (int w = 1; w < 4; ++w) {
+        const f32x4_t x = sh.red[4 * ht + w][j][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += x[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = t * kMlaTile + 16 * j + 4 * kq + i;
+        zz[4 * j + i] = (tt < ntok && sh.rowoff[tt] >= 0) ? acc[i] * a.sm_scale_log2 : kNegInf;
+        bm = fmaxf(bm, zz[4 * j + i]);
+      }
     }
-    // lane: head col; tokens 4kq + i (half 0) and 16 + 4kq + i (half 1)
-    float z[8], bm = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t0 = t * kMlaTile + 4 * kq + i, t1 = t0 + 16;
-      z[i] = (t0 < ntok && sh.rowoff[t0] >= 0) ? zs0[i] * a.sm_scale_log2 : kNegInf;
-      z[4 + i] = (t1 < ntok && sh.rowoff[t1] >= 0) ? zs1[i] * a.sm_scale_log2 : kNegInf;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) bm = fmaxf(bm, z[i]);
     float lo, hi;
     xor_pair<16>(bm, lo, hi);
     bm = fmaxf(lo, hi);
@@ -151,17 +163,17 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
     bm = fmaxf(lo, hi);
     const float mn = fmaxf(m, bm);
     const float alpha = mn == kNegInf ? 1.0f : exp2f(m - mn);
-    float p[8], ps = 0.0f;
+    float p[16], ps = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = z[i] == kNegInf ? 0.0f : exp2f(z[i] - mn);
+    for (int i = 0; i < 16; ++i) {
+      p[i] = zz[i] == kNegInf ? 0.0f : exp2f(zz[i] - mn);
       ps += p[i];
     }
     ps = xor_pair_sum<16>(ps);
     ps = xor_pair_sum<32>(ps);
     l = l * alpha + ps;
     m = mn;
-    // o rows are heads 4kq + i: their alphas live in lanes 4kq + i
+    // o rows are heads 4kq + i of the tile: their alphas live in lanes 4kq + i
     if (__ballot(alpha != 1.0f)) {
       float ar[4];
 #pragma unroll
@@ -171,34 +183,38 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[n][i] *= ar[i];
     }
-    // P (A operand: row = head col, k-slice kq = tokens 4kq+i, 16+4kq+i)
-    uint32_t h16[8], l16[8], m16[8];
+    // P . V in two k-steps of 32 tokens: step js covers row tiles 2js and
+    // 2js + 1; lane's k-slice = tokens 4kq + i of each (P as A: row = head col)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float r1, r2;
-      h16[i] = mla_bf16_split(p[i], &r1);
-      l16[i] = mla_bf16_split(r1, &r2);
-      m16[i] = f32_to_bf16_rne(r2);
-    }
-    const uint4 ph = make_uint4(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16),
-                                h16[4] | (h16[5] << 16), h16[6] | (h16[7] << 16));
-    const uint4 pl = make_uint4(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16),
-                                l16[4] | (l16[5] << 16), l16[6] | (l16[7] << 16));
-    const uint4 pm = make_uint4(m16[0] | (m16[1] << 16), m16[2] | (m16[3] << 16),
-                                m16[4] | (m16[5] << 16), m16[6] | (m16[7] << 16));
-    // o += P . V over this wave's 128 dims; B = V[the same 8 tokens][dim]
-    const uint16_t* tb = reinterpret_cast<const uint16_t*>(sh.tile);
-    constexpr int RS = 2 * kMlaRowWords;   // row stride in bf16 elements
+    for (int js = 0; js < 2; ++js) {
+      uint32_t h16[8], l16[8], m16[8];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const uint16_t* c = tb + 4 * kq * RS + 128 * wave + 16 * n + col;
-      const uint4 vb = make_uint4((uint32_t)c[0] | ((uint32_t)c[RS] << 16),
-                                  (uint32_t)c[2 * RS] | ((uint32_t)c[3 * RS] << 16),
-                                  (uint32_t)c[16 * RS] | ((uint32_t)c[17 * RS] << 16),
-                                  (uint32_t)c[18 * RS] | ((uint32_t)c[19 * RS] << 16));
-      o[n] = mfma_16x16x32(ph, vb, o[n]);
-      o[n] = mfma_16x16x32(pl, vb, o[n]);
-      if (out32) o[n] = mfma_16x16x32(pm, vb, o[n]);
+      for (int i = 0; i < 8; ++i) {
+        float r1, r2;
+        h16[i] = mla_bf16_split(p[8 * js + i], &r1);
+        l16[i] = mla_bf16_split(r1, &r2);
+        m16[i] = f32_to_bf16_rne(r2);
+      }
+      const uint4 ph = make_uint4(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16),
+                                  h16[4] | (h16[5] << 16), h16[6] | (h16[7] << 16));
+      const uint4 pl = make_uint4(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16),
+                                  l16[4] | (l16[5] << 16), l16[6] | (l16[7] << 16));
+      const uint4 pm = make_uint4(m16[0] | (m16[1] << 16), m16[2] | (m16[3] << 16),
+                                  m16[4] | (m16[5] << 16), m16[6] | (m16[7] << 16));
+      // V as B operand via transpose reads: this lane addresses row
+      // 32 js + 4 kq + (col / 4) (and + 16) at columns 4 (col % 4) of the
+      // 16-dim tile, and receives column col of rows 32 js + 4 kq + 0..3 (+ 16)
+      const uint16_t* tb = reinterpret_cast<const uint16_t*>(sh.tile) +
+                           (32 * js + 4 * kq + (col >> 2)) * RS + 128 * sub + 4 * (col & 3);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint2 v0 = lds_read_tr16(tb + 16 * n);
+        const uint2 v1 = lds_read_tr16(tb + 16 * RS + 16 * n);
+        const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        o[n] = mfma_16x16x32(ph, vb, o[n]);
+        o[n] = mfma_16x16x32(pl, vb, o[n]);
+        if (out32) o[n] = mfma_16x16x32(pm, vb, o[n]);
+      }
     }
     __syncthreads();   // the tile and the logit partials are rewritten next
   };
@@ -209,14 +225,14 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaArgs a) {
     tile_step(t, ldA);
     if (t + 1 < ntiles) tile_step(t + 1, ldB);
   }
-  // partial state: o rows = heads 4kq + i, column = dim 128 wave + 16 n + col
-  float* part = a.partials + (((size_t)r * H + kMlaHeadsPerWg * hg) * S + s) * (kMlaPartStride);
-  const size_t hstride = (size_t)S * (kMlaPartStride);
+  // partial state: o rows = heads 4kq + i of the tile, column = dim 128 sub + 16 n + col
+  float* part = a.partials + (((size_t)r * H + head0) * S + s) * kMlaPartStride;
+  const size_t hstride = (size_t)S * kMlaPartStride;
 #pragma unroll
   for (int n = 0; n < 8; ++n)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[(4 * kq + i) * hstride + 128 * wave + 16 * n + col] = o[n][i];
-  if (wave == 0 && kq == 0) {
+    for (int i = 0; i < 4; ++i) part[(4 * kq + i) * hstride + 128 * sub + 16 * n + col] = o[n][i];
+  if (sub == 0 && kq == 0) {
     part[col * hstride + kMlaDv] = m;
     part[col * hstride + kMlaDv + 1] = l;
   }
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t st) {
-  const int nwg = a.b.batch * a.num_splits * (a.num_q_heads / kMlaHeadsPerWg);
+  const int nwg = a.b.batch * a.num_splits * (a.num_q_heads / kMlaHeadsPerWg);   // H % 32 == 0
   hipLaunchKernelGGL(mla_split_kernel, dim3(nwg), dim3(kMlaThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -568,8 +568,8 @@ ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_hea
     return fail(LS_ERR_UNSUPPORTED, "latent pool must be bf16 with num_heads 1 and head_dim 576");
   if (pool.page_size < 1 || pool.page_size > 1024)
     return fail(LS_ERR_UNSUPPORTED, "pool.page_size %d (supported: 1 .. 1024)", pool.page_size);
-  if (num_q_heads < 16 || num_q_heads > 256 || num_q_heads % 16 != 0)
-    return fail(LS_ERR_UNSUPPORTED, "num_q_heads %d (supported: multiples of 16 up to 256)",
+  if (num_q_heads < 32 || num_q_heads > 256 || num_q_heads % 32 != 0)
+    return fail(LS_ERR_UNSUPPORTED, "num_q_heads %d (supported: multiples of 32 up to 256)",
                 num_q_heads);
   if ((selected == nullptr) != (selected_count == nullptr))
     return fail(LS_ERR_INVALID, "selected and selected_count must both be set or both NULL");

@@ -285,7 +285,7 @@ def test_mla_small_selected(out_dtype):
 
 def test_mla_dense_equals_all_tokens():
     say("mla dense")
-    cfg = reduced(INDEXER_128K, batch=2, context=64 * 9, mla_heads=16, seed=22)
+    cfg = reduced(INDEXER_128K, batch=2, context=64 * 9, mla_heads=32, seed=22)
     inp = make_indexer_inputs(cfg, device=_dev())
     inp.seq_lens.copy_(torch.tensor([576, 300], dtype=torch.int32))
     h = _host(inp)
