@@ -1,14 +1,14 @@
 """Benchmark of the decode-step sparse-attention hot path on one MI355X.
 
 One step = the whole path for one batch of synthetic input:
-  1. summaries of the pages that just filled (ls_build_block_summaries),
+  1. summaries of the pages that just filled,
   2. GQA block scoring + top-k + forced sink/recent, and
-  3. split-K attention over the selected blocks,
-where 2 + 3 run as ONE persistent launch (ls_sparse_decode_step) by default
-(--separate: ls_score_select then ls_sparse_attn_decode). Step 1 runs on a
-side stream, forked and joined inside the step: the pages that just filled
-are in the recent window, so this step's selection does not read their
-summaries.
+  3. attention over the selected blocks,
+all in ONE library call (ls_sparse_decode_step with the filled pages; one
+launch: the pairs' workgroups plus a few that rebuild those summaries --
+the pages that just filled are recent blocks, so this step's selection does
+not read them). --separate: ls_build_block_summaries on a side stream, then
+ls_score_select, then ls_sparse_attn_decode.
 
 Workload: Llama-3-8B-shaped decode attention, 16 requests x 32K tokens,
 32 query / 8 KV heads, head_dim 128, 16-token pages in a seeded random
@@ -108,7 +108,7 @@ def call_first(rep, cfg, sm_scale, fused):
                               max_selected=rep["maxsel"], sm_scale=sm_scale,
                               group_agg=cfg.group_agg, selected=rep["sel"],
                               selected_count=rep["cnt"], out=rep["out"],
-                              workspace=rep["ws_step"])
+                              new_pages=rep["new_pages"], workspace=rep["ws_step"])
     else:
         ls.score_select(inp.q, rep["summ"], cfg.page_size, rep["batch"], topk=inp.topk,
                         n_sink=cfg.n_sink, n_recent=cfg.n_recent, max_selected=rep["maxsel"],
@@ -125,9 +125,15 @@ def call_second(rep, sm_scale):
 
 
 def run_step(rep, cfg, sm_scale, fused=True, side=None):
-    """One step. With `side`, the summary update runs on that stream, forked
-    from and joined back into the current stream."""
+    """One step. Fused: ONE library call, which also rebuilds the summaries
+    of the pages that filled at this step (they are recent blocks, so this
+    step does not score them). Separate: the summary update on `side`
+    (forked from and joined back into the current stream), then selection,
+    then attention."""
     import torch
+    if fused:
+        call_first(rep, cfg, sm_scale, fused)
+        return
     main = torch.cuda.current_stream()
     if side is not None:
         side.wait_stream(main)
@@ -136,8 +142,7 @@ def run_step(rep, cfg, sm_scale, fused=True, side=None):
     else:
         call_update(rep)
     call_first(rep, cfg, sm_scale, fused)
-    if not fused:
-        call_second(rep, sm_scale)
+    call_second(rep, sm_scale)
     if side is not None:
         main.wait_stream(side)
 
@@ -153,8 +158,9 @@ def per_call_ms(reps, cfg, sm_scale, fused, n):
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e8))
     ev[0].record()
-    for i in range(n):
-        call_update(reps[i % R])
+    if not fused:   # the fused call rebuilds them itself
+        for i in range(n):
+            call_update(reps[i % R])
     ev[1].record()
     for i in range(n):
         call_first(reps[i % R], cfg, sm_scale, fused)
@@ -631,9 +637,10 @@ def main(argv=None) -> int:
     calls_per_s = 1e3 / ms_step
     gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
     sel_bytes = B * Hkv * n_sel * 4 + B * Hkv * 4      # selection written (+ counts)
-    fused_bytes = nbytes["total"] - nbytes["summary_update"] + sel_bytes
+    fused_bytes = nbytes["total"] + sel_bytes           # summary refresh included
     if fused:
-        # one (request, kv head) pair per workgroup: the whole call is one launch
+        # one (request, kv head) pair per workgroup plus the summary-refresh
+        # workgroups: the whole call is one launch
         dom_ms, dom_bytes = first, fused_bytes
         dom_key, dom_match = "step_item_kernel.llama8b_32k_b16", "ls::step_item_kernel<128, 2048>"
     else:
@@ -656,7 +663,7 @@ def main(argv=None) -> int:
         "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
         "achieved_GBps_step": round(gbps, 1),
         "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "call_ms": ({"summary_update": round(upd, 5), "decode_step": round(first, 5)} if fused
+        "call_ms": ({"decode_step_with_summary_refresh": round(first, 5)} if fused
                     else {"summary_update": round(upd, 5), "score_select": round(first, 5),
                           "sparse_attn_decode": round(second, 5)}),
         "roofline": {"kernel": dom_match, "bound": "hbm", "achieved": round(dom_gbps, 1),

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 1
+#define LS_ABI_VERSION 2
 
 typedef enum ls_status {
   LS_OK = 0,
@@ -252,6 +252,16 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
  * selected_count) and ls_sparse_attn_decode (k_pool, v_pool with geometry
  * `pool`, sm_scale, out, out_dtype, lse_out); the summary pool shares the
  * K/V pool's num_pages, num_heads and head_dim.
+ * new_page_ids, n_new_pages: optional (NULL, 0) device list of physical
+ *   pages that filled at this step; the call also (re)builds their bf16
+ *   summaries, exactly as ls_build_block_summaries would (summaries are
+ *   built when a block fills up -- Vortex post, "Why Long Generations Are
+ *   Expensive"). On the one-launch path this runs in extra workgroups of the
+ *   same launch, concurrently with the pairs, so it is only valid if no
+ *   selection of this call reads those summaries: each listed page must be
+ *   a forced block of its request in this call -- e.g. its last block, with
+ *   p->n_recent >= 1 (checked). Otherwise call ls_build_block_summaries
+ *   first.
  * workspace: >= ls_sparse_decode_step_workspace_size() bytes, 256-byte
  *   aligned, need not be initialised (block scores and split partials of the
  *   split path; calls that run concurrently need separate workspaces).
@@ -263,10 +273,11 @@ size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_he
                                             int32_t max_blocks, int32_t max_selected);
 
 ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads,
-                                const void* summaries, const void* k_pool, const void* v_pool,
+                                void* summaries, const void* k_pool, const void* v_pool,
                                 ls_pool pool, ls_batch batch, const ls_select_params* p,
                                 int32_t* selected, int32_t* selected_count, float sm_scale,
-                                void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                                void* out, int32_t out_dtype, float* lse_out,
+                                const int32_t* new_page_ids, int32_t n_new_pages, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
@@ -399,7 +410,7 @@ ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_hea
  * none). Host pointer owned by the library. */
 const char* ls_last_error(void);
 
-/* Library version and build string, e.g. "libls 0.1.0 abi 1 gfx950". */
+/* Library version and build string, e.g. "libls 0.2.0 abi 2 gfx950". */
 const char* ls_version(void);
 
 /* Number of split-K partitions ls_sparse_attn_decode uses for a given

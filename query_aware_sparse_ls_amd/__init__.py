@@ -212,10 +212,13 @@ def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.T
                        selected_count: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
                        lse: Optional[torch.Tensor] = None,
+                       new_pages: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, stream=None):
     """score_select + sparse_attn_decode as one call (one launch when there
-    are at least 64 (request, kv head) pairs). Returns (out, lse, selected,
-    selected_count)."""
+    are at least 64 (request, kv head) pairs). new_pages (int32, optional):
+    pages that filled at this step, whose summaries the call also rebuilds
+    (they must be forced blocks of this call, e.g. last blocks with
+    n_recent >= 1). Returns (out, lse, selected, selected_count)."""
     _need(q, torch.bfloat16); _need(summaries, torch.bfloat16)
     _need(k_pool, torch.bfloat16); _need(v_pool, torch.bfloat16)
     B, Hq, D = q.shape
@@ -237,12 +240,16 @@ def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.T
                             LS_AGG_MAX if group_agg == "max" else LS_AGG_MEAN,
                             int(topk), float(keep_ratio), int(n_sink), int(n_recent),
                             int(max_selected))
+    n_new = 0
+    if new_pages is not None:
+        _need(new_pages, torch.int32)
+        n_new = int(new_pages.numel())
     pool = _pool(k_pool, int(Hkv), int(P), int(D))
     check(_L.ls_sparse_decode_step(q.data_ptr(), LS_DTYPE_BF16, int(Hq), summaries.data_ptr(),
                                    k_pool.data_ptr(), v_pool.data_ptr(), pool, batch.c(),
                                    C.byref(params), selected.data_ptr(), selected_count.data_ptr(),
                                    float(sm_scale), out.data_ptr(), _DT[out.dtype], _ptr(lse),
-                                   workspace.data_ptr(),
+                                   _ptr(new_pages), n_new, workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse, selected, selected_count
 

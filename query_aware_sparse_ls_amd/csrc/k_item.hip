@@ -6,6 +6,7 @@
 //    the selection goes to the caller's buffers and stays in LDS for the
 //    attention, so the step is one launch with no hand-off between workgroups.
 #include "dev_item.h"
+#include "dev_summary.h"
 
 namespace ls {
 
@@ -58,9 +59,19 @@ __global__ __launch_bounds__(kItemThreads) void attn_item_kernel(AttnArgs a) {
   item_attn<D>(a, r, g, sel, cnt, sh);
 }
 
+// Rows of the grid past the batch refresh the summaries of the pages that
+// just filled (one wave per (page, head) tile), concurrently with the pairs'
+// steps: those pages are not scored in this call (the caller guarantees it).
 template <int D, int MAXC>
 __global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, TopkArgs ta,
-                                                                 AttnArgs aa) {
+                                                                 AttnArgs aa, SummaryUpdate up) {
+  if ((int)blockIdx.y >= sa.b.batch) {
+    const int tile = ((blockIdx.y - sa.b.batch) * gridDim.x + blockIdx.x) * kItemWaves + wave_id();
+    if (tile < up.n_tiles)
+      summary_tile_bf16<D, false>(up.keys, up.pages, tile, sa.b.num_pages, sa.num_kv_heads,
+                                  sa.b.page_size, up.out);
+    return;
+  }
   __shared__ int pg[MAXC];
   __shared__ int sel[MAXC + kItemEntryPad];
   __shared__ union {
@@ -242,8 +253,17 @@ hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,
-                            hipStream_t st) {
+                            const SummaryUpdate& up, hipStream_t st) {
   const int D = sa.head_dim, n = sa.b.max_blocks;
+  const bool one_launch = !pair_path(sa.b.batch, sa.num_kv_heads, n) && n <= 4096;
+  if (up.n_tiles > 0 && !one_launch) {
+    // the multi-launch forms refresh the summaries first
+    SummaryArgs su{up.keys, nullptr, ls_pool{sa.b.num_pages, sa.num_kv_heads, sa.b.page_size, D,
+                                             LS_DTYPE_BF16},
+                   up.pages, up.n_tiles / sa.num_kv_heads, up.out, LS_DTYPE_BF16};
+    const hipError_t e = launch_summaries(su, st);
+    if (e != hipSuccess) return e;
+  }
   if (pair_path(sa.b.batch, sa.num_kv_heads, n)) {
     // scoring over both workgroups of each pair, then top-k + attention
     const int pairs = sa.b.batch * sa.num_kv_heads;
@@ -269,11 +289,12 @@ hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnA
     const hipError_t e = launch_select_item(sa, ta, st);
     return e != hipSuccess ? e : launch_attn_item(aa, st);
   }
-  const dim3 grid(sa.num_kv_heads, sa.b.batch);
+  const int per_row = kItemWaves * sa.num_kv_heads;   // update tiles per extra grid row
+  const dim3 grid(sa.num_kv_heads, sa.b.batch + (up.n_tiles + per_row - 1) / per_row);
 #define LAUNCH(DD, MC)                                                                      \
   do {                                                                                      \
     hipLaunchKernelGGL((step_item_kernel<DD, MC>), grid, dim3(kItemThreads), 0, st, sa, ta, \
-                       aa);                                                                 \
+                       aa, up);                                                             \
     return hipGetLastError();                                                               \
   } while (0)
   if (D == 128) {

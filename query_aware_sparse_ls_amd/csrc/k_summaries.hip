@@ -11,7 +11,7 @@
 // float64, so the column sum is exact unless its terms span more than ~2^41
 // in magnitude; page_size is a power of two, so the mean is exact too, and it
 // is rounded once (nearest-even) to the summary dtype.
-#include "ls_internal.h"
+#include "dev_summary.h"
 
 namespace ls {
 
@@ -19,37 +19,9 @@ template <int D, bool kOutF32>
 __global__ __launch_bounds__(256) void summaries_bf16_kernel(
     const uint16_t* __restrict__ keys, const int32_t* __restrict__ page_ids, int n_pages,
     int num_pages, int num_heads, int page_size, void* __restrict__ out) {
-  constexpr int DPL = D / kWave;  // dims per lane: 1 or 2
   const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
   if (tile >= n_pages * num_heads) return;
-  const int i = tile / num_heads, h = tile - i * num_heads;
-  const int page = page_ids[i];
-  if (page < 0 || page >= num_pages) return;
-  const uint16_t* base = keys + ((size_t)page * num_heads + h) * (size_t)page_size * D + lane * DPL;
-  double acc[DPL];
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) acc[j] = 0.0;
-  for (int s = 0; s < page_size; ++s) {
-    if constexpr (DPL == 2) {
-      uint32_t pr = *reinterpret_cast<const uint32_t*>(base + (size_t)s * D);
-      acc[0] += (double)bf16_lo(pr);
-      acc[1] += (double)bf16_hi(pr);
-    } else {
-      acc[0] += (double)bf16_to_f32(base[(size_t)s * D]);
-    }
-  }
-  const double inv = 1.0 / (double)page_size;  // exact: power of two
-  const size_t o = ((size_t)page * num_heads + h) * D + lane * DPL;
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) {
-    double mean = acc[j] * inv;
-    if constexpr (kOutF32) {
-      reinterpret_cast<float*>(out)[o + j] = (float)mean;  // one RNE rounding
-    } else {
-      reinterpret_cast<uint16_t*>(out)[o + j] = f64_to_bf16_rne(mean);
-    }
-  }
+  summary_tile_bf16<D, kOutF32>(keys, page_ids, tile, num_pages, num_heads, page_size, out);
 }
 
 // fp8 e4m3fn keys with a per-token fp32 scale, single-head pool

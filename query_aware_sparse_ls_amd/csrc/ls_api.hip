@@ -151,7 +151,7 @@ extern "C" {
 
 const char* ls_last_error(void) { return g_err; }
 
-const char* ls_version(void) { return "libls 0.1.0 abi 1 gfx950"; }
+const char* ls_version(void) { return "libls 0.2.0 abi 2 gfx950"; }
 
 int32_t ls_attn_num_splits(int32_t max_selected) {
   if (max_selected < 1) return 1;
@@ -322,10 +322,11 @@ size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_he
 }
 
 ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads,
-                                const void* summaries, const void* k_pool, const void* v_pool,
+                                void* summaries, const void* k_pool, const void* v_pool,
                                 ls_pool pool, ls_batch batch, const ls_select_params* p,
                                 int32_t* selected, int32_t* selected_count, float sm_scale,
-                                void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                                void* out, int32_t out_dtype, float* lse_out,
+                                const int32_t* new_page_ids, int32_t n_new_pages, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   if (!p) return fail(LS_ERR_INVALID, "params must be non-null");
   if (p->struct_size != (int32_t)sizeof(ls_select_params))
@@ -350,6 +351,13 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
   if (p->topk == -1 && !(p->keep_ratio >= 0.0f && p->keep_ratio <= 1.0f))
     return fail(LS_ERR_INVALID, "keep_ratio must be in [0, 1]");
   if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
+  if (n_new_pages < 0) return fail(LS_ERR_INVALID, "n_new_pages < 0");
+  if (n_new_pages > 0 && !new_page_ids)
+    return fail(LS_ERR_INVALID, "new_page_ids must be non-null when n_new_pages > 0");
+  if (n_new_pages > 0 && p->n_recent < 1)
+    return fail(LS_ERR_INVALID,
+                "refreshing summaries in the step needs n_recent >= 1 (a page that just filled "
+                "must not be scored in the same call)");
   if (batch.batch_size == 0) return ok();
   if (batch.max_blocks > 16384)
     return fail(LS_ERR_UNSUPPORTED, "max_blocks %d (supported: <= 16384)", batch.max_blocks);
@@ -378,13 +386,22 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
                                     selected_count, p->max_selected,
                                     ls_attn_num_splits(p->max_selected), sm_scale, partials, out,
                                     out_dtype, lse_out);
+  const ls::SummaryUpdate up{static_cast<const uint16_t*>(k_pool), new_page_ids,
+                             n_new_pages * pool.num_heads, summaries};
   if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, num_q_heads / pool.num_heads,
                     batch.max_blocks, pool.num_pages)) {
     ls::ScoreArgs si = sa;
     si.scores = nullptr;
-    return hip_status(ls::launch_step_item(si, ta, aa, stream), "decode-step kernel launch");
+    return hip_status(ls::launch_step_item(si, ta, aa, up, stream), "decode-step kernel launch");
   }
-  hipError_t e = ls::launch_score(sa, stream);
+  hipError_t e = hipSuccess;
+  if (n_new_pages > 0) {
+    const ls::SummaryArgs su{k_pool, nullptr, pool, new_page_ids, n_new_pages, summaries,
+                             LS_DTYPE_BF16};
+    e = ls::launch_summaries(su, stream);
+    if (e != hipSuccess) return hip_status(e, "summary kernel launch");
+  }
+  e = ls::launch_score(sa, stream);
   if (e == hipSuccess) e = ls::launch_topk(ta, stream);
   if (e == hipSuccess) e = ls::launch_attn(aa, stream);
   return hip_status(e, "decode-step kernel launches");

@@ -68,6 +68,15 @@ struct AttnArgs {
 };
 
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t st);
+
+// Pages whose bf16 summaries a decode step refreshes alongside its work
+// (pages that just filled; n_tiles = pages * kv heads, 0 = none).
+struct SummaryUpdate {
+  const uint16_t* keys;     // K pool [num_pages][Hkv][P][D]
+  const int32_t* pages;
+  int32_t n_tiles;
+  void* out;                // summary pool [num_pages][Hkv][D] bf16
+};
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
@@ -99,7 +108,7 @@ inline uint32_t* pair_arrivals(float* partials, int pairs, int head_dim) {
 hipError_t launch_select_item(const ScoreArgs& sa, const TopkArgs& ta, hipStream_t st);
 hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st);
 hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,
-                            hipStream_t st);
+                            const SummaryUpdate& up, hipStream_t st);
 
 // Learned-indexer selection (k_indexer.hip): scoring of tokens (fp8 keys) or
 // blocks (bf16 block-mean keys) and the token top-k.

@@ -184,7 +184,7 @@ def check_pair(inp: BlockTopKInputs, res: GpuStep, r: int, g: int, *, topk, n_si
 
 def run_gpu_fused(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None, agg=None,
                   out_dtype=None, keep_ratio=0.0, sm_scale=None, workspace=None,
-                  summaries=None) -> GpuStep:
+                  summaries=None, new_pages=None) -> GpuStep:
     """The whole step in one call (ls_sparse_decode_step); it keeps its
     block scores on chip, so the result carries none."""
     import query_aware_sparse_ls_amd as ls
@@ -209,6 +209,7 @@ def run_gpu_fused(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None
     out, _, sel, cnt = ls.sparse_decode_step(
         inp.q, summaries, inp.k_pool, inp.v_pool, batch, topk=topk, n_sink=n_sink,
         n_recent=n_recent, max_selected=maxsel, sm_scale=sm_scale, group_agg=agg,
-        keep_ratio=keep_ratio, out_dtype=out_dtype, lse=lse, workspace=workspace)
+        keep_ratio=keep_ratio, out_dtype=out_dtype, lse=lse, new_pages=new_pages,
+        workspace=workspace)
     torch.cuda.synchronize()
     return GpuStep(summaries, None, sel, cnt, out, lse)

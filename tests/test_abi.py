@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 def test_version_and_empty_error():
     lib = _lib.load()
     assert b"gfx950" in lib.ls_version()
-    assert b"abi 1" in lib.ls_version()
+    assert b"abi 2" in lib.ls_version()
 
 
 def _pool(**kw):
@@ -138,3 +138,27 @@ def test_summaries_validation():
     assert f(FAKE, None, _pool(), FAKE, 1, FAKE, _lib.LS_DTYPE_FP8_E4M3FN,
              None) == _lib.LS_ERR_UNSUPPORTED
     assert f(None, None, _pool(), FAKE, 1, FAKE, 1, None) == _lib.LS_ERR_INVALID
+
+
+def test_step_validation():
+    lib = _lib.load()
+
+    def call(p=None, **kw):
+        a = dict(q=FAKE, summ=FAKE, k=FAKE, v=FAKE, pool=_pool(), batch=_batch(), sel=FAKE,
+                 cnt=FAKE, scale=0.1, out=FAKE, out_dtype=_lib.LS_DTYPE_BF16, lse=None,
+                 new=None, n_new=0, ws=FAKE, ws_bytes=0)
+        a.update(kw)
+        pp = C.byref(p if p is not None else _params())
+        return lib.ls_sparse_decode_step(a["q"], _lib.LS_DTYPE_BF16, 32, a["summ"], a["k"], a["v"],
+                                         a["pool"], a["batch"], pp, a["sel"], a["cnt"],
+                                         a["scale"], a["out"], a["out_dtype"], a["lse"],
+                                         a["new"], a["n_new"], a["ws"], a["ws_bytes"], None)
+
+    assert call() == _lib.LS_ERR_WORKSPACE
+    assert call(n_new=-1) == _lib.LS_ERR_INVALID
+    assert call(n_new=2) == _lib.LS_ERR_INVALID                  # pages missing
+    assert b"new_page_ids" in lib.ls_last_error()
+    # a page that just filled must be a forced (recent) block of the call
+    assert call(p=_params(n_recent=0), new=FAKE, n_new=2) == _lib.LS_ERR_INVALID
+    assert b"n_recent" in lib.ls_last_error()
+    assert call(batch=_batch(batch_size=0), new=FAKE, n_new=2) == _lib.LS_OK

@@ -122,3 +122,32 @@ def test_fused_full_size_llama8b_32k_b16():
     _same(sep, fus)
     for r, g in [(0, 0), (7, 3), (15, 7)]:
         check_pair(inp, fus, r, g, **_kw(inp))
+
+
+@pytest.mark.parametrize("batch", [16, 2])   # one launch (128 pairs) / split kernels (16 pairs)
+def test_step_refreshes_pages_that_filled(batch):
+    """Every request's last page just filled: the step rebuilds those pages'
+    summaries itself (rows start as NaN) and gives the same summaries,
+    selections and outputs, bit for bit, as building them first."""
+    import query_aware_sparse_ls_amd as ls
+    from oracle import block_summaries
+    from parity_util import complete_pages
+    from workloads import bf16_bits
+    cfg = reduced(LLAMA8B_32K_B16, batch=batch, context=4096)
+    say(f"step with summary refresh, batch {batch}")
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=31)
+    P, Hkv, D = cfg.page_size, cfg.num_kv_heads, cfg.head_dim
+    indptr = inp.page_indptr.cpu().tolist()
+    idx = inp.page_indices.cpu()
+    new = torch.tensor([int(idx[indptr[r] + cfg.context // P - 1]) for r in range(batch)],
+                       dtype=torch.int32, device="cuda")
+    full = torch.zeros(inp.num_pages, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    ls.build_block_summaries(inp.k_pool, complete_pages(inp).cuda(), full)
+    stale = full.clone()
+    stale[new.long()] = float("nan")
+    a = run_gpu_fused(inp, summaries=stale, new_pages=new)
+    b = run_gpu_fused(inp, summaries=full)
+    assert torch.equal(stale.view(torch.int16), full.view(torch.int16))
+    _same(a, b)
+    want = block_summaries(bf16_bits(inp.k_pool), new.cpu().numpy())
+    assert np.array_equal(bf16_bits(stale)[new.cpu().numpy()], want)
