@@ -28,7 +28,6 @@
 namespace ls {
 
 constexpr int kMlaDk = 576, kMlaDv = 512;
-constexpr int kMlaPartStride = kMlaDv + 4;   // o[512], m, l, pad: 16-byte aligned rows
 constexpr int kMlaThreads = 512, kMlaWaves = 8;
 constexpr int kMlaHeadsPerWg = 32;                     // two 16-head tiles
 constexpr int kMlaTile = 64;                           // tokens per LDS tile (4 MFMA row tiles)
@@ -37,6 +36,13 @@ constexpr int kMlaChunks = kMlaTile * (kMlaDk / 8);    // 16-byte chunks per til
 constexpr int kMlaChunksPerThread = kMlaChunks / kMlaThreads;
 static_assert(kMlaChunks % kMlaThreads == 0, "tile chunks per thread");
 static_assert(kMlaSplitTokens % kMlaTile == 0, "whole tiles per split");
+
+// Byte offset of the o partials in the workspace: after the (m, l) pairs of
+// every (request, head, split) row, 256-byte aligned.
+__device__ __forceinline__ size_t mla_o_offset(const MlaArgs& a) {
+  const size_t ml = (size_t)a.b.batch * a.num_q_heads * a.num_splits * 2 * sizeof(float);
+  return (ml + 255) / 256 * 256;
+}
 
 struct MlaLds {
   alignas(16) uint32_t tile[kMlaTile * kMlaRowWords];
@@ -225,16 +231,36 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     tile_step(t, ldA);
     if (t + 1 < ntiles) tile_step(t + 1, ldB);
   }
-  // partial state: o rows = heads 4kq + i of the tile, column = dim 128 sub + 16 n + col
-  float* part = a.partials + (((size_t)r * H + head0) * S + s) * kMlaPartStride;
-  const size_t hstride = (size_t)S * kMlaPartStride;
-#pragma unroll
-  for (int n = 0; n < 8; ++n)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[(4 * kq + i) * hstride + 128 * sub + 16 * n + col] = o[n][i];
+  // partial state: (m, l) per head, and o, rows = heads 4kq + i of the tile,
+  // column = dim 128 sub + 16 n + col: unnormalised fp32 for fp32 output,
+  // normalised (o / l, bounded by the largest |v|) bf16 for bf16 output
+  const size_t prow = ((size_t)r * H + head0) * S + s;   // (head0, s) partial row
+  float* ml = a.partials;
   if (sub == 0 && kq == 0) {
-    part[col * hstride + kMlaDv] = m;
-    part[col * hstride + kMlaDv + 1] = l;
+    ml[(prow + (size_t)col * S) * 2] = m;
+    ml[(prow + (size_t)col * S) * 2 + 1] = l;
+  }
+  char* obase = reinterpret_cast<char*>(a.partials) + mla_o_offset(a);
+  if (out32) {
+    float* po = reinterpret_cast<float*>(obase) + prow * kMlaDv;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        po[(size_t)(4 * kq + i) * S * kMlaDv + 128 * sub + 16 * n + col] = o[n][i];
+  } else {
+    uint16_t* po = reinterpret_cast<uint16_t*>(obase) + prow * kMlaDv;
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(l, 4 * kq + i);
+      inv[i] = li > 0.0f ? 1.0f / li : 0.0f;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        po[(size_t)(4 * kq + i) * S * kMlaDv + 128 * sub + 16 * n + col] = f32_to_bf16_rne(o[n][i] * inv[i]);
   }
 }
 
@@ -245,22 +271,44 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const int t = threadIdx.x & 127;
   if (row >= a.b.batch * a.num_q_heads) return;
   const int S = a.num_splits;
-  const float* part = a.partials + (size_t)row * S * (kMlaPartStride);
+  const bool out32 = a.out_dtype == LS_DTYPE_FP32;
+  const float* ml = a.partials + (size_t)row * S * 2;
+  const char* obase = reinterpret_cast<const char*>(a.partials) + mla_o_offset(a);
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part[s * (kMlaPartStride) + kMlaDv]);
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
   float O[4] = {0.0f, 0.0f, 0.0f, 0.0f}, Ls = 0.0f;
   if (M != kNegInf) {
-    for (int s = 0; s < S; ++s) {
-      const float* ps = part + s * (kMlaPartStride);
-      const float f = exp2f(ps[kMlaDv] - M);   // splits with m = -inf give 0
-      Ls += f * ps[kMlaDv + 1];
-      const float4 v = *reinterpret_cast<const float4*>(ps + 4 * t);
-      O[0] += f * v.x; O[1] += f * v.y; O[2] += f * v.z; O[3] += f * v.w;
+    // 4 splits per round with their loads issued together (in split order)
+    constexpr int U = 4;
+    for (int s0 = 0; s0 < S; s0 += U) {
+      float f[U], ls[U];
+      float4 vf[U];
+      uint2 vb[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int s = s0 + j < S ? s0 + j : S - 1;
+        f[j] = s0 + j < S ? exp2f(ml[2 * s] - M) : 0.0f;   // splits with m = -inf give 0
+        ls[j] = ml[2 * s + 1];
+        const size_t oi = ((size_t)row * S + s) * kMlaDv + 4 * t;
+        if (out32) vf[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(obase) + oi);
+        else vb[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(obase) + oi);
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        Ls += f[j] * ls[j];
+        if (out32) {
+          O[0] += f[j] * vf[j].x; O[1] += f[j] * vf[j].y; O[2] += f[j] * vf[j].z; O[3] += f[j] * vf[j].w;
+        } else {
+          const float w = f[j] * ls[j];   // the split's o was stored divided by its l
+          O[0] += w * bf16_lo(vb[j].x); O[1] += w * bf16_hi(vb[j].x);
+          O[2] += w * bf16_lo(vb[j].y); O[3] += w * bf16_hi(vb[j].y);
+        }
+      }
     }
   }
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
   const size_t base = (size_t)row * kMlaDv + 4 * t;
-  if (a.out_dtype == LS_DTYPE_FP32) {
+  if (out32) {
     float* out = reinterpret_cast<float*>(a.out) + base;
     *reinterpret_cast<float4*>(out) = make_float4(O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv);
   } else {

@@ -565,8 +565,8 @@ int32_t ls_mla_num_splits(int32_t max_tokens) {
 size_t ls_sparse_mla_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
                                            int32_t max_tokens) {
   if (batch_size <= 0 || num_q_heads <= 0) return 0;
-  return align_up((size_t)batch_size * num_q_heads * ls_mla_num_splits(max_tokens) * (512 + 4) *
-                  sizeof(float));
+  const size_t rows = (size_t)batch_size * num_q_heads * ls_mla_num_splits(max_tokens);
+  return align_up(rows * 2 * sizeof(float)) + align_up(rows * 512 * sizeof(float));
 }
 
 ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,

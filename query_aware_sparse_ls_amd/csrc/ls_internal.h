@@ -160,7 +160,7 @@ struct MlaArgs {
   int32_t max_selected;
   int32_t num_splits;
   float sm_scale_log2;
-  float* partials;            // [B][H][S][512 + 4] (o, m, l, pad)
+  float* partials;            // (m, l) [B][H][S][2], then o [B][H][S][512] (fp32 or bf16)
   void* out;                  // [B][H][512]
   int32_t out_dtype;
   float* lse;
