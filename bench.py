@@ -530,6 +530,72 @@ def bench_indexer(args, coarse: bool) -> int:
     return 0
 
 
+def bench_dense(args) -> int:
+    """Time the k = all path: split-K attention over every block of the
+    8B/32K/B16 workload (ls_sparse_attn_decode with no selection), the dense
+    baseline the sparse step's speedup is judged against."""
+    import torch
+    import query_aware_sparse_ls_amd as ls
+    from workloads import LLAMA8B_32K_B16, make_block_topk_inputs
+    cfg = LLAMA8B_32K_B16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Hq, Hkv, D, P = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
+    sm = 1.0 / math.sqrt(D)
+    R = max(1, min(args.replicas, 2))    # one step reads 2 GiB: no cache reuse either way
+    reps = []
+    for i in range(R):
+        inp = make_block_topk_inputs(cfg, device=dev, seed=cfg.seed + i)
+        b = ls.PagedBatch(inp.page_indptr, inp.page_indices, inp.seq_lens, inp.max_blocks())
+        reps.append(dict(inp=inp, batch=b,
+                         out=torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev),
+                         ws=torch.empty(ls.sparse_attn_decode_workspace_size(
+                             B, Hq, D, 0, b.max_blocks), dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    print(f"# {R} replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
+
+    def call(rp):
+        inp = rp["inp"]
+        ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, rp["batch"], None, None,
+                              sm_scale=sm, out=rp["out"], workspace=rp["ws"])
+
+    for i in range(max(1, args.warmup)):
+        call(reps[i % R])
+    torch.cuda.synchronize()
+    steps = max(R, args.steps // R * R)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(1e8))     # the host enqueues ahead of the device
+    e0.record()
+    for i in range(steps):
+        call(reps[i % R])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    L = cfg.context
+    kv = B * L * Hkv * D * 2 * 2
+    nbytes = {"kv": kv, "q_out_pagetable": B * Hq * D * 2 * 2 + B * (L // P) * 4}
+    nbytes["total"] = sum(nbytes.values())
+    gbps = nbytes["total"] / (ms * 1e-3) / 1e9
+    res = {"metric": "dense (k = all) split-K decode attention calls/sec at 8B/32K/B16",
+           "value": round(1e3 / ms, 2), "unit": "calls/s", "n_gpus": 1, "steps": steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg.name + " dense", "batch": B, "context": L, "q_heads": Hq,
+                      "kv_heads": Hkv, "head_dim": D, "page_size": P, "replicas": R,
+                      "timing": "eager, back-to-back calls"},
+           "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
+           "roofline": {"kernel": "ls::attn_chunk_kernel<128> + ls::attn_combine_kernel<128> "
+                                  "(one library call)", "bound": "hbm",
+                        "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "algorithmic_bytes_per_launch": nbytes["total"],
+                        "avg_launch_ms": round(ms, 5)},
+           "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,10 +616,11 @@ def main(argv=None) -> int:
               "copy-fetch-cmd", "copy-write-cmd"):
         ap.add_argument("--" + a, default="")
     ap.add_argument("--copy-bytes", type=int, default=0)
-    ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine"),
+    ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense"),
                     default="block-topk",
                     help="block-topk: the 8B/32K/B16 block top-k step (default); indexer: "
-                         "token top-2048 of 8 x 128K + sparse MLA; coarse-to-fine: 4 x 950K")
+                         "token top-2048 of 8 x 128K + sparse MLA; coarse-to-fine: 4 x 950K; "
+                         "dense: k = all split-K attention on the 8B/32K/B16 workload")
     args = ap.parse_args(argv)
     if args.summarize_profiles:
         return summarize_profiles(args)
@@ -563,6 +630,8 @@ def main(argv=None) -> int:
         return 2
     if args.copy_calibrate:
         return copy_calibration(args.copy_calibrate)
+    if args.path == "dense":
+        return bench_dense(args)
     if args.path != "block-topk":
         return bench_indexer(args, coarse=args.path == "coarse-to-fine")
 

@@ -199,10 +199,13 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
  *   lse_out[r][h] = M + ln sum_t e^{z_t - M}
  * with fp32 logits, softmax and accumulation; partial softmax states over
  * disjoint token sets are merged by log-sum-exp in a fixed order
- * (deterministic). With at least 64 (request, kv head) pairs one workgroup
- * owns each pair and merges on chip; with fewer, the selected blocks are
- * split over several workgroups whose partial results go through the
- * workspace and are merged by a second kernel. An empty T gives out = 0 and
+ * (deterministic). For a selection with at least 64 (request, kv head)
+ * pairs one workgroup owns each pair and merges on chip (two workgroups
+ * merging through the workspace for requests of more than 4096 blocks in
+ * calls of at most 256 pairs); with fewer pairs, and always for the dense
+ * path, the blocks are split over several workgroups per pair (8 blocks
+ * each) whose partial results go through the workspace and are merged by a
+ * second kernel (split-K). An empty T gives out = 0 and
  * lse = -inf. The output is rounded once (nearest-even) to out_dtype.
  * For a selection written by ls_score_select the entries past the count are
  * -1; other callers may leave them undefined (they are never read as blocks).

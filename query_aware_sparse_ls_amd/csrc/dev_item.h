@@ -266,10 +266,21 @@ struct ItemPair {
   int half;            // which of the two workgroups this is
 };
 
+// Split s of num_splits of a (request, kv head) pair's positions: the merged
+// state is written unnormalised as split s of the split-K partials
+// (o relative to the split maximum, then m in the log2 domain, then l; the
+// layout attn_split writes), for the combine kernel to merge.
+struct ItemSplit {
+  float* part;
+  int num_splits;
+  int s;
+};
+
 template <int D>
 __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const int* ent,
                                           int cnt, ItemAttnLds<D>& sh,
-                                          const ItemPair* pair = nullptr) {
+                                          const ItemPair* pair = nullptr,
+                                          const ItemSplit* split = nullptr) {
   using ST = Stage<D>;
   constexpr int KS = D / 32, NL = ST::NL, NT = D / 16, NPF = kItemPrefetch;
   constexpr int RW = ST::kVRowWords;
@@ -322,6 +333,15 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
       const int ie = first + step * (k + NPF);
       const int en = ie < nent ? ent[ie] : -1;
       if (k < nbw) {
+        // V rows past the block's tokens (a partly filled last page, or an
+        // invalid entry) are zeroed: their weights are 0, but their contents
+        // are unspecified and 0 * NaN would reach the output. K rows need no
+        // such care: their logits are masked.
+        if (ntok[s] < 16) {
+#pragma unroll
+          for (int j = 0; j < NL; ++j)
+            if (j * ST::RPI + lane / ST::LPR >= ntok[s]) vr[s][j] = make_uint4(0, 0, 0, 0);
+        }
         // stage the K and V tiles (row-major, padded rows)
         stage_k<D>(kt, kr[s], 0u);
 #pragma unroll
@@ -436,6 +456,18 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
         Ls += f * sh.l[w][h];
       }
     }
+  }
+  if (split) {
+    if (e < 4 * D) {
+      float* ph = split->part + (((size_t)r * a.num_q_heads + g * 4 + h) * split->num_splits +
+                                 split->s) * (D + 2);
+      ph[d] = O;
+      if (d == 0) {
+        ph[D] = M;
+        ph[D + 1] = Ls;
+      }
+    }
+    return;
   }
   if (pair) {
     // publish, count the arrival, and let the second workgroup finish

@@ -30,6 +30,15 @@ static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st) {
+  const int items = a.b.batch * a.num_q_heads;
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((items + 3) / 4), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((items + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   if (a.head_dim == 128) return launch_d<128>(a, st);
   return launch_d<64>(a, st);

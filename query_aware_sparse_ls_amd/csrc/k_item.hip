@@ -190,6 +190,45 @@ __global__ __launch_bounds__(kItemThreads) void attn_pair_kernel(AttnArgs a, flo
   item_attn<D>(a, r, g, sel, cnt, sh, &pr);
 }
 
+// Split s of pair (r, g): positions [s * chunk, s * chunk + chunk) of the
+// pair's selection row (of its block list when there is no selection), read
+// straight from the page table into walk entries, attended by the eight
+// waves and written as split s of the partials.
+template <int D>
+__global__ __launch_bounds__(kItemThreads) void attn_chunk_kernel(AttnArgs a, int chunk) {
+  __shared__ int ent[kChunkMaxBlocks + kItemEntryPad];
+  __shared__ ItemAttnLds<D> sh;
+  const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const size_t item = (size_t)r * a.num_kv_heads + g;
+  const ReqGeom geo = req_geom(a.b, r, 0, 0);
+  const bool sparse = a.selected != nullptr;
+  int total = geo.nb;
+  if (sparse) {
+    total = a.selected_count[item];
+    total = total < 0 ? 0 : (total > a.max_selected ? a.max_selected : total);
+  }
+  const int p0 = s * chunk;
+  int cnt = total - p0;
+  cnt = cnt < 0 ? 0 : (cnt > chunk ? chunk : cnt);
+  const int32_t* pages = a.b.indices + geo.page_base;
+  const int32_t* row = sparse ? a.selected + item * a.max_selected + p0 : nullptr;
+  for (int pos = threadIdx.x; pos < item_entry_count(cnt); pos += kItemThreads) {
+    int e = -1;
+    if (pos < cnt) {
+      const int blk = sparse ? row[pos] : p0 + pos;
+      if (blk >= 0 && blk < geo.nb) {
+        const int p = pages[blk];
+        const int nt = geo.L - blk * 16 < 16 ? geo.L - blk * 16 : 16;
+        if (p >= 0 && p < a.b.num_pages && nt > 0) e = p * 32 + nt;
+      }
+    }
+    ent[pos] = e;
+  }
+  __syncthreads();
+  const ItemSplit sp{a.partials, a.num_splits, s};
+  item_attn<D>(a, r, g, ent, cnt, sh, nullptr, &sp);
+}
+
 bool pair_path(int batch, int hkv, int max_blocks) {
   return (long long)batch * hkv <= kPairMaxPairs && max_blocks > kPairMinBlocks;
 }
@@ -250,6 +289,34 @@ hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st) {
   } while (0)
   LS_ITEM_DISPATCH(LAUNCH)
 #undef LAUNCH
+}
+
+hipError_t launch_attn_chunked(const AttnArgs& a0, hipStream_t st) {
+  AttnArgs a = a0;
+  const int n = a.selected ? a.max_selected : a.b.max_blocks;   // positions per pair
+  const int pairs = a.b.batch * a.num_kv_heads;
+  // about 2048 workgroups (8 per CU), at least 16 positions (two per wave)
+  // per split and at most kChunkMaxBlocks
+  constexpr int kTargetWgs = 2048;
+  int splits = (kTargetWgs + pairs - 1) / pairs;
+  const int most = (n + 15) / 16;
+  splits = splits > most ? most : splits;
+  splits = splits < 1 ? 1 : splits;
+  int chunk = (n + splits - 1) / splits;
+  chunk = (chunk + kAttnBlocksPerSplit - 1) / kAttnBlocksPerSplit * kAttnBlocksPerSplit;
+  chunk = chunk > kChunkMaxBlocks ? kChunkMaxBlocks : chunk;
+  chunk = chunk < kAttnBlocksPerSplit ? kAttnBlocksPerSplit : chunk;
+  a.num_splits = (n + chunk - 1) / chunk;
+  if (a.num_splits < 1) a.num_splits = 1;
+  if (a.num_splits > a0.num_splits) return hipErrorInvalidValue;   // partials capacity
+  const dim3 grid(a.num_splits, a.num_kv_heads, a.b.batch);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((attn_chunk_kernel<128>), grid, dim3(kItemThreads), 0, st, a, chunk);
+  else
+    hipLaunchKernelGGL((attn_chunk_kernel<64>), grid, dim3(kItemThreads), 0, st, a, chunk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn_combine(a, st);
 }
 
 hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,

@@ -34,6 +34,7 @@ constexpr int kMlaTile = 64;                           // tokens per LDS tile (4
 constexpr int kMlaRowWords = kMlaDk / 2 + 4;           // 1168-byte padded rows (16-byte aligned)
 constexpr int kMlaChunks = kMlaTile * (kMlaDk / 8);    // 16-byte chunks per tile
 constexpr int kMlaChunksPerThread = kMlaChunks / kMlaThreads;
+static_assert(kMlaChunksPerThread <= 32, "one mask bit per chunk");
 static_assert(kMlaChunks % kMlaThreads == 0, "tile chunks per thread");
 static_assert(kMlaSplitTokens % kMlaTile == 0, "whole tiles per split");
 
@@ -103,12 +104,17 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
   // tile loads: chunk c = tid + 512 i -> token c / 72, 16 bytes at 8 (c % 72);
   // two tiles of loads are in flight (register buffers A and B)
-  auto issue = [&](int t, uint4* ld) {
+  // vm: bit i set when chunk i belongs to a selected token (the others read
+  // row 0 and are zeroed when staged: their weights are 0, but 0 * NaN would
+  // reach the output)
+  auto issue = [&](int t, uint4* ld, uint32_t& vm) {
+    vm = 0u;
 #pragma unroll
     for (int i = 0; i < kMlaChunksPerThread; ++i) {
       const int c = tid + kMlaThreads * i;
       const int tok = t * kMlaTile + c / (kMlaDk / 8);
       const int off = (t < ntiles && tok < ntok) ? sh.rowoff[tok] : -1;
+      vm |= off >= 0 ? (1u << i) : 0u;
       ld[i] = ldg16_stream(a.latent + (size_t)(uint32_t)(off >= 0 ? off : 0) * kMlaDk + 8 * (c % (kMlaDk / 8)));
     }
   };
@@ -117,15 +123,21 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   for (int n = 0; n < 8; ++n) o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m = kNegInf, l = 0.0f;   // state of head head0 + col
   constexpr int RS = 2 * kMlaRowWords;   // LDS row stride in bf16 elements
-  auto tile_step = [&](int t, uint4* ld) {
+  constexpr uint32_t kAllChunks = (1u << kMlaChunksPerThread) - 1u;
+  auto tile_step = [&](int t, uint4* ld, uint32_t& vm) {
     // stage tile t, then start loading tile t + 2 into the same registers
+    if (vm != kAllChunks) {
+#pragma unroll
+      for (int i = 0; i < kMlaChunksPerThread; ++i)
+        if (!((vm >> i) & 1u)) ld[i] = make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < kMlaChunksPerThread; ++i) {
       const int c = tid + kMlaThreads * i;
       *reinterpret_cast<uint4*>(sh.tile + (c / (kMlaDk / 8)) * kMlaRowWords + 4 * (c % (kMlaDk / 8))) = ld[i];
     }
     __syncthreads();
-    issue(t + 2, ld);
+    issue(t + 2, ld, vm);
     // partial logits over this wave's k-steps, 4 row tiles of 16 tokens
     f32x4_t z[4];
 #pragma unroll
@@ -225,11 +237,12 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     __syncthreads();   // the tile and the logit partials are rewritten next
   };
   uint4 ldA[kMlaChunksPerThread], ldB[kMlaChunksPerThread];
-  issue(0, ldA);
-  issue(1, ldB);
+  uint32_t vmA, vmB;
+  issue(0, ldA, vmA);
+  issue(1, ldB, vmB);
   for (int t = 0; t < ntiles; t += 2) {
-    tile_step(t, ldA);
-    if (t + 1 < ntiles) tile_step(t + 1, ldB);
+    tile_step(t, ldA, vmA);
+    if (t + 1 < ntiles) tile_step(t + 1, ldB, vmB);
   }
   // partial state: (m, l) per head, and o, rows = heads 4kq + i of the tile,
   // column = dim 128 sub + 16 n + col: unnormalised fp32 for fp32 output,

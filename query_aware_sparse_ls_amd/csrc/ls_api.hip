@@ -304,9 +304,14 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                     selected_count, max_selected, ls_attn_num_splits(cap),
                                     sm_scale, static_cast<float*>(workspace), out, out_dtype,
                                     lse_out);
-  if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, num_q_heads / pool.num_heads,
-                    batch.max_blocks, pool.num_pages))
+  // a selection goes to one workgroup per pair (or two); the dense path
+  // (every block) is split-K over many workgroups per pair, runs of up to
+  // 512 blocks each
+  if (selected && ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim,
+                                num_q_heads / pool.num_heads, batch.max_blocks, pool.num_pages))
     return hip_status(ls::launch_attn_item(aa, stream), "attention kernel launch");
+  if (!selected && pool.num_pages < (1 << 26))
+    return hip_status(ls::launch_attn_chunked(aa, stream), "attention kernel launch");
   return hip_status(ls::launch_attn(aa, stream), "attention kernel launch");
 }
 

@@ -80,6 +80,8 @@ struct SummaryUpdate {
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+// The combine kernel alone: merges a.num_splits partials per query head.
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);
 
 // Per-(request, kv head) kernels (one 1024-thread workgroup per pair), used
 // when there are at least kItemMinPairs pairs: the selection and the
@@ -107,6 +109,13 @@ inline uint32_t* pair_arrivals(float* partials, int pairs, int head_dim) {
 }
 hipError_t launch_select_item(const ScoreArgs& sa, const TopkArgs& ta, hipStream_t st);
 hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st);
+// Split-K with the per-pair attention body: each workgroup attends a run of
+// up to kChunkMaxBlocks consecutive positions of a pair's selection (of its
+// block list on the dense path), then the combine kernel merges the runs.
+// Needs num_pages < 2^26; a.num_splits on entry is the capacity of the
+// partials (splits of kAttnBlocksPerSplit), which the chunking never exceeds.
+constexpr int kChunkMaxBlocks = 512;
+hipError_t launch_attn_chunked(const AttnArgs& a, hipStream_t st);
 hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,
                             const SummaryUpdate& up, hipStream_t st);
 

@@ -62,6 +62,26 @@ def max_selected_for(topk, n_sink, n_recent, max_blocks, keep_ratio=None):
     return min(max_blocks, max(n_sink + n_recent + 1, by_ratio))
 
 
+def poison_padding(inp: BlockTopKInputs) -> int:
+    """Fill the slots past each request's last token, in its last page, with
+    NaN in K and V (their contents are unspecified; the kernels must weigh
+    them by 0 without reading NaN into the output). Returns the slots set."""
+    from workloads.generate import BF16_NAN_BITS
+    P = inp.cfg.page_size
+    nan = torch.tensor(BF16_NAN_BITS, dtype=torch.int16).view(torch.bfloat16).item()
+    lens = inp.seq_lens.cpu().tolist()
+    indptr = inp.page_indptr.cpu().tolist()
+    idx = inp.page_indices.cpu().tolist()
+    n = 0
+    for r, L in enumerate(lens):
+        if L % P:
+            page = idx[indptr[r] + L // P]
+            inp.k_pool[page, :, L % P:] = nan
+            inp.v_pool[page, :, L % P:] = nan
+            n += P - L % P
+    return n
+
+
 def run_gpu_step(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None, agg=None,
                  out_dtype=None, keep_ratio=0.0, sm_scale=None, dense=False) -> GpuStep:
     import query_aware_sparse_ls_amd as ls

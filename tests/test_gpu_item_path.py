@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity_util import check_pair, run_gpu_fused, run_gpu_step, say
+from parity_util import check_pair, poison_padding, run_gpu_fused, run_gpu_step, say
 from oracle.method import topk_from_keep_ratio
 from workloads import LLAMA8B_32K_B16, TINY_4K, RAGGED_B64, make_block_topk_inputs, reduced
 
@@ -111,10 +111,12 @@ def test_item_path_ragged_keep_ratio(ratio):
 def test_item_path_poisoned_unused_pages():
     cfg = reduced(RAGGED_B64, batch=8, ragged_range=(100, 6000), topk=8, keep_ratio=None,
                   pool_occupancy=0.7)
-    say("per-pair kernels, NaN-poisoned unused pool pages")
+    say("per-pair kernels, NaN-poisoned unused pool pages and page padding")
     inp = make_block_topk_inputs(cfg, device="cuda", poison_unused=True)
+    assert poison_padding(inp) > 0
     res = run_gpu_step(inp)
     assert torch.isfinite(res.out.float()).all()
+    _same(res, run_gpu_fused(inp, summaries=res.summaries))
     for r, g in _pairs(cfg, 6, seed=4):
         check_pair(inp, res, r, g, **_kw(inp))
 
