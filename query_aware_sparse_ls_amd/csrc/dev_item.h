@@ -36,8 +36,8 @@ namespace ls {
 
 constexpr int kItemThreads = 512;
 constexpr int kItemWaves = kItemThreads / kWave;
-constexpr int kItemScorePrefetch = 6;   // summary tiles in flight per wave
-constexpr int kItemPrefetch = 4;        // K/V blocks in flight per wave
+constexpr int kItemScorePrefetch = 2;   // summary tiles in flight per wave
+constexpr int kItemPrefetch = 2;        // K/V blocks in flight per wave
 // Walk entries past the selection that item_attn may read: wave w refills
 // its slots with position w + 8(k + kItemPrefetch) for k < nbw + kItemPrefetch
 // - 1, nbw = ceil((cnt - w) / 8), i.e. at most cnt + 7 + 8(2 kItemPrefetch - 2).
