@@ -46,7 +46,7 @@ namespace ls {
 constexpr int kIdxDim = 128;            // indexer key / query dim
 constexpr int kIdxThreads = 256;
 constexpr int kIdxWaves = kIdxThreads / kWave;
-constexpr int kIdxPrefetch = 6;         // key tiles in flight per wave
+constexpr int kIdxPrefetch = 2;         // key tiles in flight per wave
 constexpr int kIdxMaxTilesPerWg = 128;  // units per scoring workgroup <= 2048
 constexpr int kIdxMaxWords = kIdxMaxUnits / 32;
 

@@ -238,13 +238,6 @@ __device__ __forceinline__ void item_entries(const AttnArgs& a, const ReqGeom& g
 // Number of walk entries item_attn reads for a selection of cnt blocks.
 __device__ __forceinline__ int item_entry_count(int cnt) { return cnt + kItemEntryPad; }
 
-// bf16 bits of x rounded to nearest even; *rest = x - that value.
-__device__ __forceinline__ uint32_t bf16_split(float x, float* rest) {
-  const uint32_t b = f32_to_bf16_rne(x);
-  *rest = x - __uint_as_float(b << 16);
-  return b;
-}
-
 // Attention of the G = 4 query heads of (r, g) over the walk entries ent[]
 // (LDS, from item_entries; cnt = selection size), written as out / lse.
 // Wave w takes selection positions w, w + 8, ...; per block it computes the
@@ -368,11 +361,13 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
         xor_pair<32>(bm, lo, hi);
         bm = fmaxf(lo, hi);
         const float mn = fmaxf(m, bm);
-        const float alpha = mn == kNegInf ? 1.0f : exp2f(m - mn);
+        // exp2 of values <= 0 with -inf -> 0 (mn = -inf: nothing seen yet, all 0)
+        const float mref = mn == kNegInf ? 0.0f : mn;
+        const float alpha = mn == kNegInf ? 1.0f : exp2_fast(m - mref);
         float p[4], ps = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = z[i] == kNegInf ? 0.0f : exp2f(z[i] - mn);
+          p[i] = exp2_fast(z[i] - mref);
           ps += p[i];
         }
         xor_pair<16>(ps, lo, hi);
@@ -390,18 +385,14 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
             o[n][0] *= a0; o[n][1] *= a1; o[n][2] *= a2; o[n][3] *= a3;
           }
         }
-        // P in bf16 parts, in the A-operand layout (row = head, k = 4 tokens)
-        float r1[4], r2[4];
-        uint32_t h16[4], l16[4], m16[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h16[i] = bf16_split(p[i], &r1[i]);
-          l16[i] = bf16_split(r1[i], &r2[i]);
-          m16[i] = f32_to_bf16_rne(r2[i]);
-        }
-        const uint2 ph = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
-        const uint2 pl = make_uint2(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16));
-        const uint2 pm = make_uint2(m16[0] | (m16[1] << 16), m16[2] | (m16[3] << 16));
+        // P in bf16 parts hi + lo (+ lo2 for fp32 output), in the A-operand
+        // layout (row = head, k = 4 tokens)
+        uint2 ph, pl, pm = make_uint2(0u, 0u);
+        bf16x2_split(p[0], p[1], &ph.x);
+        bf16x2_split(p[2], p[3], &ph.y);
+        bf16x2_split(p[0], p[1], &pl.x);
+        bf16x2_split(p[2], p[3], &pl.y);
+        if (out32) pm = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
         // o += P . V, one 16-dim tile at a time; B = V[tokens 4kq..+4][dim],
         // gathered by one transpose read: this lane addresses row
         // 4 kq + row / 4 at columns 4 (row % 4) of the 16-dim tile

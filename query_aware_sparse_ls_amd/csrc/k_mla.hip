@@ -49,13 +49,9 @@ struct MlaLds {
   alignas(16) uint32_t tile[kMlaTile * kMlaRowWords];
   f32x4_t red[kMlaWaves][4][kWave];   // partial logits: wave, 16-token row tile, lane
   int rowoff[kMlaSplitTokens];        // token row index in the pool (page * P + slot), -1 = skip
+  unsigned long long valid[kMlaSplitTokens / kMlaTile];   // per tile: bit = token row present
 };
-
-__device__ __forceinline__ uint32_t mla_bf16_split(float x, float* rest) {
-  const uint32_t b = f32_to_bf16_rne(x);
-  *rest = x - __uint_as_float(b << 16);
-  return b;
-}
+static_assert(kMlaSplitTokens <= kMlaThreads && kMlaTile == kWave, "one ballot per tile");
 
 // Workgroup (request r, 32 heads, split s), 8 waves. Wave w works on head
 // tile w / 4 (16 heads): the QK^T k-steps of quarter w % 4 (5, 5, 4, 4 of the
@@ -89,6 +85,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
       }
     }
     sh.rowoff[i] = off;
+    const unsigned long long vb = __ballot(off >= 0);   // a wave = one tile's tokens
+    if ((i & (kWave - 1)) == 0) sh.valid[i / kWave] = vb;
   }
   // q^T operand of this wave's k-steps: head 32 hg + 16 ht + col, dims 32k + 8kq
   const int ks0 = sub < 2 ? 5 * sub : 10 + 4 * (sub - 2);
@@ -103,7 +101,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   const bool out32 = a.out_dtype == LS_DTYPE_FP32;
   const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
   // tile loads: chunk c = tid + 512 i -> token c / 72, 16 bytes at 8 (c % 72);
-  // two tiles of loads are in flight (register buffers A and B)
+  // one tile of loads is in flight while the staged one is used (more in
+  // flight only lengthens the memory-side queues)
   // vm: bit i set when chunk i belongs to a selected token (the others read
   // row 0 and are zeroed when staged: their weights are 0, but 0 * NaN would
   // reach the output)
@@ -125,7 +124,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   constexpr int RS = 2 * kMlaRowWords;   // LDS row stride in bf16 elements
   constexpr uint32_t kAllChunks = (1u << kMlaChunksPerThread) - 1u;
   auto tile_step = [&](int t, uint4* ld, uint32_t& vm) {
-    // stage tile t, then start loading tile t + 2 into the same registers
+    // stage tile t, then start loading tile t + 1 into the same registers
     if (vm != kAllChunks) {
 #pragma unroll
       for (int i = 0; i < kMlaChunksPerThread; ++i)
@@ -137,7 +136,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
       *reinterpret_cast<uint4*>(sh.tile + (c / (kMlaDk / 8)) * kMlaRowWords + 4 * (c % (kMlaDk / 8))) = ld[i];
     }
     __syncthreads();
-    issue(t + 2, ld, vm);
+    issue(t + 1, ld, vm);
     // partial logits over this wave's k-steps, 4 row tiles of 16 tokens
     f32x4_t z[4];
 #pragma unroll
@@ -157,6 +156,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     for (int j = 0; j < 4; ++j) sh.red[wave][j][lane] = z[j];
     __syncthreads();
     // full logits of head tile ht: lane = head col, tokens 16 j + 4 kq + i
+    const unsigned long long vbits = sh.valid[t] >> (4 * kq);
     float zz[16], bm = kNegInf;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -169,8 +169,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tt = t * kMlaTile + 16 * j + 4 * kq + i;
-        zz[4 * j + i] = (tt < ntok && sh.rowoff[tt] >= 0) ? acc[i] * a.sm_scale_log2 : kNegInf;
+        zz[4 * j + i] = ((vbits >> (16 * j + i)) & 1ull) ? acc[i] * a.sm_scale_log2 : kNegInf;
         bm = fmaxf(bm, zz[4 * j + i]);
       }
     }
@@ -180,11 +179,13 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     xor_pair<32>(bm, lo, hi);
     bm = fmaxf(lo, hi);
     const float mn = fmaxf(m, bm);
-    const float alpha = mn == kNegInf ? 1.0f : exp2f(m - mn);
+    // exp2 of values <= 0 with -inf -> 0 (mn = -inf: nothing seen yet, all 0)
+    const float mref = mn == kNegInf ? 0.0f : mn;
+    const float alpha = mn == kNegInf ? 1.0f : exp2_fast(m - mref);
     float p[16], ps = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p[i] = zz[i] == kNegInf ? 0.0f : exp2f(zz[i] - mn);
+      p[i] = exp2_fast(zz[i] - mref);
       ps += p[i];
     }
     ps = xor_pair_sum<16>(ps);
@@ -205,20 +206,18 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     // 2js + 1; lane's k-slice = tokens 4kq + i of each (P as A: row = head col)
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
-      uint32_t h16[8], l16[8], m16[8];
+      // p = hi + lo (+ lo2) in bf16 parts, two tokens per conversion
+      uint32_t hw[4], lw[4], mw[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float r1, r2;
-        h16[i] = mla_bf16_split(p[8 * js + i], &r1);
-        l16[i] = mla_bf16_split(r1, &r2);
-        m16[i] = f32_to_bf16_rne(r2);
+      for (int i = 0; i < 4; ++i) {
+        float x = p[8 * js + 2 * i], y = p[8 * js + 2 * i + 1];
+        bf16x2_split(x, y, &hw[i]);
+        bf16x2_split(x, y, &lw[i]);
+        mw[i] = out32 ? pack_bf16x2(x, y) : 0u;
       }
-      const uint4 ph = make_uint4(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16),
-                                  h16[4] | (h16[5] << 16), h16[6] | (h16[7] << 16));
-      const uint4 pl = make_uint4(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16),
-                                  l16[4] | (l16[5] << 16), l16[6] | (l16[7] << 16));
-      const uint4 pm = make_uint4(m16[0] | (m16[1] << 16), m16[2] | (m16[3] << 16),
-                                  m16[4] | (m16[5] << 16), m16[6] | (m16[7] << 16));
+      const uint4 ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      const uint4 pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      const uint4 pm = make_uint4(mw[0], mw[1], mw[2], mw[3]);
       // V as B operand via transpose reads: this lane addresses row
       // 32 js + 4 kq + (col / 4) (and + 16) at columns 4 (col % 4) of the
       // 16-dim tile, and receives column col of rows 32 js + 4 kq + 0..3 (+ 16)
@@ -236,14 +235,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     }
     __syncthreads();   // the tile and the logit partials are rewritten next
   };
-  uint4 ldA[kMlaChunksPerThread], ldB[kMlaChunksPerThread];
-  uint32_t vmA, vmB;
+  uint4 ldA[kMlaChunksPerThread];
+  uint32_t vmA;
   issue(0, ldA, vmA);
-  issue(1, ldB, vmB);
-  for (int t = 0; t < ntiles; t += 2) {
-    tile_step(t, ldA, vmA);
-    if (t + 1 < ntiles) tile_step(t + 1, ldB, vmB);
-  }
+  for (int t = 0; t < ntiles; ++t) tile_step(t, ldA, vmA);
   // partial state: (m, l) per head, and o, rows = heads 4kq + i of the tile,
   // column = dim 128 sub + 16 n + col: unnormalised fp32 for fp32 output,
   // normalised (o / l, bounded by the largest |v|) bf16 for bf16 output

@@ -16,9 +16,30 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// a and b rounded to bf16 (nearest even) and packed (a in the low half): one
+// gfx950 v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// One step of splitting two floats into bf16 parts: *part = their bf16
+// roundings (packed), and a, b become what is left (a - bf16(a), ...).
+__device__ __forceinline__ void bf16x2_split(float& a, float& b, uint32_t* part) {
+  const uint32_t h = pack_bf16x2(a, b);
+  *part = h;
+  a -= bf16_lo(h);
+  b -= bf16_hi(h);
+}
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // fp32 -> bf16, round to nearest even (NaN -> quiet NaN).
+// 2^x by the hardware exponential (v_exp_f32, about 1 ulp; 2^-inf = 0):
+// softmax weights of arguments <= 0, where the library exp2f's extra range
+// handling is not needed.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
