@@ -37,10 +37,10 @@ struct TopkLds {
   int hist[256];
   float red_f[2][kTopkMaxWaves];
   int red_i[4][kTopkMaxWaves];
-  int bstar, cabove;
-  float list_key[kWave];
+  int bstar, cabove, cstar;   // boundary bucket, candidates above it, candidates in it
+  float list_key[kWave];   // the last (at most 64) undecided candidates, in any order
   int list_idx[kWave];
-  int chosen[kWave];    // final-sort verdict per list position
+  int list_n;
 };
 
 // Monotone bucket of a score between mn and mx (scale = 256 / (mx - mn)).
@@ -112,6 +112,7 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = geo.c1 - geo.c0;
   int need = k < n ? k : n;
+  if (tid == 0) sh.list_n = 0;   // first used after at least one barrier
   float key[PER];
   unsigned long long act = 0, sel = 0;
 #pragma unroll
@@ -126,65 +127,59 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
     need = 0;
   }
   bool robust = false;
+  int known = -1;   // the undecided count, when the last pass's histogram gives it
   for (int it = 0; need > 0; ++it) {
     float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool a = (act >> j) & 1ull;
-      mn = a ? fminf(mn, key[j]) : mn;
-      mx = a ? fmaxf(mx, key[j]) : mx;
-    }
     int cnt;
-    (void)wave_excl_scan_small<7>(__popcll(act), &cnt);
-    mn = wave_min_fast(mn);
-    mx = wave_max_fast(mx);
-    if (lane == 0) { sh.red_i[0][wave] = cnt; sh.red_f[0][wave] = mn; sh.red_f[1][wave] = mx; }
-    __syncthreads();
-    cnt = 0;
+    if (known >= 0 && (known <= need || known <= kWave)) {
+      cnt = known;   // the remainder is filled or sorted: no range needed
+    } else {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      cnt += sh.red_i[0][w];
-      mn = fminf(mn, sh.red_f[0][w]);
-      mx = fmaxf(mx, sh.red_f[1][w]);
+      for (int j = 0; j < PER; ++j) {
+        const bool a = (act >> j) & 1ull;
+        mn = a ? fminf(mn, key[j]) : mn;
+        mx = a ? fmaxf(mx, key[j]) : mx;
+      }
+      (void)wave_excl_scan_small<7>(__popcll(act), &cnt);
+      mn = wave_min_fast(mn);
+      mx = wave_max_fast(mx);
+      if (lane == 0) { sh.red_i[0][wave] = cnt; sh.red_f[0][wave] = mn; sh.red_f[1][wave] = mx; }
+      __syncthreads();
+      cnt = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        cnt += sh.red_i[0][w];
+        mn = fminf(mn, sh.red_f[0][w]);
+        mx = fmaxf(mx, sh.red_f[1][w]);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (cnt <= need) {          // the boundary bucket holds exactly the remainder
       sel |= act;
       act = 0;
       break;
     }
     if (cnt <= kWave) {
-      // the undecided candidates, sorted by one wave; the first `need` win
-      int total;
-      const int pos0 = wg_excl_scan_i<NW>(sh, __popcll(act), 1, &total);
-      int pos = pos0;
+      // the undecided candidates go to a list in any order; each is ranked by
+      // counting the listed ones ahead of it (the order is total, so the list
+      // order does not matter) and the first `need` win
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         if ((act >> j) & 1ull) {
+          const int pos = atomicAdd(&sh.list_n, 1);
           sh.list_key[pos] = key[j];
           sh.list_idx[pos] = tid * PER + j;
-          ++pos;
         }
       }
       __syncthreads();
-      if (tid < cnt) {
-        // rank = number of undecided candidates ahead of this one
-        const float mk = sh.list_key[tid];
-        const int mi = sh.list_idx[tid];
-        int rank = 0;
-#pragma unroll 8
-        for (int u = 0; u < kWave; ++u) {
-          if (u < cnt) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
-        }
-        sh.chosen[tid] = rank < need ? 1 : 0;
-      }
-      __syncthreads();
-      pos = pos0;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         if ((act >> j) & 1ull) {
-          if (sh.chosen[pos]) sel |= 1ull << j;
-          ++pos;
+          const float mk = key[j];
+          const int mi = tid * PER + j;
+          int rank = 0;
+          for (int u = 0; u < cnt; ++u) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
+          if (rank < need) sel |= 1ull << j;
         }
       }
       act = 0;
@@ -220,10 +215,12 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
       if (best == bmax && best >= 0) {
         sh.bstar = best;
         sh.cabove = sbest - hbest;
+        sh.cstar = hbest;
       }
     }
     __syncthreads();
     const int bstar = sh.bstar, cabove = sh.cabove;
+    known = sh.cstar;
     unsigned long long up = 0, keep = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
