@@ -577,6 +577,7 @@ def bench_dense(args) -> int:
     nbytes = {"kv": kv, "q_out_pagetable": B * Hq * D * 2 * 2 + B * (L // P) * 4}
     nbytes["total"] = sum(nbytes.values())
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
+    tr = stored_traffic("attn_chunk_kernel.llama8b_32k_b16_dense")
     res = {"metric": "dense (k = all) split-K decode attention calls/sec at 8B/32K/B16",
            "value": round(1e3 / ms, 2), "unit": "calls/s", "n_gpus": 1, "steps": steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
@@ -588,9 +589,12 @@ def bench_dense(args) -> int:
            "roofline": {"kernel": "ls::attn_chunk_kernel<128> + ls::attn_combine_kernel<128> "
                                   "(one library call)", "bound": "hbm",
                         "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "traffic": tr["traffic_bytes"] if tr else None,
                         "algorithmic_bytes_per_launch": nbytes["total"],
-                        "avg_launch_ms": round(ms, 5)},
+                        "avg_launch_ms": round(ms, 5),
+                        "traffic_source": ("profiles/attn_chunk_kernel.llama8b_32k_b16_dense.md"
+                                           if tr else None)},
            "device": torch.cuda.get_device_name(0)}
     print(json.dumps(res), flush=True)
     return 0
