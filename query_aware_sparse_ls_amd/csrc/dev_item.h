@@ -112,7 +112,7 @@ __device__ __forceinline__ uint4 k_operand(const uint32_t* tile, int j) {
 // after its use; every load is issued -- a row outside the candidates reads
 // page 0 and is discarded -- so the number in flight is fixed). A candidate
 // whose page id is out of range scores 0.
-template <int D, int MAXC>
+template <int D, int MAXC, bool kLds = true>
 __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, const ReqGeom& geo,
                                            const int* pg, float* sc, uint32_t* stage) {
   using ST = Stage<D>;
@@ -146,26 +146,31 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
   };
   // score the staged tile and store the candidate rows (tiles past the
   // wave's range hold page-0 rows and store nothing)
+  // (both aggregations are formed and one is picked: no branch per value;
+  // the LDS form stores the tile's 4 scores as one 16-byte write, scores of
+  // non-candidate rows included -- the top-k reads only [c0, c1), and tile
+  // ends stay below MAXC)
+  static_assert(MAXC % 16 == 0, "whole score tiles");
+  const bool mean = a.group_agg == LS_AGG_MEAN;
   auto finish = [&](const f32x4_t& acc, int k) {
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x = acc[i];
-      if (a.group_agg == LS_AGG_MEAN) {
-        x += dpp_mov<kDppXor1>(x);
-        x += dpp_mov<kDppXor2>(x);
-        x *= 0.25f;
-      } else {
-        x = fmaxf(x, dpp_mov<kDppXor1>(x));
-        x = fmaxf(x, dpp_mov<kDppXor2>(x));
-      }
-      v[i] = x;
+      const float x = acc[i];
+      const float y = dpp_mov<kDppXor1>(x);
+      const float m1 = fmaxf(x, y), s1 = x + y;
+      const float m2 = dpp_mov<kDppXor2>(m1), s2 = dpp_mov<kDppXor2>(s1);
+      v[i] = mean ? (s1 + s2) * 0.25f : fmaxf(m1, m2);
     }
-    if (row == 0) {
+    if (row == 0 && k < ntw) {
       const int tb = (t0 + wave + kItemWaves * k) * 16 + 4 * kq;
+      if constexpr (kLds) {
+        *reinterpret_cast<float4*>(sc + tb) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (tb + i >= geo.c0 && tb + i < geo.c1) sc[tb + i] = v[i];
+        for (int i = 0; i < 4; ++i)
+          if (tb + i >= geo.c0 && tb + i < geo.c1) sc[tb + i] = v[i];
+      }
     }
   };
   uint4 buf[NS][NL];

@@ -13,7 +13,7 @@ namespace ls {
 template <int D, int MAXC>
 __global__ __launch_bounds__(kItemThreads) void select_item_kernel(ScoreArgs sa, TopkArgs ta) {
   __shared__ int pg[MAXC];
-  __shared__ float sc[MAXC];
+  __shared__ __attribute__((aligned(16))) float sc[MAXC];
   __shared__ TopkLds tk;
   __shared__ __attribute__((aligned(16))) uint32_t stage[kItemWaves * 2 * 16 * Stage<D>::kKRowWords];
   const int g = blockIdx.x, r = blockIdx.y;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, T
   __shared__ int sel[MAXC + kItemEntryPad];
   __shared__ union {
     struct {
-      float sc[MAXC];
+      alignas(16) float sc[MAXC];
       TopkLds tk;
       alignas(16) uint32_t stage[kItemWaves * 2 * 16 * Stage<D>::kKRowWords];
     } s;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kItemThreads) void score_part_kernel(ScoreArgs sa, 
   for (int b = geo.c0 + threadIdx.x; b < geo.c1; b += kItemThreads)
     pg[b] = sa.b.indices[geo.page_base + b];
   __syncthreads();
-  item_score<D, MAXC>(sa, r, g, geo, pg, scores + (size_t)item * sa.b.max_blocks, stage);
+  item_score<D, MAXC, false>(sa, r, g, geo, pg, scores + (size_t)item * sa.b.max_blocks, stage);
 }
 
 template <int D, int MAXC>
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kItemThreads) void select_attn_pair_kernel(TopkArgs
   __shared__ int sel[MAXC + kItemEntryPad];
   __shared__ union {
     struct {
-      float sc[MAXC];
+      alignas(16) float sc[MAXC];
       TopkLds tk;
     } s;
     ItemAttnLds<D> at;
