@@ -44,7 +44,10 @@ constexpr int kItemPrefetch = 2;        // K/V blocks in flight per wave
 constexpr int kItemEntryPad = kItemWaves * 2 * kItemPrefetch;
 static_assert(kItemEntryPad >= 7 + kItemWaves * (2 * kItemPrefetch - 2) + 1, "entry padding");
 
-// Q^T as the B operand of the D/32 k-steps of a 16x16x32 MFMA (G = 4 heads).
+// The 4 group queries as a 16x16x32 MFMA operand, one per k-step of D/32:
+// lane i holds head i%16 (zero past the 4 heads), dims 32j + 8(i/16) .. +8.
+// The A and B operands take the same lane layout, so the same registers
+// serve as Q (A: rows = heads) or Q^T (B: columns = heads).
 template <int D>
 struct QOperand {
   uint4 b[D / 32];
@@ -96,8 +99,9 @@ __device__ __forceinline__ void stage_k(uint32_t* tile, const uint4* d, uint32_t
   }
 }
 
-// The MFMA A operand of k-step j from a K-style LDS tile: row i%16, dims
-// [32j + 8(i/16), +8).
+// The MFMA operand of k-step j from a K-style LDS tile: row i%16, dims
+// [32j + 8(i/16), +8) -- the tile as A (rows = tile rows) or as B (columns =
+// tile rows, i.e. the tile transposed).
 template <int D>
 __device__ __forceinline__ uint4 k_operand(const uint32_t* tile, int j) {
   const int lane = threadIdx.x & 63;
@@ -146,31 +150,20 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
   };
   // score the staged tile and store the candidate rows (tiles past the
   // wave's range hold page-0 rows and store nothing)
-  // (both aggregations are formed and one is picked: no branch per value;
-  // the LDS form stores the tile's 4 scores as one 16-byte write, scores of
-  // non-candidate rows included -- the top-k reads only [c0, c1), and tile
-  // ends stay below MAXC)
+  // The logits come out as D[head][token] (A = the queries, B = the tile's
+  // rows as K^T): lanes 0..15 hold heads 0..3 of token `row` in acc[0..3], so
+  // the group aggregation is lane-local and the 16 lanes store the tile's 16
+  // scores with one LDS write. The LDS form stores non-candidate rows too
+  // (the top-k reads only [c0, c1), and tile ends stay below MAXC).
   static_assert(MAXC % 16 == 0, "whole score tiles");
   const bool mean = a.group_agg == LS_AGG_MEAN;
   auto finish = [&](const f32x4_t& acc, int k) {
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = acc[i];
-      const float y = dpp_mov<kDppXor1>(x);
-      const float m1 = fmaxf(x, y), s1 = x + y;
-      const float m2 = dpp_mov<kDppXor2>(m1), s2 = dpp_mov<kDppXor2>(s1);
-      v[i] = mean ? (s1 + s2) * 0.25f : fmaxf(m1, m2);
-    }
-    if (row == 0 && k < ntw) {
-      const int tb = (t0 + wave + kItemWaves * k) * 16 + 4 * kq;
-      if constexpr (kLds) {
-        *reinterpret_cast<float4*>(sc + tb) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tb + i >= geo.c0 && tb + i < geo.c1) sc[tb + i] = v[i];
-      }
+    const float v = mean ? ((acc[0] + acc[1]) + (acc[2] + acc[3])) * 0.25f
+                         : fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+    if (kq == 0 && k < ntw) {
+      const int b = (t0 + wave + kItemWaves * k) * 16 + row;
+      if constexpr (kLds) sc[b] = v;
+      else if (b >= geo.c0 && b < geo.c1) sc[b] = v;
     }
   };
   uint4 buf[NS][NL];
@@ -200,11 +193,10 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
       f32x4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        acc0 = mfma_16x16x32(k_operand<D>(ta, j), qo.b[j], acc0);
-        acc1 = mfma_16x16x32(k_operand<D>(tb, j), qo.b[j], acc1);
+        acc0 = mfma_16x16x32(qo.b[j], k_operand<D>(ta, j), acc0);
+        acc1 = mfma_16x16x32(qo.b[j], k_operand<D>(tb, j), acc1);
       }
-      // acc[i] = q_h . k of tile row 4kq + i, head h = lane%16; aggregate
-      // the group's heads 0..3 (the first quad of each 16-lane row)
+      // acc[i] = q_h . k of tile row `row` for head h = 4kq + i
       finish(acc0, k0 + s);
       finish(acc1, k0 + s + 1);
     }
