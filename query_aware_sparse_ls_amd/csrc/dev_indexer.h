@@ -99,6 +99,13 @@ __device__ __forceinline__ int idx_unit_block(const IndexerArgs& a, const IdxUni
 
 __device__ __forceinline__ uint32_t idx_bin(uint32_t key) { return key >> 20; }
 
+// max(x, 0) as one integer max on the bits: a negative float (sign bit set)
+// is a negative int and becomes +0; anything else is kept (NaN included).
+__device__ __forceinline__ float relu_bits(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
+
 // bf16 pair of fp8 bytes 0,1 (hi = false) or 2,3 (hi = true) of x, exact.
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x, bool hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -11,6 +11,13 @@ namespace ls {
 // Per-mode tile geometry: a tile is 16 units; TOKENS rows are 128 fp8 bytes
 // (16 consecutive tokens of one page: 2 KB contiguous), BLOCKS rows are 256
 // bytes of bf16 (one summary row per block, scattered by the page table).
+//
+// TOKENS tiles go straight from memory into the MFMA B operand: lane
+// (col, kq) loads bytes [16 kq, +16) and [64 + 16 kq, +16) of unit col's row
+// (each instruction reads the 16 rows' first or second halves), and k-step s
+// takes dims 16 kq + 8 s (s < 2) or 64 + 16 kq + 8 (s - 2) (s >= 2). The q
+// operand uses the same dims, which leaves every dot product unchanged.
+// BLOCKS tiles are loaded row-major and transposed through LDS.
 template <int MODE>
 struct IdxTile {
   static constexpr int kRowBytes = MODE == kIdxTokens ? kIdxDim : 2 * kIdxDim;
@@ -20,9 +27,17 @@ struct IdxTile {
   static constexpr int RW = kRowBytes / 4 + 4;               // LDS row stride (words), padded
 };
 
+// Dim of element e (0..7) of k-step s in lane group kq (the q operand's
+// layout; see above).
+template <int MODE>
+__device__ __forceinline__ int idx_kstep_dim(int s, int kq) {
+  if constexpr (MODE == kIdxTokens) return s < 2 ? 16 * kq + 8 * s : 64 + 16 * kq + 8 * (s - 2);
+  else return 32 * kq + 8 * s;
+}
+
 template <int MODE, int NHT>
 struct IdxScoreLds {
-  alignas(16) uint32_t tiles[kIdxWaves][2][16 * IdxTile<MODE>::RW];
+  alignas(16) uint32_t tiles[MODE == kIdxTokens ? 1 : kIdxWaves][2][16 * IdxTile<MODE>::RW];
   uint4 q[NHT][4][kWave];   // the q operand, in lane order (one 16-byte read per lane)
   // page ids of the workgroup's blocks: one per 16+ tokens, one per block
   int pg[MODE == kIdxTokens ? kIdxMaxTilesPerWg + 1 : kIdxMaxTilesPerWg * 16];
@@ -30,9 +45,10 @@ struct IdxScoreLds {
 };
 
 template <int MODE, int NHT>
-__global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a) {
   using T = IdxTile<MODE>;
   constexpr int NL = T::NL, NS = kIdxPrefetch, H = 16 * NHT;
+  static_assert(MODE != kIdxTokens || NL == 2, "token rows: two 16-byte loads per lane");
   __shared__ IdxScoreLds<MODE, NHT> sh;
   const int r = blockIdx.y, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
@@ -83,19 +99,27 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
     for (int i = tid; i < kIdxBins; i += kIdxThreads) sh.hist[i] = 0u;
   }
 
-  // q (A operand: row = head 16ht + col, dims 32kq + 8s .. +8 of k-step s)
-  // and the head weights of this lane's output rows (heads 16ht + 4kq + i)
-  // (kept in LDS: in registers it would cost 16 NHT VGPRs and occupancy)
+  // q (A operand: row = head 16ht + col, dims 32kq + 8s .. +8 of k-step s),
+  // loaded once per workgroup through LDS and then held in registers (read
+  // from LDS per tile it cost 16 KB of LDS reads per wave and tile, which
+  // bounded the loop), and the head weights of this lane's output rows
+  // (heads 16ht + 4kq + i)
   float wv[NHT][4];
   for (int e = tid; e < NHT * 4 * kWave; e += kIdxThreads) {
     const int ht = e / (4 * kWave), s = (e / kWave) % 4, ln = e % kWave;
-    sh.q[ht][s][ln] = ldg16(a.q + ((size_t)r * H + 16 * ht + (ln & 15)) * kIdxDim + 32 * (ln >> 4) + 8 * s);
+    sh.q[ht][s][ln] = ldg16(a.q + ((size_t)r * H + 16 * ht + (ln & 15)) * kIdxDim +
+                            idx_kstep_dim<MODE>(s, ln >> 4));
   }
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)r * H + 16 * ht + 4 * kq + i];
   __syncthreads();
+  uint4 qr[NHT][4];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) qr[ht][s2] = sh.q[ht][s2][lane];
 
   const int ntw = a.tiles_per_wg / kIdxWaves;
   float* srow = a.scores + (size_t)r * a.max_units + u0;
@@ -120,13 +144,23 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
   };
   auto issue = [&](int k, uint4* d, uint32_t& badm, float& sig) {
     badm = 0;
+    if constexpr (MODE == kIdxTokens) {
+      // this lane's own unit (col) of the wave's k-th tile, both halves
+      const int u = u0 + 16 * (wave + kIdxWaves * k) + col;
+      const int page = k < ntw ? sh.pg[(u >> PS) - bi0] : -1;
+      badm = page == -2 ? 0x3u : 0u;
+      const uint8_t* rowp =
+          kbase + ((size_t)(uint32_t)(page >= 0 ? page : 0) * P + (u & (P - 1))) * kIdxDim;
+      d[0] = ldg16_stream(rowp + 16 * kq);
+      d[1] = ldg16_stream(rowp + 64 + 16 * kq);
+    } else {
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      size_t off;
-      const int page = row_page(k, j, &off);
-      badm |= (uint32_t)(page == -2) << j;
-      if constexpr (MODE == kIdxTokens) d[j] = ldg16_stream(kbase + off + 16 * (lane % T::LPR));
-      else d[j] = ldg16(kbase + off + 16 * (lane % T::LPR));
+      for (int j = 0; j < NL; ++j) {
+        size_t off;
+        const int page = row_page(k, j, &off);
+        badm |= (uint32_t)(page == -2) << j;
+        d[j] = ldg16(kbase + off + 16 * (lane % T::LPR));
+      }
     }
     sig = 1.0f;
     if constexpr (MODE == kIdxTokens) {
@@ -160,20 +194,18 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
       issue(k + NS, buf[s], badm[s], sig[s]);
       __builtin_amdgcn_sched_barrier(0);
       if (k < ntw) {
-        uint32_t* tile = sh.tiles[wave][s & 1];
-        // stage row-major (rows with a bad page become zeros)
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          const int row = j * T::RPI + lane / T::LPR;
-          *reinterpret_cast<uint4*>(tile + row * T::RW + 4 * (lane % T::LPR)) =
-              ((bm >> j) & 1u) ? make_uint4(0, 0, 0, 0) : c[j];
-        }
-        wave_lds_sync();
-        // B operand (key^T): unit `col`, dims 32kq + 8s .. +8 of k-step s
+        // B operand (key^T): unit `col`, the dims idx_kstep_dim gives
         uint4 kb[4];
         if constexpr (MODE == kIdxTokens) {
-          const uint4 x0 = *reinterpret_cast<const uint4*>(tile + col * T::RW + 8 * kq);
-          const uint4 x1 = *reinterpret_cast<const uint4*>(tile + col * T::RW + 8 * kq + 4);
+          // a unit with a bad page scores 0 (its bytes are replaced by zeros;
+          // the wave-wide test keeps the common case free of per-lane selects)
+          uint4 x0 = c[0], x1 = c[1];
+          if (__ballot(bm != 0u) != 0) {
+            if (bm) {
+              x0 = make_uint4(0, 0, 0, 0);
+              x1 = make_uint4(0, 0, 0, 0);
+            }
+          }
           const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2)
@@ -182,6 +214,15 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
                                 fp8x2_to_bf16x2(xs[2 * s2 + 1], false),
                                 fp8x2_to_bf16x2(xs[2 * s2 + 1], true));
         } else {
+          uint32_t* tile = sh.tiles[wave][s & 1];
+          // stage row-major (rows with a bad page become zeros)
+#pragma unroll
+          for (int j = 0; j < NL; ++j) {
+            const int row = j * T::RPI + lane / T::LPR;
+            *reinterpret_cast<uint4*>(tile + row * T::RW + 4 * (lane % T::LPR)) =
+                ((bm >> j) & 1u) ? make_uint4(0, 0, 0, 0) : c[j];
+          }
+          wave_lds_sync();
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2)
             kb[s2] = *reinterpret_cast<const uint4*>(tile + col * T::RW + 16 * kq + 4 * s2);
@@ -191,7 +232,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
         for (int ht = 0; ht < NHT; ++ht) {
           acc[ht] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) acc[ht] = mfma_16x16x32(sh.q[ht][s2][lane], kb[s2], acc[ht]);
+          for (int s2 = 0; s2 < 4; ++s2) acc[ht] = mfma_16x16x32(qr[ht][s2], kb[s2], acc[ht]);
         }
         // s = sum_h w_h max(0, sigma * d_h); lane holds heads 16ht + 4kq + i
         float v = 0.0f;
@@ -199,7 +240,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaf(wv[ht][i], fmaxf(acc[ht][i], 0.0f), v);
+            for (int i = 0; i < 4; ++i) v = fmaf(wv[ht][i], relu_bits(acc[ht][i]), v);
           v = xor_pair_sum<16>(v);
           v = xor_pair_sum<32>(v);
           v *= sg;
@@ -207,7 +248,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_kernel(IndexerArgs a) {
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaf(wv[ht][i], fmaxf(acc[ht][i] * sg, 0.0f), v);
+            for (int i = 0; i < 4; ++i) v = fmaf(wv[ht][i], relu_bits(acc[ht][i] * sg), v);
           v = xor_pair_sum<16>(v);
           v = xor_pair_sum<32>(v);
         }
