@@ -96,12 +96,15 @@ __device__ __forceinline__ int tot_minus_prefix(int v, int* total) {
   return *total - pre;
 }
 
+// kPad16: srow holds candidate e at srow[e + e / 16] (one pad word after
+// every 16, so that the thread-owns-PER-consecutive reads of an LDS row hit
+// distinct banks).
 // srow: scores of candidate blocks c0 .. c1-1 (srow[0] is block c0), in
 // global memory or LDS; c1 - c0 <= NT * PER <= kTopkMaxCand. Called by all
 // NT threads of the workgroup. The selection goes to out[0 .. max_selected)
 // (unused entries -1) and its size to *count_out; sel_lds, when given, gets a
 // copy of the first min(total, max_selected) entries. Returns that count.
-template <int PER, int NT = kTopkThreads>
+template <int PER, int NT = kTopkThreads, bool kPad16 = false>
 __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k,
                         int32_t* __restrict__ out, int max_selected,
                         int32_t* __restrict__ count_out, TopkLds& sh,
@@ -118,7 +121,7 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int e = tid * PER + j;
-    key[j] = e < n ? srow[e] : 0.0f;
+    key[j] = e < n ? srow[kPad16 ? e + (e >> 4) : e] : 0.0f;
     act |= (unsigned long long)(e < n) << j;
   }
   if (need >= n) {
@@ -178,7 +181,13 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
           const float mk = key[j];
           const int mi = tid * PER + j;
           int rank = 0;
-          for (int u = 0; u < cnt; ++u) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
+          for (int u0 = 0; u0 < cnt; u0 += 8) {   // 8 list reads in flight
+#pragma unroll
+            for (int uu = 0; uu < 8; ++uu) {
+              const int u = u0 + uu;
+              if (u < cnt) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
+            }
+          }
           if (rank < need) sel |= 1ull << j;
         }
       }

@@ -4,15 +4,34 @@
 
 namespace ls {
 
+// The candidates' scores are first copied into LDS with coalesced loads
+// (consecutive lanes, consecutive scores; one pad word after every 16): the
+// top-k's thread-owns-PER-consecutive-candidates layout read straight from
+// memory would have each lane touch its own line.
 template <int PER, int NT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   __shared__ TopkLds sh;
+  __shared__ float stage[PER * NT + PER * NT / 16];
   const int g = blockIdx.x, r = blockIdx.y;
   const ReqGeom geo = req_geom(a.b, r, a.n_sink, a.n_recent);
   const int item = r * a.num_kv_heads + g;
   const float* srow = a.scores + (size_t)item * a.b.max_blocks + geo.c0;
-  topk_wg<PER, NT>(srow, geo, topk_budget(a, geo), a.selected + (size_t)item * a.max_selected,
-                   a.max_selected, a.selected_count + item, sh);
+  const int n = geo.c1 - geo.c0;
+  float v[PER];   // every load issued before any is stored
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int i = threadIdx.x + m * NT;
+    v[m] = i < n ? srow[i] : 0.0f;
+  }
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int i = threadIdx.x + m * NT;
+    stage[i + (i >> 4)] = v[m];
+  }
+  __syncthreads();
+  topk_wg<PER, NT, true>(stage, geo, topk_budget(a, geo),
+                         a.selected + (size_t)item * a.max_selected, a.max_selected,
+                         a.selected_count + item, sh);
 }
 
 template <int PER, int NT>
