@@ -150,7 +150,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, const ReqGeom& geo
     if (M[h] != kNegInf) {
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
-        const float p = ok[i] ? exp2f(z[i][h] - M[h]) : 0.0f;
+        const float p = ok[i] ? exp2_fast(z[i][h] - M[h]) : 0.0f;
         l[h] += p;
         const uint4 v = vr[i];
         acc[h][0] += p * bf16_lo(v.x); acc[h][1] += p * bf16_hi(v.x);
@@ -231,7 +231,7 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, int item, int la
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float e = exp2f(ms[u] - M);   // 0 for absent / empty splits
+        const float e = exp2_fast(ms[u] - M);   // 0 for absent / empty splits
         Ls += e * ls[u];
 #pragma unroll
         for (int j = 0; j < DPL; ++j) O[j] += e * os[u][j];

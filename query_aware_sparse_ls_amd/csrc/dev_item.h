@@ -118,7 +118,8 @@ __device__ __forceinline__ uint4 k_operand(const uint32_t* tile, int j) {
 // whose page id is out of range scores 0.
 template <int D, int MAXC, bool kLds = true>
 __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, const ReqGeom& geo,
-                                           const int* pg, float* sc, uint32_t* stage) {
+                                           const int* pg, float* sc, uint32_t* stage,
+                                           float* range = nullptr) {
   using ST = Stage<D>;
   constexpr int KS = D / 32, NL = ST::NL, NS = kItemScorePrefetch;
   static_assert(NS % 2 == 0, "slots are consumed in pairs");
@@ -157,13 +158,18 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
   // (the top-k reads only [c0, c1), and tile ends stay below MAXC).
   static_assert(MAXC % 16 == 0, "whole score tiles");
   const bool mean = a.group_agg == LS_AGG_MEAN;
+  // this lane's smallest and largest candidate score (for range[])
+  float smin = __builtin_huge_valf(), smax = -__builtin_huge_valf();
   auto finish = [&](const f32x4_t& acc, int k) {
     const float v = mean ? ((acc[0] + acc[1]) + (acc[2] + acc[3])) * 0.25f
                          : fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     if (kq == 0 && k < ntw) {
       const int b = (t0 + wave + kItemWaves * k) * 16 + row;
+      const bool cand = b >= geo.c0 && b < geo.c1;
       if constexpr (kLds) sc[b] = v;
-      else if (b >= geo.c0 && b < geo.c1) sc[b] = v;
+      else if (cand) sc[b] = v;
+      smin = cand ? fminf(smin, v) : smin;
+      smax = cand ? fmaxf(smax, v) : smax;
     }
   };
   uint4 buf[NS][NL];
@@ -199,6 +205,14 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
       // acc[i] = q_h . k of tile row `row` for head h = 4kq + i
       finish(acc0, k0 + s);
       finish(acc1, k0 + s + 1);
+    }
+  }
+  if (range) {   // range[wave] = the wave's smallest score, range[kItemWaves + wave] its largest
+    smin = wave_min_fast(smin);
+    smax = wave_max_fast(smax);
+    if (lane == 0) {
+      range[wave] = smin;
+      range[kItemWaves + wave] = smax;
     }
   }
 }
@@ -439,7 +453,7 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
     if (M != kNegInf) {
 #pragma unroll
       for (int w = 0; w < kItemWaves; ++w) {
-        const float f = exp2f(sh.m[w][h] - M);   // waves with m = -inf give 0
+        const float f = exp2_fast(sh.m[w][h] - M);   // waves with m = -inf give 0
         O += f * sh.acc[w][h][d];
         Ls += f * sh.l[w][h];
       }
@@ -490,7 +504,7 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
       O = 0.0f;
       Ls = 0.0f;
       if (Mn != kNegInf) {
-        const float f0 = exp2f(M0 - Mn), f1 = exp2f(M1 - Mn);
+        const float f0 = exp2_fast(M0 - Mn), f1 = exp2_fast(M1 - Mn);
         O = f0 * O0 + f1 * O1;
         Ls = f0 * L0 + f1 * L1;
       }

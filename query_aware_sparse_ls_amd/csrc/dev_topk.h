@@ -96,6 +96,9 @@ __device__ __forceinline__ int tot_minus_prefix(int v, int* total) {
   return *total - pre;
 }
 
+// range (optional, LDS): the candidates' smallest scores in range[0 ..
+// range_n) and largest in range[range_n .. 2 range_n), when the producer of
+// the scores found them; the first pass then needs no reduction.
 // kPad16: srow holds candidate e at srow[e + e / 16] (one pad word after
 // every 16, so that the thread-owns-PER-consecutive reads of an LDS row hit
 // distinct banks).
@@ -108,7 +111,8 @@ template <int PER, int NT = kTopkThreads, bool kPad16 = false>
 __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k,
                         int32_t* __restrict__ out, int max_selected,
                         int32_t* __restrict__ count_out, TopkLds& sh,
-                        int32_t* __restrict__ sel_lds = nullptr) {
+                        int32_t* __restrict__ sel_lds = nullptr,
+                        const float* __restrict__ range = nullptr, int range_n = 0) {
   constexpr int NW = NT / kWave;
   static_assert(NT % kWave == 0 && NW <= kTopkMaxWaves && NT >= 256, "workgroup size");
   static_assert(PER >= 1 && PER <= 64 && PER * NT <= kTopkMaxCand, "PER");
@@ -136,6 +140,12 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
     int cnt;
     if (known >= 0 && (known <= need || known <= kWave)) {
       cnt = known;   // the remainder is filled or sorted: no range needed
+    } else if (it == 0 && range && n > kWave) {   // (a barrier precedes any ranking)
+      cnt = n;       // every candidate, over the range the scores' producer found
+      for (int w = 0; w < range_n; ++w) {
+        mn = fminf(mn, range[w]);
+        mx = fmaxf(mx, range[range_n + w]);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {

@@ -15,13 +15,14 @@ __global__ __launch_bounds__(kItemThreads) void select_item_kernel(ScoreArgs sa,
   __shared__ int pg[MAXC];
   __shared__ __attribute__((aligned(16))) float sc[MAXC];
   __shared__ TopkLds tk;
+  __shared__ float range[2 * kItemWaves];
   __shared__ __attribute__((aligned(16))) uint32_t stage[kItemWaves * 2 * 16 * Stage<D>::kKRowWords];
   const int g = blockIdx.x, r = blockIdx.y;
   const int item = r * sa.num_kv_heads + g;
   const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
   load_page_row(sa.b, geo, pg);
   __syncthreads();
-  item_score<D, MAXC>(sa, r, g, geo, pg, sc, stage);
+  item_score<D, MAXC>(sa, r, g, geo, pg, sc, stage, range);
   __syncthreads();
   if (sa.scores) {
     float* out = sa.scores + (size_t)item * sa.b.max_blocks;
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(kItemThreads) void select_item_kernel(ScoreArgs sa,
   }
   (void)topk_wg<MAXC / kItemThreads, kItemThreads>(
       sc + geo.c0, geo, topk_budget(ta, geo), ta.selected + (size_t)item * ta.max_selected,
-      ta.max_selected, ta.selected_count + item, tk);
+      ta.max_selected, ta.selected_count + item, tk, nullptr, range, kItemWaves);
 }
 
 template <int D, int MAXC>
@@ -78,6 +79,7 @@ __global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, T
     struct {
       alignas(16) float sc[MAXC];
       TopkLds tk;
+      float range[2 * kItemWaves];
       alignas(16) uint32_t stage[kItemWaves * 2 * 16 * Stage<D>::kKRowWords];
     } s;
     ItemAttnLds<D> at;
@@ -87,11 +89,11 @@ __global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, T
   const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
   load_page_row(sa.b, geo, pg);
   __syncthreads();
-  item_score<D, MAXC>(sa, r, g, geo, pg, u.s.sc, u.s.stage);
+  item_score<D, MAXC>(sa, r, g, geo, pg, u.s.sc, u.s.stage, u.s.range);
   __syncthreads();
   const int cnt = topk_wg<MAXC / kItemThreads, kItemThreads>(
       u.s.sc + geo.c0, geo, topk_budget(ta, geo), ta.selected + (size_t)item * ta.max_selected,
-      ta.max_selected, ta.selected_count + item, u.s.tk, sel);
+      ta.max_selected, ta.selected_count + item, u.s.tk, sel, u.s.range, kItemWaves);
   item_entries(aa, geo, sel, cnt, pg, item_entry_count(cnt));
   __syncthreads();
   item_attn<D>(aa, r, g, sel, cnt, u.at);

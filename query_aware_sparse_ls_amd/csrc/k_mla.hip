@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int s = s0 + j < S ? s0 + j : S - 1;
-        f[j] = s0 + j < S ? exp2f(ml[2 * s] - M) : 0.0f;   // splits with m = -inf give 0
+        f[j] = s0 + j < S ? exp2_fast(ml[2 * s] - M) : 0.0f;   // splits with m = -inf give 0
         ls[j] = ml[2 * s + 1];
         const size_t oi = ((size_t)row * S + s) * kMlaDv + 4 * t;
         if (out32) vf[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(obase) + oi);
