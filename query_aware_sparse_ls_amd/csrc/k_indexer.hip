@@ -352,6 +352,24 @@ __device__ __forceinline__ int idx_token_of(const IndexerArgs& a, const IdxUnits
   return a.cand_blocks[(size_t)r * a.cand_cap + (u >> PS)] * P + (u & (P - 1));
 }
 
+// dst[i] = src[i] for i < n (n <= NPT * kIdxMarkThreads), every load of a
+// thread issued before its stores (a plain strided loop would wait out one
+// memory round trip per iteration).
+template <int NPT>
+__device__ __forceinline__ void idx_copy_in(uint32_t* dst, const uint32_t* src, int n) {
+  uint32_t v[NPT];
+#pragma unroll
+  for (int m = 0; m < NPT; ++m) {
+    const int i = threadIdx.x + m * kIdxMarkThreads;
+    v[m] = i < n ? src[i] : 0u;
+  }
+#pragma unroll
+  for (int m = 0; m < NPT; ++m) {
+    const int i = threadIdx.x + m * kIdxMarkThreads;
+    if (i < n) dst[i] = v[m];
+  }
+}
+
 // Second digit of a score key: bits [19:8]; third digit: bits [7:0].
 __device__ __forceinline__ uint32_t idx_d2(uint32_t key) { return (key >> 8) & 0xFFFu; }
 
@@ -369,10 +387,8 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
 
   // 1. threshold bucket b* from the request's first-digit histogram
   const uint32_t* gh = a.hist + (size_t)r * kIdxBins;
-  for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) {
-    sh.h[i] = gh[i];
-    sh.h2[i] = 0u;
-  }
+  idx_copy_in<kIdxBins / kIdxMarkThreads>(sh.h, gh, kIdxBins);
+  for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) sh.h2[i] = 0u;
   if (tid == 0) {
     sh.bstar = kIdxBins;   // nothing definite, no candidates
     sh.cabove = 0;
@@ -494,15 +510,19 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
 
   const int kr = sh.kr;
   const int nwr = (g.n + 31) / 32;
-  for (int w = tid; w < nwr; w += kIdxMarkThreads) {
-    sh.bm[w] = bmrow[w];
-    sh.tie[w] = 0u;
-  }
+  idx_copy_in<kIdxMaxWords / kIdxMarkThreads>(sh.bm, bmrow, nwr);
+  for (int w = tid; w < nwr; w += kIdxMarkThreads) sh.tie[w] = 0u;
+  // the candidate blocks (unit -> token map), in LDS when they fit (h2 is
+  // free from here on)
+  const bool cand_lds = g.ncand >= 0 && g.ncand <= kIdxBins;
+  if (cand_lds)
+    idx_copy_in<kIdxBins / kIdxMarkThreads>(
+        sh.h2, reinterpret_cast<const uint32_t*>(a.cand_blocks + (size_t)r * a.cand_cap), g.ncand);
   int ties_to_take = 0;
   if (refine) {
     const int need = kr - sh.cabove;   // >= 1 units of bucket b* to select
     const int nc = (int)ld_dev(ctl);   // units in bucket b*
-    for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) sh.h[i] = gh2[i];
+    idx_copy_in<kIdxBins / kIdxMarkThreads>(sh.h, gh2, kIdxBins);
     __syncthreads();
     idx_find_digit(sh.h, kIdxBins, need, sh.red, &sh.b2, &sh.above2);
     const uint32_t b2 = (uint32_t)sh.b2;
@@ -557,6 +577,7 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   __syncthreads();
 
   // 4. emit in ascending unit order: the bitmap plus the first ties
+  const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);
   const int wpt = (nwr + kIdxMarkThreads - 1) / kIdxMarkThreads;
   const int w0 = tid * wpt, w1 = w0 + wpt < nwr ? w0 + wpt : nwr;
   int tcount = 0;
@@ -587,7 +608,10 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
     while (x) {
       const int b = __ffs(x) - 1;
       x &= x - 1u;
-      if (pos < a.max_selected) out[pos] = idx_token_of(a, g, r, 32 * w + b);
+      if (pos < a.max_selected) {
+        const int u = 32 * w + b;
+        out[pos] = cand_lds ? (int)sh.h2[u >> PS] * P + (u & (P - 1)) : idx_token_of(a, g, r, u);
+      }
       ++pos;
     }
   }
