@@ -64,10 +64,23 @@ __device__ __forceinline__ QOperand<D> load_q_operand(const uint16_t* q, int num
   return o;
 }
 
-// Page ids of blocks [0, nb) of request r into pg[] (LDS); the caller
-// synchronises before use. One coalesced pass over the page-table row.
+// Page ids of blocks [0, nb) of request r into pg[] (LDS; nb <= MAXC); the
+// caller synchronises before use. One coalesced pass over the page-table
+// row, every load of a thread issued before its stores.
+template <int MAXC>
 __device__ __forceinline__ void load_page_row(const BatchArgs& b, const ReqGeom& geo, int* pg) {
-  for (int i = threadIdx.x; i < geo.nb; i += kItemThreads) pg[i] = b.indices[geo.page_base + i];
+  constexpr int NPT = (MAXC + kItemThreads - 1) / kItemThreads;
+  int v[NPT];
+#pragma unroll
+  for (int m = 0; m < NPT; ++m) {
+    const int i = threadIdx.x + m * kItemThreads;
+    v[m] = i < geo.nb ? b.indices[geo.page_base + i] : 0;
+  }
+#pragma unroll
+  for (int m = 0; m < NPT; ++m) {
+    const int i = threadIdx.x + m * kItemThreads;
+    if (i < geo.nb) pg[i] = v[m];
+  }
 }
 
 // Row-major staging of a 16 x D bf16 tile: lane i loads rows j*RPI + i/LPR,

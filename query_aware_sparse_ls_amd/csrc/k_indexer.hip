@@ -105,10 +105,21 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
   // bounded the loop), and the head weights of this lane's output rows
   // (heads 16ht + 4kq + i)
   float wv[NHT][4];
-  for (int e = tid; e < NHT * 4 * kWave; e += kIdxThreads) {
-    const int ht = e / (4 * kWave), s = (e / kWave) % 4, ln = e % kWave;
-    sh.q[ht][s][ln] = ldg16(a.q + ((size_t)r * H + 16 * ht + (ln & 15)) * kIdxDim +
-                            idx_kstep_dim<MODE>(s, ln >> 4));
+  {
+    constexpr int NQ = NHT * 4 * kWave / kIdxThreads;   // every load issued before the stores
+    uint4 qv[NQ];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const int e = tid + m * kIdxThreads;
+      const int ht = e / (4 * kWave), s = (e / kWave) % 4, ln = e % kWave;
+      qv[m] = ldg16(a.q + ((size_t)r * H + 16 * ht + (ln & 15)) * kIdxDim +
+                    idx_kstep_dim<MODE>(s, ln >> 4));
+    }
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const int e = tid + m * kIdxThreads;
+      sh.q[e / (4 * kWave)][(e / kWave) % 4][e % kWave] = qv[m];
+    }
   }
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht)

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kItemThreads) void select_item_kernel(ScoreArgs sa,
   const int g = blockIdx.x, r = blockIdx.y;
   const int item = r * sa.num_kv_heads + g;
   const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
-  load_page_row(sa.b, geo, pg);
+  load_page_row<MAXC>(sa.b, geo, pg);
   __syncthreads();
   item_score<D, MAXC>(sa, r, g, geo, pg, sc, stage, range);
   __syncthreads();
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kItemThreads) void attn_item_kernel(AttnArgs a) {
   const int g = blockIdx.x, r = blockIdx.y;
   const size_t item = (size_t)r * a.num_kv_heads + g;
   const ReqGeom geo = req_geom(a.b, r, 0, 0);
-  load_page_row(a.b, geo, pg);
+  load_page_row<MAXC>(a.b, geo, pg);
   int cnt;
   if (a.selected) {
     // the count and the entries in one hop; entries past the count are unused
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, T
   const int g = blockIdx.x, r = blockIdx.y;
   const int item = r * sa.num_kv_heads + g;
   const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
-  load_page_row(sa.b, geo, pg);
+  load_page_row<MAXC>(sa.b, geo, pg);
   __syncthreads();
   item_score<D, MAXC>(sa, r, g, geo, pg, u.s.sc, u.s.stage, u.s.range);
   __syncthreads();
@@ -146,9 +146,22 @@ __global__ __launch_bounds__(kItemThreads) void select_attn_pair_kernel(TopkArgs
   const int half = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const int item = r * ta.num_kv_heads + g;
   const ReqGeom geo = req_geom(ta.b, r, ta.n_sink, ta.n_recent);
-  load_page_row(ta.b, geo, pg);
+  load_page_row<MAXC>(ta.b, geo, pg);
   const float* srow = ta.scores + (size_t)item * ta.b.max_blocks;
-  for (int b = geo.c0 + threadIdx.x; b < geo.c1; b += kItemThreads) u.s.sc[b] = srow[b];
+  {
+    constexpr int NPT = MAXC / kItemThreads;   // every load issued before the stores
+    float v[NPT];
+#pragma unroll
+    for (int m = 0; m < NPT; ++m) {
+      const int b = geo.c0 + threadIdx.x + m * kItemThreads;
+      v[m] = b < geo.c1 ? srow[b] : 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < NPT; ++m) {
+      const int b = geo.c0 + threadIdx.x + m * kItemThreads;
+      if (b < geo.c1) u.s.sc[b] = v[m];
+    }
+  }
   __syncthreads();
   const int cnt = topk_wg<MAXC / kItemThreads, kItemThreads>(
       u.s.sc + geo.c0, geo, topk_budget(ta, geo), ta.selected + (size_t)item * ta.max_selected,
@@ -173,7 +186,7 @@ __global__ __launch_bounds__(kItemThreads) void attn_pair_kernel(AttnArgs a, flo
   const int half = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const size_t item = (size_t)r * a.num_kv_heads + g;
   const ReqGeom geo = req_geom(a.b, r, 0, 0);
-  load_page_row(a.b, geo, pg);
+  load_page_row<MAXC>(a.b, geo, pg);
   int cnt;
   if (a.selected) {
     cnt = a.selected_count[item];
