@@ -143,6 +143,48 @@ def block_summaries(key_bits: np.ndarray, page_ids: Sequence[int], *,
 
 
 # --------------------------------------------------------------------------
+# Quest bounds: element-wise max and min key of each full page
+# --------------------------------------------------------------------------
+
+def block_bounds(key_bits: np.ndarray, page_ids: Sequence[int]) -> np.ndarray:
+    """Element-wise maximum and minimum key of each listed physical page, per
+    head (Vortex, "Writing an algorithm: vFlow": Quest's cache step keeps the
+    block-wise Max and Min of the keys). key_bits: bf16 bits [num_pages][H][P][D].
+    Returns bf16 bits [n][H][2][D]: row 0 the maximum, row 1 the minimum.
+    Exact: the maximum and minimum of bf16 values are bf16 values."""
+    page_ids = np.asarray(page_ids, dtype=np.int64)
+    k = bf16_to_f64(np.asarray(key_bits)[page_ids])       # [n][H][P][D]
+    hi = k.max(axis=2)
+    lo = k.min(axis=2)
+    return f64_to_bf16_bits(np.stack([hi, lo], axis=2))
+
+
+def bound_scores(q_bits: np.ndarray, bounds: np.ndarray, batch: BatchView, r: int, g: int,
+                 *, num_kv_heads: int, agg: str = "max") -> np.ndarray:
+    """Quest score of request r's complete blocks for kv head g (Vortex,
+    "Writing an algorithm: vFlow", the Quest listing): for each block j and
+    query head h of the group, the element-wise Maximum of q_h * max_j and
+    q_h * min_j, summed over the dims -- the largest value q_h . k can take
+    for a key inside the block's box -- then agg over the group's heads
+    (max, the listing's reduction over heads, or mean). bounds: bf16 bits
+    [num_pages][Hkv][2][D] from block_bounds. Returns float64 [num_complete(r)]."""
+    Hq = q_bits.shape[1]
+    G = Hq // num_kv_heads
+    q = bf16_to_f64(q_bits[r, g * G:(g + 1) * G])                  # [G][D]
+    nc = batch.num_complete(r)
+    pages = batch.pages(r)[:nc]
+    b = bf16_to_f64(np.asarray(bounds)[pages, g])                   # [nc][2][D]
+    hi, lo = b[:, 0], b[:, 1]
+    s = np.maximum(q[None] * hi[:, None], q[None] * lo[:, None])     # [nc][G][D]
+    per_head = s.sum(axis=2)                                         # [nc][G]
+    if agg == "max":
+        return per_head.max(axis=1) if nc else np.zeros(0)
+    if agg == "mean":
+        return per_head.mean(axis=1) if nc else np.zeros(0)
+    raise ValueError(agg)
+
+
+# --------------------------------------------------------------------------
 # Scoring
 # --------------------------------------------------------------------------
 

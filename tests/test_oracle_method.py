@@ -18,7 +18,8 @@ import numpy as np
 import pytest
 
 from oracle.method import (
-    BatchView, attention_over_tokens, block_scores, block_summaries, coarse_to_fine_select,
+    BatchView, attention_over_tokens, block_bounds, block_scores, block_summaries,
+    bound_scores, coarse_to_fine_select,
     decode_step,
     dense_attention, forced_blocks, indexer_block_scores, indexer_token_scores, lse_merge,
     mla_attention, select_blocks, select_tokens, sparse_attention, tokens_of_blocks,
@@ -190,6 +191,88 @@ def test_block_scores_vs_exact_rationals():
                             for h in (2 * g, 2 * g + 1)]
                     want = max(dots) if agg == "max" else sum(dots) / 2
                     assert abs(Fraction(float(s[j])) - want) <= abs(want) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 300)
+
+
+# ------------------------------------------------------------ Quest bounds
+
+def test_quest_worked_example():
+    # one head, one 2-token block: k1 = (3, 1), k2 = (-1, 4) -> max (3, 4),
+    # min (-1, 1); q = (1, -2): max(1*3, 1*-1) + max(-2*4, -2*1) = 3 - 2 = 1,
+    # while the tokens' own dot products are 1 and -9
+    keys = f64_to_bf16_bits(np.array([[[[3.0, 1.0], [-1.0, 4.0]]]]))       # [1][1][2][2]
+    b = block_bounds(keys, [0])
+    assert b.shape == (1, 1, 2, 2)
+    assert bf16_to_f64(b[0, 0, 0]).tolist() == [3.0, 4.0]
+    assert bf16_to_f64(b[0, 0, 1]).tolist() == [-1.0, 1.0]
+    q = f64_to_bf16_bits(np.array([[[1.0, -2.0]]]))
+    batch = BatchView([0, 1], [0], [2], 2)
+    s = bound_scores(q, b, batch, 0, 0, num_kv_heads=1)
+    assert s.tolist() == [1.0]
+
+
+def test_quest_score_is_the_max_over_the_box_corners():
+    # the largest q . x over the box [min, max] sits at a corner: enumerate
+    # all 2^D corners with exact rationals
+    rng = np.random.default_rng(31)
+    D, P = 6, 4
+    keys = _rand_bf16(rng, (3, 1, P, D))
+    b = block_bounds(keys, [0, 1, 2])
+    q = _rand_bf16(rng, (1, 1, D))
+    batch = BatchView([0, 3], [0, 1, 2], [3 * P], P)
+    s = bound_scores(q, b, batch, 0, 0, num_kv_heads=1)
+    qf = [Fraction(float(x)) for x in bf16_to_f64(q[0, 0])]
+    for j in range(3):
+        hi = [Fraction(float(x)) for x in bf16_to_f64(b[j, 0, 0])]
+        lo = [Fraction(float(x)) for x in bf16_to_f64(b[j, 0, 1])]
+        best = max(sum(qf[d] * (hi[d] if (c >> d) & 1 else lo[d]) for d in range(D))
+                   for c in range(2 ** D))
+        assert Fraction(float(s[j])) == best          # few exact products: no rounding
+
+
+def test_quest_bounds_and_scores_bound_every_token():
+    rng = np.random.default_rng(32)
+    batch, npg = _tiny_batch(rng)
+    keys = _rand_bf16(rng, (npg, 2, 4, 8))
+    q = _rand_bf16(rng, (2, 4, 8))
+    b = block_bounds(keys, range(npg))
+    for p in range(npg):
+        for h in range(2):
+            for d in range(8):
+                col = [Fraction(float(x)) for x in bf16_to_f64(keys[p, h, :, d])]
+                assert Fraction(float(bf16_to_f64(b[p, h, 0, d]))) == max(col)
+                assert Fraction(float(bf16_to_f64(b[p, h, 1, d]))) == min(col)
+    for r in range(2):
+        for g in range(2):
+            # head 2g + i alone: both of the group's slots hold it
+            per_head = []
+            for i in range(2):
+                qq = q.copy()
+                qq[:, 2 * g] = qq[:, 2 * g + 1] = q[:, 2 * g + i]
+                per_head.append(bound_scores(qq, b, batch, r, g, num_kv_heads=2))
+            s = bound_scores(q, b, batch, r, g, num_kv_heads=2, agg="max")
+            assert np.array_equal(s, np.maximum(per_head[0], per_head[1]))
+            for j in range(batch.num_complete(r)):
+                p = batch.pages(r)[j]
+                for i in range(2):
+                    qh = [Fraction(float(x)) for x in bf16_to_f64(q[r, 2 * g + i])]
+                    for t in range(4):
+                        kt = [Fraction(float(x)) for x in bf16_to_f64(keys[p, g, t])]
+                        dot = sum(a * c for a, c in zip(qh, kt))
+                        assert dot <= Fraction(float(per_head[i][j])) * (1 + Fraction(1, 10 ** 12)) + Fraction(1, 10 ** 300)
+
+
+def test_quest_block_of_equal_tokens_scores_its_dot_product():
+    rng = np.random.default_rng(33)
+    tok = _rand_bf16(rng, (8,))
+    keys = np.broadcast_to(tok, (1, 1, 4, 8)).copy()
+    b = block_bounds(keys, [0])
+    assert np.array_equal(b[0, 0, 0], tok) and np.array_equal(b[0, 0, 1], tok)
+    q = _rand_bf16(rng, (1, 1, 8))
+    batch = BatchView([0, 1], [0], [4], 4)
+    s = bound_scores(q, b, batch, 0, 0, num_kv_heads=1)
+    want = sum(Fraction(float(a)) * Fraction(float(c))
+               for a, c in zip(bf16_to_f64(q[0, 0]), bf16_to_f64(tok)))
+    assert abs(Fraction(float(s[0])) - want) <= abs(want) * Fraction(1, 10 ** 14)
 
 
 def test_max_and_mean_agree_for_one_head_per_group():
