@@ -42,23 +42,24 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 
 
-def step_bytes(B, Hq, Hkv, D, P, nb, n_sel, n_cand, n_new_pages, out_bytes=2):
+def step_bytes(B, Hq, Hkv, D, P, nb, n_sel, n_cand, n_new_pages, out_bytes=2, rows=1):
     """Algorithmic bytes of one step: what the method itself must move.
 
-    Per (request, kv head): the candidate summaries scanned (n_cand rows of
-    D bf16) and the selected blocks' K and V (n_sel * P tokens * D * 2 B * 2).
+    Per (request, kv head): the candidate summaries scanned (n_cand * rows
+    rows of D bf16: rows = 1 for block means, 2 for Quest bounds) and the
+    selected blocks' K and V (n_sel * P tokens * D * 2 B * 2).
     Per request: q (Hq * D bf16), output (Hq * D), page table (nb int32).
     Summary update: the new pages' keys read (Hkv * P * D bf16) and their
-    summaries written (Hkv * D bf16)."""
-    summ = B * Hkv * n_cand * D * 2
+    summaries written (Hkv * rows * D bf16)."""
+    summ = B * Hkv * n_cand * rows * D * 2
     kv = B * Hkv * n_sel * P * D * 2 * 2
     misc = B * Hq * D * 2 + B * Hq * D * out_bytes + B * nb * 4
-    upd = n_new_pages * Hkv * (P * D * 2 + D * 2)
+    upd = n_new_pages * Hkv * (P * D * 2 + rows * D * 2)
     return {"summaries": summ, "selected_kv": kv, "q_out_pagetable": misc, "summary_update": upd,
             "total": summ + kv + misc + upd}
 
 
-def make_replica(cfg, seed, device):
+def make_replica(cfg, seed, device, score_mode="mean"):
     import torch
     import query_aware_sparse_ls_amd as ls
     from workloads import make_block_topk_inputs
@@ -74,10 +75,14 @@ def make_replica(cfg, seed, device):
     # the pages that filled at this step: the last page of requests whose
     # length is a multiple of the page size
     new = [int(idx[indptr[r] + lens[r] // P - 1]) for r in range(B) if lens[r] % P == 0]
-    summ = torch.zeros(inp.num_pages, Hkv, D, dtype=torch.bfloat16, device=device)
-    ls.build_block_summaries(inp.k_pool, full.to(torch.int32).to(device), summ)
+    if score_mode == "bounds":
+        summ = torch.zeros(inp.num_pages, Hkv, 2, D, dtype=torch.bfloat16, device=device)
+        ls.build_block_bounds(inp.k_pool, full.to(torch.int32).to(device), summ)
+    else:
+        summ = torch.zeros(inp.num_pages, Hkv, D, dtype=torch.bfloat16, device=device)
+        ls.build_block_summaries(inp.k_pool, full.to(torch.int32).to(device), summ)
     maxsel = min(batch.max_blocks, inp.topk + cfg.n_sink + cfg.n_recent + 1)
-    rep = dict(inp=inp, batch=batch, summ=summ,
+    rep = dict(inp=inp, batch=batch, summ=summ, mode=score_mode,
                ws_step=ls.sparse_decode_step_workspace(B, Hq, Hkv, D, batch.max_blocks,
                                                        maxsel, device),
                new_pages=torch.tensor(new, dtype=torch.int32, device=device),
@@ -93,9 +98,12 @@ def make_replica(cfg, seed, device):
 
 
 def call_update(rep):
-    """Summaries of the pages that filled at this step."""
+    """Summaries (or bounds) of the pages that filled at this step."""
     import query_aware_sparse_ls_amd as ls
-    ls.build_block_summaries(rep["inp"].k_pool, rep["new_pages"], rep["summ"])
+    if rep["mode"] == "bounds":
+        ls.build_block_bounds(rep["inp"].k_pool, rep["new_pages"], rep["summ"])
+    else:
+        ls.build_block_summaries(rep["inp"].k_pool, rep["new_pages"], rep["summ"])
 
 
 def call_first(rep, cfg, sm_scale, fused):
@@ -108,12 +116,13 @@ def call_first(rep, cfg, sm_scale, fused):
                               max_selected=rep["maxsel"], sm_scale=sm_scale,
                               group_agg=cfg.group_agg, selected=rep["sel"],
                               selected_count=rep["cnt"], out=rep["out"],
-                              new_pages=rep["new_pages"], workspace=rep["ws_step"])
+                              new_pages=rep["new_pages"], workspace=rep["ws_step"],
+                              score_mode=rep["mode"])
     else:
         ls.score_select(inp.q, rep["summ"], cfg.page_size, rep["batch"], topk=inp.topk,
                         n_sink=cfg.n_sink, n_recent=cfg.n_recent, max_selected=rep["maxsel"],
                         group_agg=cfg.group_agg, selected=rep["sel"], selected_count=rep["cnt"],
-                        workspace=rep["ws_sel"])
+                        workspace=rep["ws_sel"], score_mode=rep["mode"])
 
 
 def call_second(rep, sm_scale):
@@ -185,6 +194,8 @@ def cpu_baseline(rep, cfg, sm_scale, budget_s: float):
     from workloads import bf16_bits
     inp = rep["inp"]
     P, Hkv = cfg.page_size, cfg.num_kv_heads
+    bounds = rep["mode"] == "bounds"
+    build = oracle.block_bounds if bounds else oracle.block_summaries
     prepared = {}
 
     def prepare(r):
@@ -197,8 +208,8 @@ def cpu_baseline(rep, cfg, sm_scale, budget_s: float):
         q = bf16_bits(inp.q[r:r + 1].contiguous())
         bv = oracle.BatchView(np.array([0, nb]), np.arange(nb), np.array([L]), P)
         nc = L // P
-        summ = np.zeros((nb, Hkv, cfg.head_dim), dtype=np.uint16)
-        summ[:nc] = oracle.block_summaries(k, np.arange(nc))      # setup: not timed
+        summ = np.zeros((nb, Hkv) + ((2,) if bounds else ()) + (cfg.head_dim,), dtype=np.uint16)
+        summ[:nc] = build(k, np.arange(nc))                        # setup: not timed
         return L, nc, k, v, q, bv, summ
 
     times = []
@@ -211,15 +222,17 @@ def cpu_baseline(rep, cfg, sm_scale, budget_s: float):
             t0 = time.perf_counter()
             new = [nc - 1] if L % P == 0 and nc > 0 else []
             if new:
-                summ[new] = oracle.block_summaries(k, new)
+                summ[new] = build(k, new)
             oracle.decode_step(q, k, v, bv, num_kv_heads=Hkv, topk=inp.topk, n_sink=cfg.n_sink,
                                n_recent=cfg.n_recent, sm_scale=np.float32(sm_scale),
-                               agg=cfg.group_agg, out_dtype="bf16", summaries=summ)
+                               agg=cfg.group_agg, out_dtype="bf16", summaries=summ,
+                               score_mode=rep["mode"])
             times.append(time.perf_counter() - t0)
     per_call = sum(times) / len(times) * cfg.batch
     return {"value": 1.0 / per_call, "unit": "calls/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(times)} request-steps ({len(times) / cfg.batch:.1f} calls' worth; "
-                      f"each: new-page summary, scores, top-k selection and attention for all "
+                      f"each: new-page {'bounds' if bounds else 'summary'}, "
+                      f"{'Quest bound ' if bounds else ''}scores, top-k selection and attention for all "
                       f"{Hkv} kv heads of one request), float64 NumPy on one thread, "
                       f"{sum(times):.1f} s; mean per request x {cfg.batch} requests = one call",
             "seconds_per_call": per_call}
@@ -620,6 +633,8 @@ def main(argv=None) -> int:
               "copy-fetch-cmd", "copy-write-cmd"):
         ap.add_argument("--" + a, default="")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
+                    help="block-topk path: block-mean summaries (default) or Quest bounds")
     ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense"),
                     default="block-topk",
                     help="block-topk: the 8B/32K/B16 block top-k step (default); indexer: "
@@ -649,7 +664,7 @@ def main(argv=None) -> int:
     sm_scale = 1.0 / math.sqrt(cfg.head_dim)
     fused = not args.separate
     R = max(1, args.replicas)
-    reps = [make_replica(cfg, cfg.seed + i, dev) for i in range(R)]
+    reps = [make_replica(cfg, cfg.seed + i, dev, args.score) for i in range(R)]
     torch.cuda.synchronize()
     print(f"# {R} replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB",
           file=sys.stderr, flush=True)
@@ -660,7 +675,9 @@ def main(argv=None) -> int:
     n_forced = cfg.n_sink + cfg.n_recent
     n_sel = inp0.topk + n_forced
     n_cand = nb - n_forced
-    nbytes = step_bytes(B, Hq, Hkv, D, P, nb, n_sel, n_cand, int(reps[0]["new_pages"].numel()))
+    quest = args.score == "bounds"
+    nbytes = step_bytes(B, Hq, Hkv, D, P, nb, n_sel, n_cand, int(reps[0]["new_pages"].numel()),
+                        rows=2 if quest else 1)
     main_stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
 
@@ -715,11 +732,13 @@ def main(argv=None) -> int:
         # one (request, kv head) pair per workgroup plus the summary-refresh
         # workgroups: the whole call is one launch
         dom_ms, dom_bytes = first, fused_bytes
-        dom_key, dom_match = "step_item_kernel.llama8b_32k_b16", "ls::step_item_kernel<128, 2048>"
+        dom_key = "step_item_kernel.llama8b_32k_b16" + ("_quest" if quest else "")
+        dom_match = f"ls::step_item_kernel<128, 2048, {'true' if quest else 'false'}>"
     else:
         dom_ms = second
         dom_bytes = nbytes["selected_kv"] + B * Hq * D * 2 + sel_bytes + B * nb * 4
-        dom_key, dom_match = "attn_item_kernel.llama8b_32k_b16", "ls::attn_item_kernel<128, 2048>"
+        dom_key = "attn_item_kernel.llama8b_32k_b16" + ("_quest" if quest else "")
+        dom_match = "ls::attn_item_kernel<128, 2048>"
     dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
     tr = stored_traffic(dom_key)
 
@@ -728,10 +747,12 @@ def main(argv=None) -> int:
         "value": round(calls_per_s, 1), "unit": "calls/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": B, "context": cfg.context, "q_heads": Hq,
+        "config": {"workload": cfg.name + (" quest bounds" if quest else ""), "batch": B,
+                   "context": cfg.context, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "page_size": P, "topk": inp0.topk,
                    "n_sink": cfg.n_sink, "n_recent": cfg.n_recent, "replicas": R,
                    "path": "fused" if fused else "separate",
+                   "block_scores": "quest bounds" if quest else "block-mean keys",
                    "timing": "hip graph" if graph is not None else "eager"},
         "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
         "achieved_GBps_step": round(gbps, 1),

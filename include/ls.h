@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 2
+#define LS_ABI_VERSION 3
 
 typedef enum ls_status {
   LS_OK = 0,
@@ -79,6 +79,9 @@ typedef enum ls_dtype {
 
 /* GQA aggregation of the per-head block scores of one KV group. */
 enum { LS_AGG_MAX = 0, LS_AGG_MEAN = 1 };
+
+/* Block scores (ls_select_params.score_mode). */
+enum { LS_SCORE_MEAN = 0, LS_SCORE_BOUNDS = 1 };
 
 /* Geometry of a paged pool (K, V or summaries). */
 typedef struct ls_pool {
@@ -111,6 +114,11 @@ typedef struct ls_select_params {
   int32_t n_sink;        /* forced: blocks 0 .. n_sink-1                      */
   int32_t n_recent;      /* forced: the last n_recent blocks                  */
   int32_t max_selected;  /* row capacity of `selected` (see ls_score_select)  */
+  int32_t score_mode;    /* LS_SCORE_MEAN: summaries are block-mean keys      */
+                         /*   [num_pages][num_heads][head_dim];               */
+                         /* LS_SCORE_BOUNDS: summaries are Quest bounds from  */
+                         /*   ls_build_block_bounds,                          */
+                         /*   [num_pages][num_heads][2][head_dim]             */
 } ls_select_params;
 
 /* ------------------------------------------------------------------------ */
@@ -142,6 +150,24 @@ ls_status ls_build_block_summaries(const void* keys, const float* key_scales,
                                    int32_t n_pages, void* summaries,
                                    int32_t summary_dtype, hipStream_t stream);
 
+/*
+ * Quest bounds (Vortex post, "Writing an algorithm: vFlow", the Quest
+ * listing: its cache step keeps the element-wise maximum and minimum key of
+ * each block):
+ *   bounds[p][h][0][d] = max_s keys[p][h][s][d],
+ *   bounds[p][h][1][d] = min_s keys[p][h][s][d]
+ * for every listed page p and head h. Exact (a copy of bf16 values). Keys
+ * are taken to be finite.
+ *
+ * keys:     bf16 key pool, layout HND; key_pool.dtype = LS_DTYPE_BF16,
+ *           page_size in {16, 32, 64}, head_dim in {64, 128}.
+ * page_ids: [n_pages] physical page ids (complete pages); n_pages >= 0.
+ * bounds:   bf16 [key_pool.num_pages][key_pool.num_heads][2][head_dim];
+ *           only the rows of the listed pages are written.
+ */
+ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_t* page_ids,
+                                int32_t n_pages, void* bounds, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* 2. Scoring and selection                                                  */
 /* ------------------------------------------------------------------------ */
@@ -152,8 +178,14 @@ ls_status ls_build_block_summaries(const void* keys, const float* key_scales,
  *   forced F = {0 .. min(n_sink,nb)-1} U {max(0,nb-n_recent) .. nb-1}
  *              U {nb-1 if the last block is partial},
  *   candidates C = {j < nc} \ F,
- *   score s_j = agg_{h in group g} sum_d q[r][h][d] * summaries[page(r,j)][g][d]
- *              (fp32 accumulation of exact bf16 products; unscaled),
+ *   score s_j = agg_{h in group g} u_h(j), unscaled, fp32 accumulation of
+ *              exact bf16 products, with
+ *     LS_SCORE_MEAN:   u_h(j) = sum_d q[r][h][d] * summaries[page(r,j)][g][d]
+ *                      (Vortex post, block top-k equation),
+ *     LS_SCORE_BOUNDS: u_h(j) = sum_d max(q[r][h][d] * bounds[page][g][0][d],
+ *                                         q[r][h][d] * bounds[page][g][1][d])
+ *                      (Vortex post, the Quest listing: an upper bound of
+ *                      q . k over the block's keys),
  *   k_r = topk, or from keep_ratio when topk == -1,
  *   top = the first min(k_r, |C|) candidates ordered by (s_j descending,
  *         j ascending) -- ties go to the LOWEST block index,
@@ -176,7 +208,8 @@ ls_status ls_build_block_summaries(const void* keys, const float* key_scales,
  * workspace:      device scratch of at least ls_score_select_workspace_size()
  *                 bytes, 256-byte aligned; contents need not be initialised.
  * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
- *            page_size 16; max_blocks <= 16384.
+ *            page_size 16; max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192,
+ *            num_pages < 2^26).
  */
 size_t ls_score_select_workspace_size(int32_t batch_size, int32_t num_kv_heads,
                                       int32_t max_blocks);
@@ -257,7 +290,8 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
  * K/V pool's num_pages, num_heads and head_dim.
  * new_page_ids, n_new_pages: optional (NULL, 0) device list of physical
  *   pages that filled at this step; the call also (re)builds their bf16
- *   summaries, exactly as ls_build_block_summaries would (summaries are
+ *   summaries, exactly as ls_build_block_summaries would (as
+ *   ls_build_block_bounds would with p->score_mode = LS_SCORE_BOUNDS; summaries are
  *   built when a block fills up -- Vortex post, "Why Long Generations Are
  *   Expensive"). On the one-launch path this runs in extra workgroups of the
  *   same launch, concurrently with the pairs, so it is only valid if no
@@ -269,7 +303,10 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
  *   aligned, need not be initialised (block scores and split partials of the
  *   split path; calls that run concurrently need separate workspaces).
  * Supported: head_dim 64 or 128; GQA group 4; page_size 16;
- *   max_blocks <= 16384.
+ *   max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192 and num_pages < 2^26;
+ *   bounds of requests of more than 4096 blocks in batches of at most 256
+ *   (request, kv head) pairs take three launches: bounds refresh,
+ *   selection, attention).
  */
 size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_heads,
                                             int32_t num_kv_heads, int32_t head_dim,

@@ -387,12 +387,19 @@ def mla_attention(q_bits: np.ndarray, latent_bits: np.ndarray, batch: BatchView,
 
 def select_blocks_batch(q_bits, summaries, batch: BatchView, pairs, *, num_kv_heads: int,
                         topk: int, n_sink: int, n_recent: int, agg: str = "max",
-                        summary_format: str = "bf16") -> Dict:
-    """Scores and selections for the (r, g) pairs listed."""
+                        summary_format: str = "bf16", score_mode: str = "mean") -> Dict:
+    """Scores and selections for the (r, g) pairs listed. score_mode "mean":
+    summaries are block-mean keys (block_scores); "bounds": Quest bounds
+    [num_pages][Hkv][2][D] (bound_scores)."""
     res = {}
     for r, g in pairs:
-        s = block_scores(q_bits, summaries, batch, r, g, num_kv_heads=num_kv_heads,
-                         agg=agg, summary_format=summary_format)
+        if score_mode == "bounds":
+            s = bound_scores(q_bits, summaries, batch, r, g, num_kv_heads=num_kv_heads, agg=agg)
+        elif score_mode == "mean":
+            s = block_scores(q_bits, summaries, batch, r, g, num_kv_heads=num_kv_heads,
+                             agg=agg, summary_format=summary_format)
+        else:
+            raise ValueError(score_mode)
         sel = select_blocks(s, batch.num_blocks(r), batch.num_complete(r), topk,
                             n_sink, n_recent)
         res[(r, g)] = (s, sel)
@@ -401,20 +408,25 @@ def select_blocks_batch(q_bits, summaries, batch: BatchView, pairs, *, num_kv_he
 
 def decode_step(q_bits, k_bits, v_bits, batch: BatchView, *, num_kv_heads: int, topk: int,
                 n_sink: int, n_recent: int, sm_scale: float, agg: str = "max",
-                out_dtype: str = "bf16", pairs=None, summaries=None) -> Dict:
-    """Summaries of the requests' complete pages (unless given), block scores,
-    selection and attention for each (r, g) in `pairs` (default: all)."""
+                out_dtype: str = "bf16", pairs=None, summaries=None,
+                score_mode: str = "mean") -> Dict:
+    """Summaries of the requests' complete pages (unless given: block means,
+    or Quest bounds when score_mode is "bounds"), block scores, selection and
+    attention for each (r, g) in `pairs` (default: all)."""
     if pairs is None:
         pairs = [(r, g) for r in range(batch.batch) for g in range(num_kv_heads)]
     if summaries is None:
         pages = sorted({int(p) for r in {r for r, _ in pairs}
                         for p in batch.pages(r)[:batch.num_complete(r)]})
-        summaries = np.zeros((np.asarray(k_bits).shape[0],) + np.asarray(k_bits).shape[1:2]
-                             + np.asarray(k_bits).shape[3:], dtype=np.uint16)
+        kb = np.asarray(k_bits)
+        rows = (2,) if score_mode == "bounds" else ()
+        summaries = np.zeros((kb.shape[0], kb.shape[1]) + rows + (kb.shape[3],), dtype=np.uint16)
         if pages:
-            summaries[pages] = block_summaries(k_bits, pages)
+            build = block_bounds if score_mode == "bounds" else block_summaries
+            summaries[pages] = build(k_bits, pages)
     sel = select_blocks_batch(q_bits, summaries, batch, pairs, num_kv_heads=num_kv_heads,
-                              topk=topk, n_sink=n_sink, n_recent=n_recent, agg=agg)
+                              topk=topk, n_sink=n_sink, n_recent=n_recent, agg=agg,
+                              score_mode=score_mode)
     out = {}
     for (r, g), (s, blocks) in sel.items():
         o, lse = sparse_attention(q_bits, k_bits, v_bits, batch, r, g, blocks,

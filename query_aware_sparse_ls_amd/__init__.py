@@ -16,12 +16,13 @@ import torch
 
 from . import _lib
 from ._lib import (LS_AGG_MAX, LS_AGG_MEAN, LS_DTYPE_BF16, LS_DTYPE_FP32,  # noqa: F401
-                   LS_DTYPE_FP8_E4M3FN, LS_SEL_BLOCKS, LS_SEL_TOKENS, LsBatch, LsError,
+                   LS_DTYPE_FP8_E4M3FN, LS_SCORE_BOUNDS, LS_SCORE_MEAN, LS_SEL_BLOCKS,
+                   LS_SEL_TOKENS, LsBatch, LsError,
                    LsIndexerParams, LsPool, LsSelectParams, check)
 
 _L = _lib.load()
 
-__all__ = ["PagedBatch", "build_block_summaries", "score_select", "sparse_attn_decode",
+__all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_select", "sparse_attn_decode",
            "score_select_workspace_size", "sparse_attn_decode_workspace_size",
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
            "sparse_decode_step_workspace", "indexer_select", "indexer_select_workspace_size",
@@ -107,6 +108,36 @@ def build_block_summaries(keys: torch.Tensor, page_ids: torch.Tensor, summaries:
     return summaries
 
 
+def build_block_bounds(keys: torch.Tensor, page_ids: torch.Tensor, bounds: torch.Tensor,
+                       stream=None) -> torch.Tensor:
+    """Quest bounds of every listed page: the element-wise maximum and
+    minimum key over the page's tokens, per head.
+
+    keys: bf16 [pages][Hkv][P][D]; bounds: bf16 [pages][Hkv][2][D] (maximum
+    row, then minimum row); rows of the listed pages are overwritten."""
+    _need(keys, torch.bfloat16); _need(page_ids, torch.int32); _need(bounds, torch.bfloat16)
+    n, H, P, D = keys.shape
+    if tuple(bounds.shape) != (n, H, 2, D):
+        raise ValueError(f"bounds must be [{n}][{H}][2][{D}], got {tuple(bounds.shape)}")
+    check(_L.ls_build_block_bounds(keys.data_ptr(), _pool(keys, H, P, D), page_ids.data_ptr(),
+                                   int(page_ids.numel()), bounds.data_ptr(), _stream(stream)))
+    return bounds
+
+
+def _score_mode(mode: str, summaries: torch.Tensor, head_dim: int) -> int:
+    """LS_SCORE_MEAN for block-mean summaries [pages][Hkv][D], LS_SCORE_BOUNDS
+    for Quest bounds [pages][Hkv][2][D]."""
+    if mode == "mean":
+        if summaries.dim() != 3 or summaries.shape[2] != head_dim:
+            raise ValueError("block-mean summaries must be [pages][Hkv][D]")
+        return LS_SCORE_MEAN
+    if mode == "bounds":
+        if summaries.dim() != 4 or summaries.shape[2] != 2 or summaries.shape[3] != head_dim:
+            raise ValueError("Quest bounds must be [pages][Hkv][2][D]")
+        return LS_SCORE_BOUNDS
+    raise ValueError(f"score_mode {mode!r} (expected 'mean' or 'bounds')")
+
+
 # ------------------------------------------------------------------ selection
 
 def score_select_workspace_size(batch_size: int, num_kv_heads: int, max_blocks: int) -> int:
@@ -115,7 +146,7 @@ def score_select_workspace_size(batch_size: int, num_kv_heads: int, max_blocks: 
 
 def score_select(q: torch.Tensor, summaries: torch.Tensor, page_size: int, batch: PagedBatch, *,
                  topk: int, n_sink: int, n_recent: int, max_selected: int,
-                 group_agg: str = "max", keep_ratio: float = 0.0,
+                 group_agg: str = "max", keep_ratio: float = 0.0, score_mode: str = "mean",
                  selected: Optional[torch.Tensor] = None,
                  selected_count: Optional[torch.Tensor] = None,
                  scores_out: Optional[torch.Tensor] = None,
@@ -139,7 +170,7 @@ def score_select(q: torch.Tensor, summaries: torch.Tensor, page_size: int, batch
     params = LsSelectParams(C.sizeof(LsSelectParams),
                             LS_AGG_MAX if group_agg == "max" else LS_AGG_MEAN,
                             int(topk), float(keep_ratio), int(n_sink), int(n_recent),
-                            int(max_selected))
+                            int(max_selected), _score_mode(score_mode, summaries, D))
     pool = LsPool(int(summaries.shape[0]), int(Hkv), int(page_size), int(D), LS_DTYPE_BF16)
     check(_L.ls_score_select(q.data_ptr(), LS_DTYPE_BF16, int(Hq), summaries.data_ptr(), pool,
                              batch.c(), C.byref(params), selected.data_ptr(),
@@ -208,7 +239,7 @@ def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.T
                        v_pool: torch.Tensor, batch: PagedBatch, *, topk: int, n_sink: int,
                        n_recent: int, max_selected: int, sm_scale: float,
                        group_agg: str = "max", keep_ratio: float = 0.0,
-                       selected: Optional[torch.Tensor] = None,
+                       score_mode: str = "mean", selected: Optional[torch.Tensor] = None,
                        selected_count: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
                        lse: Optional[torch.Tensor] = None,
@@ -239,7 +270,7 @@ def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.T
     params = LsSelectParams(C.sizeof(LsSelectParams),
                             LS_AGG_MAX if group_agg == "max" else LS_AGG_MEAN,
                             int(topk), float(keep_ratio), int(n_sink), int(n_recent),
-                            int(max_selected))
+                            int(max_selected), _score_mode(score_mode, summaries, D))
     n_new = 0
     if new_pages is not None:
         _need(new_pages, torch.int32)

@@ -12,6 +12,7 @@ LS_OK, LS_ERR_INVALID, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP = range(
 LS_DTYPE_BF16, LS_DTYPE_FP32, LS_DTYPE_FP8_E4M3FN = 1, 2, 3
 LS_AGG_MAX, LS_AGG_MEAN = 0, 1
 LS_SEL_TOKENS, LS_SEL_BLOCKS = 0, 1
+LS_SCORE_MEAN, LS_SCORE_BOUNDS = 0, 1
 
 # every function the header declares, with its ctypes signature
 EXPORTS = {}
@@ -31,7 +32,7 @@ class LsBatch(C.Structure):
 class LsSelectParams(C.Structure):
     _fields_ = [("struct_size", C.c_int32), ("group_agg", C.c_int32), ("topk", C.c_int32),
                 ("keep_ratio", C.c_float), ("n_sink", C.c_int32), ("n_recent", C.c_int32),
-                ("max_selected", C.c_int32)]
+                ("max_selected", C.c_int32), ("score_mode", C.c_int32)]
 
 
 class LsIndexerParams(C.Structure):
@@ -42,6 +43,7 @@ class LsIndexerParams(C.Structure):
 _P = C.c_void_p
 _SIGS = {
     "ls_build_block_summaries": (C.c_int, [_P, _P, LsPool, _P, C.c_int32, _P, C.c_int32, _P]),
+    "ls_build_block_bounds": (C.c_int, [_P, LsPool, _P, C.c_int32, _P, _P]),
     "ls_score_select_workspace_size": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32]),
     "ls_score_select": (C.c_int, [_P, C.c_int32, C.c_int32, _P, LsPool, LsBatch,
                                   C.POINTER(LsSelectParams), _P, _P, _P, _P, C.c_size_t, _P]),

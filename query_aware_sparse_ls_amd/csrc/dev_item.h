@@ -230,6 +230,120 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
   }
 }
 
+// Quest bound scores (Vortex, "Writing an algorithm: vFlow", the Quest
+// listing) of the candidate blocks of (r, g) into sc[] (LDS), from the bounds
+// pool [num_pages][Hkv][2][D] (maximum row, then minimum row):
+//     u_h(b) = sum_d max(q_hd * max_bd, q_hd * min_bd)
+//            = q_h+ . max_b + q_h- . min_b,  q+ = max(q, 0), q- = min(q, 0)
+// (max_bd >= min_bd, so q_hd >= 0 picks the maximum and q_hd < 0 the
+// minimum), i.e. two dense contractions: each k-step runs one MFMA with the
+// staged maximum rows and one with the minimum rows. q+ and q- are bf16
+// values (q or 0), the products are exact in fp32. The group aggregation,
+// score stores and range are those of item_score; one slot holds both rows
+// of a 16-block tile.
+template <int D, int MAXC>
+__device__ __forceinline__ void item_score_bounds(const ScoreArgs& a, int r, int g,
+                                                  const ReqGeom& geo, const int* pg, float* sc,
+                                                  uint32_t* stage, float* range = nullptr) {
+  using ST = Stage<D>;
+  constexpr int KS = D / 32, NL = ST::NL, NS = kItemScorePrefetch;
+  const int HKV = a.num_kv_heads;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int row = lane & 15, kq = lane >> 4;
+  QOperand<D> qp = load_q_operand<D>(a.q, a.num_q_heads, r, g), qn;
+  // q- keeps the negative bf16 halves, q+ the others (by the sign bit)
+  auto split = [](uint32_t w, uint32_t* pos) {
+    const uint32_t neg = ((w & 0x80008000u) >> 15) * 0xFFFFu;
+    *pos = w & ~neg;
+    return w & neg;
+  };
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    uint4& b = qp.b[j];
+    uint4 nb;
+    nb.x = split(b.x, &b.x);
+    nb.y = split(b.y, &b.y);
+    nb.z = split(b.z, &b.z);
+    nb.w = split(b.w, &b.w);
+    qn.b[j] = nb;
+  }
+  const uint16_t* base = a.summaries + (size_t)g * 2 * D + 8 * (lane % ST::LPR);
+  const uint32_t pstride = (uint32_t)HKV * 2 * D;   // elements per page (< 2^32)
+  uint32_t* tiles = stage + wave * 2 * 16 * ST::kKRowWords;   // maximum rows, minimum rows
+  const int t0 = geo.c0 / 16, t1 = (geo.c1 + 15) / 16;
+  const int ntw = t1 - t0 > wave ? (t1 - t0 - wave + kItemWaves - 1) / kItemWaves : 0;
+  auto page_of = [&](int k, int j) {
+    const int b = (t0 + wave + kItemWaves * k) * 16 + j * ST::RPI + lane / ST::LPR;
+    if (k >= ntw || b < geo.c0 || b >= geo.c1) return -1;
+    const int p = pg[b < MAXC ? b : MAXC - 1];
+    return (p >= 0 && p < a.b.num_pages) ? p : -2;
+  };
+  // slot layout: d[j] = maximum-row chunk j, d[NL + j] = minimum-row chunk j
+  auto issue = [&](int k, uint4* d, uint32_t& badm) {
+    badm = 0;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int p = page_of(k, j);
+      badm |= (uint32_t)(p == -2) << j;
+      const uint16_t* rp = base + (uint64_t)(uint32_t)(p >= 0 ? p : 0) * pstride;
+      d[j] = ldg16_stream(rp);
+      d[NL + j] = ldg16_stream(rp + D);
+    }
+  };
+  static_assert(MAXC % 16 == 0, "whole score tiles");
+  const bool mean = a.group_agg == LS_AGG_MEAN;
+  float smin = __builtin_huge_valf(), smax = -__builtin_huge_valf();
+  auto finish = [&](const f32x4_t& acc, int k) {
+    const float v = mean ? ((acc[0] + acc[1]) + (acc[2] + acc[3])) * 0.25f
+                         : fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+    if (kq == 0 && k < ntw) {
+      const int b = (t0 + wave + kItemWaves * k) * 16 + row;
+      const bool cand = b >= geo.c0 && b < geo.c1;
+      sc[b] = v;
+      smin = cand ? fminf(smin, v) : smin;
+      smax = cand ? fmaxf(smax, v) : smax;
+    }
+  };
+  uint4 buf[NS][2 * NL];
+  uint32_t badm[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    issue(s, buf[s], badm[s]);
+    __builtin_amdgcn_sched_barrier(0);   // issue the slots in order (oldest = slot 0)
+  }
+  for (int k0 = 0; k0 < ntw; k0 += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      uint4 c[2 * NL];
+      const uint32_t bm = badm[s];
+#pragma unroll
+      for (int j = 0; j < 2 * NL; ++j) c[j] = buf[s][j];
+      __builtin_amdgcn_sched_barrier(0);
+      issue(k0 + s + NS, buf[s], badm[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t* thi = tiles;
+      uint32_t* tlo = tiles + 16 * ST::kKRowWords;
+      stage_k<D>(thi, c, bm);        // rows with a bad page score 0
+      stage_k<D>(tlo, c + NL, bm);
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        acc = mfma_16x16x32(qp.b[j], k_operand<D>(thi, j), acc);
+        acc = mfma_16x16x32(qn.b[j], k_operand<D>(tlo, j), acc);
+      }
+      finish(acc, k0 + s);
+    }
+  }
+  if (range) {
+    smin = wave_min_fast(smin);
+    smax = wave_max_fast(smax);
+    if (lane == 0) {
+      range[wave] = smin;
+      range[kItemWaves + wave] = smax;
+    }
+  }
+}
+
 // LDS of the attention: per-wave V staging tiles and the wave states.
 template <int D>
 struct alignas(16) ItemAttnLds {   // 16-byte aligned: the tiles take 16-byte LDS accesses

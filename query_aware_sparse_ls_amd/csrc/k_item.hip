@@ -10,7 +10,8 @@
 
 namespace ls {
 
-template <int D, int MAXC>
+// kBounds: the summaries are Quest bounds, scored by item_score_bounds.
+template <int D, int MAXC, bool kBounds>
 __global__ __launch_bounds__(kItemThreads) void select_item_kernel(ScoreArgs sa, TopkArgs ta) {
   __shared__ int pg[MAXC];
   __shared__ __attribute__((aligned(16))) float sc[MAXC];
@@ -22,7 +23,8 @@ __global__ __launch_bounds__(kItemThreads) void select_item_kernel(ScoreArgs sa,
   const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
   load_page_row<MAXC>(sa.b, geo, pg);
   __syncthreads();
-  item_score<D, MAXC>(sa, r, g, geo, pg, sc, stage, range);
+  if constexpr (kBounds) item_score_bounds<D, MAXC>(sa, r, g, geo, pg, sc, stage, range);
+  else item_score<D, MAXC>(sa, r, g, geo, pg, sc, stage, range);
   __syncthreads();
   if (sa.scores) {
     float* out = sa.scores + (size_t)item * sa.b.max_blocks;
@@ -63,14 +65,19 @@ __global__ __launch_bounds__(kItemThreads) void attn_item_kernel(AttnArgs a) {
 // Rows of the grid past the batch refresh the summaries of the pages that
 // just filled (one wave per (page, head) tile), concurrently with the pairs'
 // steps: those pages are not scored in this call (the caller guarantees it).
-template <int D, int MAXC>
+template <int D, int MAXC, bool kBounds>
 __global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, TopkArgs ta,
                                                                  AttnArgs aa, SummaryUpdate up) {
   if ((int)blockIdx.y >= sa.b.batch) {
     const int tile = ((blockIdx.y - sa.b.batch) * gridDim.x + blockIdx.x) * kItemWaves + wave_id();
-    if (tile < up.n_tiles)
-      summary_tile_bf16<D, false>(up.keys, up.pages, tile, sa.b.num_pages, sa.num_kv_heads,
-                                  sa.b.page_size, up.out);
+    if (tile < up.n_tiles) {
+      if constexpr (kBounds)
+        bounds_tile_bf16<D>(up.keys, up.pages, tile, sa.b.num_pages, sa.num_kv_heads,
+                            sa.b.page_size, static_cast<uint16_t*>(up.out));
+      else
+        summary_tile_bf16<D, false>(up.keys, up.pages, tile, sa.b.num_pages, sa.num_kv_heads,
+                                    sa.b.page_size, up.out);
+    }
     return;
   }
   __shared__ int pg[MAXC];
@@ -89,7 +96,8 @@ __global__ __launch_bounds__(kItemThreads) void step_item_kernel(ScoreArgs sa, T
   const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
   load_page_row<MAXC>(sa.b, geo, pg);
   __syncthreads();
-  item_score<D, MAXC>(sa, r, g, geo, pg, u.s.sc, u.s.stage, u.s.range);
+  if constexpr (kBounds) item_score_bounds<D, MAXC>(sa, r, g, geo, pg, u.s.sc, u.s.stage, u.s.range);
+  else item_score<D, MAXC>(sa, r, g, geo, pg, u.s.sc, u.s.stage, u.s.range);
   __syncthreads();
   const int cnt = topk_wg<MAXC / kItemThreads, kItemThreads>(
       u.s.sc + geo.c0, geo, topk_budget(ta, geo), ta.selected + (size_t)item * ta.max_selected,
@@ -268,10 +276,15 @@ bool item_path(int batch, int hkv, int head_dim, int group, int max_blocks, int 
 hipError_t launch_select_item(const ScoreArgs& sa, const TopkArgs& ta, hipStream_t st) {
   const int D = sa.head_dim, n = sa.b.max_blocks;
   const dim3 grid(sa.num_kv_heads, sa.b.batch);
-#define LAUNCH(DD, MC)                                                                      \
-  do {                                                                                      \
-    hipLaunchKernelGGL((select_item_kernel<DD, MC>), grid, dim3(kItemThreads), 0, st, sa, ta); \
-    return hipGetLastError();                                                               \
+#define LAUNCH(DD, MC)                                                                    \
+  do {                                                                                    \
+    if (sa.bounds)                                                                        \
+      hipLaunchKernelGGL((select_item_kernel<DD, MC, true>), grid, dim3(kItemThreads), 0, \
+                         st, sa, ta);                                                     \
+    else                                                                                  \
+      hipLaunchKernelGGL((select_item_kernel<DD, MC, false>), grid, dim3(kItemThreads), 0, \
+                         st, sa, ta);                                                     \
+    return hipGetLastError();                                                             \
   } while (0)
   LS_ITEM_DISPATCH(LAUNCH)
 #undef LAUNCH
@@ -338,12 +351,14 @@ hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnA
                             const SummaryUpdate& up, hipStream_t st) {
   const int D = sa.head_dim, n = sa.b.max_blocks;
   const bool one_launch = !pair_path(sa.b.batch, sa.num_kv_heads, n) && n <= 4096;
+  if (sa.bounds && pair_path(sa.b.batch, sa.num_kv_heads, n))
+    return hipErrorInvalidValue;   // no two-workgroup scoring of bounds (checked by the caller)
   if (up.n_tiles > 0 && !one_launch) {
     // the multi-launch forms refresh the summaries first
     SummaryArgs su{up.keys, nullptr, ls_pool{sa.b.num_pages, sa.num_kv_heads, sa.b.page_size, D,
                                              LS_DTYPE_BF16},
                    up.pages, up.n_tiles / sa.num_kv_heads, up.out, LS_DTYPE_BF16};
-    const hipError_t e = launch_summaries(su, st);
+    const hipError_t e = sa.bounds ? launch_bounds(su, st) : launch_summaries(su, st);
     if (e != hipSuccess) return e;
   }
   if (pair_path(sa.b.batch, sa.num_kv_heads, n)) {
@@ -375,8 +390,12 @@ hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnA
   const dim3 grid(sa.num_kv_heads, sa.b.batch + (up.n_tiles + per_row - 1) / per_row);
 #define LAUNCH(DD, MC)                                                                      \
   do {                                                                                      \
-    hipLaunchKernelGGL((step_item_kernel<DD, MC>), grid, dim3(kItemThreads), 0, st, sa, ta, \
-                       aa, up);                                                             \
+    if (sa.bounds)                                                                          \
+      hipLaunchKernelGGL((step_item_kernel<DD, MC, true>), grid, dim3(kItemThreads), 0, st, \
+                         sa, ta, aa, up);                                                   \
+    else                                                                                    \
+      hipLaunchKernelGGL((step_item_kernel<DD, MC, false>), grid, dim3(kItemThreads), 0, st, \
+                         sa, ta, aa, up);                                                   \
     return hipGetLastError();                                                               \
   } while (0)
   if (D == 128) {

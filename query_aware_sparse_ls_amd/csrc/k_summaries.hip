@@ -80,6 +80,29 @@ static hipError_t launch_fp8(const SummaryArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void bounds_bf16_kernel(
+    const uint16_t* __restrict__ keys, const int32_t* __restrict__ page_ids, int n_pages,
+    int num_pages, int num_heads, int page_size, uint16_t* __restrict__ out) {
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= n_pages * num_heads) return;
+  bounds_tile_bf16<D>(keys, page_ids, tile, num_pages, num_heads, page_size, out);
+}
+
+hipError_t launch_bounds(const SummaryArgs& a, hipStream_t st) {
+  const int tiles = a.n_pages * a.pool.num_heads;
+  dim3 grid((tiles + 3) / 4);
+  if (a.pool.head_dim == 128)
+    hipLaunchKernelGGL((bounds_bf16_kernel<128>), grid, dim3(256), 0, st,
+                       (const uint16_t*)a.keys, a.page_ids, a.n_pages, a.pool.num_pages,
+                       a.pool.num_heads, a.pool.page_size, (uint16_t*)a.out);
+  else
+    hipLaunchKernelGGL((bounds_bf16_kernel<64>), grid, dim3(256), 0, st,
+                       (const uint16_t*)a.keys, a.page_ids, a.n_pages, a.pool.num_pages,
+                       a.pool.num_heads, a.pool.page_size, (uint16_t*)a.out);
+  return hipGetLastError();
+}
+
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t st) {
   const bool f32 = a.out_dtype == LS_DTYPE_FP32;
   const int D = a.pool.head_dim;

@@ -102,7 +102,14 @@ ls::ScoreArgs score_args(const void* q, int num_q_heads, const void* summaries,
   sa.n_sink = p.n_sink;
   sa.n_recent = p.n_recent;
   sa.scores = scores;
+  sa.bounds = p.score_mode == LS_SCORE_BOUNDS ? 1 : 0;
   return sa;
+}
+
+// Shapes the bounds scoring supports: the per-pair selection kernel (any
+// number of pairs) with its walk-entry encoding.
+bool bounds_ok(const ls_pool& pool, const ls_batch& batch) {
+  return batch.max_blocks <= 8192 && pool.num_pages < (1 << 26);
 }
 
 ls::TopkArgs topk_args(const ls::ScoreArgs& sa, const ls_select_params& p, const float* scores,
@@ -151,7 +158,7 @@ extern "C" {
 
 const char* ls_last_error(void) { return g_err; }
 
-const char* ls_version(void) { return "libls 0.2.0 abi 2 gfx950"; }
+const char* ls_version(void) { return "libls 0.3.0 abi 3 gfx950"; }
 
 int32_t ls_attn_num_splits(int32_t max_selected) {
   if (max_selected < 1) return 1;
@@ -188,6 +195,25 @@ ls_status ls_build_block_summaries(const void* keys, const float* key_scales, ls
   return hip_status(ls::launch_summaries(a, stream), "ls_build_block_summaries launch");
 }
 
+ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_t* page_ids,
+                                int32_t n_pages, void* bounds, hipStream_t stream) {
+  if (n_pages < 0) return fail(LS_ERR_INVALID, "n_pages < 0");
+  if (key_pool.num_pages < 1 || key_pool.num_heads < 1)
+    return fail(LS_ERR_INVALID, "key_pool: num_pages and num_heads must be >= 1");
+  if (!pow2(key_pool.page_size) || key_pool.page_size < 16 || key_pool.page_size > 64)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.page_size %d (supported: 16, 32, 64)",
+                key_pool.page_size);
+  if (key_pool.head_dim != 64 && key_pool.head_dim != 128)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.head_dim %d (supported: 64, 128)", key_pool.head_dim);
+  if (key_pool.dtype != LS_DTYPE_BF16)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.dtype %d (supported: bf16)", key_pool.dtype);
+  if (n_pages == 0) return ok();
+  if (!keys || !page_ids || !bounds)
+    return fail(LS_ERR_INVALID, "keys, page_ids and bounds must be non-null");
+  ls::SummaryArgs a{keys, nullptr, key_pool, page_ids, n_pages, bounds, LS_DTYPE_BF16};
+  return hip_status(ls::launch_bounds(a, stream), "ls_build_block_bounds launch");
+}
+
 size_t ls_score_select_workspace_size(int32_t batch_size, int32_t num_kv_heads,
                                       int32_t max_blocks) {
   if (batch_size <= 0 || num_kv_heads <= 0 || max_blocks <= 0) return 0;
@@ -215,6 +241,11 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
                 num_q_heads / pool.num_heads);
   if (p->group_agg != LS_AGG_MAX && p->group_agg != LS_AGG_MEAN)
     return fail(LS_ERR_INVALID, "group_agg %d", p->group_agg);
+  if (p->score_mode != LS_SCORE_MEAN && p->score_mode != LS_SCORE_BOUNDS)
+    return fail(LS_ERR_INVALID, "score_mode %d", p->score_mode);
+  if (p->score_mode == LS_SCORE_BOUNDS && batch.batch_size > 0 && !bounds_ok(pool, batch))
+    return fail(LS_ERR_UNSUPPORTED,
+                "bounds scoring needs max_blocks <= 8192 and num_pages < 2^26");
   if (p->n_sink < 0 || p->n_recent < 0) return fail(LS_ERR_INVALID, "n_sink/n_recent < 0");
   if (p->topk < -1) return fail(LS_ERR_INVALID, "topk %d (>= 0, or -1 for keep_ratio)", p->topk);
   if (p->topk == -1 && !(p->keep_ratio >= 0.0f && p->keep_ratio <= 1.0f))
@@ -242,8 +273,10 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
   }
   const ls::ScoreArgs sa = score_args(q, num_q_heads, summaries, pool, batch, *p, scores);
   const ls::TopkArgs ta = topk_args(sa, *p, scores, selected, selected_count);
-  if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, num_q_heads / pool.num_heads,
-                    batch.max_blocks, pool.num_pages)) {
+  if (sa.bounds || ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim,
+                                 num_q_heads / pool.num_heads, batch.max_blocks,
+                                 pool.num_pages)) {
+    // (bounds are scored by the per-pair selection kernel at any batch size)
     ls::ScoreArgs si = sa;
     si.scores = scores_out;   // scores stay in LDS unless the caller asked for them
     return hip_status(ls::launch_select_item(si, ta, stream), "selection kernel launch");
@@ -351,6 +384,11 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
                 num_q_heads / pool.num_heads);
   if (p->group_agg != LS_AGG_MAX && p->group_agg != LS_AGG_MEAN)
     return fail(LS_ERR_INVALID, "group_agg %d", p->group_agg);
+  if (p->score_mode != LS_SCORE_MEAN && p->score_mode != LS_SCORE_BOUNDS)
+    return fail(LS_ERR_INVALID, "score_mode %d", p->score_mode);
+  if (p->score_mode == LS_SCORE_BOUNDS && batch.batch_size > 0 && !bounds_ok(pool, batch))
+    return fail(LS_ERR_UNSUPPORTED,
+                "bounds scoring needs max_blocks <= 8192 and num_pages < 2^26");
   if (p->n_sink < 0 || p->n_recent < 0) return fail(LS_ERR_INVALID, "n_sink/n_recent < 0");
   if (p->topk < -1) return fail(LS_ERR_INVALID, "topk %d (>= 0, or -1 for keep_ratio)", p->topk);
   if (p->topk == -1 && !(p->keep_ratio >= 0.0f && p->keep_ratio <= 1.0f))
@@ -393,13 +431,30 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
                                     out_dtype, lse_out);
   const ls::SummaryUpdate up{static_cast<const uint16_t*>(k_pool), new_page_ids,
                              n_new_pages * pool.num_heads, summaries};
-  if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, num_q_heads / pool.num_heads,
-                    batch.max_blocks, pool.num_pages)) {
+  const bool item = ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim,
+                                  num_q_heads / pool.num_heads, batch.max_blocks, pool.num_pages);
+  // the fused kernels score bounds in one workgroup per pair only
+  const bool split_pairs = ls::pair_path(batch.batch_size, pool.num_heads, batch.max_blocks);
+  if (item && !(sa.bounds && split_pairs)) {
     ls::ScoreArgs si = sa;
     si.scores = nullptr;
     return hip_status(ls::launch_step_item(si, ta, aa, up, stream), "decode-step kernel launch");
   }
   hipError_t e = hipSuccess;
+  if (sa.bounds) {
+    // bounds first (if asked), the per-pair selection, then the attention
+    if (n_new_pages > 0) {
+      const ls::SummaryArgs su{k_pool, nullptr, pool, new_page_ids, n_new_pages, summaries,
+                               LS_DTYPE_BF16};
+      e = ls::launch_bounds(su, stream);
+      if (e != hipSuccess) return hip_status(e, "bounds kernel launch");
+    }
+    ls::ScoreArgs si = sa;
+    si.scores = nullptr;
+    e = ls::launch_select_item(si, ta, stream);
+    if (e == hipSuccess) e = item ? ls::launch_attn_item(aa, stream) : ls::launch_attn(aa, stream);
+    return hip_status(e, "decode-step kernel launches");
+  }
   if (n_new_pages > 0) {
     const ls::SummaryArgs su{k_pool, nullptr, pool, new_page_ids, n_new_pages, summaries,
                              LS_DTYPE_BF16};

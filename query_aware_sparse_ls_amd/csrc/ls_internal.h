@@ -36,6 +36,7 @@ struct ScoreArgs {
   int32_t group_agg;
   int32_t n_sink, n_recent;
   float* scores;              // [B][Hkv][max_blocks]
+  int32_t bounds;             // 1: summaries are Quest bounds [num_pages][Hkv][2][D]
 };
 
 struct TopkArgs {
@@ -68,6 +69,8 @@ struct AttnArgs {
 };
 
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t st);
+// Quest bounds (bf16 keys): out = [num_pages][num_heads][2][D] bf16.
+hipError_t launch_bounds(const SummaryArgs& a, hipStream_t st);
 
 // Pages whose bf16 summaries a decode step refreshes alongside its work
 // (pages that just filled; n_tiles = pages * kv heads, 0 = none).

@@ -82,8 +82,23 @@ def poison_padding(inp: BlockTopKInputs) -> int:
     return n
 
 
+def build_summaries(inp: BlockTopKInputs, score_mode: str = "mean") -> torch.Tensor:
+    """Block-mean summaries [pages][Hkv][D] or Quest bounds [pages][Hkv][2][D]
+    of every complete page (other rows zero)."""
+    import query_aware_sparse_ls_amd as ls
+    dev = inp.k_pool.device
+    Hkv, D = inp.cfg.num_kv_heads, inp.cfg.head_dim
+    ids = complete_pages(inp).to(dev)
+    if score_mode == "bounds":
+        out = torch.zeros(inp.num_pages, Hkv, 2, D, dtype=torch.bfloat16, device=dev)
+        return ls.build_block_bounds(inp.k_pool, ids, out)
+    out = torch.zeros(inp.num_pages, Hkv, D, dtype=torch.bfloat16, device=dev)
+    return ls.build_block_summaries(inp.k_pool, ids, out)
+
+
 def run_gpu_step(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None, agg=None,
-                 out_dtype=None, keep_ratio=0.0, sm_scale=None, dense=False) -> GpuStep:
+                 out_dtype=None, keep_ratio=0.0, sm_scale=None, dense=False,
+                 score_mode="mean") -> GpuStep:
     import query_aware_sparse_ls_amd as ls
     cfg = inp.cfg
     topk = inp.topk if topk is None else topk
@@ -96,13 +111,12 @@ def run_gpu_step(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None,
     B, Hq, D = inp.q.shape
     Hkv = cfg.num_kv_heads
     batch = paged_batch(inp)
-    summ = torch.zeros(inp.num_pages, Hkv, D, dtype=torch.bfloat16, device=dev)
-    ls.build_block_summaries(inp.k_pool, complete_pages(inp).to(dev), summ)
+    summ = build_summaries(inp, score_mode)
     maxsel = max_selected_for(topk, n_sink, n_recent, batch.max_blocks, keep_ratio)
     scores = torch.full((B, Hkv, batch.max_blocks), float("nan"), dtype=torch.float32, device=dev)
     sel, cnt = ls.score_select(inp.q, summ, cfg.page_size, batch, topk=topk, n_sink=n_sink,
                                n_recent=n_recent, max_selected=maxsel, group_agg=agg,
-                               keep_ratio=keep_ratio, scores_out=scores)
+                               keep_ratio=keep_ratio, scores_out=scores, score_mode=score_mode)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
     if dense:
         out, _ = ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, batch, None, None,
@@ -152,23 +166,32 @@ def check_selection(gpu_sel: List[int], scores: np.ndarray, nb: int, nc: int, k:
 
 
 def check_pair(inp: BlockTopKInputs, res: GpuStep, r: int, g: int, *, topk, n_sink, n_recent,
-               agg, sm_scale, out_dtype, check_scores=True, dense=False):
-    """Full parity of one (request, kv head): summaries, scores, selection and
-    attention output (oracle attention on the GPU's own selection)."""
+               agg, sm_scale, out_dtype, check_scores=True, dense=False, score_mode="mean"):
+    """Full parity of one (request, kv head): summaries (block means, or Quest
+    bounds), scores, selection and attention output (oracle attention on the
+    GPU's own selection)."""
     q, k, v, batch = sub_problem(inp, r, g)
     L = int(batch.seq_lens[0])
     nb, nc = batch.num_blocks(0), batch.num_complete(0)
     P = inp.cfg.page_size
     G = inp.cfg.group
     # summaries: bit-exact
-    summ = oracle.block_summaries(k, np.arange(nc)) if nc else np.zeros((0, 1, k.shape[-1]), np.uint16)
+    D = k.shape[-1]
+    if score_mode == "bounds":
+        summ = oracle.block_bounds(k, np.arange(nc))
+    else:
+        summ = oracle.block_summaries(k, np.arange(nc)) if nc else np.zeros((0, 1, D), np.uint16)
     p0 = int(inp.page_indptr[r])
     pages = inp.page_indices[p0:p0 + nc].long()
     gsum = bf16_bits(res.summaries[pages, g:g + 1].contiguous())
     assert np.array_equal(gsum, summ), "summaries differ"
     # scores (fp32 GPU vs fp64 oracle)
-    s = oracle.block_scores(q, summ if nc else summ, batch, 0, 0, num_kv_heads=1, agg=agg) \
-        if nc else np.zeros(0)
+    if not nc:
+        s = np.zeros(0)
+    elif score_mode == "bounds":
+        s = oracle.bound_scores(q, summ, batch, 0, 0, num_kv_heads=1, agg=agg)
+    else:
+        s = oracle.block_scores(q, summ, batch, 0, 0, num_kv_heads=1, agg=agg)
     forced = set(forced_blocks(nb, nc, n_sink, n_recent))
     cands = [j for j in range(nc) if j not in forced]
     if check_scores and cands and res.scores is not None:
@@ -204,7 +227,7 @@ def check_pair(inp: BlockTopKInputs, res: GpuStep, r: int, g: int, *, topk, n_si
 
 def run_gpu_fused(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None, agg=None,
                   out_dtype=None, keep_ratio=0.0, sm_scale=None, workspace=None,
-                  summaries=None, new_pages=None) -> GpuStep:
+                  summaries=None, new_pages=None, score_mode="mean") -> GpuStep:
     """The whole step in one call (ls_sparse_decode_step); it keeps its
     block scores on chip, so the result carries none."""
     import query_aware_sparse_ls_amd as ls
@@ -220,8 +243,7 @@ def run_gpu_fused(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None
     Hkv = cfg.num_kv_heads
     batch = paged_batch(inp)
     if summaries is None:
-        summaries = torch.zeros(inp.num_pages, Hkv, D, dtype=torch.bfloat16, device=dev)
-        ls.build_block_summaries(inp.k_pool, complete_pages(inp).to(dev), summaries)
+        summaries = build_summaries(inp, score_mode)
     maxsel = max_selected_for(topk, n_sink, n_recent, batch.max_blocks, keep_ratio)
     if workspace is None:
         workspace = ls.sparse_decode_step_workspace(B, Hq, Hkv, D, batch.max_blocks, maxsel, dev)
@@ -230,6 +252,6 @@ def run_gpu_fused(inp: BlockTopKInputs, *, topk=None, n_sink=None, n_recent=None
         inp.q, summaries, inp.k_pool, inp.v_pool, batch, topk=topk, n_sink=n_sink,
         n_recent=n_recent, max_selected=maxsel, sm_scale=sm_scale, group_agg=agg,
         keep_ratio=keep_ratio, out_dtype=out_dtype, lse=lse, new_pages=new_pages,
-        workspace=workspace)
+        workspace=workspace, score_mode=score_mode)
     torch.cuda.synchronize()
     return GpuStep(summaries, None, sel, cnt, out, lse)

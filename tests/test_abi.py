@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 def test_version_and_empty_error():
     lib = _lib.load()
     assert b"gfx950" in lib.ls_version()
-    assert b"abi 2" in lib.ls_version()
+    assert b"abi 3" in lib.ls_version()
 
 
 def _pool(**kw):
@@ -85,6 +85,10 @@ def test_score_select_validation():
     assert _score(lib, p=_params(), num_q_heads=16) == _lib.LS_ERR_UNSUPPORTED  # group 2
     assert _score(lib, p=_params(), q_dtype=_lib.LS_DTYPE_FP32) == _lib.LS_ERR_UNSUPPORTED
     assert _score(lib, p=_params(group_agg=7)) == _lib.LS_ERR_INVALID
+    assert _score(lib, p=_params(score_mode=2)) == _lib.LS_ERR_INVALID
+    assert b"score_mode" in lib.ls_last_error()
+    assert _score(lib, p=_params(score_mode=_lib.LS_SCORE_BOUNDS, max_selected=10000),
+                  batch=_batch(max_blocks=9000)) == _lib.LS_ERR_UNSUPPORTED   # bounds <= 8192
     assert _score(lib, p=_params(topk=-3)) == _lib.LS_ERR_INVALID
     assert _score(lib, p=_params(topk=-1, keep_ratio=1.5)) == _lib.LS_ERR_INVALID
     assert _score(lib, p=_params(max_selected=2)) == _lib.LS_ERR_INVALID
@@ -162,3 +166,17 @@ def test_step_validation():
     assert call(p=_params(n_recent=0), new=FAKE, n_new=2) == _lib.LS_ERR_INVALID
     assert b"n_recent" in lib.ls_last_error()
     assert call(batch=_batch(batch_size=0), new=FAKE, n_new=2) == _lib.LS_OK
+
+
+def test_bounds_validation():
+    lib = _lib.load()
+    f = lib.ls_build_block_bounds
+    assert f(FAKE, _pool(), FAKE, -1, FAKE, None) == _lib.LS_ERR_INVALID
+    assert f(FAKE, _pool(), FAKE, 0, FAKE, None) == _lib.LS_OK
+    assert f(FAKE, _pool(page_size=12), FAKE, 1, FAKE, None) == _lib.LS_ERR_UNSUPPORTED
+    assert f(FAKE, _pool(head_dim=96), FAKE, 1, FAKE, None) == _lib.LS_ERR_UNSUPPORTED
+    assert f(FAKE, _pool(dtype=_lib.LS_DTYPE_FP8_E4M3FN), FAKE, 1, FAKE,
+             None) == _lib.LS_ERR_UNSUPPORTED                  # bf16 keys only
+    assert f(FAKE, _pool(num_heads=0), FAKE, 1, FAKE, None) == _lib.LS_ERR_INVALID
+    assert f(None, _pool(), FAKE, 1, FAKE, None) == _lib.LS_ERR_INVALID
+    assert f(FAKE, _pool(), FAKE, 1, None, None) == _lib.LS_ERR_INVALID

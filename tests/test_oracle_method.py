@@ -275,6 +275,31 @@ def test_quest_block_of_equal_tokens_scores_its_dot_product():
     assert abs(Fraction(float(s[0])) - want) <= abs(want) * Fraction(1, 10 ** 14)
 
 
+def test_quest_step_finds_the_block_of_a_planted_key():
+    """A key aligned with a query head, planted in one block of each request
+    among small keys: the Quest step (bounds, top-1 + 1 recent) keeps that
+    block, and its attention is the attention over the kept blocks."""
+    rng = np.random.default_rng(34)
+    batch, npg = _tiny_batch(rng, lens=(24, 20))
+    keys = _rand_bf16(rng, (npg, 2, 4, 8), scale=0.05)
+    vals = _rand_bf16(rng, (npg, 2, 4, 8))
+    q = _rand_bf16(rng, (2, 4, 8))
+    planted = {0: 2, 1: 1}                      # request -> block holding the key
+    for r, j in planted.items():
+        p = batch.pages(r)[j]
+        keys[p, 1, 3] = f64_to_bf16_bits(4 * bf16_to_f64(q[r, 3]))   # kv head 1, head 3
+    res = decode_step(q, keys, vals, batch, num_kv_heads=2, topk=1, n_sink=0, n_recent=1,
+                      sm_scale=0.25, score_mode="bounds", out_dtype="fp64")
+    for r, j in planted.items():
+        nb = batch.num_blocks(r)
+        got = res["pairs"][(r, 1)]
+        assert got["selected"] == sorted({j, nb - 1})
+        o, lse = sparse_attention(q, keys, vals, batch, r, 1, got["selected"], num_kv_heads=2,
+                                  sm_scale=0.25, out_dtype="fp64")
+        assert np.array_equal(o, got["out"]) and np.array_equal(lse, got["lse"])
+    assert res["summaries"].shape == (npg, 2, 2, 8)
+
+
 def test_max_and_mean_agree_for_one_head_per_group():
     rng = np.random.default_rng(15)
     batch, npg = _tiny_batch(rng, Hq=2, Hkv=2)
