@@ -37,6 +37,7 @@ namespace ls {
 constexpr int kItemThreads = 512;
 constexpr int kItemWaves = kItemThreads / kWave;
 constexpr int kItemScorePrefetch = 2;   // summary tiles in flight per wave
+constexpr int kItemBoundsPrefetch = 1;  // bounds tiles (max + min rows) in flight per wave
 constexpr int kItemPrefetch = 2;        // K/V blocks in flight per wave
 // Walk entries past the selection that item_attn may read: wave w refills
 // its slots with position w + 8(k + kItemPrefetch) for k < nbw + kItemPrefetch
@@ -246,7 +247,7 @@ __device__ __forceinline__ void item_score_bounds(const ScoreArgs& a, int r, int
                                                   const ReqGeom& geo, const int* pg, float* sc,
                                                   uint32_t* stage, float* range = nullptr) {
   using ST = Stage<D>;
-  constexpr int KS = D / 32, NL = ST::NL, NS = kItemScorePrefetch;
+  constexpr int KS = D / 32, NL = ST::NL, NS = kItemBoundsPrefetch;
   const int HKV = a.num_kv_heads;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int row = lane & 15, kq = lane >> 4;
