@@ -14,6 +14,8 @@ written from the pages:
 * LeanSparse ("LeanSparse: Memory-Efficient Serving for Native
   Sparse-Attention LLMs"): the learned indexer's weighted-ReLU head
   aggregation (§5, Eq. 6) and coarse-to-fine candidate refinement (§5).
+* LeanSparse §5, "Approximate scoring with PQ": PQ32 codes, k-means
+  codebooks, coarse scores with centroids and exact refinement (pq.py).
 * ByteCross ("Where Activation Sparsity and KV-Cache Sparsity Cross in LLM
   Decoding"): merging attention over disjoint token sets by log-sum-exp
   (App. A) and the byte account of a decode step (§3.1, Eq. 1-4).
@@ -28,7 +30,7 @@ the oracle itself (brute force, exact rationals, closed forms, the pages'
 worked example), except where a header says "parity unpinned".
 """
 
-from . import method, numerics  # noqa: F401
+from . import method, numerics, pq  # noqa: F401
 from .numerics import (  # noqa: F401
     bf16_to_f64, fp8e4m3fn_to_f64, f64_to_bf16_bits, f64_to_f32, fraction_to_bf16_bits,
 )
