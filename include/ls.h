@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 3
+#define LS_ABI_VERSION 4
 
 typedef enum ls_status {
   LS_OK = 0,
@@ -359,6 +359,14 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
  * cand_blocks:  tokens only, optional: [batch][cand_cap] ascending block
  *               indices with counts cand_counts[batch] (e.g. the selection
  *               of a LS_SEL_BLOCKS call); entries past the count are ignored.
+ *               With p->candidates == LS_CAND_TOKENS the list holds TOKEN
+ *               ids instead, strictly ascending, all in complete pages (e.g.
+ *               the candidates of ls_pq_select), and the units are those
+ *               tokens followed by the tokens of the request's partial last
+ *               page (LeanSparse §5, "Retrieving and refining candidates":
+ *               exact scores of the candidates and of the recent keys not
+ *               yet encoded). A list that breaks this rule gives an
+ *               unspecified selection (never an out-of-range access).
  * p:            host pointer. max_selected >= topk (tokens), or
  *               >= min(max_blocks, topk + n_sink + n_recent + 1) (blocks).
  * selected, selected_count: [batch][max_selected] int32, [batch] int32.
@@ -369,7 +377,8 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
  * workspace:    >= ls_indexer_select_workspace_size(batch, granularity, U)
  *               bytes, 256-byte aligned, need not be initialised; U = units
  *               per request at most: tokens max_blocks * page_size, or
- *               cand_cap * page_size with candidates (<= 262144); blocks
+ *               cand_cap * page_size with block candidates, or cand_cap +
+ *               page_size with token candidates (<= 262144); blocks
  *               max_blocks (<= 16384).
  * Token mode is three launches: a histogram of the score keys while scoring,
  * a pass that keeps every unit above the k-th score's 12-bit bucket and
@@ -377,6 +386,7 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
  * key (in the last workgroup of each request to finish the pass).
  */
 enum { LS_SEL_TOKENS = 0, LS_SEL_BLOCKS = 1 };
+enum { LS_CAND_BLOCKS = 0, LS_CAND_TOKENS = 1 };
 
 typedef struct ls_indexer_params {
   int32_t struct_size;   /* = sizeof(ls_indexer_params)                       */
@@ -385,6 +395,8 @@ typedef struct ls_indexer_params {
   int32_t n_sink;        /* blocks only: forced blocks 0 .. n_sink-1          */
   int32_t n_recent;      /* blocks only: forced last n_recent blocks          */
   int32_t max_selected;  /* row capacity of `selected`                        */
+  int32_t candidates;    /* LS_CAND_BLOCKS or LS_CAND_TOKENS: what cand_blocks */
+                         /* holds (tokens mode with a candidate list)         */
 } ls_indexer_params;
 
 /* Row stride (in floats) of scores_out for up to max_units units. */
@@ -442,6 +454,68 @@ ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_hea
                                int32_t max_selected, float sm_scale, void* out,
                                int32_t out_dtype, float* lse_out, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* 7. PQ32 coarse scoring of indexer keys                                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * LeanSparse §5, "Approximate scoring with PQ": each 128-dim indexer key
+ * x = scale * fp8 is cut into 32 subvectors of 4 dims and stored as 32
+ * one-byte codes, code j = the nearest centroid of subvector j in codebook
+ * C_j (256 centroids). The coarse score of a token replaces every subvector
+ * by its centroid in the indexer score (Eq. 6):
+ *   s~_t = sum_h head_weights[r][h] * max(0, sum_j q[r][h][4j..4j+3] . C_j[c_t,j]).
+ * The C best tokens by s~ are candidates; ls_indexer_select with
+ * LS_CAND_TOKENS then scores them and the partial last page's tokens
+ * exactly and picks the final top-k ("Retrieving and refining candidates").
+ *
+ * codebooks: [32][256][4] bf16, 16-byte aligned.
+ * codes:     [key_pool.num_pages][page_size][32] uint8, 8-byte aligned: the
+ *            codes of token slot s of physical page p at codes[p][s].
+ * key_pool:  the fp8 indexer key pool (dtype LS_DTYPE_FP8_E4M3FN, num_heads
+ *            1, head_dim 128, page_size 16, 32 or 64).
+ */
+
+/* Codes of every token of the listed pages (pages as they fill). Nearest
+ * centroid by squared Euclidean distance computed in float64 in the order
+ * ((d0 d0 + d1 d1) + d2 d2) + d3 d3, d_t = x_t - c_t, each operation rounded
+ * once; ties to the lowest centroid. Pages outside [0, num_pages) are
+ * skipped. keys / key_scales as in ls_indexer_select (key_scales NULL: 1). */
+ls_status ls_pq_encode(const void* keys, const float* key_scales, ls_pool key_pool,
+                       const int32_t* page_ids, int32_t n_pages, const void* codebooks,
+                       uint8_t* codes, hipStream_t stream);
+
+/* Codebooks trained by k-means (Lloyd) on the tokens of the listed pages
+ * (offline; token i = slot i % page_size of page_ids[i / page_size]).
+ * Centroid c of subspace j starts as subvector j of token init_tokens[c]
+ * (device int32 [256]; zero for an entry outside [0, n_pages * page_size)),
+ * rounded to bf16; each of `iters` iterations encodes every token, then sets
+ * each centroid with members to their mean and keeps the others. The mean
+ * is order-independent: member values are summed as the integers
+ * rint(v * 2^24) (64-bit), and (sum / count) * 2^-24 (float64) is rounded
+ * once to bf16; sums must stay below 2^53 in magnitude (n_pages * page_size
+ * * max |x| < 2^29). codebooks is written (it is the iteration state).
+ * workspace: >= ls_pq_train_workspace_size() bytes, 256-byte aligned.
+ * iters: 0 .. 1000. */
+size_t ls_pq_train_workspace_size(void);
+ls_status ls_pq_train(const void* keys, const float* key_scales, ls_pool key_pool,
+                      const int32_t* page_ids, int32_t n_pages, const int32_t* init_tokens,
+                      int32_t iters, void* codebooks, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Coarse selection: per request, the n_candidates tokens of the complete
+ * pages with the largest s~ (ties to the lowest token), as token ids,
+ * ascending, in candidates[r][0 .. counts[r]-1]; -1 after. q / head_weights
+ * / batch as in ls_indexer_select. scores_out: NULL or
+ * [batch][ls_indexer_score_stride(LS_SEL_TOKENS, max_blocks * page_size)]
+ * fp32 (s~ at token t). workspace: >= ls_indexer_select_workspace_size(batch,
+ * LS_SEL_TOKENS, max_blocks * page_size) bytes. Three launches: zero, coarse
+ * scores + histogram, then the token top-k of ls_indexer_select. */
+ls_status ls_pq_select(const void* q, int32_t q_dtype, int32_t num_heads,
+                       const float* head_weights, const uint8_t* codes, const void* codebooks,
+                       ls_pool key_pool, ls_batch batch, int32_t n_candidates,
+                       int32_t* candidates, int32_t* candidate_counts, float* scores_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Introspection                                                             */

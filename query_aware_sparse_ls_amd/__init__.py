@@ -16,7 +16,8 @@ import torch
 
 from . import _lib
 from ._lib import (LS_AGG_MAX, LS_AGG_MEAN, LS_DTYPE_BF16, LS_DTYPE_FP32,  # noqa: F401
-                   LS_DTYPE_FP8_E4M3FN, LS_SCORE_BOUNDS, LS_SCORE_MEAN, LS_SEL_BLOCKS,
+                   LS_CAND_BLOCKS, LS_CAND_TOKENS, LS_DTYPE_FP8_E4M3FN, LS_SCORE_BOUNDS,
+                   LS_SCORE_MEAN, LS_SEL_BLOCKS,
                    LS_SEL_TOKENS, LsBatch, LsError,
                    LsIndexerParams, LsPool, LsSelectParams, check)
 
@@ -27,7 +28,7 @@ __all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_s
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
            "sparse_decode_step_workspace", "indexer_select", "indexer_select_workspace_size",
            "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
-           "mla_num_splits"]
+           "mla_num_splits", "pq_encode", "pq_train", "pq_select"]
 
 _DT = {torch.bfloat16: LS_DTYPE_BF16, torch.float32: LS_DTYPE_FP32,
        torch.float8_e4m3fn: LS_DTYPE_FP8_E4M3FN}
@@ -302,7 +303,7 @@ def indexer_select(q: torch.Tensor, head_weights: torch.Tensor, keys: torch.Tens
                    max_selected: int, key_scales: Optional[torch.Tensor] = None,
                    cand_blocks: Optional[torch.Tensor] = None,
                    cand_counts: Optional[torch.Tensor] = None,
-                   n_sink: int = 0, n_recent: int = 0,
+                   n_sink: int = 0, n_recent: int = 0, token_candidates: bool = False,
                    selected: Optional[torch.Tensor] = None,
                    selected_count: Optional[torch.Tensor] = None,
                    scores_out: Optional[torch.Tensor] = None,
@@ -330,13 +331,16 @@ def indexer_select(q: torch.Tensor, head_weights: torch.Tensor, keys: torch.Tens
         _need(key_scales, torch.float32)
     if scores_out is not None:
         _need(scores_out, torch.float32)
-    if tokens:
+    if tokens and token_candidates:
+        max_units = cand_cap + page_size
+    elif tokens:
         max_units = (cand_cap if cand_blocks is not None else batch.max_blocks) * page_size
     else:
         max_units = batch.max_blocks
     ws = _workspace(int(_L.ls_indexer_select_workspace_size(B, g, max_units)), dev, workspace)
     params = LsIndexerParams(C.sizeof(LsIndexerParams), g, int(topk), int(n_sink),
-                             int(n_recent), int(max_selected))
+                             int(n_recent), int(max_selected),
+                             LS_CAND_TOKENS if token_candidates else LS_CAND_BLOCKS)
     pool = LsPool(int(keys.shape[0]), 1, int(page_size), int(D), _DT[keys.dtype])
     check(_L.ls_indexer_select(q.data_ptr(), LS_DTYPE_BF16, int(H), head_weights.data_ptr(),
                                keys.data_ptr(), _ptr(key_scales), pool, batch.c(),
@@ -387,3 +391,81 @@ def sparse_mla_decode(q: torch.Tensor, latent: torch.Tensor, batch: PagedBatch,
                                   float(sm_scale), out.data_ptr(), _DT[out.dtype], _ptr(lse),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, lse
+
+
+# ------------------------------------------------------------------ PQ32
+
+def _fp8_pool(keys: torch.Tensor) -> LsPool:
+    return LsPool(int(keys.shape[0]), 1, int(keys.shape[1]), int(keys.shape[2]),
+                  LS_DTYPE_FP8_E4M3FN)
+
+
+def pq_encode(keys: torch.Tensor, key_scales: Optional[torch.Tensor], page_ids: torch.Tensor,
+              codebooks: torch.Tensor, codes: torch.Tensor, stream=None) -> torch.Tensor:
+    """PQ32 codes [pages][P][32] uint8 of every token of the listed pages
+    (nearest of 256 centroids per 4-dim subspace; codebooks bf16 [32][256][4])."""
+    _need(keys, torch.float8_e4m3fn); _need(page_ids, torch.int32)
+    _need(codebooks, torch.bfloat16); _need(codes, torch.uint8)
+    if key_scales is not None:
+        _need(key_scales, torch.float32)
+    check(_L.ls_pq_encode(keys.data_ptr(), _ptr(key_scales), _fp8_pool(keys), page_ids.data_ptr(),
+                          int(page_ids.numel()), codebooks.data_ptr(), codes.data_ptr(),
+                          _stream(stream)))
+    return codes
+
+
+def pq_train(keys: torch.Tensor, key_scales: Optional[torch.Tensor], page_ids: torch.Tensor,
+             init_tokens: torch.Tensor, iters: int, codebooks: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """k-means codebooks bf16 [32][256][4] over the tokens of the listed pages,
+    from centroids at the 256 tokens init_tokens (int32, indices into the
+    listed pages' tokens)."""
+    _need(keys, torch.float8_e4m3fn); _need(page_ids, torch.int32)
+    _need(init_tokens, torch.int32)
+    if init_tokens.numel() != 256:
+        raise ValueError("init_tokens must hold 256 token indices")
+    if key_scales is not None:
+        _need(key_scales, torch.float32)
+    dev = keys.device
+    if codebooks is None:
+        codebooks = torch.empty(32, 256, 4, dtype=torch.bfloat16, device=dev)
+    _need(codebooks, torch.bfloat16)
+    ws = torch.empty(int(_L.ls_pq_train_workspace_size()), dtype=torch.uint8, device=dev)
+    check(_L.ls_pq_train(keys.data_ptr(), _ptr(key_scales), _fp8_pool(keys), page_ids.data_ptr(),
+                         int(page_ids.numel()), init_tokens.data_ptr(), int(iters),
+                         codebooks.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return codebooks
+
+
+def pq_select(q: torch.Tensor, head_weights: torch.Tensor, codes: torch.Tensor,
+              codebooks: torch.Tensor, batch: PagedBatch, n_candidates: int, *,
+              candidates: Optional[torch.Tensor] = None,
+              counts: Optional[torch.Tensor] = None,
+              scores_out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The n_candidates tokens of each request's complete pages with the best
+    PQ coarse score sum_h w_h ReLU(q_h . decoded key), ascending token ids.
+    codes: [pages][P][32] uint8. Returns (candidates [B][n], counts [B])."""
+    _need(q, torch.bfloat16); _need(head_weights, torch.float32)
+    _need(codes, torch.uint8); _need(codebooks, torch.bfloat16)
+    B, H, D = q.shape
+    dev = q.device
+    if candidates is None:
+        candidates = torch.empty(B, max(1, n_candidates), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(candidates, torch.int32); _need(counts, torch.int32)
+    if scores_out is not None:
+        _need(scores_out, torch.float32)
+    P = int(codes.shape[1])
+    max_units = batch.max_blocks * P
+    ws = _workspace(int(_L.ls_indexer_select_workspace_size(B, LS_SEL_TOKENS, max_units)), dev,
+                    workspace)
+    pool = LsPool(int(codes.shape[0]), 1, P, 128, LS_DTYPE_FP8_E4M3FN)
+    check(_L.ls_pq_select(q.data_ptr(), LS_DTYPE_BF16, int(H), head_weights.data_ptr(),
+                          codes.data_ptr(), codebooks.data_ptr(), pool, batch.c(),
+                          int(n_candidates), candidates.data_ptr(), counts.data_ptr(),
+                          _ptr(scores_out), ws.data_ptr(), ws.numel() * ws.element_size(),
+                          _stream(stream)))
+    return candidates, counts

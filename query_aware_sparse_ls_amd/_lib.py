@@ -13,6 +13,7 @@ LS_DTYPE_BF16, LS_DTYPE_FP32, LS_DTYPE_FP8_E4M3FN = 1, 2, 3
 LS_AGG_MAX, LS_AGG_MEAN = 0, 1
 LS_SEL_TOKENS, LS_SEL_BLOCKS = 0, 1
 LS_SCORE_MEAN, LS_SCORE_BOUNDS = 0, 1
+LS_CAND_BLOCKS, LS_CAND_TOKENS = 0, 1
 
 # every function the header declares, with its ctypes signature
 EXPORTS = {}
@@ -37,7 +38,8 @@ class LsSelectParams(C.Structure):
 
 class LsIndexerParams(C.Structure):
     _fields_ = [("struct_size", C.c_int32), ("granularity", C.c_int32), ("topk", C.c_int32),
-                ("n_sink", C.c_int32), ("n_recent", C.c_int32), ("max_selected", C.c_int32)]
+                ("n_sink", C.c_int32), ("n_recent", C.c_int32), ("max_selected", C.c_int32),
+                ("candidates", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -65,6 +67,12 @@ _SIGS = {
     "ls_sparse_mla_decode": (C.c_int, [_P, C.c_int32, C.c_int32, _P, LsPool, LsBatch, _P, _P,
                                        C.c_int32, C.c_float, _P, C.c_int32, _P, _P, C.c_size_t,
                                        _P]),
+    "ls_pq_encode": (C.c_int, [_P, _P, LsPool, _P, C.c_int32, _P, _P, _P]),
+    "ls_pq_train_workspace_size": (C.c_size_t, []),
+    "ls_pq_train": (C.c_int, [_P, _P, LsPool, _P, C.c_int32, _P, C.c_int32, _P, _P, C.c_size_t,
+                              _P]),
+    "ls_pq_select": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, LsPool, LsBatch, C.c_int32,
+                               _P, _P, _P, _P, C.c_size_t, _P]),
     "ls_last_error": (C.c_char_p, []),
     "ls_version": (C.c_char_p, []),
     "ls_attn_num_splits": (C.c_int32, [C.c_int32]),

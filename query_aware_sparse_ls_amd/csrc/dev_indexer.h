@@ -54,10 +54,14 @@ constexpr int kIdxMaxWords = kIdxMaxUnits / 32;
 // [0, L); with candidates, n_c blocks of P units each (unit u = slot u % P of
 // candidate block u / P), valid when the block id is valid and the token is
 // cached.
+// With token candidates (unit_kind kUnitsTokenCands) unit u < n_c is token
+// cand[u] and unit n_c + i is token tail0 + i of the partial last page; with
+// kUnitsComplete the units are the tokens [0, tail0) of the complete pages.
 struct IdxUnits {
   int n;          // units (valid or not) of the request
   int L, nb, page_base;
   int ncand;      // -1: no candidate list
+  int tail0;      // first token of the partial last page (= L when none)
 };
 
 __device__ __forceinline__ IdxUnits idx_units(const IndexerArgs& a, int r) {
@@ -66,7 +70,16 @@ __device__ __forceinline__ IdxUnits idx_units(const IndexerArgs& a, int r) {
   u.L = geo.L;
   u.nb = geo.nb;
   u.page_base = geo.page_base;
-  if (a.cand_blocks) {
+  u.tail0 = geo.L & ~(a.b.page_size - 1);   // a power of two
+  if (a.unit_kind == kUnitsTokenCands) {
+    int c = a.cand_counts[r];
+    c = c < 0 ? 0 : (c > a.cand_cap ? a.cand_cap : c);
+    u.ncand = c;
+    u.n = c + (geo.L - u.tail0);
+  } else if (a.unit_kind == kUnitsComplete) {
+    u.ncand = -1;
+    u.n = u.tail0;
+  } else if (a.cand_blocks) {
     int c = a.cand_counts[r];
     c = c < 0 ? 0 : (c > a.cand_cap ? a.cand_cap : c);
     u.ncand = c;
@@ -84,6 +97,12 @@ __device__ __forceinline__ int idx_unit_block(const IndexerArgs& a, const IdxUni
                                               int u, int* token) {
   const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);   // a power of two
   if (u < 0 || u >= g.n) return -1;
+  if (a.unit_kind == kUnitsTokenCands) {
+    const int t = u < g.ncand ? a.cand_blocks[(size_t)r * a.cand_cap + u] : g.tail0 + (u - g.ncand);
+    if (t < 0 || t >= g.L) return -1;
+    *token = t;
+    return t >> PS;
+  }
   int blk;
   if (g.ncand < 0) {
     blk = u >> PS;

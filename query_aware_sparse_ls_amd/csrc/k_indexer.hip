@@ -39,8 +39,9 @@ template <int MODE, int NHT>
 struct IdxScoreLds {
   alignas(16) uint32_t tiles[MODE == kIdxTokens ? 1 : kIdxWaves][2][16 * IdxTile<MODE>::RW];
   uint4 q[NHT][4][kWave];   // the q operand, in lane order (one 16-byte read per lane)
-  // page ids of the workgroup's blocks: one per 16+ tokens, one per block
-  int pg[MODE == kIdxTokens ? kIdxMaxTilesPerWg + 1 : kIdxMaxTilesPerWg * 16];
+  // page ids of the workgroup's blocks (one per 16+ tokens, one per block),
+  // or with token candidates the key row of every unit
+  int pg[kIdxMaxTilesPerWg * 16];
   uint32_t hist[MODE == kIdxTokens ? kIdxBins : 1];
 };
 
@@ -76,7 +77,29 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
   // page ids of the workgroup's blocks (-1: no unit of this block is scored)
   const int bi0 = MODE == kIdxTokens ? u0 >> PS : u0;
   const int npg = MODE == kIdxTokens ? (upw + P - 1) >> PS : upw;
-  for (int i = tid; i < npg; i += kIdxThreads) {
+  const bool tok_cands = MODE == kIdxTokens && a.unit_kind == kUnitsTokenCands;
+  if (tok_cands) {
+    // key row (page * P + slot) of each unit: -1 not a token, -2 bad page;
+    // every thread's loads issued before the dependent ones
+    constexpr int NPT = kIdxMaxTilesPerWg * 16 / kIdxThreads;
+    int tok[NPT], blk[NPT], pgid[NPT];
+#pragma unroll
+    for (int m = 0; m < NPT; ++m) {
+      const int i = tid + m * kIdxThreads;
+      blk[m] = i < upw ? idx_unit_block(a, gu, r, u0 + i, &tok[m]) : -1;
+    }
+#pragma unroll
+    for (int m = 0; m < NPT; ++m) pgid[m] = blk[m] >= 0 ? a.b.indices[gu.page_base + blk[m]] : -1;
+#pragma unroll
+    for (int m = 0; m < NPT; ++m) {
+      const int i = tid + m * kIdxThreads;
+      if (i < upw)
+        sh.pg[i] = blk[m] < 0 ? -1
+                 : (pgid[m] >= 0 && pgid[m] < a.b.num_pages) ? pgid[m] * P + (tok[m] & (P - 1))
+                                                              : -2;
+    }
+  }
+  for (int i = tid; i < npg && !tok_cands; i += kIdxThreads) {
     const int bi = bi0 + i;
     int page = -1;
     if constexpr (MODE == kIdxTokens) {
@@ -157,13 +180,21 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
     badm = 0;
     if constexpr (MODE == kIdxTokens) {
       // this lane's own unit (col) of the wave's k-th tile, both halves
-      const int u = u0 + 16 * (wave + kIdxWaves * k) + col;
-      const int page = k < ntw ? sh.pg[(u >> PS) - bi0] : -1;
-      badm = page == -2 ? 0x3u : 0u;
-      const uint8_t* rowp =
-          kbase + ((size_t)(uint32_t)(page >= 0 ? page : 0) * P + (u & (P - 1))) * kIdxDim;
+      const int ul = 16 * (wave + kIdxWaves * k) + col, u = u0 + ul;
+      size_t row;
+      if (tok_cands) {
+        const int kr = k < ntw ? sh.pg[ul] : -1;
+        badm = kr == -2 ? 0x3u : 0u;
+        row = (size_t)(uint32_t)(kr >= 0 ? kr : 0);
+      } else {
+        const int page = k < ntw ? sh.pg[(u >> PS) - bi0] : -1;
+        badm = page == -2 ? 0x3u : 0u;
+        row = (size_t)(uint32_t)(page >= 0 ? page : 0) * P + (u & (P - 1));
+      }
+      const uint8_t* rowp = kbase + (size_t)row * kIdxDim;
       d[0] = ldg16_stream(rowp + 16 * kq);
       d[1] = ldg16_stream(rowp + 64 + 16 * kq);
+      sig = a.scales ? a.scales[row] : 1.0f;
     } else {
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
@@ -173,15 +204,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
         d[j] = ldg16(kbase + off + 16 * (lane % T::LPR));
       }
     }
-    sig = 1.0f;
-    if constexpr (MODE == kIdxTokens) {
-      if (a.scales) {
-        const int t = wave + kIdxWaves * k;
-        const int u = u0 + 16 * t + col;
-        const int page = k < ntw ? sh.pg[(u >> PS) - bi0] : -1;
-        sig = a.scales[(size_t)(uint32_t)(page >= 0 ? page : 0) * P + (u & (P - 1))];
-      }
-    }
+    if constexpr (MODE != kIdxTokens) sig = 1.0f;
   };
 
   uint4 buf[NS][NL];
@@ -358,6 +381,8 @@ __device__ __forceinline__ void idx_find_digit(const uint32_t* h, int nbins, int
 
 __device__ __forceinline__ int idx_token_of(const IndexerArgs& a, const IdxUnits& g, int r,
                                            int u) {
+  if (a.unit_kind == kUnitsTokenCands)
+    return u < g.ncand ? a.cand_blocks[(size_t)r * a.cand_cap + u] : g.tail0 + (u - g.ncand);
   if (g.ncand < 0) return u;
   const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);
   return a.cand_blocks[(size_t)r * a.cand_cap + (u >> PS)] * P + (u & (P - 1));
@@ -525,7 +550,7 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   for (int w = tid; w < nwr; w += kIdxMarkThreads) sh.tie[w] = 0u;
   // the candidate blocks (unit -> token map), in LDS when they fit (h2 is
   // free from here on)
-  const bool cand_lds = g.ncand >= 0 && g.ncand <= kIdxBins;
+  const bool cand_lds = a.unit_kind == kUnitsDefault && g.ncand >= 0 && g.ncand <= kIdxBins;
   if (cand_lds)
     idx_copy_in<kIdxBins / kIdxMarkThreads>(
         sh.h2, reinterpret_cast<const uint32_t*>(a.cand_blocks + (size_t)r * a.cand_cap), g.ncand);
@@ -649,16 +674,24 @@ hipError_t launch_indexer_score(const IndexerArgs& a, int mode, hipStream_t st) 
                             : launch_score_mode<kIdxBlocks>(a, st);
 }
 
-hipError_t launch_indexer_token_select(const IndexerArgs& a, hipStream_t st) {
+hipError_t launch_indexer_zero(const IndexerArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(idx_zero_kernel, dim3(16), dim3(kIdxThreads), 0, st, a.hist, a.ctl,
                      a.b.batch);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_score_mode<kIdxTokens>(a, st);
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_mark(const IndexerArgs& a, hipStream_t st) {
   dim3 grid((a.max_units + kIdxMarkUnits - 1) / kIdxMarkUnits, a.b.batch);
   hipLaunchKernelGGL(idx_mark_kernel, grid, dim3(kIdxMarkThreads), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_indexer_token_select(const IndexerArgs& a, hipStream_t st) {
+  hipError_t e = launch_indexer_zero(a, st);
+  if (e != hipSuccess) return e;
+  e = launch_score_mode<kIdxTokens>(a, st);
+  if (e != hipSuccess) return e;
+  return launch_indexer_mark(a, st);
 }
 
 }  // namespace ls

@@ -1,0 +1,347 @@
+// PQ32 codes of indexer keys and coarse scoring from them (LeanSparse §5,
+// "Approximate scoring with PQ", Eq. 6).
+//
+// A 128-dim indexer key x = scale * fp8 is cut into 32 subvectors of 4 dims;
+// each is stored as the one-byte index of its nearest centroid in that
+// subspace's codebook of 256 bf16 centroids ([32][256][4] bf16, 64 KB).
+//
+// Encoding decides an integer from floating point, so the distance is fixed
+// to the bit: float64, d_t = x_t - c_t, ((d0 d0 + d1 d1) + d2 d2) + d3 d3 with
+// every operation rounded once (no contraction), ties to the lowest centroid.
+// x_t is exact in float64 (a 24-bit scale times a 4-bit fp8 value).
+//
+// Codebook training is Lloyd's k-means with order-independent means: each
+// member value v is added as the integer rint(v * 2^24) with 64-bit integer
+// atomics (first within the workgroup in LDS, then into global sums), so the
+// sums, and the means (sum / count) * 2^-24 rounded once to bf16, do not
+// depend on the order of the additions.
+//
+// Coarse scoring reads 32 bytes of codes per token instead of 128 + 4 bytes
+// of fp8 key and scale. The 64 KB codebook sits in LDS; a lane rebuilds its
+// slice of the MFMA B operand (key^T) from 8 code bytes: k-step s of lane
+// group kq covers dims 32 kq + 8 s .. + 8, i.e. subspaces 8 kq + 2 s and
+// 8 kq + 2 s + 1, one 8-byte LDS read each. The rest (weighted ReLU over the
+// heads, first-digit histogram, mark + finish) is the token top-k of the
+// learned indexer.
+#include "dev_indexer.h"
+#include "dev_mfma.h"
+
+namespace ls {
+
+// Key token i of the listed pages: its row (page * P + slot), or -1.
+__device__ __forceinline__ long long pq_key_row(const PqArgs& a, long long i) {
+  const int P = a.page_size;
+  if (i < 0 || i >= (long long)a.n_pages * P) return -1;
+  const int page = a.page_ids[i / P];
+  if (page < 0 || page >= a.num_pages) return -1;
+  return (long long)page * P + (int)(i % P);
+}
+
+// Subvector j of key row `row`, exact in float64.
+__device__ __forceinline__ void pq_subvector(const PqArgs& a, long long row, int j, double x[4]) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(a.keys + row * 128 + 4 * j);
+  const double sc = a.scales ? (double)a.scales[row] : 1.0;
+  const uint32_t lo = fp8x2_to_bf16x2(w, false), hi = fp8x2_to_bf16x2(w, true);
+  x[0] = sc * (double)__uint_as_float(lo << 16);
+  x[1] = sc * (double)__uint_as_float(lo & 0xffff0000u);
+  x[2] = sc * (double)__uint_as_float(hi << 16);
+  x[3] = sc * (double)__uint_as_float(hi & 0xffff0000u);
+}
+
+// Nearest centroid of x among cb[0..255] (float64 rows in LDS).
+__device__ __forceinline__ int pq_nearest(const double x[4], const double (*cb)[4]) {
+#pragma clang fp contract(off)
+  double best = __builtin_huge_val();
+  int arg = 0;
+  for (int c = 0; c < kPqCent; ++c) {
+    const double d0 = x[0] - cb[c][0], d1 = x[1] - cb[c][1];
+    const double d2 = x[2] - cb[c][2], d3 = x[3] - cb[c][3];
+    const double dist = ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
+    if (dist < best) {
+      best = dist;
+      arg = c;
+    }
+  }
+  return arg;
+}
+
+// One thread per listed token, one subspace per grid row: the code, and
+// (training) the fixed-point sums and counts of the chosen centroids.
+__global__ __launch_bounds__(256) void pq_assign_kernel(PqArgs a) {
+  __shared__ double cb[kPqCent][4];
+  __shared__ unsigned long long s_sum[kPqCent][4];
+  __shared__ uint32_t s_cnt[kPqCent];
+  const int j = blockIdx.y, tid = threadIdx.x;
+  {
+    const uint2 c = *reinterpret_cast<const uint2*>(a.codebooks + ((size_t)j * kPqCent + tid) * 4);
+    cb[tid][0] = (double)__uint_as_float(c.x << 16);
+    cb[tid][1] = (double)__uint_as_float(c.x & 0xffff0000u);
+    cb[tid][2] = (double)__uint_as_float(c.y << 16);
+    cb[tid][3] = (double)__uint_as_float(c.y & 0xffff0000u);
+    if (a.sums) {
+      s_sum[tid][0] = s_sum[tid][1] = s_sum[tid][2] = s_sum[tid][3] = 0ull;
+      s_cnt[tid] = 0u;
+    }
+  }
+  __syncthreads();
+  const long long i = (long long)blockIdx.x * 256 + tid;
+  const long long row = pq_key_row(a, i);
+  if (row >= 0) {
+    double x[4];
+    pq_subvector(a, row, j, x);
+    const int c = pq_nearest(x, cb);
+    if (a.codes) a.codes[row * kPqSub + j] = (uint8_t)c;
+    if (a.sums) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const long long v = (long long)rint(x[t] * (double)(1 << kPqFixedBits));
+        atomicAdd(&s_sum[c][t], (unsigned long long)v);   // two's complement: a signed sum
+      }
+      atomicAdd(&s_cnt[c], 1u);
+    }
+  }
+  if (a.sums) {
+    __syncthreads();
+    const uint32_t n = s_cnt[tid];
+    if (n) {
+      atomicAdd(a.counts + (size_t)j * kPqCent + tid, n);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        atomicAdd(a.sums + ((size_t)j * kPqCent + tid) * 4 + t, s_sum[tid][t]);
+    }
+  }
+}
+
+// Centroid c of subspace j = subvector j of listed token init[c], rounded
+// to bf16 (zero for an init token outside the listed pages); sums and
+// counts cleared.
+__global__ __launch_bounds__(256) void pq_init_kernel(PqArgs a, const int32_t* init) {
+  const int j = blockIdx.x, c = threadIdx.x;
+  const long long row = pq_key_row(a, init[c]);
+  double x[4] = {0.0, 0.0, 0.0, 0.0};
+  if (row >= 0) pq_subvector(a, row, j, x);
+  uint16_t* o = a.codebooks + ((size_t)j * kPqCent + c) * 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    o[t] = f64_to_bf16_rne(x[t]);
+    a.sums[((size_t)j * kPqCent + c) * 4 + t] = 0ull;
+  }
+  a.counts[(size_t)j * kPqCent + c] = 0u;
+}
+
+// Centroids with members become their fixed-point mean; sums and counts are
+// cleared for the next iteration.
+__global__ __launch_bounds__(256) void pq_update_kernel(PqArgs a) {
+  const int j = blockIdx.x, c = threadIdx.x;
+  const size_t e = (size_t)j * kPqCent + c;
+  const uint32_t n = a.counts[e];
+  if (n) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const long long s = (long long)a.sums[e * 4 + t];
+      const double m = ((double)s / (double)n) * (1.0 / (double)(1 << kPqFixedBits));
+      a.codebooks[e * 4 + t] = f64_to_bf16_rne(m);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) a.sums[e * 4 + t] = 0ull;
+  a.counts[e] = 0u;
+}
+
+hipError_t launch_pq_encode(const PqArgs& a, hipStream_t st) {
+  const long long n = (long long)a.n_pages * a.page_size;
+  PqArgs e = a;
+  e.sums = nullptr;
+  e.counts = nullptr;
+  hipLaunchKernelGGL(pq_assign_kernel, dim3((unsigned)((n + 255) / 256), kPqSub), dim3(256), 0,
+                     st, e);
+  return hipGetLastError();
+}
+
+hipError_t launch_pq_train(const PqArgs& a, const int32_t* init_tokens, int iters,
+                           hipStream_t st) {
+  const long long n = (long long)a.n_pages * a.page_size;
+  hipLaunchKernelGGL(pq_init_kernel, dim3(kPqSub), dim3(kPqCent), 0, st, a, init_tokens);
+  hipError_t e = hipGetLastError();
+  PqArgs t = a;
+  t.codes = nullptr;
+  for (int it = 0; it < iters && e == hipSuccess; ++it) {
+    hipLaunchKernelGGL(pq_assign_kernel, dim3((unsigned)((n + 255) / 256), kPqSub), dim3(256),
+                       0, st, t);
+    e = hipGetLastError();
+    if (e != hipSuccess) break;
+    hipLaunchKernelGGL(pq_update_kernel, dim3(kPqSub), dim3(kPqCent), 0, st, t);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// ------------------------------------------------------- coarse scoring ----
+
+template <int NHT>
+struct PqScoreLds {
+  union {
+    uint4 q[NHT][4][kWave];            // the q operand, staged once
+    uint2 cb[kPqSub * kPqCent];        // the codebook (4 bf16 per centroid)
+  } u;
+  uint32_t hist[kIdxBins / 2];         // first-digit counts, two 16-bit bins per word
+  int pg[kIdxMaxTilesPerWg + 1];       // page ids of the workgroup's blocks
+};
+
+template <int NHT>
+__global__ __launch_bounds__(kIdxThreads, 2) void pq_score_kernel(IndexerArgs a) {
+  constexpr int NS = kIdxPrefetch, H = 16 * NHT;
+  __shared__ PqScoreLds<NHT> sh;
+  const int r = blockIdx.y, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);
+  const int upw = a.tiles_per_wg * 16;
+  const int u0 = blockIdx.x * upw;
+  const IdxUnits gu = idx_units(a, r);   // the complete pages' tokens
+  if (u0 >= gu.n) return;
+
+  const int bi0 = u0 >> PS;
+  const int npg = (upw + P - 1) >> PS;
+  for (int i = tid; i < npg; i += kIdxThreads) {
+    const int blk = bi0 + i;
+    int page = -1;
+    if (blk < gu.nb) {
+      const int p = a.b.indices[gu.page_base + blk];
+      page = (p >= 0 && p < a.b.num_pages) ? p : -2;   // -2: bad page id, scores 0
+    }
+    sh.pg[i] = page;
+  }
+  for (int i = tid; i < kIdxBins / 2; i += kIdxThreads) sh.hist[i] = 0u;
+
+  // q as the A operand (rows = heads 16 ht + col, k-step s of lane group kq
+  // = dims 32 kq + 8 s .. + 8), through LDS into registers
+  float wv[NHT][4];
+  {
+    constexpr int NQ = NHT * 4 * kWave / kIdxThreads;
+    uint4 qv[NQ];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const int e = tid + m * kIdxThreads;
+      const int ht = e / (4 * kWave), s = (e / kWave) % 4, ln = e % kWave;
+      qv[m] = ldg16(a.q + ((size_t)r * H + 16 * ht + (ln & 15)) * kIdxDim + 32 * (ln >> 4) + 8 * s);
+    }
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const int e = tid + m * kIdxThreads;
+      sh.u.q[e / (4 * kWave)][(e / kWave) % 4][e % kWave] = qv[m];
+    }
+  }
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)r * H + 16 * ht + 4 * kq + i];
+  __syncthreads();
+  uint4 qr[NHT][4];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) qr[ht][s2] = sh.u.q[ht][s2][lane];
+  __syncthreads();
+  {
+    // the codebook: 4,096 16-byte pieces, every load of a thread issued first
+    constexpr int NC = kPqSub * kPqCent * 8 / 16 / kIdxThreads;
+    const uint4* src = reinterpret_cast<const uint4*>(a.codebooks);
+    uint4 cv[NC];
+#pragma unroll
+    for (int m = 0; m < NC; ++m) cv[m] = ldg16(src + tid + m * kIdxThreads);
+    uint4* dst = reinterpret_cast<uint4*>(sh.u.cb);
+#pragma unroll
+    for (int m = 0; m < NC; ++m) dst[tid + m * kIdxThreads] = cv[m];
+  }
+  __syncthreads();
+
+  const int ntw = a.tiles_per_wg / kIdxWaves;
+  float* srow = a.scores + (size_t)r * a.max_units + u0;
+  const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.keys);
+  auto issue = [&](int k, uint2& d, bool& bad) {
+    const int u = u0 + 16 * (wave + kIdxWaves * k) + col;
+    const int page = k < ntw ? sh.pg[(u >> PS) - bi0] : -1;
+    bad = page == -2;
+    const size_t row = (size_t)(uint32_t)(page >= 0 ? page : 0) * P + (u & (P - 1));
+    d = *reinterpret_cast<const uint2*>(codes + row * kPqSub + 8 * kq);
+  };
+  uint2 buf[NS];
+  bool bad[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    issue(s, buf[s], bad[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int k0 = 0; k0 < ntw; k0 += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int k = k0 + s;
+      const uint2 c = buf[s];
+      const bool bd = bad[s];
+      __builtin_amdgcn_sched_barrier(0);
+      issue(k + NS, buf[s], bad[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k < ntw) {
+        uint4 kb[4];
+        const uint32_t cw[2] = {c.x, c.y};
+        const int jb = 8 * kq;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const uint32_t w = cw[s2 >> 1] >> (16 * (s2 & 1));
+          const uint2 e0 = sh.u.cb[(jb + 2 * s2) * kPqCent + (w & 0xffu)];
+          const uint2 e1 = sh.u.cb[(jb + 2 * s2 + 1) * kPqCent + ((w >> 8) & 0xffu)];
+          kb[s2] = bd ? make_uint4(0, 0, 0, 0) : make_uint4(e0.x, e0.y, e1.x, e1.y);
+        }
+        f32x4_t acc[NHT];
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          acc[ht] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) acc[ht] = mfma_16x16x32(qr[ht][s2], kb[s2], acc[ht]);
+        }
+        float v = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v = fmaf(wv[ht][i], relu_bits(acc[ht][i]), v);
+        v = xor_pair_sum<16>(v);
+        v = xor_pair_sum<32>(v);
+        v += 0.0f;   // -0 -> +0: equal scores get equal keys
+        if (kq == 0) {
+          const int ul = 16 * (wave + kIdxWaves * k) + col;
+          int tok;
+          const bool valid = idx_unit_block(a, gu, r, u0 + ul, &tok) >= 0;
+          if (valid) {
+            const uint32_t bin = idx_bin(score_key(v));
+            atomicAdd(&sh.hist[bin >> 1], 1u << (16 * (bin & 1u)));
+          }
+          if (u0 + ul < gu.n) srow[ul] = valid ? v : 0.0f;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)r * kIdxBins;
+  for (int i = tid; i < kIdxBins / 2; i += kIdxThreads) {
+    const uint32_t c = sh.hist[i];
+    if (c & 0xffffu) atomicAdd(gh + 2 * i, c & 0xffffu);
+    if (c >> 16) atomicAdd(gh + 2 * i + 1, c >> 16);
+  }
+}
+
+hipError_t launch_pq_select(const IndexerArgs& a, hipStream_t st) {
+  hipError_t e = launch_indexer_zero(a, st);
+  if (e != hipSuccess) return e;
+  const int upw = a.tiles_per_wg * 16;
+  dim3 grid((a.max_units + upw - 1) / upw, a.b.batch);
+  switch (a.num_heads) {
+    case 16: hipLaunchKernelGGL((pq_score_kernel<1>), grid, dim3(kIdxThreads), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((pq_score_kernel<2>), grid, dim3(kIdxThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((pq_score_kernel<4>), grid, dim3(kIdxThreads), 0, st, a); break;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_indexer_mark(a, st);
+}
+
+}  // namespace ls

@@ -158,7 +158,7 @@ extern "C" {
 
 const char* ls_last_error(void) { return g_err; }
 
-const char* ls_version(void) { return "libls 0.3.0 abi 3 gfx950"; }
+const char* ls_version(void) { return "libls 0.4.0 abi 4 gfx950"; }
 
 int32_t ls_attn_num_splits(int32_t max_selected) {
   if (max_selected < 1) return 1;
@@ -519,6 +519,14 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
                 key_pool.page_size);
   if (p->topk < 0) return fail(LS_ERR_INVALID, "topk %d must be >= 0", p->topk);
   if (p->n_sink < 0 || p->n_recent < 0) return fail(LS_ERR_INVALID, "n_sink/n_recent < 0");
+  if (p->candidates != LS_CAND_BLOCKS && p->candidates != LS_CAND_TOKENS)
+    return fail(LS_ERR_INVALID, "candidates %d (LS_CAND_BLOCKS or LS_CAND_TOKENS)",
+                p->candidates);
+  const bool tok_cands = p->candidates == LS_CAND_TOKENS;
+  if (tok_cands && (!tokens || !cand_blocks))
+    return fail(LS_ERR_INVALID, "LS_CAND_TOKENS needs LS_SEL_TOKENS and a candidate list");
+  if (tok_cands && (long long)key_pool.num_pages * key_pool.page_size >= (1ll << 31))
+    return fail(LS_ERR_UNSUPPORTED, "LS_CAND_TOKENS needs num_pages * page_size < 2^31");
   int max_units;
   if (tokens) {
     if (key_pool.dtype != LS_DTYPE_FP8_E4M3FN)
@@ -528,7 +536,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
     if (cand_blocks) {
       if (!cand_counts || cand_cap < 1)
         return fail(LS_ERR_INVALID, "cand_blocks needs cand_counts and cand_cap >= 1");
-      max_units = cand_cap * key_pool.page_size;
+      max_units = tok_cands ? cand_cap + key_pool.page_size : cand_cap * key_pool.page_size;
     } else {
       max_units = batch.max_blocks * key_pool.page_size;
     }
@@ -575,6 +583,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
   a.cand_blocks = cand_blocks;
   a.cand_counts = cand_counts;
   a.cand_cap = cand_cap;
+  a.unit_kind = tok_cands ? ls::kUnitsTokenCands : ls::kUnitsDefault;
   a.max_units = U;
   a.n_sink = p->n_sink;
   a.n_recent = p->n_recent;
@@ -680,6 +689,138 @@ ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_hea
   a.out_dtype = out_dtype;
   a.lse = lse_out;
   return hip_status(ls::launch_mla(a, stream), "MLA kernel launches");
+}
+
+
+// ------------------------------------------------------------------ PQ32 ----
+
+namespace {
+
+ls_status check_pq_pool(const ls_pool& key_pool) {
+  if (key_pool.num_pages < 1) return fail(LS_ERR_INVALID, "key_pool.num_pages must be >= 1");
+  if (key_pool.num_heads != 1 || key_pool.head_dim != 128)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool: num_heads 1 and head_dim 128 (got %d, %d)",
+                key_pool.num_heads, key_pool.head_dim);
+  if (key_pool.page_size != 16 && key_pool.page_size != 32 && key_pool.page_size != 64)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.page_size %d (supported: 16, 32, 64)",
+                key_pool.page_size);
+  if (key_pool.dtype != LS_DTYPE_FP8_E4M3FN)
+    return fail(LS_ERR_UNSUPPORTED, "key_pool.dtype must be fp8_e4m3fn");
+  return LS_OK;
+}
+
+}  // namespace
+
+ls_status ls_pq_encode(const void* keys, const float* key_scales, ls_pool key_pool,
+                       const int32_t* page_ids, int32_t n_pages, const void* codebooks,
+                       uint8_t* codes, hipStream_t stream) {
+  ls_status st = check_pq_pool(key_pool);
+  if (st != LS_OK) return st;
+  if (n_pages < 0) return fail(LS_ERR_INVALID, "n_pages < 0");
+  if (n_pages == 0) return ok();
+  if (!keys || !page_ids || !codebooks || !codes)
+    return fail(LS_ERR_INVALID, "keys, page_ids, codebooks and codes must be non-null");
+  if ((uintptr_t)keys % 4 || (uintptr_t)codebooks % 16)
+    return fail(LS_ERR_INVALID, "keys must be 4-byte and codebooks 16-byte aligned");
+  ls::PqArgs a{static_cast<const uint8_t*>(keys), key_scales, key_pool.num_pages,
+               key_pool.page_size, page_ids, n_pages,
+               const_cast<uint16_t*>(static_cast<const uint16_t*>(codebooks)), codes, nullptr,
+               nullptr};
+  return hip_status(ls::launch_pq_encode(a, stream), "PQ encode launch");
+}
+
+size_t ls_pq_train_workspace_size(void) {
+  return align_up((size_t)ls::kPqSub * ls::kPqCent * ls::kPqDim * sizeof(unsigned long long)) +
+         align_up((size_t)ls::kPqSub * ls::kPqCent * sizeof(uint32_t));
+}
+
+ls_status ls_pq_train(const void* keys, const float* key_scales, ls_pool key_pool,
+                      const int32_t* page_ids, int32_t n_pages, const int32_t* init_tokens,
+                      int32_t iters, void* codebooks, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  ls_status st = check_pq_pool(key_pool);
+  if (st != LS_OK) return st;
+  if (n_pages < 1) return fail(LS_ERR_INVALID, "n_pages must be >= 1");
+  if (iters < 0 || iters > 1000) return fail(LS_ERR_INVALID, "iters %d (0 .. 1000)", iters);
+  if ((long long)n_pages * key_pool.page_size > (1ll << 31) - 1)
+    return fail(LS_ERR_UNSUPPORTED, "more than 2^31 - 1 training tokens");
+  if (!keys || !page_ids || !init_tokens || !codebooks)
+    return fail(LS_ERR_INVALID, "keys, page_ids, init_tokens and codebooks must be non-null");
+  if ((uintptr_t)keys % 4 || (uintptr_t)codebooks % 16)
+    return fail(LS_ERR_INVALID, "keys must be 4-byte and codebooks 16-byte aligned");
+  if (!workspace || workspace_bytes < ls_pq_train_workspace_size())
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                ls_pq_train_workspace_size());
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  char* w = static_cast<char*>(workspace);
+  auto* sums = reinterpret_cast<unsigned long long*>(w);
+  auto* counts = reinterpret_cast<uint32_t*>(
+      w + align_up((size_t)ls::kPqSub * ls::kPqCent * ls::kPqDim * sizeof(unsigned long long)));
+  ls::PqArgs a{static_cast<const uint8_t*>(keys), key_scales, key_pool.num_pages,
+               key_pool.page_size, page_ids, n_pages, static_cast<uint16_t*>(codebooks), nullptr,
+               sums, counts};
+  return hip_status(ls::launch_pq_train(a, init_tokens, iters, stream), "PQ training launches");
+}
+
+ls_status ls_pq_select(const void* q, int32_t q_dtype, int32_t num_heads,
+                       const float* head_weights, const uint8_t* codes, const void* codebooks,
+                       ls_pool key_pool, ls_batch batch, int32_t n_candidates,
+                       int32_t* candidates, int32_t* candidate_counts, float* scores_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  st = check_pq_pool(key_pool);
+  if (st != LS_OK) return st;
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (num_heads != 16 && num_heads != 32 && num_heads != 64)
+    return fail(LS_ERR_UNSUPPORTED, "num_heads %d (supported: 16, 32, 64)", num_heads);
+  if (n_candidates < 0) return fail(LS_ERR_INVALID, "n_candidates %d must be >= 0", n_candidates);
+  const long long mu = (long long)batch.max_blocks * key_pool.page_size;
+  if (batch.batch_size > 0 && (mu < 1 || mu > ls::kIdxMaxUnits))
+    return fail(LS_ERR_UNSUPPORTED, "%lld tokens per request (supported: <= %d)", mu,
+                ls::kIdxMaxUnits);
+  if (batch.batch_size == 0) return ok();
+  if (!q || !head_weights || !codes || !codebooks || !candidates || !candidate_counts)
+    return fail(LS_ERR_INVALID,
+                "q, head_weights, codes, codebooks, candidates and counts must be non-null");
+  if (!aligned16(q) || (uintptr_t)codebooks % 16 || (uintptr_t)codes % 8)
+    return fail(LS_ERR_INVALID, "q and codebooks must be 16-byte, codes 8-byte aligned");
+  const int max_units = (int)mu;
+  const size_t ws = ls_indexer_select_workspace_size(batch.batch_size, LS_SEL_TOKENS, max_units);
+  if (!workspace || workspace_bytes < ws)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  const size_t B = (size_t)batch.batch_size;
+  const int U = ls_indexer_score_stride(LS_SEL_TOKENS, max_units);
+  char* w = static_cast<char*>(workspace);
+  ls::IndexerArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.w = head_weights;
+  a.keys = codes;
+  a.codebooks = static_cast<const uint16_t*>(codebooks);
+  a.b = batch_args(batch, key_pool);
+  a.num_heads = num_heads;
+  a.unit_kind = ls::kUnitsComplete;
+  a.max_units = U;
+  a.scores = scores_out ? scores_out : reinterpret_cast<float*>(w);
+  w += align_up(B * U * sizeof(float));
+  a.topk = n_candidates;
+  a.max_selected = n_candidates;
+  a.selected = candidates;
+  a.selected_count = candidate_counts;
+  int tiles = 128;
+  while (tiles > 4 && (long long)B * ((U + 16 * tiles - 1) / (16 * tiles)) < 512) tiles /= 2;
+  a.tiles_per_wg = tiles;
+  a.hist = reinterpret_cast<uint32_t*>(w);
+  w += align_up(2 * B * ls::kIdxBins * sizeof(uint32_t));
+  a.ctl = reinterpret_cast<uint32_t*>(w);
+  w += align_up(B * 4 * sizeof(uint32_t));
+  a.cand = reinterpret_cast<uint2*>(w);
+  w += align_up(B * U * sizeof(uint2));
+  a.bitmap = reinterpret_cast<uint32_t*>(w);
+  return hip_status(ls::launch_pq_select(a, stream), "PQ selection launches");
 }
 
 }  // extern "C"

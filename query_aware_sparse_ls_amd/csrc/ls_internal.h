@@ -129,6 +129,11 @@ constexpr int kIdxMarkUnits = 4096;     // units per mark workgroup (score row s
 constexpr int kIdxMaxUnits = 262144;    // units per request (token mode)
 
 enum { kIdxTokens = 0, kIdxBlocks = 1 };
+// Units of a request in token mode: every cached token, or the tokens of the
+// candidate blocks (kUnitsDefault); the candidate tokens, then the tokens of
+// the partial last page (kUnitsTokenCands); the tokens of the complete pages
+// (kUnitsComplete, PQ coarse scoring).
+enum { kUnitsDefault = 0, kUnitsTokenCands = 1, kUnitsComplete = 2 };
 
 struct IndexerArgs {
   const uint16_t* q;           // [B][H][128] bf16
@@ -138,6 +143,9 @@ struct IndexerArgs {
   BatchArgs b;
   int32_t num_heads;
   const int32_t* cand_blocks;  // tokens, optional: [B][cand_cap] ascending block ids
+                               // (token ids with kUnitsTokenCands)
+  int32_t unit_kind;           // kUnits*
+  const uint16_t* codebooks;   // PQ coarse scoring: [32][256][4] bf16 (keys = codes)
   const int32_t* cand_counts;  // [B]
   int32_t cand_cap;
   int32_t max_units;           // row stride of scores (units per request, max)
@@ -155,6 +163,30 @@ struct IndexerArgs {
 };
 
 hipError_t launch_indexer_score(const IndexerArgs& a, int mode, hipStream_t st);
+// the token top-k's two halves: zero the histograms and counters (before
+// the scoring), mark + finish (after it)
+hipError_t launch_indexer_zero(const IndexerArgs& a, hipStream_t st);
+hipError_t launch_indexer_mark(const IndexerArgs& a, hipStream_t st);
+// PQ32 coarse selection (k_pq.hip): zero, coarse scores of the complete
+// pages' tokens from their codes, mark + finish
+hipError_t launch_pq_select(const IndexerArgs& a, hipStream_t st);
+
+// PQ32 codes and codebooks (k_pq.hip).
+constexpr int kPqSub = 32, kPqCent = 256, kPqDim = 4, kPqFixedBits = 24;
+struct PqArgs {
+  const uint8_t* keys;          // fp8 e4m3fn [num_pages][P][128]
+  const float* scales;          // [num_pages][P], or null (1)
+  int32_t num_pages, page_size;
+  const int32_t* page_ids;      // the listed pages; token i = slot i % P of page_ids[i / P]
+  int32_t n_pages;
+  uint16_t* codebooks;          // [32][256][4] bf16
+  uint8_t* codes;               // encode: [num_pages][P][32]
+  unsigned long long* sums;     // training: [32][256][4] fixed-point sums
+  uint32_t* counts;             // training: [32][256]
+};
+hipError_t launch_pq_encode(const PqArgs& a, hipStream_t st);
+hipError_t launch_pq_train(const PqArgs& a, const int32_t* init_tokens, int iters,
+                           hipStream_t st);
 // zero the histogram and counters, score, mark + finish (three launches)
 hipError_t launch_indexer_token_select(const IndexerArgs& a, hipStream_t st);
 

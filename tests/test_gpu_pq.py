@@ -1,0 +1,208 @@
+"""GPU parity of PQ32 coarse-to-fine indexing (LeanSparse §5, "Approximate
+scoring with PQ" and "Retrieving and refining candidates"): k-means
+codebooks and codes bit-exact against the oracle; coarse scores within 1e-5
+of the oracle's (relative to the sum of absolute terms); candidate and final
+selections exact outside the near-tie band.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.method import BatchView
+from oracle.pq import dequantize_index_keys, pq_encode, pq_kmeans, pq_token_scores
+from parity_util import TIE_ABS_OF_MAX, TIE_REL, say
+from workloads import (PQ32_128K, bf16_bits, fp8_bits, make_indexer_inputs, pq_init_tokens,
+                       reduced)
+
+pytestmark = pytest.mark.gpu
+
+ls = pytest.importorskip("query_aware_sparse_ls_amd")
+
+SCORE_REL = 1e-5
+
+
+def _dev():
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+def _inputs(batch=2, blocks=40, lens=None, seed=11):
+    cfg = reduced(PQ32_128K, batch=batch, context=blocks * 64, seed=seed)
+    inp = make_indexer_inputs(cfg, device=_dev())
+    if lens is not None:
+        inp.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+    return inp
+
+
+def _batch(inp):
+    P = inp.cfg.page_size
+    nb = max(1, int((inp.seq_lens.max().item() + P - 1) // P))
+    return ls.PagedBatch(inp.idx_indptr, inp.idx_indices, inp.seq_lens, nb)
+
+
+def _train(inp, iters, n_pages=None):
+    """Codebooks trained on the first n_pages pages of the pool (GPU)."""
+    P = inp.cfg.page_size
+    n_pages = n_pages or int(inp.idx_keys.shape[0])
+    ids = torch.arange(n_pages, dtype=torch.int32, device=_dev())
+    init = pq_init_tokens(n_pages * P, inp.cfg.seed).to(_dev())
+    cb = ls.pq_train(inp.idx_keys, inp.idx_scale, ids, init, iters)
+    return cb, ids, init
+
+
+def _encode_all(inp, cb):
+    n = int(inp.idx_keys.shape[0])
+    codes = torch.zeros(n, inp.cfg.page_size, 32, dtype=torch.uint8, device=_dev())
+    ids = torch.arange(n, dtype=torch.int32, device=_dev())
+    ls.pq_encode(inp.idx_keys, inp.idx_scale, ids, cb, codes)
+    return codes
+
+
+def _host_keys(inp):
+    return dequantize_index_keys(fp8_bits(inp.idx_keys), inp.idx_scale.cpu().numpy())
+
+
+def _check_topk(gpu_sel, scores, cands, k, what):
+    """gpu_sel (ascending ids) vs the oracle's top-k of `cands` by (score
+    desc, id asc): exact outside the near-tie band around the k-th score."""
+    want = oracle.select_tokens(scores, k, candidates=cands)
+    assert gpu_sel == sorted(set(gpu_sel)), (what, "not ascending/unique")
+    assert len(gpu_sel) == len(want), (what, len(gpu_sel), len(want))
+    band = set()
+    if 0 < k < len(cands):
+        s = np.array([scores[j] for j in cands])
+        sk = np.sort(s)[::-1][k - 1]
+        tau = TIE_REL * abs(sk) + TIE_ABS_OF_MAX * np.max(np.abs(s))
+        band = {j for j in cands if abs(scores[j] - sk) <= tau}
+    diff = set(gpu_sel) ^ set(want)
+    assert diff <= band, (what, sorted(diff)[:10], len(band))
+    return len(band)
+
+
+def test_pq_train_and_encode_bit_exact():
+    """k-means (3 iterations over 40 pages x 64 tokens) and the codes of
+    every page equal the oracle's, bit for bit."""
+    inp = _inputs(batch=1, blocks=40, seed=21)
+    cb, _, init = _train(inp, 3)
+    codes = _encode_all(inp, cb)
+    torch.cuda.synchronize()
+    x = _host_keys(inp).reshape(-1, 128)
+    want_cb = pq_kmeans(x, init.cpu().numpy(), 3)
+    assert np.array_equal(bf16_bits(cb), want_cb)
+    want_codes = pq_encode(x, want_cb).reshape(codes.shape)
+    assert np.array_equal(codes.cpu().numpy(), want_codes)
+    # zero iterations: the starting centroids
+    cb0, _, _ = _train(inp, 0)
+    assert np.array_equal(bf16_bits(cb0), pq_kmeans(x, init.cpu().numpy(), 0))
+
+
+def test_pq_encode_listed_pages_only():
+    """Only the listed pages' codes are written (duplicates allowed; ids out
+    of range skipped); codebook random bf16."""
+    inp = _inputs(batch=1, blocks=30, seed=22)
+    g = torch.Generator().manual_seed(5)
+    cb = torch.randn(32, 256, 4, generator=g).to(torch.bfloat16).to(_dev())
+    n = int(inp.idx_keys.shape[0])
+    ids = torch.tensor([3, 7, 7, 0, n - 1, -1, n + 5], dtype=torch.int32, device=_dev())
+    codes = torch.full((n, 64, 32), 255, dtype=torch.uint8, device=_dev())
+    ls.pq_encode(inp.idx_keys, inp.idx_scale, ids, cb, codes)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    x = _host_keys(inp)
+    listed = [3, 7, 0, n - 1]
+    want = pq_encode(x[listed].reshape(-1, 128), bf16_bits(cb)).reshape(len(listed), 64, 32)
+    assert np.array_equal(got[listed], want)
+    others = np.setdiff1d(np.arange(n), listed)
+    assert (got[others] == 255).all()
+
+
+@pytest.mark.parametrize("lens,C", [((2500, 1300), 300), ((64, 3), 10), ((1000, 640), 5000),
+                                    ((2560, 2000), 0)])
+def test_pq_select_and_refine_small(lens, C):
+    """Coarse scores, top-C candidates and the exact rerank (top-64 of the
+    candidates and the partial page) against the oracle; lengths with no
+    complete page, no partial page, and C above the number of tokens."""
+    inp = _inputs(batch=2, blocks=40, lens=lens, seed=23)
+    say(f"pq select: lens {lens}, C {C}")
+    cb, _, _ = _train(inp, 2)
+    codes = _encode_all(inp, cb)
+    b = _batch(inp)
+    P = inp.cfg.page_size
+    stride = ls.indexer_score_stride("tokens", b.max_blocks * P)
+    sc = torch.full((2, stride), float("nan"), device=_dev())
+    cand, cnt = ls.pq_select(inp.q_idx, inp.head_w, codes, cb, b, C, scores_out=sc)
+    k = 64
+    ex_stride = ls.indexer_score_stride("tokens", max(C, 1) + P)
+    esc = torch.full((2, ex_stride), float("nan"), device=_dev())
+    sel, n = ls.indexer_select(inp.q_idx, inp.head_w, inp.idx_keys, P, b, granularity="tokens",
+                               topk=k, max_selected=k, key_scales=inp.idx_scale,
+                               cand_blocks=cand, cand_counts=cnt, token_candidates=True,
+                               scores_out=esc)
+    torch.cuda.synchronize()
+    q, w = bf16_bits(inp.q_idx), inp.head_w.cpu().numpy()
+    bv = BatchView(inp.idx_indptr.cpu().numpy(), inp.idx_indices.cpu().numpy(),
+                   inp.seq_lens.cpu().numpy(), P)
+    cbb = bf16_bits(cb)
+    codes_h = codes.cpu().numpy()
+    kb, ks = fp8_bits(inp.idx_keys), inp.idx_scale.cpu().numpy()
+    for r in range(2):
+        L = lens[r]
+        nc = L // P
+        coarse = pq_token_scores(q, w, codes_h, cbb, bv, r)
+        # tolerance scale: the sum of absolute terms with the decoded keys
+        dec = oracle.pq.pq_decode(codes_h[bv.pages(r)[:nc]].reshape(-1, 32), cbb)
+        mag = (np.abs(dec) @ np.abs(oracle.bf16_to_f64(q[r])).T) @ np.abs(w[r].astype(np.float64))
+        got = sc[r, :nc * P].cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - coarse) <= SCORE_REL * mag + 1e-30), "coarse scores"
+        c_n = int(cnt[r])
+        gc = cand[r, :c_n].cpu().tolist()
+        _check_topk(gc, coarse, list(range(nc * P)), C, f"candidates r{r}")
+        if C > c_n:
+            assert (cand[r, c_n:] == -1).all()
+        # the exact pass scores the GPU's candidates and the tail
+        refined = np.array(gc + list(range(nc * P, L)), dtype=np.int64)
+        exact = oracle.indexer_token_scores(q, w, kb, ks, bv, r, tokens=refined)
+        gx = esc[r, :len(refined)].cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(gx, exact, rtol=2e-5,
+                                   atol=1e-5 * max(1.0, np.abs(exact).max(initial=0.0)))
+        pos = {t: i for i, t in enumerate(refined.tolist())}
+        gsel = sorted(pos[t] for t in sel[r, :int(n[r])].cpu().tolist())
+        _check_topk(gsel, exact, list(range(len(refined))), k, f"final r{r}")
+        assert (sel[r, int(n[r]):] == -1).all()
+
+
+def test_pq_full_size_sampled():
+    """The bench shape (8 x 128K, 64 heads, C = 2,048, k = 512), codebooks
+    trained on the cache: requests 0 and 7 against the oracle."""
+    cfg = PQ32_128K
+    say(f"pq at full size: {cfg.name}")
+    inp = make_indexer_inputs(cfg, device=_dev())
+    P = cfg.page_size
+    cb, _, _ = _train(inp, 2)
+    codes = _encode_all(inp, cb)
+    b = _batch(inp)
+    stride = ls.indexer_score_stride("tokens", b.max_blocks * P)
+    sc = torch.empty((cfg.batch, stride), device=_dev())
+    cand, cnt = ls.pq_select(inp.q_idx, inp.head_w, codes, cb, b, cfg.n_candidates, scores_out=sc)
+    sel, n = ls.indexer_select(inp.q_idx, inp.head_w, inp.idx_keys, P, b, granularity="tokens",
+                               topk=cfg.topk_tokens, max_selected=cfg.topk_tokens,
+                               key_scales=inp.idx_scale, cand_blocks=cand, cand_counts=cnt,
+                               token_candidates=True)
+    torch.cuda.synchronize()
+    q, w = bf16_bits(inp.q_idx), inp.head_w.cpu().numpy()
+    bv = BatchView(inp.idx_indptr.cpu().numpy(), inp.idx_indices.cpu().numpy(),
+                   inp.seq_lens.cpu().numpy(), P)
+    cbb, codes_h = bf16_bits(cb), codes.cpu().numpy()
+    kb, ks = fp8_bits(inp.idx_keys), inp.idx_scale.cpu().numpy()
+    for r in (0, 7):
+        coarse = pq_token_scores(q, w, codes_h, cbb, bv, r)
+        gc = cand[r, :int(cnt[r])].cpu().tolist()
+        _check_topk(gc, coarse, list(range(len(coarse))), cfg.n_candidates, f"candidates r{r}")
+        exact = oracle.indexer_token_scores(q, w, kb, ks, bv, r, tokens=np.array(gc))
+        pos = {t: i for i, t in enumerate(gc)}
+        gsel = [pos[t] for t in sel[r, :int(n[r])].cpu().tolist()]
+        _check_topk(sorted(gsel), exact, list(range(len(gc))), cfg.topk_tokens, f"final r{r}")

@@ -11,6 +11,8 @@ from .configs import (  # noqa: F401
     BlockTopKConfig,
     IndexerConfig,
     CoarseToFineConfig,
+    PqConfig,
+    PQ32_128K,
     TINY_4K,
     LLAMA8B_32K_B16,
     RAGGED_B64,
@@ -24,6 +26,7 @@ from .generate import (  # noqa: F401
     IndexerInputs,
     make_indexer_inputs,
     indexer_queries,
+    pq_init_tokens,
     bf16_bits,
     fp8_bits,
 )

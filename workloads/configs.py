@@ -80,6 +80,15 @@ class CoarseToFineConfig(IndexerConfig):
     seed: int = 1004
 
 
+@dataclass(frozen=True)
+class PqConfig(IndexerConfig):
+    """PQ32 coarse scores -> top-C candidate tokens -> exact rerank -> top-k."""
+
+    n_candidates: int = 2048
+    kmeans_iters: int = 8
+    seed: int = 1005
+
+
 # Tiny single-request step: 1 layer, 8 q heads / 2 kv heads, d 64, 4K context,
 # contiguous page table, 8 hot blocks, top-16 + block 0 + last block, fp32 out.
 TINY_4K = BlockTopKConfig(
@@ -113,6 +122,13 @@ INDEXER_128K = IndexerConfig(name="indexer_fp8_128k_b8_top2048", batch=8,
 
 COARSE_TO_FINE_950K = CoarseToFineConfig(
     name="coarse_to_fine_950k_b4", batch=4, context=972800)
+
+
+# PQ32 coarse-to-fine indexing: 8 requests x 128K tokens in 64-token pages,
+# 64 indexer heads x 128, codebooks trained on the cache, C = 2,048
+# candidates, top-512 tokens after the exact rerank.
+PQ32_128K = PqConfig(name="pq32_128k_b8_c2048_top512", batch=8, context=131072,
+                     topk_tokens=512)
 
 
 def reduced(cfg, **changes):

@@ -290,3 +290,12 @@ def make_indexer_inputs(cfg: IndexerConfig, device="cpu", seed: Optional[int] = 
         indptr.to(device), idx_perm.to(device),
         q_mla.to(device), lat.view(used, P, -1), indptr.clone().to(device),
         kv_perm.to(device), torch.full((B,), L, dtype=torch.int32).to(device))
+
+
+def pq_init_tokens(n_tokens: int, seed: int, k: int = 256) -> torch.Tensor:
+    """k distinct token indices in [0, n_tokens) (seeded): the k-means
+    starting points, drawn here so both sides take the same ones."""
+    g = _cpu_gen(seed)
+    if n_tokens >= k:
+        return torch.randperm(n_tokens, generator=g)[:k].to(torch.int32)
+    return torch.randint(0, n_tokens, (k,), generator=g).to(torch.int32)
