@@ -364,17 +364,25 @@ def summarize_profiles(args) -> int:
 
 # ------------------------------------------------- learned-indexer paths ----
 
-def indexer_step_bytes(cfg, coarse: bool):
+def indexer_step_bytes(cfg, coarse: bool, pq: bool = False):
     """Algorithmic bytes of one learned-indexer step (per call, all requests).
     Token keys are fp8 (1 B per dim) with one fp32 scale per token; latent
-    rows are 576 bf16 (the whole row is read: key = all 576 dims)."""
+    rows are 576 bf16 (the whole row is read: key = all 576 dims). PQ32: 32 B
+    of codes per complete-page token, then the candidates' keys, and the
+    codes of the pages that filled this step (keys read, codes written)."""
     B, L, H, D, P = cfg.batch, cfg.context, cfg.index_heads, cfg.index_dim, cfg.page_size
     k = cfg.topk_tokens
     dk = cfg.kv_lora_dim + cfg.rope_dim
     d = {"q_idx_w": B * H * (D * 2 + 4), "selection": B * k * 4,
          "mla_kv": B * k * dk * 2, "q_mla": B * cfg.mla_heads * dk * 2,
          "out": B * cfg.mla_heads * cfg.kv_lora_dim * 2}
-    if coarse:
+    if pq:
+        C = cfg.n_candidates
+        d["pq_codes"] = B * (L // P) * P * 32
+        d["candidates"] = B * C * 4 * 2                   # written, then read
+        d["candidate_keys"] = B * (C + L % P) * (D + 4)
+        d["encode_new_pages"] = B * P * (D + 4 + 32)
+    elif coarse:
         nb = L // P
         kb = cfg.coarse_topk_blocks + 1                  # + the forced last block
         d["coarse_summaries"] = B * (nb - 1) * D * 2     # every complete, non-forced block
@@ -386,15 +394,16 @@ def indexer_step_bytes(cfg, coarse: bool):
     return d
 
 
-def bench_indexer(args, coarse: bool) -> int:
+def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
     """Time the learned-indexer path: token top-k over every cached token
-    (128K workload) or coarse block top-k -> exact token top-k among the kept
-    blocks (950K workload), then sparse MLA over the selected tokens."""
+    (128K workload), coarse block top-k -> exact token top-k among the kept
+    blocks (950K workload), or PQ32 coarse top-C -> exact rerank of the
+    candidates (128K workload); then sparse MLA over the selected tokens."""
     import torch
     import query_aware_sparse_ls_amd as ls
-    from workloads import (COARSE_TO_FINE_950K, INDEXER_128K, indexer_queries,
-                           make_indexer_inputs)
-    cfg = COARSE_TO_FINE_950K if coarse else INDEXER_128K
+    from workloads import (COARSE_TO_FINE_950K, INDEXER_128K, PQ32_128K, indexer_queries,
+                           make_indexer_inputs, pq_init_tokens)
+    cfg = PQ32_128K if pq else (COARSE_TO_FINE_950K if coarse else INDEXER_128K)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B, P, k = cfg.batch, cfg.page_size, cfg.topk_tokens
@@ -404,6 +413,21 @@ def bench_indexer(args, coarse: bool) -> int:
     reps = []
     base = make_indexer_inputs(cfg, device=dev)
     summ = None
+    codes = codebooks = None
+    if pq:
+        # one cache with its codebooks (trained on it) and codes, built once
+        # (setup, not timed); replicas differ in their queries
+        npg = base.idx_keys.shape[0]
+        ids = torch.arange(npg, dtype=torch.int32, device=dev)
+        init = pq_init_tokens(npg * P, cfg.seed).to(dev)
+        codebooks = ls.pq_train(base.idx_keys, base.idx_scale, ids, init, cfg.kmeans_iters)
+        codes = torch.zeros(npg, P, 32, dtype=torch.uint8, device=dev)
+        ls.pq_encode(base.idx_keys, base.idx_scale, ids, codebooks, codes)
+        lens = base.seq_lens.cpu().tolist()
+        indptr = base.idx_indptr.cpu().tolist()
+        idx = base.idx_indices.cpu()
+        new_pages = torch.tensor([int(idx[indptr[r] + lens[r] // P - 1]) for r in range(B)
+                                  if lens[r] % P == 0], dtype=torch.int32, device=dev)
     if coarse:
         # one cache; replicas differ in their queries and own a copy of the
         # block means (read in full every step)
@@ -412,10 +436,12 @@ def bench_indexer(args, coarse: bool) -> int:
         ls.build_block_summaries(base.idx_keys, torch.arange(npg, dtype=torch.int32, device=dev),
                                  summ, key_scales=base.idx_scale)
     for i in range(R):
-        if coarse:
+        if coarse or pq:
             q_idx, w, q_mla = indexer_queries(cfg, cfg.seed + 7 * i, dev)
             inp = base
-            rep = dict(q_idx=q_idx, w=w, q_mla=q_mla, summ=summ.clone())
+            rep = dict(q_idx=q_idx, w=w, q_mla=q_mla)
+            if coarse:
+                rep["summ"] = summ.clone()
         else:
             inp = base if i == 0 else make_indexer_inputs(cfg, device=dev, seed=cfg.seed + 7 * i)
             rep = dict(q_idx=inp.q_idx, w=inp.head_w, q_mla=inp.q_mla)
@@ -428,7 +454,15 @@ def bench_indexer(args, coarse: bool) -> int:
                                    device=dev),
                    ws_mla=torch.empty(ls.sparse_mla_decode_workspace_size(B, cfg.mla_heads, k),
                                       dtype=torch.uint8, device=dev))
-        if coarse:
+        if pq:
+            C = cfg.n_candidates
+            rep.update(cand=torch.empty(B, C, dtype=torch.int32, device=dev),
+                       ccnt=torch.empty(B, dtype=torch.int32, device=dev),
+                       ws_c=torch.empty(ls.indexer_select_workspace_size(B, "tokens", nb * P),
+                                        dtype=torch.uint8, device=dev),
+                       ws_t=torch.empty(ls.indexer_select_workspace_size(B, "tokens", C + P),
+                                        dtype=torch.uint8, device=dev))
+        elif coarse:
             kb = cfg.coarse_topk_blocks + 2
             rep.update(bsel=torch.empty(B, kb, dtype=torch.int32, device=dev),
                        bcnt=torch.empty(B, dtype=torch.int32, device=dev),
@@ -454,14 +488,23 @@ def bench_indexer(args, coarse: bool) -> int:
         inp = rp["inp"]
         ls.indexer_select(rp["q_idx"], rp["w"], inp.idx_keys, P, rp["ib"], granularity="tokens",
                           topk=k, max_selected=k, key_scales=inp.idx_scale,
-                          cand_blocks=rp.get("bsel"), cand_counts=rp.get("bcnt"),
+                          cand_blocks=rp.get("cand", rp.get("bsel")),
+                          cand_counts=rp.get("ccnt", rp.get("bcnt")), token_candidates=pq,
                           selected=rp["sel"], selected_count=rp["cnt"], workspace=rp["ws_t"])
+
+    def c_encode(rp):
+        ls.pq_encode(rp["inp"].idx_keys, rp["inp"].idx_scale, new_pages, codebooks, codes)
+
+    def c_pq(rp):
+        ls.pq_select(rp["q_idx"], rp["w"], codes, codebooks, rp["ib"], cfg.n_candidates,
+                     candidates=rp["cand"], counts=rp["ccnt"], workspace=rp["ws_c"])
 
     def c_mla(rp):
         ls.sparse_mla_decode(rp["q_mla"], rp["inp"].latent, rp["kb"], rp["sel"], rp["cnt"],
                              sm_scale=sm, out=rp["out"], workspace=rp["ws_mla"])
 
     calls = ([("coarse_block_select", c_blocks)] if coarse else []) + \
+        ([("pq_encode_new_pages", c_encode), ("pq_coarse_select", c_pq)] if pq else []) + \
         [("token_select", c_tokens), ("sparse_mla", c_mla)]
 
     def step(rp):
@@ -509,26 +552,57 @@ def bench_indexer(args, coarse: bool) -> int:
         b.record()
         torch.cuda.synchronize()
         per[name] = a.elapsed_time(b) / n
-    nbytes = indexer_step_bytes(cfg, coarse)
+    nbytes = indexer_step_bytes(cfg, coarse, pq)
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
     dom = max(per, key=per.get)
     if dom == "token_select":
-        dbytes = (nbytes["candidate_keys"] if coarse else nbytes["indexer_keys"]) + \
+        dbytes = (nbytes["candidate_keys"] if coarse or pq else nbytes["indexer_keys"]) + \
             nbytes["q_idx_w"] + nbytes["selection"]
+    elif dom == "pq_coarse_select":
+        dbytes = nbytes["pq_codes"] + nbytes["q_idx_w"] + B * cfg.n_candidates * 4
+    elif dom == "pq_encode_new_pages":
+        dbytes = nbytes["encode_new_pages"]
     elif dom == "sparse_mla":
         dbytes = nbytes["mla_kv"] + nbytes["q_mla"] + nbytes["out"] + nbytes["selection"]
     else:
         dbytes = nbytes["coarse_summaries"] + nbytes["q_idx_w"] + nbytes["block_selection"]
     dgbps = dbytes / (per[dom] * 1e-3) / 1e9
-    res = {"metric": ("coarse-to-fine indexer selection + sparse MLA decode calls/sec"
-                      if coarse else "learned-indexer token selection + sparse MLA decode calls/sec"),
+    recall = None
+    if pq:
+        # recall against the exact top-k over every token (GPU, replica 0):
+        # the coarse top-k alone, and the top-C + exact rerank of the step
+        rp = reps[0]
+        step(rp)
+        ex, exn = ls.indexer_select(rp["q_idx"], rp["w"], base.idx_keys, P, rp["ib"],
+                                    granularity="tokens", topk=k, max_selected=k,
+                                    key_scales=base.idx_scale)
+        direct, dn = ls.pq_select(rp["q_idx"], rp["w"], codes, codebooks, rp["ib"], k)
+        torch.cuda.synchronize()
+
+        def rec(a, an):
+            hits = 0
+            for r in range(B):
+                sa = set(a[r, :int(an[r])].tolist())
+                hits += len(sa & set(ex[r, :int(exn[r])].tolist()))
+            return round(hits / float(exn.sum().item()), 4)
+        recall = {f"pq_direct_top{k}": rec(direct, dn),
+                  f"c{cfg.n_candidates}_rerank_top{k}": rec(rp["sel"], rp["cnt"])}
+    if pq:
+        metric = "PQ32 coarse-to-fine token selection + sparse MLA decode calls/sec"
+    elif coarse:
+        metric = "coarse-to-fine indexer selection + sparse MLA decode calls/sec"
+    else:
+        metric = "learned-indexer token selection + sparse MLA decode calls/sec"
+    res = {"metric": metric,
            "value": round(1e3 / ms, 1), "unit": "calls/s", "n_gpus": 1, "steps": steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": cfg.name, "batch": B, "context": cfg.context,
                       "index_heads": cfg.index_heads, "topk_tokens": k,
                       "mla_heads": cfg.mla_heads, "page_size": P, "replicas": R,
-                      **({"coarse_topk_blocks": cfg.coarse_topk_blocks} if coarse else {})},
+                      **({"coarse_topk_blocks": cfg.coarse_topk_blocks} if coarse else {}),
+                      **({"n_candidates": cfg.n_candidates, "kmeans_iters": cfg.kmeans_iters}
+                         if pq else {})},
            "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
            "achieved_GBps_step": round(gbps, 1),
            "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -539,6 +613,8 @@ def bench_indexer(args, coarse: bool) -> int:
                         "algorithmic_bytes_per_launch": dbytes,
                         "avg_launch_ms": round(per[dom], 5)},
            "device": torch.cuda.get_device_name(0)}
+    if recall is not None:
+        res["recall_vs_exact"] = recall
     print(json.dumps(res), flush=True)
     return 0
 
@@ -635,11 +711,12 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
                     help="block-topk path: block-mean summaries (default) or Quest bounds")
-    ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense"),
+    ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense", "pq"),
                     default="block-topk",
                     help="block-topk: the 8B/32K/B16 block top-k step (default); indexer: "
                          "token top-2048 of 8 x 128K + sparse MLA; coarse-to-fine: 4 x 950K; "
-                         "dense: k = all split-K attention on the 8B/32K/B16 workload")
+                         "dense: k = all split-K attention on the 8B/32K/B16 workload; pq: PQ32 "
+                         "top-2048 candidates + exact rerank to top-512 of 8 x 128K + sparse MLA")
     args = ap.parse_args(argv)
     if args.summarize_profiles:
         return summarize_profiles(args)
@@ -652,7 +729,7 @@ def main(argv=None) -> int:
     if args.path == "dense":
         return bench_dense(args)
     if args.path != "block-topk":
-        return bench_indexer(args, coarse=args.path == "coarse-to-fine")
+        return bench_indexer(args, coarse=args.path == "coarse-to-fine", pq=args.path == "pq")
 
     import torch
     import query_aware_sparse_ls_amd as ls

@@ -315,13 +315,13 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
 
 // ------------------------------------------------------------ token top-k ----
 
+// One 16-byte store per thread (the histograms are 256-byte aligned).
 __global__ __launch_bounds__(kIdxThreads) void idx_zero_kernel(uint32_t* hist, uint32_t* ctl,
                                                                int batch) {
-  const int n = 2 * batch * kIdxBins;   // first-digit and second-digit histograms
-  for (int i = blockIdx.x * kIdxThreads + threadIdx.x; i < n; i += gridDim.x * kIdxThreads)
-    hist[i] = 0u;
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < batch * 4; i += kIdxThreads) ctl[i] = 0u;
+  const int n4 = 2 * batch * kIdxBins / 4;   // first-digit and second-digit histograms
+  const int i = blockIdx.x * kIdxThreads + threadIdx.x;
+  if (i < n4) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (i < batch * 4) ctl[i] = 0u;
 }
 
 constexpr int kIdxMarkThreads = 512;
@@ -675,8 +675,9 @@ hipError_t launch_indexer_score(const IndexerArgs& a, int mode, hipStream_t st) 
 }
 
 hipError_t launch_indexer_zero(const IndexerArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(idx_zero_kernel, dim3(16), dim3(kIdxThreads), 0, st, a.hist, a.ctl,
-                     a.b.batch);
+  const int n4 = 2 * a.b.batch * kIdxBins / 4;
+  hipLaunchKernelGGL(idx_zero_kernel, dim3((n4 + kIdxThreads - 1) / kIdxThreads), dim3(kIdxThreads),
+                     0, st, a.hist, a.ctl, a.b.batch);
   return hipGetLastError();
 }
 

@@ -148,13 +148,66 @@ __global__ __launch_bounds__(256) void pq_update_kernel(PqArgs a) {
   a.counts[e] = 0u;
 }
 
+// Encoding of a few pages (the ones that filled at a step): the 256
+// centroids of subspace j are spread over a wave's lanes (4 each, in
+// registers), so a code costs 4 distances per lane and a wave reduction of
+// (distance, index) that keeps the lowest index among equal distances (the
+// same result as the serial scan). Each wave codes kPqEncTokens tokens, their
+// key loads issued before the first distance.
+constexpr int kPqEncTokens = 4;
+
+__global__ __launch_bounds__(256) void pq_encode_kernel(PqArgs a) {
+#pragma clang fp contract(off)
+  const int j = blockIdx.y, lane = threadIdx.x & 63;
+  const long long t0 = ((long long)blockIdx.x * 4 + wave_id()) * kPqEncTokens;
+  long long row[kPqEncTokens];
+#pragma unroll
+  for (int t = 0; t < kPqEncTokens; ++t) row[t] = pq_key_row(a, t0 + t);
+  double x[kPqEncTokens][4];
+#pragma unroll
+  for (int t = 0; t < kPqEncTokens; ++t) pq_subvector(a, row[t] >= 0 ? row[t] : 0, j, x[t]);
+  double c[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint2 v = *reinterpret_cast<const uint2*>(a.codebooks +
+                                                    ((size_t)j * kPqCent + lane + 64 * m) * 4);
+    c[m][0] = (double)__uint_as_float(v.x << 16);
+    c[m][1] = (double)__uint_as_float(v.x & 0xffff0000u);
+    c[m][2] = (double)__uint_as_float(v.y << 16);
+    c[m][3] = (double)__uint_as_float(v.y & 0xffff0000u);
+  }
+#pragma unroll
+  for (int t = 0; t < kPqEncTokens; ++t) {
+    double best = __builtin_huge_val();
+    int arg = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {   // ascending centroid index: strict < keeps the lowest
+      const double d0 = x[t][0] - c[m][0], d1 = x[t][1] - c[m][1];
+      const double d2 = x[t][2] - c[m][2], d3 = x[t][3] - c[m][3];
+      const double dist = ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
+      if (dist < best) {
+        best = dist;
+        arg = lane + 64 * m;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ob = __shfl_xor(best, off);
+      const int oa = __shfl_xor(arg, off);
+      if (ob < best || (ob == best && oa < arg)) {
+        best = ob;
+        arg = oa;
+      }
+    }
+    if (lane == 0 && row[t] >= 0) a.codes[row[t] * kPqSub + j] = (uint8_t)arg;
+  }
+}
+
 hipError_t launch_pq_encode(const PqArgs& a, hipStream_t st) {
   const long long n = (long long)a.n_pages * a.page_size;
-  PqArgs e = a;
-  e.sums = nullptr;
-  e.counts = nullptr;
-  hipLaunchKernelGGL(pq_assign_kernel, dim3((unsigned)((n + 255) / 256), kPqSub), dim3(256), 0,
-                     st, e);
+  const long long per_block = 4 * kPqEncTokens;
+  hipLaunchKernelGGL(pq_encode_kernel, dim3((unsigned)((n + per_block - 1) / per_block), kPqSub),
+                     dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -178,6 +231,8 @@ hipError_t launch_pq_train(const PqArgs& a, const int32_t* init_tokens, int iter
 
 // ------------------------------------------------------- coarse scoring ----
 
+constexpr int kPqPrefetch = 4;   // code tiles in flight per wave (8 bytes per lane each)
+
 template <int NHT>
 struct PqScoreLds {
   union {
@@ -190,7 +245,7 @@ struct PqScoreLds {
 
 template <int NHT>
 __global__ __launch_bounds__(kIdxThreads, 2) void pq_score_kernel(IndexerArgs a) {
-  constexpr int NS = kIdxPrefetch, H = 16 * NHT;
+  constexpr int NS = kPqPrefetch, H = 16 * NHT;
   __shared__ PqScoreLds<NHT> sh;
   const int r = blockIdx.y, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
