@@ -293,6 +293,40 @@ def select_tokens(scores: np.ndarray, k: int, candidates: Optional[Iterable[int]
     return sorted(fs | set(rank_top(scores, cands, k)))
 
 
+def score_bucket(scores: np.ndarray, bits: int = 12) -> np.ndarray:
+    """Bucket of each score for the approximate top-k: the score is taken in
+    fp32 (the precision the kernels rank in), mapped to an unsigned 32-bit
+    key that orders like the floats (negative: all bits inverted; otherwise
+    the sign bit set; -0 counts as +0), and the bucket is the key's top
+    `bits` bits: sign, exponent and the leading mantissa bits, i.e. a
+    monotonic, roughly logarithmic remap of the scores."""
+    f = np.asarray(scores, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = np.where(u == 0x80000000, 0, u)
+    key = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
+    return (key >> (32 - bits)).astype(np.int64)
+
+
+def approx_select_tokens(scores: np.ndarray, k: int,
+                         candidates: Optional[Iterable[int]] = None) -> List[int]:
+    """Approximate top-k (Vortex, "Making it fast": a monotonic remap of the
+    scores into buckets and an early exit that stops refining once enough
+    winners are certain, filling the rest from the boundary bucket): every
+    candidate whose bucket is above the bucket b* holding the k-th best
+    score, then candidates of b* in ascending index order until there are k
+    (this build fills deterministically instead of by random sampling).
+    Ascending ids."""
+    cands = np.arange(len(scores)) if candidates is None else np.asarray(list(candidates))
+    k = min(max(0, k), len(cands))
+    if k == 0:
+        return []
+    b = score_bucket(np.asarray(scores)[cands])
+    kth = np.sort(b)[::-1][k - 1]
+    above = cands[b > kth]
+    fill = np.sort(cands[b == kth])[:k - len(above)]
+    return sorted(int(t) for t in np.concatenate([above, fill]))
+
+
 def tokens_of_blocks(blocks: Iterable[int], page_size: int, seq_len: int) -> np.ndarray:
     t = [b * page_size + s for b in blocks for s in range(page_size)]
     t = np.asarray(t, dtype=np.int64)

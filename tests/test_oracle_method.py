@@ -572,3 +572,52 @@ def test_coarse_to_fine_never_leaves_the_kept_blocks():
     for a in res["tokens"]:
         for b in allowed - set(res["tokens"]):
             assert s[a] > s[b] or (s[a] == s[b] and a < b)
+
+
+# ------------------------------------------------------- approximate top-k
+
+def test_approx_topk_hand_worked():
+    from oracle.method import approx_select_tokens, score_bucket
+    # 1.0, 1.01 and 1.02 share a bucket (same exponent, same leading three
+    # mantissa bits); 3.0 is above it, 0.5 below. k = 3: 3.0 is certain, the
+    # two others come from the boundary bucket in index order.
+    s = np.array([1.0, 1.01, 1.02, 3.0, 0.5])
+    b = score_bucket(s)
+    assert b[0] == b[1] == b[2] and b[3] > b[0] > b[4]
+    assert approx_select_tokens(s, 3) == [0, 1, 3]
+    assert select_tokens(s, 3) == [1, 2, 3]          # the exact one differs
+    # 1.125 has the next mantissa pattern: its own bucket above 1.0's
+    s2 = np.array([1.0, 1.125, 1.1])
+    assert score_bucket(s2)[1] == score_bucket(s2)[0] + 1
+    assert approx_select_tokens(s2, 1) == [1]
+
+
+def test_approx_topk_order_and_exactness_when_buckets_are_distinct():
+    from oracle.method import approx_select_tokens, score_bucket
+    # negative, zero and positive scores keep their order through the key
+    vals = np.array([-8.0, -1.0, -0.0, 0.0, 0.75, 2.0, 40.0])
+    b = score_bucket(vals)
+    assert list(b) == sorted(b) and b[2] == b[3]
+    # one score per power of two: every bucket holds one candidate, so the
+    # approximate top-k is the exact one for every k
+    rng = np.random.default_rng(50)
+    s = 2.0 ** rng.permutation(np.arange(-20, 20)) * np.where(rng.random(40) < 0.5, -1, 1)
+    for k in (0, 1, 7, 20, 40):
+        assert approx_select_tokens(s, k) == select_tokens(s, k)
+    # candidates restrict the ranking
+    assert approx_select_tokens(s, 3, candidates=[0, 5, 9, 11]) == \
+        select_tokens(s, 3, candidates=[0, 5, 9, 11])
+
+
+def test_approx_topk_keeps_every_certain_winner():
+    from oracle.method import approx_select_tokens, score_bucket
+    rng = np.random.default_rng(51)
+    s = rng.standard_normal(3000) * 5
+    for k in (10, 300, 2999):
+        got = set(approx_select_tokens(s, k))
+        exact = set(select_tokens(s, k))
+        b = score_bucket(s)
+        kth = np.sort(b)[::-1][k - 1]
+        assert len(got) == k
+        assert {i for i in range(3000) if b[i] > kth} <= got & exact
+        assert all(b[i] >= kth for i in got)
