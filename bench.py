@@ -490,6 +490,7 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
                           topk=k, max_selected=k, key_scales=inp.idx_scale,
                           cand_blocks=rp.get("cand", rp.get("bsel")),
                           cand_counts=rp.get("ccnt", rp.get("bcnt")), token_candidates=pq,
+                          approx=args.approx_topk,
                           selected=rp["sel"], selected_count=rp["cnt"], workspace=rp["ws_t"])
 
     def c_encode(rp):
@@ -568,7 +569,25 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
         dbytes = nbytes["coarse_summaries"] + nbytes["q_idx_w"] + nbytes["block_selection"]
     dgbps = dbytes / (per[dom] * 1e-3) / 1e9
     recall = None
-    if pq:
+    if args.approx_topk:
+        # recall of the approximate top-k against the exact one (replica 0)
+        rp = reps[0]
+        step(rp)
+        ex_sel = torch.empty_like(rp["sel"])
+        ex_cnt = torch.empty_like(rp["cnt"])
+        ls.indexer_select(rp["q_idx"], rp["w"], rp["inp"].idx_keys, P, rp["ib"],
+                          granularity="tokens", topk=k, max_selected=k,
+                          key_scales=rp["inp"].idx_scale,
+                          cand_blocks=rp.get("cand", rp.get("bsel")),
+                          cand_counts=rp.get("ccnt", rp.get("bcnt")), token_candidates=pq,
+                          selected=ex_sel, selected_count=ex_cnt)
+        torch.cuda.synchronize()
+        hits = 0
+        for r in range(B):
+            hits += len(set(rp["sel"][r, :int(rp["cnt"][r])].tolist()) &
+                        set(ex_sel[r, :int(ex_cnt[r])].tolist()))
+        recall = {"approx_topk_vs_exact": round(hits / float(ex_cnt.sum().item()), 4)}
+    if pq and not args.approx_topk:
         # recall against the exact top-k over every token (GPU, replica 0):
         # the coarse top-k alone, and the top-C + exact rerank of the step
         rp = reps[0]
@@ -602,7 +621,8 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
                       "mla_heads": cfg.mla_heads, "page_size": P, "replicas": R,
                       **({"coarse_topk_blocks": cfg.coarse_topk_blocks} if coarse else {}),
                       **({"n_candidates": cfg.n_candidates, "kmeans_iters": cfg.kmeans_iters}
-                         if pq else {})},
+                         if pq else {}),
+                      "token_topk": "approximate" if args.approx_topk else "exact"},
            "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
            "achieved_GBps_step": round(gbps, 1),
            "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -709,6 +729,9 @@ def main(argv=None) -> int:
               "copy-fetch-cmd", "copy-write-cmd"):
         ap.add_argument("--" + a, default="")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--approx-topk", action="store_true",
+                    help="indexer paths: the approximate token top-k (boundary bucket filled "
+                         "in index order) instead of the exact one; reports its recall")
     ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
                     help="block-topk path: block-mean summaries (default) or Quest bounds")
     ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense", "pq"),

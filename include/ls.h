@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 4
+#define LS_ABI_VERSION 5
 
 typedef enum ls_status {
   LS_OK = 0,
@@ -384,6 +384,14 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
  * a pass that keeps every unit above the k-th score's 12-bit bucket and
  * gathers that bucket's units, and the ranking of those by the rest of their
  * key (in the last workgroup of each request to finish the pass).
+ * p->approx = 1 (tokens mode) is the approximate top-k of the Vortex post
+ * ("Making it fast": a monotonic remap of the scores into buckets, and an
+ * early exit that stops refining and fills the rest from the boundary
+ * bucket): every unit whose 12-bit bucket of the order-preserving key of its
+ * fp32 score (sign, exponent, three mantissa bits) lies above the bucket b*
+ * holding the k-th score, then units of b* in ascending unit order until
+ * there are topk. Deterministic; not the exact top-k when b* holds more
+ * units than it contributes.
  */
 enum { LS_SEL_TOKENS = 0, LS_SEL_BLOCKS = 1 };
 enum { LS_CAND_BLOCKS = 0, LS_CAND_TOKENS = 1 };
@@ -397,6 +405,8 @@ typedef struct ls_indexer_params {
   int32_t max_selected;  /* row capacity of `selected`                        */
   int32_t candidates;    /* LS_CAND_BLOCKS or LS_CAND_TOKENS: what cand_blocks */
                          /* holds (tokens mode with a candidate list)         */
+  int32_t approx;        /* tokens mode: 0 exact top-k; 1 approximate top-k   */
+                         /* (see below)                                       */
 } ls_indexer_params;
 
 /* Row stride (in floats) of scores_out for up to max_units units. */

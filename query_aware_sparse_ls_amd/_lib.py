@@ -39,7 +39,7 @@ class LsSelectParams(C.Structure):
 class LsIndexerParams(C.Structure):
     _fields_ = [("struct_size", C.c_int32), ("granularity", C.c_int32), ("topk", C.c_int32),
                 ("n_sink", C.c_int32), ("n_recent", C.c_int32), ("max_selected", C.c_int32),
-                ("candidates", C.c_int32)]
+                ("candidates", C.c_int32), ("approx", C.c_int32)]
 
 
 _P = C.c_void_p

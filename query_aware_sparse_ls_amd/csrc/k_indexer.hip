@@ -459,6 +459,7 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   __syncthreads();
   const int bstar = sh.bstar;
   const bool refine = bstar >= 0 && bstar < kIdxBins;
+  const bool digits = refine && !a.approx;   // approximate: no second / third digit
 
   // 2. this chunk: selected bits above b*; units of b* to the candidate list
   // and into the second-digit histogram
@@ -513,13 +514,13 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
       if ((cm >> lane) & 1ull) {
         const int u = cu0 + it * kIdxMarkThreads + wave * kWave + lane;
         st_dev(crow + cpos + mbcnt(cm), make_uint2(key[it], (uint32_t)u));
-        atomicAdd(&sh.h2[idx_d2(key[it])], 1u);
+        if (digits) atomicAdd(&sh.h2[idx_d2(key[it])], 1u);
       }
       cpos += __popcll(cm);
     }
   }
   __syncthreads();
-  if (refine) {
+  if (digits) {
     for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) {
       const uint32_t c = sh.h2[i];
       if (c) atomicAdd(gh2 + i, c);
@@ -555,7 +556,25 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
     idx_copy_in<kIdxBins / kIdxMarkThreads>(
         sh.h2, reinterpret_cast<const uint32_t*>(a.cand_blocks + (size_t)r * a.cand_cap), g.ncand);
   int ties_to_take = 0;
-  if (refine) {
+  constexpr int UN = 4;   // candidate loads in flight per thread
+  if (refine && a.approx) {
+    // early exit (Vortex, "Making it fast"): every unit of bucket b* is a
+    // tie; the emission takes the first `need` of them in unit order
+    const int nc = (int)ld_dev(ctl);
+    ties_to_take = kr - sh.cabove;
+    __syncthreads();
+    for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
+      uint2 c[UN];
+#pragma unroll
+      for (int j = 0; j < UN; ++j) {
+        const int i = i0 + j * kIdxMarkThreads + tid;
+        c[j] = i < nc ? crow[i] : make_uint2(0u, 0xFFFFFFFFu);
+      }
+#pragma unroll
+      for (int j = 0; j < UN; ++j)
+        if (c[j].y != 0xFFFFFFFFu) atomicOr(&sh.tie[c[j].y >> 5], 1u << (c[j].y & 31));
+    }
+  } else if (refine) {
     const int need = kr - sh.cabove;   // >= 1 units of bucket b* to select
     const int nc = (int)ld_dev(ctl);   // units in bucket b*
     idx_copy_in<kIdxBins / kIdxMarkThreads>(sh.h, gh2, kIdxBins);
@@ -566,7 +585,6 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
     // third digit over the candidates whose second digit is b2
     for (int i = tid; i < 256; i += kIdxMarkThreads) sh.h[i] = 0u;
     __syncthreads();
-    constexpr int UN = 4;   // candidate loads in flight per thread
     for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
       uint2 c[UN];
 #pragma unroll

@@ -158,7 +158,7 @@ extern "C" {
 
 const char* ls_last_error(void) { return g_err; }
 
-const char* ls_version(void) { return "libls 0.4.0 abi 4 gfx950"; }
+const char* ls_version(void) { return "libls 0.5.0 abi 5 gfx950"; }
 
 int32_t ls_attn_num_splits(int32_t max_selected) {
   if (max_selected < 1) return 1;
@@ -523,6 +523,8 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
     return fail(LS_ERR_INVALID, "candidates %d (LS_CAND_BLOCKS or LS_CAND_TOKENS)",
                 p->candidates);
   const bool tok_cands = p->candidates == LS_CAND_TOKENS;
+  if (p->approx != 0 && p->approx != 1) return fail(LS_ERR_INVALID, "approx %d (0 or 1)", p->approx);
+  if (p->approx && !tokens) return fail(LS_ERR_UNSUPPORTED, "approx is for LS_SEL_TOKENS");
   if (tok_cands && (!tokens || !cand_blocks))
     return fail(LS_ERR_INVALID, "LS_CAND_TOKENS needs LS_SEL_TOKENS and a candidate list");
   if (tok_cands && (long long)key_pool.num_pages * key_pool.page_size >= (1ll << 31))
@@ -584,6 +586,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
   a.cand_counts = cand_counts;
   a.cand_cap = cand_cap;
   a.unit_kind = tok_cands ? ls::kUnitsTokenCands : ls::kUnitsDefault;
+  a.approx = p->approx;
   a.max_units = U;
   a.n_sink = p->n_sink;
   a.n_recent = p->n_recent;

@@ -145,6 +145,7 @@ struct IndexerArgs {
   const int32_t* cand_blocks;  // tokens, optional: [B][cand_cap] ascending block ids
                                // (token ids with kUnitsTokenCands)
   int32_t unit_kind;           // kUnits*
+  int32_t approx;              // tokens: 1 = fill from the boundary bucket in unit order
   const uint16_t* codebooks;   // PQ coarse scoring: [32][256][4] bf16 (keys = codes)
   const int32_t* cand_counts;  // [B]
   int32_t cand_cap;
