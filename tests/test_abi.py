@@ -180,3 +180,81 @@ def test_bounds_validation():
     assert f(FAKE, _pool(num_heads=0), FAKE, 1, FAKE, None) == _lib.LS_ERR_INVALID
     assert f(None, _pool(), FAKE, 1, FAKE, None) == _lib.LS_ERR_INVALID
     assert f(FAKE, _pool(), FAKE, 1, None, None) == _lib.LS_ERR_INVALID
+
+
+def _ipool(**kw):
+    d = dict(num_pages=8, num_heads=1, page_size=64, head_dim=128,
+             dtype=_lib.LS_DTYPE_FP8_E4M3FN)
+    d.update(kw)
+    return _lib.LsPool(**d)
+
+
+def _iparams(**kw):
+    d = dict(struct_size=C.sizeof(_lib.LsIndexerParams), granularity=_lib.LS_SEL_TOKENS, topk=8,
+             n_sink=0, n_recent=0, max_selected=8, candidates=_lib.LS_CAND_BLOCKS, approx=0)
+    d.update(kw)
+    return _lib.LsIndexerParams(**d)
+
+
+def test_indexer_token_candidates_and_approx_validation():
+    lib = _lib.load()
+
+    def call(p, cand=FAKE, cap=4, pool=None, batch=None):
+        return lib.ls_indexer_select(FAKE, _lib.LS_DTYPE_BF16, 64, FAKE, FAKE, None,
+                                     pool or _ipool(), batch or _batch(), cand, FAKE, cap,
+                                     C.byref(p), FAKE, FAKE, None, None, 0, None)
+
+    assert call(_iparams(candidates=3)) == _lib.LS_ERR_INVALID
+    assert call(_iparams(candidates=_lib.LS_CAND_TOKENS), cand=None) == _lib.LS_ERR_INVALID
+    assert call(_iparams(candidates=_lib.LS_CAND_TOKENS, granularity=_lib.LS_SEL_BLOCKS),
+                pool=_ipool(dtype=_lib.LS_DTYPE_BF16)) == _lib.LS_ERR_INVALID
+    assert call(_iparams(approx=2)) == _lib.LS_ERR_INVALID
+    assert call(_iparams(approx=1, granularity=_lib.LS_SEL_BLOCKS), cand=None,
+                pool=_ipool(dtype=_lib.LS_DTYPE_BF16)) == _lib.LS_ERR_UNSUPPORTED
+    assert call(_iparams(candidates=_lib.LS_CAND_TOKENS),
+                pool=_ipool(num_pages=1 << 26)) == _lib.LS_ERR_UNSUPPORTED   # rows >= 2^31
+    # valid arguments but no workspace: the workspace check is last
+    assert call(_iparams(candidates=_lib.LS_CAND_TOKENS, approx=1)) == _lib.LS_ERR_WORKSPACE
+    # empty batch: valid, nothing enqueued
+    assert call(_iparams(candidates=_lib.LS_CAND_TOKENS),
+                batch=_batch(batch_size=0)) == _lib.LS_OK
+
+
+def test_pq_validation():
+    lib = _lib.load()
+    enc = lib.ls_pq_encode
+    assert enc(FAKE, None, _ipool(), FAKE, -1, FAKE, FAKE, None) == _lib.LS_ERR_INVALID
+    assert enc(FAKE, None, _ipool(), FAKE, 0, FAKE, FAKE, None) == _lib.LS_OK
+    assert enc(FAKE, None, _ipool(dtype=_lib.LS_DTYPE_BF16), FAKE, 1, FAKE, FAKE,
+               None) == _lib.LS_ERR_UNSUPPORTED
+    assert enc(FAKE, None, _ipool(head_dim=64), FAKE, 1, FAKE, FAKE, None) == _lib.LS_ERR_UNSUPPORTED
+    assert enc(FAKE, None, _ipool(page_size=8), FAKE, 1, FAKE, FAKE, None) == _lib.LS_ERR_UNSUPPORTED
+    assert enc(FAKE, None, _ipool(), FAKE, 1, FAKE + 8, FAKE, None) == _lib.LS_ERR_INVALID  # align
+    assert enc(FAKE, None, _ipool(), FAKE, 1, FAKE, None, None) == _lib.LS_ERR_INVALID
+    tr = lib.ls_pq_train
+    ws = lib.ls_pq_train_workspace_size()
+    assert ws >= 32 * 256 * 4 * 8 + 32 * 256 * 4
+    assert tr(FAKE, None, _ipool(), FAKE, 0, FAKE, 1, FAKE, FAKE, ws, None) == _lib.LS_ERR_INVALID
+    assert tr(FAKE, None, _ipool(), FAKE, 4, FAKE, 1001, FAKE, FAKE, ws, None) == _lib.LS_ERR_INVALID
+    assert tr(FAKE, None, _ipool(), FAKE, 4, None, 1, FAKE, FAKE, ws, None) == _lib.LS_ERR_INVALID
+    assert tr(FAKE, None, _ipool(), FAKE, 4, FAKE, 1, FAKE, FAKE, ws - 1,
+              None) == _lib.LS_ERR_WORKSPACE
+    assert tr(FAKE, None, _ipool(), FAKE, 4, FAKE, 1, FAKE, FAKE + 16, ws,
+              None) == _lib.LS_ERR_INVALID                                   # workspace align
+    sel = lib.ls_pq_select
+
+    def s(**kw):
+        a = dict(q=FAKE, qd=_lib.LS_DTYPE_BF16, h=64, w=FAKE, codes=FAKE, cb=FAKE, pool=_ipool(),
+                 batch=_batch(), n=16, cand=FAKE, cnt=FAKE, ws=None, wsb=0)
+        a.update(kw)
+        return sel(a["q"], a["qd"], a["h"], a["w"], a["codes"], a["cb"], a["pool"], a["batch"],
+                   a["n"], a["cand"], a["cnt"], None, a["ws"], a["wsb"], None)
+
+    assert s(h=48) == _lib.LS_ERR_UNSUPPORTED
+    assert s(qd=_lib.LS_DTYPE_FP32) == _lib.LS_ERR_UNSUPPORTED
+    assert s(n=-1) == _lib.LS_ERR_INVALID
+    assert s(cand=None) == _lib.LS_ERR_INVALID
+    assert s(codes=FAKE + 4) == _lib.LS_ERR_INVALID                          # codes 8-byte aligned
+    assert s(batch=_batch(max_blocks=5000)) == _lib.LS_ERR_UNSUPPORTED       # > 262144 tokens
+    assert s() == _lib.LS_ERR_WORKSPACE
+    assert s(batch=_batch(batch_size=0)) == _lib.LS_OK
