@@ -388,6 +388,36 @@ def sparse_attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     return _round_out(np.stack(outs), out_dtype), np.array(lses)
 
 
+def window_tokens(seq_len: int, n_sink: int, window: int) -> np.ndarray:
+    """Tokens of the sink + recent window (ByteCross, Appendix A, after
+    attention sinks): the first min(n_sink, L) tokens and the last `window`
+    tokens, without repeats, ascending."""
+    L = int(seq_len)
+    ns = min(int(n_sink), L)
+    lo = max(ns, L - int(window))
+    return np.concatenate([np.arange(ns), np.arange(lo, L)]).astype(np.int64)
+
+
+def window_attention(q_bits, k_bits, v_bits, batch: BatchView, r: int, g: int, *,
+                     n_sink: int, window: int, num_kv_heads: int, sm_scale: float,
+                     out_dtype: str = "bf16") -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of every query head of kv group g of request r over the
+    sink + recent window tokens, read in place (one exact softmax over the
+    union; the paper's two calls merged by log-sum-exp give the same)."""
+    Hq = q_bits.shape[1]
+    G = Hq // num_kv_heads
+    t = window_tokens(int(batch.seq_lens[r]), n_sink, window)
+    page, slot = batch.token_page_slot(r, t)
+    K = bf16_to_f64(np.asarray(k_bits)[page, g, slot])
+    V = bf16_to_f64(np.asarray(v_bits)[page, g, slot])
+    outs, lses = [], []
+    for h in range(g * G, (g + 1) * G):
+        o, lse = attention_over_tokens(bf16_to_f64(q_bits[r, h]), K, V, sm_scale)
+        outs.append(o)
+        lses.append(lse)
+    return _round_out(np.stack(outs), out_dtype), np.array(lses)
+
+
 def dense_attention(q_bits, k_bits, v_bits, batch: BatchView, r: int, g: int, *,
                     num_kv_heads: int, sm_scale: float, out_dtype: str = "bf16"):
     """The k = all case: every block of the request selected."""

@@ -621,3 +621,48 @@ def test_approx_topk_keeps_every_certain_winner():
         assert len(got) == k
         assert {i for i in range(3000) if b[i] > kth} <= got & exact
         assert all(b[i] >= kth for i in got)
+
+
+# ------------------------------------------------------- sink + recent window
+
+def test_window_tokens_cases():
+    from oracle.method import window_tokens
+    assert list(window_tokens(100, 4, 10)) == [0, 1, 2, 3] + list(range(90, 100))
+    assert list(window_tokens(12, 4, 10)) == list(range(12))        # ranges touch
+    assert list(window_tokens(3, 4, 10)) == [0, 1, 2]                # shorter than the sinks
+    assert list(window_tokens(50, 0, 5)) == list(range(45, 50))
+    assert list(window_tokens(50, 4, 0)) == [0, 1, 2, 3]
+    assert list(window_tokens(0, 4, 10)) == []
+
+
+def test_window_attention_is_the_lse_merge_of_two_calls():
+    """The paper's form: the window and the sinks as two calls merged by
+    log-sum-exp; equal to one softmax over the union."""
+    from oracle.method import window_attention, window_tokens
+    rng = np.random.default_rng(60)
+    batch, npg = _tiny_batch(rng, lens=(37, 9))
+    k = _rand_bf16(rng, (npg, 2, 4, 8))
+    v = _rand_bf16(rng, (npg, 2, 4, 8))
+    q = _rand_bf16(rng, (2, 4, 8))
+    for r in range(2):
+        L = int(batch.seq_lens[r])
+        o, lse = window_attention(q, k, v, batch, r, 1, n_sink=3, window=20, num_kv_heads=2,
+                                  sm_scale=0.3, out_dtype="fp64")
+        t = window_tokens(L, 3, 20)
+        sinks, win = t[t < 3], t[t >= 3]
+        for i, h in enumerate((2, 3)):
+            parts = []
+            for part in (sinks, win):
+                page, slot = batch.token_page_slot(r, part)
+                K = bf16_to_f64(k[page, 1, slot])
+                V = bf16_to_f64(v[page, 1, slot])
+                parts.append(attention_over_tokens(bf16_to_f64(q[r, h]), K, V, 0.3))
+            mo, ml = lse_merge(parts)
+            np.testing.assert_allclose(o[i], mo, rtol=1e-12, atol=1e-14)
+            assert abs(lse[i] - ml) <= 1e-12 * max(1.0, abs(ml))
+        # a window covering everything is dense attention
+        od, ld = dense_attention(q, k, v, batch, r, 1, num_kv_heads=2, sm_scale=0.3,
+                                 out_dtype="fp64")
+        ow, lw = window_attention(q, k, v, batch, r, 1, n_sink=0, window=L, num_kv_heads=2,
+                                  sm_scale=0.3, out_dtype="fp64")
+        np.testing.assert_allclose(ow, od, rtol=1e-12, atol=1e-14)
