@@ -639,10 +639,12 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
     return 0
 
 
-def bench_dense(args) -> int:
+def bench_dense(args, window: bool = False) -> int:
     """Time the k = all path: split-K attention over every block of the
     8B/32K/B16 workload (ls_sparse_attn_decode with no selection), the dense
-    baseline the sparse step's speedup is judged against."""
+    baseline the sparse step's speedup is judged against; or (window) the
+    sink + recent window of the same batch: 4 sinks and the last 30% of the
+    tokens, read in place (ls_window_attn_decode)."""
     import torch
     import query_aware_sparse_ls_amd as ls
     from workloads import LLAMA8B_32K_B16, make_block_topk_inputs
@@ -652,22 +654,30 @@ def bench_dense(args) -> int:
     B, Hq, Hkv, D, P = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
     sm = 1.0 / math.sqrt(D)
     R = max(1, min(args.replicas, 2))    # one step reads 2 GiB: no cache reuse either way
+    N_SINK, WIN = 4, int(0.3 * cfg.context)   # the window: 4 sinks + 30% of the tokens
     reps = []
     for i in range(R):
         inp = make_block_topk_inputs(cfg, device=dev, seed=cfg.seed + i)
         b = ls.PagedBatch(inp.page_indptr, inp.page_indices, inp.seq_lens, inp.max_blocks())
         reps.append(dict(inp=inp, batch=b,
                          out=torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev),
-                         ws=torch.empty(ls.sparse_attn_decode_workspace_size(
-                             B, Hq, D, 0, b.max_blocks), dtype=torch.uint8, device=dev)))
+                         ws=torch.empty(max(ls.sparse_attn_decode_workspace_size(
+                             B, Hq, D, 0, b.max_blocks), int(ls._lib.EXPORTS[
+                                 "ls_window_attn_decode_workspace_size"](
+                                 B, Hq, D, b.max_blocks, N_SINK, WIN))),
+                             dtype=torch.uint8, device=dev)))
     torch.cuda.synchronize()
     print(f"# {R} replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB",
           file=sys.stderr, flush=True)
 
     def call(rp):
         inp = rp["inp"]
-        ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, rp["batch"], None, None,
-                              sm_scale=sm, out=rp["out"], workspace=rp["ws"])
+        if window:
+            ls.window_attn_decode(inp.q, inp.k_pool, inp.v_pool, rp["batch"], n_sink=N_SINK,
+                                  window=WIN, sm_scale=sm, out=rp["out"], workspace=rp["ws"])
+        else:
+            ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, rp["batch"], None, None,
+                                  sm_scale=sm, out=rp["out"], workspace=rp["ws"])
 
     for i in range(max(1, args.warmup)):
         call(reps[i % R])
@@ -682,28 +692,34 @@ def bench_dense(args) -> int:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     L = cfg.context
-    kv = B * L * Hkv * D * 2 * 2
-    nbytes = {"kv": kv, "q_out_pagetable": B * Hq * D * 2 * 2 + B * (L // P) * 4}
+    ntok = min(L, N_SINK + WIN) if window else L
+    kv = B * ntok * Hkv * D * 2 * 2
+    nbytes = {"kv": kv, "q_out_pagetable": B * Hq * D * 2 * 2 + B * (-(-ntok // P) + 1) * 4}
     nbytes["total"] = sum(nbytes.values())
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
-    tr = stored_traffic("attn_chunk_kernel.llama8b_32k_b16_dense")
-    res = {"metric": "dense (k = all) split-K decode attention calls/sec at 8B/32K/B16",
+    key = "attn_window_kernel.llama8b_32k_b16_window" if window else \
+        "attn_chunk_kernel.llama8b_32k_b16_dense"
+    tr = stored_traffic(key)
+    res = {"metric": ("sink + recent window decode attention calls/sec at 8B/32K/B16" if window
+                      else "dense (k = all) split-K decode attention calls/sec at 8B/32K/B16"),
            "value": round(1e3 / ms, 2), "unit": "calls/s", "n_gpus": 1, "steps": steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": cfg.name + " dense", "batch": B, "context": L, "q_heads": Hq,
-                      "kv_heads": Hkv, "head_dim": D, "page_size": P, "replicas": R,
-                      "timing": "eager, back-to-back calls"},
+           "config": {"workload": cfg.name + (" window" if window else " dense"), "batch": B,
+                      "context": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                      "page_size": P, "replicas": R, "timing": "eager, back-to-back calls",
+                      **({"n_sink": N_SINK, "window": WIN} if window else {})},
            "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
-           "roofline": {"kernel": "ls::attn_chunk_kernel<128> + ls::attn_combine_kernel<128> "
-                                  "(one library call)", "bound": "hbm",
+           "roofline": {"kernel": ("ls::attn_window_kernel<128>" if window else
+                                   "ls::attn_chunk_kernel<128>") +
+                                  " + ls::attn_combine_kernel<128> (one library call)",
+                        "bound": "hbm",
                         "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(gbps / HBM_PEAK_GBPS, 4),
                         "traffic": tr["traffic_bytes"] if tr else None,
                         "algorithmic_bytes_per_launch": nbytes["total"],
                         "avg_launch_ms": round(ms, 5),
-                        "traffic_source": ("profiles/attn_chunk_kernel.llama8b_32k_b16_dense.md"
-                                           if tr else None)},
+                        "traffic_source": (f"profiles/{key}.md" if tr else None)},
            "device": torch.cuda.get_device_name(0)}
     print(json.dumps(res), flush=True)
     return 0
@@ -734,7 +750,8 @@ def main(argv=None) -> int:
                          "in index order) instead of the exact one; reports its recall")
     ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
                     help="block-topk path: block-mean summaries (default) or Quest bounds")
-    ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense", "pq"),
+    ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense", "pq",
+                                       "window"),
                     default="block-topk",
                     help="block-topk: the 8B/32K/B16 block top-k step (default); indexer: "
                          "token top-2048 of 8 x 128K + sparse MLA; coarse-to-fine: 4 x 950K; "
@@ -749,8 +766,8 @@ def main(argv=None) -> int:
         return 2
     if args.copy_calibrate:
         return copy_calibration(args.copy_calibrate)
-    if args.path == "dense":
-        return bench_dense(args)
+    if args.path in ("dense", "window"):
+        return bench_dense(args, window=args.path == "window")
     if args.path != "block-topk":
         return bench_indexer(args, coarse=args.path == "coarse-to-fine", pq=args.path == "pq")
 

@@ -466,6 +466,34 @@ ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_hea
                                size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* 8. Sink + recent window attention, in place                               */
+/* ------------------------------------------------------------------------ */
+/*
+ * The window baseline of the ByteCross paper ("Where Activation Sparsity and
+ * KV-Cache Sparsity Cross in LLM Decoding", §4.1 and Appendix A, after
+ * attention sinks): every query head attends, exactly, the tokens
+ *   [0, ns) and [lo, L),  ns = min(n_sink, L),  lo = max(ns, L - window)
+ * of its request, read where they are in the paged cache (no copy). The
+ * paper runs the window and the sinks as two calls merged by log-sum-exp;
+ * here both ranges are positions of one split-K call whose splits are merged
+ * by the same log-sum-exp combine. A block holding both the last sinks and
+ * the first window tokens is read twice with disjoint token ranges.
+ * Arguments as in ls_sparse_attn_decode (no selection); n_sink, window >= 0;
+ * pool.num_pages < 2^22. lse_out (optional) gets the natural-log LSE of the
+ * logits over the attended tokens (-inf for an empty request, whose output
+ * is 0). workspace: >= ls_window_attn_decode_workspace_size() bytes,
+ * 256-byte aligned.
+ */
+size_t ls_window_attn_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
+                                            int32_t head_dim, int32_t max_blocks, int32_t n_sink,
+                                            int32_t window);
+ls_status ls_window_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                const void* k_pool, const void* v_pool, ls_pool pool,
+                                ls_batch batch, int32_t n_sink, int32_t window, float sm_scale,
+                                void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* 7. PQ32 coarse scoring of indexer keys                                    */
 /* ------------------------------------------------------------------------ */
 /*

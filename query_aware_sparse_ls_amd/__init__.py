@@ -28,7 +28,7 @@ __all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_s
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
            "sparse_decode_step_workspace", "indexer_select", "indexer_select_workspace_size",
            "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
-           "mla_num_splits", "pq_encode", "pq_train", "pq_select"]
+           "mla_num_splits", "pq_encode", "pq_train", "pq_select", "window_attn_decode"]
 
 _DT = {torch.bfloat16: LS_DTYPE_BF16, torch.float32: LS_DTYPE_FP32,
        torch.float8_e4m3fn: LS_DTYPE_FP8_E4M3FN}
@@ -471,3 +471,33 @@ def pq_select(q: torch.Tensor, head_weights: torch.Tensor, codes: torch.Tensor,
                           _ptr(scores_out), ws.data_ptr(), ws.numel() * ws.element_size(),
                           _stream(stream)))
     return candidates, counts
+
+
+# ------------------------------------------------------------ sink + window
+
+def window_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                       batch: PagedBatch, *, n_sink: int, window: int, sm_scale: float,
+                       out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+                       lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Exact attention of every query head over its request's first n_sink
+    tokens and last `window` tokens, read in place."""
+    _need(q, torch.bfloat16); _need(k_pool, torch.bfloat16); _need(v_pool, torch.bfloat16)
+    B, Hq, D = q.shape
+    _, Hkv, P, _ = k_pool.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=out_dtype, device=dev)
+    _need(out)
+    if lse is not None:
+        _need(lse, torch.float32)
+    n = int(_L.ls_window_attn_decode_workspace_size(B, Hq, D, batch.max_blocks, int(n_sink),
+                                                     int(window)))
+    ws = _workspace(n, dev, workspace)
+    check(_L.ls_window_attn_decode(q.data_ptr(), LS_DTYPE_BF16, int(Hq), k_pool.data_ptr(),
+                                   v_pool.data_ptr(), _pool(k_pool, int(Hkv), int(P), int(D)),
+                                   batch.c(), int(n_sink), int(window), float(sm_scale),
+                                   out.data_ptr(), _DT[out.dtype], _ptr(lse), ws.data_ptr(),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
+    return out, lse

@@ -67,6 +67,10 @@ _SIGS = {
     "ls_sparse_mla_decode": (C.c_int, [_P, C.c_int32, C.c_int32, _P, LsPool, LsBatch, _P, _P,
                                        C.c_int32, C.c_float, _P, C.c_int32, _P, _P, C.c_size_t,
                                        _P]),
+    "ls_window_attn_decode_workspace_size": (C.c_size_t, [C.c_int32] * 6),
+    "ls_window_attn_decode": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, LsPool, LsBatch,
+                                        C.c_int32, C.c_int32, C.c_float, _P, C.c_int32, _P, _P,
+                                        C.c_size_t, _P]),
     "ls_pq_encode": (C.c_int, [_P, _P, LsPool, _P, C.c_int32, _P, _P, _P]),
     "ls_pq_train_workspace_size": (C.c_size_t, []),
     "ls_pq_train": (C.c_int, [_P, _P, LsPool, _P, C.c_int32, _P, C.c_int32, _P, _P, C.c_size_t,

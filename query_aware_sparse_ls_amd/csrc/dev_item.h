@@ -408,7 +408,10 @@ struct ItemSplit {
   int s;
 };
 
-template <int D>
+// kLo: entries carry a first valid token too (e = page * 512 + lo * 32 +
+// nt: tokens lo .. nt-1 of the block are attended; page < 2^22), for token
+// ranges that start inside a block.
+template <int D, bool kLo = false>
 __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const int* ent,
                                           int cnt, ItemAttnLds<D>& sh,
                                           const ItemPair* pair = nullptr,
@@ -437,14 +440,16 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
   const int nbw = cnt > first ? (cnt - first + step - 1) / step : 0;
   const int nent = item_entry_count(cnt);   // entries written by item_entries
 
+  constexpr int PSH = kLo ? 9 : 5;   // page bits start here
   uint4 kr[NPF][NL], vr[NPF][NL];
-  int ntok[NPF];
+  int ntok[NPF], lotok[NPF];
 #pragma unroll
   for (int s = 0; s < NPF; ++s) {
     const int ie = first + step * s;
     const int e = ie < nent ? ent[ie] : -1;
     ntok[s] = e >= 0 ? (e & 31) : 0;
-    const uint64_t off = (uint64_t)(uint32_t)(e >= 0 ? e >> 5 : 0) * pstride;
+    lotok[s] = kLo && e >= 0 ? (e >> 5) & 15 : 0;
+    const uint64_t off = (uint64_t)(uint32_t)(e >= 0 ? e >> PSH : 0) * pstride;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       kr[s][j] = ldg16_stream(kb + off + (size_t)j * ST::RPI * D);
@@ -469,10 +474,12 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
         // invalid entry) are zeroed: their weights are 0, but their contents
         // are unspecified and 0 * NaN would reach the output. K rows need no
         // such care: their logits are masked.
-        if (ntok[s] < 16) {
+        if (ntok[s] < 16 || (kLo && lotok[s] > 0)) {
 #pragma unroll
-          for (int j = 0; j < NL; ++j)
-            if (j * ST::RPI + lane / ST::LPR >= ntok[s]) vr[s][j] = make_uint4(0, 0, 0, 0);
+          for (int j = 0; j < NL; ++j) {
+            const int tr = j * ST::RPI + lane / ST::LPR;
+            if (tr >= ntok[s] || (kLo && tr < lotok[s])) vr[s][j] = make_uint4(0, 0, 0, 0);
+          }
         }
         // stage the K and V tiles (row-major, padded rows)
         stage_k<D>(kt, kr[s], 0u);
@@ -490,7 +497,7 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
         float z[4], bm = kNegInf;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = head_lane && 4 * kq + i < ntok[s];
+          const bool ok = head_lane && 4 * kq + i < ntok[s] && (!kLo || 4 * kq + i >= lotok[s]);
           z[i] = ok ? z4[i] * a.sm_scale_log2 : kNegInf;
           bm = fmaxf(bm, z[i]);
         }
@@ -548,7 +555,8 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
       }
       __builtin_amdgcn_sched_barrier(0);   // refill after the use (loads complete in order)
       ntok[s] = en >= 0 ? (en & 31) : 0;
-      const uint64_t off = (uint64_t)(uint32_t)(en >= 0 ? en >> 5 : 0) * pstride;
+      lotok[s] = kLo && en >= 0 ? (en >> 5) & 15 : 0;
+      const uint64_t off = (uint64_t)(uint32_t)(en >= 0 ? en >> PSH : 0) * pstride;
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         kr[s][j] = ldg16_stream(kb + off + (size_t)j * ST::RPI * D);

@@ -252,6 +252,84 @@ __global__ __launch_bounds__(kItemThreads) void attn_chunk_kernel(AttnArgs a, in
   item_attn<D>(a, r, g, ent, cnt, sh, nullptr, &sp);
 }
 
+// Split s of pair (r, g) of the sink + recent window: the pair's positions
+// are the sink blocks (tokens [0, ns), ns = min(win_sink, L)) then the
+// window blocks (tokens [lo, L), lo = max(ns, L - win_len)); when lo = ns the
+// two ranges touch and the positions are simply the request's blocks. A
+// block holding both the last sinks and the first window tokens appears
+// twice, with disjoint token ranges. Walk entries carry the first valid
+// token (item_attn's kLo form).
+template <int D>
+__global__ __launch_bounds__(kItemThreads) void attn_window_kernel(AttnArgs a, int chunk) {
+  __shared__ int ent[kChunkMaxBlocks + kItemEntryPad];
+  __shared__ ItemAttnLds<D> sh;
+  const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const ReqGeom geo = req_geom(a.b, r, 0, 0);
+  const int L = geo.L;
+  const int ns = a.win_sink < L ? a.win_sink : L;
+  const int lw = L - a.win_len;
+  const int lo = lw > ns ? lw : ns;
+  const bool gap = lo > ns;
+  const int nsb = gap ? (ns + 15) / 16 : 0;          // sink positions
+  const int wb0 = gap ? lo / 16 : 0;                  // first window block
+  const int t_lo = gap ? lo : 0;                      // first window token (all tokens: 0)
+  const int total = nsb + (geo.nb - wb0 > 0 ? geo.nb - wb0 : 0);
+  const int p0 = s * chunk;
+  int cnt = total - p0;
+  cnt = cnt < 0 ? 0 : (cnt > chunk ? chunk : cnt);
+  const int32_t* pages = a.b.indices + geo.page_base;
+  for (int pos = threadIdx.x; pos < item_entry_count(cnt); pos += kItemThreads) {
+    int e = -1;
+    if (pos < cnt) {
+      const int q = p0 + pos;
+      int blk, t0, t1;   // tokens [t0, t1) of block blk
+      if (q < nsb) {
+        blk = q;
+        t0 = 16 * blk;
+        t1 = ns < 16 * blk + 16 ? ns : 16 * blk + 16;
+      } else {
+        blk = wb0 + (q - nsb);
+        t0 = t_lo > 16 * blk ? t_lo : 16 * blk;
+        t1 = L < 16 * blk + 16 ? L : 16 * blk + 16;
+      }
+      if (blk >= 0 && blk < geo.nb && t1 > t0) {
+        const int p = pages[blk];
+        if (p >= 0 && p < a.b.num_pages) e = p * 512 + (t0 - 16 * blk) * 32 + (t1 - 16 * blk);
+      }
+    }
+    ent[pos] = e;
+  }
+  __syncthreads();
+  const ItemSplit sp{a.partials, a.num_splits, s};
+  item_attn<D, true>(a, r, g, ent, cnt, sh, nullptr, &sp);
+}
+
+hipError_t launch_attn_window(const AttnArgs& a0, int max_pos, hipStream_t st) {
+  AttnArgs a = a0;
+  const int n = max_pos < 1 ? 1 : max_pos;
+  const int pairs = a.b.batch * a.num_kv_heads;
+  constexpr int kTargetWgs = 2048;
+  int splits = (kTargetWgs + pairs - 1) / pairs;
+  const int most = (n + 15) / 16;
+  splits = splits > most ? most : splits;
+  splits = splits < 1 ? 1 : splits;
+  int chunk = (n + splits - 1) / splits;
+  chunk = (chunk + kAttnBlocksPerSplit - 1) / kAttnBlocksPerSplit * kAttnBlocksPerSplit;
+  chunk = chunk > kChunkMaxBlocks ? kChunkMaxBlocks : chunk;
+  chunk = chunk < kAttnBlocksPerSplit ? kAttnBlocksPerSplit : chunk;
+  a.num_splits = (n + chunk - 1) / chunk;
+  if (a.num_splits < 1) a.num_splits = 1;
+  if (a.num_splits > a0.num_splits) return hipErrorInvalidValue;   // partials capacity
+  const dim3 grid(a.num_splits, a.num_kv_heads, a.b.batch);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((attn_window_kernel<128>), grid, dim3(kItemThreads), 0, st, a, chunk);
+  else
+    hipLaunchKernelGGL((attn_window_kernel<64>), grid, dim3(kItemThreads), 0, st, a, chunk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn_combine(a, st);
+}
+
 bool pair_path(int batch, int hkv, int max_blocks) {
   return (long long)batch * hkv <= kPairMaxPairs && max_blocks > kPairMinBlocks;
 }

@@ -149,6 +149,8 @@ ls::AttnArgs attn_args(const void* q, int num_q_heads, const void* k_pool, const
   aa.out = out;
   aa.out_dtype = out_dtype;
   aa.lse = lse;
+  aa.win_sink = 0;
+  aa.win_len = 0;
   return aa;
 }
 
@@ -694,6 +696,69 @@ ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_hea
   return hip_status(ls::launch_mla(a, stream), "MLA kernel launches");
 }
 
+
+// ---------------------------------------------------- sink + window ----
+
+namespace {
+
+int window_positions(int32_t max_blocks, int32_t n_sink, int32_t window) {
+  const long long p = ((long long)n_sink + 15) / 16 + ((long long)window + 15) / 16 + 1;
+  return (int)std::min<long long>(p, (long long)max_blocks + 1);
+}
+
+}  // namespace
+
+size_t ls_window_attn_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
+                                            int32_t head_dim, int32_t max_blocks, int32_t n_sink,
+                                            int32_t window) {
+  if (batch_size <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks <= 0 || n_sink < 0 ||
+      window < 0)
+    return 0;
+  const size_t S = (size_t)ls_attn_num_splits(window_positions(max_blocks, n_sink, window));
+  return align_up((size_t)batch_size * num_q_heads * S * (head_dim + 2) * sizeof(float));
+}
+
+ls_status ls_window_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                const void* k_pool, const void* v_pool, ls_pool pool,
+                                ls_batch batch, int32_t n_sink, int32_t window, float sm_scale,
+                                void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  if ((st = check_gqa_pool(pool, "kv pool")) != LS_OK) return st;
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (out_dtype != LS_DTYPE_BF16 && out_dtype != LS_DTYPE_FP32)
+    return fail(LS_ERR_UNSUPPORTED, "out_dtype %d (supported: bf16, fp32)", out_dtype);
+  if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
+    return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                pool.num_heads);
+  if (num_q_heads / pool.num_heads != 4)
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
+                num_q_heads / pool.num_heads);
+  if (n_sink < 0 || window < 0) return fail(LS_ERR_INVALID, "n_sink and window must be >= 0");
+  if (pool.num_pages >= (1 << 22))
+    return fail(LS_ERR_UNSUPPORTED, "num_pages %d (supported: < 2^22)", pool.num_pages);
+  if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
+  if (batch.batch_size == 0) return ok();
+  if (!q || !k_pool || !v_pool || !out)
+    return fail(LS_ERR_INVALID, "q, k_pool, v_pool and out must be non-null");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(LS_ERR_INVALID, "q, k_pool and v_pool must be 16-byte aligned");
+  const int npos = window_positions(batch.max_blocks, n_sink, window);
+  const size_t ws = ls_window_attn_decode_workspace_size(batch.batch_size, num_q_heads,
+                                                         pool.head_dim, batch.max_blocks, n_sink,
+                                                         window);
+  if (!workspace || workspace_bytes < ws)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  ls::AttnArgs aa = attn_args(q, num_q_heads, k_pool, v_pool, pool, batch, nullptr, nullptr, 0,
+                              ls_attn_num_splits(npos), sm_scale,
+                              static_cast<float*>(workspace), out, out_dtype, lse_out);
+  aa.win_sink = n_sink;
+  aa.win_len = window;
+  return hip_status(ls::launch_attn_window(aa, npos, stream), "window attention launches");
+}
 
 // ------------------------------------------------------------------ PQ32 ----
 

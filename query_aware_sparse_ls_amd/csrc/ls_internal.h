@@ -66,6 +66,7 @@ struct AttnArgs {
   void* out;
   int32_t out_dtype;
   float* lse;
+  int32_t win_sink, win_len;  // window attention: sinks [0, win_sink) + the last win_len tokens
 };
 
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t st);
@@ -119,6 +120,10 @@ hipError_t launch_attn_item(const AttnArgs& a, hipStream_t st);
 // partials (splits of kAttnBlocksPerSplit), which the chunking never exceeds.
 constexpr int kChunkMaxBlocks = 512;
 hipError_t launch_attn_chunked(const AttnArgs& a, hipStream_t st);
+// Sink + recent window: tokens [0, min(win_sink, L)) and [max(that, L -
+// win_len), L) of every request, in place, split over runs of positions like
+// the dense path (max_pos: positions per pair at most).
+hipError_t launch_attn_window(const AttnArgs& a, int max_pos, hipStream_t st);
 hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnArgs& aa,
                             const SummaryUpdate& up, hipStream_t st);
 
