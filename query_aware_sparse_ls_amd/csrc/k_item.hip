@@ -308,7 +308,7 @@ hipError_t launch_attn_window(const AttnArgs& a0, int max_pos, hipStream_t st) {
   AttnArgs a = a0;
   const int n = max_pos < 1 ? 1 : max_pos;
   const int pairs = a.b.batch * a.num_kv_heads;
-  constexpr int kTargetWgs = 2048;
+  constexpr int kTargetWgs = 512;   // two per CU: windows are short, longer runs ramp less
   int splits = (kTargetWgs + pairs - 1) / pairs;
   const int most = (n + 15) / 16;
   splits = splits > most ? most : splits;
