@@ -40,5 +40,5 @@ from .method import (  # noqa: F401
     indexer_token_scores, select_tokens, mla_attention, decode_step,
     tokens_of_blocks, topk_from_keep_ratio, forced_blocks, indexer_block_scores,
     coarse_to_fine_select, block_bounds, bound_scores, approx_select_tokens, score_bucket,
-    window_tokens, window_attention,
+    window_tokens, window_attention, snapkv_scores, snapkv_select,
 )

@@ -418,6 +418,53 @@ def window_attention(q_bits, k_bits, v_bits, batch: BatchView, r: int, g: int, *
     return _round_out(np.stack(outs), out_dtype), np.array(lses)
 
 
+def snapkv_scores(q_obs_bits: np.ndarray, k_bits: np.ndarray, batch: BatchView, r: int, g: int,
+                  *, num_kv_heads: int, sm_scale: float) -> np.ndarray:
+    """One-time SnapKV-style scores of request r's cache for kv head g
+    (ByteCross §4.1 and Appendix A, "Scored selection"): the last W prompt
+    tokens' queries q_obs [B][W][Hq][D] (bf16 bits; observation query w sits
+    at position L - W + w and attends positions <= its own) each give a
+    softmax over the cache; the score of position t is the sum of those
+    probabilities over the W queries and the group's query heads (pooled).
+    Returns float64 [L]."""
+    W, Hq = q_obs_bits.shape[1], q_obs_bits.shape[2]
+    G = Hq // num_kv_heads
+    L = int(batch.seq_lens[r])
+    t = np.arange(L)
+    page, slot = batch.token_page_slot(r, t)
+    K = bf16_to_f64(np.asarray(k_bits)[page, g, slot])                  # [L][D]
+    score = np.zeros(L)
+    for w in range(W):
+        pos = L - W + w
+        for h in range(g * G, (g + 1) * G):
+            z = float(sm_scale) * (K[:pos + 1] @ bf16_to_f64(q_obs_bits[r, w, h]))
+            e = np.exp(z - z.max())
+            score[:pos + 1] += e / e.sum()
+    return score
+
+
+def snapkv_select(q_obs_bits: np.ndarray, k_bits: np.ndarray, batch: BatchView, r: int, g: int,
+                  *, num_kv_heads: int, sm_scale: float, n_sink: int, budget: int,
+                  pool: int = 7) -> List[int]:
+    """Positions kept for kv head g of request r: the first n_sink positions
+    and the W observation positions are forced; the rest of the budget goes to
+    the prefix positions [n_sink, L - W) with the largest pooled score, the
+    scores averaged over a window of `pool` positions centred on each (zero
+    outside the prefix [0, L - W), divisor `pool`); ties to the lowest
+    position. Ascending."""
+    W = q_obs_bits.shape[1]
+    L = int(batch.seq_lens[r])
+    s = snapkv_scores(q_obs_bits, k_bits, batch, r, g, num_kv_heads=num_kv_heads,
+                      sm_scale=sm_scale)
+    npre = max(0, L - W)
+    pre = np.concatenate([np.zeros(pool // 2), s[:npre], np.zeros(pool // 2)])
+    pooled = np.array([pre[i:i + pool].sum() for i in range(npre)]) / pool
+    forced = set(range(min(n_sink, npre))) | set(range(npre, L))
+    cands = [t for t in range(npre) if t not in forced]
+    k = max(0, budget - len(forced))
+    return sorted(forced | set(rank_top(pooled, cands, k)))
+
+
 def dense_attention(q_bits, k_bits, v_bits, batch: BatchView, r: int, g: int, *,
                     num_kv_heads: int, sm_scale: float, out_dtype: str = "bf16"):
     """The k = all case: every block of the request selected."""

@@ -666,3 +666,57 @@ def test_window_attention_is_the_lse_merge_of_two_calls():
         ow, lw = window_attention(q, k, v, batch, r, 1, n_sink=0, window=L, num_kv_heads=2,
                                   sm_scale=0.3, out_dtype="fp64")
         np.testing.assert_allclose(ow, od, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------ SnapKV-style selection
+
+def test_snapkv_scores_sum_to_queries_times_heads_and_match_softmax():
+    from oracle.method import snapkv_scores
+    rng = np.random.default_rng(70)
+    batch, npg = _tiny_batch(rng, lens=(30, 13))
+    k = _rand_bf16(rng, (npg, 2, 4, 8))
+    qo = _rand_bf16(rng, (2, 5, 4, 8))          # W = 5 observation queries, 4 q heads
+    for r in range(2):
+        L = int(batch.seq_lens[r])
+        s = snapkv_scores(qo, k, batch, r, 1, num_kv_heads=2, sm_scale=0.4)
+        assert abs(s.sum() - 5 * 2) < 1e-12                 # each softmax sums to 1
+        # the last position is seen only by the last observation query
+        # (its own position): p of one softmax per head
+        t = np.arange(L)
+        page, slot = batch.token_page_slot(r, t)
+        K = bf16_to_f64(k[page, 1, slot])
+        want_last = 0.0
+        for h in (2, 3):
+            # softmax weights of the last query via attention with one-hot values
+            o, _ = attention_over_tokens(bf16_to_f64(qo[r, 4, h]), K, np.eye(L), 0.4)
+            want_last += o[L - 1]
+        assert abs(s[L - 1] - want_last) < 1e-12
+
+
+def test_snapkv_select_pooling_and_forcing_hand_worked():
+    from oracle.method import snapkv_select
+    import oracle.method as om
+    # scores by hand: a spike at prefix position 10 spreads to 7..13 after
+    # the width-7 average, so with room for 7 ranked positions they are 7..13
+    L, W = 40, 4
+    batch = BatchView([0, 10], np.arange(10), [L], 4)
+    fake = np.zeros(L)
+    fake[10] = 7.0
+    fake[30] = 0.5                     # a smaller bump far away
+    orig = om.snapkv_scores
+    om.snapkv_scores = lambda *a, **kw: fake
+    try:
+        qo = np.zeros((1, W, 1, 8), dtype=np.uint16)
+        sel = snapkv_select(qo, None, batch, 0, 0, num_kv_heads=1, sm_scale=1.0, n_sink=2,
+                            budget=2 + W + 7)
+        assert sel == [0, 1] + list(range(7, 14)) + list(range(36, 40))
+        # one more slot: the bump's neighbourhood (pooled 0.5/7) beats zeros,
+        # the lowest of its 7 positions first
+        sel = snapkv_select(qo, None, batch, 0, 0, num_kv_heads=1, sm_scale=1.0, n_sink=2,
+                            budget=2 + W + 8)
+        assert 27 in sel and 33 not in sel
+        # a budget above L keeps everything
+        assert snapkv_select(qo, None, batch, 0, 0, num_kv_heads=1, sm_scale=1.0, n_sink=2,
+                             budget=100) == list(range(L))
+    finally:
+        om.snapkv_scores = orig
