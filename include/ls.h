@@ -494,6 +494,54 @@ ls_status ls_window_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* 9. One-time SnapKV-style selection and gather                             */
+/* ------------------------------------------------------------------------ */
+/*
+ * The scored KV selection of the ByteCross paper ("Where Activation Sparsity
+ * and KV-Cache Sparsity Cross in LLM Decoding", §4.1 and Appendix A, "Scored
+ * selection"), run once after prefill. For request r (L cached tokens) and
+ * KV head g, the last n_obs prompt queries q_obs[r][w] (query w at position
+ * L - n_obs + w, attending the positions up to its own) each give a softmax
+ * over the cache with the logits sm_scale * q . k; the score of position t is
+ * the sum of its probabilities over the n_obs queries and the group's 4
+ * query heads (computed in fp32: per-row max and sum over 256-position
+ * chunks, then the probabilities summed over the rows in a fixed order).
+ * Scores are averaged over the 7 positions t-3 .. t+3 (zero outside the
+ * prefix [0, L - n_obs), divisor 7). Kept: positions [0, min(n_sink, L -
+ * n_obs)), the n_obs observation positions, and the prefix positions with
+ * the largest averaged scores (ties to the lowest position) up to `budget`
+ * in all (at most L).
+ *
+ * q_obs:    [batch][n_obs][num_q_heads][head_dim] bf16 (n_obs 1 .. 64,
+ *           group size 4).
+ * max_len:  >= every seq_len, <= 131072; batch * kv heads * max_len < 2^31.
+ * selected: [batch][kv heads][budget] int32 positions, ascending, -1 after
+ *           counts[batch][kv heads].
+ * scores_out: NULL or [batch][kv heads][max_len] fp32 (the unaveraged score
+ *           of every position < L, 0 after).
+ * workspace: >= ls_snapkv_select_workspace_size() bytes, 256-byte aligned
+ *           (includes the segmented radix sort's temporary storage).
+ */
+size_t ls_snapkv_select_workspace_size(int32_t batch_size, int32_t num_kv_heads,
+                                       int32_t max_len);
+ls_status ls_snapkv_select(const void* q_obs, int32_t q_dtype, int32_t num_q_heads,
+                           int32_t n_obs, const void* k_pool, ls_pool pool, ls_batch batch,
+                           int32_t max_len, float sm_scale, int32_t n_sink, int32_t budget,
+                           int32_t* selected, int32_t* counts, float* scores_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The kept entries gathered once into contiguous buffers (the paper's
+ * contiguous cache that every later decode step reads in one call):
+ * k_out, v_out: [batch][kv heads][ceil(budget / 16) * 16][head_dim] bf16;
+ * row i of (r, g) is position selected[r][g][i] for i < counts[r][g], zero
+ * after. Reading it back with ls_sparse_attn_decode (no selection) works on
+ * the view of batch * kv heads requests of one KV head each, 16-token pages
+ * in order. */
+ls_status ls_snapkv_gather(const void* k_pool, const void* v_pool, ls_pool pool, ls_batch batch,
+                           const int32_t* selected, const int32_t* counts, int32_t budget,
+                           void* k_out, void* v_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* 7. PQ32 coarse scoring of indexer keys                                    */
 /* ------------------------------------------------------------------------ */
 /*

@@ -436,6 +436,8 @@ def snapkv_scores(q_obs_bits: np.ndarray, k_bits: np.ndarray, batch: BatchView, 
     score = np.zeros(L)
     for w in range(W):
         pos = L - W + w
+        if pos < 0:            # a request shorter than the window: no such query
+            continue
         for h in range(g * G, (g + 1) * G):
             z = float(sm_scale) * (K[:pos + 1] @ bf16_to_f64(q_obs_bits[r, w, h]))
             e = np.exp(z - z.max())

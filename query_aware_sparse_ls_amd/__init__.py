@@ -28,7 +28,8 @@ __all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_s
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
            "sparse_decode_step_workspace", "indexer_select", "indexer_select_workspace_size",
            "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
-           "mla_num_splits", "pq_encode", "pq_train", "pq_select", "window_attn_decode"]
+           "mla_num_splits", "pq_encode", "pq_train", "pq_select", "window_attn_decode",
+           "snapkv_select", "snapkv_gather"]
 
 _DT = {torch.bfloat16: LS_DTYPE_BF16, torch.float32: LS_DTYPE_FP32,
        torch.float8_e4m3fn: LS_DTYPE_FP8_E4M3FN}
@@ -501,3 +502,46 @@ def window_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
                                    out.data_ptr(), _DT[out.dtype], _ptr(lse), ws.data_ptr(),
                                    ws.numel() * ws.element_size(), _stream(stream)))
     return out, lse
+
+
+# ------------------------------------------------------------ SnapKV-style
+
+def snapkv_select(q_obs: torch.Tensor, k_pool: torch.Tensor, batch: PagedBatch, *,
+                  max_len: int, sm_scale: float, n_sink: int, budget: int,
+                  scores_out: Optional[torch.Tensor] = None, stream=None):
+    """One-time selection of each (request, kv head)'s kept positions from
+    the attention of the last prompt queries q_obs [B][W][Hq][D]. Returns
+    (selected [B][Hkv][budget], counts [B][Hkv])."""
+    _need(q_obs, torch.bfloat16); _need(k_pool, torch.bfloat16)
+    B, W, Hq, D = q_obs.shape
+    _, Hkv, P, _ = k_pool.shape
+    dev = q_obs.device
+    sel = torch.empty(B, Hkv, budget, dtype=torch.int32, device=dev)
+    cnt = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if scores_out is not None:
+        _need(scores_out, torch.float32)
+    n = int(_L.ls_snapkv_select_workspace_size(B, int(Hkv), int(max_len)))
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    check(_L.ls_snapkv_select(q_obs.data_ptr(), LS_DTYPE_BF16, int(Hq), int(W), k_pool.data_ptr(),
+                              _pool(k_pool, int(Hkv), int(P), int(D)), batch.c(), int(max_len),
+                              float(sm_scale), int(n_sink), int(budget), sel.data_ptr(),
+                              cnt.data_ptr(), _ptr(scores_out), ws.data_ptr(), ws.numel(),
+                              _stream(stream)))
+    return sel, cnt
+
+
+def snapkv_gather(k_pool: torch.Tensor, v_pool: torch.Tensor, batch: PagedBatch,
+                  selected: torch.Tensor, counts: torch.Tensor, stream=None):
+    """Kept K and V rows, contiguous: [B][Hkv][ceil(budget/16)*16][D] each."""
+    _need(k_pool, torch.bfloat16); _need(v_pool, torch.bfloat16)
+    _need(selected, torch.int32); _need(counts, torch.int32)
+    B, Hkv, budget = selected.shape
+    _, _, P, D = k_pool.shape
+    pad = -(-budget // 16) * 16
+    k_out = torch.empty(B, Hkv, pad, D, dtype=torch.bfloat16, device=k_pool.device)
+    v_out = torch.empty_like(k_out)
+    check(_L.ls_snapkv_gather(k_pool.data_ptr(), v_pool.data_ptr(),
+                              _pool(k_pool, int(Hkv), int(P), int(D)), batch.c(),
+                              selected.data_ptr(), counts.data_ptr(), int(budget),
+                              k_out.data_ptr(), v_out.data_ptr(), _stream(stream)))
+    return k_out, v_out

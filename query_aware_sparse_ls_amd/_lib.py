@@ -71,6 +71,11 @@ _SIGS = {
     "ls_window_attn_decode": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, LsPool, LsBatch,
                                         C.c_int32, C.c_int32, C.c_float, _P, C.c_int32, _P, _P,
                                         C.c_size_t, _P]),
+    "ls_snapkv_select_workspace_size": (C.c_size_t, [C.c_int32] * 3),
+    "ls_snapkv_select": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, LsPool, LsBatch,
+                                   C.c_int32, C.c_float, C.c_int32, C.c_int32, _P, _P, _P, _P,
+                                   C.c_size_t, _P]),
+    "ls_snapkv_gather": (C.c_int, [_P, _P, LsPool, LsBatch, _P, _P, C.c_int32, _P, _P, _P]),
     "ls_pq_encode": (C.c_int, [_P, _P, LsPool, _P, C.c_int32, _P, _P, _P]),
     "ls_pq_train_workspace_size": (C.c_size_t, []),
     "ls_pq_train": (C.c_int, [_P, _P, LsPool, _P, C.c_int32, _P, C.c_int32, _P, _P, C.c_size_t,

@@ -760,6 +760,126 @@ ls_status ls_window_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
   return hip_status(ls::launch_attn_window(aa, npos, stream), "window attention launches");
 }
 
+// ------------------------------------------------------ SnapKV selection ----
+
+namespace {
+
+struct SnapLayout {
+  size_t stats, rowstat, scores, keys, vals, skeys, svals, seg, sort, total;
+};
+
+SnapLayout snap_layout(int batch_size, int num_kv_heads, int max_len) {
+  const size_t pairs = (size_t)batch_size * num_kv_heads;
+  const size_t n_chunks = ((size_t)max_len + 255) / 256;
+  const size_t cells = pairs * (size_t)max_len;
+  SnapLayout l{};
+  size_t o = 0;
+  l.stats = o;   o += align_up(pairs * n_chunks * ls::kSnapMaxObs * 4 * 2 * sizeof(float));
+  l.rowstat = o; o += align_up(pairs * ls::kSnapMaxObs * 4 * 2 * sizeof(float));
+  l.scores = o;  o += align_up(cells * sizeof(float));
+  l.keys = o;    o += align_up(cells * sizeof(float));
+  l.vals = o;    o += align_up(cells * sizeof(int32_t));
+  l.skeys = o;   o += align_up(cells * sizeof(float));
+  l.svals = o;   o += align_up(cells * sizeof(int32_t));
+  l.seg = o;     o += align_up(2 * pairs * sizeof(int32_t));
+  l.sort = o;    o += align_up(ls::snap_sort_bytes((int)pairs, max_len));
+  l.total = o;
+  return l;
+}
+
+}  // namespace
+
+size_t ls_snapkv_select_workspace_size(int32_t batch_size, int32_t num_kv_heads,
+                                       int32_t max_len) {
+  if (batch_size <= 0 || num_kv_heads <= 0 || max_len <= 0 || max_len > ls::kSnapMaxLen) return 0;
+  return snap_layout(batch_size, num_kv_heads, max_len).total;
+}
+
+ls_status ls_snapkv_select(const void* q_obs, int32_t q_dtype, int32_t num_q_heads,
+                           int32_t n_obs, const void* k_pool, ls_pool pool, ls_batch batch,
+                           int32_t max_len, float sm_scale, int32_t n_sink, int32_t budget,
+                           int32_t* selected, int32_t* counts, float* scores_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  if ((st = check_gqa_pool(pool, "kv pool")) != LS_OK) return st;
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (num_q_heads != 4 * pool.num_heads)
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size must be 4");
+  if (n_obs < 1 || n_obs > ls::kSnapMaxObs)
+    return fail(LS_ERR_UNSUPPORTED, "n_obs %d (supported: 1 .. %d)", n_obs, ls::kSnapMaxObs);
+  if (max_len < 1 || max_len > ls::kSnapMaxLen)
+    return fail(LS_ERR_UNSUPPORTED, "max_len %d (supported: 1 .. %d)", max_len, ls::kSnapMaxLen);
+  if ((long long)max_len * batch.batch_size * pool.num_heads >= (1ll << 31))
+    return fail(LS_ERR_UNSUPPORTED, "batch * kv heads * max_len must be < 2^31");
+  if (n_sink < 0 || budget < 1) return fail(LS_ERR_INVALID, "n_sink >= 0 and budget >= 1");
+  if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
+  if (batch.batch_size == 0) return ok();
+  if (!q_obs || !k_pool || !selected || !counts)
+    return fail(LS_ERR_INVALID, "q_obs, k_pool, selected and counts must be non-null");
+  if (!aligned16(q_obs) || !aligned16(k_pool))
+    return fail(LS_ERR_INVALID, "q_obs and k_pool must be 16-byte aligned");
+  const SnapLayout l = snap_layout(batch.batch_size, pool.num_heads, max_len);
+  if (!workspace || workspace_bytes < l.total)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, l.total);
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  char* w = static_cast<char*>(workspace);
+  const size_t pairs = (size_t)batch.batch_size * pool.num_heads;
+  ls::SnapArgs a{};
+  a.q_obs = static_cast<const uint16_t*>(q_obs);
+  a.n_obs = n_obs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool.num_heads;
+  a.head_dim = pool.head_dim;
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.b = batch_args(batch, pool);
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.n_sink = n_sink;
+  a.budget = budget;
+  a.max_len = max_len;
+  a.n_chunks = (max_len + 255) / 256;
+  a.stats = reinterpret_cast<float*>(w + l.stats);
+  a.rowstat = reinterpret_cast<float*>(w + l.rowstat);
+  a.scores = scores_out ? scores_out : reinterpret_cast<float*>(w + l.scores);
+  a.keys = reinterpret_cast<float*>(w + l.keys);
+  a.vals = reinterpret_cast<int32_t*>(w + l.vals);
+  a.sorted_keys = reinterpret_cast<float*>(w + l.skeys);
+  a.sorted_vals = reinterpret_cast<int32_t*>(w + l.svals);
+  a.seg_begin = reinterpret_cast<int32_t*>(w + l.seg);
+  a.seg_end = a.seg_begin + pairs;
+  a.sort_tmp = w + l.sort;
+  a.sort_bytes = l.total - l.sort;
+  a.selected = selected;
+  a.counts = counts;
+  return hip_status(ls::launch_snapkv_select(a, stream), "SnapKV selection launches");
+}
+
+ls_status ls_snapkv_gather(const void* k_pool, const void* v_pool, ls_pool pool, ls_batch batch,
+                           const int32_t* selected, const int32_t* counts, int32_t budget,
+                           void* k_out, void* v_out, hipStream_t stream) {
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  if ((st = check_gqa_pool(pool, "kv pool")) != LS_OK) return st;
+  if (budget < 1) return fail(LS_ERR_INVALID, "budget must be >= 1");
+  if (batch.batch_size == 0) return ok();
+  if (!k_pool || !v_pool || !selected || !counts || !k_out || !v_out)
+    return fail(LS_ERR_INVALID, "pools, selection and outputs must be non-null");
+  ls::SnapArgs a{};
+  a.num_kv_heads = pool.num_heads;
+  a.head_dim = pool.head_dim;
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.b = batch_args(batch, pool);
+  a.budget = budget;
+  a.selected = const_cast<int32_t*>(selected);
+  a.counts = const_cast<int32_t*>(counts);
+  a.k_out = static_cast<uint16_t*>(k_out);
+  a.v_out = static_cast<uint16_t*>(v_out);
+  const int budget_pad = (budget + 15) / 16 * 16;
+  return hip_status(ls::launch_snapkv_gather(a, budget_pad, stream), "SnapKV gather launch");
+}
+
 // ------------------------------------------------------------------ PQ32 ----
 
 namespace {

@@ -177,6 +177,37 @@ hipError_t launch_indexer_mark(const IndexerArgs& a, hipStream_t st);
 // pages' tokens from their codes, mark + finish
 hipError_t launch_pq_select(const IndexerArgs& a, hipStream_t st);
 
+// One-time SnapKV-style selection and gather (k_snapkv.hip).
+constexpr int kSnapMaxObs = 64;        // observation queries
+constexpr int kSnapMaxLen = 131072;    // cache positions per request
+struct SnapArgs {
+  const uint16_t* q_obs;     // [B][n_obs][Hq][D] bf16
+  int32_t n_obs, num_q_heads, num_kv_heads, head_dim;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  BatchArgs b;
+  float sm_scale_log2;
+  int32_t n_sink, budget, max_len, n_chunks;
+  float* stats;              // [pairs][n_chunks][4 kSnapMaxObs][2]
+  float* rowstat;            // [pairs][4 kSnapMaxObs][2]
+  float* scores;             // [pairs][max_len]
+  float* keys;               // [pairs][max_len] sort keys / values, then sorted
+  int32_t* vals;
+  float* sorted_keys;
+  int32_t* sorted_vals;
+  int32_t* seg_begin;        // [pairs]
+  int32_t* seg_end;
+  void* sort_tmp;
+  size_t sort_bytes;
+  int32_t* selected;         // [pairs][budget]
+  int32_t* counts;           // [pairs]
+  uint16_t* k_out;           // gather: [pairs][budget_pad][D]
+  uint16_t* v_out;
+};
+size_t snap_sort_bytes(int pairs, int max_len);
+hipError_t launch_snapkv_select(const SnapArgs& a, hipStream_t st);
+hipError_t launch_snapkv_gather(const SnapArgs& a, int budget_pad, hipStream_t st);
+
 // PQ32 codes and codebooks (k_pq.hip).
 constexpr int kPqSub = 32, kPqCent = 256, kPqDim = 4, kPqFixedBits = 24;
 struct PqArgs {

@@ -1,0 +1,105 @@
+"""GPU parity of the one-time SnapKV-style selection and gather
+(ls_snapkv_select / ls_snapkv_gather) and of a decode step over the
+gathered buffer: scores within 1e-4 relative of the oracle's float64 ones,
+selections exact outside the near-tie band of the averaged scores, the
+gather bit-exact, attention within 1e-5 (fp32 output).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import FP32_ATOL, TIE_REL, paged_batch, say, sub_problem
+from workloads import LLAMA8B_32K_B16, make_block_topk_inputs, reduced
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _q_obs(B, W, Hq, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(B, W, Hq, D, generator=g).to(torch.bfloat16).cuda()
+
+
+def _pooled(s, L, W):
+    npre = max(0, L - W)
+    pre = np.concatenate([np.zeros(3), s[:npre], np.zeros(3)])
+    return np.array([pre[i:i + 7].sum() for i in range(npre)]) / 7
+
+
+@pytest.mark.parametrize("lens,W,budget", [([3000, 700, 65, 64], 64, 900), ([2000, 1500], 16, 300)])
+def test_snapkv_select_gather_and_decode(lens, W, budget):
+    import query_aware_sparse_ls_amd as ls
+    cfg = reduced(LLAMA8B_32K_B16, batch=len(lens), context=max(lens))
+    say(f"snapkv: lens {lens}, W {W}, budget {budget}")
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=91, seq_lens=lens)
+    B, Hq, D, Hkv = cfg.batch, cfg.num_q_heads, cfg.head_dim, cfg.num_kv_heads
+    qo = _q_obs(B, W, Hq, D, 5)
+    sm = 1.0 / math.sqrt(D)
+    batch = paged_batch(inp)
+    max_len = max(lens)
+    sc = torch.full((B, Hkv, max_len), float("nan"), device="cuda")
+    sel, cnt = ls.snapkv_select(qo, inp.k_pool, batch, max_len=max_len, sm_scale=sm, n_sink=4,
+                                budget=budget, scores_out=sc)
+    k_out, v_out = ls.snapkv_gather(inp.k_pool, inp.v_pool, batch, sel, cnt)
+    # decode over the gathered buffer: B * Hkv requests of one kv head
+    pad = k_out.shape[2]
+    nblk = pad // 16
+    pairs = B * Hkv
+    vb = ls.PagedBatch(torch.arange(0, pairs * nblk + 1, nblk, dtype=torch.int32, device="cuda"),
+                       torch.arange(pairs * nblk, dtype=torch.int32, device="cuda"),
+                       cnt.reshape(-1).contiguous(), nblk)
+    q1 = inp.q.reshape(pairs, 4, D).contiguous()
+    out, _ = ls.sparse_attn_decode(q1, k_out.reshape(pairs * nblk, 1, 16, D),
+                                   v_out.reshape(pairs * nblk, 1, 16, D), vb, None, None,
+                                   sm_scale=sm, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qo_bits = oracle.f64_to_bf16_bits(qo.double().cpu().numpy())
+    for r, L in enumerate(lens):
+        for g in (0, 5):
+            q, k, v, bv = sub_problem(inp, r, g)
+            qo_rg = qo_bits[r:r + 1, :, g * 4:(g + 1) * 4]
+            s = oracle.snapkv_scores(qo_rg, k, bv, 0, 0, num_kv_heads=1, sm_scale=sm)
+            got = sc[r, g, :L].double().cpu().numpy()
+            np.testing.assert_allclose(got, s, rtol=1e-4, atol=1e-6 * max(1.0, s.max()))
+            want = oracle.snapkv_select(qo_rg, k, bv, 0, 0, num_kv_heads=1, sm_scale=sm,
+                                        n_sink=4, budget=budget)
+            n = int(cnt[r, g])
+            gs = sel[r, g, :n].cpu().tolist()
+            assert gs == sorted(set(gs)) and len(gs) == len(want)
+            assert (sel[r, g, n:] == -1).all()
+            npre = max(0, L - W)
+            forced = set(range(min(4, npre))) | set(range(npre, L))
+            assert forced <= set(gs)
+            band = set()
+            pooled = _pooled(s, L, W)
+            cands = [t for t in range(npre) if t not in forced]
+            kk = budget - len(forced)
+            if 0 < kk < len(cands):
+                kth = np.sort(pooled[cands])[::-1][kk - 1]
+                tau = TIE_REL * abs(kth) + 1e-6 * np.abs(pooled).max()
+                band = {t for t in cands if abs(pooled[t] - kth) <= tau}
+            assert set(gs) - band == set(want) - band, sorted(set(gs) ^ set(want))[:10]
+            # gather: bit-exact rows, zeros after the count
+            kg = k_out[r, g].cpu()
+            page, slot = bv.token_page_slot(0, np.array(gs, dtype=np.int64))
+            assert np.array_equal(oracle.f64_to_bf16_bits(kg[:n].double().numpy()),
+                                  k[page, 0, slot])
+            assert not kg[n:].float().abs().sum().item()
+            # attention over the gathered entries against the oracle's over
+            # the same positions
+            K = oracle.bf16_to_f64(k[page, 0, slot])
+            V = oracle.bf16_to_f64(v[page, 0, slot])
+            for h in range(4):
+                o, _ = oracle.attention_over_tokens(oracle.bf16_to_f64(q[0, h]), K, V,
+                                                    np.float64(np.float32(sm)))
+                np.testing.assert_allclose(out[r * Hkv + g, h].double().cpu().numpy(), o,
+                                           rtol=0, atol=FP32_ATOL)
