@@ -725,6 +725,90 @@ def bench_dense(args, window: bool = False) -> int:
     return 0
 
 
+def bench_snapkv(args) -> int:
+    """SnapKV-style selection on the 8B/32K/B16 batch: the one-time selection
+    (64 observation queries, 4 sinks, budget 30% of the context) and gather,
+    timed once per replica, then the decode step: dense split-K attention over
+    each (request, KV head)'s gathered buffer."""
+    import torch
+    import query_aware_sparse_ls_amd as ls
+    from workloads import LLAMA8B_32K_B16, make_block_topk_inputs
+    cfg = LLAMA8B_32K_B16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Hq, Hkv, D, L = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.context
+    W, NS, BUD = 64, 4, int(0.3 * cfg.context)
+    sm = 1.0 / math.sqrt(D)
+    R = max(1, min(args.replicas, 2))
+    reps, sel_ms = [], []
+    for i in range(R):
+        inp = make_block_topk_inputs(cfg, device=dev, seed=cfg.seed + i)
+        g = torch.Generator().manual_seed(cfg.seed + 17 * i)
+        qo = torch.randn(B, W, Hq, D, generator=g).to(torch.bfloat16).to(dev)
+        b = ls.PagedBatch(inp.page_indptr, inp.page_indices, inp.seq_lens, inp.max_blocks())
+        ls.snapkv_select(qo, inp.k_pool, b, max_len=L, sm_scale=sm, n_sink=NS, budget=BUD)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sel, cnt = ls.snapkv_select(qo, inp.k_pool, b, max_len=L, sm_scale=sm, n_sink=NS,
+                                    budget=BUD)
+        k_out, v_out = ls.snapkv_gather(inp.k_pool, inp.v_pool, b, sel, cnt)
+        e1.record()
+        torch.cuda.synchronize()
+        sel_ms.append(e0.elapsed_time(e1))
+        pairs, nblk = B * Hkv, k_out.shape[2] // 16
+        vb = ls.PagedBatch(torch.arange(0, pairs * nblk + 1, nblk, dtype=torch.int32, device=dev),
+                           torch.arange(pairs * nblk, dtype=torch.int32, device=dev),
+                           cnt.reshape(-1).contiguous(), nblk)
+        reps.append(dict(q=inp.q.reshape(pairs, 4, D).contiguous(),
+                         k=k_out.reshape(pairs * nblk, 1, 16, D),
+                         v=v_out.reshape(pairs * nblk, 1, 16, D), batch=vb,
+                         out=torch.empty(pairs, 4, D, dtype=torch.bfloat16, device=dev),
+                         ws=torch.empty(ls.sparse_attn_decode_workspace_size(
+                             pairs, 4, D, 0, nblk), dtype=torch.uint8, device=dev),
+                         ntok=int(cnt.sum().item())))
+        del inp
+    torch.cuda.synchronize()
+
+    def call(rp):
+        ls.sparse_attn_decode(rp["q"], rp["k"], rp["v"], rp["batch"], None, None, sm_scale=sm,
+                              out=rp["out"], workspace=rp["ws"])
+
+    for i in range(max(1, args.warmup)):
+        call(reps[i % R])
+    torch.cuda.synchronize()
+    steps = max(R, args.steps // R * R)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(1e8))
+    e0.record()
+    for i in range(steps):
+        call(reps[i % R])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ntok = reps[0]["ntok"]
+    nbytes = ntok * D * 2 * 2 + B * Hq * D * 2 * 2
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res = {"metric": "SnapKV-style decode attention calls/sec over the gathered buffer at "
+                     "8B/32K/B16",
+           "value": round(1e3 / ms, 2), "unit": "calls/s", "n_gpus": 1, "steps": steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg.name + " snapkv", "batch": B, "context": L, "q_heads": Hq,
+                      "kv_heads": Hkv, "head_dim": D, "observation_queries": W, "n_sink": NS,
+                      "budget": BUD, "replicas": R, "timing": "eager, back-to-back calls"},
+           "one_time_select_and_gather_ms": [round(x, 3) for x in sel_ms],
+           "step_bytes": nbytes,
+           "roofline": {"kernel": "ls::attn_chunk_kernel<128> + ls::attn_combine_kernel<128> "
+                                  "(one library call over the gathered buffer)", "bound": "hbm",
+                        "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)},
+           "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -751,7 +835,7 @@ def main(argv=None) -> int:
     ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
                     help="block-topk path: block-mean summaries (default) or Quest bounds")
     ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense", "pq",
-                                       "window"),
+                                       "window", "snapkv"),
                     default="block-topk",
                     help="block-topk: the 8B/32K/B16 block top-k step (default); indexer: "
                          "token top-2048 of 8 x 128K + sparse MLA; coarse-to-fine: 4 x 950K; "
@@ -766,6 +850,8 @@ def main(argv=None) -> int:
         return 2
     if args.copy_calibrate:
         return copy_calibration(args.copy_calibrate)
+    if args.path == "snapkv":
+        return bench_snapkv(args)
     if args.path in ("dense", "window"):
         return bench_dense(args, window=args.path == "window")
     if args.path != "block-topk":

@@ -402,8 +402,9 @@ hipError_t launch_attn_chunked(const AttnArgs& a0, hipStream_t st) {
   const int n = a.selected ? a.max_selected : a.b.max_blocks;   // positions per pair
   const int pairs = a.b.batch * a.num_kv_heads;
   // about 2048 workgroups (8 per CU), at least 16 positions (two per wave)
-  // per split and at most kChunkMaxBlocks
-  constexpr int kTargetWgs = 2048;
+  // per split and at most kChunkMaxBlocks; pairs of at most 1024 positions
+  // take about 512 (longer runs ramp less)
+  const int kTargetWgs = n <= 1024 ? 512 : 2048;
   int splits = (kTargetWgs + pairs - 1) / pairs;
   const int most = (n + 15) / 16;
   splits = splits > most ? most : splits;
