@@ -314,7 +314,7 @@ def approx_select_tokens(scores: np.ndarray, k: int,
     winners are certain, filling the rest from the boundary bucket): every
     candidate whose bucket is above the bucket b* holding the k-th best
     score, then candidates of b* in ascending index order until there are k
-    (this build fills deterministically instead of by random sampling).
+    (filled in index order here, deterministically, where the page samples).
     Ascending ids."""
     cands = np.arange(len(scores)) if candidates is None else np.asarray(list(candidates))
     k = min(max(0, k), len(cands))
