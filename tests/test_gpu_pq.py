@@ -30,8 +30,9 @@ def _dev():
     return torch.device("cuda:0")
 
 
-def _inputs(batch=2, blocks=40, lens=None, seed=11):
-    cfg = reduced(PQ32_128K, batch=batch, context=blocks * 64, seed=seed)
+def _inputs(batch=2, blocks=40, lens=None, seed=11, page_size=64):
+    cfg = reduced(PQ32_128K, batch=batch, context=blocks * page_size, seed=seed,
+                  page_size=page_size)
     inp = make_indexer_inputs(cfg, device=_dev())
     if lens is not None:
         inp.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
@@ -206,3 +207,37 @@ def test_pq_full_size_sampled():
         pos = {t: i for i, t in enumerate(gc)}
         gsel = [pos[t] for t in sel[r, :int(n[r])].cpu().tolist()]
         _check_topk(sorted(gsel), exact, list(range(len(gc))), cfg.topk_tokens, f"final r{r}")
+
+
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_pq_small_pages(page_size):
+    """16- and 32-token pages: codes, candidates and the exact rerank against
+    the oracle (ragged lengths with a partial page)."""
+    lens = (150 * page_size + 5, 37 * page_size)
+    inp = _inputs(batch=2, blocks=160, lens=lens, seed=31 + page_size, page_size=page_size)
+    P = page_size
+    cb, _, _ = _train(inp, 1)
+    codes = _encode_all(inp, cb)
+    b = _batch(inp)
+    C, k = 700, 100
+    cand, cnt = ls.pq_select(inp.q_idx, inp.head_w, codes, cb, b, C)
+    sel, n = ls.indexer_select(inp.q_idx, inp.head_w, inp.idx_keys, P, b, granularity="tokens",
+                               topk=k, max_selected=k, key_scales=inp.idx_scale,
+                               cand_blocks=cand, cand_counts=cnt, token_candidates=True)
+    torch.cuda.synchronize()
+    q, w = bf16_bits(inp.q_idx), inp.head_w.cpu().numpy()
+    bv = BatchView(inp.idx_indptr.cpu().numpy(), inp.idx_indices.cpu().numpy(),
+                   inp.seq_lens.cpu().numpy(), P)
+    x = _host_keys(inp).reshape(-1, 128)
+    assert np.array_equal(codes.cpu().numpy().reshape(-1, 32), pq_encode(x, bf16_bits(cb)))
+    kb, ks = fp8_bits(inp.idx_keys), inp.idx_scale.cpu().numpy()
+    for r, L in enumerate(lens):
+        nc = L // P
+        coarse = pq_token_scores(q, w, codes.cpu().numpy(), bf16_bits(cb), bv, r)
+        gc = cand[r, :int(cnt[r])].cpu().tolist()
+        _check_topk(gc, coarse, list(range(nc * P)), C, f"candidates r{r}")
+        refined = np.array(gc + list(range(nc * P, L)), dtype=np.int64)
+        exact = oracle.indexer_token_scores(q, w, kb, ks, bv, r, tokens=refined)
+        pos = {t: i for i, t in enumerate(refined.tolist())}
+        gsel = sorted(pos[t] for t in sel[r, :int(n[r])].cpu().tolist())
+        _check_topk(gsel, exact, list(range(len(refined))), k, f"final r{r}")
