@@ -391,7 +391,9 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
  * fp32 score (sign, exponent, three mantissa bits) lies above the bucket b*
  * holding the k-th score, then units of b* in ascending unit order until
  * there are topk. Deterministic; not the exact top-k when b* holds more
- * units than it contributes.
+ * units than it contributes. p->approx = 2 exits after the second digit
+ * instead: buckets of the key's top 24 bits (the boundary is then a
+ * 2^-15-relative slice of the scores).
  */
 enum { LS_SEL_TOKENS = 0, LS_SEL_BLOCKS = 1 };
 enum { LS_CAND_BLOCKS = 0, LS_CAND_TOKENS = 1 };
@@ -405,8 +407,8 @@ typedef struct ls_indexer_params {
   int32_t max_selected;  /* row capacity of `selected`                        */
   int32_t candidates;    /* LS_CAND_BLOCKS or LS_CAND_TOKENS: what cand_blocks */
                          /* holds (tokens mode with a candidate list)         */
-  int32_t approx;        /* tokens mode: 0 exact top-k; 1 approximate top-k   */
-                         /* (see below)                                       */
+  int32_t approx;        /* tokens mode: 0 exact top-k; 1 or 2: approximate  */
+                         /* top-k with buckets of 12 or 24 key bits (below)   */
 } ls_indexer_params;
 
 /* Row stride (in floats) of scores_out for up to max_units units. */

@@ -308,19 +308,21 @@ def score_bucket(scores: np.ndarray, bits: int = 12) -> np.ndarray:
 
 
 def approx_select_tokens(scores: np.ndarray, k: int,
-                         candidates: Optional[Iterable[int]] = None) -> List[int]:
+                         candidates: Optional[Iterable[int]] = None,
+                         bits: int = 12) -> List[int]:
     """Approximate top-k (Vortex, "Making it fast": a monotonic remap of the
     scores into buckets and an early exit that stops refining once enough
     winners are certain, filling the rest from the boundary bucket): every
     candidate whose bucket is above the bucket b* holding the k-th best
     score, then candidates of b* in ascending index order until there are k
     (filled in index order here, deterministically, where the page samples).
-    Ascending ids."""
+    `bits`: the key bits that make a bucket (12: one radix digit; 24: the
+    early exit after two digits). Ascending ids."""
     cands = np.arange(len(scores)) if candidates is None else np.asarray(list(candidates))
     k = min(max(0, k), len(cands))
     if k == 0:
         return []
-    b = score_bucket(np.asarray(scores)[cands])
+    b = score_bucket(np.asarray(scores)[cands], bits)
     kth = np.sort(b)[::-1][k - 1]
     above = cands[b > kth]
     fill = np.sort(cands[b == kth])[:k - len(above)]

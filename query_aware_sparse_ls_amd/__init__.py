@@ -305,7 +305,7 @@ def indexer_select(q: torch.Tensor, head_weights: torch.Tensor, keys: torch.Tens
                    cand_blocks: Optional[torch.Tensor] = None,
                    cand_counts: Optional[torch.Tensor] = None,
                    n_sink: int = 0, n_recent: int = 0, token_candidates: bool = False,
-                   approx: bool = False,
+                   approx: int = 0,
                    selected: Optional[torch.Tensor] = None,
                    selected_count: Optional[torch.Tensor] = None,
                    scores_out: Optional[torch.Tensor] = None,
@@ -343,7 +343,7 @@ def indexer_select(q: torch.Tensor, head_weights: torch.Tensor, keys: torch.Tens
     params = LsIndexerParams(C.sizeof(LsIndexerParams), g, int(topk), int(n_sink),
                              int(n_recent), int(max_selected),
                              LS_CAND_TOKENS if token_candidates else LS_CAND_BLOCKS,
-                             1 if approx else 0)
+                             int(approx))
     pool = LsPool(int(keys.shape[0]), 1, int(page_size), int(D), _DT[keys.dtype])
     check(_L.ls_indexer_select(q.data_ptr(), LS_DTYPE_BF16, int(H), head_weights.data_ptr(),
                                keys.data_ptr(), _ptr(key_scales), pool, batch.c(),

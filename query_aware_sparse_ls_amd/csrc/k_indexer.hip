@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   __syncthreads();
   const int bstar = sh.bstar;
   const bool refine = bstar >= 0 && bstar < kIdxBins;
-  const bool digits = refine && !a.approx;   // approximate: no second / third digit
+  const bool digits = refine && a.approx != 1;   // one-digit approximation: no second digit
 
   // 2. this chunk: selected bits above b*; units of b* to the candidate list
   // and into the second-digit histogram
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
         sh.h2, reinterpret_cast<const uint32_t*>(a.cand_blocks + (size_t)r * a.cand_cap), g.ncand);
   int ties_to_take = 0;
   constexpr int UN = 4;   // candidate loads in flight per thread
-  if (refine && a.approx) {
+  if (refine && a.approx == 1) {
     // early exit (Vortex, "Making it fast"): every unit of bucket b* is a
     // tie; the emission takes the first `need` of them in unit order
     const int nc = (int)ld_dev(ctl);
@@ -582,6 +582,27 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
     idx_find_digit(sh.h, kIdxBins, need, sh.red, &sh.b2, &sh.above2);
     const uint32_t b2 = (uint32_t)sh.b2;
     const int need2 = need - sh.above2;
+    if (a.approx == 2) {
+      // early exit after two digits: units above the 24-bit boundary prefix
+      // are selected, the boundary's own units are ties taken in unit order
+      const uint32_t theta24 = ((uint32_t)bstar << 12) | b2;
+      ties_to_take = need2;
+      for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
+        uint2 c[UN];
+#pragma unroll
+        for (int j = 0; j < UN; ++j) {
+          const int i = i0 + j * kIdxMarkThreads + tid;
+          c[j] = i < nc ? crow[i] : make_uint2(0u, 0xFFFFFFFFu);
+        }
+#pragma unroll
+        for (int j = 0; j < UN; ++j) {
+          if (c[j].y == 0xFFFFFFFFu) continue;
+          const uint32_t u = c[j].y, pre = c[j].x >> 8;
+          if (pre > theta24) atomicOr(&sh.bm[u >> 5], 1u << (u & 31));
+          else if (pre == theta24) atomicOr(&sh.tie[u >> 5], 1u << (u & 31));
+        }
+      }
+    } else {
     // third digit over the candidates whose second digit is b2
     for (int i = tid; i < 256; i += kIdxMarkThreads) sh.h[i] = 0u;
     __syncthreads();
@@ -626,6 +647,7 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
         if (c[j].x > theta) atomicOr(&sh.bm[u >> 5], 1u << (u & 31));
         else if (c[j].x == theta) atomicOr(&sh.tie[u >> 5], 1u << (u & 31));
       }
+    }
     }
   }
   __syncthreads();

@@ -525,7 +525,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
     return fail(LS_ERR_INVALID, "candidates %d (LS_CAND_BLOCKS or LS_CAND_TOKENS)",
                 p->candidates);
   const bool tok_cands = p->candidates == LS_CAND_TOKENS;
-  if (p->approx != 0 && p->approx != 1) return fail(LS_ERR_INVALID, "approx %d (0 or 1)", p->approx);
+  if (p->approx < 0 || p->approx > 2) return fail(LS_ERR_INVALID, "approx %d (0, 1 or 2)", p->approx);
   if (p->approx && !tokens) return fail(LS_ERR_UNSUPPORTED, "approx is for LS_SEL_TOKENS");
   if (tok_cands && (!tokens || !cand_blocks))
     return fail(LS_ERR_INVALID, "LS_CAND_TOKENS needs LS_SEL_TOKENS and a candidate list");

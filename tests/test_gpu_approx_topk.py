@@ -64,19 +64,22 @@ def _host(inp):
             inp.idx_scale.cpu().numpy(), bv)
 
 
+@pytest.mark.parametrize("level", [1, 2])
 @pytest.mark.parametrize("k", [1, 100, 2048, 5000])
-def test_approx_topk_integer_scores_bit_exact(k):
+def test_approx_topk_integer_scores_bit_exact(k, level):
     """Integer scores: many equal scores per bucket, so the boundary bucket is
-    large and its fill order (ascending tokens) decides; ragged lengths."""
+    large and its fill order (ascending tokens) decides; ragged lengths.
+    Level 1 exits after one radix digit (12-bit buckets), level 2 after two
+    (24-bit buckets)."""
     lens = [9000, 4500, 63, 1]
     inp = _inputs(lens, seed=70 + k, integer=True)
-    say(f"approx top-k, integer scores, k {k}")
-    sel, n = _run(inp, k, True)
+    say(f"approx top-k, integer scores, k {k}, level {level}")
+    sel, n = _run(inp, k, level)
     q, w, kb, ks, bv = _host(inp)
     for r, L in enumerate(lens):
         s = oracle.indexer_token_scores(q, w, kb, ks, bv, r)
         assert np.all(s == np.round(s)) and np.abs(s).max(initial=0) < 2 ** 24
-        want = oracle.approx_select_tokens(s, k)
+        want = oracle.approx_select_tokens(s, k, bits=12 * level)
         assert sel[r, :n[r]].tolist() == want, (r, len(want), int(n[r]))
         assert (sel[r, n[r]:] == -1).all()
 
@@ -87,7 +90,7 @@ def test_approx_topk_integer_scores_with_block_candidates():
     cand = torch.tensor([[0, 3, 7, 20, 50, 93], [1, 2, 40, 46, -1, -1]], dtype=torch.int32,
                         device=_dev())
     cnt = torch.tensor([6, 4], dtype=torch.int32, device=_dev())
-    sel, n = _run(inp, 150, True, cand, cnt)
+    sel, n = _run(inp, 150, 1, cand, cnt)
     q, w, kb, ks, bv = _host(inp)
     P = inp.cfg.page_size
     for r, L in enumerate(lens):
@@ -105,8 +108,8 @@ def test_approx_topk_real_scores_properties_and_recall():
     lens = [131072, 70000]
     inp = _inputs(lens, seed=78)
     k = 2048
-    sel, n = _run(inp, k, True)
-    ex, exn = _run(inp, k, False)
+    sel, n = _run(inp, k, 1)
+    ex, exn = _run(inp, k, 0)
     q, w, kb, ks, bv = _host(inp)
     for r, L in enumerate(lens):
         s = oracle.indexer_token_scores(q, w, kb, ks, bv, r)

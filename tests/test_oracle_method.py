@@ -720,3 +720,18 @@ def test_snapkv_select_pooling_and_forcing_hand_worked():
                              budget=100) == list(range(L))
     finally:
         om.snapkv_scores = orig
+
+
+def test_approx_topk_two_digits_refines_the_boundary():
+    from oracle.method import approx_select_tokens, score_bucket
+    # 1.0, 1.01 and 1.02 share a 12-bit bucket but not a 24-bit one
+    s = np.array([1.0, 1.01, 1.02, 3.0, 0.5])
+    assert len(set(score_bucket(s[:3], 24))) == 3
+    assert approx_select_tokens(s, 3, bits=24) == [1, 2, 3]
+    # equal 24-bit prefixes still fill in index order: 1 + 2^-20 and 1 + 2^-19
+    # differ only below the top 24 key bits
+    t = np.array([1.0 + 2.0 ** -19, 1.0 + 2.0 ** -20, 5.0])
+    assert score_bucket(t, 24)[0] == score_bucket(t, 24)[1]
+    assert approx_select_tokens(t, 2, bits=24) == [0, 2]
+    assert select_tokens(t, 2) == [0, 2]
+    assert approx_select_tokens(t[::-1].copy(), 2, bits=24) == [0, 1]   # 5.0 and the lower index
