@@ -258,3 +258,50 @@ def test_pq_validation():
     assert s(batch=_batch(max_blocks=5000)) == _lib.LS_ERR_UNSUPPORTED       # > 262144 tokens
     assert s() == _lib.LS_ERR_WORKSPACE
     assert s(batch=_batch(batch_size=0)) == _lib.LS_OK
+
+
+def test_window_and_snapkv_validation():
+    lib = _lib.load()
+
+    def win(**kw):
+        a = dict(q=FAKE, hq=32, pool=_pool(), batch=_batch(), ns=4, w=100, scale=0.1,
+                 out=FAKE, odt=_lib.LS_DTYPE_BF16, ws=None, wsb=0)
+        a.update(kw)
+        return lib.ls_window_attn_decode(a["q"], _lib.LS_DTYPE_BF16, a["hq"], FAKE, FAKE,
+                                         a["pool"], a["batch"], a["ns"], a["w"], a["scale"],
+                                         a["out"], a["odt"], None, a["ws"], a["wsb"], None)
+
+    assert win(ns=-1) == _lib.LS_ERR_INVALID
+    assert win(w=-5) == _lib.LS_ERR_INVALID
+    assert win(hq=16) == _lib.LS_ERR_UNSUPPORTED                       # group 2
+    assert win(pool=_pool(num_pages=1 << 22)) == _lib.LS_ERR_UNSUPPORTED
+    assert win(scale=float("nan")) == _lib.LS_ERR_INVALID
+    assert win(odt=_lib.LS_DTYPE_FP8_E4M3FN) == _lib.LS_ERR_UNSUPPORTED
+    assert win() == _lib.LS_ERR_WORKSPACE
+    assert win(batch=_batch(batch_size=0)) == _lib.LS_OK
+    need = lib.ls_window_attn_decode_workspace_size(2, 32, 128, 4, 4, 100)
+    assert need >= 2 * 32 * 130 * 4
+
+    def snap(**kw):
+        a = dict(hq=32, nobs=64, pool=_pool(), batch=_batch(), max_len=64, ns=4, bud=16,
+                 sel=FAKE, ws=None, wsb=0)
+        a.update(kw)
+        return lib.ls_snapkv_select(FAKE, _lib.LS_DTYPE_BF16, a["hq"], a["nobs"], FAKE, a["pool"],
+                                    a["batch"], a["max_len"], 0.1, a["ns"], a["bud"], a["sel"],
+                                    FAKE, None, a["ws"], a["wsb"], None)
+
+    assert snap(nobs=0) == _lib.LS_ERR_UNSUPPORTED
+    assert snap(nobs=65) == _lib.LS_ERR_UNSUPPORTED
+    assert snap(max_len=131073) == _lib.LS_ERR_UNSUPPORTED
+    assert snap(hq=64) == _lib.LS_ERR_UNSUPPORTED                      # group 8
+    assert snap(bud=0) == _lib.LS_ERR_INVALID
+    assert snap(sel=None) == _lib.LS_ERR_INVALID
+    assert snap() == _lib.LS_ERR_WORKSPACE
+    assert snap(batch=_batch(batch_size=0)) == _lib.LS_OK
+    assert lib.ls_snapkv_select_workspace_size(2, 8, 64) > 0
+    assert lib.ls_snapkv_select_workspace_size(2, 8, 131073) == 0
+    g = lib.ls_snapkv_gather
+    assert g(FAKE, FAKE, _pool(), _batch(), FAKE, FAKE, 0, FAKE, FAKE, None) == _lib.LS_ERR_INVALID
+    assert g(FAKE, FAKE, _pool(), _batch(), None, FAKE, 8, FAKE, FAKE, None) == _lib.LS_ERR_INVALID
+    assert g(FAKE, FAKE, _pool(), _batch(batch_size=0), FAKE, FAKE, 8, FAKE, FAKE,
+             None) == _lib.LS_OK
