@@ -334,10 +334,71 @@ def test_indexer_scores_vs_rationals_and_homogeneity():
     s2 = indexer_token_scores(q, w, keys, scales2, batch, 0)
     assert s2[1] == 2 * s[1]
     assert np.array_equal(np.delete(s2, 1), np.delete(s, 1))
-    # block form on summaries agrees with the same Eq. 6 written over rationals
+    # block form on summaries: Eq. 6 applied to the block-mean keys, written
+    # over rationals by the brute force below (its own decoder, its own walk
+    # of the page table)
     summ = _rand_bf16(rng, (npg, 6))
-    sb = indexer_block_scores(q, w, summ, batch, 0)
-    assert sb.shape == (2,)
+    for r in range(2):
+        sb = indexer_block_scores(q, w, summ, batch, r)
+        want = _fraction_indexer_block_scores(q, w, summ, batch, r)
+        assert sb.shape == (len(want),) == (int(batch.seq_lens[r]) // 4,)
+        for got, ref in zip(sb, want):
+            assert abs(Fraction(float(got)) - ref) <= abs(ref) * Fraction(1, 10 ** 13) + Fraction(1, 10 ** 300)
+
+
+def _bf16_bits_to_fraction(bits):
+    """Exact value of a bf16 bit pattern (finite), from the IEEE fields."""
+    bits = int(bits) & 0xFFFF
+    sign = -1 if bits >> 15 else 1
+    exp, man = (bits >> 7) & 0xFF, bits & 0x7F
+    assert exp != 0xFF
+    if exp == 0:
+        return sign * Fraction(man, 1 << 7) * Fraction(1, 1 << 126)
+    v = Fraction((1 << 7) + man, 1 << 7)
+    e = exp - 127
+    return sign * (v * (1 << e) if e >= 0 else v / (1 << -e))
+
+
+def _fraction_indexer_block_scores(q_bits, w, summ_bits, batch, r):
+    """s_j = sum_h w_h * max(0, q_h . kbar_j) over the complete blocks j of
+    request r (LeanSparse §5, Eq. 6 on block-mean keys), in rationals, with
+    block j's summary at row page_indices[page_indptr[r] + j]."""
+    P = batch.page_size
+    nc = int(batch.seq_lens[r]) // P
+    base = int(batch.page_indptr[r])
+    out = []
+    for j in range(nc):
+        page = int(batch.page_indices[base + j])
+        kbar = [_bf16_bits_to_fraction(b) for b in np.asarray(summ_bits)[page]]
+        total = Fraction(0)
+        for h in range(q_bits.shape[1]):
+            qh = [_bf16_bits_to_fraction(b) for b in q_bits[r, h]]
+            dot = sum((a * b for a, b in zip(qh, kbar)), Fraction(0))
+            total += Fraction(float(w[r, h])) * max(dot, Fraction(0))
+        out.append(total)
+    return out
+
+
+def test_indexer_block_scores_brute_force_catches_plausible_mistakes():
+    """The rational brute force separates the oracle's block score from the
+    nearby wrong readings: logical instead of physical page, ReLU after the
+    head sum, unweighted heads."""
+    rng = np.random.default_rng(161)
+    batch, npg = _tiny_batch(rng, lens=(28,), P=4)
+    q = _rand_bf16(rng, (1, 3, 6))
+    w = rng.standard_normal((1, 3)).astype(np.float32)
+    summ = _rand_bf16(rng, (npg, 6))
+    ref = [float(x) for x in _fraction_indexer_block_scores(q, w, summ, batch, 0)]
+    got = indexer_block_scores(q, w, summ, batch, 0)
+    assert np.allclose(got, ref, rtol=1e-13, atol=0)
+    S = bf16_to_f64(summ)
+    qq = bf16_to_f64(q[0])
+    ww = w[0].astype(np.float64)
+    logical = np.maximum(S[: len(ref)] @ qq.T, 0.0) @ ww
+    late_relu = np.maximum((S[batch.pages(0)[: len(ref)]] @ qq.T) @ ww, 0.0)
+    unweighted = np.maximum(S[batch.pages(0)[: len(ref)]] @ qq.T, 0.0).sum(axis=1)
+    for wrong in (logical, late_relu, unweighted):
+        assert not np.allclose(wrong, ref, rtol=1e-9, atol=0)
 
 
 # ---------------------------------------------------------------- attention
@@ -560,8 +621,8 @@ def test_coarse_to_fine_never_leaves_the_kept_blocks():
                                 n_recent_blocks=1, topk_tokens=6)
     nb = batch.num_blocks(0)
     assert len(res["blocks"]) == 4 and nb - 1 in res["blocks"]
-    # the coarse pass ranks blocks by the block-mean score (brute force)
-    sb = indexer_block_scores(q, w, summ, batch, 0)
+    # the coarse pass ranks blocks by the block-mean score (rational brute force)
+    sb = _fraction_indexer_block_scores(q, w, summ, batch, 0)
     cands = [j for j in range(nb) if j != nb - 1]
     top = sorted(cands, key=lambda j: (-sb[j], j))[:3]
     assert sorted(top + [nb - 1]) == res["blocks"]

@@ -74,7 +74,7 @@ class BlockTopKInputs:
     page_indptr: torch.Tensor    # [B+1] int32
     page_indices: torch.Tensor   # [nnz] int32, physical page ids in logical order
     seq_lens: torch.Tensor       # [B] int32, tokens cached (current one included)
-    topk: int                    # k blocks chosen by score (forced excluded)
+    topk: int                    # k blocks chosen by score (forced excluded); -1: keep ratio
     hot_blocks: Dict = field(default_factory=dict)  # (r, g) -> list of logical blocks
     unused_pages: Optional[torch.Tensor] = None     # int64 page ids no request uses
 
@@ -101,20 +101,6 @@ def _seq_lens(cfg: BlockTopKConfig, gen: torch.Generator) -> List[int]:
     u = torch.rand(cfg.batch, generator=gen, dtype=torch.float64)
     lens = torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))
     return [int(min(hi, max(lo, round(float(x))))) for x in lens]
-
-
-def topk_for(cfg: BlockTopKConfig, nb: int) -> int:
-    """k for one request: cfg.topk, or (keep_ratio * nb) minus the forced count.
-
-    With a keep ratio the forced blocks count inside the budget, as the
-    ByteCross paper counts its sink tokens inside the kept fraction
-    (§4.1, App. A); ratio 1 keeps every block.
-    """
-    if cfg.topk >= 0:
-        return cfg.topk
-    forced = min(nb, cfg.n_sink + cfg.n_recent)
-    total = max(forced, math.ceil(cfg.keep_ratio * nb - 1e-9))
-    return max(0, total - forced)
 
 
 def make_block_topk_inputs(cfg: BlockTopKConfig, device="cpu", seed: Optional[int] = None,
@@ -208,7 +194,7 @@ def make_block_topk_inputs(cfg: BlockTopKConfig, device="cpu", seed: Optional[in
             k_pool[ud] = nan
             v_pool[ud] = nan
 
-    topk = topk_for(cfg, max(nbs)) if cfg.topk < 0 else cfg.topk
+    topk = cfg.topk   # -1: the keep ratio decides k per request (the oracle's rule)
     return BlockTopKInputs(cfg, q_cpu.to(device), k_pool, v_pool,
                            page_indptr.to(device), page_indices.to(device),
                            torch.tensor(lens, dtype=torch.int32).to(device),
