@@ -89,9 +89,9 @@ def make_replica(cfg, seed, device, score_mode="mean"):
                sel=torch.empty(B, Hkv, maxsel, dtype=torch.int32, device=device),
                cnt=torch.empty(B, Hkv, dtype=torch.int32, device=device),
                out=torch.empty(B, Hq, D, dtype=torch.bfloat16, device=device),
-               ws_sel=torch.empty(ls.score_select_workspace_size(B, Hkv, batch.max_blocks),
+               ws_sel=torch.zeros(ls.score_select_workspace_size(B, Hkv, batch.max_blocks),
                                   dtype=torch.uint8, device=device),
-               ws_attn=torch.empty(ls.sparse_attn_decode_workspace_size(
+               ws_attn=torch.zeros(ls.sparse_attn_decode_workspace_size(
                    B, Hq, D, maxsel, batch.max_blocks), dtype=torch.uint8, device=device),
                maxsel=maxsel)
     return rep

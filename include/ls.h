@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LS_ABI_VERSION 5
+#define LS_ABI_VERSION 6
 
 typedef enum ls_status {
   LS_OK = 0,
@@ -206,7 +206,16 @@ ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_
  * scores_out:     NULL, or [batch][num_kv_heads][max_blocks] fp32 receiving
  *                 s_j for candidate blocks (other entries unspecified).
  * workspace:      device scratch of at least ls_score_select_workspace_size()
- *                 bytes, 256-byte aligned; contents need not be initialised.
+ *                 bytes, 256-byte aligned, always required (also with
+ *                 scores_out); its first ls_workspace_control_bytes(batch,
+ *                 num_kv_heads) bytes must be zero before its first use
+ *                 (every call leaves them zero), the rest need not be
+ *                 initialised.
+ * Execution (requests of at most 8192 blocks): one launch; the candidate
+ *                 blocks of each (request, kv head) pair are scored in chunks
+ *                 of 64-128 blocks by separate workgroups, and the last chunk
+ *                 of a pair to finish ranks the pair (longer requests: a
+ *                 scoring kernel, then a top-k kernel).
  * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
  *            page_size 16; max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192,
  *            num_pages < 2^26).
@@ -232,13 +241,13 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
  *   lse_out[r][h] = M + ln sum_t e^{z_t - M}
  * with fp32 logits, softmax and accumulation; partial softmax states over
  * disjoint token sets are merged by log-sum-exp in a fixed order
- * (deterministic). For a selection with at least 64 (request, kv head)
- * pairs one workgroup owns each pair and merges on chip (two workgroups
- * merging through the workspace for requests of more than 4096 blocks in
- * calls of at most 256 pairs); with fewer pairs, and always for the dense
- * path, the blocks are split over several workgroups per pair (8 blocks
- * each) whose partial results go through the workspace and are merged by a
- * second kernel (split-K). An empty T gives out = 0 and
+ * (deterministic). A selection (requests of at most 8192 blocks) is split
+ * over workgroups of at most 16 selected blocks per (request, kv head) pair;
+ * each writes its partial softmax state to the workspace and the last of a
+ * pair's workgroups to finish merges them in split order, in the same
+ * launch. The dense path splits each pair into runs of up to 512 blocks
+ * whose states a second kernel merges (split-K); longer requests take the
+ * split-K kernels of 8 blocks per split. An empty T gives out = 0 and
  * lse = -inf. The output is rounded once (nearest-even) to out_dtype.
  * For a selection written by ls_score_select the entries past the count are
  * -1; other callers may leave them undefined (they are never read as blocks).
@@ -254,7 +263,9 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
  * out:            [batch][num_q_heads][head_dim] of out_dtype (bf16 or fp32).
  * lse_out:        NULL or [batch][num_q_heads] fp32.
  * workspace:      >= ls_sparse_attn_decode_workspace_size() bytes, 256-byte
- *                 aligned (split partial results); need not be initialised.
+ *                 aligned (split partial results); its first
+ *                 ls_workspace_control_bytes(batch, num_kv_heads) bytes must
+ *                 be zero before its first use (every call leaves them zero).
  * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
  *            page_size 16.
  */
@@ -275,14 +286,18 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
 /* ------------------------------------------------------------------------ */
 /*
  * ls_score_select followed by ls_sparse_attn_decode (same definitions, same
- * results bit for bit: both take the same kernel path for the same shapes).
- * With at least 64 (request, kv head) pairs (and max_blocks <= 8192) the
- * step is ONE launch in which one workgroup owns a
- * pair from scoring to output: its scores, top-k and selection stay on chip
- * and its attention merge happens on chip, so no intermediate result goes
- * through memory and no workgroup waits for another (the Vortex post fuses
- * the operators of a decode step, "Making it fast"). Otherwise it runs the
- * split kernels of the two calls back to back.
+ * results bit for bit: both take the same kernel code, chunking and merge
+ * order for the same shapes). For requests of at most 8192 blocks the step
+ * is ONE launch (the Vortex post fuses the operators of a decode step,
+ * "Making it fast") spread over the whole chip: workgroups score chunks of
+ * each pair's candidate blocks, the last chunk of a pair to finish ranks the
+ * pair and publishes its selection, workgroups of at most 16 selected
+ * blocks attend it (each waits for its pair's selection; every wait is on a
+ * workgroup of lower index, which the hardware starts first) and the last of
+ * them merges the pair's partial softmax states in split order. Scores,
+ * selection and partial states go through the workspace with device-coherent
+ * accesses. Longer requests run the split kernels of the two calls back to
+ * back.
  *
  * Arguments: as ls_score_select (q, summaries, batch, p, selected,
  * selected_count) and ls_sparse_attn_decode (k_pool, v_pool with geometry
@@ -300,8 +315,10 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
  *   p->n_recent >= 1 (checked). Otherwise call ls_build_block_summaries
  *   first.
  * workspace: >= ls_sparse_decode_step_workspace_size() bytes, 256-byte
- *   aligned, need not be initialised (block scores and split partials of the
- *   split path; calls that run concurrently need separate workspaces).
+ *   aligned (control words, block scores, split partials); its first
+ *   ls_workspace_control_bytes(batch, num_kv_heads) bytes must be zero before
+ *   its first use and every call leaves them zero; calls that run
+ *   concurrently need separate workspaces.
  * Supported: head_dim 64 or 128; GQA group 4; page_size 16;
  *   max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192 and num_pages < 2^26;
  *   bounds of requests of more than 4096 blocks in batches of at most 256
@@ -618,6 +635,17 @@ const char* ls_version(void);
 /* Number of split-K partitions ls_sparse_attn_decode uses for a given
  * selection capacity (max_selected, or max_blocks on the dense path). */
 int32_t ls_attn_num_splits(int32_t max_selected);
+
+/* Bytes of control words at the start of the workspace of ls_score_select,
+ * ls_sparse_attn_decode and ls_sparse_decode_step for a batch of batch_size
+ * requests with num_kv_heads KV heads.
+ * These words (per-(request, kv head) arrival counters, ready flags and an
+ * error word) must be zero before the workspace is first used; every call
+ * leaves them zero again, so a workspace can be reused by calls that do not
+ * run concurrently. A non-zero error word after a call means a workgroup gave
+ * up waiting for a selection (never expected; the results of that call are
+ * then unspecified). The rest of a workspace needs no initialisation. */
+size_t ls_workspace_control_bytes(int32_t batch_size, int32_t num_kv_heads);
 
 #ifdef __cplusplus
 }

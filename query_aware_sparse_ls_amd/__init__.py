@@ -26,7 +26,7 @@ _L = _lib.load()
 __all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_select", "sparse_attn_decode",
            "score_select_workspace_size", "sparse_attn_decode_workspace_size",
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
-           "sparse_decode_step_workspace", "indexer_select", "indexer_select_workspace_size",
+           "sparse_decode_step_workspace", "workspace_control_bytes", "indexer_select", "indexer_select_workspace_size",
            "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
            "mla_num_splits", "pq_encode", "pq_train", "pq_select", "window_attn_decode",
            "snapkv_select", "snapkv_gather"]
@@ -82,9 +82,12 @@ def _pool(t: torch.Tensor, num_heads: int, page_size: int, head_dim: int) -> LsP
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    """The caller's workspace, or a new zero-filled one (the selection and
+    attention calls keep control words at the start of their workspace that
+    must be zero before its first use; every call leaves them zero)."""
     if ws is not None:
         return ws
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ summaries
@@ -168,7 +171,7 @@ def score_select(q: torch.Tensor, summaries: torch.Tensor, page_size: int, batch
     if scores_out is not None:
         _need(scores_out, torch.float32)
     ws_bytes = score_select_workspace_size(B, Hkv, batch.max_blocks)
-    ws = _workspace(ws_bytes, dev, workspace) if scores_out is None else workspace
+    ws = _workspace(ws_bytes, dev, workspace)
     params = LsSelectParams(C.sizeof(LsSelectParams),
                             LS_AGG_MAX if group_agg == "max" else LS_AGG_MEAN,
                             int(topk), float(keep_ratio), int(n_sink), int(n_recent),
@@ -186,6 +189,12 @@ def score_select(q: torch.Tensor, summaries: torch.Tensor, page_size: int, batch
 
 def attn_num_splits(max_selected: int) -> int:
     return int(_L.ls_attn_num_splits(int(max_selected)))
+
+
+def workspace_control_bytes(batch_size: int, num_kv_heads: int) -> int:
+    """Bytes of control words at the start of a selection / attention / step
+    workspace (zero before first use, left zero by every call)."""
+    return int(_L.ls_workspace_control_bytes(int(batch_size), int(num_kv_heads)))
 
 
 def sparse_attn_decode_workspace_size(batch_size: int, num_q_heads: int, head_dim: int,
@@ -231,10 +240,12 @@ def sparse_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
 def sparse_decode_step_workspace(batch_size: int, num_q_heads: int, num_kv_heads: int,
                                  head_dim: int, max_blocks: int, max_selected: int,
                                  device) -> torch.Tensor:
-    """A workspace for sparse_decode_step (need not be initialised)."""
+    """A zero-filled workspace for sparse_decode_step (its control words must
+    be zero before the first call; every call leaves them zero, so the
+    workspace can be reused by calls that do not run concurrently)."""
     n = int(_L.ls_sparse_decode_step_workspace_size(batch_size, num_q_heads, num_kv_heads,
                                                    head_dim, max_blocks, max_selected))
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.Tensor,
@@ -247,8 +258,8 @@ def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.T
                        lse: Optional[torch.Tensor] = None,
                        new_pages: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, stream=None):
-    """score_select + sparse_attn_decode as one call (one launch when there
-    are at least 64 (request, kv head) pairs). new_pages (int32, optional):
+    """score_select + sparse_attn_decode as one call (one launch for requests
+    of at most 8192 blocks). new_pages (int32, optional):
     pages that filled at this step, whose summaries the call also rebuilds
     (they must be forced blocks of this call, e.g. last blocks with
     n_recent >= 1). Returns (out, lse, selected, selected_count)."""

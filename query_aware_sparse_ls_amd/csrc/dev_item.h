@@ -42,8 +42,16 @@ constexpr int kItemPrefetch = 2;        // K/V blocks in flight per wave
 // Walk entries past the selection that item_attn may read: wave w refills
 // its slots with position w + 8(k + kItemPrefetch) for k < nbw + kItemPrefetch
 // - 1, nbw = ceil((cnt - w) / 8), i.e. at most cnt + 7 + 8(2 kItemPrefetch - 2).
-constexpr int kItemEntryPad = kItemWaves * 2 * kItemPrefetch;
+template <int NW>
+constexpr int item_entry_pad() { return NW * 2 * kItemPrefetch; }
+constexpr int kItemEntryPad = item_entry_pad<kItemWaves>();
 static_assert(kItemEntryPad >= 7 + kItemWaves * (2 * kItemPrefetch - 2) + 1, "entry padding");
+
+// Where item_score / item_score_bounds put the scores: every row of the
+// scored tiles into LDS, or the candidate rows into a global score row with
+// plain stores (read by a later launch) or device-coherent stores (read by
+// another workgroup of the same launch).
+enum { kStoreLds = 0, kStoreGlobal = 1, kStoreDev = 2 };
 
 // The 4 group queries as a 16x16x32 MFMA operand, one per k-step of D/32:
 // lane i holds head i%16 (zero past the 4 heads), dims 32j + 8(i/16) .. +8.
@@ -130,10 +138,11 @@ __device__ __forceinline__ uint4 k_operand(const uint32_t* tile, int j) {
 // after its use; every load is issued -- a row outside the candidates reads
 // page 0 and is discarded -- so the number in flight is fixed). A candidate
 // whose page id is out of range scores 0.
-template <int D, int MAXC, bool kLds = true>
+// pg[b - pg_off] is the page id of candidate b; NW waves take the tiles.
+template <int D, int MAXC, int kStore = kStoreLds, int NW = kItemWaves>
 __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, const ReqGeom& geo,
                                            const int* pg, float* sc, uint32_t* stage,
-                                           float* range = nullptr) {
+                                           float* range = nullptr, int pg_off = 0) {
   using ST = Stage<D>;
   constexpr int KS = D / 32, NL = ST::NL, NS = kItemScorePrefetch;
   static_assert(NS % 2 == 0, "slots are consumed in pairs");
@@ -145,13 +154,13 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
   const uint32_t pstride = (uint32_t)HKV * D;   // elements per page (< 2^32)
   uint32_t* tiles = stage + wave * 2 * 16 * ST::kKRowWords;   // two tiles per wave
   const int t0 = geo.c0 / 16, t1 = (geo.c1 + 15) / 16;
-  const int ntw = t1 - t0 > wave ? (t1 - t0 - wave + kItemWaves - 1) / kItemWaves : 0;
+  const int ntw = t1 - t0 > wave ? (t1 - t0 - wave + NW - 1) / NW : 0;
   // page of the row this lane loads with instruction j of the wave's k-th
   // tile: -1 if not a candidate, -2 for a candidate with a bad page id
   auto page_of = [&](int k, int j) {
-    const int b = (t0 + wave + kItemWaves * k) * 16 + j * ST::RPI + lane / ST::LPR;
+    const int b = (t0 + wave + NW * k) * 16 + j * ST::RPI + lane / ST::LPR;
     if (k >= ntw || b < geo.c0 || b >= geo.c1) return -1;
-    const int p = pg[b < MAXC ? b : MAXC - 1];
+    const int p = pg[b - pg_off];   // b in [c0, c1): inside the caller's page list
     return (p >= 0 && p < a.b.num_pages) ? p : -2;
   };
   auto issue = [&](int k, uint4* d, uint32_t& badm) {
@@ -178,10 +187,10 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
     const float v = mean ? ((acc[0] + acc[1]) + (acc[2] + acc[3])) * 0.25f
                          : fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     if (kq == 0 && k < ntw) {
-      const int b = (t0 + wave + kItemWaves * k) * 16 + row;
+      const int b = (t0 + wave + NW * k) * 16 + row;
       const bool cand = b >= geo.c0 && b < geo.c1;
-      if constexpr (kLds) sc[b] = v;
-      else if (cand) sc[b] = v;
+      if constexpr (kStore == kStoreLds) sc[b] = v;
+      else if (cand) st_x<kStore == kStoreDev>(&sc[b], v);
       smin = cand ? fminf(smin, v) : smin;
       smax = cand ? fmaxf(smax, v) : smax;
     }
@@ -221,12 +230,12 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
       finish(acc1, k0 + s + 1);
     }
   }
-  if (range) {   // range[wave] = the wave's smallest score, range[kItemWaves + wave] its largest
+  if (range) {   // range[wave] = the wave's smallest score, range[NW + wave] its largest
     smin = wave_min_fast(smin);
     smax = wave_max_fast(smax);
     if (lane == 0) {
       range[wave] = smin;
-      range[kItemWaves + wave] = smax;
+      range[NW + wave] = smax;
     }
   }
 }
@@ -242,10 +251,11 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
 // values (q or 0), the products are exact in fp32. The group aggregation,
 // score stores and range are those of item_score; one slot holds both rows
 // of a 16-block tile.
-template <int D, int MAXC>
+template <int D, int MAXC, int kStore = kStoreLds, int NW = kItemWaves>
 __device__ __forceinline__ void item_score_bounds(const ScoreArgs& a, int r, int g,
                                                   const ReqGeom& geo, const int* pg, float* sc,
-                                                  uint32_t* stage, float* range = nullptr) {
+                                                  uint32_t* stage, float* range = nullptr,
+                                                  int pg_off = 0) {
   using ST = Stage<D>;
   constexpr int KS = D / 32, NL = ST::NL, NS = kItemBoundsPrefetch;
   const int HKV = a.num_kv_heads;
@@ -272,11 +282,11 @@ __device__ __forceinline__ void item_score_bounds(const ScoreArgs& a, int r, int
   const uint32_t pstride = (uint32_t)HKV * 2 * D;   // elements per page (< 2^32)
   uint32_t* tiles = stage + wave * 2 * 16 * ST::kKRowWords;   // maximum rows, minimum rows
   const int t0 = geo.c0 / 16, t1 = (geo.c1 + 15) / 16;
-  const int ntw = t1 - t0 > wave ? (t1 - t0 - wave + kItemWaves - 1) / kItemWaves : 0;
+  const int ntw = t1 - t0 > wave ? (t1 - t0 - wave + NW - 1) / NW : 0;
   auto page_of = [&](int k, int j) {
-    const int b = (t0 + wave + kItemWaves * k) * 16 + j * ST::RPI + lane / ST::LPR;
+    const int b = (t0 + wave + NW * k) * 16 + j * ST::RPI + lane / ST::LPR;
     if (k >= ntw || b < geo.c0 || b >= geo.c1) return -1;
-    const int p = pg[b < MAXC ? b : MAXC - 1];
+    const int p = pg[b - pg_off];   // b in [c0, c1): inside the caller's page list
     return (p >= 0 && p < a.b.num_pages) ? p : -2;
   };
   // slot layout: d[j] = maximum-row chunk j, d[NL + j] = minimum-row chunk j
@@ -298,9 +308,10 @@ __device__ __forceinline__ void item_score_bounds(const ScoreArgs& a, int r, int
     const float v = mean ? ((acc[0] + acc[1]) + (acc[2] + acc[3])) * 0.25f
                          : fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     if (kq == 0 && k < ntw) {
-      const int b = (t0 + wave + kItemWaves * k) * 16 + row;
+      const int b = (t0 + wave + NW * k) * 16 + row;
       const bool cand = b >= geo.c0 && b < geo.c1;
-      sc[b] = v;
+      if constexpr (kStore == kStoreLds) sc[b] = v;
+      else if (cand) st_x<kStore == kStoreDev>(&sc[b], v);
       smin = cand ? fminf(smin, v) : smin;
       smax = cand ? fmaxf(smax, v) : smax;
     }
@@ -340,27 +351,31 @@ __device__ __forceinline__ void item_score_bounds(const ScoreArgs& a, int r, int
     smax = wave_max_fast(smax);
     if (lane == 0) {
       range[wave] = smin;
-      range[kItemWaves + wave] = smax;
+      range[NW + wave] = smax;
     }
   }
 }
 
-// LDS of the attention: per-wave V staging tiles and the wave states.
-template <int D>
+// LDS of the attention: per-wave K and V staging tiles and the wave states.
+// A wave's o accumulator (4 heads x D floats) goes into its own K tile once
+// its walk is done (acc_of), so the merge needs no space of its own.
+template <int D, int NW = kItemWaves>
 struct alignas(16) ItemAttnLds {   // 16-byte aligned: the tiles take 16-byte LDS accesses
-  alignas(16) uint32_t k[kItemWaves][16 * Stage<D>::kKRowWords];
-  alignas(16) uint32_t v[kItemWaves][16 * Stage<D>::kVRowWords];
-  float acc[kItemWaves][4][D];
-  float m[kItemWaves][4];
-  float l[kItemWaves][4];
+  alignas(16) uint32_t k[NW][16 * Stage<D>::kKRowWords];
+  alignas(16) uint32_t v[NW][16 * Stage<D>::kVRowWords];
+  float m[NW][4];
+  float l[NW][4];
+  static_assert(4 * D <= 16 * Stage<D>::kKRowWords, "o accumulator fits a K tile");
+  __device__ float* acc_of(int w) { return reinterpret_cast<float*>(k[w]); }
 };
 
 // Rewrites the selection sel[0 .. npad) (LDS) in place into walk entries:
 // e = page * 32 + (valid tokens of the block) for positions < cnt whose block
 // and page are valid, -1 otherwise. Requires num_pages < 2^26.
+template <int NT = kItemThreads>
 __device__ __forceinline__ void item_entries(const AttnArgs& a, const ReqGeom& geo, int* sel,
                                              int cnt, const int* pg, int npad) {
-  for (int pos = threadIdx.x; pos < npad; pos += kItemThreads) {
+  for (int pos = threadIdx.x; pos < npad; pos += NT) {
     int e = -1;
     if (pos < cnt) {
       const int blk = sel[pos];
@@ -375,7 +390,8 @@ __device__ __forceinline__ void item_entries(const AttnArgs& a, const ReqGeom& g
 }
 
 // Number of walk entries item_attn reads for a selection of cnt blocks.
-__device__ __forceinline__ int item_entry_count(int cnt) { return cnt + kItemEntryPad; }
+template <int NW = kItemWaves>
+__device__ __forceinline__ int item_entry_count(int cnt) { return cnt + item_entry_pad<NW>(); }
 
 // Attention of the G = 4 query heads of (r, g) over the walk entries ent[]
 // (LDS, from item_entries; cnt = selection size), written as out / lse.
@@ -411,13 +427,18 @@ struct ItemSplit {
 // kLo: entries carry a first valid token too (e = page * 512 + lo * 32 +
 // nt: tokens lo .. nt-1 of the block are attended; page < 2^22), for token
 // ranges that start inside a block.
-template <int D, bool kLo = false>
+// NW: waves of the workgroup; NPF: K/V blocks in flight per wave (at most
+// kItemPrefetch). kDevStore: the split state is written with device-coherent
+// stores (its reader is another workgroup of the same launch).
+template <int D, bool kLo = false, int NW = kItemWaves, bool kDevStore = false,
+          int NPF = kItemPrefetch>
 __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const int* ent,
-                                          int cnt, ItemAttnLds<D>& sh,
+                                          int cnt, ItemAttnLds<D, NW>& sh,
                                           const ItemPair* pair = nullptr,
                                           const ItemSplit* split = nullptr) {
   using ST = Stage<D>;
-  constexpr int KS = D / 32, NL = ST::NL, NT = D / 16, NPF = kItemPrefetch;
+  constexpr int KS = D / 32, NL = ST::NL, NT = D / 16;
+  static_assert(NPF >= 1 && NPF <= kItemPrefetch, "entry padding covers kItemPrefetch");
   constexpr int RW = ST::kVRowWords;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int row = lane & 15, kq = lane >> 4;
@@ -435,10 +456,10 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
   uint32_t* vt = sh.v[wave];
   // wave w walks selection positions first, first + step, ... (one
   // workgroup: w, w + 8, ...; a pair: w + 8 half, w + 8 half + 16, ...)
-  const int step = pair ? 2 * kItemWaves : kItemWaves;
-  const int first = wave + (pair ? kItemWaves * pair->half : 0);
+  const int step = pair ? 2 * NW : NW;
+  const int first = wave + (pair ? NW * pair->half : 0);
   const int nbw = cnt > first ? (cnt - first + step - 1) / step : 0;
-  const int nent = item_entry_count(cnt);   // entries written by item_entries
+  const int nent = item_entry_count<NW>(cnt);   // entries written by item_entries
 
   constexpr int PSH = kLo ? 9 : 5;   // page bits start here
   uint4 kr[NPF][NL], vr[NPF][NL];
@@ -564,12 +585,15 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
       }
     }
   }
-  // wave states to LDS: o rows 0..3 (heads) live in lanes 0..15
+  // wave states to LDS: o rows 0..3 (heads) live in lanes 0..15; the wave's
+  // own K tile holds its o (its walk is over: every LDS read of the tile has
+  // completed at the last wave_lds_sync)
+  float* acc = sh.acc_of(wave);
   if (kq == 0) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) sh.acc[wave][h][16 * n + row] = o[n][h];
+      for (int h = 0; h < 4; ++h) acc[h * D + 16 * n + row] = o[n][h];
     }
   }
   if (lane < 4) {
@@ -577,84 +601,110 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
     sh.l[wave][lane] = l;
   }
   __syncthreads();
-  // merge the 8 wave states in wave order; one output element per thread
-  // (4 D <= 512 elements)
-  static_assert(4 * D <= kItemThreads, "one merged element per thread");
-  const int e = tid;
-  const int h = e / D, d = e % D;
-  float M = kNegInf, O = 0.0f, Ls = 0.0f;
-  if (e < 4 * D) {
+  // merge the wave states in wave order: output elements e = h * D + d,
+  // EPT per thread
+  constexpr int NTH = NW * kWave, EPT = (4 * D + NTH - 1) / NTH;
+  float Mv[EPT], Ov[EPT], Lv[EPT];
 #pragma unroll
-    for (int w = 0; w < kItemWaves; ++w) M = fmaxf(M, sh.m[w][h]);
-    if (M != kNegInf) {
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + j * NTH;
+    const int h = e / D;
+    float M = kNegInf, O = 0.0f, Ls = 0.0f;
+    if (e < 4 * D) {
 #pragma unroll
-      for (int w = 0; w < kItemWaves; ++w) {
-        const float f = exp2_fast(sh.m[w][h] - M);   // waves with m = -inf give 0
-        O += f * sh.acc[w][h][d];
-        Ls += f * sh.l[w][h];
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sh.m[w][h]);
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = exp2_fast(sh.m[w][h] - M);   // waves with m = -inf give 0
+          O += f * sh.acc_of(w)[e];
+          Ls += f * sh.l[w][h];
+        }
       }
     }
+    Mv[j] = M;
+    Ov[j] = O;
+    Lv[j] = Ls;
   }
   if (split) {
-    if (e < 4 * D) {
-      float* ph = split->part + (((size_t)r * a.num_q_heads + g * 4 + h) * split->num_splits +
-                                 split->s) * (D + 2);
-      ph[d] = O;
-      if (d == 0) {
-        ph[D] = M;
-        ph[D + 1] = Ls;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + j * NTH;
+      const int h = e / D, d = e % D;
+      if (e < 4 * D) {
+        float* ph = split->part + (((size_t)r * a.num_q_heads + g * 4 + h) * split->num_splits +
+                                   split->s) * (D + 2);
+        st_x<kDevStore>(ph + d, Ov[j]);
+        if (d == 0) {
+          st_x<kDevStore>(ph + D, Mv[j]);
+          st_x<kDevStore>(ph + D + 1, Lv[j]);
+        }
       }
     }
     return;
   }
-  if (pair) {
-    // publish, count the arrival, and let the second workgroup finish
-    float* mine = pair->part + (size_t)pair->half * 4 * D;
-    float* ml = pair->part + 2 * 4 * D;
-    if (e < 4 * D) {
-      st_dev(mine + e, O);
-      if (d == 0) {
-        st_dev(ml + pair->half * 8 + 2 * h, M);
-        st_dev(ml + pair->half * 8 + 2 * h + 1, Ls);
+  if constexpr (EPT == 1) {
+    if (pair) {
+      // publish, count the arrival, and let the second workgroup finish
+      const int e = tid;
+      const int h = e / D, d = e % D;
+      float M = Mv[0], O = Ov[0], Ls = Lv[0];
+      float* mine = pair->part + (size_t)pair->half * 4 * D;
+      float* ml = pair->part + 2 * 4 * D;
+      if (e < 4 * D) {
+        st_dev(mine + e, O);
+        if (d == 0) {
+          st_dev(ml + pair->half * 8 + 2 * h, M);
+          st_dev(ml + pair->half * 8 + 2 * h + 1, Ls);
+        }
       }
-    }
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(pair->arrivals, 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      sh.m[0][0] = __int_as_float(prev == 1u ? 1 : 0);
-    }
-    __syncthreads();
-    if (__float_as_int(sh.m[0][0]) == 0) return;   // the other workgroup finishes
-    if (e < 4 * D) {
-      const int oh = 1 - pair->half;
-      const float Mo = ld_dev(ml + oh * 8 + 2 * h), Lo = ld_dev(ml + oh * 8 + 2 * h + 1);
-      const float Oo = ld_dev(pair->part + (size_t)oh * 4 * D + e);
-      // merge in half order (half 0 first), so the result does not depend on
-      // which workgroup arrives last
-      const float M0 = pair->half == 0 ? M : Mo, M1 = pair->half == 0 ? Mo : M;
-      const float O0 = pair->half == 0 ? O : Oo, O1 = pair->half == 0 ? Oo : O;
-      const float L0 = pair->half == 0 ? Ls : Lo, L1 = pair->half == 0 ? Lo : Ls;
-      const float Mn = fmaxf(M0, M1);
-      O = 0.0f;
-      Ls = 0.0f;
-      if (Mn != kNegInf) {
-        const float f0 = exp2_fast(M0 - Mn), f1 = exp2_fast(M1 - Mn);
-        O = f0 * O0 + f1 * O1;
-        Ls = f0 * L0 + f1 * L1;
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(pair->arrivals, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        sh.m[0][0] = __int_as_float(prev == 1u ? 1 : 0);
       }
-      M = Mn;
+      __syncthreads();
+      if (__float_as_int(sh.m[0][0]) == 0) return;   // the other workgroup finishes
+      if (e < 4 * D) {
+        const int oh = 1 - pair->half;
+        const float Mo = ld_dev(ml + oh * 8 + 2 * h), Lo = ld_dev(ml + oh * 8 + 2 * h + 1);
+        const float Oo = ld_dev(pair->part + (size_t)oh * 4 * D + e);
+        // merge in half order (half 0 first), so the result does not depend on
+        // which workgroup arrives last
+        const float M0 = pair->half == 0 ? M : Mo, M1 = pair->half == 0 ? Mo : M;
+        const float O0 = pair->half == 0 ? O : Oo, O1 = pair->half == 0 ? Oo : O;
+        const float L0 = pair->half == 0 ? Ls : Lo, L1 = pair->half == 0 ? Lo : Ls;
+        const float Mn = fmaxf(M0, M1);
+        O = 0.0f;
+        Ls = 0.0f;
+        if (Mn != kNegInf) {
+          const float f0 = exp2_fast(M0 - Mn), f1 = exp2_fast(M1 - Mn);
+          O = f0 * O0 + f1 * O1;
+          Ls = f0 * L0 + f1 * L1;
+        }
+        M = Mn;
+      }
+      Mv[0] = M;
+      Ov[0] = O;
+      Lv[0] = Ls;
     }
   }
-  if (e < 4 * D) {
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    const size_t idx = ((size_t)r * a.num_q_heads + g * 4 + h) * D + d;
-    if (out32) reinterpret_cast<float*>(a.out)[idx] = O * inv;
-    else reinterpret_cast<uint16_t*>(a.out)[idx] = f32_to_bf16_rne(O * inv);
-    if (a.lse && d == 0)
-      a.lse[(size_t)r * a.num_q_heads + g * 4 + h] =
-          (M == kNegInf || !(Ls > 0.0f)) ? kNegInf : (M + log2f(Ls)) * kLn2;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + j * NTH;
+    const int h = e / D, d = e % D;
+    if (e < 4 * D) {
+      const float M = Mv[j], Ls = Lv[j];
+      const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+      const size_t idx = ((size_t)r * a.num_q_heads + g * 4 + h) * D + d;
+      if (out32) reinterpret_cast<float*>(a.out)[idx] = Ov[j] * inv;
+      else reinterpret_cast<uint16_t*>(a.out)[idx] = f32_to_bf16_rne(Ov[j] * inv);
+      if (a.lse && d == 0)
+        a.lse[(size_t)r * a.num_q_heads + g * 4 + h] =
+            (M == kNegInf || !(Ls > 0.0f)) ? kNegInf : (M + log2f(Ls)) * kLn2;
+    }
   }
 }
 

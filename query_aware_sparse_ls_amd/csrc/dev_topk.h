@@ -107,7 +107,9 @@ __device__ __forceinline__ int tot_minus_prefix(int v, int* total) {
 // NT threads of the workgroup. The selection goes to out[0 .. max_selected)
 // (unused entries -1) and its size to *count_out; sel_lds, when given, gets a
 // copy of the first min(total, max_selected) entries. Returns that count.
-template <int PER, int NT = kTopkThreads, bool kPad16 = false>
+// kDev: out and *count_out are written with device-coherent stores, for
+// readers in other workgroups of the same launch.
+template <int PER, int NT = kTopkThreads, bool kPad16 = false, bool kDev = false>
 __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k,
                         int32_t* __restrict__ out, int max_selected,
                         int32_t* __restrict__ count_out, TopkLds& sh,
@@ -298,7 +300,7 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
     if ((sel >> j) & 1ull) {
       if (pos < max_selected) {
         const int b = geo.c0 + tid * PER + j;
-        out[pos] = b;
+        st_x<kDev>(&out[pos], b);
         if (sel_lds) sel_lds[pos] = b;
       }
       ++pos;
@@ -308,22 +310,247 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
   const int total = nlow + ncand + nhigh;
   for (int i = tid; i < nlow; i += NT) {
     if (i < max_selected) {
-      out[i] = i;
+      st_x<kDev>(&out[i], i);
       if (sel_lds) sel_lds[i] = i;
     }
   }
   for (int i = tid; i < nhigh; i += NT) {
     const int p = nlow + ncand + i;
     if (p < max_selected) {
-      out[p] = geo.c1 + i;
+      st_x<kDev>(&out[p], geo.c1 + i);
       if (sel_lds) sel_lds[p] = geo.c1 + i;
     }
   }
-  for (int i = total + tid; i < max_selected; i += NT) out[i] = -1;
+  for (int i = total + tid; i < max_selected; i += NT) st_x<kDev>(&out[i], -1);
   const int stored = total < max_selected ? total : max_selected;
-  if (tid == 0) *count_out = stored;
+  if (tid == 0) st_x<kDev>(count_out, stored);
   __syncthreads();
   return stored;
+}
+
+// ---------------------------------------------------------------------------
+// topk_fast: the same exact selection (the first k candidates under (score
+// descending, block index ascending), forced blocks added, ascending
+// output) for up to kTopkFastMaxBlocks blocks when the candidates' score
+// range is known up front, with fewer barriers than topk_wg:
+//  * each bucketing pass has its own pre-zeroed histogram (no zeroing
+//    barrier), and every wave finds the boundary bucket by itself from a DPP
+//    prefix sum over the 256 buckets (no second barrier);
+//  * the kept blocks (candidates and forced) go into an LDS bitmap, from
+//    which one wave writes the ascending selection (one word per lane, a
+//    wave prefix sum of the word counts gives each lane its output slot).
+// Degenerate score ranges, or more passes than histograms, fall back to
+// topk_wg on the same scores (same result).
+constexpr int kTopkFastPasses = 4;
+constexpr int kTopkFastMaxBlocks = 4096;
+
+struct TopkFastLds {
+  int hist[kTopkFastPasses][256];
+  unsigned bm[kTopkFastMaxBlocks / 32];
+  float list_key[kWave];
+  int list_idx[kWave];
+  int list_n;
+  int total;
+};
+
+// Inclusive prefix sum over the 64 lanes: DPP shifts inside each 16-lane
+// row, then the row totals read into scalars.
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = __lane_id() >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// topk_wg on a padded LDS score row, as a real call: the fast path's rare
+// fallback should not add its registers to the caller's.
+template <int PER, int NT, bool kDev>
+__device__ __noinline__ int topk_fallback(const float* srow, const ReqGeom& geo, int k,
+                                          int32_t* out, int max_selected, int32_t* count_out,
+                                          TopkLds& sh, int32_t* sel_lds) {
+  return topk_wg<PER, NT, true, kDev>(srow, geo, k, out, max_selected, count_out, sh, sel_lds);
+}
+
+// srow: LDS, candidate e at srow[e + e / 16] (c1 - c0 <= NT * PER); mn0 / mx0:
+// the smallest and largest candidate score. Called by all NT threads; the
+// caller synchronises after writing srow. sel_lds (optional): a copy of the
+// stored selection. Returns the stored count.
+template <int PER, int NT, bool kDev = false>
+__device__ int topk_fast(const float* __restrict__ srow, const ReqGeom& geo, int k,
+                         int32_t* __restrict__ out, int max_selected,
+                         int32_t* __restrict__ count_out, TopkFastLds& sh, TopkLds& fallback,
+                         int32_t* __restrict__ sel_lds, float mn0, float mx0) {
+  constexpr int NW = NT / kWave;
+  static_assert(NT % kWave == 0 && NW <= kTopkMaxWaves && PER >= 1 && PER <= 32, "shape");
+  static_assert(NT * PER <= kTopkFastMaxBlocks, "blocks");
+  constexpr int WPL = (kTopkFastMaxBlocks / 32 + kWave - 1) / kWave;   // bitmap words per lane
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = geo.c1 - geo.c0;
+  for (int i = tid; i < kTopkFastPasses * 256; i += NT) (&sh.hist[0][0])[i] = 0;
+  for (int i = tid; i < kTopkFastMaxBlocks / 32; i += NT) sh.bm[i] = 0u;
+  if (tid == 0) sh.list_n = 0;
+  float key[PER];
+  uint32_t act = 0, sel = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid * PER + j;
+    key[j] = e < n ? srow[e + (e >> 4)] : 0.0f;
+    act |= (uint32_t)(e < n) << j;
+  }
+  int need = k < n ? k : n;
+  int cnt = n;   // undecided candidates (exact: from the last pass's histogram)
+  float mn = mn0, mx = mx0;
+  bool robust = false;
+  __syncthreads();
+  for (int it = 0; need > 0; ++it) {
+    if (cnt <= need) {   // every undecided candidate is in
+      sel |= act;
+      act = 0;
+      break;
+    }
+    if (cnt <= kWave) {
+      // list the undecided; each is ranked by counting those ahead of it
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if ((act >> j) & 1u) {
+          const int pos = atomicAdd(&sh.list_n, 1);
+          sh.list_key[pos] = key[j];
+          sh.list_idx[pos] = tid * PER + j;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if ((act >> j) & 1u) {
+          const float mk = key[j];
+          const int mi = tid * PER + j;
+          int rank = 0;
+          for (int u0 = 0; u0 < cnt; u0 += 8) {
+#pragma unroll
+            for (int uu = 0; uu < 8; ++uu) {
+              const int u = u0 + uu;
+              if (u < cnt) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
+            }
+          }
+          if (rank < need) sel |= 1u << j;
+        }
+      }
+      act = 0;
+      break;
+    }
+    const float range = mx - mn;
+    const float scale = 256.0f / range;
+    if (it >= kTopkFastPasses || !(range > 0.0f) || !(scale < __builtin_huge_valf())) {
+      robust = true;
+      break;
+    }
+    int* h = sh.hist[it];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if ((act >> j) & 1u) atomicAdd(&h[bucket_of(key[j], mn, scale)], 1);
+    __syncthreads();
+    // every wave: the boundary bucket b* = the highest bucket whose suffix
+    // count (candidates in buckets >= b) is at least `need`
+    const int h0 = h[4 * lane], h1 = h[4 * lane + 1], h2 = h[4 * lane + 2], h3 = h[4 * lane + 3];
+    const int lsum = (h0 + h1) + (h2 + h3);
+    const int incl = wave_incl_scan_dpp(lsum);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const int s0 = total - (incl - lsum), s1 = s0 - h0, s2 = s1 - h1, s3 = s2 - h2;
+    int best = -1, sb = 0, hb = 0;
+    if (s0 >= need) { best = 4 * lane; sb = s0; hb = h0; }
+    if (s1 >= need) { best = 4 * lane + 1; sb = s1; hb = h1; }
+    if (s2 >= need) { best = 4 * lane + 2; sb = s2; hb = h2; }
+    if (s3 >= need) { best = 4 * lane + 3; sb = s3; hb = h3; }
+    const unsigned long long m = __ballot(best >= 0);   // lane 0 is in: s0 = cnt >= need
+    const int L = 63 - __builtin_clzll(m);
+    const int bstar = __builtin_amdgcn_readlane(best, L);
+    const int cabove = __builtin_amdgcn_readlane(sb, L) - __builtin_amdgcn_readlane(hb, L);
+    const int cstar = __builtin_amdgcn_readlane(hb, L);
+    uint32_t up = 0, keep = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int b = bucket_of(key[j], mn, scale);
+      up |= (uint32_t)(b > bstar) << j;
+      keep |= (uint32_t)(b == bstar) << j;
+    }
+    sel |= act & up;
+    act &= keep;
+    need -= cabove;
+    cnt = cstar;
+    // the boundary bucket's score interval (the map stays monotone if it is
+    // not exact: keys outside clamp to the edge buckets)
+    const float lo = mn + (float)bstar / scale, hi = mn + (float)(bstar + 1) / scale;
+    mn = lo;
+    mx = hi;
+  }
+  if (robust) {
+    return topk_fallback<PER, NT, kDev>(srow, geo, k, out, max_selected, count_out, fallback,
+                                        sel_lds);
+  }
+  // the kept blocks into the bitmap: this thread's candidates (consecutive
+  // blocks), then the forced ones
+  {
+    int word = -1;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if ((sel >> j) & 1u) {
+        const int b = geo.c0 + tid * PER + j;
+        if ((b >> 5) != word) {
+          if (bits) atomicOr(&sh.bm[word], bits);
+          word = b >> 5;
+          bits = 0;
+        }
+        bits |= 1u << (b & 31);
+      }
+    }
+    if (bits) atomicOr(&sh.bm[word], bits);
+  }
+  for (int i = tid; i < geo.c0; i += NT) atomicOr(&sh.bm[i >> 5], 1u << (i & 31));
+  for (int i = geo.c1 + tid; i < geo.nb; i += NT) atomicOr(&sh.bm[i >> 5], 1u << (i & 31));
+  __syncthreads();
+  if (tid < kWave) {
+    const int nwords = (geo.nb + 31) >> 5;
+    uint32_t w[WPL];
+    int pos[WPL];
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < WPL; ++q) {
+      const int wi = q * kWave + lane;
+      w[q] = wi < nwords ? sh.bm[wi] : 0u;
+      const int c = __popc(w[q]);
+      const int incl = wave_incl_scan_dpp(c);
+      pos[q] = base + incl - c;
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+    const int total = base;
+#pragma unroll
+    for (int q = 0; q < WPL; ++q) {
+      uint32_t x = w[q];
+      int p = pos[q];
+      while (x) {
+        const int b = (q * kWave + lane) * 32 + (__ffs(x) - 1);
+        x &= x - 1;
+        if (p < max_selected) {
+          st_x<kDev>(&out[p], b);
+          if (sel_lds) sel_lds[p] = b;
+        }
+        ++p;
+      }
+    }
+    for (int i = total + lane; i < max_selected; i += kWave) st_x<kDev>(&out[i], -1);
+    const int stored = total < max_selected ? total : max_selected;
+    if (lane == 0) {
+      st_x<kDev>(count_out, stored);
+      sh.total = stored;
+    }
+  }
+  __syncthreads();
+  return sh.total;
 }
 
 __device__ __forceinline__ int topk_budget(const TopkArgs& a, const ReqGeom& geo) {

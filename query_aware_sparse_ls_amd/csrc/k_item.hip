@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kItemThreads) void score_part_kernel(ScoreArgs sa, 
   for (int b = geo.c0 + threadIdx.x; b < geo.c1; b += kItemThreads)
     pg[b] = sa.b.indices[geo.page_base + b];
   __syncthreads();
-  item_score<D, MAXC, false>(sa, r, g, geo, pg, scores + (size_t)item * sa.b.max_blocks, stage);
+  item_score<D, MAXC, kStoreGlobal>(sa, r, g, geo, pg, scores + (size_t)item * sa.b.max_blocks, stage);
 }
 
 template <int D, int MAXC>

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 
+#include "ls_flow.h"
 #include "ls_internal.h"
 
 namespace {
@@ -154,13 +155,208 @@ ls::AttnArgs attn_args(const void* q, int num_q_heads, const void* k_pool, const
   return aa;
 }
 
+// ---- workspace layouts: the flow kernel's control words first (they must
+// be zero before a workspace's first use, and every call leaves them zero),
+// then the regions each path needs -------------------------------------------
+struct SelectWs {
+  size_t rows, ranges, total;
+};
+SelectWs select_ws(int B, int hkv, int max_blocks) {
+  const int P = B * hkv;
+  SelectWs w;
+  w.rows = ls::flow_ctl_bytes(P);
+  w.ranges = w.rows + ls::flow_rows_bytes(P, max_blocks);
+  w.total = w.ranges + ls::flow_ranges_bytes(P);
+  return w;
+}
+
+// Split partials of the attention: the split-K kernels' and the flow kernel's.
+size_t attn_parts_bytes(int B, int hq, int head_dim, int max_selected, int max_blocks) {
+  const int cap = max_selected > 0 ? max_selected : max_blocks;
+  const size_t split = (size_t)B * hq * ls_attn_num_splits(cap) * (head_dim + 2) * sizeof(float);
+  const int pairs = B * ((hq + 3) / 4);
+  const size_t flow =
+      ls::flow_parts_bytes(pairs, head_dim, ls::flow_plan(pairs, max_blocks, cap).splits);
+  return align_up(split > flow ? split : flow);
+}
+
+struct AttnWs {
+  size_t parts, total;
+};
+// ctl_heads: num_kv_heads in a call; the size query only knows num_q_heads
+// (an upper bound), so it may reserve more than a call uses.
+AttnWs attn_ws(int B, int ctl_heads, int hq, int head_dim, int max_selected, int max_blocks) {
+  AttnWs w;
+  w.parts = ls::flow_ctl_bytes(B * ctl_heads);
+  w.total = w.parts + attn_parts_bytes(B, hq, head_dim, max_selected, max_blocks);
+  return w;
+}
+
+struct StepWs {
+  size_t rows, ranges, ents, parts, total;
+};
+StepWs step_ws(int B, int hq, int hkv, int head_dim, int max_blocks, int max_selected) {
+  StepWs w;
+  w.rows = ls::flow_ctl_bytes(B * hkv);
+  w.ranges = w.rows + ls::flow_rows_bytes(B * hkv, max_blocks);
+  w.ents = w.ranges + ls::flow_ranges_bytes(B * hkv);
+  w.parts = w.ents + ls::flow_ents_bytes(B * hkv, max_selected);
+  w.total = w.parts + attn_parts_bytes(B, hq, head_dim, max_selected, max_blocks);
+  return w;
+}
+
+// Which kernels serve a selection / attention / step call. The per-pair
+// kernels (one workgroup owns a (request, kv head) pair from scoring to
+// output, no hand-off between workgroups) are faster when there are at
+// least kItemMinPairs pairs of at most 4096 blocks; the flow kernel (a
+// pair spread over many workgroups) serves the other shapes up to
+// kFlowMaxBlocks blocks; longer requests take the split kernels.
+enum Route { kRouteItem, kRouteFlow, kRouteSplit };
+Route route(const ls_pool& pool, const ls_batch& batch, int num_q_heads) {
+  const int group = num_q_heads / pool.num_heads;
+  if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, group, batch.max_blocks,
+                    pool.num_pages) &&
+      batch.max_blocks <= 4096)
+    return kRouteItem;
+  if (ls::flow_ok(group, pool.head_dim, batch.max_blocks, pool.num_pages)) return kRouteFlow;
+  return kRouteSplit;
+}
+
+ls::FlowArgs flow_args(const ls::ScoreArgs& sa, const ls::TopkArgs& ta, const ls::AttnArgs& aa,
+                       const ls::SummaryUpdate& up, int pairs, int max_blocks, int max_selected,
+                       char* w, size_t rows_off, size_t ranges_off, size_t parts_off,
+                       float* rows, size_t ents_off = 0) {
+  ls::FlowArgs f;
+  f.sa = sa;
+  f.ta = ta;
+  f.aa = aa;
+  f.up = up;
+  f.ctl = reinterpret_cast<uint32_t*>(w);
+  f.score_rows = rows ? rows : reinterpret_cast<float*>(w + rows_off);
+  f.ranges = reinterpret_cast<float*>(w + ranges_off);
+  f.parts = reinterpret_cast<float*>(w + parts_off);
+  f.ents = ents_off ? reinterpret_cast<int32_t*>(w + ents_off) : nullptr;
+  f.pairs = pairs;
+  f.max_blocks = max_blocks;
+  const ls::FlowPlan pl = ls::flow_plan(pairs, max_blocks, max_selected);
+  f.chunks = pl.chunks;
+  f.chunk_tiles = pl.chunk_tiles;
+  f.splits = pl.splits;
+  f.split = pl.split;
+  f.n_refresh = (up.n_tiles + ls::kFlowWaves - 1) / ls::kFlowWaves;
+  return f;
+}
+
+// Host-side validation of ls_sparse_decode_step's arguments (workspace aside).
+ls_status check_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const void* summaries,
+                     const void* k_pool, const void* v_pool, const ls_pool& pool,
+                     const ls_batch& batch, const ls_select_params* p, const int32_t* selected,
+                     const int32_t* selected_count, float sm_scale, const void* out,
+                     int32_t out_dtype, const int32_t* new_page_ids, int32_t n_new_pages) {
+  if (!p) return fail(LS_ERR_INVALID, "params must be non-null");
+  if (p->struct_size != (int32_t)sizeof(ls_select_params))
+    return fail(LS_ERR_INVALID, "params.struct_size %d != %d", p->struct_size,
+                (int)sizeof(ls_select_params));
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  if ((st = check_gqa_pool(pool, "kv pool")) != LS_OK) return st;
+  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
+  if (out_dtype != LS_DTYPE_BF16 && out_dtype != LS_DTYPE_FP32)
+    return fail(LS_ERR_UNSUPPORTED, "out_dtype %d (supported: bf16, fp32)", out_dtype);
+  if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
+    return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                pool.num_heads);
+  if (num_q_heads / pool.num_heads != 4)
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
+                num_q_heads / pool.num_heads);
+  if (p->group_agg != LS_AGG_MAX && p->group_agg != LS_AGG_MEAN)
+    return fail(LS_ERR_INVALID, "group_agg %d", p->group_agg);
+  if (p->score_mode != LS_SCORE_MEAN && p->score_mode != LS_SCORE_BOUNDS)
+    return fail(LS_ERR_INVALID, "score_mode %d", p->score_mode);
+  if (p->score_mode == LS_SCORE_BOUNDS && batch.batch_size > 0 && !bounds_ok(pool, batch))
+    return fail(LS_ERR_UNSUPPORTED,
+                "bounds scoring needs max_blocks <= 8192 and num_pages < 2^26");
+  if (p->n_sink < 0 || p->n_recent < 0) return fail(LS_ERR_INVALID, "n_sink/n_recent < 0");
+  if (p->topk < -1) return fail(LS_ERR_INVALID, "topk %d (>= 0, or -1 for keep_ratio)", p->topk);
+  if (p->topk == -1 && !(p->keep_ratio >= 0.0f && p->keep_ratio <= 1.0f))
+    return fail(LS_ERR_INVALID, "keep_ratio must be in [0, 1]");
+  if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
+  if (n_new_pages < 0) return fail(LS_ERR_INVALID, "n_new_pages < 0");
+  if (n_new_pages > 0 && !new_page_ids)
+    return fail(LS_ERR_INVALID, "new_page_ids must be non-null when n_new_pages > 0");
+  if (n_new_pages > 0 && p->n_recent < 1)
+    return fail(LS_ERR_INVALID,
+                "refreshing summaries in the step needs n_recent >= 1 (a page that just filled "
+                "must not be scored in the same call)");
+  if (batch.batch_size == 0) return ok();
+  if (batch.max_blocks > 16384)
+    return fail(LS_ERR_UNSUPPORTED, "max_blocks %d (supported: <= 16384)", batch.max_blocks);
+  const int need = max_total_selected(*p, batch.max_blocks);
+  if (p->max_selected < need)
+    return fail(LS_ERR_INVALID, "max_selected %d < %d (largest possible selection)",
+                p->max_selected, need);
+  if (!q || !summaries || !k_pool || !v_pool || !selected || !selected_count || !out)
+    return fail(LS_ERR_INVALID, "q, summaries, pools, selection and out must be non-null");
+  if (!aligned16(q) || !aligned16(summaries) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(LS_ERR_INVALID, "q, summaries, k_pool and v_pool must be 16-byte aligned");
+  return ok();
+}
+
+// The step over a validated workspace `w` laid out as `lay`.
+ls_status run_step(const void* q, int32_t num_q_heads, void* summaries, const void* k_pool,
+                   const void* v_pool, const ls_pool& pool, const ls_batch& batch,
+                   const ls_select_params& p, int32_t* selected, int32_t* selected_count,
+                   float sm_scale, void* out, int32_t out_dtype, float* lse_out,
+                   const int32_t* new_page_ids, int32_t n_new_pages, char* w, const StepWs& lay,
+                   hipStream_t stream) {
+  float* scores = reinterpret_cast<float*>(w + lay.rows);
+  float* partials = reinterpret_cast<float*>(w + lay.parts);
+  const ls::ScoreArgs sa = score_args(q, num_q_heads, summaries, pool, batch, p, scores);
+  const ls::TopkArgs ta = topk_args(sa, p, scores, selected, selected_count);
+  const ls::AttnArgs aa = attn_args(q, num_q_heads, k_pool, v_pool, pool, batch, selected,
+                                    selected_count, p.max_selected,
+                                    ls_attn_num_splits(p.max_selected), sm_scale, partials, out,
+                                    out_dtype, lse_out);
+  const ls::SummaryUpdate up{static_cast<const uint16_t*>(k_pool), new_page_ids,
+                             n_new_pages * pool.num_heads, summaries};
+  const Route rt = route(pool, batch, num_q_heads);
+  if (rt == kRouteItem) {
+    ls::ScoreArgs si = sa;
+    si.scores = nullptr;
+    return hip_status(ls::launch_step_item(si, ta, aa, up, stream), "decode-step kernel launch");
+  }
+  if (rt == kRouteFlow) {
+    const ls::FlowArgs f = flow_args(sa, ta, aa, up, batch.batch_size * pool.num_heads,
+                                     batch.max_blocks, p.max_selected, w, lay.rows, lay.ranges,
+                                     lay.parts, nullptr, lay.ents);
+    return hip_status(ls::launch_flow(f, ls::kFlowStep, stream), "decode-step kernel launch");
+  }
+  // longer requests: the split kernels of the two calls back to back
+  hipError_t e = hipSuccess;
+  if (n_new_pages > 0) {
+    const ls::SummaryArgs su{k_pool, nullptr, pool, new_page_ids, n_new_pages, summaries,
+                             LS_DTYPE_BF16};
+    e = ls::launch_summaries(su, stream);
+    if (e != hipSuccess) return hip_status(e, "summary kernel launch");
+  }
+  e = ls::launch_score(sa, stream);
+  if (e == hipSuccess) e = ls::launch_topk(ta, stream);
+  if (e == hipSuccess) e = ls::launch_attn(aa, stream);
+  return hip_status(e, "decode-step kernel launches");
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* ls_last_error(void) { return g_err; }
 
-const char* ls_version(void) { return "libls 0.5.0 abi 5 gfx950"; }
+const char* ls_version(void) { return "libls 0.6.0 abi 6 gfx950"; }
+
+size_t ls_workspace_control_bytes(int32_t batch_size, int32_t num_kv_heads) {
+  if (batch_size <= 0 || num_kv_heads <= 0) return 0;
+  return ls::flow_ctl_bytes(batch_size * num_kv_heads);
+}
 
 int32_t ls_attn_num_splits(int32_t max_selected) {
   if (max_selected < 1) return 1;
@@ -219,7 +415,7 @@ ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_
 size_t ls_score_select_workspace_size(int32_t batch_size, int32_t num_kv_heads,
                                       int32_t max_blocks) {
   if (batch_size <= 0 || num_kv_heads <= 0 || max_blocks <= 0) return 0;
-  return align_up((size_t)batch_size * num_kv_heads * max_blocks * sizeof(float));
+  return select_ws(batch_size, num_kv_heads, max_blocks).total;
 }
 
 ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
@@ -263,25 +459,26 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
     return fail(LS_ERR_INVALID, "q, summaries, selected and selected_count must be non-null");
   if (!aligned16(q) || !aligned16(summaries))
     return fail(LS_ERR_INVALID, "q and summaries must be 16-byte aligned");
-  const size_t ws = ls_score_select_workspace_size(batch.batch_size, pool.num_heads,
-                                                   batch.max_blocks);
-  float* scores = scores_out;
-  if (!scores) {
-    if (!workspace || workspace_bytes < ws)
-      return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
-    if ((uintptr_t)workspace % kAlign)
-      return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
-    scores = static_cast<float*>(workspace);
-  }
+  const SelectWs lay = select_ws(batch.batch_size, pool.num_heads, batch.max_blocks);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
+  if ((uintptr_t)workspace % kAlign)
+    return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  char* w = static_cast<char*>(workspace);
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(w + lay.rows);
   const ls::ScoreArgs sa = score_args(q, num_q_heads, summaries, pool, batch, *p, scores);
   const ls::TopkArgs ta = topk_args(sa, *p, scores, selected, selected_count);
-  if (sa.bounds || ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim,
-                                 num_q_heads / pool.num_heads, batch.max_blocks,
-                                 pool.num_pages)) {
-    // (bounds are scored by the per-pair selection kernel at any batch size)
+  const Route rt = route(pool, batch, num_q_heads);
+  if (rt == kRouteItem) {
     ls::ScoreArgs si = sa;
     si.scores = scores_out;   // scores stay in LDS unless the caller asked for them
     return hip_status(ls::launch_select_item(si, ta, stream), "selection kernel launch");
+  }
+  if (rt == kRouteFlow) {
+    const ls::FlowArgs f = flow_args(sa, ta, ls::AttnArgs{}, ls::SummaryUpdate{},
+                                     batch.batch_size * pool.num_heads, batch.max_blocks,
+                                     p->max_selected, w, lay.rows, lay.ranges, 0, scores);
+    return hip_status(ls::launch_flow(f, ls::kFlowSelect, stream), "selection kernel launch");
   }
   hipError_t e = ls::launch_score(sa, stream);
   if (e != hipSuccess) return hip_status(e, "score kernel launch");
@@ -292,12 +489,7 @@ size_t ls_sparse_attn_decode_workspace_size(int32_t batch_size, int32_t num_q_he
                                             int32_t head_dim, int32_t max_selected,
                                             int32_t max_blocks) {
   if (batch_size <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  const int cap = max_selected > 0 ? max_selected : max_blocks;
-  const size_t S = (size_t)ls_attn_num_splits(cap);
-  const size_t split = (size_t)batch_size * num_q_heads * S * (head_dim + 2) * sizeof(float);
-  // exchange areas of the two-workgroup pair path (GQA groups of 4)
-  const size_t pair = ls::pair_workspace_bytes(batch_size * ((num_q_heads + 3) / 4), head_dim);
-  return align_up(split > pair ? split : pair);
+  return attn_ws(batch_size, num_q_heads, num_q_heads, head_dim, max_selected, max_blocks).total;
 }
 
 ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,
@@ -328,23 +520,29 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(LS_ERR_INVALID, "q, k_pool and v_pool must be 16-byte aligned");
   const int cap = selected ? max_selected : batch.max_blocks;
-  const size_t ws = ls_sparse_attn_decode_workspace_size(batch.batch_size, num_q_heads,
-                                                         pool.head_dim, selected ? max_selected : 0,
-                                                         batch.max_blocks);
-  if (!workspace || workspace_bytes < ws)
-    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+  const AttnWs lay = attn_ws(batch.batch_size, pool.num_heads, num_q_heads, pool.head_dim,
+                             selected ? max_selected : 0, batch.max_blocks);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
   if ((uintptr_t)workspace % kAlign)
     return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  char* w = static_cast<char*>(workspace);
+  float* partials = reinterpret_cast<float*>(w + lay.parts);
   const ls::AttnArgs aa = attn_args(q, num_q_heads, k_pool, v_pool, pool, batch, selected,
                                     selected_count, max_selected, ls_attn_num_splits(cap),
-                                    sm_scale, static_cast<float*>(workspace), out, out_dtype,
-                                    lse_out);
-  // a selection goes to one workgroup per pair (or two); the dense path
-  // (every block) is split-K over many workgroups per pair, runs of up to
-  // 512 blocks each
-  if (selected && ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim,
-                                num_q_heads / pool.num_heads, batch.max_blocks, pool.num_pages))
+                                    sm_scale, partials, out, out_dtype, lse_out);
+  // a selection: split over several workgroups per pair, merged by the last
+  // one to finish; the dense path (every block) is split-K over runs of up
+  // to 512 blocks, merged by a second kernel
+  const Route rt = route(pool, batch, num_q_heads);
+  if (selected && rt == kRouteItem)
     return hip_status(ls::launch_attn_item(aa, stream), "attention kernel launch");
+  if (selected && rt == kRouteFlow) {
+    const ls::FlowArgs f = flow_args(ls::ScoreArgs{}, ls::TopkArgs{}, aa, ls::SummaryUpdate{},
+                                     batch.batch_size * pool.num_heads, batch.max_blocks,
+                                     max_selected, w, 0, 0, lay.parts, nullptr);
+    return hip_status(ls::launch_flow(f, ls::kFlowAttend, stream), "attention kernel launch");
+  }
   if (!selected && pool.num_pages < (1 << 26))
     return hip_status(ls::launch_attn_chunked(aa, stream), "attention kernel launch");
   return hip_status(ls::launch_attn(aa, stream), "attention kernel launch");
@@ -356,9 +554,7 @@ size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_he
   if (batch_size <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_blocks <= 0 || max_selected <= 0)
     return 0;
-  return ls_score_select_workspace_size(batch_size, num_kv_heads, max_blocks) +
-         ls_sparse_attn_decode_workspace_size(batch_size, num_q_heads, head_dim, max_selected,
-                                              max_blocks);
+  return step_ws(batch_size, num_q_heads, num_kv_heads, head_dim, max_blocks, max_selected).total;
 }
 
 ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads,
@@ -368,105 +564,19 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
                                 void* out, int32_t out_dtype, float* lse_out,
                                 const int32_t* new_page_ids, int32_t n_new_pages, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-  if (!p) return fail(LS_ERR_INVALID, "params must be non-null");
-  if (p->struct_size != (int32_t)sizeof(ls_select_params))
-    return fail(LS_ERR_INVALID, "params.struct_size %d != %d", p->struct_size,
-                (int)sizeof(ls_select_params));
-  ls_status st = check_batch(batch);
-  if (st != LS_OK) return st;
-  if ((st = check_gqa_pool(pool, "kv pool")) != LS_OK) return st;
-  if (q_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "q_dtype must be bf16");
-  if (out_dtype != LS_DTYPE_BF16 && out_dtype != LS_DTYPE_FP32)
-    return fail(LS_ERR_UNSUPPORTED, "out_dtype %d (supported: bf16, fp32)", out_dtype);
-  if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
-    return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
-                pool.num_heads);
-  if (num_q_heads / pool.num_heads != 4)
-    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
-                num_q_heads / pool.num_heads);
-  if (p->group_agg != LS_AGG_MAX && p->group_agg != LS_AGG_MEAN)
-    return fail(LS_ERR_INVALID, "group_agg %d", p->group_agg);
-  if (p->score_mode != LS_SCORE_MEAN && p->score_mode != LS_SCORE_BOUNDS)
-    return fail(LS_ERR_INVALID, "score_mode %d", p->score_mode);
-  if (p->score_mode == LS_SCORE_BOUNDS && batch.batch_size > 0 && !bounds_ok(pool, batch))
-    return fail(LS_ERR_UNSUPPORTED,
-                "bounds scoring needs max_blocks <= 8192 and num_pages < 2^26");
-  if (p->n_sink < 0 || p->n_recent < 0) return fail(LS_ERR_INVALID, "n_sink/n_recent < 0");
-  if (p->topk < -1) return fail(LS_ERR_INVALID, "topk %d (>= 0, or -1 for keep_ratio)", p->topk);
-  if (p->topk == -1 && !(p->keep_ratio >= 0.0f && p->keep_ratio <= 1.0f))
-    return fail(LS_ERR_INVALID, "keep_ratio must be in [0, 1]");
-  if (!std::isfinite(sm_scale)) return fail(LS_ERR_INVALID, "sm_scale must be finite");
-  if (n_new_pages < 0) return fail(LS_ERR_INVALID, "n_new_pages < 0");
-  if (n_new_pages > 0 && !new_page_ids)
-    return fail(LS_ERR_INVALID, "new_page_ids must be non-null when n_new_pages > 0");
-  if (n_new_pages > 0 && p->n_recent < 1)
-    return fail(LS_ERR_INVALID,
-                "refreshing summaries in the step needs n_recent >= 1 (a page that just filled "
-                "must not be scored in the same call)");
-  if (batch.batch_size == 0) return ok();
-  if (batch.max_blocks > 16384)
-    return fail(LS_ERR_UNSUPPORTED, "max_blocks %d (supported: <= 16384)", batch.max_blocks);
-  const int need = max_total_selected(*p, batch.max_blocks);
-  if (p->max_selected < need)
-    return fail(LS_ERR_INVALID, "max_selected %d < %d (largest possible selection)",
-                p->max_selected, need);
-  if (!q || !summaries || !k_pool || !v_pool || !selected || !selected_count || !out)
-    return fail(LS_ERR_INVALID, "q, summaries, pools, selection and out must be non-null");
-  if (!aligned16(q) || !aligned16(summaries) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(LS_ERR_INVALID, "q, summaries, k_pool and v_pool must be 16-byte aligned");
-  const size_t ws = ls_sparse_decode_step_workspace_size(batch.batch_size, num_q_heads,
-                                                         pool.num_heads, pool.head_dim,
-                                                         batch.max_blocks, p->max_selected);
-  if (!workspace || workspace_bytes < ws)
-    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, ws);
+  const ls_status st = check_step(q, q_dtype, num_q_heads, summaries, k_pool, v_pool, pool, batch,
+                                  p, selected, selected_count, sm_scale, out, out_dtype,
+                                  new_page_ids, n_new_pages);
+  if (st != LS_OK || batch.batch_size == 0) return st;
+  const StepWs lay = step_ws(batch.batch_size, num_q_heads, pool.num_heads, pool.head_dim,
+                             batch.max_blocks, p->max_selected);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
   if ((uintptr_t)workspace % kAlign)
     return fail(LS_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
-  char* w = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(w);
-  float* partials = reinterpret_cast<float*>(
-      w + ls_score_select_workspace_size(batch.batch_size, pool.num_heads, batch.max_blocks));
-  const ls::ScoreArgs sa = score_args(q, num_q_heads, summaries, pool, batch, *p, scores);
-  const ls::TopkArgs ta = topk_args(sa, *p, scores, selected, selected_count);
-  const ls::AttnArgs aa = attn_args(q, num_q_heads, k_pool, v_pool, pool, batch, selected,
-                                    selected_count, p->max_selected,
-                                    ls_attn_num_splits(p->max_selected), sm_scale, partials, out,
-                                    out_dtype, lse_out);
-  const ls::SummaryUpdate up{static_cast<const uint16_t*>(k_pool), new_page_ids,
-                             n_new_pages * pool.num_heads, summaries};
-  const bool item = ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim,
-                                  num_q_heads / pool.num_heads, batch.max_blocks, pool.num_pages);
-  // the fused kernels score bounds in one workgroup per pair only
-  const bool split_pairs = ls::pair_path(batch.batch_size, pool.num_heads, batch.max_blocks);
-  if (item && !(sa.bounds && split_pairs)) {
-    ls::ScoreArgs si = sa;
-    si.scores = nullptr;
-    return hip_status(ls::launch_step_item(si, ta, aa, up, stream), "decode-step kernel launch");
-  }
-  hipError_t e = hipSuccess;
-  if (sa.bounds) {
-    // bounds first (if asked), the per-pair selection, then the attention
-    if (n_new_pages > 0) {
-      const ls::SummaryArgs su{k_pool, nullptr, pool, new_page_ids, n_new_pages, summaries,
-                               LS_DTYPE_BF16};
-      e = ls::launch_bounds(su, stream);
-      if (e != hipSuccess) return hip_status(e, "bounds kernel launch");
-    }
-    ls::ScoreArgs si = sa;
-    si.scores = nullptr;
-    e = ls::launch_select_item(si, ta, stream);
-    if (e == hipSuccess) e = item ? ls::launch_attn_item(aa, stream) : ls::launch_attn(aa, stream);
-    return hip_status(e, "decode-step kernel launches");
-  }
-  if (n_new_pages > 0) {
-    const ls::SummaryArgs su{k_pool, nullptr, pool, new_page_ids, n_new_pages, summaries,
-                             LS_DTYPE_BF16};
-    e = ls::launch_summaries(su, stream);
-    if (e != hipSuccess) return hip_status(e, "summary kernel launch");
-  }
-  e = ls::launch_score(sa, stream);
-  if (e == hipSuccess) e = ls::launch_topk(ta, stream);
-  if (e == hipSuccess) e = ls::launch_attn(aa, stream);
-  return hip_status(e, "decode-step kernel launches");
+  return run_step(q, num_q_heads, summaries, k_pool, v_pool, pool, batch, *p, selected,
+                  selected_count, sm_scale, out, out_dtype, lse_out, new_page_ids, n_new_pages,
+                  static_cast<char*>(workspace), lay, stream);
 }
 
 // ------------------------------------------------------ learned indexer ----

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 def test_version_and_empty_error():
     lib = _lib.load()
     assert b"gfx950" in lib.ls_version()
-    assert b"abi 5" in lib.ls_version()
+    assert b"abi 6" in lib.ls_version()
 
 
 def _pool(**kw):

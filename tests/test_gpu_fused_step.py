@@ -70,6 +70,49 @@ def test_fused_workspace_reuse_across_calls():
         sep = run_gpu_step(inp)
         fus = run_gpu_fused(inp, summaries=sep.summaries, workspace=ws)
         _same(sep, fus)
+        # every arrival counter, ready flag and the error word are back at zero
+        ctl = ls.workspace_control_bytes(inp.q.shape[0], cfg.num_kv_heads)
+        torch.cuda.synchronize()
+        assert ctl > 0 and int(torch.count_nonzero(ws[:ctl])) == 0
+
+
+def test_control_words_left_zero_by_every_call():
+    """Selection, attention and step calls each leave the control words of
+    their workspace at zero (counters reset by their last arrival, no wait
+    gave up), also when one workspace serves all three in turn."""
+    import query_aware_sparse_ls_amd as ls
+    from parity_util import paged_batch
+    cfg = reduced(LLAMA8B_32K_B16, batch=5, context=2500)
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=9)
+    B, Hq, D = inp.q.shape
+    Hkv = cfg.num_kv_heads
+    batch = paged_batch(inp)
+    maxsel = inp.topk + cfg.n_sink + cfg.n_recent + 1
+    n = max(ls.score_select_workspace_size(B, Hkv, batch.max_blocks),
+            ls.sparse_attn_decode_workspace_size(B, Hq, D, maxsel, batch.max_blocks),
+            ls.sparse_decode_step_workspace(B, Hq, Hkv, D, batch.max_blocks, maxsel,
+                                            "cuda").numel())
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    ctl = ls.workspace_control_bytes(B, Hkv)
+    ref = run_gpu_step(inp)
+    for it in range(3):
+        sel, cnt = ls.score_select(inp.q, ref.summaries, cfg.page_size, batch, topk=inp.topk,
+                                   n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                                   max_selected=maxsel, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:ctl])) == 0, f"select {it}"
+        assert torch.equal(cnt, ref.counts)
+        out, _ = ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, batch, sel, cnt,
+                                       sm_scale=1.0 / math.sqrt(D), workspace=ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:ctl])) == 0, f"attention {it}"
+        out2, _, _, cnt2 = ls.sparse_decode_step(inp.q, ref.summaries, inp.k_pool, inp.v_pool,
+                                                 batch, topk=inp.topk, n_sink=cfg.n_sink,
+                                                 n_recent=cfg.n_recent, max_selected=maxsel,
+                                                 sm_scale=1.0 / math.sqrt(D), workspace=ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:ctl])) == 0, f"step {it}"
+        assert torch.equal(out, out2) and torch.equal(cnt2, ref.counts)
 
 
 def test_fused_step_hip_graph_replay():
@@ -124,7 +167,7 @@ def test_fused_full_size_llama8b_32k_b16():
         check_pair(inp, fus, r, g, **_kw(inp))
 
 
-@pytest.mark.parametrize("batch", [16, 2])   # one launch (128 pairs) / split kernels (16 pairs)
+@pytest.mark.parametrize("batch", [16, 2])   # 128 and 16 (request, kv head) pairs
 def test_step_refreshes_pages_that_filled(batch):
     """Every request's last page just filled: the step rebuilds those pages'
     summaries itself (rows start as NaN) and gives the same summaries,
