@@ -337,6 +337,30 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
                                 const int32_t* new_page_ids, int32_t n_new_pages, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The same step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument. Its scratch is a fixed device array inside the
+ * library, ls_noalloc_scratch_bytes() bytes (32 MiB) per GPU, held until the
+ * process ends; the call allocates and frees nothing. Shapes whose
+ * ls_sparse_decode_step_workspace_size() exceeds that size are rejected with
+ * LS_ERR_UNSUPPORTED. Each call clears the array's control words itself (one
+ * small fill kernel on `stream` before the step). Every call on a GPU uses
+ * that GPU's one array, so calls that overlap on one GPU (other streams,
+ * other host threads) race and give unspecified results: serialise them.
+ * Arguments, results and errors otherwise as ls_sparse_decode_step (the
+ * same kernels, hence the same bits).
+ */
+size_t ls_noalloc_scratch_bytes(void);
+
+ls_status ls_sparse_decode_step_noalloc(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                        void* summaries, const void* k_pool, const void* v_pool,
+                                        ls_pool pool, ls_batch batch, const ls_select_params* p,
+                                        int32_t* selected, int32_t* selected_count,
+                                        float sm_scale, void* out, int32_t out_dtype,
+                                        float* lse_out, const int32_t* new_page_ids,
+                                        int32_t n_new_pages, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* 5. Learned-indexer selection                                             */
 /* ------------------------------------------------------------------------ */

@@ -26,7 +26,7 @@ _L = _lib.load()
 __all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_select", "sparse_attn_decode",
            "score_select_workspace_size", "sparse_attn_decode_workspace_size",
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
-           "sparse_decode_step_workspace", "workspace_control_bytes", "indexer_select", "indexer_select_workspace_size",
+           "sparse_decode_step_workspace", "sparse_decode_step_noalloc", "workspace_control_bytes", "indexer_select", "indexer_select_workspace_size",
            "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
            "mla_num_splits", "pq_encode", "pq_train", "pq_select", "window_attn_decode",
            "snapkv_select", "snapkv_gather"]
@@ -295,6 +295,41 @@ def sparse_decode_step(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.T
                                    float(sm_scale), out.data_ptr(), _DT[out.dtype], _ptr(lse),
                                    _ptr(new_pages), n_new, workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse, selected, selected_count
+
+
+def sparse_decode_step_noalloc(q: torch.Tensor, summaries: torch.Tensor, k_pool: torch.Tensor,
+                               v_pool: torch.Tensor, batch: PagedBatch, *, topk: int,
+                               n_sink: int, n_recent: int, max_selected: int, sm_scale: float,
+                               selected: torch.Tensor, selected_count: torch.Tensor,
+                               out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                               group_agg: str = "max", keep_ratio: float = 0.0,
+                               score_mode: str = "mean",
+                               new_pages: Optional[torch.Tensor] = None, stream=None):
+    """sparse_decode_step with the library's fixed scratch array instead of
+    a workspace (no device allocation; outputs are the caller's)."""
+    _need(q, torch.bfloat16); _need(summaries, torch.bfloat16)
+    _need(k_pool, torch.bfloat16); _need(v_pool, torch.bfloat16)
+    _need(selected, torch.int32); _need(selected_count, torch.int32); _need(out)
+    if lse is not None:
+        _need(lse, torch.float32)
+    B, Hq, D = q.shape
+    _, Hkv, P, _ = k_pool.shape
+    params = LsSelectParams(C.sizeof(LsSelectParams),
+                            LS_AGG_MAX if group_agg == "max" else LS_AGG_MEAN,
+                            int(topk), float(keep_ratio), int(n_sink), int(n_recent),
+                            int(max_selected), _score_mode(score_mode, summaries, D))
+    n_new = 0
+    if new_pages is not None:
+        _need(new_pages, torch.int32)
+        n_new = int(new_pages.numel())
+    pool = _pool(k_pool, int(Hkv), int(P), int(D))
+    check(_L.ls_sparse_decode_step_noalloc(q.data_ptr(), LS_DTYPE_BF16, int(Hq),
+                                           summaries.data_ptr(), k_pool.data_ptr(),
+                                           v_pool.data_ptr(), pool, batch.c(), C.byref(params),
+                                           selected.data_ptr(), selected_count.data_ptr(),
+                                           float(sm_scale), out.data_ptr(), _DT[out.dtype],
+                                           _ptr(lse), _ptr(new_pages), n_new, _stream(stream)))
     return out, lse, selected, selected_count
 
 

@@ -57,6 +57,10 @@ _SIGS = {
     "ls_sparse_decode_step": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, LsPool, LsBatch,
                                         C.POINTER(LsSelectParams), _P, _P, C.c_float, _P,
                                         C.c_int32, _P, _P, C.c_int32, _P, C.c_size_t, _P]),
+    "ls_noalloc_scratch_bytes": (C.c_size_t, []),
+    "ls_sparse_decode_step_noalloc": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, LsPool,
+                                                LsBatch, C.POINTER(LsSelectParams), _P, _P,
+                                                C.c_float, _P, C.c_int32, _P, _P, C.c_int32, _P]),
     "ls_indexer_score_stride": (C.c_int32, [C.c_int32, C.c_int32]),
     "ls_indexer_select_workspace_size": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32]),
     "ls_indexer_select": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, LsPool, LsBatch, _P,

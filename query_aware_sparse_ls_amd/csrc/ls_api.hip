@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include <algorithm>
+#include <mutex>
 
 #include "ls_flow.h"
 #include "ls_internal.h"
@@ -345,6 +346,45 @@ ls_status run_step(const void* q, int32_t num_q_heads, void* summaries, const vo
   return hip_status(e, "decode-step kernel launches");
 }
 
+// ---- no-allocation step: a fixed device array instead of a caller workspace
+
+// Bytes of the array; ls_sparse_decode_step_noalloc rejects shapes whose
+// step workspace is larger.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+constexpr int kNoAllocMaxDevices = 64;
+
+// One copy per GPU, held by the loaded library until the process ends. In
+// host code the name is only a stand-in: the device address comes from
+// hipGetSymbolAddress (scratch_ptr), and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// The calling thread's current device's copy of the array (looked up once
+// per device, with that device current).
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -577,6 +617,41 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
   return run_step(q, num_q_heads, summaries, k_pool, v_pool, pool, batch, *p, selected,
                   selected_count, sm_scale, out, out_dtype, lse_out, new_page_ids, n_new_pages,
                   static_cast<char*>(workspace), lay, stream);
+}
+
+size_t ls_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+ls_status ls_sparse_decode_step_noalloc(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                        void* summaries, const void* k_pool, const void* v_pool,
+                                        ls_pool pool, ls_batch batch, const ls_select_params* p,
+                                        int32_t* selected, int32_t* selected_count,
+                                        float sm_scale, void* out, int32_t out_dtype,
+                                        float* lse_out, const int32_t* new_page_ids,
+                                        int32_t n_new_pages, hipStream_t stream) {
+  const ls_status st = check_step(q, q_dtype, num_q_heads, summaries, k_pool, v_pool, pool, batch,
+                                  p, selected, selected_count, sm_scale, out, out_dtype,
+                                  new_page_ids, n_new_pages);
+  if (st != LS_OK || batch.batch_size == 0) return st;
+  const StepWs lay = step_ws(batch.batch_size, num_q_heads, pool.num_heads, pool.head_dim,
+                             batch.max_blocks, p->max_selected);
+  if (lay.total > kNoAllocScratchBytes)
+    return fail(LS_ERR_UNSUPPORTED,
+                "ls_sparse_decode_step_noalloc: this shape needs %zu bytes of scratch, more than "
+                "the library's fixed %zu (use ls_sparse_decode_step with a workspace)",
+                lay.total, kNoAllocScratchBytes);
+  void* w = nullptr;
+  hipError_t e = scratch_ptr(&w);
+  if (e != hipSuccess) return hip_status(e, "scratch address lookup");
+  // the control words must start at zero; the array keeps the last call's
+  // contents, so clear them here (a fill kernel: capturable in a graph)
+  const size_t nz = lay.rows / sizeof(uint32_t);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(w), nz);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_status(e, "scratch clear launch");
+  return run_step(q, num_q_heads, summaries, k_pool, v_pool, pool, batch, *p, selected,
+                  selected_count, sm_scale, out, out_dtype, lse_out, new_page_ids, n_new_pages,
+                  static_cast<char*>(w), lay, stream);
 }
 
 // ------------------------------------------------------ learned indexer ----

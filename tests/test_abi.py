@@ -168,6 +168,35 @@ def test_step_validation():
     assert call(batch=_batch(batch_size=0), new=FAKE, n_new=2) == _lib.LS_OK
 
 
+def test_noalloc_step_validation():
+    """The no-allocation step validates like the step, and rejects on the host
+    any shape whose scratch need exceeds the library's fixed array."""
+    lib = _lib.load()
+    assert lib.ls_noalloc_scratch_bytes() == 32 << 20
+
+    def call(p=None, **kw):
+        a = dict(q=FAKE, summ=FAKE, k=FAKE, v=FAKE, pool=_pool(num_pages=1 << 20),
+                 batch=_batch(), sel=FAKE, cnt=FAKE, scale=0.1, out=FAKE,
+                 out_dtype=_lib.LS_DTYPE_BF16, lse=None, new=None, n_new=0)
+        a.update(kw)
+        pp = C.byref(p if p is not None else _params())
+        return lib.ls_sparse_decode_step_noalloc(a["q"], _lib.LS_DTYPE_BF16, 32, a["summ"],
+                                                 a["k"], a["v"], a["pool"], a["batch"], pp,
+                                                 a["sel"], a["cnt"], a["scale"], a["out"],
+                                                 a["out_dtype"], a["lse"], a["new"], a["n_new"],
+                                                 None)
+
+    assert call(n_new=2) == _lib.LS_ERR_INVALID                  # pages missing
+    assert call(p=_params(struct_size=3)) == _lib.LS_ERR_INVALID
+    assert call(batch=_batch(batch_size=0)) == _lib.LS_OK
+    # 1024 (request, kv head) pairs x 8192 blocks: 32 MiB of scores alone
+    big = _batch(batch_size=128, max_blocks=8192)
+    assert call(batch=big, p=_params(max_selected=8192)) == _lib.LS_ERR_UNSUPPORTED
+    assert b"scratch" in lib.ls_last_error()
+    need = lib.ls_sparse_decode_step_workspace_size(128, 32, 8, 128, 8192, 8192)
+    assert need > lib.ls_noalloc_scratch_bytes()
+
+
 def test_bounds_validation():
     lib = _lib.load()
     f = lib.ls_build_block_bounds
