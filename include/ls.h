@@ -49,6 +49,16 @@
  *   (Vortex, "Running it: vTensor": cache entries live in pages of the KV
  *   allocator).
  * - bf16 is IEEE binary32's upper half; fp8 is OCP e4m3fn.
+ * - Workspaces of ls_score_select, ls_sparse_attn_decode and
+ *   ls_sparse_decode_step: device memory the caller zero-fills before its
+ *   first use (e.g. hipMemset once at allocation). Every call leaves it zero
+ *   again, so it can be reused by later calls of any of the three (not by
+ *   calls running concurrently). Inside a call, workgroups hand data to
+ *   each other through it (block scores, walk entries of the selection,
+ *   partial softmax states): a word is zero until written, the reader polls
+ *   it and writes zero back. Word 0 is an error word: non-zero after a call
+ *   means a workgroup gave up waiting for a hand-off (never expected; that
+ *   call's results are then unspecified).
  */
 #ifndef LS_H_
 #define LS_H_
@@ -207,15 +217,14 @@ ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_
  *                 s_j for candidate blocks (other entries unspecified).
  * workspace:      device scratch of at least ls_score_select_workspace_size()
  *                 bytes, 256-byte aligned, always required (also with
- *                 scores_out); its first ls_workspace_control_bytes(batch,
- *                 num_kv_heads) bytes must be zero before its first use
- *                 (every call leaves them zero), the rest need not be
- *                 initialised.
- * Execution (requests of at most 8192 blocks): one launch; the candidate
- *                 blocks of each (request, kv head) pair are scored in chunks
- *                 of 64-128 blocks by separate workgroups, and the last chunk
- *                 of a pair to finish ranks the pair (longer requests: a
- *                 scoring kernel, then a top-k kernel).
+ *                 scores_out); zero-filled before its first use (every
+ *                 call leaves it zero, see "Workspaces" below).
+ * Execution: one workgroup per (request, kv head) pair scores and ranks it
+ *                 in LDS when there are at least 64 pairs of at most 4096
+ *                 blocks; other shapes of at most 8192 blocks take one
+ *                 launch in which workgroups score chunks of 64-128 blocks
+ *                 and the pair's last chunk ranks it; longer requests take a
+ *                 scoring kernel and a top-k kernel.
  * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
  *            page_size 16; max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192,
  *            num_pages < 2^26).
@@ -263,9 +272,8 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
  * out:            [batch][num_q_heads][head_dim] of out_dtype (bf16 or fp32).
  * lse_out:        NULL or [batch][num_q_heads] fp32.
  * workspace:      >= ls_sparse_attn_decode_workspace_size() bytes, 256-byte
- *                 aligned (split partial results); its first
- *                 ls_workspace_control_bytes(batch, num_kv_heads) bytes must
- *                 be zero before its first use (every call leaves them zero).
+ *                 aligned (split partial results); zero-filled before its
+ *                 first use (every call leaves it zero).
  * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
  *            page_size 16.
  */
@@ -315,9 +323,8 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
  *   p->n_recent >= 1 (checked). Otherwise call ls_build_block_summaries
  *   first.
  * workspace: >= ls_sparse_decode_step_workspace_size() bytes, 256-byte
- *   aligned (control words, block scores, split partials); its first
- *   ls_workspace_control_bytes(batch, num_kv_heads) bytes must be zero before
- *   its first use and every call leaves them zero; calls that run
+ *   aligned (block scores, walk entries, split states); zero-filled before
+ *   its first use, and every call leaves it zero; calls that run
  *   concurrently need separate workspaces.
  * Supported: head_dim 64 or 128; GQA group 4; page_size 16;
  *   max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192 and num_pages < 2^26;
@@ -660,16 +667,6 @@ const char* ls_version(void);
  * selection capacity (max_selected, or max_blocks on the dense path). */
 int32_t ls_attn_num_splits(int32_t max_selected);
 
-/* Bytes of control words at the start of the workspace of ls_score_select,
- * ls_sparse_attn_decode and ls_sparse_decode_step for a batch of batch_size
- * requests with num_kv_heads KV heads.
- * These words (per-(request, kv head) arrival counters, ready flags and an
- * error word) must be zero before the workspace is first used; every call
- * leaves them zero again, so a workspace can be reused by calls that do not
- * run concurrently. A non-zero error word after a call means a workgroup gave
- * up waiting for a selection (never expected; the results of that call are
- * then unspecified). The rest of a workspace needs no initialisation. */
-size_t ls_workspace_control_bytes(int32_t batch_size, int32_t num_kv_heads);
 
 #ifdef __cplusplus
 }

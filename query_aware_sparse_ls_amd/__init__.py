@@ -26,7 +26,7 @@ _L = _lib.load()
 __all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_select", "sparse_attn_decode",
            "score_select_workspace_size", "sparse_attn_decode_workspace_size",
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
-           "sparse_decode_step_workspace", "sparse_decode_step_noalloc", "workspace_control_bytes", "indexer_select", "indexer_select_workspace_size",
+           "sparse_decode_step_workspace", "sparse_decode_step_noalloc", "indexer_select", "indexer_select_workspace_size",
            "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
            "mla_num_splits", "pq_encode", "pq_train", "pq_select", "window_attn_decode",
            "snapkv_select", "snapkv_gather"]
@@ -82,9 +82,9 @@ def _pool(t: torch.Tensor, num_heads: int, page_size: int, head_dim: int) -> LsP
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
-    """The caller's workspace, or a new zero-filled one (the selection and
-    attention calls keep control words at the start of their workspace that
-    must be zero before its first use; every call leaves them zero)."""
+    """The caller's workspace, or a new zero-filled one (the selection,
+    attention and step calls need a workspace that is zero before its first
+    use; every call leaves it zero)."""
     if ws is not None:
         return ws
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -191,11 +191,6 @@ def attn_num_splits(max_selected: int) -> int:
     return int(_L.ls_attn_num_splits(int(max_selected)))
 
 
-def workspace_control_bytes(batch_size: int, num_kv_heads: int) -> int:
-    """Bytes of control words at the start of a selection / attention / step
-    workspace (zero before first use, left zero by every call)."""
-    return int(_L.ls_workspace_control_bytes(int(batch_size), int(num_kv_heads)))
-
 
 def sparse_attn_decode_workspace_size(batch_size: int, num_q_heads: int, head_dim: int,
                                       max_selected: int, max_blocks: int) -> int:
@@ -240,9 +235,9 @@ def sparse_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
 def sparse_decode_step_workspace(batch_size: int, num_q_heads: int, num_kv_heads: int,
                                  head_dim: int, max_blocks: int, max_selected: int,
                                  device) -> torch.Tensor:
-    """A zero-filled workspace for sparse_decode_step (its control words must
-    be zero before the first call; every call leaves them zero, so the
-    workspace can be reused by calls that do not run concurrently)."""
+    """A zero-filled workspace for sparse_decode_step (it must be zero before
+    the first call; every call leaves it zero, so it can be reused by calls
+    that do not run concurrently)."""
     n = int(_L.ls_sparse_decode_step_workspace_size(batch_size, num_q_heads, num_kv_heads,
                                                    head_dim, max_blocks, max_selected))
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)

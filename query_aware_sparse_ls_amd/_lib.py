@@ -89,7 +89,6 @@ _SIGS = {
     "ls_last_error": (C.c_char_p, []),
     "ls_version": (C.c_char_p, []),
     "ls_attn_num_splits": (C.c_int32, [C.c_int32]),
-    "ls_workspace_control_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
 }
 
 _lib = None

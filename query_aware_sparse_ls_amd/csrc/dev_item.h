@@ -50,8 +50,23 @@ static_assert(kItemEntryPad >= 7 + kItemWaves * (2 * kItemPrefetch - 2) + 1, "en
 // Where item_score / item_score_bounds put the scores: every row of the
 // scored tiles into LDS, or the candidate rows into a global score row with
 // plain stores (read by a later launch) or device-coherent stores (read by
-// another workgroup of the same launch).
-enum { kStoreLds = 0, kStoreGlobal = 1, kStoreDev = 2 };
+// another workgroup of the same launch); kStoreDevKey stores the
+// order-preserving key of the score (score_key, never 0 for a finite score)
+// as a uint32, so that a zero word means "not written yet".
+enum { kStoreLds = 0, kStoreGlobal = 1, kStoreDev = 2, kStoreDevKey = 3 };
+
+// How item_attn writes a split's state: plain stores, device-coherent
+// stores, or device-coherent stores of the bitwise complement (never 0 for
+// a finite value: a zero word means "not written yet").
+enum { kSplitPlain = 0, kSplitDev = 1, kSplitDevEnc = 2 };
+
+template <int kMode>
+__device__ __forceinline__ void store_split_word(float* p, float v) {
+  if constexpr (kMode == kSplitDevEnc)
+    st_dev(reinterpret_cast<uint32_t*>(p), ~__float_as_uint(v));
+  else
+    st_x<kMode == kSplitDev>(p, v);
+}
 
 // The 4 group queries as a 16x16x32 MFMA operand, one per k-step of D/32:
 // lane i holds head i%16 (zero past the 4 heads), dims 32j + 8(i/16) .. +8.
@@ -190,7 +205,9 @@ __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, con
       const int b = (t0 + wave + NW * k) * 16 + row;
       const bool cand = b >= geo.c0 && b < geo.c1;
       if constexpr (kStore == kStoreLds) sc[b] = v;
-      else if (cand) st_x<kStore == kStoreDev>(&sc[b], v);
+      else if constexpr (kStore == kStoreDevKey) {
+        if (cand) st_dev(reinterpret_cast<uint32_t*>(sc) + b, score_key(v));
+      } else if (cand) st_x<kStore == kStoreDev>(&sc[b], v);
       smin = cand ? fminf(smin, v) : smin;
       smax = cand ? fmaxf(smax, v) : smax;
     }
@@ -311,7 +328,9 @@ __device__ __forceinline__ void item_score_bounds(const ScoreArgs& a, int r, int
       const int b = (t0 + wave + NW * k) * 16 + row;
       const bool cand = b >= geo.c0 && b < geo.c1;
       if constexpr (kStore == kStoreLds) sc[b] = v;
-      else if (cand) st_x<kStore == kStoreDev>(&sc[b], v);
+      else if constexpr (kStore == kStoreDevKey) {
+        if (cand) st_dev(reinterpret_cast<uint32_t*>(sc) + b, score_key(v));
+      } else if (cand) st_x<kStore == kStoreDev>(&sc[b], v);
       smin = cand ? fminf(smin, v) : smin;
       smax = cand ? fmaxf(smax, v) : smax;
     }
@@ -428,9 +447,8 @@ struct ItemSplit {
 // nt: tokens lo .. nt-1 of the block are attended; page < 2^22), for token
 // ranges that start inside a block.
 // NW: waves of the workgroup; NPF: K/V blocks in flight per wave (at most
-// kItemPrefetch). kDevStore: the split state is written with device-coherent
-// stores (its reader is another workgroup of the same launch).
-template <int D, bool kLo = false, int NW = kItemWaves, bool kDevStore = false,
+// kItemPrefetch). kSplitStore: how the split state is written (kSplit*).
+template <int D, bool kLo = false, int NW = kItemWaves, int kSplitStore = kSplitPlain,
           int NPF = kItemPrefetch>
 __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const int* ent,
                                           int cnt, ItemAttnLds<D, NW>& sh,
@@ -634,10 +652,10 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
       if (e < 4 * D) {
         float* ph = split->part + (((size_t)r * a.num_q_heads + g * 4 + h) * split->num_splits +
                                    split->s) * (D + 2);
-        st_x<kDevStore>(ph + d, Ov[j]);
+        store_split_word<kSplitStore>(ph + d, Ov[j]);
         if (d == 0) {
-          st_x<kDevStore>(ph + D, Mv[j]);
-          st_x<kDevStore>(ph + D + 1, Lv[j]);
+          store_split_word<kSplitStore>(ph + D, Mv[j]);
+          store_split_word<kSplitStore>(ph + D + 1, Lv[j]);
         }
       }
     }

@@ -377,13 +377,17 @@ __device__ __noinline__ int topk_fallback(const float* srow, const ReqGeom& geo,
 
 // srow: LDS, candidate e at srow[e + e / 16] (c1 - c0 <= NT * PER); mn0 / mx0:
 // the smallest and largest candidate score. Called by all NT threads; the
-// caller synchronises after writing srow. sel_lds (optional): a copy of the
-// stored selection. Returns the stored count.
-template <int PER, int NT, bool kDev = false>
+// caller synchronises after writing srow. The selection is handed out as
+// emit(p, b) for every output position p < max_selected: b = the p-th
+// selected block in ascending order, or -1 past the selection (wave 0
+// calls it, except on the fallback path, where every thread may; the
+// fallback writes the selection to fb_out with device-coherent stores and
+// reads it back). Returns the stored count, min(selected, max_selected).
+template <int PER, int NT, class Emit>
 __device__ int topk_fast(const float* __restrict__ srow, const ReqGeom& geo, int k,
-                         int32_t* __restrict__ out, int max_selected,
-                         int32_t* __restrict__ count_out, TopkFastLds& sh, TopkLds& fallback,
-                         int32_t* __restrict__ sel_lds, float mn0, float mx0) {
+                         int max_selected, TopkFastLds& sh, TopkLds& fallback,
+                         int32_t* __restrict__ fb_out, int32_t* __restrict__ fb_count, float mn0,
+                         float mx0, Emit emit) {
   constexpr int NW = NT / kWave;
   static_assert(NT % kWave == 0 && NW <= kTopkMaxWaves && PER >= 1 && PER <= 32, "shape");
   static_assert(NT * PER <= kTopkFastMaxBlocks, "blocks");
@@ -488,8 +492,13 @@ __device__ int topk_fast(const float* __restrict__ srow, const ReqGeom& geo, int
     mx = hi;
   }
   if (robust) {
-    return topk_fallback<PER, NT, kDev>(srow, geo, k, out, max_selected, count_out, fallback,
-                                        sel_lds);
+    const int stored = topk_fallback<PER, NT, true>(srow, geo, k, fb_out, max_selected,
+                                                    fb_count, fallback, nullptr);
+    wait_stores();
+    __syncthreads();
+    for (int p = tid; p < max_selected; p += NT) emit(p, ld_dev(&fb_out[p]));
+    __syncthreads();
+    return stored;
   }
   // the kept blocks into the bitmap: this thread's candidates (consecutive
   // blocks), then the forced ones
@@ -535,19 +544,12 @@ __device__ int topk_fast(const float* __restrict__ srow, const ReqGeom& geo, int
       while (x) {
         const int b = (q * kWave + lane) * 32 + (__ffs(x) - 1);
         x &= x - 1;
-        if (p < max_selected) {
-          st_x<kDev>(&out[p], b);
-          if (sel_lds) sel_lds[p] = b;
-        }
+        if (p < max_selected) emit(p, b);
         ++p;
       }
     }
-    for (int i = total + lane; i < max_selected; i += kWave) st_x<kDev>(&out[i], -1);
-    const int stored = total < max_selected ? total : max_selected;
-    if (lane == 0) {
-      st_x<kDev>(count_out, stored);
-      sh.total = stored;
-    }
+    for (int i = total + lane; i < max_selected; i += kWave) emit(i, -1);
+    if (lane == 0) sh.total = total < max_selected ? total : max_selected;
   }
   __syncthreads();
   return sh.total;

@@ -159,19 +159,22 @@ ls::AttnArgs attn_args(const void* q, int num_q_heads, const void* k_pool, const
 // ---- workspace layouts: the flow kernel's control words first (they must
 // be zero before a workspace's first use, and every call leaves them zero),
 // then the regions each path needs -------------------------------------------
+// ---- workspace layouts. A workspace must be zero-filled before its first
+// use and every call leaves it zero again: the flow kernel's hand-off words
+// are zero until written and are reset by their readers; the split and
+// dense paths zero what they wrote once their last kernel has run.
+// [control words][block scores or keys][walk entries (step)][split states]
 struct SelectWs {
-  size_t rows, ranges, total;
+  size_t rows, total;
 };
 SelectWs select_ws(int B, int hkv, int max_blocks) {
-  const int P = B * hkv;
   SelectWs w;
-  w.rows = ls::flow_ctl_bytes(P);
-  w.ranges = w.rows + ls::flow_rows_bytes(P, max_blocks);
-  w.total = w.ranges + ls::flow_ranges_bytes(P);
+  w.rows = ls::flow_ctl_bytes(B * hkv);
+  w.total = w.rows + ls::flow_keys_bytes(B * hkv, max_blocks);
   return w;
 }
 
-// Split partials of the attention: the split-K kernels' and the flow kernel's.
+// Split states of the attention: the split-K kernels' and the flow kernel's.
 size_t attn_parts_bytes(int B, int hq, int head_dim, int max_selected, int max_blocks) {
   const int cap = max_selected > 0 ? max_selected : max_blocks;
   const size_t split = (size_t)B * hq * ls_attn_num_splits(cap) * (head_dim + 2) * sizeof(float);
@@ -184,23 +187,21 @@ size_t attn_parts_bytes(int B, int hq, int head_dim, int max_selected, int max_b
 struct AttnWs {
   size_t parts, total;
 };
-// ctl_heads: num_kv_heads in a call; the size query only knows num_q_heads
-// (an upper bound), so it may reserve more than a call uses.
-AttnWs attn_ws(int B, int ctl_heads, int hq, int head_dim, int max_selected, int max_blocks) {
+// (counters for up to B * hq pairs: the size query does not know num_kv_heads)
+AttnWs attn_ws(int B, int hq, int head_dim, int max_selected, int max_blocks) {
   AttnWs w;
-  w.parts = ls::flow_ctl_bytes(B * ctl_heads);
+  w.parts = ls::flow_ctl_bytes(B * hq);
   w.total = w.parts + attn_parts_bytes(B, hq, head_dim, max_selected, max_blocks);
   return w;
 }
 
 struct StepWs {
-  size_t rows, ranges, ents, parts, total;
+  size_t rows, ents, parts, total;
 };
 StepWs step_ws(int B, int hq, int hkv, int head_dim, int max_blocks, int max_selected) {
   StepWs w;
   w.rows = ls::flow_ctl_bytes(B * hkv);
-  w.ranges = w.rows + ls::flow_rows_bytes(B * hkv, max_blocks);
-  w.ents = w.ranges + ls::flow_ranges_bytes(B * hkv);
+  w.ents = w.rows + ls::flow_keys_bytes(B * hkv, max_blocks);
   w.parts = w.ents + ls::flow_ents_bytes(B * hkv, max_selected);
   w.total = w.parts + attn_parts_bytes(B, hq, head_dim, max_selected, max_blocks);
   return w;
@@ -225,18 +226,18 @@ Route route(const ls_pool& pool, const ls_batch& batch, int num_q_heads) {
 
 ls::FlowArgs flow_args(const ls::ScoreArgs& sa, const ls::TopkArgs& ta, const ls::AttnArgs& aa,
                        const ls::SummaryUpdate& up, int pairs, int max_blocks, int max_selected,
-                       char* w, size_t rows_off, size_t ranges_off, size_t parts_off,
-                       float* rows, size_t ents_off = 0) {
+                       char* w, size_t keys_off, size_t ents_off, size_t parts_off,
+                       float* scores_out) {
   ls::FlowArgs f;
   f.sa = sa;
   f.ta = ta;
   f.aa = aa;
   f.up = up;
   f.ctl = reinterpret_cast<uint32_t*>(w);
-  f.score_rows = rows ? rows : reinterpret_cast<float*>(w + rows_off);
-  f.ranges = reinterpret_cast<float*>(w + ranges_off);
-  f.parts = reinterpret_cast<float*>(w + parts_off);
-  f.ents = ents_off ? reinterpret_cast<int32_t*>(w + ents_off) : nullptr;
+  f.keys = reinterpret_cast<uint32_t*>(w + keys_off);
+  f.ents = reinterpret_cast<int32_t*>(w + ents_off);
+  f.parts = reinterpret_cast<uint32_t*>(w + parts_off);
+  f.scores_out = scores_out;
   f.pairs = pairs;
   f.max_blocks = max_blocks;
   const ls::FlowPlan pl = ls::flow_plan(pairs, max_blocks, max_selected);
@@ -328,8 +329,8 @@ ls_status run_step(const void* q, int32_t num_q_heads, void* summaries, const vo
   }
   if (rt == kRouteFlow) {
     const ls::FlowArgs f = flow_args(sa, ta, aa, up, batch.batch_size * pool.num_heads,
-                                     batch.max_blocks, p.max_selected, w, lay.rows, lay.ranges,
-                                     lay.parts, nullptr, lay.ents);
+                                     batch.max_blocks, p.max_selected, w, lay.rows, lay.ents,
+                                     lay.parts, nullptr);
     return hip_status(ls::launch_flow(f, ls::kFlowStep, stream), "decode-step kernel launch");
   }
   // longer requests: the split kernels of the two calls back to back
@@ -343,6 +344,8 @@ ls_status run_step(const void* q, int32_t num_q_heads, void* summaries, const vo
   e = ls::launch_score(sa, stream);
   if (e == hipSuccess) e = ls::launch_topk(ta, stream);
   if (e == hipSuccess) e = ls::launch_attn(aa, stream);
+  // leave the workspace zero
+  if (e == hipSuccess) e = ls::launch_zero(w + lay.rows, lay.total - lay.rows, stream);
   return hip_status(e, "decode-step kernel launches");
 }
 
@@ -379,12 +382,6 @@ hipError_t scratch_ptr(void** out) {
   return hipSuccess;
 }
 
-__global__ void zero_words_kernel(uint32_t* p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
 }  // namespace
 
 extern "C" {
@@ -392,11 +389,6 @@ extern "C" {
 const char* ls_last_error(void) { return g_err; }
 
 const char* ls_version(void) { return "libls 0.6.0 abi 6 gfx950"; }
-
-size_t ls_workspace_control_bytes(int32_t batch_size, int32_t num_kv_heads) {
-  if (batch_size <= 0 || num_kv_heads <= 0) return 0;
-  return ls::flow_ctl_bytes(batch_size * num_kv_heads);
-}
 
 int32_t ls_attn_num_splits(int32_t max_selected) {
   if (max_selected < 1) return 1;
@@ -517,19 +509,21 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
   if (rt == kRouteFlow) {
     const ls::FlowArgs f = flow_args(sa, ta, ls::AttnArgs{}, ls::SummaryUpdate{},
                                      batch.batch_size * pool.num_heads, batch.max_blocks,
-                                     p->max_selected, w, lay.rows, lay.ranges, 0, scores);
+                                     p->max_selected, w, lay.rows, 0, 0, scores_out);
     return hip_status(ls::launch_flow(f, ls::kFlowSelect, stream), "selection kernel launch");
   }
   hipError_t e = ls::launch_score(sa, stream);
   if (e != hipSuccess) return hip_status(e, "score kernel launch");
-  return hip_status(ls::launch_topk(ta, stream), "top-k kernel launch");
+  e = ls::launch_topk(ta, stream);
+  if (e == hipSuccess && !scores_out) e = ls::launch_zero(w + lay.rows, lay.total - lay.rows, stream);
+  return hip_status(e, "top-k kernel launch");
 }
 
 size_t ls_sparse_attn_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
                                             int32_t head_dim, int32_t max_selected,
                                             int32_t max_blocks) {
   if (batch_size <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return attn_ws(batch_size, num_q_heads, num_q_heads, head_dim, max_selected, max_blocks).total;
+  return attn_ws(batch_size, num_q_heads, head_dim, max_selected, max_blocks).total;
 }
 
 ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_heads,
@@ -560,7 +554,7 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(LS_ERR_INVALID, "q, k_pool and v_pool must be 16-byte aligned");
   const int cap = selected ? max_selected : batch.max_blocks;
-  const AttnWs lay = attn_ws(batch.batch_size, pool.num_heads, num_q_heads, pool.head_dim,
+  const AttnWs lay = attn_ws(batch.batch_size, num_q_heads, pool.head_dim,
                              selected ? max_selected : 0, batch.max_blocks);
   if (!workspace || workspace_bytes < lay.total)
     return fail(LS_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
@@ -583,9 +577,11 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                      max_selected, w, 0, 0, lay.parts, nullptr);
     return hip_status(ls::launch_flow(f, ls::kFlowAttend, stream), "attention kernel launch");
   }
-  if (!selected && pool.num_pages < (1 << 26))
-    return hip_status(ls::launch_attn_chunked(aa, stream), "attention kernel launch");
-  return hip_status(ls::launch_attn(aa, stream), "attention kernel launch");
+  hipError_t e = (!selected && pool.num_pages < (1 << 26)) ? ls::launch_attn_chunked(aa, stream)
+                                                            : ls::launch_attn(aa, stream);
+  // leave the workspace zero
+  if (e == hipSuccess) e = ls::launch_zero(w + lay.parts, lay.total - lay.parts, stream);
+  return hip_status(e, "attention kernel launch");
 }
 
 size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_heads,
@@ -642,12 +638,10 @@ ls_status ls_sparse_decode_step_noalloc(const void* q, int32_t q_dtype, int32_t 
   void* w = nullptr;
   hipError_t e = scratch_ptr(&w);
   if (e != hipSuccess) return hip_status(e, "scratch address lookup");
-  // the control words must start at zero; the array keeps the last call's
-  // contents, so clear them here (a fill kernel: capturable in a graph)
-  const size_t nz = lay.rows / sizeof(uint32_t);
-  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<uint32_t*>(w), nz);
-  e = hipGetLastError();
+  // the step expects a zero workspace; the array keeps the last call's
+  // contents (zero after every call that completed), so clear what this
+  // call uses first (a fill kernel: capturable in a graph)
+  e = ls::launch_zero(w, lay.total, stream);
   if (e != hipSuccess) return hip_status(e, "scratch clear launch");
   return run_step(q, num_q_heads, summaries, k_pool, v_pool, pool, batch, *p, selected,
                   selected_count, sm_scale, out, out_dtype, lse_out, new_page_ids, n_new_pages,

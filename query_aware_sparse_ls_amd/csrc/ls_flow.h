@@ -13,9 +13,9 @@ constexpr int kFlowMaxChunks = 64;          // score chunks per pair
 constexpr int kFlowMaxChunkBlocks = 256;    // blocks per score chunk (16 tiles)
 constexpr int kFlowMaxSplit = 64;           // selection positions per attention split
 constexpr int kFlowMaxBlocks = 8192;        // blocks per request
-constexpr int kFlowSpinLimit = 1 << 20;     // polls of a ready flag before giving up
+constexpr int kFlowSpinLimit = 1 << 20;     // polls of a hand-off before giving up
 
-// Default chunk and split sizes (measured on MI355X at the 8B/32K/B16 shape).
+// Default chunk and split sizes (measured on MI355X).
 #ifndef LS_FLOW_CHUNK_TILES
 #define LS_FLOW_CHUNK_TILES 8               // 128 candidate blocks per score item
 #endif
@@ -23,29 +23,27 @@ constexpr int kFlowSpinLimit = 1 << 20;     // polls of a ready flag before givi
 #define LS_FLOW_SPLIT 16                    // selection positions per attention item (at most)
 #endif
 
-// Control words: per pair [score arrivals, split arrivals, ready flag, unused],
-// then one error word (set when a wait gives up). Zero between calls.
-constexpr int kFlowCtlPerPair = 4;
-enum { kCtlScoreArrivals = 0, kCtlSplitArrivals = 1, kCtlReady = 2, kCtlError = 0 };
+// Control words: ctl[kCtlError] is set when a hand-off wait gives up; then,
+// from word kFlowCtlWords on, two arrival counters per pair (score chunks,
+// attention splits).
+constexpr int kFlowCtlWords = 64;
+enum { kCtlError = 0 };
 
 enum { kFlowStep = 0, kFlowSelect = 1, kFlowAttend = 2 };
 
-// In the step, the ranking workgroup of a pair also writes the walk entries
-// (page * 32 + valid tokens) of its selection, from a copy of the pair's
-// page-table row loaded together with the scores, when that row fits its LDS.
-template <int MAXC>
-constexpr bool kFlowEntries = MAXC <= 2048;
-
+// Every word handed over is reset to zero by its reader, so that the
+// regions are zero between calls; walk entries are also polled (zero = not
+// written yet).
 struct FlowArgs {
   ScoreArgs sa;
   TopkArgs ta;
   AttnArgs aa;
   SummaryUpdate up;
-  float* score_rows;   // [pairs][max_blocks] fp32
-  float* ranges;       // [pairs][kFlowMaxChunks][2] fp32 (min, max)
-  float* parts;        // [batch][Hq][splits][D + 2] fp32
-  int32_t* ents;       // step, kFlowEntries: [pairs][max_selected] walk entries
-  uint32_t* ctl;       // [pairs][kFlowCtlPerPair] + error word
+  uint32_t* keys;       // [pairs][max_blocks] score keys (score_key)
+  int32_t* ents;        // step: [pairs][max_selected] walk entries (-1: none)
+  uint32_t* parts;      // [batch][Hq][splits][D + 2] split states (fp32 bits)
+  uint32_t* ctl;        // kFlowCtlWords words, then [pairs][2] arrival counters
+  float* scores_out;    // optional: the decoded block scores [pairs][max_blocks]
   int32_t pairs;
   int32_t max_blocks;
   int32_t chunks, chunk_tiles;   // score items per pair, 16-block tiles per item
@@ -78,21 +76,17 @@ inline FlowPlan flow_plan(int pairs, int max_blocks, int max_selected) {
 
 inline size_t flow_align(size_t x) { return (x + 255) / 256 * 256; }
 
-// Bytes of control words at the start of a workspace serving `pairs` pairs.
 inline size_t flow_ctl_bytes(int pairs) {
-  return flow_align(((size_t)pairs * kFlowCtlPerPair + 64) * sizeof(uint32_t));
+  return flow_align(((size_t)kFlowCtlWords + 2 * (size_t)pairs) * sizeof(uint32_t));
 }
-inline size_t flow_rows_bytes(int pairs, int max_blocks) {
-  return flow_align((size_t)pairs * max_blocks * sizeof(float));
-}
-inline size_t flow_ranges_bytes(int pairs) {
-  return flow_align((size_t)pairs * kFlowMaxChunks * 2 * sizeof(float));
+inline size_t flow_keys_bytes(int pairs, int max_blocks) {
+  return flow_align((size_t)pairs * max_blocks * sizeof(uint32_t));
 }
 inline size_t flow_ents_bytes(int pairs, int max_selected) {
   return flow_align((size_t)pairs * max_selected * sizeof(int32_t));
 }
 inline size_t flow_parts_bytes(int pairs, int head_dim, int splits) {
-  return flow_align((size_t)pairs * 4 * splits * (head_dim + 2) * sizeof(float));
+  return flow_align((size_t)pairs * 4 * splits * (head_dim + 2) * sizeof(uint32_t));
 }
 
 // Shapes the flow kernel serves: GQA groups of 4, page = block = 16 tokens,
@@ -104,5 +98,8 @@ inline bool flow_ok(int group, int head_dim, int max_blocks, int num_pages) {
 }
 
 hipError_t launch_flow(const FlowArgs& f, int mode, hipStream_t st);
+// Zero n bytes (a multiple of 4) at p: the split and dense paths leave the
+// workspace as they found it, zero.
+hipError_t launch_zero(void* p, size_t n, hipStream_t st);
 
 }  // namespace ls

@@ -44,7 +44,11 @@ def _same(a, b):
     reduced(LLAMA8B_32K_B16, batch=3, context=4096 + 5),
     reduced(LLAMA8B_32K_B16, batch=11, context=1000),
     reduced(RAGGED_B64, batch=9, ragged_range=(40, 5000), topk=8, keep_ratio=None),
-], ids=["tiny", "8b_b3", "8b_b11", "ragged_b9"])
+    # 40 pairs: many workgroups per pair, the pair's last score chunk has candidates
+    reduced(LLAMA8B_32K_B16, batch=5, context=2500),
+    # 24 pairs of up to 5000 blocks: the 8192-block ranking
+    reduced(RAGGED_B64, batch=3, ragged_range=(20000, 80000), topk=40, keep_ratio=None),
+], ids=["tiny", "8b_b3", "8b_b11", "ragged_b9", "8b_b5_2500", "ragged_b3_long"])
 def test_fused_equals_separate_and_oracle(cfg):
     say(f"fused step vs separate calls and oracle: {cfg.name}")
     inp = make_block_topk_inputs(cfg, device="cuda", seed=31)
@@ -70,19 +74,19 @@ def test_fused_workspace_reuse_across_calls():
         sep = run_gpu_step(inp)
         fus = run_gpu_fused(inp, summaries=sep.summaries, workspace=ws)
         _same(sep, fus)
-        # every arrival counter, ready flag and the error word are back at zero
-        ctl = ls.workspace_control_bytes(inp.q.shape[0], cfg.num_kv_heads)
+        # every hand-off word and the error word are back at zero
         torch.cuda.synchronize()
-        assert ctl > 0 and int(torch.count_nonzero(ws[:ctl])) == 0
+        assert int(torch.count_nonzero(ws)) == 0
 
 
-def test_control_words_left_zero_by_every_call():
-    """Selection, attention and step calls each leave the control words of
-    their workspace at zero (counters reset by their last arrival, no wait
-    gave up), also when one workspace serves all three in turn."""
+@pytest.mark.parametrize("batch", [5, 16])   # 40 pairs: many workgroups per pair; 128: one
+def test_workspace_left_zero_by_every_call(batch):
+    """Selection, attention and step calls each leave their workspace zero
+    (hand-off words reset by their readers, no wait gave up), also when one
+    workspace serves all three in turn."""
     import query_aware_sparse_ls_amd as ls
     from parity_util import paged_batch
-    cfg = reduced(LLAMA8B_32K_B16, batch=5, context=2500)
+    cfg = reduced(LLAMA8B_32K_B16, batch=batch, context=2500)
     inp = make_block_topk_inputs(cfg, device="cuda", seed=9)
     B, Hq, D = inp.q.shape
     Hkv = cfg.num_kv_heads
@@ -93,25 +97,24 @@ def test_control_words_left_zero_by_every_call():
             ls.sparse_decode_step_workspace(B, Hq, Hkv, D, batch.max_blocks, maxsel,
                                             "cuda").numel())
     ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
-    ctl = ls.workspace_control_bytes(B, Hkv)
     ref = run_gpu_step(inp)
     for it in range(3):
         sel, cnt = ls.score_select(inp.q, ref.summaries, cfg.page_size, batch, topk=inp.topk,
                                    n_sink=cfg.n_sink, n_recent=cfg.n_recent,
                                    max_selected=maxsel, workspace=ws)
         torch.cuda.synchronize()
-        assert int(torch.count_nonzero(ws[:ctl])) == 0, f"select {it}"
+        assert int(torch.count_nonzero(ws)) == 0, f"select {it}"
         assert torch.equal(cnt, ref.counts)
         out, _ = ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, batch, sel, cnt,
                                        sm_scale=1.0 / math.sqrt(D), workspace=ws)
         torch.cuda.synchronize()
-        assert int(torch.count_nonzero(ws[:ctl])) == 0, f"attention {it}"
+        assert int(torch.count_nonzero(ws)) == 0, f"attention {it}"
         out2, _, _, cnt2 = ls.sparse_decode_step(inp.q, ref.summaries, inp.k_pool, inp.v_pool,
                                                  batch, topk=inp.topk, n_sink=cfg.n_sink,
                                                  n_recent=cfg.n_recent, max_selected=maxsel,
                                                  sm_scale=1.0 / math.sqrt(D), workspace=ws)
         torch.cuda.synchronize()
-        assert int(torch.count_nonzero(ws[:ctl])) == 0, f"step {it}"
+        assert int(torch.count_nonzero(ws)) == 0, f"step {it}"
         assert torch.equal(out, out2) and torch.equal(cnt2, ref.counts)
 
 
