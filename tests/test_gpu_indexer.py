@@ -383,3 +383,45 @@ def test_indexer_fp8_codes_exact():
     want = oracle.numerics.fp8e4m3fn_to_f64(codes)
     got = sc[0, :256].cpu().numpy().astype(np.float64)
     assert np.array_equal(got, want), np.nonzero(got != want)[0][:10]
+
+
+def test_indexer_block_mode_950k_coarse_shape():
+    """The coarse pass of the 950K coarse-to-fine workload at full shape: 4
+    requests x 15,200 blocks of 64 tokens, block-mean keys (bf16), 64 heads,
+    top-256 blocks + the last block (the 1024-thread workgroup top-k).
+    Every candidate's score against the oracle's float64 Eq. 6 over the
+    block means; the selection exact outside the near-tie band."""
+    say("indexer blocks at 4 x 15,200 blocks")
+    dev = _dev()
+    B, H, P, nb, kb = 4, 64, 64, 15200, 256
+    g = torch.Generator().manual_seed(77)
+    npg = B * nb
+    summ = torch.randn(npg, 128, generator=g).to(torch.bfloat16).to(dev)
+    q = torch.randn(B, H, 128, generator=g).to(torch.bfloat16).to(dev)
+    w = (torch.randn(B, H, generator=g) / 8).to(dev)
+    perm = torch.randperm(npg, generator=g).to(torch.int32).to(dev)
+    lens = [nb * P - 40, nb * P, nb * P - 1, nb * P - 63]   # partial and complete last blocks
+    b = ls.PagedBatch(torch.arange(0, npg + 1, nb, dtype=torch.int32, device=dev), perm,
+                      torch.tensor(lens, dtype=torch.int32, device=dev), nb)
+    sc = torch.full((B, nb), float("nan"), device=dev)
+    sel, cnt = ls.indexer_select(q, w, summ, P, b, granularity="blocks", topk=kb, n_recent=1,
+                                 max_selected=kb + 2, scores_out=sc)
+    torch.cuda.synchronize()
+    qb, wb, sb = bf16_bits(q), w.cpu().numpy(), bf16_bits(summ)
+    bv = BatchView(np.arange(0, npg + 1, nb), perm.cpu().numpy(), np.array(lens), P)
+    for r in range(B):
+        s = oracle.indexer_block_scores(qb, wb, sb, bv, r)
+        ncomp = bv.num_complete(r)
+        nbr = bv.num_blocks(r)
+        forced = set(oracle.method.forced_blocks(nbr, ncomp, 0, 1))
+        cands = [j for j in range(ncomp) if j not in forced]
+        got = sc[r, cands].double().cpu().numpy()
+        mag = np.abs(np.maximum(oracle.bf16_to_f64(sb[bv.pages(r)[cands]]) @
+                                oracle.bf16_to_f64(qb[r]).T, 0.0)) @ np.abs(wb[r].astype(np.float64))
+        assert np.all(np.abs(got - s[cands]) <= 1e-5 * mag + 1e-6), f"scores r{r}"
+        gsel = [int(x) for x in sel[r, :cnt[r]].cpu()]
+        assert len(gsel) == kb + len(forced) and forced <= set(gsel)
+        full = np.full(nbr, -np.inf)
+        full[:ncomp] = s
+        band = _check_topk(sorted(set(gsel) - forced), full, cands, kb, f"blocks r{r}")
+        say(f"  r{r}: {len(gsel)} blocks, band {band}")

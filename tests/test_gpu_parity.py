@@ -206,3 +206,30 @@ def test_llama8b_32k_b16_full_size_sampled():
     # still rank below the 64th score)
     assert hot_hit >= 0.95 * hot_all, (hot_hit, hot_all)
     say(f"near-tie band blocks: {bands}; hot blocks selected {hot_hit}/{hot_all}")
+
+
+def test_ragged_many_pairs_long_requests_keep_ratio():
+    """The batch-64 ragged sweep's shape class: 264 (request, kv head) pairs,
+    lengths log-uniform in [2K, 128K] (requests of up to 8192 blocks), keep
+    ratio 1/16 -- the many-workgroups route with 8192-block ranking rows.
+    Sampled pairs (the shortest, the longest, and two in between) against the
+    oracle; the fused step equals the separate calls bit for bit."""
+    from parity_util import run_gpu_fused
+    cfg = reduced(RAGGED_B64, batch=33)
+    say(f"ragged {cfg.batch} requests, 2K-128K, keep 1/16")
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=24)   # longest: 112,317 tokens
+    lens = inp.seq_lens.tolist()
+    assert max(lens) > 16 * 4096, "a request of more than 4096 blocks"
+    res = run_gpu_step(inp, topk=-1, keep_ratio=cfg.keep_ratio)
+    fus = run_gpu_fused(inp, summaries=res.summaries, topk=-1, keep_ratio=cfg.keep_ratio)
+    assert torch.equal(res.counts, fus.counts)
+    assert torch.equal(res.out, fus.out) and torch.equal(res.lse, fus.lse)
+    P = cfg.page_size
+    order = np.argsort(lens)
+    for r in (int(order[0]), int(order[-1]), int(order[len(lens) // 2]), int(order[-2])):
+        L = lens[r]
+        k = topk_from_keep_ratio(-(-L // P), L // P, cfg.keep_ratio, cfg.n_sink, cfg.n_recent)
+        for g in (0, 7):
+            say(f"  r{r} (L={L}) g{g}")
+            check_pair(inp, res, r, g, **{kk: v for kk, v in _kw(inp, res, topk=k).items()
+                                           if kk != "res"})

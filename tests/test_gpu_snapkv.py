@@ -35,7 +35,12 @@ def _pooled(s, L, W):
     return np.array([pre[i:i + 7].sum() for i in range(npre)]) / 7
 
 
-@pytest.mark.parametrize("lens,W,budget", [([3000, 700, 65, 64], 64, 900), ([2000, 1500], 16, 300)])
+@pytest.mark.parametrize("lens,W,budget", [
+    ([3000, 700, 65, 64], 64, 900),
+    ([2000, 1500], 16, 300),
+    # the benchmark's shape per request: 32K positions, 30% budget (9,830)
+    ([32768, 32768], 64, 9830),
+], ids=["mixed", "w16", "32k_budget9830"])
 def test_snapkv_select_gather_and_decode(lens, W, budget):
     import query_aware_sparse_ls_amd as ls
     cfg = reduced(LLAMA8B_32K_B16, batch=len(lens), context=max(lens))
