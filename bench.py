@@ -15,14 +15,37 @@ Workload: Llama-3-8B-shaped decode attention, 16 requests x 32K tokens,
 permutation page table, bf16 K/V ~ N(0,1) with 2% hot blocks, top-64 blocks
 + 1 sink + 2 recent per KV head, bf16 output.
 
-Timing: R input replicas (each its own pools, summaries, page table and
-query), R x step bytes >> the 256 MB Infinity Cache, so consecutive steps
-cannot be served from it. One HIP graph holds one step per replica; it is
-replayed, and the timed region (hipEvents on the launch stream, bracketed by
-device synchronisations) covers exactly `steps` steps. A second, eager pass
-times each library call alone: 8R launches of it back to back between two
-hipEvents (behind a GPU-side sleep so the host enqueues ahead of the device);
-that mean launch duration prices the roofline line.
+Timing (ByteCross App. A and App. E adapted):
+  * R input replicas (each its own pools, summaries, page table and query),
+    R x step bytes >> the 256 MB Infinity Cache, so consecutive steps
+    cannot be served from it.
+  * The JSON line's value: exactly --steps steps cycling over the replicas
+    in one HIP graph, after --warmup eager steps and one untimed launch of
+    the graph; one HIP-event pair on the launch stream, device-synchronised
+    on both sides.
+  * Repeat blocks: --blocks fresh processes (this script again), started
+    one after the other before this process makes its first GPU call. Each
+    builds its own replicas and times every cell of the session -- the step,
+    a plain streaming read of the step's byte count (ls_stream_read), and
+    k = all attention -- in an order rotated by the block index: 10 untimed
+    then 20 timed launches of a graph of the cell's steps, median per step.
+    Reported: the median over the blocks and their range; % of the stream
+    read's bandwidth and the cost beyond byte time at the dense rate
+    (c_b = t_b - t_D * B_b / B_D, ByteCross §4.3 and App. D), each paired
+    within a block.
+  * Per-call durations (roofline): back-to-back eager launches of one call
+    between two HIP events, behind a GPU-side sleep. Also one call alone
+    (latency), and the same graph on one replica (warm, labelled so).
+  * Oracle baseline: the oracle as it stands, in one process per host core
+    (os.sched_getaffinity, at most 16; one BLAS thread each; spawned before
+    the first GPU call), parallel over (request, kv head) units of one
+    replica, for about --cpu-seconds CPU seconds; the CPU model and the
+    process count are recorded.
+
+--path ragged: the batch-64 sweep (lengths log-uniform in [2K, 128K], a
+shared pool at 70% occupancy): the fused step at keep 1/64, 1/16 and 1/4,
+each one cell, k = all, and the stream read; --keep names the cell the
+value is for. Bytes per step come from the selections the steps make.
 
 Prints ONE JSON line.
 """
@@ -182,60 +205,225 @@ def per_call_ms(reps, cfg, sm_scale, fused, n):
     return [ev[a].elapsed_time(ev[a + 1]) / n for a in range(3)]
 
 
-def cpu_baseline(rep, cfg, sm_scale, budget_s: float):
-    """Time the oracle (unchanged, one thread) on whole requests of replica 0:
-    summary update of the request's new page, scores, selection and attention
-    for all its kv heads. Requests are taken in turn (wrapping around) until
-    `budget_s` seconds of oracle time are spent; the mean time per request,
-    times the batch size, is the time of one call."""
+# ------------------------------------------------------- oracle baseline ----
+#
+# The oracle, as it stands, on the host's cores: one process per core (one
+# BLAS thread each), parallel over (request, kv head) units. The processes are
+# spawned before this process touches the GPU; later they read a sample of
+# one replica's inputs from memory-mapped files, prepare their units (the
+# summaries of the complete pages: setup, not timed), meet at a barrier, and
+# run passes over their units until their share of the time budget is spent.
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_units(job, barrier):
+    """Prepare the job's units, wait for the others, then time passes over
+    them. A unit (r, g) is kv head g of sampled request r alone: its G query
+    heads, its K/V pages and its summaries (GQA groups do not interact)."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
     import oracle
-    from workloads import bf16_bits
-    inp = rep["inp"]
-    P, Hkv = cfg.page_size, cfg.num_kv_heads
-    bounds = rep["mode"] == "bounds"
+    d, m = job["dir"], job["meta"]
+    kmm = np.load(os.path.join(d, "k.npy"), mmap_mode="r")     # [pages][Hkv][P][D] bf16 bits
+    vmm = np.load(os.path.join(d, "v.npy"), mmap_mode="r")
+    q = np.load(os.path.join(d, "q.npy"))                       # [requests][Hq][D] bf16 bits
+    off, lens, P, G = m["page_offsets"], m["seq_lens"], m["page_size"], m["group"]
+    bounds = m["score_mode"] == "bounds"
     build = oracle.block_bounds if bounds else oracle.block_summaries
-    prepared = {}
-
-    def prepare(r):
-        L = int(inp.seq_lens[r])
-        nb = -(-L // P)
-        p0 = int(inp.page_indptr[r])
-        pages = inp.page_indices[p0:p0 + nb].long()
-        k = bf16_bits(inp.k_pool[pages].contiguous())
-        v = bf16_bits(inp.v_pool[pages].contiguous())
-        q = bf16_bits(inp.q[r:r + 1].contiguous())
+    units = []
+    for r, g in job["units"]:
+        L = int(lens[r])
+        nb, nc = -(-L // P), L // P
+        k = kmm[off[r]:off[r] + nb, g:g + 1]
+        v = vmm[off[r]:off[r] + nb, g:g + 1]
+        qu = np.ascontiguousarray(q[r:r + 1, g * G:(g + 1) * G])
         bv = oracle.BatchView(np.array([0, nb]), np.arange(nb), np.array([L]), P)
-        nc = L // P
-        summ = np.zeros((nb, Hkv) + ((2,) if bounds else ()) + (cfg.head_dim,), dtype=np.uint16)
-        summ[:nc] = build(k, np.arange(nc))                        # setup: not timed
-        return L, nc, k, v, q, bv, summ
+        summ = np.zeros((nb, 1) + ((2,) if bounds else ()) + (k.shape[-1],), dtype=np.uint16)
+        if nc:
+            summ[:nc] = build(k, np.arange(nc))
+        topk = m["topk"]
+        if topk < 0:
+            topk = oracle.topk_from_keep_ratio(nb, nc, m["keep_ratio"], m["n_sink"], m["n_recent"])
+        units.append((L, nc, k, v, qu, bv, summ, topk))
+    barrier.wait()
+    t0 = time.perf_counter()
+    passes, el = 0, 0.0
+    while units:
+        for L, nc, k, v, qu, bv, summ, topk in units:
+            if L % P == 0 and nc:               # the page that filled at this step
+                summ[[nc - 1]] = build(k, [nc - 1])
+            oracle.decode_step(qu, k, v, bv, num_kv_heads=1, topk=topk, n_sink=m["n_sink"],
+                               n_recent=m["n_recent"], sm_scale=np.float32(m["sm_scale"]),
+                               agg=m["agg"], out_dtype=m["out_dtype"], summaries=summ,
+                               score_mode=m["score_mode"])
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= job["budget_s"]:
+            break
+    return {"passes": passes, "seconds": el, "units": len(units)}
 
-    times = []
+
+_ONE_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+
+
+def _oracle_worker(w, jobs, results, barrier):
+    # one thread per process (also set in the environment the process was
+    # started with); limit whatever pools NumPy and the oracle loaded
+    for var in _ONE_THREAD_VARS:
+        os.environ[var] = "1"
+    import numpy  # noqa: F401
+    import oracle  # noqa: F401
+    from threadpoolctl import threadpool_limits
     with threadpool_limits(1):
-        while sum(times) < budget_s:
-            r = len(times) % cfg.batch
-            if r not in prepared:
-                prepared[r] = prepare(r)
-            L, nc, k, v, q, bv, summ = prepared[r]
-            t0 = time.perf_counter()
-            new = [nc - 1] if L % P == 0 and nc > 0 else []
-            if new:
-                summ[new] = build(k, new)
-            oracle.decode_step(q, k, v, bv, num_kv_heads=Hkv, topk=inp.topk, n_sink=cfg.n_sink,
-                               n_recent=cfg.n_recent, sm_scale=np.float32(sm_scale),
-                               agg=cfg.group_agg, out_dtype="bf16", summaries=summ,
-                               score_mode=rep["mode"])
-            times.append(time.perf_counter() - t0)
-    per_call = sum(times) / len(times) * cfg.batch
-    return {"value": 1.0 / per_call, "unit": "calls/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} request-steps ({len(times) / cfg.batch:.1f} calls' worth; "
-                      f"each: new-page {'bounds' if bounds else 'summary'}, "
-                      f"{'Quest bound ' if bounds else ''}scores, top-k selection and attention for all "
-                      f"{Hkv} kv heads of one request), float64 NumPy on one thread, "
-                      f"{sum(times):.1f} s; mean per request x {cfg.batch} requests = one call",
-            "seconds_per_call": per_call}
+        while True:
+            job = jobs.get()
+            if job is None:
+                return
+            try:
+                res = _oracle_units(job, barrier)
+            except BaseException as e:      # report it; never leave the others waiting
+                res = {"error": repr(e)}
+                barrier.abort()
+            res["worker"] = w
+            results.put(res)
+
+
+class OraclePool:
+    """Oracle worker processes (spawned: fresh interpreters that never touch
+    the GPU). Start it before the first GPU call of this process."""
+
+    def __init__(self, n: int):
+        import multiprocessing as mp
+        ctx = mp.get_context("spawn")
+        self.n = n
+        self.barrier = ctx.Barrier(n + 1)
+        self.jobs = [ctx.Queue() for _ in range(n)]
+        self.results = ctx.Queue()
+        self.procs = [ctx.Process(target=_oracle_worker,
+                                  args=(w, self.jobs[w], self.results, self.barrier), daemon=True)
+                      for w in range(n)]
+        # the children inherit this environment: one BLAS / OpenMP thread each
+        saved = {v: os.environ.get(v) for v in _ONE_THREAD_VARS}
+        os.environ.update({v: "1" for v in _ONE_THREAD_VARS})
+        try:
+            for p in self.procs:
+                p.start()
+        finally:
+            for v, x in saved.items():
+                if x is None:
+                    os.environ.pop(v, None)
+                else:
+                    os.environ[v] = x
+
+    def run(self, job_dir: str, meta: dict, units, cost, budget_s: float,
+            timeout_s: float = 600.0):
+        """Deal `units` to the workers, the costliest first, each to the
+        worker with the least cost so far (cost: e.g. the unit's tokens);
+        returns the workers' {passes, seconds, units} records and the wall
+        time from the barrier."""
+        per, load = [[] for _ in range(self.n)], [0.0] * self.n
+        for u, c in sorted(zip(units, cost), key=lambda uc: -uc[1]):
+            w = load.index(min(load))
+            per[w].append(u)
+            load[w] += c
+        for w in range(self.n):
+            self.jobs[w].put({"dir": job_dir, "meta": meta, "units": per[w],
+                              "budget_s": budget_s})
+        self.barrier.wait(timeout=timeout_s)
+        t0 = time.perf_counter()
+        recs = [self.results.get(timeout=timeout_s) for _ in range(self.n)]
+        wall = time.perf_counter() - t0
+        errs = [r["error"] for r in recs if "error" in r]
+        if errs:
+            raise RuntimeError(f"oracle worker failed: {errs[0]}")
+        return recs, wall
+
+    def close(self):
+        for q in self.jobs:
+            q.put(None)
+        for p in self.procs:
+            p.join(timeout=30)
+
+
+def oracle_workers() -> int:
+    """Worker processes for the oracle: the cores this process may run on
+    (sched_getaffinity), at most 16 (one GPU's share of a host's cores)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def write_oracle_sample(dirpath: str, inp, requests):
+    """The listed requests' pages (logical order) of one replica as .npy
+    files: k, v [pages][Hkv][P][D] and q [requests][Hq][D], bf16 bits."""
+    import numpy as np
+    import torch
+    P = inp.cfg.page_size
+    indptr = inp.page_indptr.cpu().tolist()
+    lens = inp.seq_lens.cpu().tolist()
+    ids, offs = [], [0]
+    for r in requests:
+        nb = -(-int(lens[r]) // P)
+        ids.append(inp.page_indices[indptr[r]:indptr[r] + nb].long())
+        offs.append(offs[-1] + nb)
+    ids = torch.cat(ids)
+    for name, pool in (("k", inp.k_pool), ("v", inp.v_pool)):
+        arr = np.lib.format.open_memmap(os.path.join(dirpath, name + ".npy"), mode="w+",
+                                        dtype=np.uint16, shape=(len(ids),) + tuple(pool.shape[1:]))
+        for s in range(0, len(ids), 4096):
+            part = pool[ids[s:s + 4096]].view(torch.int16).cpu().numpy().view(np.uint16)
+            arr[s:s + len(part)] = part
+        arr.flush()
+        del arr
+    q = inp.q[torch.tensor(list(requests), device=inp.q.device)]
+    np.save(os.path.join(dirpath, "q.npy"), q.view(torch.int16).cpu().numpy().view(np.uint16))
+    return offs[:-1], [int(lens[r]) for r in requests]
+
+
+def cpu_baseline(pool: OraclePool, inp, cfg, *, requests, topk, keep_ratio, score_mode,
+                 sm_scale, step_bytes_total, budget_s):
+    """Oracle calls/s on the host cores over a sample of one replica's
+    requests (every kv head of each): wall seconds per pass over the sample,
+    scaled by batch / sampled requests to one call. A single-core time per
+    call is the sum of the workers' per-pass times, scaled the same way."""
+    import tempfile
+    requests = list(requests)
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    with tempfile.TemporaryDirectory(prefix="ls_oracle_") as d:
+        offs, lens = write_oracle_sample(d, inp, requests)
+        meta = {"page_offsets": offs, "seq_lens": lens, "page_size": cfg.page_size, "group": G,
+                "topk": int(topk), "keep_ratio": float(keep_ratio), "n_sink": cfg.n_sink,
+                "n_recent": cfg.n_recent, "sm_scale": float(sm_scale), "agg": cfg.group_agg,
+                "out_dtype": "fp32" if cfg.out_dtype == "fp32" else "bf16",
+                "score_mode": score_mode}
+        units = [(i, g) for i in range(len(requests)) for g in range(cfg.num_kv_heads)]
+        recs, wall = pool.run(d, meta, units, [lens[i] for i, _ in units], budget_s / pool.n)
+    busy = [r for r in recs if r["units"]]
+    per_pass = [r["seconds"] / r["passes"] for r in busy]
+    scale = cfg.batch / len(requests)
+    par = max(per_pass) * scale
+    single = sum(per_pass) * scale
+    cpu_s = sum(r["seconds"] for r in busy)
+    return {"value": 1.0 / par, "unit": "calls/s", "cores": pool.n, "kind": "oracle",
+            "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "seconds_per_call": par, "single_core_seconds_per_call": single,
+            "effective_GBps": step_bytes_total / par / 1e9,
+            "sample": (f"{len(requests)} of {cfg.batch} requests of one replica x "
+                       f"{cfg.num_kv_heads} kv heads = {len(units)} (request, kv head) units "
+                       f"over {pool.n} processes (one BLAS thread each, units dealt by "
+                       f"length), "
+                       f"{min(r['passes'] for r in busy)}-{max(r['passes'] for r in busy)} passes "
+                       f"each, {cpu_s:.1f} CPU-s in {wall:.1f} s wall; per unit: the page that "
+                       f"filled, {'Quest bound' if score_mode == 'bounds' else 'block'} scores, "
+                       f"selection and attention, float64 NumPy; one call = the slowest "
+                       f"process's time per pass x {scale:g}")}
 
 
 def copy_calibration(nbytes: int) -> int:
@@ -409,7 +597,7 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
     B, P, k = cfg.batch, cfg.page_size, cfg.topk_tokens
     nb = cfg.context // P
     sm = 1.0 / math.sqrt(cfg.kv_lora_dim + cfg.rope_dim)
-    R = max(1, args.replicas)
+    R = max(1, args.replicas or 8)
     reps = []
     base = make_indexer_inputs(cfg, device=dev)
     summ = None
@@ -655,7 +843,7 @@ def bench_dense(args, window: bool = False) -> int:
     torch.cuda.set_device(dev)
     B, Hq, Hkv, D, P = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
     sm = 1.0 / math.sqrt(D)
-    R = max(1, min(args.replicas, 2))    # one step reads 2 GiB: no cache reuse either way
+    R = max(1, min(args.replicas or 2, 2))    # one step reads 2 GiB: no cache reuse either way
     N_SINK, WIN = 4, int(0.3 * cfg.context)   # the window: 4 sinks + 30% of the tokens
     reps = []
     for i in range(R):
@@ -741,7 +929,7 @@ def bench_snapkv(args) -> int:
     B, Hq, Hkv, D, L = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.context
     W, NS, BUD = 64, 4, int(0.3 * cfg.context)
     sm = 1.0 / math.sqrt(D)
-    R = max(1, min(args.replicas, 2))
+    R = max(1, min(args.replicas or 2, 2))
     reps, sel_ms = [], []
     for i in range(R):
         inp = make_block_topk_inputs(cfg, device=dev, seed=cfg.seed + i)
@@ -811,13 +999,557 @@ def bench_snapkv(args) -> int:
     return 0
 
 
+# -------------------------------------------------- the timing protocol ----
+#
+# A Cell is one measured operation of a session: fn(i) enqueues one step of
+# it on replica i on the current stream; nbytes is its algorithmic bytes per
+# step (mean over the replicas); steps is the number of steps one graph
+# launch holds when the cell is timed as a repeat block.
+
+class Cell:
+    def __init__(self, name, fn, nbytes, steps, kernel=""):
+        self.name, self.fn, self.nbytes, self.steps, self.kernel = name, fn, nbytes, steps, kernel
+
+
+def capture(fns):
+    """One HIP graph of fns in order (each enqueues work on the current
+    stream), captured after one eager pass of the same work."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def cell_graph(cell, R, n, replica=None):
+    """A graph of n steps of `cell`, cycling over the R replicas (or all on
+    one replica)."""
+    return capture([(lambda i=i: cell.fn(i % R if replica is None else replica))
+                    for i in range(n)])
+
+
+def launch_ms(g, launches, warm):
+    """Durations (ms) of `launches` replays of g, each between two HIP events
+    on the launch stream, after `warm` untimed replays."""
+    import torch
+    for _ in range(warm):
+        g.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def measure_cells(sess, order, launches, warm):
+    """Median, min and max ms per step of every cell, one cell after the
+    other in `order`: `launches` timed replays of a graph of cell.steps
+    steps, after `warm` untimed ones."""
+    import statistics
+    out = {}
+    for name in order:
+        c = sess["cells"][name]
+        print(f"#   {name}: graph of {c.steps} steps", file=sys.stderr, flush=True)
+        g = cell_graph(c, sess["R"], c.steps)
+        per = [m / c.steps for m in launch_ms(g, launches, warm)]
+        del g
+        out[name] = {"median_ms_per_step": statistics.median(per), "min_ms_per_step": min(per),
+                     "max_ms_per_step": max(per), "steps_per_launch": c.steps,
+                     "launches": launches, "bytes_per_step": c.nbytes}
+    return out
+
+
+def child_block(args) -> int:
+    """One repeat block in a fresh process: the session's cells in an order
+    rotated by the block index; one JSON line on stdout."""
+    import torch
+    b = args.child_block
+    torch.cuda.set_device(0)
+    sess = make_session(args, torch.device("cuda:0"), block=b)
+    names = list(sess["cells"])
+    order = names[b % len(names):] + names[:b % len(names)]
+    cells = measure_cells(sess, order, args.launches, args.warm_launches)
+    print(json.dumps({"block": b, "pid": os.getpid(), "order": order, "cells": cells}), flush=True)
+    return 0
+
+
+def run_blocks(args, argv):
+    """The repeat blocks: this script again with --child-block i, one fresh
+    process after the other, all before this process makes a GPU call."""
+    import subprocess
+    out = []
+    for b in range(args.blocks):
+        print(f"# repeat block {b + 1}/{args.blocks} (fresh process)", file=sys.stderr, flush=True)
+        p = subprocess.run([sys.executable, "-u", os.path.abspath(__file__)] + list(argv)
+                           + ["--child-block", str(b)], stdout=subprocess.PIPE, text=True,
+                           timeout=args.block_timeout)
+        if p.returncode != 0:
+            raise SystemExit(f"repeat block {b} ended with status {p.returncode}")
+        out.append(json.loads(p.stdout.strip().splitlines()[-1]))
+    return out
+
+
+def summarize_blocks(blocks, primary):
+    """Per cell: the median over the blocks of their medians, and the range;
+    per block, paired with the primary cell in the same process: % of the
+    stream-read bandwidth and the cost beyond byte time at the dense rate
+    (t_b - t_D * B_b / B_D, ByteCross §4.3 and App. D)."""
+    import statistics
+    names = list(blocks[0]["cells"])
+    cells = {}
+    for n in names:
+        meds = [b["cells"][n]["median_ms_per_step"] for b in blocks]
+        nbytes = blocks[0]["cells"][n]["bytes_per_step"]
+        m = statistics.median(meds)
+        cells[n] = {"median_ms_per_step": round(m, 6),
+                    "range_ms_per_step": [round(min(meds), 6), round(max(meds), 6)],
+                    "per_block_ms_per_step": [round(x, 6) for x in meds],
+                    "bytes_per_step": nbytes, "GBps_at_median": round(nbytes / (m * 1e-3) / 1e9, 1),
+                    "pct_of_hbm_peak_at_median": round(100 * nbytes / (m * 1e-3) / 1e9
+                                                       / HBM_PEAK_GBPS, 2)}
+    res = {"blocks": len(blocks), "orders": [b["order"] for b in blocks],
+           "launches_per_block": blocks[0]["cells"][primary]["launches"], "cells": cells}
+
+    def gbps(b, n):
+        c = b["cells"][n]
+        return c["bytes_per_step"] / (c["median_ms_per_step"] * 1e-3) / 1e9
+
+    if "stream_read" in names:
+        ratios = {n: [100 * gbps(b, n) / gbps(b, "stream_read") for b in blocks]
+                  for n in names if n != "stream_read"}
+        res["pct_of_stream_read"] = {n: {"median": round(statistics.median(v), 2),
+                                         "range": [round(min(v), 2), round(max(v), 2)]}
+                                     for n, v in ratios.items()}
+    if "dense" in names:
+        beyond = {}
+        for n in names:
+            if n in ("dense", "stream_read"):
+                continue
+            cb = []
+            for b in blocks:
+                tb, td = b["cells"][n]["median_ms_per_step"], b["cells"]["dense"]["median_ms_per_step"]
+                cb.append((tb - td * b["cells"][n]["bytes_per_step"]
+                           / b["cells"]["dense"]["bytes_per_step"]) * 1e3)
+            beyond[n] = {"c_b_us_median": round(statistics.median(cb), 3),
+                         "c_b_us_range": [round(min(cb), 3), round(max(cb), 3)]}
+        res["beyond_byte_time"] = beyond
+    return res
+
+
+def eager_mean_ms(fn, R, n):
+    """Mean duration of n eager launches of fn (cycling over the replicas)
+    between two HIP events, queued behind a GPU-side sleep so that the
+    launches run back to back."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    a.record()
+    for i in range(n):
+        fn(i % R)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def single_call_us(fn, R, n=21):
+    """Median latency of one call alone (synchronised before and after)."""
+    import statistics
+    import torch
+    ts = []
+    for j in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        fn(j % R)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    return statistics.median(ts)
+
+
+def contract_timing(sess, args):
+    """Exactly args.steps steps of the primary cell, cycling over the
+    replicas, after args.warmup eager steps and one untimed launch of the
+    same graph; one HIP-event pair on the launch stream, synchronised on
+    both sides. Returns (ms per step, wall seconds, timing label)."""
+    import torch
+    c, R, K = sess["cells"][sess["primary"]], sess["R"], args.steps
+    for i in range(max(1, args.warmup)):
+        c.fn(i % R)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.no_graph:
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        a.record()
+        for i in range(K):
+            c.fn(i % R)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K, time.perf_counter() - w0, "eager"
+    g = cell_graph(c, R, K)
+    g.replay()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return a.elapsed_time(b) / K, wall, "hip graph"
+
+
+# ------------------------------------------------------------- sessions ----
+
+def stream_cell(reps, nbytes, steps):
+    """The stream-read reference over nbytes of each replica's K pool."""
+    import torch
+    import query_aware_sparse_ls_amd as ls
+    n16 = int(nbytes) // 16 * 16
+    srcs = [r["inp"].k_pool.view(-1).view(torch.uint8)[:n16] for r in reps]
+    sink = torch.empty(int(ls._lib.EXPORTS["ls_stream_read_sink_words"]()), dtype=torch.int32,
+                       device=reps[0]["inp"].q.device)
+    return Cell("stream_read", lambda i: ls.stream_read(srcs[i], sink), n16, steps,
+                "ls::stream_read_kernel")
+
+
+def dense_cell(reps, sm_scale, nbytes, steps):
+    """k = all: split-K attention over every cached token (no selection)."""
+    import torch
+    import query_aware_sparse_ls_amd as ls
+    inp0 = reps[0]["inp"]
+    B, Hq, D = inp0.q.shape
+    ws = [torch.zeros(ls.sparse_attn_decode_workspace_size(B, Hq, D, 0, r["batch"].max_blocks),
+                      dtype=torch.uint8, device=inp0.q.device) for r in reps]
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=inp0.q.device)
+
+    def fn(i):
+        inp = reps[i]["inp"]
+        ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, reps[i]["batch"], None, None,
+                              sm_scale=sm_scale, out=out, workspace=ws[i])
+    return Cell("dense", fn, nbytes, steps, "ls::attn_chunk_kernel")
+
+
+def make_session(args, dev, block=None):
+    return ragged_session(args, dev, block) if args.path == "ragged" else \
+        block_topk_session(args, dev, block)
+
+
+def block_topk_session(args, dev, block=None):
+    """Llama-3-8B-shaped decode at 16 x 32K: the step (fused, or the
+    separate calls), the stream read of the step's byte count, and k = all."""
+    import torch
+    from workloads import LLAMA8B_32K_B16
+    cfg = LLAMA8B_32K_B16
+    sm = 1.0 / math.sqrt(cfg.head_dim)
+    fused = not args.separate
+    R = args.replicas or 8
+    reps = [make_replica(cfg, cfg.seed + i, dev, args.score) for i in range(R)]
+    torch.cuda.synchronize()
+    print(f"# {R} replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB"
+          + ("" if block is None else f" (block {block})"), file=sys.stderr, flush=True)
+    inp0 = reps[0]["inp"]
+    P, Hkv, D, Hq, B = cfg.page_size, cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads, cfg.batch
+    nb = cfg.context // P
+    n_forced = cfg.n_sink + cfg.n_recent
+    quest = args.score == "bounds"
+    nbytes = step_bytes(B, Hq, Hkv, D, P, nb, inp0.topk + n_forced, nb - n_forced,
+                        int(reps[0]["new_pages"].numel()), rows=2 if quest else 1)
+    side = torch.cuda.Stream()
+    dense_bytes = B * Hkv * cfg.context * D * 2 * 2 + 2 * B * Hq * D * 2 + B * nb * 4
+    cells = {"step": Cell("step", lambda i: run_step(reps[i], cfg, sm, fused, side),
+                          nbytes["total"], args.steps),
+             "stream_read": stream_cell(reps, nbytes["total"], args.steps),
+             "dense": dense_cell(reps, sm, dense_bytes, min(args.steps, 2 * R))}
+    return {"cfg": cfg, "reps": reps, "R": R, "cells": cells, "primary": "step",
+            "sm_scale": sm, "fused": fused, "quest": quest, "nbytes": nbytes, "side": side}
+
+
+KEEPS = {"1/64": 1.0 / 64, "1/16": 1.0 / 16, "1/4": 1.0 / 4}
+
+
+def ragged_pair_bytes(inp, sel, cnt, n_sink, n_recent):
+    """Algorithmic bytes of one keep-ratio step on a ragged batch, from the
+    selection the step made: the selected blocks' tokens (a partial last
+    block counts its cached tokens), the complete non-forced blocks'
+    summaries, q, output, the page table, and the pages that filled."""
+    import torch
+    cfg = inp.cfg
+    P, D, Hq, Hkv = cfg.page_size, cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
+    lens = inp.seq_lens.long()
+    pos = torch.arange(sel.shape[2], device=sel.device)
+    valid = pos[None, None, :] < cnt.long()[:, :, None]
+    tok = (lens[:, None, None] - sel.long() * P).clamp(0, P)
+    tokens = int((tok * valid).sum())
+    cand = 0
+    n_new = 0
+    for L in lens.cpu().tolist():
+        nb, nc = -(-L // P), L // P
+        forced = set(range(min(n_sink, nb))) | set(range(max(0, nb - n_recent), nb))
+        cand += nc - sum(1 for b in forced if b < nc)
+        n_new += 1 if (L % P == 0 and nc) else 0
+    nb_all = sum(-(-L // P) for L in lens.cpu().tolist())
+    return {"summaries": Hkv * cand * D * 2, "selected_kv": tokens * D * 2 * 2,
+            "q_out_pagetable": 2 * inp.q.shape[0] * Hq * D * 2 + nb_all * 4,
+            "summary_update": n_new * Hkv * (P * D * 2 + D * 2)}
+
+
+def ragged_session(args, dev, block=None):
+    """The batch-64 ragged sweep (lengths log-uniform in [2K, 128K], shared
+    page pool at 70% occupancy): the fused step at keep 1/64, 1/16 and 1/4,
+    k = all, and the stream read of the primary keep ratio's bytes."""
+    import torch
+    import query_aware_sparse_ls_amd as ls
+    from workloads import RAGGED_B64, make_block_topk_inputs
+    cfg = RAGGED_B64
+    P, Hkv, D, Hq, B = cfg.page_size, cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads, cfg.batch
+    sm = 1.0 / math.sqrt(D)
+    R = args.replicas or 3
+    reps = []
+    for i in range(R):
+        inp = make_block_topk_inputs(cfg, device=dev, seed=cfg.seed + i)
+        batch = ls.PagedBatch(inp.page_indptr, inp.page_indices, inp.seq_lens, inp.max_blocks())
+        lens = inp.seq_lens.cpu().tolist()
+        indptr = inp.page_indptr.cpu().tolist()
+        idx = inp.page_indices.cpu()
+        full = torch.cat([idx[indptr[r]:indptr[r] + lens[r] // P] for r in range(B)])
+        new = [int(idx[indptr[r] + lens[r] // P - 1]) for r in range(B)
+               if lens[r] % P == 0 and lens[r] >= P]
+        summ = torch.zeros(inp.num_pages, Hkv, D, dtype=torch.bfloat16, device=dev)
+        ls.build_block_summaries(inp.k_pool, full.to(torch.int32).to(dev), summ)
+        rep = dict(inp=inp, batch=batch, summ=summ,
+                   new_pages=torch.tensor(new, dtype=torch.int32, device=dev), keeps={})
+        mb = batch.max_blocks
+        for name, kr in KEEPS.items():
+            maxsel = min(mb, max(cfg.n_sink + cfg.n_recent + 1,
+                                 math.ceil(float(torch.tensor(kr, dtype=torch.float32)) * mb) + 1))
+            rep["keeps"][name] = dict(
+                ratio=kr, maxsel=maxsel,
+                ws=ls.sparse_decode_step_workspace(B, Hq, Hkv, D, mb, maxsel, dev),
+                sel=torch.empty(B, Hkv, maxsel, dtype=torch.int32, device=dev),
+                cnt=torch.empty(B, Hkv, dtype=torch.int32, device=dev),
+                out=torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev))
+        reps.append(rep)
+    torch.cuda.synchronize()
+    print(f"# {R} ragged replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB"
+          + ("" if block is None else f" (block {block})"), file=sys.stderr, flush=True)
+
+    def step(i, name):
+        rp = reps[i]
+        k = rp["keeps"][name]
+        inp = rp["inp"]
+        ls.sparse_decode_step(inp.q, rp["summ"], inp.k_pool, inp.v_pool, rp["batch"], topk=-1,
+                              keep_ratio=k["ratio"], n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                              max_selected=k["maxsel"], sm_scale=sm, group_agg=cfg.group_agg,
+                              selected=k["sel"], selected_count=k["cnt"], out=k["out"],
+                              new_pages=rp["new_pages"], workspace=k["ws"])
+
+    # bytes per step from the selections themselves (one untimed step each)
+    cells, breakdown = {}, {}
+    for name in KEEPS:
+        parts = []
+        for i in range(R):
+            step(i, name)
+            k = reps[i]["keeps"][name]
+            parts.append(ragged_pair_bytes(reps[i]["inp"], k["sel"], k["cnt"], cfg.n_sink,
+                                           cfg.n_recent))
+        mean = {key: sum(p[key] for p in parts) / R for key in parts[0]}
+        mean["total"] = sum(mean.values())
+        breakdown[name] = mean
+        cells["keep_" + name] = Cell("keep_" + name, lambda i, n=name: step(i, n), mean["total"],
+                                     args.steps)
+    dense_bytes = sum(float(r["inp"].seq_lens.long().sum()) * Hkv * D * 2 * 2
+                      + 2 * B * Hq * D * 2 + 4 * sum(-(-int(L) // P)
+                                                     for L in r["inp"].seq_lens.tolist())
+                      for r in reps) / R
+    cells["dense"] = dense_cell(reps, sm, dense_bytes, min(args.steps, 2 * R))
+    primary = "keep_" + args.keep
+    cells["stream_read"] = stream_cell(reps, cells[primary].nbytes, args.steps)
+    return {"cfg": cfg, "reps": reps, "R": R, "cells": cells, "primary": primary,
+            "sm_scale": sm, "breakdown": breakdown, "step": step}
+
+
+# ----------------------------------------------------------------- main ----
+
+METRIC = "sparse decode attention calls/sec + achieved HBM GB/s (% of peak) at 8B/32K/B16"
+
+
+def bench_block_topk(args, argv) -> int:
+    """The block top-k decode step (default path) or the ragged sweep."""
+    if args.child_block is not None:
+        return child_block(args)
+    pool = None
+    if not args.no_cpu_baseline:
+        pool = OraclePool(oracle_workers())        # spawned before any GPU call here
+    try:
+        blocks = run_blocks(args, argv) if args.blocks > 0 else []
+        return _bench_block_topk_parent(args, blocks, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def _bench_block_topk_parent(args, blocks, pool) -> int:
+    import statistics
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sess = make_session(args, dev)
+    cfg, R, cells = sess["cfg"], sess["R"], sess["cells"]
+    prim = cells[sess["primary"]]
+    ragged = args.path == "ragged"
+    print("# timing", file=sys.stderr, flush=True)
+    ms_step, wall, timing = contract_timing(sess, args)
+    steps = args.steps
+    if blocks:
+        rb = summarize_blocks(blocks, sess["primary"])
+    else:   # no fresh-process blocks asked for: one block in this process
+        print("# cells in this process", file=sys.stderr, flush=True)
+        rb = summarize_blocks([{"order": list(cells), "cells": measure_cells(
+            sess, list(cells), args.launches, args.warm_launches)}], sess["primary"])
+        rb["in_parent_process"] = True
+    lat_us = single_call_us(prim.fn, R)
+    warm_g = cell_graph(prim, R, steps, replica=0)
+    warm_ms = launch_ms(warm_g, 1, 1)[0] / steps
+    del warm_g
+
+    calls_per_s = 1e3 / ms_step
+    gbps = prim.nbytes / (ms_step * 1e-3) / 1e9
+    B = cfg.batch
+    if ragged:
+        dom_ms = eager_mean_ms(prim.fn, R, 4 * R)
+        dom_bytes = prim.nbytes
+        dom_key = f"step_flow_kernel.ragged_b64_keep{args.keep.replace('/', 'of')}"
+        dom_match = "flow_kernel<128, 8192"
+        call_ms = {"decode_step_with_summary_refresh": round(dom_ms, 5)}
+    else:
+        cfg8 = cfg
+        upd, first, second = per_call_ms(sess["reps"], cfg8, sess["sm_scale"], sess["fused"],
+                                         min(steps, 8 * R))
+        quest = sess["quest"]
+        n_sel = sess["reps"][0]["inp"].topk + cfg.n_sink + cfg.n_recent
+        nb = cfg.context // cfg.page_size
+        sel_bytes = B * cfg.num_kv_heads * n_sel * 4 + B * cfg.num_kv_heads * 4
+        if sess["fused"]:
+            dom_ms, dom_bytes = first, prim.nbytes + sel_bytes
+            dom_key = "step_item_kernel.llama8b_32k_b16" + ("_quest" if quest else "")
+            dom_match = f"ls::step_item_kernel<128, 2048, {'true' if quest else 'false'}>"
+            call_ms = {"decode_step_with_summary_refresh": round(first, 5)}
+        else:
+            nbd = sess["nbytes"]
+            dom_ms = second
+            dom_bytes = (nbd["selected_kv"] + B * cfg.num_q_heads * cfg.head_dim * 2 + sel_bytes
+                         + B * nb * 4)
+            dom_key = "attn_item_kernel.llama8b_32k_b16" + ("_quest" if quest else "")
+            dom_match = "ls::attn_item_kernel<128, 2048>"
+            call_ms = {"summary_update": round(upd, 5), "score_select": round(first, 5),
+                       "sparse_attn_decode": round(second, 5)}
+    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+    tr = stored_traffic(dom_key)
+    sr = rb["cells"]["stream_read"]
+    workload = (f"ragged_b64_2k_128k keep {args.keep}" if ragged
+                else cfg.name + (" quest bounds" if sess["quest"] else ""))
+    config = {"workload": workload, "batch": B, "q_heads": cfg.num_q_heads,
+              "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
+              "page_size": cfg.page_size, "n_sink": cfg.n_sink, "n_recent": cfg.n_recent,
+              "replicas": R, "timing": timing}
+    if ragged:
+        config.update({"context": "log-uniform [2048, 131072] per request, pool 70% occupied",
+                       "keep_ratio": args.keep, "path": "fused"})
+    else:
+        config.update({"context": cfg.context, "topk": sess["reps"][0]["inp"].topk,
+                       "path": "fused" if sess["fused"] else "separate",
+                       "block_scores": "quest bounds" if sess["quest"] else "block-mean keys"})
+    res = {
+        "metric": METRIC if not ragged else
+        "sparse decode attention calls/sec + achieved HBM GB/s (% of peak) at ragged B64 2K-128K",
+        "value": round(calls_per_s, 1), "unit": "calls/s", "n_gpus": 1,
+        "steps": steps, "steps_requested": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
+        "step_bytes": round(prim.nbytes),
+        "step_bytes_breakdown": sess["breakdown"][args.keep] if ragged else sess["nbytes"],
+        "achieved_GBps_step": round(gbps, 1),
+        "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "pct_of_stream_read_step": rb.get("pct_of_stream_read", {}).get(sess["primary"]),
+        "stream_read": {"bytes": sr["bytes_per_step"], "ms_median": sr["median_ms_per_step"],
+                        "GBps_median": sr["GBps_at_median"],
+                        "pct_of_hbm_peak": sr["pct_of_hbm_peak_at_median"],
+                        "kernel": "ls::stream_read_kernel (16-byte non-temporal loads)"},
+        "beyond_byte_time": rb.get("beyond_byte_time"),
+        "repeat_blocks": rb,
+        "single_call_latency_us": round(lat_us, 2),
+        "warm_same_replica_ms_per_step": round(warm_ms, 5),
+        "call_ms": call_ms,
+        "roofline": {"kernel": dom_match, "bound": "hbm", "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": tr["traffic_bytes"] if tr else None,
+                     "algorithmic_bytes_per_launch": round(dom_bytes),
+                     "avg_launch_ms": round(dom_ms, 5),
+                     "traffic_source": f"profiles/{dom_key}.md" if tr else None},
+        "wall_s_timed": round(wall, 4),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if ragged:
+        res["cells"] = {n: {"ms_per_step_median": c["median_ms_per_step"],
+                            "calls_per_s_median": round(1e3 / c["median_ms_per_step"], 1),
+                            "GBps": c["GBps_at_median"],
+                            "pct_of_hbm_peak": c["pct_of_hbm_peak_at_median"],
+                            "bytes_per_step": round(c["bytes_per_step"])}
+                        for n, c in rb["cells"].items()}
+        res["ragged_bytes_breakdown"] = sess["breakdown"]
+    if pool is not None:
+        print(f"# cpu baseline ({pool.n} processes)", file=sys.stderr, flush=True)
+        inp0 = sess["reps"][0]["inp"]
+        if ragged:
+            order = sorted(range(B), key=lambda r: int(inp0.seq_lens[r]))
+            sample = [order[s * B // 8 + B // 16] for s in range(8)]   # one per length octile
+            topk, kr = -1, KEEPS[args.keep]
+        else:
+            sample, topk, kr = list(range(B)), inp0.topk, 0.0
+        res["cpu_baseline"] = cpu_baseline(
+            pool, inp0, cfg, requests=sample, topk=topk, keep_ratio=kr,
+            score_mode="bounds" if (not ragged and sess["quest"]) else "mean",
+            sm_scale=sess["sm_scale"], step_bytes_total=prim.nbytes, budget_s=args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
+    argv = list(sys.argv[1:] if argv is None else argv)
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=400,
+                    help="steps in the timed region (exactly; one graph of that many steps)")
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--replicas", type=int, default=8)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="input replicas cycled by the steps (default: 8 at 16 x 32K, 3 ragged)")
+    ap.add_argument("--blocks", type=int, default=3,
+                    help="repeat blocks, each in a fresh process started before this one "
+                         "touches the GPU (0: one block in this process)")
+    ap.add_argument("--launches", type=int, default=20, help="timed graph launches per block")
+    ap.add_argument("--warm-launches", type=int, default=10)
+    ap.add_argument("--block-timeout", type=float, default=400.0)
+    ap.add_argument("--child-block", type=int, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--keep", choices=tuple(KEEPS), default="1/16",
+                    help="ragged path: the keep ratio the JSON line's value is for")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU seconds (all processes together) for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--separate", action="store_true",
@@ -837,13 +1569,15 @@ def main(argv=None) -> int:
                          "the exact one; reports its recall")
     ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
                     help="block-topk path: block-mean summaries (default) or Quest bounds")
-    ap.add_argument("--path", choices=("block-topk", "indexer", "coarse-to-fine", "dense", "pq",
-                                       "window", "snapkv"),
+    ap.add_argument("--path", choices=("block-topk", "ragged", "indexer", "coarse-to-fine",
+                                       "dense", "pq", "window", "snapkv"),
                     default="block-topk",
-                    help="block-topk: the 8B/32K/B16 block top-k step (default); indexer: "
-                         "token top-2048 of 8 x 128K + sparse MLA; coarse-to-fine: 4 x 950K; "
-                         "dense: k = all split-K attention on the 8B/32K/B16 workload; pq: PQ32 "
-                         "top-2048 candidates + exact rerank to top-512 of 8 x 128K + sparse MLA")
+                    help="block-topk: the 8B/32K/B16 block top-k step (default); ragged: the "
+                         "batch-64 sweep, lengths 2K-128K, keep 1/64, 1/16, 1/4 and k = all; "
+                         "indexer: token top-2048 of 8 x 128K + sparse MLA; coarse-to-fine: "
+                         "4 x 950K; dense: k = all split-K attention on the 8B/32K/B16 "
+                         "workload; pq: PQ32 top-2048 candidates + exact rerank to top-512 of "
+                         "8 x 128K + sparse MLA")
     args = ap.parse_args(argv)
     if args.summarize_profiles:
         return summarize_profiles(args)
@@ -851,136 +1585,18 @@ def main(argv=None) -> int:
         print("bench.py measures one GPU: the sparse-attention path has no multi-GPU mode "
               "(run with --gpus 1).", file=sys.stderr)
         return 2
+    if args.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
+        return 2
     if args.copy_calibrate:
         return copy_calibration(args.copy_calibrate)
     if args.path == "snapkv":
         return bench_snapkv(args)
     if args.path in ("dense", "window"):
         return bench_dense(args, window=args.path == "window")
-    if args.path != "block-topk":
-        return bench_indexer(args, coarse=args.path == "coarse-to-fine", pq=args.path == "pq")
-
-    import torch
-    import query_aware_sparse_ls_amd as ls
-    from workloads import LLAMA8B_32K_B16
-
-    cfg = LLAMA8B_32K_B16
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    sm_scale = 1.0 / math.sqrt(cfg.head_dim)
-    fused = not args.separate
-    R = max(1, args.replicas)
-    reps = [make_replica(cfg, cfg.seed + i, dev, args.score) for i in range(R)]
-    torch.cuda.synchronize()
-    print(f"# {R} replicas ready, {torch.cuda.memory_allocated() / 2**30:.1f} GiB",
-          file=sys.stderr, flush=True)
-
-    inp0 = reps[0]["inp"]
-    P, Hkv, D, Hq, B = cfg.page_size, cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads, cfg.batch
-    nb = cfg.context // P
-    n_forced = cfg.n_sink + cfg.n_recent
-    n_sel = inp0.topk + n_forced
-    n_cand = nb - n_forced
-    quest = args.score == "bounds"
-    nbytes = step_bytes(B, Hq, Hkv, D, P, nb, n_sel, n_cand, int(reps[0]["new_pages"].numel()),
-                        rows=2 if quest else 1)
-    main_stream = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-
-    for i in range(max(1, args.warmup)):
-        run_step(reps[i % R], cfg, sm_scale, fused, side)
-    torch.cuda.synchronize()
-
-    graph = None
-    if not args.no_graph:
-        cap = torch.cuda.Stream()
-        cap.wait_stream(main_stream)
-        with torch.cuda.stream(cap):
-            for i in range(R):
-                run_step(reps[i], cfg, sm_scale, fused, side)
-        main_stream.wait_stream(cap)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(R):
-                run_step(reps[i], cfg, sm_scale, fused, side)
-        torch.cuda.synchronize()
-        for _ in range(max(1, args.warmup // R)):
-            graph.replay()
-        torch.cuda.synchronize()
-    print("# timing", file=sys.stderr, flush=True)
-
-    replays = max(1, args.steps // R)
-    steps = replays * R
-    t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0e.record()
-    if graph is not None:
-        for _ in range(replays):
-            graph.replay()
-    else:
-        for i in range(steps):
-            run_step(reps[i % R], cfg, sm_scale, fused, side)
-    t1e.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t0e.elapsed_time(t1e) / steps
-
-    # per-call durations (eager, back-to-back launches of one call)
-    upd, first, second = per_call_ms(reps, cfg, sm_scale, fused, min(steps, 8 * R))
-
-    calls_per_s = 1e3 / ms_step
-    gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
-    sel_bytes = B * Hkv * n_sel * 4 + B * Hkv * 4      # selection written (+ counts)
-    fused_bytes = nbytes["total"] + sel_bytes           # summary refresh included
-    if fused:
-        # one (request, kv head) pair per workgroup plus the summary-refresh
-        # workgroups: the whole call is one launch
-        dom_ms, dom_bytes = first, fused_bytes
-        dom_key = "step_item_kernel.llama8b_32k_b16" + ("_quest" if quest else "")
-        dom_match = f"ls::step_item_kernel<128, 2048, {'true' if quest else 'false'}>"
-    else:
-        dom_ms = second
-        dom_bytes = nbytes["selected_kv"] + B * Hq * D * 2 + sel_bytes + B * nb * 4
-        dom_key = "attn_item_kernel.llama8b_32k_b16" + ("_quest" if quest else "")
-        dom_match = "ls::attn_item_kernel<128, 2048>"
-    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
-    tr = stored_traffic(dom_key)
-
-    res = {
-        "metric": "sparse decode attention calls/sec + achieved HBM GB/s (% of peak) at 8B/32K/B16",
-        "value": round(calls_per_s, 1), "unit": "calls/s", "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name + (" quest bounds" if quest else ""), "batch": B,
-                   "context": cfg.context, "q_heads": Hq,
-                   "kv_heads": Hkv, "head_dim": D, "page_size": P, "topk": inp0.topk,
-                   "n_sink": cfg.n_sink, "n_recent": cfg.n_recent, "replicas": R,
-                   "path": "fused" if fused else "separate",
-                   "block_scores": "quest bounds" if quest else "block-mean keys",
-                   "timing": "hip graph" if graph is not None else "eager"},
-        "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
-        "achieved_GBps_step": round(gbps, 1),
-        "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "call_ms": ({"decode_step_with_summary_refresh": round(first, 5)} if fused
-                    else {"summary_update": round(upd, 5), "score_select": round(first, 5),
-                          "sparse_attn_decode": round(second, 5)}),
-        "roofline": {"kernel": dom_match, "bound": "hbm", "achieved": round(dom_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": tr["traffic_bytes"] if tr else None,
-                     "algorithmic_bytes_per_launch": dom_bytes,
-                     "avg_launch_ms": round(dom_ms, 5),
-                     "traffic_source": f"profiles/{dom_key}.md" if tr else None},
-        "wall_s_timed": round(wall, 4),
-        "device": torch.cuda.get_device_name(0),
-    }
-    if not args.no_cpu_baseline:
-        print("# cpu baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(reps[0], cfg, sm_scale, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
-    return 0
+    if args.path in ("block-topk", "ragged"):
+        return bench_block_topk(args, argv)
+    return bench_indexer(args, coarse=args.path == "coarse-to-fine", pq=args.path == "pq")
 
 
 if __name__ == "__main__":

@@ -663,6 +663,19 @@ const char* ls_last_error(void);
 /* Library version and build string, e.g. "libls 0.2.0 abi 2 gfx950". */
 const char* ls_version(void);
 
+/* Measurement reference: one plain streaming read of `bytes` bytes at `src`
+ * (every 16-byte word read once, non-temporal, many loads in flight), the
+ * bandwidth this GPU delivers to a pure read, against which the decode
+ * step's bandwidth is reported (ByteCross §4.4 and App. D price decode
+ * kernels against the bandwidth the memory actually delivers). src: 16-byte
+ * aligned, bytes a multiple of 16. sink: device, ls_stream_read_sink_words()
+ * uint32 words, overwritten so that their XOR is the XOR of all 32-bit words
+ * of the buffer (no load is dead, and the read can be checked). bytes == 0:
+ * nothing is launched and sink is left as it was. Errors: LS_ERR_INVALID
+ * for a null or misaligned pointer or a size not a multiple of 16. */
+int32_t ls_stream_read_sink_words(void);
+ls_status ls_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Number of split-K partitions ls_sparse_attn_decode uses for a given
  * selection capacity (max_selected, or max_blocks on the dense path). */
 int32_t ls_attn_num_splits(int32_t max_selected);

@@ -26,7 +26,7 @@ _L = _lib.load()
 __all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_select", "sparse_attn_decode",
            "score_select_workspace_size", "sparse_attn_decode_workspace_size",
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
-           "sparse_decode_step_workspace", "sparse_decode_step_noalloc", "indexer_select", "indexer_select_workspace_size",
+           "sparse_decode_step_workspace", "sparse_decode_step_noalloc", "stream_read", "indexer_select", "indexer_select_workspace_size",
            "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
            "mla_num_splits", "pq_encode", "pq_train", "pq_select", "window_attn_decode",
            "snapkv_select", "snapkv_gather"]
@@ -186,6 +186,18 @@ def score_select(q: torch.Tensor, summaries: torch.Tensor, page_size: int, batch
 
 
 # ------------------------------------------------------------------ attention
+
+def stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One streaming read of the whole of `src` (the bandwidth reference);
+    returns the sink words."""
+    _need(src)
+    if sink is None:
+        sink = torch.empty(int(_L.ls_stream_read_sink_words()), dtype=torch.int32,
+                           device=src.device)
+    check(_L.ls_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                            _stream(stream)))
+    return sink
+
 
 def attn_num_splits(max_selected: int) -> int:
     return int(_L.ls_attn_num_splits(int(max_selected)))

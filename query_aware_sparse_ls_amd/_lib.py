@@ -89,6 +89,8 @@ _SIGS = {
     "ls_last_error": (C.c_char_p, []),
     "ls_version": (C.c_char_p, []),
     "ls_attn_num_splits": (C.c_int32, [C.c_int32]),
+    "ls_stream_read_sink_words": (C.c_int32, []),
+    "ls_stream_read": (C.c_int, [_P, C.c_size_t, _P, _P]),
 }
 
 _lib = None

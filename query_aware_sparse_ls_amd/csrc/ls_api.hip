@@ -617,6 +617,17 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
 
 size_t ls_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
+int32_t ls_stream_read_sink_words(void) { return ls::kStreamReadWorkgroups; }
+
+ls_status ls_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(LS_ERR_INVALID, "src and sink must be non-null");
+  if (!aligned16(src) || bytes % 16)
+    return fail(LS_ERR_INVALID, "src must be 16-byte aligned and bytes a multiple of 16");
+  return hip_status(ls::launch_stream_read(src, bytes, sink, ls::kStreamReadWorkgroups, stream),
+                    "stream read launch");
+}
+
 ls_status ls_sparse_decode_step_noalloc(const void* q, int32_t q_dtype, int32_t num_q_heads,
                                         void* summaries, const void* k_pool, const void* v_pool,
                                         ls_pool pool, ls_batch batch, const ls_select_params* p,

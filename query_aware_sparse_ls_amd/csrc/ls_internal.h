@@ -249,6 +249,11 @@ struct MlaArgs {
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t st);
 
+// Measurement reference (k_probe.hip): one streaming read of `bytes` bytes.
+constexpr int kStreamReadWorkgroups = 4096;
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
+                              hipStream_t st);
+
 // Blocks per attention split (one register-resident chunk per workgroup).
 constexpr int kAttnBlocksPerSplit = 8;
 

@@ -334,3 +334,16 @@ def test_window_and_snapkv_validation():
     assert g(FAKE, FAKE, _pool(), _batch(), None, FAKE, 8, FAKE, FAKE, None) == _lib.LS_ERR_INVALID
     assert g(FAKE, FAKE, _pool(), _batch(batch_size=0), FAKE, FAKE, 8, FAKE, FAKE,
              None) == _lib.LS_OK
+
+
+def test_stream_read_validation():
+    """The stream-read reference rejects null and misaligned arguments on
+    the host and launches nothing for zero bytes."""
+    lib = _lib.load()
+    assert lib.ls_stream_read_sink_words() > 0
+    assert lib.ls_stream_read(FAKE, 0, FAKE, None) == _lib.LS_OK
+    assert lib.ls_stream_read(None, 64, FAKE, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_stream_read(FAKE, 64, None, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_stream_read(FAKE + 8, 64, FAKE, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_stream_read(FAKE, 40, FAKE, None) == _lib.LS_ERR_INVALID
+    assert b"aligned" in lib.ls_last_error()
