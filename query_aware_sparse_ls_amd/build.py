@@ -42,9 +42,14 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-file flags. The planned attention keeps its MFMA accumulators in VGPRs
+# (the AGPR form would add 32 registers and halve its occupancy).
+FILE_FLAGS = {"k_plan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -433,6 +433,19 @@ struct ItemPair {
   int half;            // which of the two workgroups this is
 };
 
+// Elements of the merged state each thread of an NW-wave workgroup holds:
+// element e = tid + j * NW * 64 (head e / D, dim e % D), j < item_ept.
+template <int D, int NW>
+constexpr int item_ept() { return (4 * D + NW * kWave - 1) / (NW * kWave); }
+
+// The merged state of the positions item_attn walked, in the element layout
+// above: o relative to the maximum, m (log2 domain) and l per element's
+// head. Given to item_attn, it receives the state instead of any store.
+template <int EPT>
+struct ItemState {
+  float m[EPT], o[EPT], l[EPT];
+};
+
 // Split s of num_splits of a (request, kv head) pair's positions: the merged
 // state is written unnormalised as split s of the split-K partials
 // (o relative to the split maximum, then m in the log2 domain, then l; the
@@ -453,7 +466,8 @@ template <int D, bool kLo = false, int NW = kItemWaves, int kSplitStore = kSplit
 __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const int* ent,
                                           int cnt, ItemAttnLds<D, NW>& sh,
                                           const ItemPair* pair = nullptr,
-                                          const ItemSplit* split = nullptr) {
+                                          const ItemSplit* split = nullptr,
+                                          ItemState<item_ept<D, NW>()>* state = nullptr) {
   using ST = Stage<D>;
   constexpr int KS = D / 32, NL = ST::NL, NT = D / 16;
   static_assert(NPF >= 1 && NPF <= kItemPrefetch, "entry padding covers kItemPrefetch");
@@ -643,6 +657,15 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
     Mv[j] = M;
     Ov[j] = O;
     Lv[j] = Ls;
+  }
+  if (state) {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      state->m[j] = Mv[j];
+      state->o[j] = Ov[j];
+      state->l[j] = Lv[j];
+    }
+    return;
   }
   if (split) {
 #pragma unroll

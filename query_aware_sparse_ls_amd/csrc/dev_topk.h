@@ -344,9 +344,11 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
 constexpr int kTopkFastPasses = 4;
 constexpr int kTopkFastMaxBlocks = 4096;
 
+template <int MAXB = kTopkFastMaxBlocks>
 struct TopkFastLds {
+  static_assert(MAXB % 32 == 0, "whole bitmap words");
   int hist[kTopkFastPasses][256];
-  unsigned bm[kTopkFastMaxBlocks / 32];
+  unsigned bm[MAXB / 32];
   float list_key[kWave];
   int list_idx[kWave];
   int list_n;
@@ -383,19 +385,20 @@ __device__ __noinline__ int topk_fallback(const float* srow, const ReqGeom& geo,
 // calls it, except on the fallback path, where every thread may; the
 // fallback writes the selection to fb_out with device-coherent stores and
 // reads it back). Returns the stored count, min(selected, max_selected).
-template <int PER, int NT, class Emit>
+// MAXB: the bitmap's blocks (geo.nb <= MAXB).
+template <int PER, int NT, class Emit, int MAXB>
 __device__ int topk_fast(const float* __restrict__ srow, const ReqGeom& geo, int k,
-                         int max_selected, TopkFastLds& sh, TopkLds& fallback,
+                         int max_selected, TopkFastLds<MAXB>& sh, TopkLds& fallback,
                          int32_t* __restrict__ fb_out, int32_t* __restrict__ fb_count, float mn0,
                          float mx0, Emit emit) {
   constexpr int NW = NT / kWave;
   static_assert(NT % kWave == 0 && NW <= kTopkMaxWaves && PER >= 1 && PER <= 32, "shape");
-  static_assert(NT * PER <= kTopkFastMaxBlocks, "blocks");
-  constexpr int WPL = (kTopkFastMaxBlocks / 32 + kWave - 1) / kWave;   // bitmap words per lane
+  static_assert(NT * PER <= MAXB, "blocks");
+  constexpr int WPL = (MAXB / 32 + kWave - 1) / kWave;   // bitmap words per lane
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = geo.c1 - geo.c0;
   for (int i = tid; i < kTopkFastPasses * 256; i += NT) (&sh.hist[0][0])[i] = 0;
-  for (int i = tid; i < kTopkFastMaxBlocks / 32; i += NT) sh.bm[i] = 0u;
+  for (int i = tid; i < MAXB / 32; i += NT) sh.bm[i] = 0u;
   if (tid == 0) sh.list_n = 0;
   float key[PER];
   uint32_t act = 0, sel = 0;

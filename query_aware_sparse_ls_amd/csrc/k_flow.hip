@@ -60,7 +60,7 @@ struct FlowLds {
     struct {
       alignas(16) float sc[MAXC + MAXC / 16];       // padded score row
       TopkLds tk;
-      TopkFastLds tf[MAXC <= kTopkFastMaxBlocks ? 1 : 0];
+      TopkFastLds<> tf[MAXC <= kTopkFastMaxBlocks ? 1 : 0];
       int pgrow[kPgLds<MAXC> ? MAXC : 1];           // the pair's page-table row
     } t;
     ItemAttnLds<D, NW> at;

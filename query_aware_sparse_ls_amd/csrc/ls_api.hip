@@ -11,6 +11,7 @@
 
 #include "ls_flow.h"
 #include "ls_internal.h"
+#include "ls_plan.h"
 
 namespace {
 
@@ -174,14 +175,16 @@ SelectWs select_ws(int B, int hkv, int max_blocks) {
   return w;
 }
 
-// Split states of the attention: the split-K kernels' and the flow kernel's.
+// Split states of the attention: the split-K kernels', the flow kernel's
+// and the planned kernels' (one slot pair per attention workgroup).
 size_t attn_parts_bytes(int B, int hq, int head_dim, int max_selected, int max_blocks) {
   const int cap = max_selected > 0 ? max_selected : max_blocks;
   const size_t split = (size_t)B * hq * ls_attn_num_splits(cap) * (head_dim + 2) * sizeof(float);
   const int pairs = B * ((hq + 3) / 4);
   const size_t flow =
       ls::flow_parts_bytes(pairs, head_dim, ls::flow_plan(pairs, max_blocks, cap).splits);
-  return align_up(split > flow ? split : flow);
+  const size_t plan = ls::plan_slots_bytes(head_dim);
+  return align_up(std::max(split, std::max(flow, plan)));
 }
 
 struct AttnWs {
@@ -209,19 +212,43 @@ StepWs step_ws(int B, int hq, int hkv, int head_dim, int max_blocks, int max_sel
 
 // Which kernels serve a selection / attention / step call. The per-pair
 // kernels (one workgroup owns a (request, kv head) pair from scoring to
-// output, no hand-off between workgroups) are faster when there are at
-// least kItemMinPairs pairs of at most 4096 blocks; the flow kernel (a
-// pair spread over many workgroups) serves the other shapes up to
-// kFlowMaxBlocks blocks; longer requests take the split kernels.
-enum Route { kRouteItem, kRouteFlow, kRouteSplit };
+// output, no hand-off between workgroups) are fastest when there are at
+// least kItemMinPairs pairs of at most 4096 blocks. Longer requests in such
+// batches take the planned kernels (work cut into equal ranges over all
+// pairs, whatever their lengths). Fewer pairs take the flow kernel (a pair
+// spread over many workgroups in one launch) up to kFlowMaxBlocks blocks,
+// then the planned kernels; other shapes take the split kernels.
+enum Route { kRouteItem, kRouteFlow, kRoutePlan, kRouteSplit };
 Route route(const ls_pool& pool, const ls_batch& batch, int num_q_heads) {
   const int group = num_q_heads / pool.num_heads;
+  const int pairs = batch.batch_size * pool.num_heads;
   if (ls::item_path(batch.batch_size, pool.num_heads, pool.head_dim, group, batch.max_blocks,
                     pool.num_pages) &&
       batch.max_blocks <= 4096)
     return kRouteItem;
+  const bool plan = ls::plan_ok(group, pool.head_dim, batch.max_blocks, pool.num_pages, pairs);
+  if (plan && pairs >= ls::kItemMinPairs) return kRoutePlan;
   if (ls::flow_ok(group, pool.head_dim, batch.max_blocks, pool.num_pages)) return kRouteFlow;
+  if (plan) return kRoutePlan;
   return kRouteSplit;
+}
+
+ls::PlanArgs plan_args(const ls::ScoreArgs& sa, const ls::TopkArgs& ta, const ls::AttnArgs& aa,
+                       const ls::SummaryUpdate& up, int pairs, int max_blocks, char* w,
+                       size_t rows_off, size_t slots_off, float* scores_out) {
+  ls::PlanArgs p;
+  p.sa = sa;
+  p.ta = ta;
+  p.aa = aa;
+  p.up = up;
+  p.rows = scores_out ? scores_out : reinterpret_cast<float*>(w + rows_off);
+  p.zero_rows = scores_out == nullptr;
+  p.ta.scores = p.rows;
+  p.ctl = reinterpret_cast<uint32_t*>(w);
+  p.slots = reinterpret_cast<float*>(w + slots_off);
+  p.pairs = pairs;
+  p.max_blocks = max_blocks;
+  return p;
 }
 
 ls::FlowArgs flow_args(const ls::ScoreArgs& sa, const ls::TopkArgs& ta, const ls::AttnArgs& aa,
@@ -332,6 +359,15 @@ ls_status run_step(const void* q, int32_t num_q_heads, void* summaries, const vo
                                      batch.max_blocks, p.max_selected, w, lay.rows, lay.ents,
                                      lay.parts, nullptr);
     return hip_status(ls::launch_flow(f, ls::kFlowStep, stream), "decode-step kernel launch");
+  }
+  if (rt == kRoutePlan) {
+    // the selection calls, then the attention call, as ls_score_select and
+    // ls_sparse_attn_decode run them (same kernels, same bits)
+    const ls::PlanArgs pa = plan_args(sa, ta, aa, up, batch.batch_size * pool.num_heads,
+                                      batch.max_blocks, w, lay.rows, lay.parts, nullptr);
+    hipError_t e = ls::launch_plan_select(pa, stream);
+    if (e == hipSuccess) e = ls::launch_plan_attend(pa, stream);
+    return hip_status(e, "decode-step kernel launches");
   }
   // longer requests: the split kernels of the two calls back to back
   hipError_t e = hipSuccess;
@@ -512,6 +548,12 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
                                      p->max_selected, w, lay.rows, 0, 0, scores_out);
     return hip_status(ls::launch_flow(f, ls::kFlowSelect, stream), "selection kernel launch");
   }
+  if (rt == kRoutePlan) {
+    const ls::PlanArgs pa = plan_args(sa, ta, ls::AttnArgs{}, ls::SummaryUpdate{},
+                                      batch.batch_size * pool.num_heads, batch.max_blocks, w,
+                                      lay.rows, 0, scores_out);
+    return hip_status(ls::launch_plan_select(pa, stream), "selection kernel launches");
+  }
   hipError_t e = ls::launch_score(sa, stream);
   if (e != hipSuccess) return hip_status(e, "score kernel launch");
   e = ls::launch_topk(ta, stream);
@@ -576,6 +618,12 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                      batch.batch_size * pool.num_heads, batch.max_blocks,
                                      max_selected, w, 0, 0, lay.parts, nullptr);
     return hip_status(ls::launch_flow(f, ls::kFlowAttend, stream), "attention kernel launch");
+  }
+  if (rt == kRoutePlan) {   // a selection, or every block (dense)
+    const ls::PlanArgs pa = plan_args(ls::ScoreArgs{}, ls::TopkArgs{}, aa, ls::SummaryUpdate{},
+                                      batch.batch_size * pool.num_heads, batch.max_blocks, w, 0,
+                                      lay.parts, nullptr);
+    return hip_status(ls::launch_plan_attend(pa, stream), "attention kernel launch");
   }
   hipError_t e = (!selected && pool.num_pages < (1 << 26)) ? ls::launch_attn_chunked(aa, stream)
                                                             : ls::launch_attn(aa, stream);

@@ -48,10 +48,17 @@ def _same(a, b):
     reduced(LLAMA8B_32K_B16, batch=5, context=2500),
     # 24 pairs of up to 5000 blocks: the 8192-block ranking
     reduced(RAGGED_B64, batch=3, ragged_range=(20000, 80000), topk=40, keep_ratio=None),
-], ids=["tiny", "8b_b3", "8b_b11", "ragged_b9", "8b_b5_2500", "ragged_b3_long"])
+    # 72 pairs, the longest over 4096 blocks: the planned route (scoring and
+    # attention cut into equal ranges across pairs)
+    reduced(RAGGED_B64, batch=9, ragged_range=(17, 80000), topk=40, keep_ratio=None),
+], ids=["tiny", "8b_b3", "8b_b11", "ragged_b9", "8b_b5_2500", "ragged_b3_long", "planned_b9"])
 def test_fused_equals_separate_and_oracle(cfg):
     say(f"fused step vs separate calls and oracle: {cfg.name}")
-    inp = make_block_topk_inputs(cfg, device="cuda", seed=31)
+    lens = None
+    if cfg.batch == 9 and cfg.ragged_range == (17, 80000):
+        # an empty request, one of a partial page, short and long ones
+        lens = [80000, 2000, 35000, 65600, 17, 4100, 70001, 0, 50000]
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=31, seq_lens=lens)
     sep = run_gpu_step(inp)
     fus = run_gpu_fused(inp, summaries=sep.summaries)
     _same(sep, fus)
@@ -79,14 +86,18 @@ def test_fused_workspace_reuse_across_calls():
         assert int(torch.count_nonzero(ws)) == 0
 
 
-@pytest.mark.parametrize("batch", [5, 16])   # 40 pairs: many workgroups per pair; 128: one
-def test_workspace_left_zero_by_every_call(batch):
+@pytest.mark.parametrize("batch,context", [
+    (5, 2500),     # 40 pairs: many workgroups per pair
+    (16, 2500),    # 128 pairs: one workgroup per pair
+    (8, 70000),    # 64 pairs of 4375 blocks: the planned route
+])
+def test_workspace_left_zero_by_every_call(batch, context):
     """Selection, attention and step calls each leave their workspace zero
     (hand-off words reset by their readers, no wait gave up), also when one
     workspace serves all three in turn."""
     import query_aware_sparse_ls_amd as ls
     from parity_util import paged_batch
-    cfg = reduced(LLAMA8B_32K_B16, batch=batch, context=2500)
+    cfg = reduced(LLAMA8B_32K_B16, batch=batch, context=context)
     inp = make_block_topk_inputs(cfg, device="cuda", seed=9)
     B, Hq, D = inp.q.shape
     Hkv = cfg.num_kv_heads
@@ -118,10 +129,12 @@ def test_workspace_left_zero_by_every_call(batch):
         assert torch.equal(out, out2) and torch.equal(cnt2, ref.counts)
 
 
-def test_fused_step_hip_graph_replay():
-    say("fused step captured in a HIP graph, replayed with eager work in between")
+@pytest.mark.parametrize("batch,context", [(4, 5000), (8, 70000)])   # flow; planned (3 launches)
+def test_fused_step_hip_graph_replay(batch, context):
+    say(f"fused step captured in a HIP graph, replayed with eager work in between: "
+        f"{batch} x {context}")
     import query_aware_sparse_ls_amd as ls
-    cfg = reduced(LLAMA8B_32K_B16, batch=4, context=5000)
+    cfg = reduced(LLAMA8B_32K_B16, batch=batch, context=context)
     inp = make_block_topk_inputs(cfg, device="cuda", seed=4)
     eager = run_gpu_step(inp)
     B, Hq, D = inp.q.shape

@@ -233,3 +233,30 @@ def test_ragged_many_pairs_long_requests_keep_ratio():
             say(f"  r{r} (L={L}) g{g}")
             check_pair(inp, res, r, g, **{kk: v for kk, v in _kw(inp, res, topk=k).items()
                                            if kk != "res"})
+
+
+@pytest.mark.parametrize("keep", [1.0 / 64, 1.0 / 4])
+def test_ragged_b64_full_size_keep_ratios(keep):
+    """The batch-64 ragged sweep at full size (512 pairs, lengths log-uniform
+    in [2K, 128K], shared pool at 70% occupancy): the planned route. Fused
+    step equal to the separate calls; sampled pairs (the shortest, the
+    longest, two in between) against the oracle."""
+    from parity_util import run_gpu_fused
+    cfg = RAGGED_B64
+    say(f"ragged B64 full size, keep {keep}")
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=cfg.seed)
+    lens = inp.seq_lens.tolist()
+    assert max(lens) > 16 * 4096
+    res = run_gpu_step(inp, topk=-1, keep_ratio=keep)
+    fus = run_gpu_fused(inp, summaries=res.summaries, topk=-1, keep_ratio=keep)
+    assert torch.equal(res.counts, fus.counts)
+    assert torch.equal(res.out, fus.out) and torch.equal(res.lse, fus.lse)
+    P = cfg.page_size
+    order = np.argsort(lens)
+    for r in (int(order[0]), int(order[-1]), int(order[len(lens) // 3]), int(order[-5])):
+        L = lens[r]
+        k = topk_from_keep_ratio(-(-L // P), L // P, keep, cfg.n_sink, cfg.n_recent)
+        for g in (0, 5):
+            say(f"  r{r} (L={L}) g{g}")
+            check_pair(inp, res, r, g, **{kk: v for kk, v in _kw(inp, res, topk=k).items()
+                                           if kk != "res"})

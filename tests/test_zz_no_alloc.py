@@ -2,8 +2,8 @@
 array instead of a caller workspace) gives the same bits as
 ls_sparse_decode_step, call after call on the one shared array, the second
 call with a smaller input; shapes on the per-pair route (no scratch used) and
-on the many-workgroups route (scratch used: control words, scores,
-selection entries, split states)."""
+on the many-workgroups and planned routes (scratch used: control words,
+scores, selection entries, split states)."""
 
 import math
 
@@ -61,6 +61,9 @@ def _both(inp, summaries):
     ("flow", dict(batch=2, context=4096 + 7), dict(batch=1, context=2500)),
     # 128 and 64 pairs of at most 4096 blocks: one workgroup per pair
     ("per-pair", dict(batch=16, context=3000), dict(batch=8, context=1100)),
+    # 64 pairs of more than 4096 blocks: the planned route (score rows, split
+    # states of pairs cut by range ends, arrival counters in scratch)
+    ("planned", dict(batch=8, context=70000), dict(batch=8, context=66000)),
 ])
 def test_noalloc_matches_step_two_calls(route, first, second):
     for i, shape in enumerate((first, second)):
