@@ -1245,8 +1245,11 @@ def dense_cell(reps, sm_scale, nbytes, steps):
 
 
 def make_session(args, dev, block=None):
-    return ragged_session(args, dev, block) if args.path == "ragged" else \
+    sess = ragged_session(args, dev, block) if args.path == "ragged" else \
         block_topk_session(args, dev, block)
+    if getattr(args, "only_primary", False):
+        sess["cells"] = {sess["primary"]: sess["cells"][sess["primary"]]}
+    return sess
 
 
 def block_topk_session(args, dev, block=None):
@@ -1358,8 +1361,31 @@ def ragged_session(args, dev, block=None):
                               selected=k["sel"], selected_count=k["cnt"], out=k["out"],
                               new_pages=rp["new_pages"], workspace=k["ws"])
 
+    def select(i, name):
+        rp = reps[i]
+        k = rp["keeps"][name]
+        ls.score_select(rp["inp"].q, rp["summ"], P, rp["batch"], topk=-1, keep_ratio=k["ratio"],
+                        n_sink=cfg.n_sink, n_recent=cfg.n_recent, max_selected=k["maxsel"],
+                        group_agg=cfg.group_agg, selected=k["sel"], selected_count=k["cnt"],
+                        workspace=k["ws_sel"])
+
+    def attend(i, name):
+        rp = reps[i]
+        k = rp["keeps"][name]
+        inp = rp["inp"]
+        ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, rp["batch"], k["sel"], k["cnt"],
+                              sm_scale=sm, out=k["out"], workspace=k["ws_attn"])
+
+    for rp in reps:
+        mb = rp["batch"].max_blocks
+        for k in rp["keeps"].values():
+            k["ws_sel"] = torch.zeros(ls.score_select_workspace_size(B, Hkv, mb),
+                                      dtype=torch.uint8, device=dev)
+            k["ws_attn"] = torch.zeros(ls.sparse_attn_decode_workspace_size(
+                B, Hq, D, k["maxsel"], mb), dtype=torch.uint8, device=dev)
+
     # bytes per step from the selections themselves (one untimed step each)
-    cells, breakdown = {}, {}
+    cells, breakdown, positions = {}, {}, {}
     for name in KEEPS:
         parts = []
         for i in range(R):
@@ -1370,6 +1396,7 @@ def ragged_session(args, dev, block=None):
         mean = {key: sum(p[key] for p in parts) / R for key in parts[0]}
         mean["total"] = sum(mean.values())
         breakdown[name] = mean
+        positions[name] = sum(int(reps[i]["keeps"][name]["cnt"].sum()) for i in range(R)) / R
         cells["keep_" + name] = Cell("keep_" + name, lambda i, n=name: step(i, n), mean["total"],
                                      args.steps)
     dense_bytes = sum(float(r["inp"].seq_lens.long().sum()) * Hkv * D * 2 * 2
@@ -1380,7 +1407,8 @@ def ragged_session(args, dev, block=None):
     primary = "keep_" + args.keep
     cells["stream_read"] = stream_cell(reps, cells[primary].nbytes, args.steps)
     return {"cfg": cfg, "reps": reps, "R": R, "cells": cells, "primary": primary,
-            "sm_scale": sm, "breakdown": breakdown, "step": step}
+            "sm_scale": sm, "breakdown": breakdown, "positions": positions, "step": step,
+            "select": select, "attend": attend}
 
 
 # ----------------------------------------------------------------- main ----
@@ -1392,6 +1420,8 @@ def bench_block_topk(args, argv) -> int:
     """The block top-k decode step (default path) or the ragged sweep."""
     if args.child_block is not None:
         return child_block(args)
+    if args.only_primary:
+        args.blocks, args.no_cpu_baseline = 0, True
     pool = None
     if not args.no_cpu_baseline:
         pool = OraclePool(oracle_workers())        # spawned before any GPU call here
@@ -1431,11 +1461,20 @@ def _bench_block_topk_parent(args, blocks, pool) -> int:
     gbps = prim.nbytes / (ms_step * 1e-3) / 1e9
     B = cfg.batch
     if ragged:
-        dom_ms = eager_mean_ms(prim.fn, R, 4 * R)
-        dom_bytes = prim.nbytes
-        dom_key = f"step_flow_kernel.ragged_b64_keep{args.keep.replace('/', 'of')}"
-        dom_match = "flow_kernel<128, 8192"
-        call_ms = {"decode_step_with_summary_refresh": round(dom_ms, 5)}
+        # the step is three launches (scoring, ranking, attention); the
+        # attention call alone is one kernel, the one moving the most bytes
+        step_ms = eager_mean_ms(prim.fn, R, 4 * R)
+        sel_ms = eager_mean_ms(lambda i: sess["select"](i, args.keep), R, 4 * R)
+        att_ms = eager_mean_ms(lambda i: sess["attend"](i, args.keep), R, 4 * R)
+        bd = sess["breakdown"][args.keep]
+        Hq, D = cfg.num_q_heads, cfg.head_dim
+        n_pos = sess["positions"][args.keep]
+        dom_ms = att_ms
+        dom_bytes = bd["selected_kv"] + 2 * B * Hq * D * 2 + n_pos * 4 * 2 + B * cfg.num_kv_heads * 4
+        dom_key = f"plan_attn_kernel.ragged_b64_keep{args.keep.replace('/', 'of')}"
+        dom_match = "plan_attn_kernel<128, false>"
+        call_ms = {"decode_step_with_summary_refresh": round(step_ms, 5),
+                   "score_select": round(sel_ms, 5), "sparse_attn_decode": round(att_ms, 5)}
     else:
         cfg8 = cfg
         upd, first, second = per_call_ms(sess["reps"], cfg8, sess["sm_scale"], sess["fused"],
@@ -1460,7 +1499,7 @@ def _bench_block_topk_parent(args, blocks, pool) -> int:
                        "sparse_attn_decode": round(second, 5)}
     dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
     tr = stored_traffic(dom_key)
-    sr = rb["cells"]["stream_read"]
+    sr = rb["cells"].get("stream_read")
     workload = (f"ragged_b64_2k_128k keep {args.keep}" if ragged
                 else cfg.name + (" quest bounds" if sess["quest"] else ""))
     config = {"workload": workload, "batch": B, "q_heads": cfg.num_q_heads,
@@ -1486,10 +1525,10 @@ def _bench_block_topk_parent(args, blocks, pool) -> int:
         "achieved_GBps_step": round(gbps, 1),
         "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "pct_of_stream_read_step": rb.get("pct_of_stream_read", {}).get(sess["primary"]),
-        "stream_read": {"bytes": sr["bytes_per_step"], "ms_median": sr["median_ms_per_step"],
-                        "GBps_median": sr["GBps_at_median"],
-                        "pct_of_hbm_peak": sr["pct_of_hbm_peak_at_median"],
-                        "kernel": "ls::stream_read_kernel (16-byte non-temporal loads)"},
+        "stream_read": None if sr is None else {
+            "bytes": sr["bytes_per_step"], "ms_median": sr["median_ms_per_step"],
+            "GBps_median": sr["GBps_at_median"], "pct_of_hbm_peak": sr["pct_of_hbm_peak_at_median"],
+            "kernel": "ls::stream_read_kernel (16-byte non-temporal loads)"},
         "beyond_byte_time": rb.get("beyond_byte_time"),
         "repeat_blocks": rb,
         "single_call_latency_us": round(lat_us, 2),
@@ -1546,6 +1585,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warm-launches", type=int, default=10)
     ap.add_argument("--block-timeout", type=float, default=400.0)
     ap.add_argument("--child-block", type=int, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--only-primary", action="store_true",
+                    help="time only the cell the value is for (no repeat blocks, no oracle): "
+                         "for profiling one kernel's launches")
     ap.add_argument("--keep", choices=tuple(KEEPS), default="1/16",
                     help="ragged path: the keep ratio the JSON line's value is for")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,

@@ -175,32 +175,45 @@ __device__ int topk_wg(const float* __restrict__ srow, const ReqGeom& geo, int k
       break;
     }
     if (cnt <= kWave) {
-      // the undecided candidates go to a list in any order; each is ranked by
-      // counting the listed ones ahead of it (the order is total, so the list
-      // order does not matter) and the first `need` win
+      // the undecided candidates (at most one wave's worth) go to a list in
+      // thread order; wave 0 ranks them, lane i entry i, by counting the
+      // entries ahead of it (read from the other lanes; the order is total),
+      // flags the first `need`, and the owners take the flagged ones
+      int listed;
+      const int base = wg_excl_scan_i<NW>(sh, __popcll(act), 1, &listed);
+      listed = listed < kWave ? listed : kWave;
+      {
+        int pos = base;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if ((act >> j) & 1ull) {
-          const int pos = atomicAdd(&sh.list_n, 1);
-          sh.list_key[pos] = key[j];
-          sh.list_idx[pos] = tid * PER + j;
+        for (int j = 0; j < PER; ++j) {
+          if ((act >> j) & 1ull) {
+            if (pos < kWave) {
+              sh.list_key[pos] = key[j];
+              sh.list_idx[pos] = tid * PER + j;
+            }
+            ++pos;
+          }
         }
       }
       __syncthreads();
+      if (tid < kWave) {
+        const float mk = lane < listed ? sh.list_key[lane] : 0.0f;
+        const int mi = lane < listed ? sh.list_idx[lane] : 0;
+        int rank = 0;
+        for (int u = 0; u < listed; ++u)
+          rank += ahead(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), u)),
+                        __builtin_amdgcn_readlane(mi, u), mk, mi);
+        if (lane < listed) sh.list_idx[lane] = rank < need ? 1 : 0;
+      }
+      __syncthreads();
+      {
+        int pos = base;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if ((act >> j) & 1ull) {
-          const float mk = key[j];
-          const int mi = tid * PER + j;
-          int rank = 0;
-          for (int u0 = 0; u0 < cnt; u0 += 8) {   // 8 list reads in flight
-#pragma unroll
-            for (int uu = 0; uu < 8; ++uu) {
-              const int u = u0 + uu;
-              if (u < cnt) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
-            }
+        for (int j = 0; j < PER; ++j) {
+          if ((act >> j) & 1ull) {
+            if (pos < kWave && sh.list_idx[pos]) sel |= 1ull << j;
+            ++pos;
           }
-          if (rank < need) sel |= 1ull << j;
         }
       }
       act = 0;
@@ -420,7 +433,9 @@ __device__ int topk_fast(const float* __restrict__ srow, const ReqGeom& geo, int
       break;
     }
     if (cnt <= kWave) {
-      // list the undecided; each is ranked by counting those ahead of it
+      // list the undecided (at most one wave's worth); wave 0 ranks them,
+      // lane i entry i, by counting the entries ahead of it (read from the
+      // other lanes), and the first `need` go straight into the bitmap
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         if ((act >> j) & 1u) {
@@ -430,20 +445,16 @@ __device__ int topk_fast(const float* __restrict__ srow, const ReqGeom& geo, int
         }
       }
       __syncthreads();
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if ((act >> j) & 1u) {
-          const float mk = key[j];
-          const int mi = tid * PER + j;
-          int rank = 0;
-          for (int u0 = 0; u0 < cnt; u0 += 8) {
-#pragma unroll
-            for (int uu = 0; uu < 8; ++uu) {
-              const int u = u0 + uu;
-              if (u < cnt) rank += ahead(sh.list_key[u], sh.list_idx[u], mk, mi);
-            }
-          }
-          if (rank < need) sel |= 1u << j;
+      if (tid < kWave) {
+        const float mk = lane < cnt ? sh.list_key[lane] : 0.0f;
+        const int mi = lane < cnt ? sh.list_idx[lane] : 0;
+        int rank = 0;
+        for (int u = 0; u < cnt; ++u)
+          rank += ahead(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), u)),
+                        __builtin_amdgcn_readlane(mi, u), mk, mi);
+        if (lane < cnt && rank < need) {
+          const int b = geo.c0 + mi;
+          atomicOr(&sh.bm[b >> 5], 1u << (b & 31));
         }
       }
       act = 0;
