@@ -154,12 +154,13 @@ __device__ __forceinline__ uint4 k_operand(const uint32_t* tile, int j) {
 // page 0 and is discarded -- so the number in flight is fixed). A candidate
 // whose page id is out of range scores 0.
 // pg[b - pg_off] is the page id of candidate b; NW waves take the tiles.
-template <int D, int MAXC, int kStore = kStoreLds, int NW = kItemWaves>
+template <int D, int MAXC, int kStore = kStoreLds, int NW = kItemWaves,
+          int NS = kItemScorePrefetch>
 __device__ __forceinline__ void item_score(const ScoreArgs& a, int r, int g, const ReqGeom& geo,
                                            const int* pg, float* sc, uint32_t* stage,
                                            float* range = nullptr, int pg_off = 0) {
   using ST = Stage<D>;
-  constexpr int KS = D / 32, NL = ST::NL, NS = kItemScorePrefetch;
+  constexpr int KS = D / 32, NL = ST::NL;
   static_assert(NS % 2 == 0, "slots are consumed in pairs");
   const int HKV = a.num_kv_heads;
   const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -470,7 +471,8 @@ __device__ __forceinline__ void item_attn(const AttnArgs& a, int r, int g, const
                                           ItemState<item_ept<D, NW>()>* state = nullptr) {
   using ST = Stage<D>;
   constexpr int KS = D / 32, NL = ST::NL, NT = D / 16;
-  static_assert(NPF >= 1 && NPF <= kItemPrefetch, "entry padding covers kItemPrefetch");
+  // (entry reads past the written ones are guarded: any depth is safe)
+  static_assert(NPF >= 1 && NPF <= 4, "K/V blocks in flight per wave");
   constexpr int RW = ST::kVRowWords;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int row = lane & 15, kq = lane >> 4;

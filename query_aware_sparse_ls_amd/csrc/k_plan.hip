@@ -39,35 +39,64 @@ namespace {
 constexpr int NW = kPlanWaves;
 constexpr int NT = kPlanThreads;
 constexpr int kPlanMergeBatch = 4;   // slot states the merger loads per round
-constexpr int kPlanPrefetch = 1;     // K/V blocks in flight per attention wave
+#ifndef LS_PLAN_PREFETCH
+#define LS_PLAN_PREFETCH 2
+#endif
+#ifndef LS_PLAN_ATTN_WAVES_PER_EU
+#define LS_PLAN_ATTN_WAVES_PER_EU 2
+#endif
+constexpr int kPlanPrefetch = LS_PLAN_PREFETCH;   // K/V blocks in flight per attention wave
+#ifndef LS_PLAN_SCORE_PREFETCH
+#define LS_PLAN_SCORE_PREFETCH 2
+#endif
+#ifndef LS_PLAN_SCORE_WAVES_PER_EU
+#define LS_PLAN_SCORE_WAVES_PER_EU 4
+#endif
+constexpr int kPlanScorePrefetch = LS_PLAN_SCORE_PREFETCH;   // summary tiles in flight per wave
+// What visiting one more pair costs a workgroup (its page ids or walk
+// entries, its queries, the merge of its waves' states, its output), in
+// items of the plan: 16-block summary tiles when scoring, positions (16-token
+// blocks) when attending (measured on MI355X).
+#ifndef LS_PLAN_SCORE_VISIT
+#define LS_PLAN_SCORE_VISIT 4
+#endif
+#ifndef LS_PLAN_ATTN_VISIT
+#define LS_PLAN_ATTN_VISIT 12
+#endif
+constexpr int kPlanScoreVisit = LS_PLAN_SCORE_VISIT;
+constexpr int kPlanAttnVisit = LS_PLAN_ATTN_VISIT;
 
 // Device-wide plan walk: the pairs' counts in pair order, this workgroup's
 // range of the flat space, and the pairs that intersect it.
 struct PlanWalkLds {
-  int wtot[NW];         // per-wave count totals (pass 1)
-  int next;             // S of the next chunk's first pair (pass 2)
-  int nhit;             // pairs of the current chunk that intersect the range
-  int hit_p[kWave];     // those pairs, in order, with their starts and counts
-  int hit_s[kWave];
-  int hit_n[kWave];
+  int wtot[NW];         // per-wave totals of a scan
+  int wcnt[NW];         // per-wave numbers of listed pairs
+  int hit_p[NT];        // the chunk's pairs of the range, wave w's at [64 w, 64 w + wcnt[w])
+  int hit_s[NT];
+  int hit_n[NT];
 };
 
-// The flat space: pair p owns items [S_p, S_p + count(p)), S_p = the sum of
-// the counts of the pairs before it; T = the sum of all. Workgroup w of
+// The flat space: pair p owns items [S_p, S_p + count(p) + C) (C more items
+// when count(p) > 0: what visiting a pair costs beyond its own items, so
+// that a range of many short pairs holds fewer items), S_p = the sum of the
+// items of the pairs before it; T = the sum of all. Workgroup w of
 // G = max(1, min(gridDim.x, T)) owns [w T / G, (w + 1) T / G) (every range
 // is then non-empty unless T = 0; workgroups w >= G have none). For each
-// pair that intersects the range, in pair order, the whole workgroup calls
-// visit(p, S_p, count(p), lo, hi, T, G); with kEmpty, also for each empty
-// pair whose S_p the range holds (S_p = T: the last range).
+// pair whose items intersect the range, in pair order, the whole workgroup
+// calls visit(p, S_p, count(p), lo, hi, T, G) (the pair's items: count(p) +
+// C from S_p); with kEmpty, also for each empty pair whose S_p the range
+// holds (S_p = T: the last range).
 // count(p) is called by one thread per pass; it must return the same value
-// each time, with T < 2^31. Pass 1 sums the counts over the workgroup; pass 2
-// has wave 0 scan them 64 pairs at a time and list the pairs of the range.
-template <bool kEmpty, class Count, class Visit>
+// each time, with T < 2^31. Pass 1 sums the counts over the workgroup;
+// pass 2 scans them NT pairs at a time (one count per thread, a workgroup
+// prefix sum) and lists the pairs of the range.
+template <bool kEmpty, int C, class Count, class Visit>
 __device__ void plan_walk(int pairs, PlanWalkLds& sh, Count count, Visit visit) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   // pass 1: the total
+  auto items = [&](int n) { return n > 0 ? n + C : 0; };
   int mine = 0;
-  for (int p = tid; p < pairs; p += NT) mine += count(p);
+  for (int p = tid; p < pairs; p += NT) mine += items(count(p));
   {
     const int incl = wave_incl_scan_dpp(mine);
     if (lane == 63) sh.wtot[wave] = incl;
@@ -77,41 +106,52 @@ __device__ void plan_walk(int pairs, PlanWalkLds& sh, Count count, Visit visit) 
 #pragma unroll
   for (int w = 0; w < NW; ++w) T += sh.wtot[w];
   T = __builtin_amdgcn_readfirstlane(T);   // uniform: keep it (and what follows) scalar
+  __syncthreads();   // wtot is rewritten by pass 2
   const int G = T < 1 ? 1 : ((int)gridDim.x < T ? (int)gridDim.x : T);
   const int w = blockIdx.x;
   if (w >= G) return;
   const int lo = (int)((long long)w * T / G), hi = (int)((long long)(w + 1) * T / G);
-  // pass 2: the pairs of [lo, hi), 64 at a time
-  int base = 0;   // S of the chunk's first pair (wave 0's copy is the one used)
-  for (int c = 0; c < pairs; c += kWave) {
-    if (wave == 0) {
-      const int p = c + lane;
-      const int n = p < pairs ? count(p) : 0;
-      const int incl = wave_incl_scan_dpp(n);
-      const int s = base + incl - n;
-      const bool hit = n > 0 ? (s < hi && s + n > lo)
-                             : (kEmpty && p < pairs && ((s >= lo && s < hi) || (s == T && w == G - 1)));
-      const unsigned long long m = __ballot(hit);
-      if (hit) {
-        const int i = mbcnt(m);
-        sh.hit_p[i] = p;
-        sh.hit_s[i] = s;
-        sh.hit_n[i] = n;
-      }
-      if (lane == 0) sh.nhit = __popcll(m);
-      base += __builtin_amdgcn_readlane(incl, 63);
-      if (lane == 0) sh.next = base;
-    }
+  // pass 2: the pairs of [lo, hi), NT at a time
+  int base = 0;   // S of the chunk's first pair
+  for (int c = 0; c < pairs; c += NT) {
+    const int p = c + tid;
+    const int n = p < pairs ? count(p) : 0;
+    const int ni = items(n);
+    const int incl = wave_incl_scan_dpp(ni);
+    if (lane == 63) sh.wtot[wave] = incl;
     __syncthreads();
-    const int nh = __builtin_amdgcn_readfirstlane(sh.nhit);
-    const int next = __builtin_amdgcn_readfirstlane(sh.next);
-    for (int i = 0; i < nh; ++i)
-      visit(__builtin_amdgcn_readfirstlane(sh.hit_p[i]), __builtin_amdgcn_readfirstlane(sh.hit_s[i]),
-            __builtin_amdgcn_readfirstlane(sh.hit_n[i]), lo, hi, T, G);
-    __syncthreads();   // the list is rewritten by the next chunk
+    int pre = 0, ctot = 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+      const int v = sh.wtot[u];
+      pre += u < wave ? v : 0;
+      ctot += v;
+    }
+    const int s = base + pre + incl - ni;
+    const bool hit = n > 0 ? (s < hi && s + ni > lo)
+                           : (kEmpty && p < pairs && ((s >= lo && s < hi) || (s == T && w == G - 1)));
+    const unsigned long long m = __ballot(hit);
+    if (hit) {
+      const int i = wave * kWave + mbcnt(m);
+      sh.hit_p[i] = p;
+      sh.hit_s[i] = s;
+      sh.hit_n[i] = n;
+    }
+    if (lane == 0) sh.wcnt[wave] = __popcll(m);
+    __syncthreads();
+    for (int u = 0; u < NW; ++u) {
+      const int nh = __builtin_amdgcn_readfirstlane(sh.wcnt[u]);
+      for (int i = 0; i < nh; ++i) {
+        const int j = u * kWave + i;
+        visit(__builtin_amdgcn_readfirstlane(sh.hit_p[j]), __builtin_amdgcn_readfirstlane(sh.hit_s[j]),
+              __builtin_amdgcn_readfirstlane(sh.hit_n[j]), lo, hi, T, G);
+      }
+    }
+    __syncthreads();   // the lists and wtot are rewritten by the next chunk
+    base += __builtin_amdgcn_readfirstlane(ctot);
     // later pairs start at or past hi: none is ours, except empty pairs at T
     // for the last range
-    if (next >= hi && !(kEmpty && hi == T)) break;
+    if (base >= hi && !(kEmpty && hi == T)) break;
   }
 }
 
@@ -130,7 +170,7 @@ __device__ __forceinline__ int cand_tiles(const ReqGeom& geo) {
 }
 
 template <int D, bool kBounds>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(LS_PLAN_SCORE_WAVES_PER_EU)))
 void plan_score_kernel(PlanArgs f) {
   __shared__ ScoreLds<D> sh;
   const ScoreArgs& sa = f.sa;
@@ -152,8 +192,8 @@ void plan_score_kernel(PlanArgs f) {
     const int r = p / HKV, g = p - r * HKV;
     const ReqGeom geo = req_geom(sa.b, r, sa.n_sink, sa.n_recent);
     const int t0 = geo.c0 / 16;
-    const int ta = (lo > s ? lo : s) - s, te = (hi < s + n ? hi : s + n) - s;
-    float* row = f.rows + (size_t)p * sa.b.max_blocks;
+    const int ta = (lo > s ? lo : s) - s, te = (hi < s + n ? hi : s + n) - s;   // ta >= te:
+    float* row = f.rows + (size_t)p * sa.b.max_blocks;                          // none
     for (int a = ta; a < te; a += kPlanSubTiles) {
       const int b = te < a + kPlanSubTiles ? te : a + kPlanSubTiles;
       ReqGeom cg = geo;
@@ -165,12 +205,12 @@ void plan_score_kernel(PlanArgs f) {
         item_score_bounds<D, kPlanMaxBlocks, kStoreGlobal, NW>(sa, r, g, cg, sh.pg, row, sh.stage,
                                                                nullptr, cg.c0);
       else
-        item_score<D, kPlanMaxBlocks, kStoreGlobal, NW>(sa, r, g, cg, sh.pg, row, sh.stage,
-                                                        nullptr, cg.c0);
+        item_score<D, kPlanMaxBlocks, kStoreGlobal, NW, kPlanScorePrefetch>(
+            sa, r, g, cg, sh.pg, row, sh.stage, nullptr, cg.c0);
       __syncthreads();   // pg and the staging tiles are reused
     }
   };
-  plan_walk<false>(f.pairs, sh.walk, count, visit);
+  plan_walk<false, kPlanScoreVisit>(f.pairs, sh.walk, count, visit);
 }
 
 // ------------------------------------------------------------- ranking ----
@@ -229,7 +269,21 @@ __attribute__((amdgpu_waves_per_eu(MAXC <= 8192 ? 4 : 2))) void plan_rank_kernel
     mx = fmaxf(mx, sh.red[1][w]);
   }
   int32_t* sel = ta.selected + (size_t)pair * ta.max_selected;
-  auto emit = [&](int p, int b) { sel[p] = b; };
+  int32_t* ent = f.ents ? f.ents + (size_t)pair * ta.max_selected : nullptr;
+  const int32_t* pages = ta.b.indices + geo.page_base;
+  auto emit = [&](int p, int b) {
+    sel[p] = b;
+    if (ent && b >= 0) {   // the attention's walk entry of position p (never 0); the
+                           // positions past the selection are never read, left 0
+      int e = -1;
+      if (b >= 0 && b < geo.nb) {
+        const int pg = pages[b];
+        const int nt = geo.L - b * 16 < 16 ? geo.L - b * 16 : 16;
+        if (pg >= 0 && pg < ta.b.num_pages && nt > 0) e = pg * 32 + nt;
+      }
+      ent[p] = e;
+    }
+  };
   const int stored = topk_fast<NPT, RT>(sh.sc, geo, topk_budget(ta, geo), ta.max_selected, sh.tf,
                                         sh.tk, sel, ta.selected_count + pair, mn, mx, emit);
   if (tid == 0) ta.selected_count[pair] = stored;
@@ -275,7 +329,7 @@ __device__ __forceinline__ int range_lo(int w, int T, int G) {
 }
 
 template <int D, bool kDense>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(LS_PLAN_ATTN_WAVES_PER_EU)))
 void plan_attn_kernel(PlanArgs f) {
   __shared__ AttnLds<D> sh;
   constexpr int EPT = item_ept<D, NW>();
@@ -312,6 +366,7 @@ void plan_attn_kernel(PlanArgs f) {
     const ReqGeom geo = req_geom(a.b, r, 0, 0);
     const int32_t* pages = a.b.indices + geo.page_base;
     const int32_t* srow = kDense ? nullptr : a.selected + (size_t)p * a.max_selected;
+    int32_t* erow = kDense || !f.ents ? nullptr : f.ents + (size_t)p * a.max_selected;
     const int pa = (lo > s ? lo : s) - s, pe = (hi < s + n ? hi : s + n) - s;
     float M[EPT], O[EPT], L[EPT];   // the running state of the pair's passes
 #pragma unroll
@@ -325,11 +380,16 @@ void plan_attn_kernel(PlanArgs f) {
       for (int pos = tid; pos < item_entry_count<NW>(cnt); pos += NT) {
         int e = -1;
         if (pos < cnt) {
-          const int blk = kDense ? q0 + pos : srow[q0 + pos];
-          if (blk >= 0 && blk < geo.nb) {
-            const int pg = pages[blk];
-            const int nt = geo.L - blk * 16 < 16 ? geo.L - blk * 16 : 16;
-            if (pg >= 0 && pg < a.b.num_pages && nt > 0) e = pg * 32 + nt;
+          if (!kDense && erow) {   // written by the ranker (one load), reset to 0
+            e = erow[q0 + pos];
+            erow[q0 + pos] = 0;
+          } else {
+            const int blk = kDense ? q0 + pos : srow[q0 + pos];
+            if (blk >= 0 && blk < geo.nb) {
+              const int pg = pages[blk];
+              const int nt = geo.L - blk * 16 < 16 ? geo.L - blk * 16 : 16;
+              if (pg >= 0 && pg < a.b.num_pages && nt > 0) e = pg * 32 + nt;
+            }
           }
         }
         sh.ent[pos] = e;
@@ -342,7 +402,8 @@ void plan_attn_kernel(PlanArgs f) {
       for (int j = 0; j < EPT; ++j) fold_state(M[j], O[j], L[j], st.m[j], st.o[j], st.l[j]);
       __syncthreads();   // the entries and the attention LDS are reused
     }
-    if (pa == 0 && pe == n) {   // the whole pair is in this range (or it is empty)
+    const int ni = n > 0 ? n + kPlanAttnVisit : 0;   // the pair's items in the plan
+    if (lo <= s && s + ni <= hi) {   // the whole pair is in this range (or it is empty)
       write_out(r, g, M, O, L);
       return;
     }
@@ -364,7 +425,7 @@ void plan_attn_kernel(PlanArgs f) {
     }
     wait_stores();   // this thread's words have reached the device-coherent level
     __syncthreads();
-    const int w0 = range_of(s, T, G), w1 = range_of(s + n - 1, T, G);
+    const int w0 = range_of(s, T, G), w1 = range_of(s + ni - 1, T, G);
     if (tid == 0) sh.flag = arrive_last(f.ctl + kPlanCtlWords + p, w1 - w0 + 1);
     __syncthreads();
     if (!sh.flag) return;
@@ -417,7 +478,7 @@ void plan_attn_kernel(PlanArgs f) {
     }
     write_out(r, g, M, O, L);
   };
-  plan_walk<true>(f.pairs, sh.walk, count, visit);
+  plan_walk<true, kPlanAttnVisit>(f.pairs, sh.walk, count, visit);
 }
 
 hipError_t launch_rank(const PlanArgs& p, hipStream_t st) {

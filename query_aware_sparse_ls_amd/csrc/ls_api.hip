@@ -235,7 +235,8 @@ Route route(const ls_pool& pool, const ls_batch& batch, int num_q_heads) {
 
 ls::PlanArgs plan_args(const ls::ScoreArgs& sa, const ls::TopkArgs& ta, const ls::AttnArgs& aa,
                        const ls::SummaryUpdate& up, int pairs, int max_blocks, char* w,
-                       size_t rows_off, size_t slots_off, float* scores_out) {
+                       size_t rows_off, size_t slots_off, float* scores_out,
+                       size_t ents_off = 0) {
   ls::PlanArgs p;
   p.sa = sa;
   p.ta = ta;
@@ -244,6 +245,7 @@ ls::PlanArgs plan_args(const ls::ScoreArgs& sa, const ls::TopkArgs& ta, const ls
   p.rows = scores_out ? scores_out : reinterpret_cast<float*>(w + rows_off);
   p.zero_rows = scores_out == nullptr;
   p.ta.scores = p.rows;
+  p.ents = ents_off ? reinterpret_cast<int32_t*>(w + ents_off) : nullptr;
   p.ctl = reinterpret_cast<uint32_t*>(w);
   p.slots = reinterpret_cast<float*>(w + slots_off);
   p.pairs = pairs;
@@ -362,9 +364,11 @@ ls_status run_step(const void* q, int32_t num_q_heads, void* summaries, const vo
   }
   if (rt == kRoutePlan) {
     // the selection calls, then the attention call, as ls_score_select and
-    // ls_sparse_attn_decode run them (same kernels, same bits)
+    // ls_sparse_attn_decode run them (same kernels, same bits; the ranker
+    // also writes the selection's walk entries, which the attention reads
+    // instead of the selection and the page table)
     const ls::PlanArgs pa = plan_args(sa, ta, aa, up, batch.batch_size * pool.num_heads,
-                                      batch.max_blocks, w, lay.rows, lay.parts, nullptr);
+                                      batch.max_blocks, w, lay.rows, lay.parts, nullptr, lay.ents);
     hipError_t e = ls::launch_plan_select(pa, stream);
     if (e == hipSuccess) e = ls::launch_plan_attend(pa, stream);
     return hip_status(e, "decode-step kernel launches");

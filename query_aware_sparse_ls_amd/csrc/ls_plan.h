@@ -19,8 +19,16 @@ namespace ls {
 constexpr int kPlanWaves = 4;
 constexpr int kPlanThreads = kPlanWaves * kWave;   // scoring and attention workgroups
 constexpr int kPlanRankThreads = 512;              // ranking workgroups (one per pair)
-constexpr int kPlanScoreGrid = 1024;               // scoring workgroups per call
-constexpr int kPlanAttnGrid = 1024;                // attention workgroups per call
+// Workgroups per call (measured on MI355X): scoring, four per CU; attention,
+// two per CU with two K/V blocks in flight per wave.
+#ifndef LS_PLAN_SCORE_GRID
+#define LS_PLAN_SCORE_GRID 1024
+#endif
+#ifndef LS_PLAN_ATTN_GRID
+#define LS_PLAN_ATTN_GRID 512
+#endif
+constexpr int kPlanScoreGrid = LS_PLAN_SCORE_GRID;   // scoring workgroups per call
+constexpr int kPlanAttnGrid = LS_PLAN_ATTN_GRID;     // attention workgroups per call
 constexpr int kPlanSubTiles = 16;                  // tiles per scoring pass (256 blocks)
 constexpr int kPlanSubPositions = 64;              // positions per attention pass
 constexpr int kPlanMaxBlocks = 16384;              // blocks per request
@@ -34,6 +42,9 @@ struct PlanArgs {
   SummaryUpdate up;
   float* rows;          // [pairs][max_blocks] block scores (the caller's scores_out, or scratch)
   bool zero_rows;       // the ranker leaves the rows it read zero (scratch rows)
+  int32_t* ents;        // step: [pairs][max_selected] walk entries the ranker writes
+                        // beside the selection (page * 32 + tokens, -1: none), which
+                        // the attention reads and resets to 0; null otherwise
   uint32_t* ctl;        // kPlanCtlWords words, then one arrival counter per pair
   float* slots;         // [2 * kPlanAttnGrid][4][D + 2] partial states of split pairs
   int32_t pairs;
