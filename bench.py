@@ -888,7 +888,7 @@ def bench_dense(args, window: bool = False) -> int:
     nbytes["total"] = sum(nbytes.values())
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
     key = "attn_window_kernel.llama8b_32k_b16_window" if window else \
-        "attn_chunk_kernel.llama8b_32k_b16_dense"
+        "plan_attn_kernel.llama8b_32k_b16_dense"
     tr = stored_traffic(key)
     res = {"metric": ("sink + recent window decode attention calls/sec at 8B/32K/B16" if window
                       else "dense (k = all) split-K decode attention calls/sec at 8B/32K/B16"),
@@ -900,9 +900,9 @@ def bench_dense(args, window: bool = False) -> int:
                       "page_size": P, "replicas": R, "timing": "eager, back-to-back calls",
                       **({"n_sink": N_SINK, "window": WIN} if window else {})},
            "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
-           "roofline": {"kernel": ("ls::attn_window_kernel<128>" if window else
-                                   "ls::attn_chunk_kernel<128>") +
-                                  " + ls::attn_combine_kernel<128> (one library call)",
+           "roofline": {"kernel": ("ls::attn_window_kernel<128> + ls::attn_combine_kernel<128> "
+                                   "(one library call)" if window else
+                                   "ls::plan_attn_kernel<128, true> (one launch)"),
                         "bound": "hbm",
                         "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(gbps / HBM_PEAK_GBPS, 4),
@@ -989,8 +989,8 @@ def bench_snapkv(args) -> int:
                       "budget": BUD, "replicas": R, "timing": "eager, back-to-back calls"},
            "one_time_select_and_gather_ms": [round(x, 3) for x in sel_ms],
            "step_bytes": nbytes,
-           "roofline": {"kernel": "ls::attn_chunk_kernel<128> + ls::attn_combine_kernel<128> "
-                                  "(one library call over the gathered buffer)", "bound": "hbm",
+           "roofline": {"kernel": "ls::plan_attn_kernel<128, true> "
+                                  "(one launch over the gathered buffer)", "bound": "hbm",
                         "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                         "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)},
@@ -1241,7 +1241,7 @@ def dense_cell(reps, sm_scale, nbytes, steps):
         inp = reps[i]["inp"]
         ls.sparse_attn_decode(inp.q, inp.k_pool, inp.v_pool, reps[i]["batch"], None, None,
                               sm_scale=sm_scale, out=out, workspace=ws[i])
-    return Cell("dense", fn, nbytes, steps, "ls::attn_chunk_kernel")
+    return Cell("dense", fn, nbytes, steps, "ls::plan_attn_kernel<128, true>")
 
 
 def make_session(args, dev, block=None):

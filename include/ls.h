@@ -221,10 +221,14 @@ ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_
  *                 call leaves it zero, see "Workspaces" below).
  * Execution: one workgroup per (request, kv head) pair scores and ranks it
  *                 in LDS when there are at least 64 pairs of at most 4096
- *                 blocks; other shapes of at most 8192 blocks take one
- *                 launch in which workgroups score chunks of 64-128 blocks
- *                 and the pair's last chunk ranks it; longer requests take a
- *                 scoring kernel and a top-k kernel.
+ *                 blocks. At least 64 pairs of longer requests (or fewer
+ *                 pairs of more than 8192 blocks) take two launches planned
+ *                 from the lengths: the candidate summary tiles of all pairs
+ *                 are cut into equal ranges, one per scoring workgroup, then
+ *                 one workgroup per pair ranks it. Fewer pairs of at most
+ *                 8192 blocks take one launch in which workgroups score
+ *                 chunks of 64-128 blocks and the pair's last chunk ranks it.
+ *                 Other shapes take a scoring kernel and a top-k kernel.
  * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
  *            page_size 16; max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192,
  *            num_pages < 2^26).
@@ -250,14 +254,19 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
  *   lse_out[r][h] = M + ln sum_t e^{z_t - M}
  * with fp32 logits, softmax and accumulation; partial softmax states over
  * disjoint token sets are merged by log-sum-exp in a fixed order
- * (deterministic). A selection (requests of at most 8192 blocks) is split
- * over workgroups of at most 16 selected blocks per (request, kv head) pair;
- * each writes its partial softmax state to the workspace and the last of a
- * pair's workgroups to finish merges them in split order, in the same
- * launch. The dense path splits each pair into runs of up to 512 blocks
- * whose states a second kernel merges (split-K); longer requests take the
- * split-K kernels of 8 blocks per split. An empty T gives out = 0 and
- * lse = -inf. The output is rounded once (nearest-even) to out_dtype.
+ * (deterministic). Batches of at least 64 pairs whose requests exceed 4096
+ * blocks, and the dense path of at least 64 pairs, are planned from the
+ * counts: the positions of all pairs (selected blocks, or every block) are
+ * cut into equal ranges, one per workgroup of a fixed grid; a pair inside
+ * one range is written by its workgroup, a pair cut by range ends is merged
+ * in range order by the last of its workgroups to finish. Other selections
+ * (requests of at most 8192 blocks) are split over workgroups of at most 16
+ * selected blocks per (request, kv head) pair, merged the same way by the
+ * pair's last workgroup. The dense path of fewer pairs splits each pair
+ * into runs of up to 512 blocks whose states a second kernel merges
+ * (split-K); longer requests take the split-K kernels of 8 blocks per split.
+ * An empty T gives out = 0 and lse = -inf. The output is rounded once
+ * (nearest-even) to out_dtype.
  * For a selection written by ls_score_select the entries past the count are
  * -1; other callers may leave them undefined (they are never read as blocks).
  *
@@ -326,11 +335,14 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
  *   aligned (block scores, walk entries, split states); zero-filled before
  *   its first use, and every call leaves it zero; calls that run
  *   concurrently need separate workspaces.
+ * Execution: the routes of ls_score_select and ls_sparse_attn_decode. One
+ *   launch for at least 64 pairs of at most 4096 blocks (one workgroup per
+ *   pair, the refresh in extra workgroups) and for fewer pairs of at most
+ *   8192 blocks (pairs spread over many workgroups, hand-offs inside the
+ *   launch); otherwise the planned route's three launches (scoring with the
+ *   refresh, ranking, attention), with the same results as the two calls.
  * Supported: head_dim 64 or 128; GQA group 4; page_size 16;
- *   max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192 and num_pages < 2^26;
- *   bounds of requests of more than 4096 blocks in batches of at most 256
- *   (request, kv head) pairs take three launches: bounds refresh,
- *   selection, attention).
+ *   max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192 and num_pages < 2^26).
  */
 size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_heads,
                                             int32_t num_kv_heads, int32_t head_dim,

@@ -612,8 +612,8 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                     selected_count, max_selected, ls_attn_num_splits(cap),
                                     sm_scale, partials, out, out_dtype, lse_out);
   // a selection: split over several workgroups per pair, merged by the last
-  // one to finish; the dense path (every block) is split-K over runs of up
-  // to 512 blocks, merged by a second kernel
+  // one to finish; the dense path (every block) of few pairs is split-K over
+  // runs of up to 512 blocks, merged by a second kernel
   const Route rt = route(pool, batch, num_q_heads);
   if (selected && rt == kRouteItem)
     return hip_status(ls::launch_attn_item(aa, stream), "attention kernel launch");
@@ -623,10 +623,15 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                      max_selected, w, 0, 0, lay.parts, nullptr);
     return hip_status(ls::launch_flow(f, ls::kFlowAttend, stream), "attention kernel launch");
   }
-  if (rt == kRoutePlan) {   // a selection, or every block (dense)
+  // every block (dense) of at least kItemMinPairs pairs: the planned
+  // kernel too (ranges balanced over the pairs, whatever their lengths)
+  const int pairs = batch.batch_size * pool.num_heads;
+  const bool plan_dense = !selected && pairs >= ls::kItemMinPairs &&
+                          ls::plan_ok(num_q_heads / pool.num_heads, pool.head_dim,
+                                      batch.max_blocks, pool.num_pages, pairs);
+  if (rt == kRoutePlan || plan_dense) {   // a selection, or every block (dense)
     const ls::PlanArgs pa = plan_args(ls::ScoreArgs{}, ls::TopkArgs{}, aa, ls::SummaryUpdate{},
-                                      batch.batch_size * pool.num_heads, batch.max_blocks, w, 0,
-                                      lay.parts, nullptr);
+                                      pairs, batch.max_blocks, w, 0, lay.parts, nullptr);
     return hip_status(ls::launch_plan_attend(pa, stream), "attention kernel launch");
   }
   hipError_t e = (!selected && pool.num_pages < (1 << 26)) ? ls::launch_attn_chunked(aa, stream)
