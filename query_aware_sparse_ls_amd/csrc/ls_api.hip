@@ -1012,7 +1012,7 @@ ls_status ls_window_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
 namespace {
 
 struct SnapLayout {
-  size_t stats, rowstat, scores, keys, vals, skeys, svals, seg, sort, total;
+  size_t stats, rowstat, scores, keys, total;
 };
 
 SnapLayout snap_layout(int batch_size, int num_kv_heads, int max_len) {
@@ -1025,11 +1025,6 @@ SnapLayout snap_layout(int batch_size, int num_kv_heads, int max_len) {
   l.rowstat = o; o += align_up(pairs * ls::kSnapMaxObs * 4 * 2 * sizeof(float));
   l.scores = o;  o += align_up(cells * sizeof(float));
   l.keys = o;    o += align_up(cells * sizeof(float));
-  l.vals = o;    o += align_up(cells * sizeof(int32_t));
-  l.skeys = o;   o += align_up(cells * sizeof(float));
-  l.svals = o;   o += align_up(cells * sizeof(int32_t));
-  l.seg = o;     o += align_up(2 * pairs * sizeof(int32_t));
-  l.sort = o;    o += align_up(ls::snap_sort_bytes((int)pairs, max_len));
   l.total = o;
   return l;
 }
@@ -1090,13 +1085,6 @@ ls_status ls_snapkv_select(const void* q_obs, int32_t q_dtype, int32_t num_q_hea
   a.rowstat = reinterpret_cast<float*>(w + l.rowstat);
   a.scores = scores_out ? scores_out : reinterpret_cast<float*>(w + l.scores);
   a.keys = reinterpret_cast<float*>(w + l.keys);
-  a.vals = reinterpret_cast<int32_t*>(w + l.vals);
-  a.sorted_keys = reinterpret_cast<float*>(w + l.skeys);
-  a.sorted_vals = reinterpret_cast<int32_t*>(w + l.svals);
-  a.seg_begin = reinterpret_cast<int32_t*>(w + l.seg);
-  a.seg_end = a.seg_begin + pairs;
-  a.sort_tmp = w + l.sort;
-  a.sort_bytes = l.total - l.sort;
   a.selected = selected;
   a.counts = counts;
   return hip_status(ls::launch_snapkv_select(a, stream), "SnapKV selection launches");

@@ -191,20 +191,12 @@ struct SnapArgs {
   float* stats;              // [pairs][n_chunks][4 kSnapMaxObs][2]
   float* rowstat;            // [pairs][4 kSnapMaxObs][2]
   float* scores;             // [pairs][max_len]
-  float* keys;               // [pairs][max_len] sort keys / values, then sorted
-  int32_t* vals;
-  float* sorted_keys;
-  int32_t* sorted_vals;
-  int32_t* seg_begin;        // [pairs]
-  int32_t* seg_end;
-  void* sort_tmp;
-  size_t sort_bytes;
+  float* keys;               // [pairs][max_len] the candidates' averaged scores
   int32_t* selected;         // [pairs][budget]
   int32_t* counts;           // [pairs]
   uint16_t* k_out;           // gather: [pairs][budget_pad][D]
   uint16_t* v_out;
 };
-size_t snap_sort_bytes(int pairs, int max_len);
 hipError_t launch_snapkv_select(const SnapArgs& a, hipStream_t st);
 hipError_t launch_snapkv_gather(const SnapArgs& a, int budget_pad, hipStream_t st);
 
