@@ -915,6 +915,72 @@ def bench_dense(args, window: bool = False) -> int:
     return 0
 
 
+def bench_summaries(args) -> int:
+    """Full summary builds: the block means of every complete page of the
+    16 x 32K bf16 key cache (8 KV heads, D 128: 1.07 GB read, 67 MB written),
+    and of the fp8 indexer key cache of 4 x 950K tokens in 64-token pages
+    (128 B per token plus its fp32 scale), each timed over back-to-back
+    builds alternating two replicas between HIP events."""
+    import torch
+    import query_aware_sparse_ls_amd as ls
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    res = {"metric": "block summary build GB/s (% of HBM peak)", "unit": "GB/s", "n_gpus": 1,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": "summaries: 16 x 32K bf16 keys (8 kv "
+                                                        "heads, D 128, 16-token pages); 4 x 950K "
+                                                        "fp8 indexer keys (64-token pages)"}}
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    # bf16: 16 x 2048 pages x 8 heads x 16 tokens x 128 dims
+    num_pages, H, P, D = 16 * 2048, 8, 16, 128
+    keys = [torch.randn(num_pages, H, P, D, generator=g, device=dev).to(torch.bfloat16)
+            for _ in range(2)]
+    ids = torch.randperm(num_pages, device=dev).to(torch.int32)
+    outs = [torch.empty(num_pages, H, D, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    ms = timed(lambda i: ls.build_block_summaries(keys[i % 2], ids, outs[i % 2]), max(4, args.steps // 20))
+    nbytes = num_pages * H * P * D * 2 + num_pages * H * D * 2 + num_pages * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res["value"] = round(gbps, 1)
+    res["bf16_build"] = {"ms": round(ms, 5), "bytes": nbytes, "GBps": round(gbps, 1),
+                         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+    res["roofline"] = {"kernel": "ls::summaries_bf16_kernel<128, false, 16>", "bound": "hbm",
+                       "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                       "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}
+    del keys, outs
+    torch.cuda.empty_cache()
+    # fp8 indexer keys: 4 x 15,200 pages of 64 tokens x 128 bytes, fp32 scales
+    npg, P8 = 4 * 15200, 64
+    k8 = [torch.randint(0, 0x7e, (npg, P8, 128), generator=g, device=dev, dtype=torch.int32)
+          .to(torch.uint8) for _ in range(2)]
+    sc = [torch.rand(npg, P8, generator=g, device=dev) for _ in range(2)]
+    ids8 = torch.arange(npg, dtype=torch.int32, device=dev)
+    o8 = [torch.empty(npg, 128, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    ms8 = timed(lambda i: ls.build_block_summaries(k8[i % 2].view(torch.float8_e4m3fn), ids8,
+                                                   o8[i % 2], key_scales=sc[i % 2]),
+                max(4, args.steps // 20))
+    nb8 = npg * P8 * (128 + 4) + npg * 128 * 2 + npg * 4
+    g8 = nb8 / (ms8 * 1e-3) / 1e9
+    res["fp8_indexer_build"] = {"ms": round(ms8, 5), "bytes": nb8, "GBps": round(g8, 1),
+                                "pct_of_hbm_peak": round(100 * g8 / HBM_PEAK_GBPS, 2)}
+    res["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_snapkv(args) -> int:
     """SnapKV-style selection on the 8B/32K/B16 batch: the one-time selection
     (64 observation queries, 4 sinks, budget 30% of the context) and gather,
@@ -1612,7 +1678,7 @@ def main(argv=None) -> int:
     ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
                     help="block-topk path: block-mean summaries (default) or Quest bounds")
     ap.add_argument("--path", choices=("block-topk", "ragged", "indexer", "coarse-to-fine",
-                                       "dense", "pq", "window", "snapkv"),
+                                       "dense", "pq", "window", "snapkv", "summaries"),
                     default="block-topk",
                     help="block-topk: the 8B/32K/B16 block top-k step (default); ragged: the "
                          "batch-64 sweep, lengths 2K-128K, keep 1/64, 1/16, 1/4 and k = all; "
@@ -1634,6 +1700,8 @@ def main(argv=None) -> int:
         return copy_calibration(args.copy_calibrate)
     if args.path == "snapkv":
         return bench_snapkv(args)
+    if args.path == "summaries":
+        return bench_summaries(args)
     if args.path in ("dense", "window"):
         return bench_dense(args, window=args.path == "window")
     if args.path in ("block-topk", "ragged"):

@@ -143,7 +143,8 @@ typedef struct ls_select_params {
  * division is exact, and the mean is rounded ONCE, to nearest-even, to
  * summary_dtype.
  *
- * keys:        key pool, layout HND (see above), dtype key_pool.dtype.
+ * keys:        key pool, layout HND (see above), dtype key_pool.dtype;
+ *              16-byte aligned.
  * key_scales:  NULL for bf16 keys. For LS_DTYPE_FP8_E4M3FN keys: per-token
  *              dequantisation scale, fp32 [num_pages][page_size] (the summand
  *              is key_scales[p][s] * keys[p][h][s][d]); key_pool.num_heads
@@ -152,8 +153,10 @@ typedef struct ls_select_params {
  * page_ids:    [n_pages] physical page ids to (re)summarise (complete pages).
  * n_pages:     >= 0; 0 enqueues nothing.
  * summaries:   [key_pool.num_pages][key_pool.num_heads][head_dim] of
- *              summary_dtype (LS_DTYPE_BF16 or LS_DTYPE_FP32); only the rows
- *              of the listed pages are written.
+ *              summary_dtype (LS_DTYPE_BF16 or LS_DTYPE_FP32), 16-byte
+ *              aligned; only the rows of the listed pages are written.
+ * Errors: LS_ERR_INVALID for a null or misaligned pointer, LS_ERR_UNSUPPORTED
+ *   for a geometry or dtype outside the sets above.
  */
 ls_status ls_build_block_summaries(const void* keys, const float* key_scales,
                                    ls_pool key_pool, const int32_t* page_ids,
@@ -169,11 +172,11 @@ ls_status ls_build_block_summaries(const void* keys, const float* key_scales,
  * for every listed page p and head h. Exact (a copy of bf16 values). Keys
  * are taken to be finite.
  *
- * keys:     bf16 key pool, layout HND; key_pool.dtype = LS_DTYPE_BF16,
- *           page_size in {16, 32, 64}, head_dim in {64, 128}.
+ * keys:     bf16 key pool, layout HND, 16-byte aligned; key_pool.dtype =
+ *           LS_DTYPE_BF16, page_size in {16, 32, 64}, head_dim in {64, 128}.
  * page_ids: [n_pages] physical page ids (complete pages); n_pages >= 0.
- * bounds:   bf16 [key_pool.num_pages][key_pool.num_heads][2][head_dim];
- *           only the rows of the listed pages are written.
+ * bounds:   bf16 [key_pool.num_pages][key_pool.num_heads][2][head_dim],
+ *           16-byte aligned; only the rows of the listed pages are written.
  */
 ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_t* page_ids,
                                 int32_t n_pages, void* bounds, hipStream_t stream);

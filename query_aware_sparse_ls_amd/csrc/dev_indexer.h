@@ -125,12 +125,4 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(b > 0 ? b : 0);
 }
 
-// bf16 pair of fp8 bytes 0,1 (hi = false) or 2,3 (hi = true) of x, exact.
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x, bool hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true)
-                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 }  // namespace ls

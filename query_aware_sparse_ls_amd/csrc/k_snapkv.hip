@@ -117,27 +117,30 @@ __global__ __launch_bounds__(kSnapChunk) void snap_stats_kernel(SnapArgs a) {
   const int rows = a.n_obs * 4;
   for (int rt = 0; rt < (rows + 15) / 16; ++rt) {
     const int w = rt * 4 + (lane >> 4);
-    float m[4], s[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      m[jj] = -__builtin_huge_valf();
-      s[jj] = 0.0f;
-    }
+    // this lane's logits (4 rows x 4 positions), masked; then per row the
+    // maximum over the row group's 64 positions and the sum of exp2(z - max)
+    float z[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const f32x4_t z = snap_logits<D>(q_lds, rt, kb[t]);
+      const f32x4_t zt = snap_logits<D>(q_lds, rt, kb[t]);
       const int p = p0 + t * 16 + (lane & 15);
       const bool ok = ((okm >> t) & 1u) && w < a.n_obs && p <= Lc - a.n_obs + w;   // causal
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        if (ok) snap_merge(m[jj], s[jj], z[jj] * a.sm_scale_log2, 1.0f);
+      for (int jj = 0; jj < 4; ++jj) z[t][jj] = ok ? zt[jj] * a.sm_scale_log2 : -__builtin_huge_valf();
     }
-    // over the 16 positions of the lane's row group, then to LDS
+    float m[4], s[4];
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
+    for (int jj = 0; jj < 4; ++jj) {
+      m[jj] = fmaxf(fmaxf(z[0][jj], z[1][jj]), fmaxf(z[2][jj], z[3][jj]));
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        snap_merge(m[jj], s[jj], __shfl_xor(m[jj], off, kWave), __shfl_xor(s[jj], off, kWave));
+      for (int off = 1; off < 16; off <<= 1) m[jj] = fmaxf(m[jj], __shfl_xor(m[jj], off, kWave));
+      s[jj] = 0.0f;
+      if (m[jj] != -__builtin_huge_valf()) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[jj] += exp2f(z[t][jj] - m[jj]);
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) s[jj] += __shfl_xor(s[jj], off, kWave);
     }
     if ((lane & 15) == 0 && w < a.n_obs) {
 #pragma unroll
@@ -383,11 +386,14 @@ __global__ __launch_bounds__(kSnapSelThreads) void snap_select_kernel(SnapArgs a
   if (tid == 0) a.counts[pair] = stot;
 }
 
+// Kept rows into the contiguous buffers: each lane moves 16 bytes of K and of
+// V; a 256-thread workgroup covers 256 * 8 / D positions.
 template <int D>
 __global__ __launch_bounds__(256) void snap_gather_kernel(SnapArgs a, int budget_pad) {
-  // one wave per kept position: D bf16 of K and of V
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6), g = blockIdx.y, r = blockIdx.z;
-  const int lane = threadIdx.x & 63;
+  constexpr int LPP = D / 8;            // lanes per position (16 or 8)
+  constexpr int PPW = 256 / LPP;        // positions per workgroup
+  const int g = blockIdx.y, r = blockIdx.z;
+  const int i = blockIdx.x * PPW + threadIdx.x / LPP, c = threadIdx.x % LPP;
   if (i >= budget_pad) return;
   const ReqGeom geo = req_geom(a.b, r, 0, 0);
   const size_t pair = (size_t)r * a.num_kv_heads + g;
@@ -396,16 +402,12 @@ __global__ __launch_bounds__(256) void snap_gather_kernel(SnapArgs a, int budget
   int page = -1;
   if (t >= 0 && t < geo.L && t / 16 < geo.nb) page = a.b.indices[geo.page_base + t / 16];
   if (page >= a.b.num_pages) page = -1;
-  constexpr int EPL = D / kWave;   // elements per lane: 1 or 2
-  uint16_t* ko = a.k_out + (pair * budget_pad + i) * D + EPL * lane;
-  uint16_t* vo = a.v_out + (pair * budget_pad + i) * D + EPL * lane;
   const size_t src = (((size_t)(uint32_t)(page >= 0 ? page : 0) * a.num_kv_heads + g) * 16 +
-                      (t >= 0 ? (t & 15) : 0)) * D + EPL * lane;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    ko[e] = page >= 0 ? a.k_pool[src + e] : (uint16_t)0;
-    vo[e] = page >= 0 ? a.v_pool[src + e] : (uint16_t)0;
-  }
+                      (t >= 0 ? (t & 15) : 0)) * D + 8 * c;
+  const uint4 kv = page >= 0 ? *reinterpret_cast<const uint4*>(a.k_pool + src) : make_uint4(0, 0, 0, 0);
+  const uint4 vv = page >= 0 ? *reinterpret_cast<const uint4*>(a.v_pool + src) : make_uint4(0, 0, 0, 0);
+  *reinterpret_cast<uint4*>(a.k_out + (pair * budget_pad + i) * D + 8 * c) = kv;
+  *reinterpret_cast<uint4*>(a.v_out + (pair * budget_pad + i) * D + 8 * c) = vv;
 }
 
 hipError_t launch_snapkv_select(const SnapArgs& a, hipStream_t st) {
@@ -433,7 +435,8 @@ hipError_t launch_snapkv_select(const SnapArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_snapkv_gather(const SnapArgs& a, int budget_pad, hipStream_t st) {
-  const dim3 grid((budget_pad + 3) / 4, a.num_kv_heads, a.b.batch);
+  const int ppw = 256 / (a.head_dim / 8);
+  const dim3 grid((budget_pad + ppw - 1) / ppw, a.num_kv_heads, a.b.batch);
   if (a.head_dim == 128)
     hipLaunchKernelGGL((snap_gather_kernel<128>), grid, dim3(256), 0, st, a, budget_pad);
   else

@@ -4,9 +4,9 @@
 // stores the mean of a block's keys over the in-block axis; "Why Long
 // Generations Are Expensive": it runs once, when a block fills up.
 //
-// Layout: one wavefront per (page, head) tile. A bf16 tile is page_size rows
-// of head_dim contiguous elements; lane l owns dims [l*DPL, l*DPL+DPL), so
-// each row read is one coalesced 64 * DPL * 2-byte access. Sums are kept in
+// Layout: one wavefront per (page, head) tile, 16-byte loads, every row of
+// the tile in flight at once (the rows a lane read are summed, then the row
+// groups by lane shuffles). Sums are kept in
 // float64: every bf16 value and every fp32-scale x fp8 product is exact in
 // float64, so the column sum is exact unless its terms span more than ~2^41
 // in magnitude; page_size is a power of two, so the mean is exact too, and it
@@ -15,49 +15,82 @@
 
 namespace ls {
 
-template <int D, bool kOutF32>
+template <int D, bool kOutF32, int PMAX>
 __global__ __launch_bounds__(256) void summaries_bf16_kernel(
     const uint16_t* __restrict__ keys, const int32_t* __restrict__ page_ids, int n_pages,
     int num_pages, int num_heads, int page_size, void* __restrict__ out) {
   const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (tile >= n_pages * num_heads) return;
-  summary_tile_bf16<D, kOutF32>(keys, page_ids, tile, num_pages, num_heads, page_size, out);
+  summary_tile_bf16<D, kOutF32, PMAX>(keys, page_ids, tile, num_pages, num_heads, page_size, out);
 }
 
 // fp8 e4m3fn keys with a per-token fp32 scale, single-head pool
-// [num_pages][page_size][D]; the summand is scale[p][s] * key[p][s][d].
-template <int D, bool kOutF32>
+// [num_pages][page_size][D]; the summand is scale[p][s] * key[p][s][d]. Lane
+// l loads 16 bytes (16 dims) of rows l / LPR, l / LPR + RPI, ... (LPR = D / 16
+// lanes per row, RPI = 64 / LPR rows per load), all issued before the first
+// use; the bytes are widened exactly with the packed convert.
+template <int D, bool kOutF32, int PMAX>
 __global__ __launch_bounds__(256) void summaries_fp8_kernel(
     const uint8_t* __restrict__ keys, const float* __restrict__ scales,
     const int32_t* __restrict__ page_ids, int n_pages, int num_pages, int page_size,
     void* __restrict__ out) {
-  constexpr int DPL = D / kWave;
+  constexpr int LPR = D / 16, RPI = kWave / LPR, NI = PMAX / RPI;
   const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (tile >= n_pages) return;
   const int page = page_ids[tile];
   if (page < 0 || page >= num_pages) return;
-  const uint8_t* base = keys + (size_t)page * page_size * D + lane * DPL;
-  const float* sc = scales + (size_t)page * page_size;
-  double acc[DPL];
+  const int ni = page_size / RPI, row0 = lane / LPR, c = lane % LPR;
+  uint4 v[NI];
+  float sv[NI];
 #pragma unroll
-  for (int j = 0; j < DPL; ++j) acc[j] = 0.0;
-  for (int s = 0; s < page_size; ++s) {
-    const double sv = (double)sc[s];
-#pragma unroll
-    for (int j = 0; j < DPL; ++j)
-      acc[j] += sv * (double)fp8e4m3fn_to_f32(base[(size_t)s * D + j]);  // exact product
+  for (int i = 0; i < NI; ++i) {
+    const size_t row = (size_t)page * page_size + row0 + (size_t)i * RPI;
+    v[i] = i < ni ? ldg16_stream(keys + row * D + 16 * c) : make_uint4(0, 0, 0, 0);
+    sv[i] = i < ni ? scales[row] : 0.0f;
   }
-  const double inv = 1.0 / (double)page_size;
-  const size_t o = (size_t)page * D + lane * DPL;
+  double acc[16];
 #pragma unroll
-  for (int j = 0; j < DPL; ++j) {
-    double mean = acc[j] * inv;
-    if constexpr (kOutF32) {
-      reinterpret_cast<float*>(out)[o + j] = (float)mean;
-    } else {
-      reinterpret_cast<uint16_t*>(out)[o + j] = f64_to_bf16_rne(mean);
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i < ni) {
+      const double s = (double)sv[i];
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t b01 = fp8x2_to_bf16x2(w[q], false), b23 = fp8x2_to_bf16x2(w[q], true);
+        acc[4 * q] += s * (double)bf16_lo(b01);       // exact products
+        acc[4 * q + 1] += s * (double)bf16_hi(b01);
+        acc[4 * q + 2] += s * (double)bf16_lo(b23);
+        acc[4 * q + 3] += s * (double)bf16_hi(b23);
+      }
     }
+  }
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] += __shfl_xor(acc[j], off, kWave);
+  }
+  if (lane >= LPR) return;
+  const double inv = 1.0 / (double)page_size;
+  const size_t o = (size_t)page * D + 16 * lane;
+  if constexpr (kOutF32) {
+    float* dst = reinterpret_cast<float*>(out) + o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(dst + 4 * q) =
+          make_float4((float)(acc[4 * q] * inv), (float)(acc[4 * q + 1] * inv),
+                      (float)(acc[4 * q + 2] * inv), (float)(acc[4 * q + 3] * inv));
+  } else {
+    uint32_t pk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      pk[j] = (uint32_t)f64_to_bf16_rne(acc[2 * j] * inv) |
+              ((uint32_t)f64_to_bf16_rne(acc[2 * j + 1] * inv) << 16);
+    uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
   }
 }
 
@@ -65,42 +98,60 @@ template <int D, bool F32>
 static hipError_t launch_bf16(const SummaryArgs& a, hipStream_t st) {
   const int tiles = a.n_pages * a.pool.num_heads;
   dim3 grid((tiles + 3) / 4);
-  hipLaunchKernelGGL((summaries_bf16_kernel<D, F32>), grid, dim3(256), 0, st,
-                     (const uint16_t*)a.keys, a.page_ids, a.n_pages, a.pool.num_pages,
-                     a.pool.num_heads, a.pool.page_size, a.out);
+  const int P = a.pool.page_size;
+#define LS_SUM_LAUNCH(PM)                                                                    \
+  hipLaunchKernelGGL((summaries_bf16_kernel<D, F32, PM>), grid, dim3(256), 0, st,           \
+                     (const uint16_t*)a.keys, a.page_ids, a.n_pages, a.pool.num_pages,      \
+                     a.pool.num_heads, P, a.out)
+  if (P <= 16) LS_SUM_LAUNCH(16);
+  else if (P <= 32) LS_SUM_LAUNCH(32);
+  else LS_SUM_LAUNCH(64);
+#undef LS_SUM_LAUNCH
   return hipGetLastError();
 }
 
 template <int D, bool F32>
 static hipError_t launch_fp8(const SummaryArgs& a, hipStream_t st) {
   dim3 grid((a.n_pages + 3) / 4);
-  hipLaunchKernelGGL((summaries_fp8_kernel<D, F32>), grid, dim3(256), 0, st,
-                     (const uint8_t*)a.keys, a.key_scales, a.page_ids, a.n_pages,
-                     a.pool.num_pages, a.pool.page_size, a.out);
+  const int P = a.pool.page_size;
+#define LS_FP8_LAUNCH(PM)                                                                    \
+  hipLaunchKernelGGL((summaries_fp8_kernel<D, F32, PM>), grid, dim3(256), 0, st,            \
+                     (const uint8_t*)a.keys, a.key_scales, a.page_ids, a.n_pages,           \
+                     a.pool.num_pages, P, a.out)
+  if (P <= 16) LS_FP8_LAUNCH(16);
+  else if (P <= 32) LS_FP8_LAUNCH(32);
+  else LS_FP8_LAUNCH(64);
+#undef LS_FP8_LAUNCH
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int PMAX>
 __global__ __launch_bounds__(256) void bounds_bf16_kernel(
     const uint16_t* __restrict__ keys, const int32_t* __restrict__ page_ids, int n_pages,
     int num_pages, int num_heads, int page_size, uint16_t* __restrict__ out) {
   const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (tile >= n_pages * num_heads) return;
-  bounds_tile_bf16<D>(keys, page_ids, tile, num_pages, num_heads, page_size, out);
+  bounds_tile_bf16<D, PMAX>(keys, page_ids, tile, num_pages, num_heads, page_size, out);
+}
+
+template <int D>
+static hipError_t launch_bounds_d(const SummaryArgs& a, hipStream_t st) {
+  const int tiles = a.n_pages * a.pool.num_heads;
+  dim3 grid((tiles + 3) / 4);
+  const int P = a.pool.page_size;
+#define LS_BND_LAUNCH(PM)                                                                    \
+  hipLaunchKernelGGL((bounds_bf16_kernel<D, PM>), grid, dim3(256), 0, st,                    \
+                     (const uint16_t*)a.keys, a.page_ids, a.n_pages, a.pool.num_pages,      \
+                     a.pool.num_heads, P, (uint16_t*)a.out)
+  if (P <= 16) LS_BND_LAUNCH(16);
+  else if (P <= 32) LS_BND_LAUNCH(32);
+  else LS_BND_LAUNCH(64);
+#undef LS_BND_LAUNCH
+  return hipGetLastError();
 }
 
 hipError_t launch_bounds(const SummaryArgs& a, hipStream_t st) {
-  const int tiles = a.n_pages * a.pool.num_heads;
-  dim3 grid((tiles + 3) / 4);
-  if (a.pool.head_dim == 128)
-    hipLaunchKernelGGL((bounds_bf16_kernel<128>), grid, dim3(256), 0, st,
-                       (const uint16_t*)a.keys, a.page_ids, a.n_pages, a.pool.num_pages,
-                       a.pool.num_heads, a.pool.page_size, (uint16_t*)a.out);
-  else
-    hipLaunchKernelGGL((bounds_bf16_kernel<64>), grid, dim3(256), 0, st,
-                       (const uint16_t*)a.keys, a.page_ids, a.n_pages, a.pool.num_pages,
-                       a.pool.num_heads, a.pool.page_size, (uint16_t*)a.out);
-  return hipGetLastError();
+  return a.pool.head_dim == 128 ? launch_bounds_d<128>(a, st) : launch_bounds_d<64>(a, st);
 }
 
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t st) {

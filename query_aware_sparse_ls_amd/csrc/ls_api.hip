@@ -461,6 +461,8 @@ ls_status ls_build_block_summaries(const void* keys, const float* key_scales, ls
   if (n_pages == 0) return ok();
   if (!keys || !page_ids || !summaries)
     return fail(LS_ERR_INVALID, "keys, page_ids and summaries must be non-null");
+  if (!aligned16(keys) || !aligned16(summaries))
+    return fail(LS_ERR_INVALID, "keys and summaries must be 16-byte aligned");
   ls::SummaryArgs a{keys, key_scales, key_pool, page_ids, n_pages, summaries, summary_dtype};
   return hip_status(ls::launch_summaries(a, stream), "ls_build_block_summaries launch");
 }
@@ -480,6 +482,8 @@ ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_
   if (n_pages == 0) return ok();
   if (!keys || !page_ids || !bounds)
     return fail(LS_ERR_INVALID, "keys, page_ids and bounds must be non-null");
+  if (!aligned16(keys) || !aligned16(bounds))
+    return fail(LS_ERR_INVALID, "keys and bounds must be 16-byte aligned");
   ls::SummaryArgs a{keys, nullptr, key_pool, page_ids, n_pages, bounds, LS_DTYPE_BF16};
   return hip_status(ls::launch_bounds(a, stream), "ls_build_block_bounds launch");
 }

@@ -87,6 +87,15 @@ __device__ __forceinline__ float fp8e4m3fn_to_f32(uint32_t b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
+// bf16 pair of fp8 e4m3fn bytes 0,1 (hi = false) or 2,3 (hi = true) of x,
+// exact (every e4m3fn value is a bf16 value): the gfx950 packed convert.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x, bool hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------- reductions ----
 
 template <typename T>

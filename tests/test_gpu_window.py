@@ -86,5 +86,5 @@ def test_window_full_size_llama8b_32k_b16():
     cfg = LLAMA8B_32K_B16
     inp = make_block_topk_inputs(cfg, device="cuda")
     out, lse = _run(inp, 4, 9830, torch.bfloat16)
-    for r, g in [(0, 0), (7, 3), (15, 7)]:
+    for r, g in [(0, 0), (2, 5), (5, 1), (7, 3), (9, 6), (11, 2), (13, 4), (15, 7)]:
         _check(inp, out, lse, r, g, 4, 9830, torch.bfloat16)
