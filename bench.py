@@ -956,11 +956,20 @@ def bench_summaries(args) -> int:
     res["value"] = round(gbps, 1)
     res["bf16_build"] = {"ms": round(ms, 5), "bytes": nbytes, "GBps": round(gbps, 1),
                          "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+    # the chip's streaming rate over a buffer of the same size (what a read
+    # of these bytes can take at best on this part)
+    sink = torch.empty(int(ls._lib.EXPORTS["ls_stream_read_sink_words"]()), dtype=torch.int32,
+                       device=dev)
+    flat = [k.view(-1)[: nbytes // 2] if k.numel() * 2 >= nbytes else k.view(-1) for k in keys]
+    ms_sr = timed(lambda i: ls.stream_read(flat[i % 2], sink), max(4, args.steps // 20))
+    sr = flat[0].numel() * 2 / (ms_sr * 1e-3) / 1e9
+    res["bf16_build"]["stream_read_GBps"] = round(sr, 1)
+    res["bf16_build"]["pct_of_stream_read"] = round(100 * gbps / sr, 2)
     res["roofline"] = {"kernel": "ls::summaries_bf16_kernel<128, false, 16>", "bound": "hbm",
                        "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                        "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}
-    del keys, outs
+    del keys, outs, flat
     torch.cuda.empty_cache()
     # fp8 indexer keys: 4 x 15,200 pages of 64 tokens x 128 bytes, fp32 scales
     npg, P8 = 4 * 15200, 64
@@ -975,7 +984,8 @@ def bench_summaries(args) -> int:
     nb8 = npg * P8 * (128 + 4) + npg * 128 * 2 + npg * 4
     g8 = nb8 / (ms8 * 1e-3) / 1e9
     res["fp8_indexer_build"] = {"ms": round(ms8, 5), "bytes": nb8, "GBps": round(g8, 1),
-                                "pct_of_hbm_peak": round(100 * g8 / HBM_PEAK_GBPS, 2)}
+                                "pct_of_hbm_peak": round(100 * g8 / HBM_PEAK_GBPS, 2),
+                                "pct_of_stream_read": round(100 * g8 / sr, 2)}
     res["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(res), flush=True)
     return 0
