@@ -39,6 +39,6 @@ from .method import (  # noqa: F401
     attention_over_tokens, sparse_attention, dense_attention, lse_merge,
     indexer_token_scores, select_tokens, mla_attention, decode_step,
     tokens_of_blocks, topk_from_keep_ratio, forced_blocks, indexer_block_scores,
-    coarse_to_fine_select, block_bounds, bound_scores, approx_select_tokens, score_bucket,
+    coarse_to_fine_select, block_bounds, bound_scores, approx_select_tokens, remap_bucket,
     window_tokens, window_attention, snapkv_scores, snapkv_select,
 )

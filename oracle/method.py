@@ -293,36 +293,46 @@ def select_tokens(scores: np.ndarray, k: int, candidates: Optional[Iterable[int]
     return sorted(fs | set(rank_top(scores, cands, k)))
 
 
-def score_bucket(scores: np.ndarray, bits: int = 12) -> np.ndarray:
-    """Bucket of each score for the approximate top-k: the score is taken in
-    fp32 (the precision the kernels rank in), mapped to an unsigned 32-bit
-    key that orders like the floats (negative: all bits inverted; otherwise
-    the sign bit set; -0 counts as +0), and the bucket is the key's top
-    `bits` bits: sign, exponent and the leading mantissa bits, i.e. a
-    monotonic, roughly logarithmic remap of the scores."""
+def remap_bucket(scores: np.ndarray, bins: int = 4096) -> np.ndarray:
+    """Bucket of each score for the top-k's first digit (Vortex, "Making it
+    fast": a monotonic remap of the scores spreads them over the buckets).
+    The reading taken here: the plainest such remap, linear between the
+    smallest and largest score of the ranked units, in fp32 (the precision
+    the kernels rank in), each operation rounded once:
+        span = mx - mn;  scale = bins / span;  t = (s - mn) * scale
+        bucket = bins - 1 if t >= bins - 1, floor(t) if t >= 1, else 0.
+    Every bucket is 0 when span is not a positive finite number (all scores
+    equal). Non-decreasing in s, so a higher bucket never holds a lower
+    score."""
     f = np.asarray(scores, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = np.where(u == 0x80000000, 0, u)
-    key = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
-    return (key >> (32 - bits)).astype(np.int64)
+    if f.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    mn, mx = f.min(), f.max()
+    with np.errstate(invalid="ignore", over="ignore"):
+        span = np.float32(mx - mn)
+        if not (np.isfinite(span) and span > 0):
+            return np.zeros(f.size, dtype=np.int64)
+        scale = np.float32(np.float32(bins) / span)
+        t = (f - mn).astype(np.float32) * scale
+        b = np.where(t >= bins - 1, bins - 1, np.where(t >= 1, np.floor(t), 0))
+    return np.nan_to_num(b, nan=0).astype(np.int64)
 
 
 def approx_select_tokens(scores: np.ndarray, k: int,
                          candidates: Optional[Iterable[int]] = None,
-                         bits: int = 12) -> List[int]:
+                         bins: int = 4096) -> List[int]:
     """Approximate top-k (Vortex, "Making it fast": a monotonic remap of the
     scores into buckets and an early exit that stops refining once enough
-    winners are certain, filling the rest from the boundary bucket): every
-    candidate whose bucket is above the bucket b* holding the k-th best
-    score, then candidates of b* in ascending index order until there are k
-    (filled in index order here, deterministically, where the page samples).
-    `bits`: the key bits that make a bucket (12: one radix digit; 24: the
-    early exit after two digits). Ascending ids."""
+    winners are certain, filling the rest from the boundary bucket): with
+    buckets from remap_bucket over the ranked units' scores, every unit whose
+    bucket is above the bucket b* holding the k-th best, then units of b* in
+    ascending index order until there are k (the page samples the boundary
+    bucket; index order is the deterministic reading). Ascending ids."""
     cands = np.arange(len(scores)) if candidates is None else np.asarray(list(candidates))
     k = min(max(0, k), len(cands))
     if k == 0:
         return []
-    b = score_bucket(np.asarray(scores)[cands], bits)
+    b = remap_bucket(np.asarray(scores)[cands], bins)
     kth = np.sort(b)[::-1][k - 1]
     above = cands[b > kth]
     fill = np.sort(cands[b == kth])[:k - len(above)]

@@ -5,7 +5,8 @@ Bit-exact against the oracle where the fp32 scores are exact (integer keys,
 queries and weights: every product and partial sum is an integer below
 2^24), so both sides see the same buckets; with real-valued scores, the
 certain winners are kept, nothing certainly below the boundary bucket is
-taken, and the count is exact.
+taken, the count is exact, and the recall of the exact top-k is at least
+97% (the figure the page reports for its approximation).
 """
 
 from __future__ import annotations
@@ -15,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.method import BatchView, score_bucket
+from oracle.method import BatchView, remap_bucket
 from parity_util import say
 from workloads import INDEXER_128K, bf16_bits, fp8_bits, make_indexer_inputs, reduced
 
@@ -64,22 +65,19 @@ def _host(inp):
             inp.idx_scale.cpu().numpy(), bv)
 
 
-@pytest.mark.parametrize("level", [1, 2])
 @pytest.mark.parametrize("k", [1, 100, 2048, 5000])
-def test_approx_topk_integer_scores_bit_exact(k, level):
+def test_approx_topk_integer_scores_bit_exact(k):
     """Integer scores: many equal scores per bucket, so the boundary bucket is
-    large and its fill order (ascending tokens) decides; ragged lengths.
-    Level 1 exits after one radix digit (12-bit buckets), level 2 after two
-    (24-bit buckets)."""
+    large and its fill order (ascending tokens) decides; ragged lengths."""
     lens = [9000, 4500, 63, 1]
     inp = _inputs(lens, seed=70 + k, integer=True)
-    say(f"approx top-k, integer scores, k {k}, level {level}")
-    sel, n = _run(inp, k, level)
+    say(f"approx top-k, integer scores, k {k}")
+    sel, n = _run(inp, k, 1)
     q, w, kb, ks, bv = _host(inp)
     for r, L in enumerate(lens):
         s = oracle.indexer_token_scores(q, w, kb, ks, bv, r)
         assert np.all(s == np.round(s)) and np.abs(s).max(initial=0) < 2 ** 24
-        want = oracle.approx_select_tokens(s, k, bits=12 * level)
+        want = oracle.approx_select_tokens(s, k)
         assert sel[r, :n[r]].tolist() == want, (r, len(want), int(n[r]))
         assert (sel[r, n[r]:] == -1).all()
 
@@ -101,25 +99,31 @@ def test_approx_topk_integer_scores_with_block_candidates():
         assert sel[r, :n[r]].tolist() == sorted(int(toks[i]) for i in pick)
 
 
-def test_approx_topk_real_scores_properties_and_recall():
-    """Real-valued scores (the indexer workload's recipe): the winners whose
-    bucket is certainly above the boundary bucket are kept, nothing whose
-    bucket is certainly below it is taken, and the count is exact."""
+@pytest.mark.parametrize("seed", [78, 79])
+def test_approx_topk_real_scores_properties_and_recall(seed):
+    """Real-valued scores (the indexer workload's recipe, 128K and a ragged
+    70,000-token request): the count is exact, every unit whose bucket is
+    more than one above the boundary bucket is kept, nothing more than one
+    bucket below it is taken (the kernel's fp32 scores may sit on the other
+    side of a bucket edge from the oracle's), and the recall of the exact
+    top-k is at least 97%."""
     lens = [131072, 70000]
-    inp = _inputs(lens, seed=78)
+    inp = _inputs(lens, seed=seed)
     k = 2048
+    say(f"approx top-k, real scores, seed {seed}")
     sel, n = _run(inp, k, 1)
     ex, exn = _run(inp, k, 0)
     q, w, kb, ks, bv = _host(inp)
     for r, L in enumerate(lens):
         s = oracle.indexer_token_scores(q, w, kb, ks, bv, r)
-        tol = 1e-5 * np.abs(s).max()
-        lo, hi = score_bucket(s - tol), score_bucket(s + tol)
-        kth = np.sort(score_bucket(s))[::-1][k - 1]
+        b = remap_bucket(s)
+        kth = np.sort(b)[::-1][k - 1]
         got = set(sel[r, :n[r]].tolist())
-        assert int(n[r]) == k
-        assert {i for i in range(L) if lo[i] > kth} <= got
-        assert all(hi[i] >= kth for i in got)
-        rec = len(got & set(ex[r, :exn[r]].tolist())) / k
-        say(f"request {r}: recall of the approximate top-{k}: {rec:.4f}")
-        assert rec > 0.5
+        assert int(n[r]) == k and (sel[r, n[r]:] == -1).all()
+        assert {i for i in range(L) if b[i] > kth + 1} <= got
+        assert all(b[i] >= kth - 1 for i in got)
+        exact = set(ex[r, :exn[r]].tolist())
+        rec = len(got & exact) / k
+        say(f"request {r}: recall of the approximate top-{k}: {rec:.4f}, "
+            f"boundary bucket {int((b == kth).sum())} units")
+        assert rec >= 0.97

@@ -637,51 +637,87 @@ def test_coarse_to_fine_never_leaves_the_kept_blocks():
 
 # ------------------------------------------------------- approximate top-k
 
+def test_remap_bucket_hand_worked():
+    from oracle.method import remap_bucket
+    # mn 0, mx 4: scale = 4096 / 4 = 1024, t = 1024 s; the largest score lands
+    # on t = 4096 and is clamped into the top bucket 4095
+    s = np.array([0.0, 4.0, 2.0, 2.0005, 1.0])
+    assert remap_bucket(s).tolist() == [0, 4095, 2048, 2048, 1024]
+    # an offset range: mn -3, span 4, the same scale
+    assert remap_bucket(np.array([-3.0, -1.0, 1.0, -2.5])).tolist() == [0, 2048, 4095, 512]
+    # span 4096: scale 1, every integer its own bucket, the top two clamped
+    s = np.arange(4097, dtype=np.float64)
+    assert remap_bucket(s).tolist() == list(range(4095)) + [4095, 4095]
+    # degenerate ranges: one bucket
+    assert remap_bucket(np.array([2.5, 2.5, 2.5])).tolist() == [0, 0, 0]
+    assert remap_bucket(np.array([7.0])).tolist() == [0]
+    assert remap_bucket(np.zeros(0)).tolist() == []
+    # a span that overflows fp32 is no usable range either
+    assert remap_bucket(np.array([-3e38, 3e38, 0.0])).tolist() == [0, 0, 0]
+
+
+def test_remap_bucket_shift_scale_invariance_and_monotone():
+    from oracle.method import remap_bucket
+    rng = np.random.default_rng(52)
+    s = rng.integers(-500, 500, 3000).astype(np.float64)
+    b = remap_bucket(s)
+    # exact integer arithmetic in fp32: shifting by an integer and scaling by
+    # a power of two leave s - mn and span in the same ratio
+    assert (remap_bucket(4.0 * s + 64.0) == b).all()
+    assert (remap_bucket(s - 1000.0) == b).all()
+    # non-decreasing, within range, ends pinned
+    o = np.argsort(s, kind="stable")
+    assert (np.diff(b[o]) >= 0).all()
+    assert b.min() == 0 and b.max() == 4095
+    assert b[np.argmin(s)] == 0 and b[np.argmax(s)] == 4095
+    # a different bin count scales the grid: 2 bins split at the midpoint
+    assert remap_bucket(np.array([0.0, 0.99, 1.0, 2.0]), bins=2).tolist() == [0, 0, 1, 1]
+
+
 def test_approx_topk_hand_worked():
-    from oracle.method import approx_select_tokens, score_bucket
-    # 1.0, 1.01 and 1.02 share a bucket (same exponent, same leading three
-    # mantissa bits); 3.0 is above it, 0.5 below. k = 3: 3.0 is certain, the
-    # two others come from the boundary bucket in index order.
-    s = np.array([1.0, 1.01, 1.02, 3.0, 0.5])
-    b = score_bucket(s)
-    assert b[0] == b[1] == b[2] and b[3] > b[0] > b[4]
-    assert approx_select_tokens(s, 3) == [0, 1, 3]
-    assert select_tokens(s, 3) == [1, 2, 3]          # the exact one differs
-    # 1.125 has the next mantissa pattern: its own bucket above 1.0's
-    s2 = np.array([1.0, 1.125, 1.1])
-    assert score_bucket(s2)[1] == score_bucket(s2)[0] + 1
-    assert approx_select_tokens(s2, 1) == [1]
+    from oracle.method import approx_select_tokens
+    # buckets [0, 4095, 2048, 2048, 1024] (above): k = 2 keeps 4.0 (certain)
+    # and fills one of the two units of bucket 2048 in index order; the exact
+    # top-2 takes the larger score of that bucket instead
+    s = np.array([0.0, 4.0, 2.0, 2.0005, 1.0])
+    assert approx_select_tokens(s, 2) == [1, 2]
+    assert select_tokens(s, 2) == [1, 3]
+    assert approx_select_tokens(s, 3) == [1, 2, 3] == select_tokens(s, 3)
+    assert approx_select_tokens(s, 5) == [0, 1, 2, 3, 4]
+    assert approx_select_tokens(s, 0) == []
+    # equal scores: one bucket, index order, as in the exact ranking
+    assert approx_select_tokens(np.ones(6), 4) == [0, 1, 2, 3] == select_tokens(np.ones(6), 4)
+    # candidates: the range is that of the candidates' scores
+    c = [1, 3, 4]
+    assert approx_select_tokens(s, 1, candidates=c) == [1]
+    assert approx_select_tokens(s, 2, candidates=c) == [1, 3]
 
 
-def test_approx_topk_order_and_exactness_when_buckets_are_distinct():
-    from oracle.method import approx_select_tokens, score_bucket
-    # negative, zero and positive scores keep their order through the key
-    vals = np.array([-8.0, -1.0, -0.0, 0.0, 0.75, 2.0, 40.0])
-    b = score_bucket(vals)
-    assert list(b) == sorted(b) and b[2] == b[3]
-    # one score per power of two: every bucket holds one candidate, so the
-    # approximate top-k is the exact one for every k
+def test_approx_topk_exact_when_buckets_are_distinct():
+    from oracle.method import approx_select_tokens, remap_bucket
+    # scores 0, 1, ..., 4094 (span 4094 < 4096: every score its own bucket):
+    # the approximate top-k is the exact one for every k
     rng = np.random.default_rng(50)
-    s = 2.0 ** rng.permutation(np.arange(-20, 20)) * np.where(rng.random(40) < 0.5, -1, 1)
-    for k in (0, 1, 7, 20, 40):
+    s = rng.permutation(4095).astype(np.float64)
+    assert len(set(remap_bucket(s).tolist())) == 4095
+    for k in (0, 1, 7, 2048, 4095):
         assert approx_select_tokens(s, k) == select_tokens(s, k)
-    # candidates restrict the ranking
-    assert approx_select_tokens(s, 3, candidates=[0, 5, 9, 11]) == \
-        select_tokens(s, 3, candidates=[0, 5, 9, 11])
 
 
 def test_approx_topk_keeps_every_certain_winner():
-    from oracle.method import approx_select_tokens, score_bucket
+    from oracle.method import approx_select_tokens, remap_bucket
     rng = np.random.default_rng(51)
-    s = rng.standard_normal(3000) * 5
-    for k in (10, 300, 2999):
+    s = rng.standard_normal(30000) * 5
+    b = remap_bucket(s)
+    for k in (10, 300, 2048, 29999):
         got = set(approx_select_tokens(s, k))
         exact = set(select_tokens(s, k))
-        b = score_bucket(s)
         kth = np.sort(b)[::-1][k - 1]
         assert len(got) == k
-        assert {i for i in range(3000) if b[i] > kth} <= got & exact
+        assert {i for i in range(len(s)) if b[i] > kth} <= got & exact
         assert all(b[i] >= kth for i in got)
+        # only the boundary bucket can differ from the exact set
+        assert len(got ^ exact) <= 2 * int((b == kth).sum())
 
 
 # ------------------------------------------------------- sink + recent window
@@ -783,16 +819,3 @@ def test_snapkv_select_pooling_and_forcing_hand_worked():
         om.snapkv_scores = orig
 
 
-def test_approx_topk_two_digits_refines_the_boundary():
-    from oracle.method import approx_select_tokens, score_bucket
-    # 1.0, 1.01 and 1.02 share a 12-bit bucket but not a 24-bit one
-    s = np.array([1.0, 1.01, 1.02, 3.0, 0.5])
-    assert len(set(score_bucket(s[:3], 24))) == 3
-    assert approx_select_tokens(s, 3, bits=24) == [1, 2, 3]
-    # equal 24-bit prefixes still fill in index order: 1 + 2^-20 and 1 + 2^-19
-    # differ only below the top 24 key bits
-    t = np.array([1.0 + 2.0 ** -19, 1.0 + 2.0 ** -20, 5.0])
-    assert score_bucket(t, 24)[0] == score_bucket(t, 24)[1]
-    assert approx_select_tokens(t, 2, bits=24) == [0, 2]
-    assert select_tokens(t, 2) == [0, 2]
-    assert approx_select_tokens(t[::-1].copy(), 2, bits=24) == [0, 1]   # 5.0 and the lower index
