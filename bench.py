@@ -810,9 +810,8 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
                       **({"coarse_topk_blocks": cfg.coarse_topk_blocks} if coarse else {}),
                       **({"n_candidates": cfg.n_candidates, "kmeans_iters": cfg.kmeans_iters}
                          if pq else {}),
-                      "token_topk": (f"approximate ({args.approx_topk} digit"
-                                     f"{'s' if args.approx_topk > 1 else ''})"
-                                     if args.approx_topk else "exact")},
+                      "token_topk": ("approximate (remapped first digit, boundary bucket "
+                                     "in index order)" if args.approx_topk else "exact")},
            "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
            "achieved_GBps_step": round(gbps, 1),
            "pct_of_hbm_peak_step": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -1681,10 +1680,10 @@ def main(argv=None) -> int:
               "copy-fetch-cmd", "copy-write-cmd"):
         ap.add_argument("--" + a, default="")
     ap.add_argument("--copy-bytes", type=int, default=0)
-    ap.add_argument("--approx-topk", type=int, nargs="?", const=1, default=0, choices=(0, 1, 2),
-                    help="indexer paths: the approximate token top-k (early exit after 1 or 2 "
-                         "radix digits, the boundary bucket filled in index order) instead of "
-                         "the exact one; reports its recall")
+    ap.add_argument("--approx-topk", type=int, nargs="?", const=1, default=0, choices=(0, 1),
+                    help="indexer paths: the approximate token top-k (early exit after the "
+                         "remapped first digit, the boundary bucket filled in index order) "
+                         "instead of the exact one; reports its recall")
     ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
                     help="block-topk path: block-mean summaries (default) or Quest bounds")
     ap.add_argument("--path", choices=("block-topk", "ragged", "indexer", "coarse-to-fine",

@@ -443,20 +443,22 @@ ls_status ls_sparse_decode_step_noalloc(const void* q, int32_t q_dtype, int32_t 
  *               cand_cap * page_size with block candidates, or cand_cap +
  *               page_size with token candidates (<= 262144); blocks
  *               max_blocks (<= 16384).
- * Token mode is three launches: a histogram of the score keys while scoring,
- * a pass that keeps every unit above the k-th score's 12-bit bucket and
- * gathers that bucket's units, and the ranking of those by the rest of their
- * key (in the last workgroup of each request to finish the pass).
- * p->approx = 1 (tokens mode) is the approximate top-k of the Vortex post
- * ("Making it fast": a monotonic remap of the scores into buckets, and an
+ * Token mode is three launches: the scoring (each workgroup also leaves the
+ * range of its scores); a histogram of the scores remapped into 4,096
+ * buckets, linearly between the request's smallest and largest score; and a
+ * pass that keeps every unit above the bucket b* holding the k-th score and
+ * lists b*'s units, which the last workgroup of each request to finish the
+ * pass ranks by their fp32 score (Vortex post, "Making it fast": a monotonic
+ * remap of the scores spreads them over the buckets, so b* holds few units).
+ * The bucket of score s is, in fp32 with each step rounded once,
+ *   t = (s - mn) * (4096 / (mx - mn)),  bucket = min(4095, floor(t)),
+ * with mn, mx the request's smallest and largest score; every bucket is 0
+ * when mx - mn is not a positive finite number.
+ * p->approx = 1 (tokens mode) is the approximate top-k of the same post (an
  * early exit that stops refining and fills the rest from the boundary
- * bucket): every unit whose 12-bit bucket of the order-preserving key of its
- * fp32 score (sign, exponent, three mantissa bits) lies above the bucket b*
- * holding the k-th score, then units of b* in ascending unit order until
- * there are topk. Deterministic; not the exact top-k when b* holds more
- * units than it contributes. p->approx = 2 exits after the second digit
- * instead: buckets of the key's top 24 bits (the boundary is then a
- * 2^-15-relative slice of the scores).
+ * bucket): every unit whose bucket lies above b*, then units of b* in
+ * ascending unit order until there are topk. Deterministic; it differs from
+ * the exact top-k only inside b*.
  */
 enum { LS_SEL_TOKENS = 0, LS_SEL_BLOCKS = 1 };
 enum { LS_CAND_BLOCKS = 0, LS_CAND_TOKENS = 1 };
@@ -470,8 +472,8 @@ typedef struct ls_indexer_params {
   int32_t max_selected;  /* row capacity of `selected`                        */
   int32_t candidates;    /* LS_CAND_BLOCKS or LS_CAND_TOKENS: what cand_blocks */
                          /* holds (tokens mode with a candidate list)         */
-  int32_t approx;        /* tokens mode: 0 exact top-k; 1 or 2: approximate  */
-                         /* top-k with buckets of 12 or 24 key bits (below)   */
+  int32_t approx;        /* tokens mode: 0 exact top-k; 1 approximate top-k */
+                         /* (the boundary bucket filled in unit order, below) */
 } ls_indexer_params;
 
 /* Row stride (in floats) of scores_out for up to max_units units. */

@@ -23,20 +23,30 @@
 // leaves every dot product unchanged (the sum over dims is over the same
 // pairs).
 //
-// Token top-k (k of up to 262,144 units per request, ties to the lowest unit),
-// a three-digit radix select over an order-preserving integer key of the
-// scores:
-//  1. the scoring workgroups histogram the key's top 12 bits in LDS and add
-//     the non-zero bins into a per-request global histogram (device-scope
-//     atomics);
-//  2. the mark kernel finds, per request, the bucket b* holding the k-th
-//     score; units above b* are selected (bitmap), units in b* are appended
-//     to a per-request list and histogrammed by their next 12 key bits;
-//  3. the last mark workgroup of each request (arrival counter) finds the
-//     second digit from that histogram, the third (last 8 bits) in one pass
-//     over the list, marks the listed units above the k-th key, takes the
-//     ones equal to it lowest index first, and emits the bitmap in ascending
-//     order.
+// Token top-k (k of up to 262,144 units per request, ties to the lowest unit).
+// The first digit is a bucket of a monotonic remap of the scores (Vortex
+// post, "Making it fast": the remap spreads the scores over the buckets):
+// linear from the request's smallest to its largest valid score onto 4,096
+// buckets, so that the bucket holding the k-th score holds few units; the
+// units that share the k-th score's first digit are then ranked by an
+// order-preserving integer key of their fp32 scores:
+//  1. every scoring workgroup leaves the (min, max) of its valid scores in a
+//     slot (workgroup 0 of a request also clears the request's histogram and
+//     counters);
+//  2. the histogram kernel reduces the request's slots to the remap, and
+//     histograms the first digit (bucket >> 4: 256 bins, so that every
+//     workgroup adds at most 256 counts into the request's global histogram
+//     with device-scope atomics);
+//  3. the mark kernel finds, per request, the first digit d* holding the
+//     k-th score; units above d* are selected (bitmap), units of d* are
+//     appended to a per-request list;
+//  4. the last mark workgroup of each request (arrival counter) ranks the
+//     listed units: up to 512 of them directly in LDS, by (key descending,
+//     unit ascending), more of them by three digits of their key (12, 12, 8
+//     bits); it marks the winners and emits the bitmap in ascending order.
+//     The approximate top-k ranks the listed units by their bucket instead
+//     of their key (an early exit at bucket resolution: the bucket holding
+//     the k-th score is filled in ascending unit order).
 #pragma once
 
 #include "ls_internal.h"
@@ -116,7 +126,55 @@ __device__ __forceinline__ int idx_unit_block(const IndexerArgs& a, const IdxUni
   return blk;
 }
 
-__device__ __forceinline__ uint32_t idx_bin(uint32_t key) { return key >> 20; }
+// The remap: scale = kIdxBins / (mx - mn) in fp32, rounded once; 0 when the
+// range is empty, negative or not finite (every unit in bucket 0).
+__device__ __forceinline__ float idx_remap_scale(float mn, float mx) {
+  const float span = mx - mn;
+  if (!(span > 0.0f) || !(span <= 3.402823466e38f)) return 0.0f;   // NaN fails both
+  return __fdiv_rn((float)kIdxBins, span);
+}
+
+// Bucket of score s: t = (s - mn) * scale, each step rounded once; the top
+// bucket takes t >= kIdxBins - 1 (the largest score lands on kIdxBins), and a
+// NaN t bucket 0.
+__device__ __forceinline__ int idx_remap_bin(float s, float mn, float scale) {
+  const float t = (s - mn) * scale;
+  return t >= (float)(kIdxBins - 1) ? kIdxBins - 1 : (t >= 1.0f ? (int)t : 0);
+}
+
+// (min, max) over the workgroup of each thread's (mn, mx); every thread gets
+// the result. red: 2 * waves floats of LDS. Synchronises.
+template <int NT>
+__device__ __forceinline__ void idx_range_reduce(float& mn, float& mx, float* red) {
+  constexpr int NW = NT / kWave;
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  }
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    red[wave] = mn;
+    red[NW + wave] = mx;
+  }
+  __syncthreads();
+  mn = red[0];
+  mx = red[NW];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    mn = fminf(mn, red[w]);
+    mx = fmaxf(mx, red[NW + w]);
+  }
+  __syncthreads();
+}
+
+// Workgroup 0 of request r clears the request's histogram and counters
+// before the histogram kernel (a later launch) uses them.
+template <int NT>
+__device__ __forceinline__ void idx_clear_request(const IndexerArgs& a, int r) {
+  uint4* h = reinterpret_cast<uint4*>(a.hist + (size_t)r * kIdxCoarse);
+  for (int i = threadIdx.x; i < kIdxCoarse / 4; i += NT) h[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x < 4) a.ctl[(size_t)r * 4 + threadIdx.x] = 0u;
+}
 
 // max(x, 0) as one integer max on the bits: a negative float (sign bit set)
 // is a negative int and becomes +0; anything else is kept (NaN included).

@@ -42,7 +42,7 @@ struct IdxScoreLds {
   // page ids of the workgroup's blocks (one per 16+ tokens, one per block),
   // or with token candidates the key row of every unit
   int pg[kIdxMaxTilesPerWg * 16];
-  uint32_t hist[MODE == kIdxTokens ? kIdxBins : 1];
+  float red[2 * kIdxWaves];
 };
 
 template <int MODE, int NHT>
@@ -72,6 +72,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
     gu.page_base = geo.page_base;
     gu.nb = geo.nb;
   }
+  if (MODE == kIdxTokens && blockIdx.x == 0) idx_clear_request<kIdxThreads>(a, r);
   if (u0 >= n_units) return;
 
   // page ids of the workgroup's blocks (-1: no unit of this block is scored)
@@ -117,9 +118,6 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
       }
     }
     sh.pg[i] = page;
-  }
-  if constexpr (MODE == kIdxTokens) {
-    for (int i = tid; i < kIdxBins; i += kIdxThreads) sh.hist[i] = 0u;
   }
 
   // q (A operand: row = head 16ht + col, dims 32kq + 8s .. +8 of k-step s),
@@ -210,6 +208,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
   uint4 buf[NS][NL];
   uint32_t badm[NS];
   float sig[NS];
+  float rmn = __builtin_inff(), rmx = -__builtin_inff();   // range of this thread's valid scores
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     issue(s, buf[s], badm[s], sig[s]);
@@ -294,7 +293,10 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
           if constexpr (MODE == kIdxTokens) {
             int tok;
             valid = idx_unit_block(a, gu, r, u0 + ul, &tok) >= 0;
-            if (valid) atomicAdd(&sh.hist[idx_bin(score_key(v))], 1u);
+            if (valid) {
+              rmn = fminf(rmn, v);
+              rmx = fmaxf(rmx, v);
+            }
           } else {
             valid = u0 + ul >= c0 && u0 + ul < c1;
           }
@@ -303,37 +305,25 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
       }
     }
   }
-  __syncthreads();
   if constexpr (MODE == kIdxTokens) {
-    uint32_t* gh = a.hist + (size_t)r * kIdxBins;
-    for (int i = tid; i < kIdxBins; i += kIdxThreads) {
-      const uint32_t c = sh.hist[i];
-      if (c) atomicAdd(gh + i, c);
-    }
+    idx_range_reduce<kIdxThreads>(rmn, rmx, sh.red);
+    if (tid == 0)
+      a.range[(size_t)r * (a.max_units / kIdxMinWgUnits) + blockIdx.x] = make_float2(rmn, rmx);
   }
 }
 
 // ------------------------------------------------------------ token top-k ----
 
-// One 16-byte store per thread (the histograms are 256-byte aligned).
-__global__ __launch_bounds__(kIdxThreads) void idx_zero_kernel(uint32_t* hist, uint32_t* ctl,
-                                                               int batch) {
-  const int n4 = 2 * batch * kIdxBins / 4;   // first-digit and second-digit histograms
-  const int i = blockIdx.x * kIdxThreads + threadIdx.x;
-  if (i < n4) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (i < batch * 4) ctl[i] = 0u;
-}
-
 constexpr int kIdxMarkThreads = 512;
 constexpr int kIdxMarkWaves = kIdxMarkThreads / kWave;
 
 struct IdxMarkLds {
-  uint32_t h[kIdxBins];        // digit histograms (first, then second, then third digit)
-  uint32_t h2[kIdxBins];       // this workgroup's second-digit histogram of bucket b*
+  alignas(16) uint32_t h[kIdxBins];   // digit histograms; the finish also lists units here
+  uint32_t h2[kIdxBins];       // finish: the candidate blocks (unit -> token map)
   uint32_t bm[kIdxMaxWords];   // finish: selected units
   uint32_t tie[kIdxMaxWords];  // finish: units equal to the k-th key
   int red[kIdxMarkWaves];
-  int bstar, cabove, kr, last, b2, above2, b3, above3;
+  int bstar, cabove, kr, last, dig, above;
 };
 
 // Exclusive prefix sum over the workgroup in thread order; *total = sum.
@@ -354,19 +344,21 @@ __device__ __forceinline__ int idx_block_scan(int v, int* red, int* total) {
   return before + inc - v;
 }
 
-// Digit search from the top over h[0 .. nbins) (nbins a multiple of the
-// workgroup size): the bin b with (count above b) < need <= (count at or
-// above b). Writes b and the count above it (one thread), then synchronises.
+// Digit search from the top over h[0 .. nbins) (a power of two, 16 ..
+// kIdxBins): the bin b with (count above b) < need <= (count at or above b).
+// Writes b and the count above it (one thread), then synchronises.
 // need >= 1 and sum(h) >= need.
 __device__ __forceinline__ void idx_find_digit(const uint32_t* h, int nbins, int need, int* red,
                                                int* b_out, int* above_out) {
-  const int per = nbins / kIdxMarkThreads, t = threadIdx.x;
+  const int per = nbins > kIdxMarkThreads ? nbins / kIdxMarkThreads : 1;
+  const int t = threadIdx.x, own = t * per < nbins;
   int mine = 0;
-  for (int i = 0; i < per; ++i) mine += (int)h[t * per + i];
+  if (own)
+    for (int i = 0; i < per; ++i) mine += (int)h[t * per + i];
   int tot;
   const int excl = idx_block_scan(mine, red, &tot);
   int above = tot - excl - mine;   // elements in bins of higher threads
-  if (above < need && above + mine >= need) {
+  if (own && above < need && above + mine >= need) {
     for (int b = t * per + per - 1; b >= t * per; --b) {
       if (above + (int)h[b] >= need) {
         *b_out = b;
@@ -377,15 +369,6 @@ __device__ __forceinline__ void idx_find_digit(const uint32_t* h, int nbins, int
     }
   }
   __syncthreads();
-}
-
-__device__ __forceinline__ int idx_token_of(const IndexerArgs& a, const IdxUnits& g, int r,
-                                           int u) {
-  if (a.unit_kind == kUnitsTokenCands)
-    return u < g.ncand ? a.cand_blocks[(size_t)r * a.cand_cap + u] : g.tail0 + (u - g.ncand);
-  if (g.ncand < 0) return u;
-  const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);
-  return a.cand_blocks[(size_t)r * a.cand_cap + (u >> PS)] * P + (u & (P - 1));
 }
 
 // dst[i] = src[i] for i < n (n <= NPT * kIdxMarkThreads), every load of a
@@ -406,8 +389,64 @@ __device__ __forceinline__ void idx_copy_in(uint32_t* dst, const uint32_t* src, 
   }
 }
 
-// Second digit of a score key: bits [19:8]; third digit: bits [7:0].
-__device__ __forceinline__ uint32_t idx_d2(uint32_t key) { return (key >> 8) & 0xFFFu; }
+__device__ __forceinline__ int idx_token_of(const IndexerArgs& a, const IdxUnits& g, int r,
+                                           int u) {
+  if (a.unit_kind == kUnitsTokenCands)
+    return u < g.ncand ? a.cand_blocks[(size_t)r * a.cand_cap + u] : g.tail0 + (u - g.ncand);
+  if (g.ncand < 0) return u;
+  const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);
+  return a.cand_blocks[(size_t)r * a.cand_cap + (u >> PS)] * P + (u & (P - 1));
+}
+
+// The request's remap (min and scale, as float bits in ctl[2], ctl[3]) from
+// the scoring workgroups' range slots, and the histogram of the first digit
+// (bucket >> 4) of this chunk's valid units. One workgroup per
+// (kIdxMarkUnits units, request).
+constexpr int kIdxHistThreads = 256;
+__global__ __launch_bounds__(kIdxHistThreads) void idx_hist_kernel(IndexerArgs a) {
+  __shared__ uint32_t h[kIdxCoarse];
+  __shared__ float red[2 * kIdxHistThreads / kWave];
+  const int r = blockIdx.y, tid = threadIdx.x;
+  const IdxUnits g = idx_units(a, r);
+  const int cu0 = blockIdx.x * kIdxMarkUnits;
+  if (cu0 >= g.n) return;
+  const int upw = a.tiles_per_wg * 16;
+  const int nwg = (g.n + upw - 1) / upw;   // the scoring workgroups that wrote a slot
+  const float2* slots = a.range + (size_t)r * (a.max_units / kIdxMinWgUnits);
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int i = tid; i < nwg; i += kIdxHistThreads) {
+    const float2 m = slots[i];
+    mn = fminf(mn, m.x);
+    mx = fmaxf(mx, m.y);
+  }
+  for (int i = tid; i < kIdxCoarse; i += kIdxHistThreads) h[i] = 0u;
+  idx_range_reduce<kIdxHistThreads>(mn, mx, red);
+  const float scale = idx_remap_scale(mn, mx);
+  if (blockIdx.x == 0 && tid == 0) {
+    a.ctl[(size_t)r * 4 + 2] = __float_as_uint(mn);
+    a.ctl[(size_t)r * 4 + 3] = __float_as_uint(scale);
+  }
+  constexpr int IT = kIdxMarkUnits / kIdxHistThreads;
+  const float* srow = a.scores + (size_t)r * a.max_units;
+  float sv[IT];
+  bool vv[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {   // every score load in flight at once
+    const int u = cu0 + it * kIdxHistThreads + tid;
+    int tok;
+    vv[it] = idx_unit_block(a, g, r, u, &tok) >= 0;
+    sv[it] = vv[it] ? srow[u] : 0.0f;
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+    if (vv[it]) atomicAdd(&h[idx_remap_bin(sv[it], mn, scale) >> 4], 1u);
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)r * kIdxCoarse;
+  for (int i = tid; i < kIdxCoarse; i += kIdxHistThreads) {
+    const uint32_t c = h[i];
+    if (c) atomicAdd(gh + i, c);
+  }
+}
 
 __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a) {
   __shared__ IdxMarkLds sh;
@@ -419,21 +458,18 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   uint32_t* ctl = a.ctl + (size_t)r * 4;
   const float* srow = a.scores + (size_t)r * a.max_units;
   uint2* crow = a.cand + (size_t)r * a.max_units;
-  uint32_t* gh2 = a.hist + ((size_t)a.b.batch + r) * kIdxBins;
+  const float rmn = __uint_as_float(ctl[2]), rscale = __uint_as_float(ctl[3]);
 
-  // 1. threshold bucket b* from the request's first-digit histogram
-  const uint32_t* gh = a.hist + (size_t)r * kIdxBins;
-  idx_copy_in<kIdxBins / kIdxMarkThreads>(sh.h, gh, kIdxBins);
-  for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) sh.h2[i] = 0u;
+  // 1. the first digit d* holding the k-th score, from the request's histogram
+  const uint32_t* gh = a.hist + (size_t)r * kIdxCoarse;
+  idx_copy_in<1>(sh.h, gh, kIdxCoarse);
   if (tid == 0) {
-    sh.bstar = kIdxBins;   // nothing definite, no candidates
+    sh.bstar = kIdxCoarse;   // nothing definite, no candidates
     sh.cabove = 0;
   }
   __syncthreads();
   {
-    int mine = 0;
-    constexpr int per = kIdxBins / kIdxMarkThreads;
-    for (int i = 0; i < per; ++i) mine += (int)sh.h[tid * per + i];
+    const int mine = tid < kIdxCoarse ? (int)sh.h[tid] : 0;
     int tot;
     const int excl = idx_block_scan(mine, sh.red, &tot);
     const int kr = a.topk < tot ? a.topk : tot;
@@ -441,28 +477,17 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
       sh.kr = kr;
       if (kr >= tot && tot > 0) sh.bstar = -1;   // every valid unit is selected
     }
-    if (kr > 0 && kr < tot) {
-      int above = tot - excl - mine;
-      if (above < kr && above + mine >= kr) {
-        for (int b = tid * per + per - 1; b >= tid * per; --b) {
-          const int hb = (int)sh.h[b];
-          if (above + hb >= kr) {
-            sh.bstar = b;
-            sh.cabove = above;
-            break;
-          }
-          above += hb;
-        }
-      }
+    const int above = tot - excl - mine;   // units in higher digits
+    if (kr > 0 && kr < tot && tid < kIdxCoarse && above < kr && above + mine >= kr) {
+      sh.bstar = tid;
+      sh.cabove = above;
     }
   }
   __syncthreads();
   const int bstar = sh.bstar;
-  const bool refine = bstar >= 0 && bstar < kIdxBins;
-  const bool digits = refine && a.approx != 1;   // one-digit approximation: no second digit
+  const bool refine = bstar >= 0 && bstar < kIdxCoarse;
 
-  // 2. this chunk: selected bits above b*; units of b* to the candidate list
-  // and into the second-digit histogram
+  // 2. this chunk: selected bits above d*; units of d* to the candidate list
   const int cu0 = chunk * kIdxMarkUnits;
   constexpr int IT = kIdxMarkUnits / kIdxMarkThreads;
   float sv[IT];
@@ -474,17 +499,15 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
     vv[it] = idx_unit_block(a, g, r, u, &tok) >= 0;
     sv[it] = vv[it] ? srow[u] : 0.0f;
   }
-  // selected bits; this wave's bucket-b* units counted first, so that the
+  // selected bits; this wave's digit-d* units counted first, so that the
   // workgroup reserves its slots of the list with ONE returning atomic
-  uint32_t key[IT];
   unsigned long long cmask[IT];
   int wcount = 0;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int ub = cu0 + it * kIdxMarkThreads + wave * kWave;   // wave's 64 units
     const bool valid = vv[it];
-    key[it] = valid ? score_key(sv[it]) : 0u;
-    const int bin = (int)idx_bin(key[it]);
+    const int bin = idx_remap_bin(sv[it], rmn, rscale) >> 4;   // first digit
     const bool def = valid && (bstar < 0 || bin > bstar);
     cmask[it] = __ballot(refine && valid && bin == bstar);
     wcount += __popcll(cmask[it]);
@@ -503,37 +526,29 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
       sh.red[w] = tot;   // the wave's offset in the workgroup's slots
       tot += c;
     }
-    sh.b2 = tot ? (int)atomicAdd(ctl, (uint32_t)tot) : 0;   // the workgroup's first slot
+    sh.dig = tot ? (int)atomicAdd(ctl, (uint32_t)tot) : 0;   // the workgroup's first slot
   }
   __syncthreads();
-  int cpos = sh.b2 + sh.red[wave];
+  int cpos = sh.dig + sh.red[wave];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const unsigned long long cm = cmask[it];
     if (cm) {
       if ((cm >> lane) & 1ull) {
         const int u = cu0 + it * kIdxMarkThreads + wave * kWave + lane;
-        st_dev(crow + cpos + mbcnt(cm), make_uint2(key[it], (uint32_t)u));
-        if (digits) atomicAdd(&sh.h2[idx_d2(key[it])], 1u);
+        st_dev(crow + cpos + mbcnt(cm), make_uint2(__float_as_uint(sv[it]), (uint32_t)u));
       }
       cpos += __popcll(cm);
     }
   }
-  __syncthreads();
-  if (digits) {
-    for (int i = tid; i < kIdxBins; i += kIdxMarkThreads) {
-      const uint32_t c = sh.h2[i];
-      if (c) atomicAdd(gh2 + i, c);
-    }
-  }
   // 3. arrival; the last workgroup of the request finishes it. Everything
-  // handed over (bitmap words, listed units, histogram adds, the list
-  // counter) goes through device-coherent stores or atomics, which write
-  // through the XCD's L2, and every thread waits for its own to complete
-  // before the workgroup's arrival is counted (no release fence: that would
-  // write back the whole L2 under every other workgroup). The finishing
-  // workgroup takes one acquire fence (its XCD's L2 drops stale lines) and
-  // then reads everything with plain, pipelined loads.
+  // handed over (bitmap words, listed units, the list counter) goes through
+  // device-coherent stores or atomics, which write through the XCD's L2,
+  // and every thread waits for its own to complete before the workgroup's
+  // arrival is counted (no release fence: that would write back the whole
+  // L2 under every other workgroup). The finishing workgroup takes one
+  // acquire fence (its XCD's L2 drops stale lines) and then reads
+  // everything with plain, pipelined loads.
   wait_stores();
   __syncthreads();
   if (tid == 0) {
@@ -549,20 +564,24 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   const int nwr = (g.n + 31) / 32;
   idx_copy_in<kIdxMaxWords / kIdxMarkThreads>(sh.bm, bmrow, nwr);
   for (int w = tid; w < nwr; w += kIdxMarkThreads) sh.tie[w] = 0u;
-  // the candidate blocks (unit -> token map), in LDS when they fit (h2 is
-  // free from here on)
+  // the candidate blocks (unit -> token map), in LDS when they fit
   const bool cand_lds = a.unit_kind == kUnitsDefault && g.ncand >= 0 && g.ncand <= kIdxBins;
   if (cand_lds)
     idx_copy_in<kIdxBins / kIdxMarkThreads>(
         sh.h2, reinterpret_cast<const uint32_t*>(a.cand_blocks + (size_t)r * a.cand_cap), g.ncand);
   int ties_to_take = 0;
   constexpr int UN = 4;   // candidate loads in flight per thread
-  if (refine && a.approx == 1) {
-    // early exit (Vortex, "Making it fast"): every unit of bucket b* is a
-    // tie; the emission takes the first `need` of them in unit order
-    const int nc = (int)ld_dev(ctl);
-    ties_to_take = kr - sh.cabove;
-    __syncthreads();
+  const int nc = refine ? (int)ld_dev(ctl) : 0;   // units with digit d*
+  const bool approx = a.approx == 1;
+  // what ranks a listed unit (larger first): its key, or its bucket for the
+  // approximate top-k (the bucket holding the k-th score is then filled in
+  // ascending unit order: ties go to the lower unit)
+  auto rank_key = [&](uint32_t sbits) -> uint32_t {
+    const float sc = __uint_as_float(sbits);
+    return approx ? (uint32_t)idx_remap_bin(sc, rmn, rscale) : score_key(sc);
+  };
+  // one pass over the listed units: f(rank key, unit) for each
+  auto each_listed = [&](auto&& f) {
     for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
       uint2 c[UN];
 #pragma unroll
@@ -572,120 +591,116 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
       }
 #pragma unroll
       for (int j = 0; j < UN; ++j)
-        if (c[j].y != 0xFFFFFFFFu) atomicOr(&sh.tie[c[j].y >> 5], 1u << (c[j].y & 31));
+        if (c[j].y != 0xFFFFFFFFu) f(rank_key(c[j].x), c[j].y);
+    }
+  };
+  int need = kr - sh.cabove;   // units of digit d* to select (>= 1 when refining)
+  if (refine && nc <= kIdxMarkThreads) {
+    // few listed units (the remap's purpose): each thread ranks one of them
+    // against all, by (rank key descending, unit ascending), in LDS
+    // as one 64-bit key (rank key << 32 | ~unit): a unit's rank is the number
+    // of larger keys. The list is padded to a multiple of 16 entries with key
+    // 0, which is larger than nothing, and read 16 bytes at a time, 8 reads
+    // in flight.
+    unsigned long long* lst = reinterpret_cast<unsigned long long*>(sh.h);   // <= 512: 4 KB of h
+    const int ncp = (nc + 15) & ~15;
+    unsigned long long me = 0ull;
+    if (tid < nc) {
+      const uint2 c = crow[tid];
+      me = ((unsigned long long)rank_key(c.x) << 32) | (uint32_t)~c.y;
+    }
+    if (tid < ncp) lst[tid] = me;
+    __syncthreads();
+    if (tid < nc) {
+      const ulonglong2* l2 = reinterpret_cast<const ulonglong2*>(lst);
+      int rank = 0;
+      for (int j = 0; j < ncp / 2; j += 8) {
+        ulonglong2 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = l2[j + q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) rank += (int)(v[q].x > me) + (int)(v[q].y > me);
+      }
+      const uint32_t u = ~(uint32_t)me;
+      if (rank < need) atomicOr(&sh.bm[u >> 5], 1u << (u & 31));
     }
   } else if (refine) {
-    const int need = kr - sh.cabove;   // >= 1 units of bucket b* to select
-    const int nc = (int)ld_dev(ctl);   // units in bucket b*
-    idx_copy_in<kIdxBins / kIdxMarkThreads>(sh.h, gh2, kIdxBins);
-    __syncthreads();
-    idx_find_digit(sh.h, kIdxBins, need, sh.red, &sh.b2, &sh.above2);
-    const uint32_t b2 = (uint32_t)sh.b2;
-    const int need2 = need - sh.above2;
-    if (a.approx == 2) {
-      // early exit after two digits: units above the 24-bit boundary prefix
-      // are selected, the boundary's own units are ties taken in unit order
-      const uint32_t theta24 = ((uint32_t)bstar << 12) | b2;
-      ties_to_take = need2;
-      for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
-        uint2 c[UN];
-#pragma unroll
-        for (int j = 0; j < UN; ++j) {
-          const int i = i0 + j * kIdxMarkThreads + tid;
-          c[j] = i < nc ? crow[i] : make_uint2(0u, 0xFFFFFFFFu);
-        }
-#pragma unroll
-        for (int j = 0; j < UN; ++j) {
-          if (c[j].y == 0xFFFFFFFFu) continue;
-          const uint32_t u = c[j].y, pre = c[j].x >> 8;
-          if (pre > theta24) atomicOr(&sh.bm[u >> 5], 1u << (u & 31));
-          else if (pre == theta24) atomicOr(&sh.tie[u >> 5], 1u << (u & 31));
-        }
-      }
-    } else {
-    // third digit over the candidates whose second digit is b2
-    for (int i = tid; i < 256; i += kIdxMarkThreads) sh.h[i] = 0u;
-    __syncthreads();
-    for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
-      uint2 c[UN];
-#pragma unroll
-      for (int j = 0; j < UN; ++j) {
-        const int i = i0 + j * kIdxMarkThreads + tid;
-        c[j] = i < nc ? crow[i] : make_uint2(0u, 0xFFFFFFFFu);
-      }
-#pragma unroll
-      for (int j = 0; j < UN; ++j)
-        if (c[j].y != 0xFFFFFFFFu && idx_d2(c[j].x) == b2) atomicAdd(&sh.h[c[j].x & 255u], 1u);
-    }
-    __syncthreads();
-    {
-      // 256 bins over 512 threads: the first 256 threads own one bin each
-      const int t = tid;
-      const int mine = t < 256 ? (int)sh.h[t] : 0;
-      int tot;
-      const int excl = idx_block_scan(t < 256 ? mine : 0, sh.red, &tot);
-      const int above = tot - excl - mine;
-      if (t < 256 && above < need2 && above + mine >= need2) {
-        sh.b3 = t;
-        sh.above3 = above;
-      }
+    // digits of the rank key among the listed units: [31:20], [19:8], [7:0]
+    // (a bucket has 12 bits: its second and third digits are 0), each among
+    // the units that share the digits found so far
+    uint32_t prefix = 0u, pmask = 0u;
+    for (int d = 0; d < 3; ++d) {
+      const int shift = d == 0 ? 20 : (d == 1 ? 8 : 0);
+      const int nbins = d == 2 ? 256 : kIdxBins;
+      for (int i = tid; i < nbins; i += kIdxMarkThreads) sh.h[i] = 0u;
       __syncthreads();
+      each_listed([&](uint32_t key, uint32_t) {
+        if ((key & pmask) == prefix) atomicAdd(&sh.h[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+      });
+      __syncthreads();
+      idx_find_digit(sh.h, nbins, need, sh.red, &sh.dig, &sh.above);
+      prefix |= (uint32_t)sh.dig << shift;
+      pmask |= (uint32_t)(nbins - 1) << shift;
+      need -= sh.above;
+      __syncthreads();   // dig / above are rewritten by the next digit
     }
-    const uint32_t theta = ((uint32_t)bstar << 20) | (b2 << 8) | (uint32_t)sh.b3;
-    ties_to_take = need2 - sh.above3;
-    for (int i0 = 0; i0 < nc; i0 += UN * kIdxMarkThreads) {
-      uint2 c[UN];
-#pragma unroll
-      for (int j = 0; j < UN; ++j) {
-        const int i = i0 + j * kIdxMarkThreads + tid;
-        c[j] = i < nc ? crow[i] : make_uint2(0u, 0xFFFFFFFFu);
-      }
-#pragma unroll
-      for (int j = 0; j < UN; ++j) {
-        if (c[j].y == 0xFFFFFFFFu) continue;
-        const uint32_t u = c[j].y;
-        if (c[j].x > theta) atomicOr(&sh.bm[u >> 5], 1u << (u & 31));
-        else if (c[j].x == theta) atomicOr(&sh.tie[u >> 5], 1u << (u & 31));
-      }
-    }
-    }
+    const uint32_t theta = prefix;   // the k-th rank key
+    ties_to_take = need;
+    each_listed([&](uint32_t key, uint32_t u) {
+      if (key > theta) atomicOr(&sh.bm[u >> 5], 1u << (u & 31));
+      else if (key == theta) atomicOr(&sh.tie[u >> 5], 1u << (u & 31));
+    });
   }
   __syncthreads();
 
-  // 4. emit in ascending unit order: the bitmap plus the first ties
+  // 4. emit in ascending unit order: the bitmap plus the first ties. Thread
+  // t owns words [t wpt, (t + 1) wpt), held in registers (wpt <= 16).
   const int P = a.b.page_size, PS = __builtin_ctz((unsigned)P);
+  constexpr int WMAX = kIdxMaxWords / kIdxMarkThreads;
   const int wpt = (nwr + kIdxMarkThreads - 1) / kIdxMarkThreads;
-  const int w0 = tid * wpt, w1 = w0 + wpt < nwr ? w0 + wpt : nwr;
-  int tcount = 0;
-  for (int w = w0; w < w1; ++w) tcount += __popc(sh.tie[w]);
-  int ttot;
-  int tpre = idx_block_scan(tcount, sh.red, &ttot);
-  int scount = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t x = sh.tie[w], kept = 0u;
-    int take = ties_to_take - tpre;
-    const int pc = __popc(x);
-    take = take < 0 ? 0 : (take > pc ? pc : take);
-    for (int i = 0; i < take; ++i) {
-      const uint32_t low = x & (0u - x);
-      kept |= low;
-      x ^= low;
+  const int w0 = tid * wpt;
+  uint32_t bw[WMAX];
+#pragma unroll
+  for (int i = 0; i < WMAX; ++i) bw[i] = (i < wpt && w0 + i < nwr) ? sh.bm[w0 + i] : 0u;
+  if (ties_to_take > 0) {   // uniform: the first ties_to_take tie units join
+    uint32_t tw[WMAX];
+    int tcount = 0;
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+      tw[i] = (i < wpt && w0 + i < nwr) ? sh.tie[w0 + i] : 0u;
+      tcount += __popc(tw[i]);
     }
-    tpre += pc;
-    const uint32_t sel = sh.bm[w] | kept;
-    sh.bm[w] = sel;
-    scount += __popc(sel);
+    int ttot;
+    int tpre = idx_block_scan(tcount, sh.red, &ttot);
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+      uint32_t x = tw[i], kept = 0u;
+      const int pc = __popc(x);
+      int take = ties_to_take - tpre;
+      take = take < 0 ? 0 : (take > pc ? pc : take);
+      for (int j = 0; j < take; ++j) {
+        const uint32_t low = x & (0u - x);
+        kept |= low;
+        x ^= low;
+      }
+      tpre += pc;
+      bw[i] |= kept;
+    }
   }
+  int scount = 0;
+#pragma unroll
+  for (int i = 0; i < WMAX; ++i) scount += __popc(bw[i]);
   int stot;
   int pos = idx_block_scan(scount, sh.red, &stot);
   int32_t* out = a.selected + (size_t)r * a.max_selected;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t x = sh.bm[w];
+#pragma unroll
+  for (int i = 0; i < WMAX; ++i) {
+    uint32_t x = bw[i];
     while (x) {
       const int b = __ffs(x) - 1;
       x &= x - 1u;
       if (pos < a.max_selected) {
-        const int u = 32 * w + b;
+        const int u = 32 * (w0 + i) + b;
         out[pos] = cand_lds ? (int)sh.h2[u >> PS] * P + (u & (P - 1)) : idx_token_of(a, g, r, u);
       }
       ++pos;
@@ -714,10 +729,9 @@ hipError_t launch_indexer_score(const IndexerArgs& a, int mode, hipStream_t st) 
                             : launch_score_mode<kIdxBlocks>(a, st);
 }
 
-hipError_t launch_indexer_zero(const IndexerArgs& a, hipStream_t st) {
-  const int n4 = 2 * a.b.batch * kIdxBins / 4;
-  hipLaunchKernelGGL(idx_zero_kernel, dim3((n4 + kIdxThreads - 1) / kIdxThreads), dim3(kIdxThreads),
-                     0, st, a.hist, a.ctl, a.b.batch);
+hipError_t launch_indexer_hist(const IndexerArgs& a, hipStream_t st) {
+  dim3 grid((a.max_units + kIdxMarkUnits - 1) / kIdxMarkUnits, a.b.batch);
+  hipLaunchKernelGGL(idx_hist_kernel, grid, dim3(kIdxHistThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -728,9 +742,9 @@ hipError_t launch_indexer_mark(const IndexerArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_indexer_token_select(const IndexerArgs& a, hipStream_t st) {
-  hipError_t e = launch_indexer_zero(a, st);
+  hipError_t e = launch_score_mode<kIdxTokens>(a, st);
   if (e != hipSuccess) return e;
-  e = launch_score_mode<kIdxTokens>(a, st);
+  e = launch_indexer_hist(a, st);
   if (e != hipSuccess) return e;
   return launch_indexer_mark(a, st);
 }

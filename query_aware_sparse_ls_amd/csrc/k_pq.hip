@@ -21,7 +21,7 @@
 // slice of the MFMA B operand (key^T) from 8 code bytes: k-step s of lane
 // group kq covers dims 32 kq + 8 s .. + 8, i.e. subspaces 8 kq + 2 s and
 // 8 kq + 2 s + 1, one 8-byte LDS read each. The rest (weighted ReLU over the
-// heads, first-digit histogram, mark + finish) is the token top-k of the
+// heads, score range, histogram, mark + finish) is the token top-k of the
 // learned indexer.
 #include "dev_indexer.h"
 #include "dev_mfma.h"
@@ -239,7 +239,7 @@ struct PqScoreLds {
     uint4 q[NHT][4][kWave];            // the q operand, staged once
     uint2 cb[kPqSub * kPqCent];        // the codebook (4 bf16 per centroid)
   } u;
-  uint32_t hist[kIdxBins / 2];         // first-digit counts, two 16-bit bins per word
+  float red[2 * kIdxWaves];
   int pg[kIdxMaxTilesPerWg + 1];       // page ids of the workgroup's blocks
 };
 
@@ -253,6 +253,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void pq_score_kernel(IndexerArgs a)
   const int upw = a.tiles_per_wg * 16;
   const int u0 = blockIdx.x * upw;
   const IdxUnits gu = idx_units(a, r);   // the complete pages' tokens
+  if (blockIdx.x == 0) idx_clear_request<kIdxThreads>(a, r);
   if (u0 >= gu.n) return;
 
   const int bi0 = u0 >> PS;
@@ -266,7 +267,6 @@ __global__ __launch_bounds__(kIdxThreads, 2) void pq_score_kernel(IndexerArgs a)
     }
     sh.pg[i] = page;
   }
-  for (int i = tid; i < kIdxBins / 2; i += kIdxThreads) sh.hist[i] = 0u;
 
   // q as the A operand (rows = heads 16 ht + col, k-step s of lane group kq
   // = dims 32 kq + 8 s .. + 8), through LDS into registers
@@ -322,6 +322,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void pq_score_kernel(IndexerArgs a)
   };
   uint2 buf[NS];
   bool bad[NS];
+  float rmn = __builtin_inff(), rmx = -__builtin_inff();   // range of this thread's valid scores
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     issue(s, buf[s], bad[s]);
@@ -367,26 +368,20 @@ __global__ __launch_bounds__(kIdxThreads, 2) void pq_score_kernel(IndexerArgs a)
           int tok;
           const bool valid = idx_unit_block(a, gu, r, u0 + ul, &tok) >= 0;
           if (valid) {
-            const uint32_t bin = idx_bin(score_key(v));
-            atomicAdd(&sh.hist[bin >> 1], 1u << (16 * (bin & 1u)));
+            rmn = fminf(rmn, v);
+            rmx = fmaxf(rmx, v);
           }
           if (u0 + ul < gu.n) srow[ul] = valid ? v : 0.0f;
         }
       }
     }
   }
-  __syncthreads();
-  uint32_t* gh = a.hist + (size_t)r * kIdxBins;
-  for (int i = tid; i < kIdxBins / 2; i += kIdxThreads) {
-    const uint32_t c = sh.hist[i];
-    if (c & 0xffffu) atomicAdd(gh + 2 * i, c & 0xffffu);
-    if (c >> 16) atomicAdd(gh + 2 * i + 1, c >> 16);
-  }
+  idx_range_reduce<kIdxThreads>(rmn, rmx, sh.red);
+  if (tid == 0)
+    a.range[(size_t)r * (a.max_units / kIdxMinWgUnits) + blockIdx.x] = make_float2(rmn, rmx);
 }
 
 hipError_t launch_pq_select(const IndexerArgs& a, hipStream_t st) {
-  hipError_t e = launch_indexer_zero(a, st);
-  if (e != hipSuccess) return e;
   const int upw = a.tiles_per_wg * 16;
   dim3 grid((a.max_units + upw - 1) / upw, a.b.batch);
   switch (a.num_heads) {
@@ -394,7 +389,9 @@ hipError_t launch_pq_select(const IndexerArgs& a, hipStream_t st) {
     case 32: hipLaunchKernelGGL((pq_score_kernel<2>), grid, dim3(kIdxThreads), 0, st, a); break;
     default: hipLaunchKernelGGL((pq_score_kernel<4>), grid, dim3(kIdxThreads), 0, st, a); break;
   }
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_indexer_hist(a, st);
   if (e != hipSuccess) return e;
   return launch_indexer_mark(a, st);
 }

@@ -735,12 +735,27 @@ size_t ls_indexer_select_workspace_size(int32_t batch_size, int32_t granularity,
   const size_t U = (size_t)ls_indexer_score_stride(granularity, max_units);
   size_t ws = align_up(B * U * sizeof(float));   // scores
   if (granularity == LS_SEL_TOKENS) {
-    ws += align_up(2 * B * ls::kIdxBins * sizeof(uint32_t));   // digit histograms
-    ws += align_up(B * 4 * sizeof(uint32_t));                  // counters
-    ws += align_up(B * U * sizeof(uint2));                     // threshold-bucket units
-    ws += align_up(B * (U / 32) * sizeof(uint32_t));           // bitmap
+    ws += align_up(B * ls::kIdxCoarse * sizeof(uint32_t));              // bucket histograms
+    ws += align_up(B * 4 * sizeof(uint32_t));                         // counters, remap
+    ws += align_up(B * (U / ls::kIdxMinWgUnits) * sizeof(float2));    // score ranges
+    ws += align_up(B * U * sizeof(uint2));                            // threshold-bucket units
+    ws += align_up(B * (U / 32) * sizeof(uint32_t));                  // bitmap
   }
   return ws;
+}
+
+// The token top-k's part of the workspace (after the scores), in the order
+// ls_indexer_select_workspace_size counts it.
+static void token_topk_layout(ls::IndexerArgs& a, char* w, size_t B, int U) {
+  a.hist = reinterpret_cast<uint32_t*>(w);
+  w += align_up(B * ls::kIdxCoarse * sizeof(uint32_t));
+  a.ctl = reinterpret_cast<uint32_t*>(w);
+  w += align_up(B * 4 * sizeof(uint32_t));
+  a.range = reinterpret_cast<float2*>(w);
+  w += align_up(B * (U / ls::kIdxMinWgUnits) * sizeof(float2));
+  a.cand = reinterpret_cast<uint2*>(w);
+  w += align_up(B * U * sizeof(uint2));
+  a.bitmap = reinterpret_cast<uint32_t*>(w);
 }
 
 ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
@@ -776,7 +791,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
     return fail(LS_ERR_INVALID, "candidates %d (LS_CAND_BLOCKS or LS_CAND_TOKENS)",
                 p->candidates);
   const bool tok_cands = p->candidates == LS_CAND_TOKENS;
-  if (p->approx < 0 || p->approx > 2) return fail(LS_ERR_INVALID, "approx %d (0, 1 or 2)", p->approx);
+  if (p->approx < 0 || p->approx > 1) return fail(LS_ERR_INVALID, "approx %d (0 or 1)", p->approx);
   if (p->approx && !tokens) return fail(LS_ERR_UNSUPPORTED, "approx is for LS_SEL_TOKENS");
   if (tok_cands && (!tokens || !cand_blocks))
     return fail(LS_ERR_INVALID, "LS_CAND_TOKENS needs LS_SEL_TOKENS and a candidate list");
@@ -870,13 +885,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
     ta.selected_count = selected_count;
     return hip_status(ls::launch_topk(ta, stream), "top-k kernel launch");
   }
-  a.hist = reinterpret_cast<uint32_t*>(w);
-  w += align_up(2 * B * ls::kIdxBins * sizeof(uint32_t));
-  a.ctl = reinterpret_cast<uint32_t*>(w);
-  w += align_up(B * 4 * sizeof(uint32_t));
-  a.cand = reinterpret_cast<uint2*>(w);
-  w += align_up(B * U * sizeof(uint2));
-  a.bitmap = reinterpret_cast<uint32_t*>(w);
+  token_topk_layout(a, w, B, U);
   return hip_status(ls::launch_indexer_token_select(a, stream), "indexer selection launches");
 }
 
@@ -1240,13 +1249,7 @@ ls_status ls_pq_select(const void* q, int32_t q_dtype, int32_t num_heads,
   int tiles = 128;
   while (tiles > 4 && (long long)B * ((U + 16 * tiles - 1) / (16 * tiles)) < 512) tiles /= 2;
   a.tiles_per_wg = tiles;
-  a.hist = reinterpret_cast<uint32_t*>(w);
-  w += align_up(2 * B * ls::kIdxBins * sizeof(uint32_t));
-  a.ctl = reinterpret_cast<uint32_t*>(w);
-  w += align_up(B * 4 * sizeof(uint32_t));
-  a.cand = reinterpret_cast<uint2*>(w);
-  w += align_up(B * U * sizeof(uint2));
-  a.bitmap = reinterpret_cast<uint32_t*>(w);
+  token_topk_layout(a, w, B, U);
   return hip_status(ls::launch_pq_select(a, stream), "PQ selection launches");
 }
 

@@ -129,8 +129,10 @@ hipError_t launch_step_item(const ScoreArgs& sa, const TopkArgs& ta, const AttnA
 
 // Learned-indexer selection (k_indexer.hip): scoring of tokens (fp8 keys) or
 // blocks (bf16 block-mean keys) and the token top-k.
-constexpr int kIdxBins = 4096;          // first radix digit: score key bits [31:20]
+constexpr int kIdxBins = 4096;          // buckets of the remapped score
+constexpr int kIdxCoarse = 256;         // first digit: bucket >> 4 (the histogram's bins)
 constexpr int kIdxMarkUnits = 4096;     // units per mark workgroup (score row strides are multiples)
+constexpr int kIdxMinWgUnits = 64;      // units per scoring workgroup at least (score-range slots)
 constexpr int kIdxMaxUnits = 262144;    // units per request (token mode)
 
 enum { kIdxTokens = 0, kIdxBlocks = 1 };
@@ -158,10 +160,12 @@ struct IndexerArgs {
   int32_t tiles_per_wg;        // multiple of 4, <= 128
   int32_t n_sink, n_recent;    // blocks mode: forced blocks (not scored)
   float* scores;               // [B][max_units]
-  uint32_t* hist;              // tokens: [2][B][kIdxBins] (first / second digit)
+  float2* range;               // tokens: [B][max_units / kIdxMinWgUnits] (min, max) of the
+                               // valid scores of each scoring workgroup
+  uint32_t* hist;              // tokens: [B][kIdxCoarse] first-digit histogram
   int32_t topk;
   int32_t max_selected;
-  uint32_t* ctl;               // tokens: [B][4] (candidates, arrivals)
+  uint32_t* ctl;               // tokens: [B][4] (candidates, arrivals, remap min, remap scale)
   uint2* cand;                 // tokens: [B][max_units] (key, unit) of the threshold bucket
   uint32_t* bitmap;            // tokens: [B][max_units / 32]
   int32_t* selected;           // tokens: [B][max_selected]
@@ -169,12 +173,13 @@ struct IndexerArgs {
 };
 
 hipError_t launch_indexer_score(const IndexerArgs& a, int mode, hipStream_t st);
-// the token top-k's two halves: zero the histograms and counters (before
-// the scoring), mark + finish (after it)
-hipError_t launch_indexer_zero(const IndexerArgs& a, hipStream_t st);
+// the token top-k after the scoring (which leaves every workgroup's score
+// range and clears the request's histogram and counters): the histogram of
+// the remapped scores, then mark + finish
+hipError_t launch_indexer_hist(const IndexerArgs& a, hipStream_t st);
 hipError_t launch_indexer_mark(const IndexerArgs& a, hipStream_t st);
-// PQ32 coarse selection (k_pq.hip): zero, coarse scores of the complete
-// pages' tokens from their codes, mark + finish
+// PQ32 coarse selection (k_pq.hip): coarse scores of the complete pages'
+// tokens from their codes, histogram, mark + finish
 hipError_t launch_pq_select(const IndexerArgs& a, hipStream_t st);
 
 // One-time SnapKV-style selection and gather (k_snapkv.hip).
@@ -216,7 +221,7 @@ struct PqArgs {
 hipError_t launch_pq_encode(const PqArgs& a, hipStream_t st);
 hipError_t launch_pq_train(const PqArgs& a, const int32_t* init_tokens, int iters,
                            hipStream_t st);
-// zero the histogram and counters, score, mark + finish (three launches)
+// score, histogram, mark + finish (three launches)
 hipError_t launch_indexer_token_select(const IndexerArgs& a, hipStream_t st);
 
 // Sparse MLA attention (k_mla.hip): one workgroup per (request, 16 query

@@ -238,6 +238,7 @@ def test_indexer_token_candidates_and_approx_validation():
     assert call(_iparams(candidates=_lib.LS_CAND_TOKENS, granularity=_lib.LS_SEL_BLOCKS),
                 pool=_ipool(dtype=_lib.LS_DTYPE_BF16)) == _lib.LS_ERR_INVALID
     assert call(_iparams(approx=3)) == _lib.LS_ERR_INVALID
+    assert call(_iparams(approx=2)) == _lib.LS_ERR_INVALID
     assert call(_iparams(approx=1, granularity=_lib.LS_SEL_BLOCKS), cand=None,
                 pool=_ipool(dtype=_lib.LS_DTYPE_BF16)) == _lib.LS_ERR_UNSUPPORTED
     assert call(_iparams(candidates=_lib.LS_CAND_TOKENS),
