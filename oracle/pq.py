@@ -28,12 +28,22 @@ Readings where the page leaves a step open:
 * Only keys of complete pages have codes (a page is encoded when it fills);
   the tokens of the partial last page are the "recent keys", scored exactly.
 * Ranking keys of both passes are (score desc, token asc).
+* Miss filter ("Retrieving and refining candidates"): the candidates whose
+  original key is resident are kept; a miss is dropped when its approximate
+  score is below theta = s_(k) - sd, read as: s_(k) the k-th largest
+  approximate score among all of the request's candidates (hits and misses;
+  the smallest when there are at most k), sd the sample standard deviation
+  (denominator n - 1; 0 for fewer than two) of those same scores, both in
+  float64 from the fp32 scores; "below" is strict, so a score equal to theta
+  is kept.
 
 Parity status: pinned by tests/test_oracle_pq.py (hand-worked k-means and
 fixed-point means, brute-force nearest centroids with exact rationals, codes
 of keys that are centroids, the reduction of the coarse score to the exact
 indexer score when every subvector is a centroid, and the reduction of the
-two-pass selection to the exact token top-k when C covers every token).
+two-pass selection to the exact token top-k when C covers every token);
+the miss filter by hand-worked thresholds (sample versus population
+deviation, the k-th largest, equality kept, hits kept).
 """
 
 from __future__ import annotations
@@ -155,3 +165,27 @@ def pq_refine_select(q_idx_bits: np.ndarray, head_w: np.ndarray, key_bits: np.nd
     pick = select_tokens(exact, topk)
     return {"coarse": coarse, "candidates": cand, "refined": refined, "exact": exact,
             "selected": sorted(int(refined[i]) for i in pick)}
+
+
+def pq_miss_filter(tokens: Sequence[int], scores: np.ndarray, resident: np.ndarray,
+                   topk: int) -> Dict:
+    """Miss filter before the exact rerank (LeanSparse §5, "Retrieving and
+    refining candidates"): of the candidates `tokens` with approximate scores
+    `scores` (fp32 values) and residency flags `resident` (the original key is
+    on the GPU), keep every hit and every miss whose score is at least
+    theta = s_(min(k, n)) - sd, with s_(j) the j-th largest score and sd the
+    sample standard deviation of the n scores (0 when n < 2), in float64.
+    Returns the kept tokens (ascending), theta, and the number of misses kept
+    (the ones whose keys cross the host link)."""
+    t = np.asarray(tokens, dtype=np.int64)
+    s = np.asarray(scores, dtype=np.float64).astype(np.float32).astype(np.float64)
+    res = np.asarray(resident, dtype=bool)
+    n = len(t)
+    if n == 0:
+        return {"kept": [], "theta": float("nan"), "misses_kept": 0}
+    kth = np.sort(s)[::-1][min(max(topk, 1), n) - 1]
+    sd = float(np.std(s, ddof=1)) if n >= 2 else 0.0
+    theta = float(kth) - sd
+    keep = res | (s >= theta)
+    return {"kept": sorted(int(x) for x in t[keep]), "theta": theta,
+            "misses_kept": int((keep & ~res).sum())}

@@ -153,3 +153,48 @@ def test_two_pass_cannot_recover_a_token_the_coarse_pass_drops():
     assert res["candidates"] == list(range(20))
     tail = set(range(batch.num_complete(0) * 16, int(batch.seq_lens[0])))
     assert set(res["selected"]) <= set(range(20)) | tail
+
+
+# ------------------------------------------------------------- miss filter
+
+def test_miss_filter_hand_worked_sample_deviation_and_equality():
+    from oracle.pq import pq_miss_filter
+    # scores 6, 4, 2 (tokens 10, 11, 12), all misses, k = 1: s_(1) = 6; mean 4,
+    # squared deviations 4 + 0 + 4 = 8, sample variance 8 / 2 = 4, sd = 2:
+    # theta = 4. The score 4 equals theta and stays; 2 is dropped. (With the
+    # population deviation sqrt(8/3) = 1.63, theta = 4.37 would drop 4 too;
+    # with a strict "above theta", 4 would go.)
+    r = pq_miss_filter([10, 11, 12], np.array([6.0, 4.0, 2.0]), np.zeros(3, bool), 1)
+    assert r["theta"] == 4.0
+    assert r["kept"] == [10, 11] and r["misses_kept"] == 2
+    # a hit is kept whatever its score
+    r = pq_miss_filter([10, 11, 12], np.array([6.0, 4.0, 2.0]), np.array([0, 0, 1], bool), 1)
+    assert r["kept"] == [10, 11, 12] and r["misses_kept"] == 2
+
+
+def test_miss_filter_hand_worked_kth_largest():
+    from oracle.pq import pq_miss_filter
+    # scores 1, 9, 5, 7, 4 (tokens 0..4), k = 1: s_(1) = 9; mean 5.2, squared
+    # deviations 17.64 + 14.44 + 0.04 + 3.24 + 1.44 = 36.8, sample variance
+    # 9.2, sd 3.0332: theta = 5.9668 keeps 9 and 7 only. (The k-th smallest,
+    # 1, would keep everything; the (k+1)-th largest, 7, would keep 5 and 4.)
+    s = np.array([1.0, 9.0, 5.0, 7.0, 4.0])
+    r = pq_miss_filter(range(5), s, np.zeros(5, bool), 1)
+    assert abs(r["theta"] - (9.0 - np.sqrt(9.2))) < 1e-12
+    assert r["kept"] == [1, 3]
+    # k = 3: s_(3) = 5, theta = 1.9668: only 1 is dropped
+    assert pq_miss_filter(range(5), s, np.zeros(5, bool), 3)["kept"] == [1, 2, 3, 4]
+
+
+def test_miss_filter_degenerate_sizes():
+    from oracle.pq import pq_miss_filter
+    # k >= n: s_(k) is the smallest score, theta <= every score: all kept
+    s = np.array([3.0, -1.0, 8.0])
+    assert pq_miss_filter([5, 6, 7], s, np.zeros(3, bool), 3)["kept"] == [5, 6, 7]
+    assert pq_miss_filter([5, 6, 7], s, np.zeros(3, bool), 50)["kept"] == [5, 6, 7]
+    # one candidate: sd = 0, theta = its score: kept
+    assert pq_miss_filter([9], np.array([2.5]), np.zeros(1, bool), 1)["kept"] == [9]
+    assert pq_miss_filter([], np.zeros(0), np.zeros(0, bool), 4)["kept"] == []
+    # scores are taken as fp32: 0.1 and its fp32 rounding are the same score
+    a = pq_miss_filter([0, 1], np.array([0.1, np.float32(0.1)]), np.zeros(2, bool), 1)
+    assert a["theta"] == float(np.float32(0.1)) and a["kept"] == [0, 1]
