@@ -552,12 +552,15 @@ def summarize_profiles(args) -> int:
 
 # ------------------------------------------------- learned-indexer paths ----
 
-def indexer_step_bytes(cfg, coarse: bool, pq: bool = False):
+def indexer_step_bytes(cfg, coarse: bool, pq: bool = False, kept_mean=None):
     """Algorithmic bytes of one learned-indexer step (per call, all requests).
     Token keys are fp8 (1 B per dim) with one fp32 scale per token; latent
     rows are 576 bf16 (the whole row is read: key = all 576 dims). PQ32: 32 B
     of codes per complete-page token, then the candidates' keys, and the
-    codes of the pages that filled this step (keys read, codes written)."""
+    codes of the pages that filled this step (keys read, codes written).
+    With the miss filter (kept_mean: kept candidates per request, measured),
+    the coarse scores are written and read back, the filter reads the
+    residency bits, and only the kept candidates' keys are read."""
     B, L, H, D, P = cfg.batch, cfg.context, cfg.index_heads, cfg.index_dim, cfg.page_size
     k = cfg.topk_tokens
     dk = cfg.kv_lora_dim + cfg.rope_dim
@@ -570,6 +573,11 @@ def indexer_step_bytes(cfg, coarse: bool, pq: bool = False):
         d["candidates"] = B * C * 4 * 2                   # written, then read
         d["candidate_keys"] = B * (C + L % P) * (D + 4)
         d["encode_new_pages"] = B * P * (D + 4 + 32)
+        if kept_mean is not None:
+            d["candidate_keys"] = int(round(B * (kept_mean + L % P) * (D + 4)))
+            d["coarse_scores"] = B * (L // P) * P * 4 + B * C * 4   # written; candidates' read
+            d["residency_bits"] = B * C * 4
+            d["kept"] = B * C * 4 * 2
     elif coarse:
         nb = L // P
         kb = cfg.coarse_topk_blocks + 1                  # + the forced last block
@@ -587,6 +595,7 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
     (128K workload), coarse block top-k -> exact token top-k among the kept
     blocks (950K workload), or PQ32 coarse top-C -> exact rerank of the
     candidates (128K workload); then sparse MLA over the selected tokens."""
+    import numpy as np
     import torch
     import query_aware_sparse_ls_amd as ls
     from workloads import (COARSE_TO_FINE_950K, INDEXER_128K, PQ32_128K, indexer_queries,
@@ -642,6 +651,20 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
                                    device=dev),
                    ws_mla=torch.empty(ls.sparse_mla_decode_workspace_size(B, cfg.mla_heads, k),
                                       dtype=torch.uint8, device=dev))
+        if pq and args.miss_filter:
+            # the keys a previous step left resident: a seeded Bernoulli mask
+            # with the given hit rate (no cache is simulated)
+            hits = np.random.default_rng(cfg.seed + 101 * i).random((B, nb * P)) < args.miss_filter
+            words = (nb * P + 31) // 32
+            padded = np.zeros((B, words * 32), dtype=np.uint64)
+            padded[:, :nb * P] = hits
+            w32 = (padded.reshape(B, words, 32) << np.arange(32, dtype=np.uint64)).sum(-1)
+            rep.update(res=torch.from_numpy(w32.astype(np.uint32).view(np.int32)).to(dev),
+                       csc=torch.empty(B, ls.indexer_score_stride("tokens", nb * P),
+                                       device=dev),
+                       kept=torch.empty(B, cfg.n_candidates, dtype=torch.int32, device=dev),
+                       kcnt=torch.empty(B, dtype=torch.int32, device=dev),
+                       mk=torch.empty(B, dtype=torch.int32, device=dev))
         if pq:
             C = cfg.n_candidates
             rep.update(cand=torch.empty(B, C, dtype=torch.int32, device=dev),
@@ -676,9 +699,9 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
         inp = rp["inp"]
         ls.indexer_select(rp["q_idx"], rp["w"], inp.idx_keys, P, rp["ib"], granularity="tokens",
                           topk=k, max_selected=k, key_scales=inp.idx_scale,
-                          cand_blocks=rp.get("cand", rp.get("bsel")),
-                          cand_counts=rp.get("ccnt", rp.get("bcnt")), token_candidates=pq,
-                          approx=args.approx_topk,
+                          cand_blocks=rp.get("kept", rp.get("cand", rp.get("bsel"))),
+                          cand_counts=rp.get("kcnt", rp.get("ccnt", rp.get("bcnt"))),
+                          token_candidates=pq, approx=args.approx_topk,
                           selected=rp["sel"], selected_count=rp["cnt"], workspace=rp["ws_t"])
 
     def c_encode(rp):
@@ -686,7 +709,12 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
 
     def c_pq(rp):
         ls.pq_select(rp["q_idx"], rp["w"], codes, codebooks, rp["ib"], cfg.n_candidates,
-                     candidates=rp["cand"], counts=rp["ccnt"], workspace=rp["ws_c"])
+                     candidates=rp["cand"], counts=rp["ccnt"], scores_out=rp.get("csc"),
+                     workspace=rp["ws_c"])
+
+    def c_filter(rp):
+        ls.pq_filter_misses(rp["cand"], rp["ccnt"], rp["csc"], rp["res"], k, kept=rp["kept"],
+                            kept_counts=rp["kcnt"], misses_kept=rp["mk"])
 
     def c_mla(rp):
         ls.sparse_mla_decode(rp["q_mla"], rp["inp"].latent, rp["kb"], rp["sel"], rp["cnt"],
@@ -694,6 +722,7 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
 
     calls = ([("coarse_block_select", c_blocks)] if coarse else []) + \
         ([("pq_encode_new_pages", c_encode), ("pq_coarse_select", c_pq)] if pq else []) + \
+        ([("pq_miss_filter", c_filter)] if pq and args.miss_filter else []) + \
         [("token_select", c_tokens), ("sparse_mla", c_mla)]
 
     def step(rp):
@@ -741,7 +770,17 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
         b.record()
         torch.cuda.synchronize()
         per[name] = a.elapsed_time(b) / n
-    nbytes = indexer_step_bytes(cfg, coarse, pq)
+    filt = None
+    if pq and args.miss_filter:
+        # what the filter did in the last step of every replica
+        kc = torch.stack([rp["kcnt"] for rp in reps]).float()
+        mk = torch.stack([rp["mk"] for rp in reps]).float()
+        cc = torch.stack([rp["ccnt"] for rp in reps]).float()
+        filt = {"hit_rate": args.miss_filter, "candidates_mean": round(cc.mean().item(), 1),
+                "kept_mean": round(kc.mean().item(), 1),
+                "misses_kept_mean": round(mk.mean().item(), 1),
+                "misses_dropped_mean": round((cc - kc).mean().item(), 1)}
+    nbytes = indexer_step_bytes(cfg, coarse, pq, kept_mean=filt["kept_mean"] if filt else None)
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
     dom = max(per, key=per.get)
     if dom == "token_select":
@@ -810,6 +849,7 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
                       **({"coarse_topk_blocks": cfg.coarse_topk_blocks} if coarse else {}),
                       **({"n_candidates": cfg.n_candidates, "kmeans_iters": cfg.kmeans_iters}
                          if pq else {}),
+                      **({"miss_filter": filt} if filt else {}),
                       "token_topk": ("approximate (remapped first digit, boundary bucket "
                                      "in index order)" if args.approx_topk else "exact")},
            "step_bytes": nbytes["total"], "step_bytes_breakdown": nbytes,
@@ -1684,6 +1724,9 @@ def main(argv=None) -> int:
                     help="indexer paths: the approximate token top-k (early exit after the "
                          "remapped first digit, the boundary bucket filled in index order) "
                          "instead of the exact one; reports its recall")
+    ap.add_argument("--miss-filter", type=float, default=0.0, metavar="HIT_RATE",
+                    help="pq path: the miss filter before the exact rerank, with a seeded "
+                         "residency mask of this hit rate (0: no filter)")
     ap.add_argument("--score", choices=("mean", "bounds"), default="mean",
                     help="block-topk path: block-mean summaries (default) or Quest bounds")
     ap.add_argument("--path", choices=("block-topk", "ragged", "indexer", "coarse-to-fine",

@@ -662,13 +662,44 @@ ls_status ls_pq_train(const void* keys, const float* key_scales, ls_pool key_poo
  * / batch as in ls_indexer_select. scores_out: NULL or
  * [batch][ls_indexer_score_stride(LS_SEL_TOKENS, max_blocks * page_size)]
  * fp32 (s~ at token t). workspace: >= ls_indexer_select_workspace_size(batch,
- * LS_SEL_TOKENS, max_blocks * page_size) bytes. Three launches: zero, coarse
- * scores + histogram, then the token top-k of ls_indexer_select. */
+ * LS_SEL_TOKENS, max_blocks * page_size) bytes. Three launches: the coarse
+ * scores, then the token top-k of ls_indexer_select (histogram of the
+ * remapped scores, mark + finish). */
 ls_status ls_pq_select(const void* q, int32_t q_dtype, int32_t num_heads,
                        const float* head_weights, const uint8_t* codes, const void* codebooks,
                        ls_pool key_pool, ls_batch batch, int32_t n_candidates,
                        int32_t* candidates, int32_t* candidate_counts, float* scores_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Miss filter before the exact rerank (LeanSparse §5, "Retrieving and
+ * refining candidates"): of request r's candidates candidates[r][0 ..
+ * counts[r]-1] (token ids, e.g. from ls_pq_select), every one whose original
+ * indexer key is resident on the GPU is kept, and a miss is kept only when its
+ * approximate score is at least
+ *   theta = s_(j) - sd,   j = min(topk, n),
+ * s_(j) the j-th largest approximate score of the n candidates and sd their
+ * sample standard deviation (denominator n - 1; 0 for n < 2), computed in
+ * float64 from the fp32 scores (a miss whose score equals theta is kept).
+ * Only the kept misses need their keys fetched over the host link.
+ * candidates, candidate_counts: [batch][cap] int32, [batch] int32 (counts
+ *   clamped to [0, cap]); an entry outside [0, score_stride) is not a
+ *   candidate (not counted, not kept). cap: 1 .. 4096.
+ * scores:   [batch][score_stride] fp32, the approximate score at token t
+ *   (ls_pq_select's scores_out, score_stride = its row stride).
+ * resident: [batch][resident_words] uint32 bitmap, bit t % 32 of word t / 32
+ *   set when token t's key is resident; tokens at or past 32 *
+ *   resident_words are misses. May be NULL when resident_words is 0.
+ * topk:     the final selection size k (>= 1).
+ * kept, kept_counts: [batch][cap] int32 (the kept candidates in their
+ *   input order, -1 after), [batch] int32. kept may be candidates itself.
+ * misses_kept: NULL or [batch] int32, the number of kept misses.
+ * One launch, one workgroup per request; deterministic (the float64 sums
+ * are reduced in a fixed order). */
+ls_status ls_pq_filter_misses(const int32_t* candidates, const int32_t* candidate_counts,
+                              int32_t cap, const float* scores, int32_t score_stride,
+                              const uint32_t* resident, int32_t resident_words,
+                              int32_t batch_size, int32_t topk, int32_t* kept,
+                              int32_t* kept_counts, int32_t* misses_kept, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Introspection                                                             */

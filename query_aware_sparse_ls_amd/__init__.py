@@ -527,6 +527,36 @@ def pq_select(q: torch.Tensor, head_weights: torch.Tensor, codes: torch.Tensor,
     return candidates, counts
 
 
+def pq_filter_misses(candidates: torch.Tensor, counts: torch.Tensor, scores: torch.Tensor,
+                     resident: Optional[torch.Tensor], topk: int, *,
+                     kept: Optional[torch.Tensor] = None,
+                     kept_counts: Optional[torch.Tensor] = None,
+                     misses_kept: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Miss filter over candidates [B][cap] (counts [B]) with approximate
+    scores [B][stride] at token t and a residency bitmap [B][words] int32
+    (bit t % 32 of word t / 32; None: every key a miss). Returns (kept
+    [B][cap], kept_counts [B], misses_kept [B])."""
+    _need(candidates, torch.int32); _need(counts, torch.int32); _need(scores, torch.float32)
+    B, cap = candidates.shape
+    dev = candidates.device
+    if resident is not None:
+        _need(resident, torch.int32)
+    words = 0 if resident is None else int(resident.shape[1])
+    if kept is None:
+        kept = torch.empty(B, cap, dtype=torch.int32, device=dev)
+    if kept_counts is None:
+        kept_counts = torch.empty(B, dtype=torch.int32, device=dev)
+    if misses_kept is None:
+        misses_kept = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(kept, torch.int32); _need(kept_counts, torch.int32); _need(misses_kept, torch.int32)
+    check(_L.ls_pq_filter_misses(candidates.data_ptr(), counts.data_ptr(), int(cap),
+                                 scores.data_ptr(), int(scores.shape[1]), _ptr(resident), words,
+                                 int(B), int(topk), kept.data_ptr(), kept_counts.data_ptr(),
+                                 misses_kept.data_ptr(), _stream(stream)))
+    return kept, kept_counts, misses_kept
+
+
 # ------------------------------------------------------------ sink + window
 
 def window_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

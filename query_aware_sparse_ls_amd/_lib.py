@@ -86,6 +86,8 @@ _SIGS = {
                               _P]),
     "ls_pq_select": (C.c_int, [_P, C.c_int32, C.c_int32, _P, _P, _P, LsPool, LsBatch, C.c_int32,
                                _P, _P, _P, _P, C.c_size_t, _P]),
+    "ls_pq_filter_misses": (C.c_int, [_P, _P, C.c_int32, _P, C.c_int32, _P, C.c_int32, C.c_int32,
+                                      C.c_int32, _P, _P, _P, _P]),
     "ls_last_error": (C.c_char_p, []),
     "ls_version": (C.c_char_p, []),
     "ls_attn_num_splits": (C.c_int32, [C.c_int32]),

@@ -396,4 +396,220 @@ hipError_t launch_pq_select(const IndexerArgs& a, hipStream_t st) {
   return launch_indexer_mark(a, st);
 }
 
+// --------------------------------------------------------- miss filter ----
+
+// LeanSparse §5, "Retrieving and refining candidates": before the original
+// keys of the candidates are fetched, every candidate whose key is resident
+// is kept, and a miss is kept only when its approximate score is at least
+// theta = s_(j) - sd, j = min(k, n), s_(j) the j-th largest approximate score
+// of the n candidates and sd their sample standard deviation (0 for n < 2),
+// both in float64. One workgroup per request
+// (consecutive entries, so that the kept ones compact in order): float64
+// sums reduced in a fixed order (the result does not depend on scheduling),
+// the j-th largest by a radix select over the order-preserving score key
+// (four 8-bit digits), then a workgroup scan places the kept candidates.
+// Eight candidates per thread.
+constexpr int kPqFilterThreads = 512;
+constexpr int kPqFilterPer = kPqFilterMaxCand / kPqFilterThreads;
+constexpr int kPqFilterWaves = kPqFilterThreads / kWave;
+
+struct PqFilterLds {
+  double dred[2][kPqFilterWaves];
+  int ired[kPqFilterWaves];
+  uint32_t hist[2][256];   // the radix rounds alternate between two histograms
+  uint32_t kmin[kPqFilterWaves], kmax[kPqFilterWaves];
+  int digit[2], above[2];
+};
+
+// Workgroup sums (float64) of a and b in a fixed order: lanes by a
+// butterfly, then the waves in order. Every thread gets them. Synchronises.
+__device__ __forceinline__ void pq_block_sum2(double& a, double& b, double (*red)[kPqFilterWaves]) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o, kWave);
+    b += __shfl_xor(b, o, kWave);
+  }
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    red[0][wave] = a;
+    red[1][wave] = b;
+  }
+  __syncthreads();
+  a = 0.0;
+  b = 0.0;
+#pragma unroll
+  for (int w = 0; w < kPqFilterWaves; ++w) {
+    a += red[0][w];
+    b += red[1][w];
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix sum over the workgroup in thread order; *total = sum.
+__device__ __forceinline__ int pq_block_scan(int v, int* red, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int inc = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) red[wave] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kPqFilterWaves; ++w) {
+    before += w < wave ? red[w] : 0;
+    tot += red[w];
+  }
+  *total = tot;
+  return before + inc - v;
+}
+
+// The float whose score_key is k.
+__device__ __forceinline__ float pq_key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__global__ __launch_bounds__(kPqFilterThreads) void pq_filter_kernel(PqFilterArgs a) {
+  __shared__ PqFilterLds sh;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+  int c = a.counts[r];
+  c = c < 0 ? 0 : (c > a.cap ? a.cap : c);
+  // this thread's candidates (entries kPqFilterPer tid + j), every load of a
+  // round issued before the dependent ones
+  int tok[kPqFilterPer];
+  float sc[kPqFilterPer];
+  bool val[kPqFilterPer], res[kPqFilterPer];
+#pragma unroll
+  for (int j = 0; j < kPqFilterPer; ++j) {
+    const int i = kPqFilterPer * tid + j;
+    tok[j] = i < c ? a.candidates[(size_t)r * a.cap + i] : -1;
+  }
+  uint32_t rw[kPqFilterPer];
+#pragma unroll
+  for (int j = 0; j < kPqFilterPer; ++j) {
+    val[j] = tok[j] >= 0 && tok[j] < a.score_stride;   // other ids are not candidates
+    sc[j] = val[j] ? a.scores[(size_t)r * a.score_stride + tok[j]] : 0.0f;
+    const int w = tok[j] >> 5;
+    rw[j] = (val[j] && w < a.resident_words) ? a.resident[(size_t)r * a.resident_words + w] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kPqFilterPer; ++j) res[j] = (rw[j] >> (tok[j] & 31)) & 1u;
+  if (tid < 256) sh.hist[0][tid] = 0u;
+  // n and the mean, then the sample standard deviation
+  double nsum = 0.0, s1 = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPqFilterPer; ++j) {
+    nsum += val[j] ? 1.0 : 0.0;
+    s1 += val[j] ? (double)sc[j] : 0.0;
+  }
+  pq_block_sum2(nsum, s1, sh.dred);
+  const int n = (int)nsum;
+  const double mean = s1 / (double)(n > 0 ? n : 1);
+  double s2 = 0.0, unused = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPqFilterPer; ++j) {
+    const double d = (double)sc[j] - mean;
+    s2 += val[j] ? d * d : 0.0;
+  }
+  pq_block_sum2(s2, unused, sh.dred);
+  const double sd = n >= 2 ? sqrt(s2 / (double)(n - 1)) : 0.0;
+  // the j-th largest score, j = min(k, n): radix select over the keys in
+  // 8-bit digits below the bits that every key shares (the top bits of
+  // scores of one magnitude agree, and counting them would pile every
+  // candidate onto one LDS counter); round d counts into hist[d & 1] while
+  // the other one is cleared for the next round
+  double theta = 0.0;
+  if (n > 0) {
+    int need = a.topk < n ? a.topk : n;
+    uint32_t key[kPqFilterPer], kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < kPqFilterPer; ++j) {
+      key[j] = score_key(sc[j]);
+      kmin = val[j] ? min(kmin, key[j]) : kmin;
+      kmax = val[j] ? max(kmax, key[j]) : kmax;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, kWave));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
+    }
+    if (lane == 0) {
+      sh.kmin[tid / kWave] = kmin;
+      sh.kmax[tid / kWave] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kPqFilterWaves; ++w) {
+      kmin = min(kmin, sh.kmin[w]);
+      kmax = max(kmax, sh.kmax[w]);
+    }
+    const uint32_t diff = kmin ^ kmax;
+    int top = diff ? 31 - __clz(diff) : -1;           // highest undecided bit
+    uint32_t pmask = top >= 0 ? ~((2u << top) - 1u) : 0xFFFFFFFFu;
+    if (top == 31) pmask = 0u;
+    uint32_t prefix = kmin & pmask;
+    for (int d = 0; top >= 0; ++d) {
+      const int width = top >= 7 ? 8 : top + 1;
+      const int shift = top - width + 1, hb = d & 1;
+      const uint32_t dm = (1u << width) - 1u;
+#pragma unroll
+      for (int j = 0; j < kPqFilterPer; ++j)
+        if (val[j] && (key[j] & pmask) == prefix) atomicAdd(&sh.hist[hb][(key[j] >> shift) & dm], 1u);
+      if (tid < 256) sh.hist[hb ^ 1][tid] = 0u;
+      __syncthreads();
+      if (tid < kWave) {
+        // lane l owns bins 4l .. 4l + 3; the digit holding the need-th largest
+        int cnt = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) cnt += (int)sh.hist[hb][4 * lane + b];
+        const int below = wave_incl_scan(cnt, lane) - cnt;
+        const int tot = __shfl(below + cnt, kWave - 1, kWave);
+        int above = tot - below - cnt;
+        if (above < need && above + cnt >= need) {
+          for (int b = 3; b >= 0; --b) {
+            const int h = (int)sh.hist[hb][4 * lane + b];
+            if (above + h >= need) {
+              sh.digit[hb] = 4 * lane + b;
+              sh.above[hb] = above;
+              break;
+            }
+            above += h;
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)sh.digit[hb] << shift;
+      pmask |= dm << shift;
+      need -= sh.above[hb];
+      top -= width;
+    }
+    theta = (double)pq_key_score(prefix) - sd;
+  }
+  // keep hits, and misses at or above theta; compact in candidate order (the
+  // kept count in the low 16 bits of the scanned value, kept misses above)
+  bool keep[kPqFilterPer];
+  int nk = 0, nm = 0;
+#pragma unroll
+  for (int j = 0; j < kPqFilterPer; ++j) {
+    keep[j] = val[j] && (res[j] || (double)sc[j] >= theta);
+    nk += keep[j];
+    nm += keep[j] && !res[j];
+  }
+  int tot;
+  const int ex = pq_block_scan(nk | (nm << 16), sh.ired, &tot);
+  const int total = tot & 0xFFFF, misses = tot >> 16;
+  int pos = ex & 0xFFFF;
+  int32_t* out = a.kept + (size_t)r * a.cap;
+#pragma unroll
+  for (int j = 0; j < kPqFilterPer; ++j)
+    if (keep[j]) out[pos++] = tok[j];
+  for (int i = total + tid; i < a.cap; i += kPqFilterThreads) out[i] = -1;
+  if (tid == 0) {
+    a.kept_counts[r] = total;
+    if (a.misses_kept) a.misses_kept[r] = misses;
+  }
+}
+
+hipError_t launch_pq_filter(const PqFilterArgs& a, int batch, hipStream_t st) {
+  hipLaunchKernelGGL(pq_filter_kernel, dim3(batch), dim3(kPqFilterThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace ls

@@ -1253,4 +1253,35 @@ ls_status ls_pq_select(const void* q, int32_t q_dtype, int32_t num_heads,
   return hip_status(ls::launch_pq_select(a, stream), "PQ selection launches");
 }
 
+ls_status ls_pq_filter_misses(const int32_t* candidates, const int32_t* candidate_counts,
+                              int32_t cap, const float* scores, int32_t score_stride,
+                              const uint32_t* resident, int32_t resident_words,
+                              int32_t batch_size, int32_t topk, int32_t* kept,
+                              int32_t* kept_counts, int32_t* misses_kept, hipStream_t stream) {
+  if (batch_size < 0) return fail(LS_ERR_INVALID, "batch_size %d must be >= 0", batch_size);
+  if (cap < 1 || cap > ls::kPqFilterMaxCand)
+    return fail(LS_ERR_UNSUPPORTED, "cap %d (supported: 1 .. %d)", cap, ls::kPqFilterMaxCand);
+  if (score_stride < 1) return fail(LS_ERR_INVALID, "score_stride %d must be >= 1", score_stride);
+  if (resident_words < 0) return fail(LS_ERR_INVALID, "resident_words %d must be >= 0", resident_words);
+  if (topk < 1) return fail(LS_ERR_INVALID, "topk %d must be >= 1", topk);
+  if (batch_size == 0) return ok();
+  if (!candidates || !candidate_counts || !scores || !kept || !kept_counts)
+    return fail(LS_ERR_INVALID, "candidates, counts, scores, kept and kept_counts must be non-null");
+  if (resident_words > 0 && !resident)
+    return fail(LS_ERR_INVALID, "resident must be non-null when resident_words > 0");
+  ls::PqFilterArgs a{};
+  a.candidates = candidates;
+  a.counts = candidate_counts;
+  a.cap = cap;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.resident = resident;
+  a.resident_words = resident_words;
+  a.topk = topk;
+  a.kept = kept;
+  a.kept_counts = kept_counts;
+  a.misses_kept = misses_kept;
+  return hip_status(ls::launch_pq_filter(a, batch_size, stream), "PQ miss filter launch");
+}
+
 }  // extern "C"

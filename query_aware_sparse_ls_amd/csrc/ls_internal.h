@@ -224,6 +224,23 @@ hipError_t launch_pq_train(const PqArgs& a, const int32_t* init_tokens, int iter
 // score, histogram, mark + finish (three launches)
 hipError_t launch_indexer_token_select(const IndexerArgs& a, hipStream_t st);
 
+// Miss filter over PQ candidates (k_pq.hip): one workgroup per request.
+constexpr int kPqFilterMaxCand = 4096;   // candidates per request
+struct PqFilterArgs {
+  const int32_t* candidates;   // [B][cap] token ids, ascending
+  const int32_t* counts;       // [B]
+  int32_t cap;
+  const float* scores;         // [B][score_stride] approximate score at token t
+  int32_t score_stride;
+  const uint32_t* resident;    // [B][resident_words] bit t: token t's key is resident
+  int32_t resident_words;
+  int32_t topk;
+  int32_t* kept;               // [B][cap] (may be candidates itself)
+  int32_t* kept_counts;        // [B]
+  int32_t* misses_kept;        // [B] or null
+};
+hipError_t launch_pq_filter(const PqFilterArgs& a, int batch, hipStream_t st);
+
 // Sparse MLA attention (k_mla.hip): one workgroup per (request, 16 query
 // heads, kMlaSplitTokens selected tokens), then a log-sum-exp combine.
 constexpr int kMlaSplitTokens = 256;

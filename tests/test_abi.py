@@ -348,3 +348,23 @@ def test_stream_read_validation():
     assert lib.ls_stream_read(FAKE + 8, 64, FAKE, None) == _lib.LS_ERR_INVALID
     assert lib.ls_stream_read(FAKE, 40, FAKE, None) == _lib.LS_ERR_INVALID
     assert b"aligned" in lib.ls_last_error()
+
+
+def test_pq_filter_misses_validation():
+    lib = _lib.load()
+    F = FAKE
+
+    def call(cap=8, stride=16, words=1, res=F, batch=2, topk=4, cand=F, kept=F):
+        return lib.ls_pq_filter_misses(cand, F, cap, F, stride, res, words, batch, topk, kept, F,
+                                       None, None)
+
+    assert call(cap=0) == _lib.LS_ERR_UNSUPPORTED
+    assert call(cap=4097) == _lib.LS_ERR_UNSUPPORTED
+    assert call(stride=0) == _lib.LS_ERR_INVALID
+    assert call(words=-1) == _lib.LS_ERR_INVALID
+    assert call(topk=0) == _lib.LS_ERR_INVALID
+    assert call(batch=-1) == _lib.LS_ERR_INVALID
+    assert call(res=None) == _lib.LS_ERR_INVALID          # words > 0 needs a bitmap
+    assert call(cand=None) == _lib.LS_ERR_INVALID
+    assert call(kept=None) == _lib.LS_ERR_INVALID
+    assert call(batch=0, cand=None) == _lib.LS_OK         # empty batch: nothing enqueued

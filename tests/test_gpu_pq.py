@@ -241,3 +241,114 @@ def test_pq_small_pages(page_size):
         pos = {t: i for i, t in enumerate(refined.tolist())}
         gsel = sorted(pos[t] for t in sel[r, :int(n[r])].cpu().tolist())
         _check_topk(gsel, exact, list(range(len(refined))), k, f"final r{r}")
+
+
+# ------------------------------------------------------------- miss filter
+
+def _resident_bits(B, n_tokens, rate, seed):
+    """Seeded residency flags [B][n_tokens] and their bitmap [B][words] int32."""
+    g = np.random.default_rng(seed)
+    flags = g.random((B, n_tokens)) < rate
+    words = (n_tokens + 31) // 32
+    bits = np.zeros((B, words * 32), dtype=bool)
+    bits[:, :n_tokens] = flags
+    w = (bits.reshape(B, words, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(-1)
+    return flags, torch.from_numpy(w.astype(np.uint32).view(np.int32)).to(_dev())
+
+
+def test_miss_filter_hand_worked():
+    """Scores 6, 4, 2 (tokens 10 .. 12), k = 1: theta = 6 - 2 = 4 exactly; the
+    miss at 4 stays, the miss at 2 goes unless it is resident."""
+    cand = torch.tensor([[10, 11, 12, -1], [10, 11, 12, -1]], dtype=torch.int32, device=_dev())
+    cnt = torch.tensor([3, 3], dtype=torch.int32, device=_dev())
+    sc = torch.zeros(2, 16, device=_dev())
+    sc[:, 10:13] = torch.tensor([6.0, 4.0, 2.0])
+    res = torch.zeros(2, 1, dtype=torch.int32, device=_dev())
+    res[1, 0] = 1 << 12
+    kept, kn, mk = ls.pq_filter_misses(cand, cnt, sc, res, 1)
+    torch.cuda.synchronize()
+    assert kept[0].tolist() == [10, 11, -1, -1] and int(kn[0]) == 2 and int(mk[0]) == 2
+    assert kept[1].tolist() == [10, 11, 12, -1] and int(kn[1]) == 3 and int(mk[1]) == 2
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+def test_miss_filter_parity_synthetic(inplace):
+    """Seeded candidates (ascending tokens), fp32 scores and residency (40%
+    hits) for requests of 2,048, 1,000, 1, 0 and 4,096 (the cap) candidates
+    with k = 512, against the oracle; only candidates within 1e-9 of theta
+    (where the two float64 sum orders could disagree) are excused."""
+    B, cap, stride, k = 5, 4096, 20000, 512
+    counts = [2048, 1000, 1, 0, 4096]
+    g = np.random.default_rng(91)
+    cand = np.full((B, cap), -1, dtype=np.int32)
+    for r, c in enumerate(counts):
+        cand[r, :c] = np.sort(g.choice(stride, size=c, replace=False))
+    scores = (g.standard_normal((B, stride)) * 7 + 3).astype(np.float32)
+    flags, res = _resident_bits(B, stride, 0.4, 92)
+    say(f"miss filter synthetic, inplace {inplace}")
+    cand_d = torch.from_numpy(cand).to(_dev())
+    cnt_d = torch.tensor(counts, dtype=torch.int32, device=_dev())
+    sc_d = torch.from_numpy(scores).to(_dev())
+    kept, kn, mk = ls.pq_filter_misses(cand_d, cnt_d, sc_d, res, k,
+                                       kept=cand_d if inplace else None)
+    torch.cuda.synchronize()
+    kept, kn, mk = kept.cpu().numpy(), kn.cpu().numpy(), mk.cpu().numpy()
+    for r, c in enumerate(counts):
+        t = cand[r, :c]
+        want = oracle.pq.pq_miss_filter(t, scores[r, t], flags[r, t], k)
+        got = kept[r, :kn[r]].tolist()
+        assert (kept[r, kn[r]:] == -1).all()
+        near = {int(x) for x in t if abs(float(scores[r, x]) - want["theta"]) <= 1e-9 * max(1.0, abs(want["theta"]))}
+        assert set(got) ^ set(want["kept"]) <= near, r
+        assert got == sorted(got)
+        if not near:
+            assert got == want["kept"] and int(mk[r]) == want["misses_kept"]
+
+
+def test_miss_filter_in_the_pq_pipeline_full_size():
+    """The bench shape (8 x 128K, C = 2,048, k = 512): PQ candidates, the miss
+    filter with seeded residency (50% hits), then the exact rerank of the kept
+    candidates; requests 0 and 7 against the oracle's filter on the oracle's
+    coarse scores of those candidates (near theta, within the coarse scores'
+    tolerance, either decision is accepted)."""
+    cfg = PQ32_128K
+    say(f"pq + miss filter at full size: {cfg.name}")
+    inp = make_indexer_inputs(cfg, device=_dev())
+    P = cfg.page_size
+    cb, _, _ = _train(inp, 2)
+    codes = _encode_all(inp, cb)
+    b = _batch(inp)
+    stride = ls.indexer_score_stride("tokens", b.max_blocks * P)
+    sc = torch.empty((cfg.batch, stride), device=_dev())
+    cand, cnt = ls.pq_select(inp.q_idx, inp.head_w, codes, cb, b, cfg.n_candidates, scores_out=sc)
+    flags, res = _resident_bits(cfg.batch, b.max_blocks * P, 0.5, 93)
+    kept, kn, mk = ls.pq_filter_misses(cand, cnt, sc, res, cfg.topk_tokens)
+    sel, n = ls.indexer_select(inp.q_idx, inp.head_w, inp.idx_keys, P, b, granularity="tokens",
+                               topk=cfg.topk_tokens, max_selected=cfg.topk_tokens,
+                               key_scales=inp.idx_scale, cand_blocks=kept, cand_counts=kn,
+                               token_candidates=True)
+    torch.cuda.synchronize()
+    q, w = bf16_bits(inp.q_idx), inp.head_w.cpu().numpy()
+    bv = BatchView(inp.idx_indptr.cpu().numpy(), inp.idx_indices.cpu().numpy(),
+                   inp.seq_lens.cpu().numpy(), P)
+    cbb, codes_h = bf16_bits(cb), codes.cpu().numpy()
+    kb, ks = fp8_bits(inp.idx_keys), inp.idx_scale.cpu().numpy()
+    for r in (0, 7):
+        coarse = pq_token_scores(q, w, codes_h, cbb, bv, r)
+        gc = cand[r, :int(cnt[r])].cpu().tolist()
+        _check_topk(gc, coarse, list(range(len(coarse))), cfg.n_candidates, f"candidates r{r}")
+        t = np.array(gc)
+        want = oracle.pq.pq_miss_filter(t, coarse[t], flags[r, t], cfg.topk_tokens)
+        got = kept[r, :int(kn[r])].cpu().tolist()
+        tol = 1e-4 * np.abs(coarse[t]).max()
+        near = {int(x) for x in t if abs(coarse[x] - want["theta"]) <= tol}
+        assert set(got) ^ set(want["kept"]) <= near, r
+        dropped = len(gc) - len(got)
+        say(f"request {r}: {len(gc)} candidates, {int((~flags[r, t]).sum())} misses, "
+            f"{dropped} dropped, {int(mk[r])} misses kept")
+        assert dropped > 0
+        # the rerank over the kept candidates (and the partial page)
+        exact = oracle.indexer_token_scores(q, w, kb, ks, bv, r, tokens=np.array(got))
+        pos = {x: i for i, x in enumerate(got)}
+        gsel = [pos[x] for x in sel[r, :int(n[r])].cpu().tolist()]
+        _check_topk(sorted(gsel), exact, list(range(len(got))), cfg.topk_tokens, f"final r{r}")
