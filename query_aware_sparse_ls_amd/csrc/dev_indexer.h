@@ -56,7 +56,10 @@ namespace ls {
 constexpr int kIdxDim = 128;            // indexer key / query dim
 constexpr int kIdxThreads = 256;
 constexpr int kIdxWaves = kIdxThreads / kWave;
-constexpr int kIdxPrefetch = 2;         // key tiles in flight per wave
+#ifndef LS_IDX_PREFETCH
+#define LS_IDX_PREFETCH 4
+#endif
+constexpr int kIdxPrefetch = LS_IDX_PREFETCH;   // key tiles in flight per wave
 constexpr int kIdxMaxTilesPerWg = 128;  // units per scoring workgroup <= 2048
 constexpr int kIdxMaxWords = kIdxMaxUnits / 32;
 

@@ -42,6 +42,9 @@ struct IdxScoreLds {
   // page ids of the workgroup's blocks (one per 16+ tokens, one per block),
   // or with token candidates the key row of every unit
   int pg[kIdxMaxTilesPerWg * 16];
+  // token mode, block units: cached tokens of each of those blocks (a unit
+  // is valid when its slot is below this; 0 for a block that is not scored)
+  int nv[kIdxMaxTilesPerWg * 16 / 16 + 1];
   float red[2 * kIdxWaves];
 };
 
@@ -107,10 +110,14 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
       int blk = -1;
       if (gu.ncand < 0) blk = bi < gu.nb ? bi : -1;
       else if (bi < gu.ncand) blk = a.cand_blocks[(size_t)r * a.cand_cap + bi];
+      int nvt = 0;
       if (blk >= 0 && blk < gu.nb) {
         const int p = a.b.indices[gu.page_base + blk];
         page = (p >= 0 && p < a.b.num_pages) ? p : -2;   // -2: bad page id, scores 0
+        nvt = gu.L - blk * P;
+        nvt = nvt < 0 ? 0 : (nvt > P ? P : nvt);
       }
+      sh.nv[i] = nvt;
     } else {
       if (bi >= c0 && bi < c1) {
         const int p = a.b.indices[gu.page_base + bi];
@@ -260,13 +267,15 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
           for (int s2 = 0; s2 < 4; ++s2)
             kb[s2] = *reinterpret_cast<const uint4*>(tile + col * T::RW + 16 * kq + 4 * s2);
         }
+        // k-step outer, head tile inner: the NHT products of a k-step are
+        // independent, so the matrix core is not left waiting on a result
         f32x4_t acc[NHT];
 #pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-          acc[ht] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ht = 0; ht < NHT; ++ht) acc[ht] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) acc[ht] = mfma_16x16x32(qr[ht][s2], kb[s2], acc[ht]);
-        }
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) acc[ht] = mfma_16x16x32(qr[ht][s2], kb[s2], acc[ht]);
         // s = sum_h w_h max(0, sigma * d_h); lane holds heads 16ht + 4kq + i
         float v = 0.0f;
         if (__ballot(!(sg > 0.0f)) == 0) {   // all scales positive: sigma factors out
@@ -291,8 +300,10 @@ __global__ __launch_bounds__(kIdxThreads, 2) void idx_score_kernel(IndexerArgs a
           const int ul = 16 * t + col;   // unit in the workgroup
           bool valid;
           if constexpr (MODE == kIdxTokens) {
-            int tok;
-            valid = idx_unit_block(a, gu, r, u0 + ul, &tok) >= 0;
+            // from LDS: a memory read here would make the wait for it also
+            // wait for the key tiles in flight
+            const int uu = u0 + ul;
+            valid = tok_cands ? sh.pg[ul] != -1 : (uu & (P - 1)) < sh.nv[(uu >> PS) - bi0];
             if (valid) {
               rmn = fminf(rmn, v);
               rmx = fmaxf(rmx, v);

@@ -28,15 +28,26 @@
 namespace ls {
 
 constexpr int kMlaDk = 576, kMlaDv = 512;
-constexpr int kMlaThreads = 512, kMlaWaves = 8;
-constexpr int kMlaHeadsPerWg = 32;                     // two 16-head tiles
-constexpr int kMlaTile = 64;                           // tokens per LDS tile (4 MFMA row tiles)
+// Workgroup shape (measured on MI355X): head tiles of 16 heads per workgroup
+// (4 waves each) and 16-token row tiles per LDS tile.
+#ifndef LS_MLA_HEAD_TILES
+#define LS_MLA_HEAD_TILES 2
+#endif
+#ifndef LS_MLA_ROW_TILES
+#define LS_MLA_ROW_TILES 4
+#endif
+constexpr int kMlaHT = LS_MLA_HEAD_TILES;              // 16-head tiles per workgroup
+constexpr int kMlaRT = LS_MLA_ROW_TILES;               // 16-token row tiles per LDS tile
+constexpr int kMlaWaves = 4 * kMlaHT, kMlaThreads = kMlaWaves * kWave;
+constexpr int kMlaHeadsPerWg = 16 * kMlaHT;
+constexpr int kMlaTile = 16 * kMlaRT;                  // tokens per LDS tile
 constexpr int kMlaRowWords = kMlaDk / 2 + 4;           // 1168-byte padded rows (16-byte aligned)
 constexpr int kMlaChunks = kMlaTile * (kMlaDk / 8);    // 16-byte chunks per tile
 constexpr int kMlaChunksPerThread = kMlaChunks / kMlaThreads;
 static_assert(kMlaChunksPerThread <= 32, "one mask bit per chunk");
 static_assert(kMlaChunks % kMlaThreads == 0, "tile chunks per thread");
-static_assert(kMlaSplitTokens % kMlaTile == 0, "whole tiles per split");
+static_assert(kMlaSplitTokens % 64 == 0 && kMlaSplitTokens % kMlaTile == 0, "whole tiles per split");
+static_assert(kMlaRT % 2 == 0, "P . V k-steps of 32 tokens");
 
 // Byte offset of the o partials in the workspace: after the (m, l) pairs of
 // every (request, head, split) row, 256-byte aligned.
@@ -47,17 +58,21 @@ __device__ __forceinline__ size_t mla_o_offset(const MlaArgs& a) {
 
 struct MlaLds {
   alignas(16) uint32_t tile[kMlaTile * kMlaRowWords];
-  f32x4_t red[kMlaWaves][4][kWave];   // partial logits: wave, 16-token row tile, lane
-  int rowoff[kMlaSplitTokens];        // token row index in the pool (page * P + slot), -1 = skip
-  unsigned long long valid[kMlaSplitTokens / kMlaTile];   // per tile: bit = token row present
+  f32x4_t red[kMlaWaves][kMlaRT][kWave];   // partial logits: wave, 16-token row tile, lane
+  int rowoff[kMlaSplitTokens];             // token row index in the pool (page * P + slot), -1 = skip
+  unsigned long long valid[kMlaSplitTokens / 64];   // bit = token row present
 };
-static_assert(kMlaSplitTokens <= kMlaThreads && kMlaTile == kWave, "one ballot per tile");
 
-// Workgroup (request r, 32 heads, split s), 8 waves. Wave w works on head
-// tile w / 4 (16 heads): the QK^T k-steps of quarter w % 4 (5, 5, 4, 4 of the
-// 18), summed with the other three waves of its head tile through LDS, and
-// the output dims [128 (w % 4), + 128) of P . V.
-__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
+// Workgroup (request r, 16 kMlaHT heads, split s), 4 kMlaHT waves. Wave w
+// works on head tile w / 4 (16 heads): the QK^T k-steps of quarter w % 4 (5,
+// 5, 4, 4 of the 18), summed with the other three waves of its head tile
+// through LDS, and the output dims [128 (w % 4), + 128) of P . V.
+#ifdef LS_MLA_WAVES_PER_EU
+#define LS_MLA_WPE __attribute__((amdgpu_waves_per_eu(LS_MLA_WAVES_PER_EU)))
+#else
+#define LS_MLA_WPE
+#endif
+__global__ __launch_bounds__(kMlaThreads) LS_MLA_WPE void mla_split_kernel(MlaArgs a) {
   __shared__ MlaLds sh;
   const int S = a.num_splits;
   const int nrs = a.b.batch * S;
@@ -68,6 +83,16 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   const int ht = wave >> 2, sub = wave & 3;
   const int P = a.b.page_size;
   const int H = a.num_q_heads;
+
+  // q^T operand of this wave's k-steps: head 16 (kMlaHT hg + ht) + col, dims
+  // 32k + 8kq (issued first: independent of the selection)
+  const int ks0 = sub < 2 ? 5 * sub : 10 + 4 * (sub - 2);
+  const int nks = sub < 2 ? 5 : 4;
+  const int head0 = kMlaHeadsPerWg * hg + 16 * ht;
+  uint4 qb[5];
+  const uint16_t* qh = a.q + ((size_t)r * H + head0 + col) * kMlaDk + 8 * kq;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) qb[k] = k < nks ? ldg16(qh + 32 * (ks0 + k)) : make_uint4(0, 0, 0, 0);
 
   const ReqGeom geo = req_geom(a.b, r, 0, 0);
   int cnt = a.selected_count ? a.selected_count[r] : geo.L;
@@ -85,24 +110,15 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
       }
     }
     sh.rowoff[i] = off;
-    const unsigned long long vb = __ballot(off >= 0);   // a wave = one tile's tokens
+    const unsigned long long vb = __ballot(off >= 0);   // a wave = 64 consecutive tokens
     if ((i & (kWave - 1)) == 0) sh.valid[i / kWave] = vb;
   }
-  // q^T operand of this wave's k-steps: head 32 hg + 16 ht + col, dims 32k + 8kq
-  const int ks0 = sub < 2 ? 5 * sub : 10 + 4 * (sub - 2);
-  const int nks = sub < 2 ? 5 : 4;
-  const int head0 = kMlaHeadsPerWg * hg + 16 * ht;
-  uint4 qb[5];
-  const uint16_t* qh = a.q + ((size_t)r * H + head0 + col) * kMlaDk + 8 * kq;
-#pragma unroll
-  for (int k = 0; k < 5; ++k) qb[k] = k < nks ? ldg16(qh + 32 * (ks0 + k)) : make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   const bool out32 = a.out_dtype == LS_DTYPE_FP32;
   const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
-  // tile loads: chunk c = tid + 512 i -> token c / 72, 16 bytes at 8 (c % 72);
-  // one tile of loads is in flight while the staged one is used (more in
-  // flight only lengthens the memory-side queues)
+  // tile loads: chunk c = tid + kMlaThreads i -> token c / 72, 16 bytes at
+  // 8 (c % 72); one tile of loads is in flight while the staged one is used.
   // vm: bit i set when chunk i belongs to a selected token (the others read
   // row 0 and are zeroed when staged: their weights are 0, but 0 * NaN would
   // reach the output)
@@ -137,29 +153,30 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     }
     __syncthreads();
     issue(t + 1, ld, vm);
-    // partial logits over this wave's k-steps, 4 row tiles of 16 tokens
-    f32x4_t z[4];
+    // partial logits over this wave's k-steps, kMlaRT row tiles of 16 tokens
+    f32x4_t z[kMlaRT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) z[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < kMlaRT; ++j) z[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
       if (k < nks) {
         const int w0 = 16 * (ks0 + k) + 4 * kq;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kMlaRT; ++j) {
           const uint4 av = *reinterpret_cast<const uint4*>(sh.tile + (16 * j + col) * kMlaRowWords + w0);
           z[j] = mfma_16x16x32(av, qb[k], z[j]);
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sh.red[wave][j][lane] = z[j];
+    for (int j = 0; j < kMlaRT; ++j) sh.red[wave][j][lane] = z[j];
     __syncthreads();
     // full logits of head tile ht: lane = head col, tokens 16 j + 4 kq + i
-    const unsigned long long vbits = sh.valid[t] >> (4 * kq);
-    float zz[16], bm = kNegInf;
+    const int tp = t * kMlaTile;   // first token of the tile in the split
+    const unsigned long long vbits = (sh.valid[tp >> 6] >> (tp & 63)) >> (4 * kq);
+    float zz[4 * kMlaRT], bm = kNegInf;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kMlaRT; ++j) {
       f32x4_t acc = sh.red[4 * ht][j][lane];
 #pragma unroll
       for (int w = 1; w < 4; ++w) {
@@ -182,9 +199,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
     // exp2 of values <= 0 with -inf -> 0 (mn = -inf: nothing seen yet, all 0)
     const float mref = mn == kNegInf ? 0.0f : mn;
     const float alpha = mn == kNegInf ? 1.0f : exp2_fast(m - mref);
-    float p[16], ps = 0.0f;
+    float p[4 * kMlaRT], ps = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4 * kMlaRT; ++i) {
       p[i] = exp2_fast(zz[i] - mref);
       ps += p[i];
     }
@@ -202,10 +219,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[n][i] *= ar[i];
     }
-    // P . V in two k-steps of 32 tokens: step js covers row tiles 2js and
+    // P . V in k-steps of 32 tokens: step js covers row tiles 2js and
     // 2js + 1; lane's k-slice = tokens 4kq + i of each (P as A: row = head col)
 #pragma unroll
-    for (int js = 0; js < 2; ++js) {
+    for (int js = 0; js < kMlaRT / 2; ++js) {
       // p = hi + lo (+ lo2) in bf16 parts, two tokens per conversion
       uint32_t hw[4], lw[4], mw[4];
 #pragma unroll

@@ -348,13 +348,14 @@ __global__ __launch_bounds__(kIdxThreads, 2) void pq_score_kernel(IndexerArgs a)
           const uint2 e1 = sh.u.cb[(jb + 2 * s2 + 1) * kPqCent + ((w >> 8) & 0xffu)];
           kb[s2] = bd ? make_uint4(0, 0, 0, 0) : make_uint4(e0.x, e0.y, e1.x, e1.y);
         }
+        // k-step outer, head tile inner: independent products back to back
         f32x4_t acc[NHT];
 #pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-          acc[ht] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ht = 0; ht < NHT; ++ht) acc[ht] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) acc[ht] = mfma_16x16x32(qr[ht][s2], kb[s2], acc[ht]);
-        }
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) acc[ht] = mfma_16x16x32(qr[ht][s2], kb[s2], acc[ht]);
         float v = 0.0f;
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht)
@@ -365,8 +366,9 @@ __global__ __launch_bounds__(kIdxThreads, 2) void pq_score_kernel(IndexerArgs a)
         v += 0.0f;   // -0 -> +0: equal scores get equal keys
         if (kq == 0) {
           const int ul = 16 * (wave + kIdxWaves * k) + col;
-          int tok;
-          const bool valid = idx_unit_block(a, gu, r, u0 + ul, &tok) >= 0;
+          // every token of a complete page is a unit (no memory read here:
+          // its wait would also wait for the code tiles in flight)
+          const bool valid = u0 + ul < gu.n;
           if (valid) {
             rmn = fminf(rmn, v);
             rmx = fmaxf(rmx, v);

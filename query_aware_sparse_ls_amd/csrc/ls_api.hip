@@ -744,6 +744,19 @@ size_t ls_indexer_select_workspace_size(int32_t batch_size, int32_t granularity,
   return ws;
 }
 
+// Scoring tiles (16 units each) per workgroup: up to 128, fewer while that
+// leaves fewer than LS_IDX_MIN_WGS workgroups (the scoring loop is bound by
+// issue and latency, so the chip needs several waves per SIMD).
+#ifndef LS_IDX_MIN_WGS
+#define LS_IDX_MIN_WGS 512
+#endif
+static int indexer_tiles_per_wg(size_t B, int U) {
+  int tiles = 128;
+  while (tiles > 4 && (long long)B * ((U + 16 * tiles - 1) / (16 * tiles)) < LS_IDX_MIN_WGS)
+    tiles /= 2;
+  return tiles;
+}
+
 // The token top-k's part of the workspace (after the scores), in the order
 // ls_indexer_select_workspace_size counts it.
 static void token_topk_layout(ls::IndexerArgs& a, char* w, size_t B, int U) {
@@ -864,11 +877,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
   a.max_selected = p->max_selected;
   a.selected = selected;
   a.selected_count = selected_count;
-  // enough workgroups to cover the chip: 2048 units each unless that leaves
-  // fewer than ~512 workgroups (two per CU)
-  int tiles = 128;
-  while (tiles > 4 && (long long)B * ((U + 16 * tiles - 1) / (16 * tiles)) < 512) tiles /= 2;
-  a.tiles_per_wg = tiles;
+  a.tiles_per_wg = indexer_tiles_per_wg(B, U);
   if (!tokens) {
     hipError_t e = ls::launch_indexer_score(a, ls::kIdxBlocks, stream);
     if (e != hipSuccess) return hip_status(e, "indexer score kernel launch");
@@ -1246,9 +1255,7 @@ ls_status ls_pq_select(const void* q, int32_t q_dtype, int32_t num_heads,
   a.max_selected = n_candidates;
   a.selected = candidates;
   a.selected_count = candidate_counts;
-  int tiles = 128;
-  while (tiles > 4 && (long long)B * ((U + 16 * tiles - 1) / (16 * tiles)) < 512) tiles /= 2;
-  a.tiles_per_wg = tiles;
+  a.tiles_per_wg = indexer_tiles_per_wg(B, U);
   token_topk_layout(a, w, B, U);
   return hip_status(ls::launch_pq_select(a, stream), "PQ selection launches");
 }
