@@ -649,7 +649,7 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
                    cnt=torch.empty(B, dtype=torch.int32, device=dev),
                    out=torch.empty(B, cfg.mla_heads, cfg.kv_lora_dim, dtype=torch.bfloat16,
                                    device=dev),
-                   ws_mla=torch.empty(ls.sparse_mla_decode_workspace_size(B, cfg.mla_heads, k),
+                   ws_mla=torch.zeros(ls.sparse_mla_decode_workspace_size(B, cfg.mla_heads, k),
                                       dtype=torch.uint8, device=dev))
         if pq and args.miss_filter:
             # the keys a previous step left resident: a seeded Bernoulli mask

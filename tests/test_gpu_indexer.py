@@ -283,6 +283,37 @@ def test_mla_small_selected(out_dtype):
         say(f"  r{r}: {len(want_tokens[r])} tokens, max err {err:.2e}")
 
 
+def test_mla_workspace_reused():
+    """One workspace serves consecutive calls of different sizes and dtypes
+    (the partial states of a call never leak into the next): each result is
+    bit-identical to a call on a fresh workspace."""
+    say("mla workspace reuse")
+    cfg = reduced(INDEXER_128K, batch=3, context=64 * 50, mla_heads=64, seed=24)
+    inp = make_indexer_inputs(cfg, device=_dev())
+    inp.seq_lens.copy_(torch.tensor([3200, 2000, 700], dtype=torch.int32))
+    b = _batch(inp, kv=True)
+    rng = np.random.default_rng(5)
+    maxsel = 1100
+    sm = 1.0 / math.sqrt(576)
+    ws = torch.full((ls.sparse_mla_decode_workspace_size(3, 64, maxsel),), 0xA5,
+                    dtype=torch.uint8, device=_dev())   # need not be initialised
+    for it, (ks, dt) in enumerate([((1100, 900, 700), torch.bfloat16),
+                                   ((300, 1100, 5), torch.float32),
+                                   ((1000, 0, 257), torch.bfloat16)]):
+        sel = np.full((3, maxsel), -1, dtype=np.int32)
+        for r, (L, k) in enumerate(zip([3200, 2000, 700], ks)):
+            sel[r, :k] = np.sort(rng.choice(L, k, replace=False))
+        sd = torch.tensor(sel, device=_dev())
+        cd = torch.tensor(ks, dtype=torch.int32, device=_dev())
+        out, _ = ls.sparse_mla_decode(inp.q_mla, inp.latent, b, sd, cd, sm_scale=sm,
+                                      out_dtype=dt, workspace=ws)
+        ref, _ = ls.sparse_mla_decode(inp.q_mla, inp.latent, b, sd, cd, sm_scale=sm,
+                                      out_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if dt == torch.bfloat16 else out.view(torch.int32),
+                           ref.view(torch.int16) if dt == torch.bfloat16 else ref.view(torch.int32)), it
+
+
 def test_mla_dense_equals_all_tokens():
     say("mla dense")
     cfg = reduced(INDEXER_128K, batch=2, context=64 * 9, mla_heads=32, seed=22)
