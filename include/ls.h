@@ -103,7 +103,13 @@ typedef struct ls_pool {
 } ls_pool;
 
 /* A ragged batch of requests over a paged pool (CSR page table, the
- * "index-pointer array" + page list of the Vortex post's vTensor). */
+ * "index-pointer array" + page list of the Vortex post's vTensor).
+ * Device data that breaks the contract is not undefined behaviour: every
+ * kernel clamps a request's length to its page list and to max_blocks
+ * pages (the tokens past them are not cached), takes a negative length as
+ * 0, and reads nothing at a page id outside [0, num_pages) (such a block
+ * scores 0 and its tokens are not attended), so no access leaves the
+ * buffers whose sizes the call states. */
 typedef struct ls_batch {
   int32_t batch_size;            /* host: number of requests (0 is allowed)  */
   int32_t max_blocks;            /* host: >= ceil(seq_lens[r]/page_size), all r */
