@@ -503,13 +503,21 @@ def summarize_profiles(args) -> int:
     """Write profiles/<kernel_key>.md from rocprofv3 CSV output: the
     kernel-trace statistics, FETCH_SIZE / WRITE_SIZE per dispatch of the
     kernel, and the same counters for a plain copy of a known byte count,
-    which scale the kernel's counters to bytes."""
-    key, match = args.kernel_key, args.kernel_match
+    which scale the kernel's counters to bytes. `--kernel-match` may list
+    several kernels separated by '|' (the launches of one library call): the
+    traffic is then the sum of their per-dispatch means."""
+    key = args.kernel_key
+    matches = args.kernel_match.split("|")
     stats = _kernel_stats(os.path.join(args.kt_dir, "run_kernel_stats.csv"))
-    fetch, nf, grid = _counter_per_dispatch(os.path.join(args.fetch_dir, "run_counter_collection.csv"),
-                                            "FETCH_SIZE", match)
-    write, nw, _ = _counter_per_dispatch(os.path.join(args.write_dir, "run_counter_collection.csv"),
-                                         "WRITE_SIZE", match)
+    per = []
+    for m in matches:
+        f, nf, grid = _counter_per_dispatch(os.path.join(args.fetch_dir, "run_counter_collection.csv"),
+                                            "FETCH_SIZE", m)
+        w, nw, _ = _counter_per_dispatch(os.path.join(args.write_dir, "run_counter_collection.csv"),
+                                         "WRITE_SIZE", m)
+        per.append((m, f, nf, grid, w, nw))
+    fetch = sum(p[1] for p in per)
+    write = sum(p[4] for p in per)
     cb = args.copy_bytes
     cfetch, _, _ = _counter_per_dispatch(os.path.join(args.copy_fetch_dir, "run_counter_collection.csv"),
                                          "FETCH_SIZE", "copyBuffer")
@@ -528,16 +536,19 @@ def summarize_profiles(args) -> int:
         lines.append(f"| `{n[:110]}` | {v['calls']} | {v['avg_us']:.2f} | {v['min_us']:.2f} | "
                      f"{v['max_us']:.2f} |")
     lines += ["", "## HBM counters per dispatch (rocprofv3 --pmc, one counter per run)", "",
-              "```", args.fetch_cmd, args.write_cmd, args.copy_fetch_cmd, args.copy_write_cmd, "```", "",
-              f"* kernel `{match}` (grid {grid}): FETCH_SIZE {fetch:.1f} KiB over {nf} dispatches, "
-              f"WRITE_SIZE {write:.1f} KiB over {nw} dispatches",
-              f"* plain copy (`__amd_rocclr_copyBuffer`, {cb} bytes read and written): "
+              "```", args.fetch_cmd, args.write_cmd, args.copy_fetch_cmd, args.copy_write_cmd, "```", ""]
+    for m, f, nf, grid, w, nw in per:
+        lines.append(f"* kernel `{m}` (grid {grid}): FETCH_SIZE {f:.1f} KiB over {nf} dispatches, "
+                     f"WRITE_SIZE {w:.1f} KiB over {nw} dispatches")
+    lines += [f"* plain copy (`__amd_rocclr_copyBuffer`, {cb} bytes read and written): "
               f"FETCH_SIZE {cfetch:.1f} KiB, WRITE_SIZE {cwrite:.1f} KiB",
               f"* scale (copy bytes / counter bytes): FETCH_SIZE x {f_scale:.4f}, "
               f"WRITE_SIZE x {w_scale:.4f}",
-              f"* traffic per launch: {fetch * 1024 * f_scale:.0f} B read + "
+              f"* traffic per launch{' (sum over the kernels)' if len(per) > 1 else ''}: "
+              f"{fetch * 1024 * f_scale:.0f} B read + "
               f"{write * 1024 * w_scale:.0f} B written = {traffic:.0f} B", ""]
-    rec = {"kernel": match, "traffic_bytes": round(traffic), "read_bytes": round(fetch * 1024 * f_scale),
+    rec = {"kernel": args.kernel_match, "traffic_bytes": round(traffic),
+           "read_bytes": round(fetch * 1024 * f_scale),
            "write_bytes": round(write * 1024 * w_scale), "fetch_kib": fetch, "write_kib": write,
            "copy_bytes": cb, "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
            "source_sha256": library_source_digest()}
@@ -862,6 +873,14 @@ def bench_indexer(args, coarse: bool, pq: bool = False) -> int:
                         "algorithmic_bytes_per_launch": dbytes,
                         "avg_launch_ms": round(per[dom], 5)},
            "device": torch.cuda.get_device_name(0)}
+    if not (coarse or pq or args.approx_topk):
+        # the exact token top-k over every cached token: the committed
+        # counters cover this call's three launches
+        tkey = f"{dom}.{cfg.name}"
+        tr = stored_traffic(tkey)
+        if tr is not None:
+            res["roofline"]["traffic"] = tr["traffic_bytes"]
+            res["roofline"]["traffic_source"] = f"profiles/{tkey}.md"
     if recall is not None:
         res["recall_vs_exact"] = recall
     print(json.dumps(res), flush=True)
@@ -1008,6 +1027,10 @@ def bench_summaries(args) -> int:
                        "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                        "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}
+    tr = stored_traffic("summaries_bf16_kernel.summaries_b16_32k_bf16")
+    if tr is not None:
+        res["roofline"]["traffic"] = tr["traffic_bytes"]
+        res["roofline"]["traffic_source"] = "profiles/summaries_bf16_kernel.summaries_b16_32k_bf16.md"
     del keys, outs, flat
     torch.cuda.empty_cache()
     # fp8 indexer keys: 4 x 15,200 pages of 64 tokens x 128 bytes, fp32 scales
