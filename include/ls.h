@@ -730,6 +730,47 @@ const char* ls_version(void);
 int32_t ls_stream_read_sink_words(void);
 ls_status ls_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* Debug check of a batch's device data                                      */
+/* ------------------------------------------------------------------------ */
+/* The kernels clamp device data that breaks the ls_batch contract (see
+ * ls_batch); these calls report it. Violation kinds (bits): */
+enum {
+  LS_BATCH_BAD_INDPTR = 1,               /* page_indptr[r] < 0 or page_indptr[r+1] < page_indptr[r] */
+  LS_BATCH_NEGATIVE_LENGTH = 2,          /* seq_lens[r] < 0                               */
+  LS_BATCH_LENGTH_BEYOND_PAGES = 4,      /* ceil(seq_lens[r]/page_size) > pages in r's list */
+  LS_BATCH_LENGTH_BEYOND_MAX_BLOCKS = 8, /* ceil(seq_lens[r]/page_size) > max_blocks       */
+  LS_BATCH_PAGE_OUT_OF_RANGE = 16        /* a page id a kernel would read is outside [0, num_pages) */
+};
+
+/* Check `batch` against a pool of num_pages pages of page_size tokens: one
+ * workgroup walks the requests and, per request, the page ids of the blocks
+ * a kernel reads (below min(ceil(seq_lens[r]/page_size), list length,
+ * max_blocks)); it reads only entries inside each request's list, so the
+ * page list must hold page_indptr[batch_size] entries, as for every call.
+ * report: device, 4 int32, overwritten on the stream: [0] the kinds found
+ * (OR of the bits above), [1] the number of violating requests, [2] the
+ * first violating request or -1, [3] the number of requests checked.
+ * Errors: LS_ERR_INVALID for a null or misaligned report, a bad batch (as
+ * every call) or page_size / num_pages < 1. batch_size 0 writes {0,0,-1,0}. */
+ls_status ls_check_batch(ls_batch batch, int32_t page_size, int32_t num_pages, int32_t* report,
+                         hipStream_t stream);
+
+/* Debug mode (off by default; on when the environment holds LS_DEBUG set to
+ * anything but "" or "0" when the library first looks, or after
+ * ls_debug_enable(1)): every call that takes an ls_batch first enqueues the
+ * same check on its stream, which adds into 4 words the library keeps per
+ * GPU: [0] the kinds found (OR), [1] calls with a violation, [2] violating
+ * requests, [3] calls checked. The check is one more kernel per call and
+ * can be captured in a graph. */
+void ls_debug_enable(int32_t on);
+int32_t ls_debug_enabled(void);
+
+/* Copy the current GPU's debug words to host_report (4 int32) and clear
+ * them. Synchronises the device (not for use under stream capture).
+ * Errors: LS_ERR_INVALID for a null host_report; LS_ERR_HIP. */
+ls_status ls_debug_report(int32_t* host_report);
+
 /* Number of split-K partitions ls_sparse_attn_decode uses for a given
  * selection capacity (max_selected, or max_blocks on the dense path). */
 int32_t ls_attn_num_splits(int32_t max_selected);

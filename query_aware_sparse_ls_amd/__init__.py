@@ -16,6 +16,9 @@ import torch
 
 from . import _lib
 from ._lib import (LS_AGG_MAX, LS_AGG_MEAN, LS_DTYPE_BF16, LS_DTYPE_FP32,  # noqa: F401
+                   LS_BATCH_BAD_INDPTR, LS_BATCH_LENGTH_BEYOND_MAX_BLOCKS,
+                   LS_BATCH_LENGTH_BEYOND_PAGES, LS_BATCH_NEGATIVE_LENGTH,
+                   LS_BATCH_PAGE_OUT_OF_RANGE,
                    LS_CAND_BLOCKS, LS_CAND_TOKENS, LS_DTYPE_FP8_E4M3FN, LS_SCORE_BOUNDS,
                    LS_SCORE_MEAN, LS_SEL_BLOCKS,
                    LS_SEL_TOKENS, LsBatch, LsError,
@@ -26,7 +29,8 @@ _L = _lib.load()
 __all__ = ["PagedBatch", "build_block_summaries", "build_block_bounds", "score_select", "sparse_attn_decode",
            "score_select_workspace_size", "sparse_attn_decode_workspace_size",
            "attn_num_splits", "version", "LsError", "sparse_decode_step",
-           "sparse_decode_step_workspace", "sparse_decode_step_noalloc", "stream_read", "indexer_select", "indexer_select_workspace_size",
+           "sparse_decode_step_workspace", "sparse_decode_step_noalloc", "stream_read",
+           "check_batch", "debug_enable", "debug_enabled", "debug_report", "indexer_select", "indexer_select_workspace_size",
            "indexer_score_stride", "sparse_mla_decode", "sparse_mla_decode_workspace_size",
            "mla_num_splits", "pq_encode", "pq_train", "pq_select", "window_attn_decode",
            "snapkv_select", "snapkv_gather"]
@@ -183,6 +187,39 @@ def score_select(q: torch.Tensor, summaries: torch.Tensor, page_size: int, batch
                              0 if ws is None else ws.numel() * ws.element_size(),
                              _stream(stream)))
     return selected, selected_count
+
+
+# ------------------------------------------------------------- batch checks
+
+def check_batch(batch: PagedBatch, page_size: int, num_pages: int,
+                report: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Check the batch's device data against a pool of num_pages pages of
+    page_size tokens; returns the 4-word device report (kinds found,
+    violating requests, first violating request or -1, requests checked)."""
+    if report is None:
+        report = torch.empty(4, dtype=torch.int32, device=batch.seq_lens.device)
+    _need(report, torch.int32)
+    check(_L.ls_check_batch(batch.c(), int(page_size), int(num_pages), report.data_ptr(),
+                            _stream(stream)))
+    return report
+
+
+def debug_enable(on: bool = True) -> None:
+    """Debug mode: every call that takes a batch checks it first and adds what
+    it finds into the library's per-GPU debug words."""
+    _L.ls_debug_enable(1 if on else 0)
+
+
+def debug_enabled() -> bool:
+    return bool(_L.ls_debug_enabled())
+
+
+def debug_report() -> Tuple[int, int, int, int]:
+    """The current GPU's debug words (kinds found, calls with a violation,
+    violating requests, calls checked), then cleared; synchronises."""
+    out = (C.c_int32 * 4)()
+    check(_L.ls_debug_report(C.cast(out, C.c_void_p)))
+    return tuple(int(x) for x in out)
 
 
 # ------------------------------------------------------------------ attention

@@ -14,6 +14,8 @@ LS_AGG_MAX, LS_AGG_MEAN = 0, 1
 LS_SEL_TOKENS, LS_SEL_BLOCKS = 0, 1
 LS_SCORE_MEAN, LS_SCORE_BOUNDS = 0, 1
 LS_CAND_BLOCKS, LS_CAND_TOKENS = 0, 1
+(LS_BATCH_BAD_INDPTR, LS_BATCH_NEGATIVE_LENGTH, LS_BATCH_LENGTH_BEYOND_PAGES,
+ LS_BATCH_LENGTH_BEYOND_MAX_BLOCKS, LS_BATCH_PAGE_OUT_OF_RANGE) = 1, 2, 4, 8, 16
 
 # every function the header declares, with its ctypes signature
 EXPORTS = {}
@@ -93,6 +95,10 @@ _SIGS = {
     "ls_attn_num_splits": (C.c_int32, [C.c_int32]),
     "ls_stream_read_sink_words": (C.c_int32, []),
     "ls_stream_read": (C.c_int, [_P, C.c_size_t, _P, _P]),
+    "ls_check_batch": (C.c_int, [LsBatch, C.c_int32, C.c_int32, _P, _P]),
+    "ls_debug_enable": (None, [C.c_int32]),
+    "ls_debug_enabled": (C.c_int32, []),
+    "ls_debug_report": (C.c_int, [_P]),
 }
 
 _lib = None

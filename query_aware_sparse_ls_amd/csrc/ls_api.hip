@@ -7,6 +7,8 @@
 #include <cstring>
 
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <mutex>
 
 #include "ls_flow.h"
@@ -77,6 +79,57 @@ ls::BatchArgs batch_args(const ls_batch& b, const ls_pool& p) {
   a.num_pages = p.num_pages;
   a.page_size = p.page_size;
   return a;
+}
+
+// ---- debug check of batches (ls_debug_enable, LS_DEBUG)
+
+constexpr int kDebugMaxDevices = 64;
+
+// Per GPU: kinds found (OR), calls with a violation, violating requests,
+// calls checked. Zero when the library is loaded; ls_debug_report clears
+// them. In host code the name is only a stand-in: the device address comes
+// from hipGetSymbolAddress.
+static __device__ __align__(16) int32_t debug_words[4];
+
+std::mutex g_debug_mu;
+void* g_debug_ptr[kDebugMaxDevices] = {};
+std::atomic<int> g_debug{-1};   // -1: the environment not read yet
+
+bool debug_on() {
+  int v = g_debug.load();
+  if (v < 0) {
+    const char* e = std::getenv("LS_DEBUG");
+    int expected = -1;
+    g_debug.compare_exchange_strong(expected, (e && e[0] && std::strcmp(e, "0") != 0) ? 1 : 0);
+    v = g_debug.load();
+  }
+  return v == 1;
+}
+
+// The calling thread's current device's copy of debug_words.
+hipError_t debug_words_ptr(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDebugMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_debug_mu);
+  if (!g_debug_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(debug_words));
+    if (e != hipSuccess) return e;
+    g_debug_ptr[dev] = p;
+  }
+  *out = static_cast<int32_t*>(g_debug_ptr[dev]);
+  return hipSuccess;
+}
+
+// In debug mode, the batch check ahead of a call's kernels, on its stream.
+ls_status debug_check(const ls::BatchArgs& b, hipStream_t stream) {
+  if (b.batch == 0 || !debug_on()) return ok();
+  int32_t* words = nullptr;
+  const hipError_t e = debug_words_ptr(&words);
+  if (e != hipSuccess) return hip_status(e, "debug words address lookup");
+  return hip_status(ls::launch_batch_check(b, words, true, stream), "batch check launch");
 }
 
 int max_total_selected(const ls_select_params& p, int max_blocks) {
@@ -343,6 +396,7 @@ ls_status run_step(const void* q, int32_t num_q_heads, void* summaries, const vo
   float* scores = reinterpret_cast<float*>(w + lay.rows);
   float* partials = reinterpret_cast<float*>(w + lay.parts);
   const ls::ScoreArgs sa = score_args(q, num_q_heads, summaries, pool, batch, p, scores);
+  if (const ls_status d = debug_check(sa.b, stream)) return d;
   const ls::TopkArgs ta = topk_args(sa, p, scores, selected, selected_count);
   const ls::AttnArgs aa = attn_args(q, num_q_heads, k_pool, v_pool, pool, batch, selected,
                                     selected_count, p.max_selected,
@@ -428,7 +482,7 @@ extern "C" {
 
 const char* ls_last_error(void) { return g_err; }
 
-const char* ls_version(void) { return "libls 0.6.0 abi 6 gfx950"; }
+const char* ls_version(void) { return "libls 0.7.0 abi 6 gfx950"; }
 
 int32_t ls_attn_num_splits(int32_t max_selected) {
   if (max_selected < 1) return 1;
@@ -543,6 +597,7 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
   char* w = static_cast<char*>(workspace);
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(w + lay.rows);
   const ls::ScoreArgs sa = score_args(q, num_q_heads, summaries, pool, batch, *p, scores);
+  if (const ls_status d = debug_check(sa.b, stream)) return d;
   const ls::TopkArgs ta = topk_args(sa, *p, scores, selected, selected_count);
   const Route rt = route(pool, batch, num_q_heads);
   if (rt == kRouteItem) {
@@ -615,6 +670,7 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
   const ls::AttnArgs aa = attn_args(q, num_q_heads, k_pool, v_pool, pool, batch, selected,
                                     selected_count, max_selected, ls_attn_num_splits(cap),
                                     sm_scale, partials, out, out_dtype, lse_out);
+  if (const ls_status d = debug_check(aa.b, stream)) return d;
   // a selection: split over several workgroups per pair, merged by the last
   // one to finish; the dense path (every block) of few pairs is split-K over
   // runs of up to 512 blocks, merged by a second kernel
@@ -679,6 +735,40 @@ ls_status ls_sparse_decode_step(const void* q, int32_t q_dtype, int32_t num_q_he
 size_t ls_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 int32_t ls_stream_read_sink_words(void) { return ls::kStreamReadWorkgroups; }
+
+ls_status ls_check_batch(ls_batch batch, int32_t page_size, int32_t num_pages, int32_t* report,
+                         hipStream_t stream) {
+  if (!report || (uintptr_t)report % 4)
+    return fail(LS_ERR_INVALID, "report must be a non-null, 4-byte aligned device pointer");
+  if (page_size < 1 || num_pages < 1)
+    return fail(LS_ERR_INVALID, "page_size and num_pages must be >= 1");
+  ls_status st = check_batch(batch);
+  if (st != LS_OK) return st;
+  ls::BatchArgs b;
+  b.batch = batch.batch_size;
+  b.max_blocks = batch.max_blocks;
+  b.indptr = batch.page_indptr;
+  b.indices = batch.page_indices;
+  b.seq_lens = batch.seq_lens;
+  b.num_pages = num_pages;
+  b.page_size = page_size;
+  return hip_status(ls::launch_batch_check(b, report, false, stream), "batch check launch");
+}
+
+void ls_debug_enable(int32_t on) { g_debug.store(on ? 1 : 0); }
+
+int32_t ls_debug_enabled(void) { return debug_on() ? 1 : 0; }
+
+ls_status ls_debug_report(int32_t* host_report) {
+  if (!host_report) return fail(LS_ERR_INVALID, "host_report must be non-null");
+  int32_t* words = nullptr;
+  hipError_t e = debug_words_ptr(&words);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(host_report, words, 4 * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(words, 0, 4 * sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return hip_status(e, "debug report");
+}
 
 ls_status ls_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
   if (bytes == 0) return ok();
@@ -878,6 +968,7 @@ ls_status ls_indexer_select(const void* q, int32_t q_dtype, int32_t num_heads,
   a.selected = selected;
   a.selected_count = selected_count;
   a.tiles_per_wg = indexer_tiles_per_wg(B, U);
+  if (const ls_status d = debug_check(a.b, stream)) return d;
   if (!tokens) {
     hipError_t e = ls::launch_indexer_score(a, ls::kIdxBlocks, stream);
     if (e != hipSuccess) return hip_status(e, "indexer score kernel launch");
@@ -962,6 +1053,7 @@ ls_status ls_sparse_mla_decode(const void* q, int32_t q_dtype, int32_t num_q_hea
   a.out = out;
   a.out_dtype = out_dtype;
   a.lse = lse_out;
+  if (const ls_status d = debug_check(a.b, stream)) return d;
   return hip_status(ls::launch_mla(a, stream), "MLA kernel launches");
 }
 
@@ -1026,6 +1118,7 @@ ls_status ls_window_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                               static_cast<float*>(workspace), out, out_dtype, lse_out);
   aa.win_sink = n_sink;
   aa.win_len = window;
+  if (const ls_status d = debug_check(aa.b, stream)) return d;
   return hip_status(ls::launch_attn_window(aa, npos, stream), "window attention launches");
 }
 
@@ -1109,6 +1202,7 @@ ls_status ls_snapkv_select(const void* q_obs, int32_t q_dtype, int32_t num_q_hea
   a.keys = reinterpret_cast<float*>(w + l.keys);
   a.selected = selected;
   a.counts = counts;
+  if (const ls_status d = debug_check(a.b, stream)) return d;
   return hip_status(ls::launch_snapkv_select(a, stream), "SnapKV selection launches");
 }
 
@@ -1134,6 +1228,7 @@ ls_status ls_snapkv_gather(const void* k_pool, const void* v_pool, ls_pool pool,
   a.k_out = static_cast<uint16_t*>(k_out);
   a.v_out = static_cast<uint16_t*>(v_out);
   const int budget_pad = (budget + 15) / 16 * 16;
+  if (const ls_status d = debug_check(a.b, stream)) return d;
   return hip_status(ls::launch_snapkv_gather(a, budget_pad, stream), "SnapKV gather launch");
 }
 
@@ -1257,6 +1352,7 @@ ls_status ls_pq_select(const void* q, int32_t q_dtype, int32_t num_heads,
   a.selected_count = candidate_counts;
   a.tiles_per_wg = indexer_tiles_per_wg(B, U);
   token_topk_layout(a, w, B, U);
+  if (const ls_status d = debug_check(a.b, stream)) return d;
   return hip_status(ls::launch_pq_select(a, stream), "PQ selection launches");
 }
 

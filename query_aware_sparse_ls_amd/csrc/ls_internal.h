@@ -265,6 +265,12 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t st);
 
 // Measurement reference (k_probe.hip): one streaming read of `bytes` bytes.
 constexpr int kStreamReadWorkgroups = 4096;
+// Debug check of a batch's device data (ls_check_batch, and LS_DEBUG): one
+// workgroup; report = the caller's 4 words (overwritten) or the library's
+// debug words (accumulated).
+hipError_t launch_batch_check(const BatchArgs& b, int32_t* report, bool accumulate,
+                              hipStream_t stream);
+
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
                               hipStream_t st);
 

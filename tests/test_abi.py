@@ -368,3 +368,41 @@ def test_pq_filter_misses_validation():
     assert call(cand=None) == _lib.LS_ERR_INVALID
     assert call(kept=None) == _lib.LS_ERR_INVALID
     assert call(batch=0, cand=None) == _lib.LS_OK         # empty batch: nothing enqueued
+
+
+def test_check_batch_and_debug_validation():
+    """The batch check rejects a null or misaligned report, a bad pool
+    geometry and a bad batch on the host; debug mode switches without a HIP
+    call, and reading the debug words needs a host buffer."""
+    lib = _lib.load()
+    b = _batch()
+    assert lib.ls_check_batch(b, 16, 8, None, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_check_batch(b, 16, 8, FAKE + 2, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_check_batch(b, 0, 8, FAKE, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_check_batch(b, 16, 0, FAKE, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_check_batch(_batch(batch_size=-1), 16, 8, FAKE, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_check_batch(_batch(seq_lens=None), 16, 8, FAKE, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_check_batch(_batch(max_blocks=0), 16, 8, FAKE, None) == _lib.LS_ERR_INVALID
+    assert lib.ls_debug_report(None) == _lib.LS_ERR_INVALID
+    was = lib.ls_debug_enabled()
+    try:
+        lib.ls_debug_enable(1)
+        assert lib.ls_debug_enabled() == 1
+        lib.ls_debug_enable(0)
+        assert lib.ls_debug_enabled() == 0
+    finally:
+        lib.ls_debug_enable(was)
+
+
+@pytest.mark.parametrize("value,want", [("1", 1), ("yes", 1), ("0", 0), ("", 0), (None, 0)])
+def test_debug_mode_from_environment(value, want):
+    """LS_DEBUG turns debug mode on when the library first looks (a fresh
+    process per case; no HIP call is made)."""
+    env = {k: v for k, v in os.environ.items() if k != "LS_DEBUG"}
+    if value is not None:
+        env["LS_DEBUG"] = value
+    code = ("import ctypes, sys; lib = ctypes.CDLL(sys.argv[1]); "
+            "print(lib.ls_debug_enabled())")
+    out = subprocess.run(["python3", "-c", code, _lib.LIB_PATH], env=env, capture_output=True,
+                         text=True, check=True).stdout.strip()
+    assert out == str(want)
