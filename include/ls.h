@@ -238,9 +238,12 @@ ls_status ls_build_block_bounds(const void* keys, ls_pool key_pool, const int32_
  *                 8192 blocks take one launch in which workgroups score
  *                 chunks of 64-128 blocks and the pair's last chunk ranks it.
  *                 Other shapes take a scoring kernel and a top-k kernel.
- * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
- *            page_size 16; max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192,
- *            num_pages < 2^26).
+ * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads in
+ *            {1, 2, 4, 8}; page_size 16; max_blocks <= 16384
+ *            (LS_SCORE_BOUNDS: group 4, max_blocks <= 8192, num_pages < 2^26).
+ *            Groups other than 4 run on the operator-per-kernel route
+ *            (scoring, top-k, split attention and combine as separate
+ *            launches); group 4 takes the matrix-core routes above.
  */
 size_t ls_score_select_workspace_size(int32_t batch_size, int32_t num_kv_heads,
                                       int32_t max_blocks);
@@ -292,8 +295,9 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
  * workspace:      >= ls_sparse_attn_decode_workspace_size() bytes, 256-byte
  *                 aligned (split partial results); zero-filled before its
  *                 first use (every call leaves it zero).
- * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads = 4;
- *            page_size 16.
+ * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads in
+ *            {1, 2, 4, 8} (other than 4: the split kernels, selection or
+ *            dense); page_size 16.
  */
 size_t ls_sparse_attn_decode_workspace_size(int32_t batch_size, int32_t num_q_heads,
                                             int32_t head_dim, int32_t max_selected,
@@ -350,8 +354,10 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
  *   8192 blocks (pairs spread over many workgroups, hand-offs inside the
  *   launch); otherwise the planned route's three launches (scoring with the
  *   refresh, ranking, attention), with the same results as the two calls.
- * Supported: head_dim 64 or 128; GQA group 4; page_size 16;
- *   max_blocks <= 16384 (LS_SCORE_BOUNDS: <= 8192 and num_pages < 2^26).
+ * Supported: head_dim 64 or 128; GQA group 1, 2, 4 or 8 (other than 4:
+ *   the summary refresh, scoring, top-k and split attention as separate
+ *   launches); page_size 16; max_blocks <= 16384 (LS_SCORE_BOUNDS: group 4,
+ *   max_blocks <= 8192 and num_pages < 2^26).
  */
 size_t ls_sparse_decode_step_workspace_size(int32_t batch_size, int32_t num_q_heads,
                                             int32_t num_kv_heads, int32_t head_dim,

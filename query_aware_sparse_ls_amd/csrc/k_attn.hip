@@ -22,7 +22,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.num_splits, a.num_kv_heads, a.b.batch);
-  hipLaunchKernelGGL((attn_split_kernel<D, 4>), grid, dim3(256), 0, st, a);
+  switch (a.num_q_heads / a.num_kv_heads) {   // GQA groups of 1, 2, 4 or 8
+    case 1: hipLaunchKernelGGL((attn_split_kernel<D, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attn_split_kernel<D, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((attn_split_kernel<D, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((attn_split_kernel<D, 8>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int items = a.b.batch * a.num_q_heads;

@@ -23,26 +23,32 @@ static hipError_t launch(const ScoreArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
-  const int D = a.head_dim, H = a.num_kv_heads;
-  if (D == 128) {
-    switch (H) {
-      case 1: return launch<128, 1, 4>(a, st);
-      case 2: return launch<128, 2, 4>(a, st);
-      case 4: return launch<128, 4, 4>(a, st);
-      case 8: return launch<128, 8, 4>(a, st);
-      case 16: return launch<128, 16, 4>(a, st);
-    }
-  } else {
-    switch (H) {
-      case 1: return launch<64, 1, 4>(a, st);
-      case 2: return launch<64, 2, 4>(a, st);
-      case 4: return launch<64, 4, 4>(a, st);
-      case 8: return launch<64, 8, 4>(a, st);
-      case 16: return launch<64, 16, 4>(a, st);
-    }
+template <int D, int G>
+static hipError_t launch_g(const ScoreArgs& a, hipStream_t st) {
+  switch (a.num_kv_heads) {
+    case 1: return launch<D, 1, G>(a, st);
+    case 2: return launch<D, 2, G>(a, st);
+    case 4: return launch<D, 4, G>(a, st);
+    case 8: return launch<D, 8, G>(a, st);
+    case 16: return launch<D, 16, G>(a, st);
   }
   return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t launch_d(const ScoreArgs& a, hipStream_t st) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_g<D, 1>(a, st);
+    case 2: return launch_g<D, 2>(a, st);
+    case 4: return launch_g<D, 4>(a, st);
+    case 8: return launch_g<D, 8>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// GQA groups of 1, 2, 4 or 8 query heads per kv head.
+hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
+  return a.head_dim == 128 ? launch_d<128>(a, st) : launch_d<64>(a, st);
 }
 
 }  // namespace ls

@@ -54,6 +54,11 @@ ls_status check_batch(const ls_batch& b) {
   return ok();
 }
 
+// GQA group sizes: 4 on every route (the matrix-core kernels tile 4 query
+// heads x 16 tokens); 1, 2 and 8 on the split kernels, which take the group
+// as a template parameter.
+bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
 ls_status check_gqa_pool(const ls_pool& p, const char* which) {
   if (p.num_pages < 1 || p.num_heads < 1)
     return fail(LS_ERR_INVALID, "%s: num_pages and num_heads must be >= 1", which);
@@ -350,13 +355,15 @@ ls_status check_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const 
   if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
     return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
                 pool.num_heads);
-  if (num_q_heads / pool.num_heads != 4)
-    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
+  if (!group_ok(num_q_heads / pool.num_heads))
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 1, 2, 4, 8)",
                 num_q_heads / pool.num_heads);
   if (p->group_agg != LS_AGG_MAX && p->group_agg != LS_AGG_MEAN)
     return fail(LS_ERR_INVALID, "group_agg %d", p->group_agg);
   if (p->score_mode != LS_SCORE_MEAN && p->score_mode != LS_SCORE_BOUNDS)
     return fail(LS_ERR_INVALID, "score_mode %d", p->score_mode);
+  if (p->score_mode == LS_SCORE_BOUNDS && num_q_heads / pool.num_heads != 4)
+    return fail(LS_ERR_UNSUPPORTED, "bounds scoring needs GQA group 4");
   if (p->score_mode == LS_SCORE_BOUNDS && batch.batch_size > 0 && !bounds_ok(pool, batch))
     return fail(LS_ERR_UNSUPPORTED,
                 "bounds scoring needs max_blocks <= 8192 and num_pages < 2^26");
@@ -564,13 +571,15 @@ ls_status ls_score_select(const void* q, int32_t q_dtype, int32_t num_q_heads,
   if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
     return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
                 pool.num_heads);
-  if (num_q_heads / pool.num_heads != 4)
-    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
+  if (!group_ok(num_q_heads / pool.num_heads))
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 1, 2, 4, 8)",
                 num_q_heads / pool.num_heads);
   if (p->group_agg != LS_AGG_MAX && p->group_agg != LS_AGG_MEAN)
     return fail(LS_ERR_INVALID, "group_agg %d", p->group_agg);
   if (p->score_mode != LS_SCORE_MEAN && p->score_mode != LS_SCORE_BOUNDS)
     return fail(LS_ERR_INVALID, "score_mode %d", p->score_mode);
+  if (p->score_mode == LS_SCORE_BOUNDS && num_q_heads / pool.num_heads != 4)
+    return fail(LS_ERR_UNSUPPORTED, "bounds scoring needs GQA group 4");
   if (p->score_mode == LS_SCORE_BOUNDS && batch.batch_size > 0 && !bounds_ok(pool, batch))
     return fail(LS_ERR_UNSUPPORTED,
                 "bounds scoring needs max_blocks <= 8192 and num_pages < 2^26");
@@ -646,8 +655,8 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
   if (num_q_heads < 1 || num_q_heads % pool.num_heads != 0)
     return fail(LS_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
                 pool.num_heads);
-  if (num_q_heads / pool.num_heads != 4)
-    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 4)",
+  if (!group_ok(num_q_heads / pool.num_heads))
+    return fail(LS_ERR_UNSUPPORTED, "GQA group size %d (supported: 1, 2, 4, 8)",
                 num_q_heads / pool.num_heads);
   if ((selected == nullptr) != (selected_count == nullptr))
     return fail(LS_ERR_INVALID, "selected and selected_count must both be set or both NULL");
@@ -694,8 +703,8 @@ ls_status ls_sparse_attn_decode(const void* q, int32_t q_dtype, int32_t num_q_he
                                       pairs, batch.max_blocks, w, 0, lay.parts, nullptr);
     return hip_status(ls::launch_plan_attend(pa, stream), "attention kernel launch");
   }
-  hipError_t e = (!selected && pool.num_pages < (1 << 26)) ? ls::launch_attn_chunked(aa, stream)
-                                                            : ls::launch_attn(aa, stream);
+  const bool chunked = !selected && num_q_heads == 4 * pool.num_heads && pool.num_pages < (1 << 26);
+  hipError_t e = chunked ? ls::launch_attn_chunked(aa, stream) : ls::launch_attn(aa, stream);
   // leave the workspace zero
   if (e == hipSuccess) e = ls::launch_zero(w + lay.parts, lay.total - lay.parts, stream);
   return hip_status(e, "attention kernel launch");

@@ -82,7 +82,16 @@ def test_score_select_validation():
     assert _score(lib, p=_params(), pool=_pool(head_dim=96)) == _lib.LS_ERR_UNSUPPORTED
     assert _score(lib, p=_params(), pool=_pool(page_size=8)) == _lib.LS_ERR_UNSUPPORTED
     assert _score(lib, p=_params(), num_q_heads=30) == _lib.LS_ERR_INVALID
-    assert _score(lib, p=_params(), num_q_heads=16) == _lib.LS_ERR_UNSUPPORTED  # group 2
+    assert _score(lib, p=_params(), num_q_heads=24) == _lib.LS_ERR_UNSUPPORTED  # group 3
+    assert _score(lib, p=_params(), num_q_heads=128) == _lib.LS_ERR_UNSUPPORTED  # group 16
+    assert b"1, 2, 4, 8" in lib.ls_last_error()
+    for hq in (8, 16, 64):                                    # groups 1, 2, 8 pass validation
+        assert _score(lib, p=_params(), num_q_heads=hq, ws=FAKE, ws_bytes=16) == \
+            _lib.LS_ERR_WORKSPACE
+    # Quest bounds only with group 4
+    assert _score(lib, p=_params(score_mode=_lib.LS_SCORE_BOUNDS), num_q_heads=16) == \
+        _lib.LS_ERR_UNSUPPORTED
+    assert b"group 4" in lib.ls_last_error()
     assert _score(lib, p=_params(), q_dtype=_lib.LS_DTYPE_FP32) == _lib.LS_ERR_UNSUPPORTED
     assert _score(lib, p=_params(group_agg=7)) == _lib.LS_ERR_INVALID
     assert _score(lib, p=_params(score_mode=2)) == _lib.LS_ERR_INVALID
@@ -125,6 +134,9 @@ def test_attention_validation():
     assert call(ws=FAKE + 1, ws_bytes=1 << 30) == _lib.LS_ERR_INVALID   # misaligned workspace
     assert call(q=FAKE + 2, ws=FAKE, ws_bytes=1 << 30) == _lib.LS_ERR_INVALID  # misaligned q
     assert call(batch=_batch(batch_size=0)) == _lib.LS_OK
+    assert call(hq=24) == _lib.LS_ERR_UNSUPPORTED                 # group 3
+    assert call(hq=64) == _lib.LS_ERR_WORKSPACE                   # group 8: valid
+    assert call(hq=8, sel=None, cnt=None) == _lib.LS_ERR_WORKSPACE   # group 1, dense
     need = lib.ls_sparse_attn_decode_workspace_size(2, 32, 128, 8, 4)
     assert need >= 2 * 32 * lib.ls_attn_num_splits(8) * 130 * 4
     assert lib.ls_attn_num_splits(67) == 9 and lib.ls_attn_num_splits(2048) == 256
