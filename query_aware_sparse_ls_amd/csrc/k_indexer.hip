@@ -384,20 +384,28 @@ __device__ __forceinline__ void idx_find_digit(const uint32_t* h, int nbins, int
 
 // dst[i] = src[i] for i < n (n <= NPT * kIdxMarkThreads), every load of a
 // thread issued before its stores (a plain strided loop would wait out one
-// memory round trip per iteration).
-template <int NPT>
+// memory round trip per iteration). kDev: device-coherent loads, for words
+// that other workgroups of the same launch wrote.
+template <int NPT, bool kDev = false>
 __device__ __forceinline__ void idx_copy_in(uint32_t* dst, const uint32_t* src, int n) {
   uint32_t v[NPT];
 #pragma unroll
   for (int m = 0; m < NPT; ++m) {
     const int i = threadIdx.x + m * kIdxMarkThreads;
-    v[m] = i < n ? src[i] : 0u;
+    v[m] = i < n ? ld_x<kDev>(src + i) : 0u;
   }
 #pragma unroll
   for (int m = 0; m < NPT; ++m) {
     const int i = threadIdx.x + m * kIdxMarkThreads;
     if (i < n) dst[i] = v[m];
   }
+}
+
+// A listed unit (score bits, unit) written by another workgroup of the same
+// launch, read device-coherently.
+__device__ __forceinline__ uint2 ld_dev_u2(const uint2* p) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+  return make_uint2(ld_dev(w), ld_dev(w + 1));
 }
 
 __device__ __forceinline__ int idx_token_of(const IndexerArgs& a, const IdxUnits& g, int r,
@@ -557,9 +565,11 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   // device-coherent stores or atomics, which write through the XCD's L2,
   // and every thread waits for its own to complete before the workgroup's
   // arrival is counted (no release fence: that would write back the whole
-  // L2 under every other workgroup). The finishing workgroup takes one
-  // acquire fence (its XCD's L2 drops stale lines) and then reads
-  // everything with plain, pipelined loads.
+  // L2 under every other workgroup). The finishing workgroup reads every
+  // handed-over word with device-coherent loads (ld_dev), issued after its
+  // arrival atomic has returned, so it needs no acquire fence (whose L2
+  // invalidation cost about 3 us here); what earlier launches wrote (the
+  // candidate blocks) is read with plain loads.
   wait_stores();
   __syncthreads();
   if (tid == 0) {
@@ -569,11 +579,10 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   }
   __syncthreads();
   if (!sh.last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   const int kr = sh.kr;
   const int nwr = (g.n + 31) / 32;
-  idx_copy_in<kIdxMaxWords / kIdxMarkThreads>(sh.bm, bmrow, nwr);
+  idx_copy_in<kIdxMaxWords / kIdxMarkThreads, true>(sh.bm, bmrow, nwr);
   for (int w = tid; w < nwr; w += kIdxMarkThreads) sh.tie[w] = 0u;
   // the candidate blocks (unit -> token map), in LDS when they fit
   const bool cand_lds = a.unit_kind == kUnitsDefault && g.ncand >= 0 && g.ncand <= kIdxBins;
@@ -598,7 +607,7 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
 #pragma unroll
       for (int j = 0; j < UN; ++j) {
         const int i = i0 + j * kIdxMarkThreads + tid;
-        c[j] = i < nc ? crow[i] : make_uint2(0u, 0xFFFFFFFFu);
+        c[j] = i < nc ? ld_dev_u2(crow + i) : make_uint2(0u, 0xFFFFFFFFu);
       }
 #pragma unroll
       for (int j = 0; j < UN; ++j)
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
     const int ncp = (nc + 15) & ~15;
     unsigned long long me = 0ull;
     if (tid < nc) {
-      const uint2 c = crow[tid];
+      const uint2 c = ld_dev_u2(crow + tid);
       me = ((unsigned long long)rank_key(c.x) << 32) | (uint32_t)~c.y;
     }
     if (tid < ncp) lst[tid] = me;
