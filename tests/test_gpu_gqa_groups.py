@@ -10,12 +10,10 @@ just filled.
 
 import math
 
-import numpy as np
 import pytest
 import torch
 
-from parity_util import (build_summaries, check_pair, complete_pages, run_gpu_fused,
-                         run_gpu_step, say)
+from parity_util import build_summaries, check_pair, run_gpu_fused, run_gpu_step, say
 from workloads import LLAMA8B_32K_B16, make_block_topk_inputs, reduced
 
 pytestmark = pytest.mark.gpu
@@ -85,7 +83,6 @@ def test_groups_fused_step_with_refresh(G, hq, hkv):
     """The step in one call equals the separate calls bit for bit, and with
     every request's last complete page stale (NaN) and passed as just filled,
     it rebuilds those summaries and still gives the same result."""
-    import query_aware_sparse_ls_amd as ls
     cfg = _cfg(G, hq, hkv, 128)
     say(f"GQA group {G}, fused step: {cfg.name}")
     inp = make_block_topk_inputs(cfg, device="cuda", seed=97 + G, seq_lens=LENS)
@@ -105,3 +102,18 @@ def test_groups_fused_step_with_refresh(G, hq, hkv):
     _same(ref, got)
     for r in range(cfg.batch):
         check_pair(inp, got, r, 0, check_scores=False, **_kw(inp))
+
+
+def test_group8_full_size_16x32k_sampled():
+    """64 query heads over 8 kv heads (group 8) at 16 requests x 32K: the
+    split kernels at the benchmark's batch and context; sampled pairs against
+    the oracle, every pair's selection size and padding checked."""
+    cfg = reduced(LLAMA8B_32K_B16, name="gqa8_16x32k", num_q_heads=64, num_kv_heads=8)
+    say(f"GQA group 8 at full size: {cfg.name}")
+    inp = make_block_topk_inputs(cfg, device="cuda", seed=99)
+    res = run_gpu_step(inp)
+    nb = cfg.context // cfg.page_size
+    want = min(nb, inp.topk + cfg.n_sink + cfg.n_recent)
+    assert (res.counts == want).all()
+    for r, g in [(0, 0), (5, 3), (11, 6), (15, 7)]:
+        check_pair(inp, res, r, g, **_kw(inp))
