@@ -1666,7 +1666,7 @@ def _bench_block_topk_parent(args, blocks, pool) -> int:
         "stream_read": None if sr is None else {
             "bytes": sr["bytes_per_step"], "ms_median": sr["median_ms_per_step"],
             "GBps_median": sr["GBps_at_median"], "pct_of_hbm_peak": sr["pct_of_hbm_peak_at_median"],
-            "kernel": "ls::stream_read_kernel (16-byte non-temporal loads)"},
+            "kernel": "ls::stream_read_kernel (4 KB chunks per wave round, 16-byte non-temporal loads)"},
         "beyond_byte_time": rb.get("beyond_byte_time"),
         "repeat_blocks": rb,
         "single_call_latency_us": round(lat_us, 2),

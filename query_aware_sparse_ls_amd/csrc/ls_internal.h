@@ -263,8 +263,9 @@ struct MlaArgs {
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t st);
 
-// Measurement reference (k_probe.hip): one streaming read of `bytes` bytes.
-constexpr int kStreamReadWorkgroups = 4096;
+// Measurement reference (k_probe.hip): one streaming read of `bytes` bytes
+// (2048 workgroups of four waves measured best on MI355X).
+constexpr int kStreamReadWorkgroups = 2048;
 // Debug check of a batch's device data (ls_check_batch, and LS_DEBUG): one
 // workgroup; report = the caller's 4 words (overwritten) or the library's
 // debug words (accumulated).
