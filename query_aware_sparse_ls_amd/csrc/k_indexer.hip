@@ -713,19 +713,27 @@ __global__ __launch_bounds__(kIdxMarkThreads) void idx_mark_kernel(IndexerArgs a
   int stot;
   int pos = idx_block_scan(scount, sh.red, &stot);
   int32_t* out = a.selected + (size_t)r * a.max_selected;
+  // one loop per unit -> token map: a map that reads global memory (token
+  // candidates) would make every store of a shared loop wait for all memory
+  // operations before it, the earlier stores included
+  auto emit_all = [&](auto token_of) {
 #pragma unroll
-  for (int i = 0; i < WMAX; ++i) {
-    uint32_t x = bw[i];
-    while (x) {
-      const int b = __ffs(x) - 1;
-      x &= x - 1u;
-      if (pos < a.max_selected) {
-        const int u = 32 * (w0 + i) + b;
-        out[pos] = cand_lds ? (int)sh.h2[u >> PS] * P + (u & (P - 1)) : idx_token_of(a, g, r, u);
+    for (int i = 0; i < WMAX; ++i) {
+      uint32_t x = bw[i];
+      while (x) {
+        const int b = __ffs(x) - 1;
+        x &= x - 1u;
+        if (pos < a.max_selected) out[pos] = token_of(32 * (w0 + i) + b);
+        ++pos;
       }
-      ++pos;
     }
-  }
+  };
+  if (cand_lds)
+    emit_all([&](int u) { return (int)sh.h2[u >> PS] * P + (u & (P - 1)); });
+  else if (a.unit_kind != kUnitsTokenCands && g.ncand < 0)
+    emit_all([](int u) { return u; });
+  else
+    emit_all([&](int u) { return idx_token_of(a, g, r, u); });
   for (int i = stot + tid; i < a.max_selected; i += kIdxMarkThreads) out[i] = -1;
   if (tid == 0) a.selected_count[r] = stot < a.max_selected ? stot : a.max_selected;
 }
