@@ -118,7 +118,7 @@ def load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} not found: build the HIP library first "
-            "(python -m query_aware_sparse_ls_amd.build)")
+            "(python query_aware_sparse_ls_amd/build.py, or __graft_entry__.build())")
     lib = C.CDLL(LIB_PATH)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)

@@ -299,32 +299,39 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const bool out32 = a.out_dtype == LS_DTYPE_FP32;
   const float* ml = a.partials + (size_t)row * S * 2;
   const char* obase = reinterpret_cast<const char*>(a.partials) + mla_o_offset(a);
+  // 8 splits per round; the o rows do not depend on the running maximum, so
+  // the first round's are issued before the (m, l) pairs and all of them
+  // arrive in one memory round trip (splits past S re-read split S - 1 and
+  // get weight 0)
+  constexpr int U = 8;
+  float4 vf[U];
+  uint2 vb[U];
+  auto load_o = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int s = s0 + j < S ? s0 + j : S - 1;
+      const size_t oi = ((size_t)row * S + s) * kMlaDv + 4 * t;
+      if (out32) vf[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(obase) + oi);
+      else vb[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(obase) + oi);
+    }
+  };
+  load_o(0);
   float M = kNegInf;
   for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
   float O[4] = {0.0f, 0.0f, 0.0f, 0.0f}, Ls = 0.0f;
   if (M != kNegInf) {
-    // 4 splits per round with their loads issued together (in split order)
-    constexpr int U = 4;
     for (int s0 = 0; s0 < S; s0 += U) {
-      float f[U], ls[U];
-      float4 vf[U];
-      uint2 vb[U];
+      if (s0 > 0) load_o(s0);
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int s = s0 + j < S ? s0 + j : S - 1;
-        f[j] = s0 + j < S ? exp2_fast(ml[2 * s] - M) : 0.0f;   // splits with m = -inf give 0
-        ls[j] = ml[2 * s + 1];
-        const size_t oi = ((size_t)row * S + s) * kMlaDv + 4 * t;
-        if (out32) vf[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(obase) + oi);
-        else vb[j] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(obase) + oi);
-      }
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        Ls += f[j] * ls[j];
+        const float f = s0 + j < S ? exp2_fast(ml[2 * s] - M) : 0.0f;   // splits with m = -inf give 0
+        const float ls = ml[2 * s + 1];
+        Ls += f * ls;
         if (out32) {
-          O[0] += f[j] * vf[j].x; O[1] += f[j] * vf[j].y; O[2] += f[j] * vf[j].z; O[3] += f[j] * vf[j].w;
+          O[0] += f * vf[j].x; O[1] += f * vf[j].y; O[2] += f * vf[j].z; O[3] += f * vf[j].w;
         } else {
-          const float w = f[j] * ls[j];   // the split's o was stored divided by its l
+          const float w = f * ls;   // the split's o was stored divided by its l
           O[0] += w * bf16_lo(vb[j].x); O[1] += w * bf16_hi(vb[j].x);
           O[2] += w * bf16_lo(vb[j].y); O[3] += w * bf16_hi(vb[j].y);
         }
