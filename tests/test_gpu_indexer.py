@@ -326,6 +326,23 @@ def test_mla_dense_equals_all_tokens():
         _check_mla(inp, h, out, lse, r, np.arange(L), torch.float32, sm, f"dense r{r}")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_mla_dense_many_splits(out_dtype):
+    """Every token of a 4,160-token cache: 17 splits of 256 tokens, so the
+    merge takes three rounds of eight splits, the last one padded; requests
+    shorter than the cache leave trailing splits empty."""
+    say(f"mla dense, 17 splits, out {out_dtype}")
+    lens = [4160, 2305, 1]
+    cfg = reduced(INDEXER_128K, batch=3, context=64 * 65, mla_heads=32, seed=27)
+    inp = make_indexer_inputs(cfg, device=_dev())
+    inp.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+    h = _host(inp)
+    sm = 0.05
+    out, lse = _run_mla(inp, None, None, out_dtype, sm)
+    for r, L in enumerate(lens):
+        _check_mla(inp, h, out, lse, r, np.arange(L), out_dtype, sm, f"dense r{r} L{L}")
+
+
 def test_mla_full_size_config4():
     """8 requests x 2,048 selected tokens of 131,072, 128 heads, bf16 out:
     every head of requests 0 and 7 against the oracle."""
